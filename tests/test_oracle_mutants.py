@@ -1,0 +1,65 @@
+"""The pins must reject plausible mistakes planted in copies of the oracle source.
+
+Each mutant is a textual edit of oracle/evo_ref.c (a dropped term, a wrong
+index, a transposed operand, a wrong constant), compiled with gcc into a
+temporary directory and loaded through the same ctypes interface.  The real
+oracle is never modified.  A mutant survives if every pin passes on it; the
+test fails if any mutant survives.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "evo_ref.c")
+
+MUTANTS = {
+    "drop_mask": [("if (a->mask) sj += load", "if (0) sj += load")],
+    "drop_pair": [("if (a->pair) sj += load", "if (0) sj += load")],
+    "pair_transposed": [("off_pair(a, b, h, i, j)", "off_pair(a, b, h, j, i)")],
+    "pair_ignores_head": [("off_pair(a, b, h, i, j)", "off_pair(a, b, 0, i, j)")],
+    "mask_by_query": [("off_mask(a, b, n, j)", "off_mask(a, b, n, i)")],
+    "mask_ignores_n": [("off_mask(a, b, n, j)", "off_mask(a, b, 0, j)")],
+    "scale_1_over_D": [("1.0 / sqrt((double)D)", "1.0 / (double)D")],
+    "no_scale": [("double sj = dot * scale;", "double sj = dot;")],
+    "scale_on_bias_too": [("double sj = dot * scale;", "double sj = dot;"), ("s[j] = sj;", "s[j] = sj * scale;")],
+    "key_index_slip": [("qrow[d] * kd[j * D + d]", "qrow[d] * kd[i * D + d]")],
+    "values_from_keys": [("w * vd[j * D + e]", "w * kd[j * D + e]")],
+    "kv_ignore_head": [("int64_t o = off_qkv(a, b, n, j, h, d);", "int64_t o = off_qkv(a, b, n, j, 0, d);")],
+    "q_ignores_head": [("off_qkv(a, b, n, i, h, d));", "off_qkv(a, b, n, i, 0, d));")],
+    "no_normaliser": [("double w = s[j] / Z;", "double w = s[j];")],
+    "lse_without_max": [("return m + log(Z);", "return log(Z);")],
+    "lse_log2": [("return m + log(Z);", "return m + log2(Z);")],
+    "lse_layout_BNLH": [("lse[((b * N + n) * H + h) * L + i]", "lse[((b * N + n) * L + i) * H + h]")],
+    "max_added_not_subtracted": [("s[j] = exp(s[j] - m);", "s[j] = exp(s[j] + m);")],
+    "max_starts_at_zero": [("double m = -INFINITY;", "double m = 0.0;")],
+    "bf16_shift": [("((uint32_t)bits) << 16", "((uint32_t)bits) << 15")],
+    "f16_exponent_bias": [("expo - 25", "expo - 24")],
+    "f16_subnormal_scale": [("(double)frac, -24)", "(double)frac, -23)")],
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_mutant(name, tmp_path):
+    with open(SRC) as f:
+        text = f.read()
+    for old, new in MUTANTS[name]:
+        assert text.count(old) == 1, f"mutation anchor {old!r} must occur exactly once"
+        text = text.replace(old, new)
+    src = tmp_path / f"mut_{name}.c"
+    src.write_text(text)
+    lib = oracle.load_library(oracle.compile_source(str(src), str(tmp_path / f"libmut_{name}.so")))
+
+    def ref(q, k, v, mask, pair, dtype):
+        return oracle.fwd(q, k, v, mask, pair, dtype=dtype, nthreads=2, lib=lib)
+
+    caught_by = None
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(ref)
+        except (AssertionError, RuntimeError):
+            caught_by = pin.__name__
+            break
+    assert caught_by is not None, f"mutant {name} passed every pin"
