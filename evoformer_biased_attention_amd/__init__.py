@@ -1,0 +1,140 @@
+"""Python binding of libevoattn.so, the MI355X Evoformer biased-attention forward library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/evo_attn.h.  The functions keep
+the C names (`evo_attn_fwd`, `evo_attn_check`, `evo_status_string`) and take
+either raw device addresses (int) or torch tensors, whose `data_ptr()` is
+passed through; PyTorch is used for device memory and streams only.
+
+The library must be built first (`python evoformer_biased_attention_amd/build.py`
+or `__graft_entry__.build()`); importing this package without it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libevoattn.so")
+
+EVO_DTYPE_F32, EVO_DTYPE_BF16, EVO_DTYPE_F16 = 0, 1, 2
+(EVO_OK, EVO_ERR_NULL_POINTER, EVO_ERR_BAD_SHAPE, EVO_ERR_BAD_DTYPE, EVO_ERR_MISALIGNED, EVO_ERR_ALIASING,
+ EVO_ERR_UNSUPPORTED, EVO_ERR_HIP) = range(8)
+
+# Symbols declared in include/evo_attn.h.
+EXPORTED = ("evo_attn_fwd", "evo_attn_check", "evo_status_string", "evo_attn_last_hip_error")
+
+
+class EvoShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("N", ctypes.c_int64), ("L", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("D", ctypes.c_int64)]
+
+
+class EvoAttnError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        msg = f"evo_attn status {status}: {evo_status_string(status)}"
+        if status == EVO_ERR_HIP:
+            msg += f" (hipError_t {evo_attn_last_hip_error()})"
+        super().__init__(msg)
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python evoformer_biased_attention_amd/build.py`")
+    # One HIP runtime per process.  PyTorch ships its own libamdhip64 (same
+    # soname, libamdhip64.so.7); loading torch first makes the dynamic loader
+    # bind this library to that runtime instead of mapping a second copy from
+    # /opt/rocm, whose device pointers and streams torch's would not know.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(LIB_PATH)
+    vp = ctypes.c_void_p
+    lib.evo_attn_fwd.restype = ctypes.c_int
+    lib.evo_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(EvoShape), ctypes.c_int, vp]
+    lib.evo_attn_check.restype = ctypes.c_int
+    lib.evo_attn_check.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(EvoShape), ctypes.c_int]
+    lib.evo_status_string.restype = ctypes.c_char_p
+    lib.evo_status_string.argtypes = [ctypes.c_int]
+    lib.evo_attn_last_hip_error.restype = ctypes.c_int
+    lib.evo_attn_last_hip_error.argtypes = []
+    return lib
+
+
+_lib = _load()
+
+
+def _addr(x):
+    """None -> NULL, int -> itself, tensor -> data_ptr()."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _shape(shape):
+    if isinstance(shape, EvoShape):
+        return shape
+    return EvoShape(*[int(s) for s in shape])
+
+
+def evo_status_string(status: int) -> str:
+    return _lib.evo_status_string(int(status)).decode()
+
+
+def evo_attn_last_hip_error() -> int:
+    """hipError_t of this thread's last launch failure (0 if none)."""
+    return _lib.evo_attn_last_hip_error()
+
+
+def evo_attn_check(q, k, v, mask_bias, pair_bias, out, lse, shape, dtype) -> int:
+    """Host-only validation; returns the status code (no HIP call is made)."""
+    return _lib.evo_attn_check(_addr(q), _addr(k), _addr(v), _addr(mask_bias), _addr(pair_bias), _addr(out),
+                               _addr(lse), ctypes.byref(_shape(shape)), int(dtype))
+
+
+def evo_attn_fwd(q, k, v, mask_bias, pair_bias, out, lse, shape, dtype, stream=None) -> int:
+    """Enqueue the forward pass; returns the status code.
+
+    `stream` is a hipStream_t as an int (e.g. torch.cuda.current_stream().cuda_stream)
+    or None for the default stream.
+    """
+    return _lib.evo_attn_fwd(_addr(q), _addr(k), _addr(v), _addr(mask_bias), _addr(pair_bias), _addr(out),
+                             _addr(lse), ctypes.byref(_shape(shape)), int(dtype), stream)
+
+
+def torch_dtype_code(dt) -> int:
+    import torch
+    return {torch.float32: EVO_DTYPE_F32, torch.bfloat16: EVO_DTYPE_BF16, torch.float16: EVO_DTYPE_F16}[dt]
+
+
+def fwd(q, k, v, mask_bias=None, pair_bias=None, out=None, lse=True, stream=None):
+    """torch convenience wrapper: allocates out (and lse) with torch, then calls evo_attn_fwd.
+
+    q, k, v: [B,N,L,H,D] contiguous device tensors; mask_bias [B,N,1,1,L] and
+    pair_bias [B,1,H,L,L] of the same dtype, or None.  Returns (out, lse or None).
+    Raises EvoAttnError for any status other than EVO_OK.
+    """
+    import torch
+    B, N, L, H, D = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("mask_bias", mask_bias), ("pair_bias", pair_bias)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is True:
+        lse_t = torch.empty((B, N, H, L), dtype=torch.float32, device=q.device)
+    elif lse is False or lse is None:
+        lse_t = None
+    else:
+        lse_t = lse
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = evo_attn_fwd(q, k, v, mask_bias, pair_bias, out, lse_t, (B, N, L, H, D), torch_dtype_code(q.dtype),
+                      stream)
+    if st != EVO_OK:
+        raise EvoAttnError(st)
+    return out, lse_t

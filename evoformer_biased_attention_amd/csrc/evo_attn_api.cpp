@@ -1,0 +1,118 @@
+// C ABI of libevoattn.so: argument validation and kernel selection.
+//
+// The checks carry over the input contract of the DS4Sci_EvoformerAttention
+// Python front end described on the page "DeepSpeed DS4Sci_EvoformerAttention
+// 内核实战指南" (hmyw.cn): fp16/bf16 inputs on the accelerator (section 5.1),
+// at most two biases whose shapes are derived from Q's and checked strictly,
+// a missing bias taking the same path as an all-zero one (sections 5.2 and
+// 5.4).  Here the shapes are passed explicitly, so "strict shape checks"
+// become size and overflow checks on evo_shape_t; the guide's L > 16 limit is
+// not kept (any L >= 1 works).
+#include "../../include/evo_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "evo_attn_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxBytes = int64_t(1) << 62;
+
+// a * b without overflow past kMaxBytes; returns -1 on overflow.
+int64_t mul_checked(int64_t a, int64_t b) {
+    if (a < 0 || b < 0) return -1;
+    if (a != 0 && b > kMaxBytes / a) return -1;
+    return a * b;
+}
+
+int64_t elem_size(evo_dtype_t dt) { return dt == EVO_DTYPE_F32 ? 4 : 2; }
+
+struct Extent {
+    uintptr_t lo = 0, hi = 0;  // [lo, hi), empty when lo == hi
+    bool overlaps(const Extent& o) const { return lo < o.hi && o.lo < hi; }
+};
+
+Extent extent(const void* p, int64_t bytes) {
+    Extent e;
+    if (p) {
+        e.lo = reinterpret_cast<uintptr_t>(p);
+        e.hi = e.lo + static_cast<uintptr_t>(bytes);
+    }
+    return e;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+thread_local int g_last_hip_error = 0;
+
+bool supported(evo_dtype_t dt, int64_t D) {
+    if (dt == EVO_DTYPE_BF16) return D == 32;
+    if (dt == EVO_DTYPE_F32) return D == 8 || D == 16 || D == 32 || D == 64;
+    return false;
+}
+
+}  // namespace
+
+extern "C" evo_status_t evo_attn_check(const void* q, const void* k, const void* v, const void* mask_bias,
+                                       const void* pair_bias, const void* out, const float* lse,
+                                       const evo_shape_t* shape, evo_dtype_t dtype) {
+    if (!shape || !q || !k || !v || !out) return EVO_ERR_NULL_POINTER;
+    const int64_t B = shape->B, N = shape->N, L = shape->L, H = shape->H, D = shape->D;
+    if (B < 1 || N < 1 || L < 1 || H < 1 || D < 1) return EVO_ERR_BAD_SHAPE;
+    if (dtype != EVO_DTYPE_F32 && dtype != EVO_DTYPE_BF16 && dtype != EVO_DTYPE_F16) return EVO_ERR_BAD_DTYPE;
+    const int64_t es = elem_size(dtype);
+
+    // Byte sizes of every tensor, each bounded by 2^62.
+    int64_t qkv = es;
+    for (int64_t s : {B, N, L, H, D}) qkv = mul_checked(qkv, s);
+    int64_t msk = es;
+    for (int64_t s : {B, N, L}) msk = mul_checked(msk, s);
+    int64_t par = es;
+    for (int64_t s : {B, H, L, L}) par = mul_checked(par, s);
+    int64_t lsb = 4;
+    for (int64_t s : {B, N, H, L}) lsb = mul_checked(lsb, s);
+    if (qkv < 0 || msk < 0 || par < 0 || lsb < 0) return EVO_ERR_BAD_SHAPE;
+
+    for (const void* p : {q, k, v, mask_bias, pair_bias, out, static_cast<const void*>(lse)})
+        if (p && !aligned16(p)) return EVO_ERR_MISALIGNED;
+
+    const Extent eo = extent(out, qkv), el = extent(lse, lsb);
+    for (const Extent& in : {extent(q, qkv), extent(k, qkv), extent(v, qkv), extent(mask_bias, msk),
+                             extent(pair_bias, par)})
+        if (eo.overlaps(in) || el.overlaps(in)) return EVO_ERR_ALIASING;
+    if (eo.overlaps(el)) return EVO_ERR_ALIASING;
+
+    if (!supported(dtype, D)) return EVO_ERR_UNSUPPORTED;
+    return EVO_OK;
+}
+
+extern "C" evo_status_t evo_attn_fwd(const void* q, const void* k, const void* v, const void* mask_bias,
+                                     const void* pair_bias, void* out, float* lse, const evo_shape_t* shape,
+                                     evo_dtype_t dtype, void* stream) {
+    const evo_status_t st = evo_attn_check(q, k, v, mask_bias, pair_bias, out, lse, shape, dtype);
+    if (st != EVO_OK) return st;
+    evo::FwdArgs a{q, k, v, mask_bias, pair_bias, out, lse, shape->B, shape->N, shape->L, shape->H, shape->D};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err = dtype == EVO_DTYPE_BF16 ? evo::launch_fwd_bf16_d32(a, s) : evo::launch_fwd_f32(a, s);
+    if (err == hipSuccess) return EVO_OK;
+    g_last_hip_error = static_cast<int>(err);
+    return EVO_ERR_HIP;
+}
+
+extern "C" int evo_attn_last_hip_error(void) { return g_last_hip_error; }
+
+extern "C" const char* evo_status_string(evo_status_t status) {
+    switch (status) {
+    case EVO_OK: return "ok";
+    case EVO_ERR_NULL_POINTER: return "a required pointer (q, k, v, out or shape) is NULL";
+    case EVO_ERR_BAD_SHAPE: return "a size is below 1 or a tensor exceeds 2^62 bytes";
+    case EVO_ERR_BAD_DTYPE: return "dtype is not an evo_dtype_t value";
+    case EVO_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
+    case EVO_ERR_ALIASING: return "out or lse overlaps an input or each other";
+    case EVO_ERR_UNSUPPORTED: return "dtype / head dimension combination not implemented";
+    case EVO_ERR_HIP: return "the HIP runtime reported an error at launch";
+    }
+    return "unknown status";
+}

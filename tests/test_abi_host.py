@@ -1,0 +1,147 @@
+"""The C ABI on the host: symbols, enum values and the pure-host validation.
+
+No compute call is made here (no GPU is needed): evo_attn_check never
+dereferences its pointers, so fake, aligned addresses are enough.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import evoformer_biased_attention_amd as E
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "evo_attn.h")
+
+
+def _header_text():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def test_header_declares_exactly_the_exported_names():
+    decls = set(re.findall(r"^\s*(?:const\s+char\s*\*|evo_status_t|int)\s+(evo_\w+)\s*\(", _header_text(), re.M))
+    assert decls == set(E.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(E.LIB_PATH)
+    for name in E.EXPORTED:
+        assert hasattr(lib, name), name
+
+
+def test_enum_values_match_header():
+    text = _header_text()
+    for name in ("EVO_DTYPE_F32", "EVO_DTYPE_BF16", "EVO_DTYPE_F16", "EVO_OK", "EVO_ERR_NULL_POINTER",
+                 "EVO_ERR_BAD_SHAPE", "EVO_ERR_BAD_DTYPE", "EVO_ERR_MISALIGNED", "EVO_ERR_ALIASING",
+                 "EVO_ERR_UNSUPPORTED", "EVO_ERR_HIP"):
+        m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
+        assert m and int(m.group(1)) == getattr(E, name), name
+
+
+def test_status_strings():
+    for s in range(8):
+        assert E.evo_status_string(s) and E.evo_status_string(s) != "unknown status"
+    assert E.evo_status_string(99) == "unknown status"
+
+
+# Fake device addresses, 1 GiB apart and 256-byte aligned; never dereferenced.
+BASE = 0x7F0000000000
+GIB = 1 << 30
+
+
+def addrs(n=8):
+    return [BASE + i * GIB for i in range(n)]
+
+
+def check(shape=(1, 2, 64, 4, 32), dtype=E.EVO_DTYPE_BF16, **over):
+    q, k, v, m, p, o, l = addrs(7)
+    args = dict(q=q, k=k, v=v, mask_bias=m, pair_bias=p, out=o, lse=l)
+    args.update(over)
+    return E.evo_attn_check(args["q"], args["k"], args["v"], args["mask_bias"], args["pair_bias"], args["out"],
+                            args["lse"], shape, dtype)
+
+
+def test_valid_bf16_and_f32():
+    assert check() == E.EVO_OK
+    assert check(mask_bias=None, pair_bias=None, lse=None) == E.EVO_OK
+    for d in (8, 16, 32, 64):
+        assert check(shape=(2, 3, 17, 2, d), dtype=E.EVO_DTYPE_F32) == E.EVO_OK
+    assert check(shape=(1, 1, 1, 1, 32)) == E.EVO_OK  # L = 1 is accepted
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "out"])
+def test_null_required_pointer(name):
+    assert check(**{name: None}) == E.EVO_ERR_NULL_POINTER
+
+
+def test_null_shape():
+    q, k, v, m, p, o, l = addrs(7)
+    st = E._lib.evo_attn_check(q, k, v, m, p, o, l, None, E.EVO_DTYPE_BF16)
+    assert st == E.EVO_ERR_NULL_POINTER
+
+
+@pytest.mark.parametrize("shape", [(0, 1, 8, 1, 32), (1, 0, 8, 1, 32), (1, 1, 0, 1, 32), (1, 1, 8, 0, 32),
+                                   (1, 1, 8, 1, 0), (-1, 1, 8, 1, 32), (1 << 20, 1 << 20, 1 << 20, 1, 32),
+                                   (1, 1, 1 << 31, 1 << 10, 32)])
+def test_bad_shape(shape):
+    assert check(shape=shape) == E.EVO_ERR_BAD_SHAPE
+
+
+def test_bad_dtype():
+    assert check(dtype=3) == E.EVO_ERR_BAD_DTYPE
+    assert check(dtype=-1) == E.EVO_ERR_BAD_DTYPE
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "mask_bias", "pair_bias", "out", "lse"])
+def test_misaligned(name):
+    a = dict(zip(["q", "k", "v", "mask_bias", "pair_bias", "out", "lse"], addrs(7)))
+    assert check(**{name: a[name] + 8}) == E.EVO_ERR_MISALIGNED
+
+
+def test_aliasing():
+    q, k, v, m, p, o, l = addrs(7)
+    assert check(out=q) == E.EVO_ERR_ALIASING
+    assert check(out=k + 1024) == E.EVO_ERR_ALIASING          # overlaps inside k's extent
+    assert check(lse=p) == E.EVO_ERR_ALIASING
+    assert check(lse=o + 256) == E.EVO_ERR_ALIASING           # lse inside out
+    assert check(out=m) == E.EVO_ERR_ALIASING
+    # adjacent but disjoint extents are fine: q of (1,2,64,4,32) bf16 is 65536 bytes
+    assert check(out=q + 65536) == E.EVO_OK
+    assert check(mask_bias=None, out=m) == E.EVO_OK            # a NULL bias has no extent
+
+
+def test_inputs_may_alias_each_other():
+    q, *_ = addrs(1)
+    assert check(k=q, v=q) == E.EVO_OK  # self-attention on one tensor is legal: inputs are read-only
+
+
+@pytest.mark.parametrize("dtype,d", [(E.EVO_DTYPE_BF16, 16), (E.EVO_DTYPE_BF16, 64), (E.EVO_DTYPE_F16, 32),
+                                     (E.EVO_DTYPE_F32, 12), (E.EVO_DTYPE_F32, 128)])
+def test_unsupported(dtype, d):
+    assert check(shape=(1, 1, 32, 1, d), dtype=dtype) == E.EVO_ERR_UNSUPPORTED
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    """The product path has no fallback: a missing library is an ImportError."""
+    import importlib.util
+    import shutil
+    pkg = tmp_path / "evoformer_biased_attention_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "evoformer_biased_attention_amd", "__init__.py"), pkg / "__init__.py")
+    spec = importlib.util.spec_from_file_location("evo_copy", pkg / "__init__.py")
+    mod = importlib.util.module_from_spec(spec)
+    with pytest.raises(ImportError):
+        spec.loader.exec_module(mod)
+
+
+def test_single_hip_runtime_in_process():
+    """Importing the binding leaves exactly one libamdhip64 mapped (torch's, when torch is installed)."""
+    import subprocess
+    import sys
+    code = ("import evoformer_biased_attention_amd, torch\n"
+            "maps = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(maps)); print(sorted(maps))")
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, check=True)
+    assert res.stdout.splitlines()[0] == "1", res.stdout

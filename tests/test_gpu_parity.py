@@ -1,0 +1,214 @@
+"""HIP path vs the fp64 oracle, element by element, through the C ABI.
+
+Tolerances (floating point):
+  f32 path:  max |dO| <= 1e-4, max |dLSE| <= 1e-4
+  bf16 path: max |dO| <= 2e-2, mean |dO| <= 2e-3, max |dLSE| <= 1e-2
+The bf16 budget is dominated by rounding O to bf16 (half an ulp is 2^-9
+relative) and by rounding the probabilities to bf16 before the P.V product;
+scores themselves are exact products of bf16 values accumulated in fp32.
+
+Outputs are poisoned with NaN before every launch, so an element the kernel
+fails to write shows up as a mismatch.
+"""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as S
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": dict(max_o=1e-4, mean_o=1e-4, max_lse=1e-4),
+       "bf16": dict(max_o=2e-2, mean_o=2e-3, max_lse=1e-2)}
+THREADS = min(16, oracle.default_threads())
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import evoformer_biased_attention_amd  # noqa: F401  (fails loudly if the library is missing)
+    return torch
+
+
+def to_dev(torch, x, dtype):
+    if x is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype == "bf16":
+        t = t.view(torch.bfloat16)
+    elif dtype == "f16":
+        t = t.view(torch.float16)
+    return t.to("cuda")
+
+
+def run_gpu(torch, w, lse=True, stream=None):
+    """Launch the HIP path on workload w; returns (out float64 numpy, lse float64 numpy or None)."""
+    import evoformer_biased_attention_amd as E
+    q, k, v = (to_dev(torch, x, w.dtype) for x in (w.q, w.k, w.v))
+    mask, pair = to_dev(torch, w.mask, w.dtype), to_dev(torch, w.pair, w.dtype)
+    out = torch.full_like(q, float("nan"))
+    B, N, L, H, D = w.shape
+    lse_t = torch.full((B, N, H, L), float("nan"), dtype=torch.float32, device="cuda") if lse else None
+    say(f"  launch {w.name} shape={w.shape} dtype={w.dtype} mask={w.mask is not None} pair={w.pair is not None}")
+    E.fwd(q, k, v, mask, pair, out=out, lse=lse_t if lse else False, stream=stream)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    l = lse_t.cpu().numpy().astype(np.float64) if lse else None
+    return o, l
+
+
+def compare(o, l, ro, rl, dtype, what=""):
+    tol = TOL[dtype]
+    assert np.isfinite(o).all(), f"{what}: non-finite output"
+    do = np.abs(o - ro)
+    msg = f"{what}: max|dO|={do.max():.3e} mean|dO|={do.mean():.3e}"
+    if l is not None:
+        neg = np.isneginf(rl)
+        assert np.array_equal(np.isneginf(l), neg), f"{what}: -inf LSE rows differ"
+        dl = np.abs(l[~neg] - rl[~neg]) if (~neg).any() else np.zeros(1)
+        msg += f" max|dLSE|={dl.max():.3e}"
+        assert dl.max() <= tol["max_lse"], msg
+    say("  " + msg)
+    assert do.max() <= tol["max_o"], msg
+    assert do.mean() <= tol["mean_o"], msg
+
+
+def parity_full(torch, w, lse=True):
+    o, l = run_gpu(torch, w, lse=lse)
+    ro, rl = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype=w.dtype, nthreads=THREADS)
+    compare(o, l, ro, rl if lse else None, w.dtype, w.name)
+    return o, l
+
+
+def parity_sampled(torch, w, count=4096, seed=7):
+    o, l = run_gpu(torch, w)
+    idx = S.sample_rows(w.shape, count, seed=seed)
+    ro, rl = oracle.rows(w.q, w.k, w.v, w.mask, w.pair, dtype=w.dtype, idx=idx, nthreads=THREADS)
+    b, n, h, i = idx.T
+    compare(o[b, n, i, h, :], l[b, n, h, i], ro, rl, w.dtype, f"{w.name} ({len(idx)} sampled rows)")
+    # properties over every row: finite, and each output is a convex combination of value rows
+    vf = S.storage_to_f32(w.v, w.dtype)
+    assert np.isfinite(l).all()
+    vmax = np.abs(vf).max(axis=2, keepdims=True)  # [B,N,1,H,D]
+    assert (np.abs(o) <= vmax * (1 + 2 ** -7) + 1e-6).all()
+    return o, l
+
+
+# ---------------------------------------------------------------------------
+# The five named workloads at full size, in the launch configuration that the
+# benchmark times.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("c", [1, 2, 4])
+def test_workload_full_oracle(torch_dev, c):
+    say(f"workload {c}: full oracle comparison")
+    parity_full(torch_dev, S.workload(c))
+
+
+@pytest.mark.parametrize("c", [3, 5])
+def test_workload_sampled_rows(torch_dev, c):
+    say(f"workload {c}: sampled-row oracle comparison")
+    parity_sampled(torch_dev, S.workload(c))
+
+
+# ---------------------------------------------------------------------------
+# Ragged and edge shapes (bf16 MFMA path).
+# ---------------------------------------------------------------------------
+RAGGED = [
+    (1, 1, 1, 1, 32), (1, 2, 5, 3, 32), (2, 3, 17, 2, 32), (1, 2, 64, 1, 32), (1, 3, 100, 2, 32),
+    (2, 2, 129, 3, 32), (1, 2, 200, 4, 32), (1, 1, 255, 1, 32), (1, 2, 257, 2, 32), (3, 2, 33, 5, 32),
+]
+
+
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("bias", ["both", "mask", "pair", "none"])
+def test_ragged_bf16(torch_dev, shape, bias):
+    B, N, L, H, D = shape
+    w = S.random_problem(B, N, L, H, D, dtype="bf16", seed=sum(shape) * 7 + len(bias),
+                         mask="tail" if bias in ("both", "mask") else None,
+                         pair="normal" if bias in ("both", "pair") else None, mask_frac=0.3)
+    say(f"ragged bf16 {shape} bias={bias}")
+    parity_full(torch_dev, w)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1, 8), (1, 2, 17, 3, 16), (2, 2, 65, 2, 32), (1, 2, 100, 2, 64),
+                                   (1, 3, 130, 1, 32)], ids=lambda s: "x".join(map(str, s)))
+def test_ragged_f32(torch_dev, shape):
+    B, N, L, H, D = shape
+    w = S.random_problem(B, N, L, H, D, dtype="f32", seed=sum(shape), mask="tail", pair="normal", mask_frac=0.3)
+    say(f"ragged f32 {shape}")
+    parity_full(torch_dev, w)
+
+
+def test_large_bias_magnitudes(torch_dev):
+    """Biases of scale 8 (peaked softmax) and random -1e9 masks."""
+    w = S.random_problem(1, 4, 192, 2, 32, dtype="bf16", seed=77, mask="random", pair="normal", mask_frac=0.5,
+                         bias_scale=8.0)
+    parity_full(torch_dev, w)
+
+
+def test_ds4sci_unit_test_shape(torch_dev):
+    """The guide's unit-test shape (1,256,256,4,32) with a mask and a random pair bias (section 4)."""
+    import json
+    with open(os.path.join(os.path.dirname(__file__), "golden", "ds4sci_guide_facts.json")) as f:
+        facts = json.load(f)
+    shape = tuple(facts["unit_test"]["shapes_B_N_L_H_D"][0])
+    w = S.random_problem(*shape, dtype="bf16", seed=4050, mask="tail", pair="normal", mask_frac=0.1)
+    o, l = parity_full(torch_dev, w)
+
+
+def test_without_lse(torch_dev):
+    w = S.random_problem(1, 2, 70, 2, 32, dtype="bf16", seed=3, mask="tail", pair="normal")
+    parity_full(torch_dev, w, lse=False)
+
+
+def test_neg_inf_mask_rows(torch_dev):
+    """-inf masks in bf16: partially masked rows are exact softmaxes over the rest; a row whose every key
+    is -inf returns out = 0 and lse = -inf."""
+    B, N, L, H, D = 1, 3, 80, 2, 32
+    w = S.random_problem(B, N, L, H, D, dtype="bf16", seed=8, mask="zero", pair="normal")
+    mf = np.zeros((B, N, 1, 1, L), np.float32)
+    mf[0, 0, ..., 10:50] = -np.inf
+    mf[0, 1] = -np.inf
+    w.mask = S.to_storage(mf, "bf16")
+    o, l = run_gpu(torch_dev, w)
+    ro, rl = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype="bf16", nthreads=THREADS)
+    assert np.all(o[0, 1] == 0) and np.all(np.isneginf(l[0, 1]))
+    compare(o, l, ro, rl, "bf16", "neg-inf mask")
+
+
+def test_non_default_stream(torch_dev):
+    torch = torch_dev
+    w = S.random_problem(1, 2, 96, 2, 32, dtype="bf16", seed=12, mask="tail", pair="normal")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, l = run_gpu(torch, w, stream=s.cuda_stream)
+    ro, rl = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype="bf16", nthreads=THREADS)
+    compare(o, l, ro, rl, "bf16", "side stream")
+
+
+def test_errors_write_nothing(torch_dev):
+    """Rejected calls return a status and leave the outputs untouched."""
+    torch = torch_dev
+    import evoformer_biased_attention_amd as E
+    q = torch.zeros((1, 1, 32, 1, 16), dtype=torch.bfloat16, device="cuda")
+    out = torch.full_like(q, 7.0)
+    st = E.evo_attn_fwd(q, q, q, None, None, out, None, (1, 1, 32, 1, 16), E.EVO_DTYPE_BF16,
+                        torch.cuda.current_stream().cuda_stream)
+    assert st == E.EVO_ERR_UNSUPPORTED
+    st = E.evo_attn_fwd(q, q, q, None, None, q, None, (1, 1, 32, 1, 16), E.EVO_DTYPE_BF16, None)
+    assert st == E.EVO_ERR_ALIASING
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+    with pytest.raises(E.EvoAttnError):
+        E.fwd(q, q, q)
