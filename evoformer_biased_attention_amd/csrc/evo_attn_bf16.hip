@@ -6,28 +6,36 @@
 //   lse_i = ln sum_j exp(...),
 // with the [L, L] score matrix never written to memory.
 //
-// Design (CDNA4, wave64):
-//  * Both dense contractions run on v_mfma_f32_16x16x32_bf16 with fp32
-//    accumulation.  Scores are formed transposed, S^T = K . Q^T, so that the
-//    MFMA result layout puts one query per lane column: lane (c + 16 g) holds
-//    query c and keys 4g..4g+3 of every 16-key tile.  Row statistics (max,
-//    sum) are therefore lane-local up to a 4-way cross-lane reduction, and the
-//    probabilities of a lane are exactly the B operand of the second MFMA,
-//    O^T = V^T . P^T, whose result again has one query per lane column: the
-//    online-softmax rescale of the output accumulator needs no data movement.
-//  * V is the only operand that needs its contraction index (the key) made
-//    contiguous per lane; each 64-key block of V is written transposed into
-//    LDS once per workgroup and read as 8-byte rows by every wavefront.
-//  * Q and K operands are read straight from global memory as 16-byte rows
-//    (D = 32 bf16 = 64 contiguous bytes per row); the 4 wavefronts of a
-//    workgroup share the K rows through the L1 cache.
-//  * The softmax works in base 2: s2 = s * log2(e), exp2 on v_exp_f32.
+// Design (CDNA4, wave64, v_mfma_f32_16x16x32_bf16 with fp32 accumulation):
+//  * Scores are formed transposed, S^T = K . Q^T: the MFMA result puts one
+//    query per lane column (lane c + 16g holds query c and keys 4g..4g+3 of a
+//    16-key tile), so each query's softmax state lives in its own 4 lanes, and
+//    those lanes' probabilities are exactly the B operand of the second MFMA,
+//    O^T = V^T . P^T, whose result again has one query per lane column.
+//  * The biases are added by the matrix cores too: an MFMA with an identity
+//    A operand and the bias rows as B operand adds sqrt(D) * bias to the
+//    accumulator before Q.K^T is accumulated on top.  sqrt(D) is split into a
+//    bf16 high part and a bf16 low part (the two halves of the 32-wide
+//    contraction), so the addition is exact to ~2^-16 relative and the biases
+//    are consumed in their stored bf16 form, one 16-byte row load per lane.
+//    Accumulator units are "sqrt(D) * score"; one fma maps them to the base-2
+//    exponent.  A bias of +-inf would turn the identity's zeros into NaN: a
+//    workgroup that sees a NaN row re-runs the slice on an exact VALU path.
+//  * Online softmax with a lazy maximum: the running maximum used for the
+//    exponent is only raised (and the output rescaled) when some score
+//    exceeds it by more than 2^8, so the common iteration costs one per-lane
+//    max and no cross-lane traffic; probabilities stay below 2^8.
+//  * K and V blocks of 64 keys are staged in LDS, double buffered, one
+//    barrier per block; V is written transposed (its contraction index, the
+//    key, must be contiguous per lane).  The pair-bias rows for the next block
+//    are loaded while the current block is processed.
 //
 // Workgroup = 4 wavefronts x 32 queries = 128 queries of one (b, n, h).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 
 #include "evo_attn_launch.h"
 
@@ -43,14 +51,16 @@ typedef uint16_t u16;
 
 constexpr int D = 32;
 constexpr int kWaves = 4;
-constexpr int kQTiles = 2;                    // 16-query MFMA tiles per wavefront
-constexpr int kWaveQ = 16 * kQTiles;          // 32 queries per wavefront
-constexpr int kBlockQ = kWaves * kWaveQ;      // 128 queries per workgroup
-constexpr int kKB = 64;                       // keys per iteration
-constexpr int kKT = kKB / 16;                 // 16-key tiles per iteration
-constexpr int kVtStride = kKB + 8;            // LDS row (one d) of transposed V, in bf16
+constexpr int kQTiles = 2;                // 16-query MFMA tiles per wavefront
+constexpr int kWaveQ = 16 * kQTiles;      // 32 queries per wavefront
+constexpr int kBlockQ = kWaves * kWaveQ;  // 128 queries per workgroup
+constexpr int kKB = 64;                   // keys per block
+constexpr int kKT = kKB / 16;             // 16-key tiles per block
+constexpr int kKStride = D + 8;           // LDS row of K (one key), bf16 elements
+constexpr int kVtStride = kKB + 8;        // LDS row of transposed V (one d), bf16 elements
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.f;              // log2 headroom before the running max is raised
 
 struct Params {
     const u16* q;
@@ -63,7 +73,14 @@ struct Params {
     int64_t N, L, H;
     int64_t qblocks;  // ceil(L / kBlockQ)
     int64_t total;    // number of workgroups
-    float c1;         // log2(e) / sqrt(D)
+    float c1;         // log2(e) / sqrt(D): accumulator units -> base-2 exponent
+    float lazy_acc;   // kLazy in accumulator units
+    uint32_t sqd;     // bf16 bits: low half = sqrt(D) high part, high half = low part
+};
+
+struct Smem {
+    u16 k[2][kKB * kKStride];
+    u16 vt[2][D * kVtStride];
 };
 
 __device__ inline float bf2f(u16 x) { return __builtin_bit_cast(float, (uint32_t)x << 16); }
@@ -77,6 +94,42 @@ __device__ inline bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, 
 
 __device__ inline uint4 load16(const u16* p) { return *reinterpret_cast<const uint4*>(p); }
 
+__device__ inline f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+// Cross-lane max / sum over the four lanes (c, c+16, c+32, c+48) that share a
+// query.  These run once per raised maximum and once in the epilogue, so the
+// LDS-routed __shfl_xor is cheap enough.  (The v_permlane16/32_swap builtins
+// were tried here: with both operands the same value the compiler folded the
+// two swapped halves into one, silently returning x op x.)
+__device__ inline float max_over_groups(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16));
+    return fmaxf(x, __shfl_xor(x, 32));
+}
+
+__device__ inline float sum_over_groups(float x) {
+    x += __shfl_xor(x, 16);
+    return x + __shfl_xor(x, 32);
+}
+
+// Eight consecutive bf16 of a bias row starting at key j0 (j0 % 8 == 0);
+// keys >= L read as 0.  ALIGNED: L % 8 == 0, so the 8 keys are all in range
+// or all out of range and a 16-byte load is legal.
+template <bool ALIGNED>
+__device__ inline uint4 load_bias8(const u16* row, int64_t j0, int64_t L) {
+    if (ALIGNED) return j0 < L ? load16(row + j0) : uint4{0u, 0u, 0u, 0u};
+    uint32_t w[4];
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = j0 + 2 * e < L ? row[j0 + 2 * e] : 0u;
+        const uint32_t hi = j0 + 2 * e + 1 < L ? row[j0 + 2 * e + 1] : 0u;
+        w[e] = lo | (hi << 16);
+    }
+    return uint4{w[0], w[1], w[2], w[3]};
+}
+
 // Workgroups are dealt round-robin over the 8 XCDs.  Renumber them so that
 // each XCD receives one contiguous range of the logical order (b, h, n, query
 // block): the query blocks of one (n, h) share K/V, and all sequences n of one
@@ -87,35 +140,225 @@ __device__ inline int64_t logical_block(int64_t hw, int64_t total) {
     return xcd < extra ? xcd * (per + 1) + j : extra * (per + 1) + (xcd - extra) * per + j;
 }
 
-__global__ __launch_bounds__(kWaves * 64) void fwd_bf16_d32_kernel(Params p) {
-    __shared__ __attribute__((aligned(16))) u16 vt[D * kVtStride];
+struct Slice {
+    int64_t b, n, h, slice, HD, q0;
+    const u16* mrow;   // mask row of (b, n) or nullptr
+    const u16* pbase;  // pair matrix of (b, h) or nullptr
+};
 
-    int64_t id = logical_block(blockIdx.x, p.total);
-    const int64_t qb = id % p.qblocks;
-    id /= p.qblocks;
-    const int64_t n = id % p.N;
-    id /= p.N;
-    const int64_t h = id % p.H;
-    const int64_t b = id / p.H;
+// Stage K and V keys [k0, k0 + 64) of the slice into LDS buffer `buf`
+// (K as [key][d], V transposed as [d][key]); keys >= L are zero.
+struct StageRegs {
+    uint4 kk, vv;
+};
 
-    const int64_t L = p.L, HD = p.H * D;
-    const int64_t slice = ((b * p.N + n) * L * p.H + h) * D;  // element (b, n, 0, h, 0)
-    const int tid = threadIdx.x;
-    const int wave = tid / 64, lane = tid % 64;
-    const int c = lane % 16, g = lane / 16;  // MFMA column (query) and lane group
-    const int64_t q0 = qb * kBlockQ + wave * kWaveQ;
+__device__ inline StageRegs stage_load(const Params& p, const Slice& s, int64_t k0, int tid) {
+    const int key = tid >> 2, dc = (tid & 3) * 8;
+    const int64_t j = k0 + key;
+    StageRegs r{{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    if (j < p.L) {
+        r.kk = load16(p.k + s.slice + j * s.HD + dc);
+        r.vv = load16(p.v + s.slice + j * s.HD + dc);
+    }
+    return r;
+}
 
-    // Q operands: B[k = d][n = query] -> lane (c + 16g) holds q[query c][8g .. 8g+7].
-    bf16x8 qop[kQTiles];
-    for (int t = 0; t < kQTiles; ++t) {
-        int64_t i = q0 + 16 * t + c;
-        if (i >= L) i = L - 1;
-        qop[t] = as_bf16x8(load16(p.q + slice + i * HD + 8 * g));
+__device__ inline void stage_store(Smem& sm, int buf, const StageRegs& r, int tid) {
+    const int key = tid >> 2, dc = (tid & 3) * 8;
+    *reinterpret_cast<uint4*>(&sm.k[buf][key * kKStride + dc]) = r.kk;
+    const uint32_t w[4] = {r.vv.x, r.vv.y, r.vv.z, r.vv.w};
+    u16* col = &sm.vt[buf][dc * kVtStride + key];
+    for (int e = 0; e < 8; ++e) col[e * kVtStride] = (u16)(w[e / 2] >> (16 * (e % 2)));
+}
+
+// ---------------------------------------------------------------------------
+// Fast path.  Returns false (for the whole workgroup) when some row produced
+// a NaN, i.e. a bias held +-inf; nothing has been written in that case.
+// ---------------------------------------------------------------------------
+template <bool PAIR, bool MASK, bool ALIGNED>
+__device__ bool run_fast(const Params& p, const Slice& s, Smem& sm, int tid) {
+    const int64_t L = p.L;
+    const int lane = tid & 63;
+    const int c = lane & 15, g = lane >> 4;
+    const int nblocks = (int)((L + kKB - 1) / kKB);
+
+    // Identity A operand: slot (g, e) stands for key 8*(g%2) + e of a 16-key
+    // tile, weighted by the high (g < 2) or low (g >= 2) part of sqrt(D).
+    bf16x8 ident;
+    {
+        const u16 wt = (u16)(g < 2 ? (p.sqd & 0xffffu) : (p.sqd >> 16));
+        uint32_t w[4];
+        for (int e2 = 0; e2 < 4; ++e2) {
+            const int e = 2 * e2;
+            const uint32_t lo = (c == 8 * (g & 1) + e) ? wt : 0u;
+            const uint32_t hi = (c == 8 * (g & 1) + e + 1) ? wt : 0u;
+            w[e2] = lo | (hi << 16);
+        }
+        ident = as_bf16x8(uint4{w[0], w[1], w[2], w[3]});
     }
 
-    const u16* mrow = p.mask ? p.mask + (b * p.N + n) * L : nullptr;
-    const u16* pbase = p.pair ? p.pair + (b * p.H + h) * L * L : nullptr;
+    // Q operands (B of S^T = K.Q^T): lane (c + 16g) holds q[query c][8g .. 8g+7].
+    bf16x8 qop[kQTiles];
+    int64_t qrow[kQTiles];
+    for (int t = 0; t < kQTiles; ++t) {
+        int64_t i = s.q0 + 16 * t + c;
+        if (i >= L) i = L - 1;
+        qrow[t] = i;
+        qop[t] = as_bf16x8(load16(p.q + s.slice + i * s.HD + 8 * g));
+    }
 
+    // bias operands of the current block: pair rows (per query tile) and the mask row
+    uint4 pop_[kQTiles][kKT];
+    uint4 mop[kKT];
+    auto load_bias = [&](int64_t k0) {
+        for (int kt = 0; kt < kKT; ++kt) {
+            const int64_t j0 = k0 + 16 * kt + 8 * (g & 1);
+            if (PAIR)
+                for (int t = 0; t < kQTiles; ++t) pop_[t][kt] = load_bias8<ALIGNED>(s.pbase + qrow[t] * L, j0, L);
+            if (MASK) mop[kt] = load_bias8<ALIGNED>(s.mrow, j0, L);
+        }
+    };
+
+    f32x4 oacc[kQTiles][2];
+    float mused[kQTiles], msub[kQTiles], mthr[kQTiles], lsum[kQTiles];
+    for (int t = 0; t < kQTiles; ++t) {
+        oacc[t][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        oacc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        mused[t] = -INFINITY;
+        msub[t] = 0.f;
+        mthr[t] = -INFINITY;
+        lsum[t] = 0.f;
+    }
+
+    {
+        const StageRegs r = stage_load(p, s, 0, tid);
+        stage_store(sm, 0, r, tid);
+    }
+    load_bias(0);
+    __syncthreads();
+
+    for (int it = 0; it < nblocks; ++it) {
+        const int buf = it & 1;
+        const int64_t k0 = (int64_t)it * kKB;
+        const bool tail = k0 + kKB > L;
+        const bool more = it + 1 < nblocks;
+        StageRegs nxt;
+        if (more) nxt = stage_load(p, s, k0 + kKB, tid);
+
+        // ---- S^T = sqrt(D)*(pair + mask) + K.Q^T, in accumulator units ----
+        bool mask_on = false;
+        if (MASK) {
+            uint32_t any = 0;
+            for (int kt = 0; kt < kKT; ++kt) any |= mop[kt].x | mop[kt].y | mop[kt].z | mop[kt].w;
+            mask_on = wave_any(any != 0);
+        }
+        f32x4 acc[kQTiles][kKT];
+        for (int kt = 0; kt < kKT; ++kt) {
+            const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.k[buf][(16 * kt + c) * kKStride + 8 * g]));
+            for (int t = 0; t < kQTiles; ++t) {
+                f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (PAIR) a = mfma(ident, as_bf16x8(pop_[t][kt]), a);
+                if (MASK && mask_on) a = mfma(ident, as_bf16x8(mop[kt]), a);
+                acc[t][kt] = mfma(kop, qop[t], a);
+            }
+        }
+        if (more && (PAIR || MASK)) load_bias(k0 + kKB);  // next block's bias rows, overlapping this block's work
+        if (tail)
+            for (int kt = 0; kt < kKT; ++kt)
+                for (int r = 0; r < 4; ++r)
+                    if (k0 + 16 * kt + 4 * g + r >= L)
+                        for (int t = 0; t < kQTiles; ++t) acc[t][kt][r] = -INFINITY;
+
+        // ---- online softmax with a lazily raised maximum ----
+        bf16x8 pmat[kQTiles][2];
+        for (int t = 0; t < kQTiles; ++t) {
+            float mloc = acc[t][0][0];
+            for (int kt = 0; kt < kKT; ++kt)
+                for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, acc[t][kt][r]);
+            if (wave_any(mloc > mthr[t])) {
+                const float mnew = fmaxf(mused[t], max_over_groups(mloc));
+                if (mnew > mused[t]) {
+                    const float alpha = __builtin_amdgcn_exp2f((mused[t] - mnew) * p.c1);  // 0 when mused = -inf
+                    lsum[t] *= alpha;
+                    oacc[t][0] *= alpha;
+                    oacc[t][1] *= alpha;
+                    mused[t] = mnew;
+                    msub[t] = mnew * p.c1;
+                    mthr[t] = mnew + p.lazy_acc;
+                }
+            }
+            float ls = 0.f;
+            for (int kt = 0; kt < kKT; ++kt)
+                for (int r = 0; r < 4; ++r) {
+                    const float e = __builtin_amdgcn_exp2f(fmaf(acc[t][kt][r], p.c1, -msub[t]));
+                    acc[t][kt][r] = e;
+                    ls += e;
+                }
+            lsum[t] += ls;
+            // B operand of O^T = V^T.P^T: element e of 32-key chunk cc is key 32cc + 16(e/4) + 4g + e%4
+            for (int cc = 0; cc < 2; ++cc) {
+                const f32x4 a = acc[t][2 * cc], b = acc[t][2 * cc + 1];
+                pmat[t][cc] = as_bf16x8(uint4{pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(b[0], b[1]), pack2(b[2], b[3])});
+            }
+        }
+
+        // ---- O^T += V^T . P^T ----
+        for (int cc = 0; cc < 2; ++cc)
+            for (int dh = 0; dh < 2; ++dh) {
+                // A[m = d][k]: lane (c + 16g) holds V[key(g, e)][16dh + c]
+                const u16* row = &sm.vt[buf][(16 * dh + c) * kVtStride + 32 * cc + 4 * g];
+                const uint2 lo = *reinterpret_cast<const uint2*>(row);
+                const uint2 hi = *reinterpret_cast<const uint2*>(row + 16);
+                const bf16x8 vop = as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y});
+                for (int t = 0; t < kQTiles; ++t) oacc[t][dh] = mfma(vop, pmat[t][cc], oacc[t][dh]);
+            }
+
+        if (more) stage_store(sm, buf ^ 1, nxt, tid);
+        __syncthreads();
+    }
+
+    // ---- epilogue: normalise, write O (bf16) and LSE (fp32, natural log) ----
+    float lt[kQTiles];
+    bool bad = false;
+    for (int t = 0; t < kQTiles; ++t) {
+        lt[t] = sum_over_groups(lsum[t]);
+        bad |= lt[t] != lt[t];
+    }
+    if (__syncthreads_or(bad)) return false;
+    for (int t = 0; t < kQTiles; ++t) {
+        const int64_t i = s.q0 + 16 * t + c;
+        if (i >= L) continue;
+        const float inv = lt[t] > 0.f ? 1.f / lt[t] : 0.f;
+        for (int dh = 0; dh < 2; ++dh) {
+            // lane (c + 16g) holds O^T[d = 16dh + 4g + r][query c], r = 0..3
+            u16* dst = p.out + s.slice + i * s.HD + 16 * dh + 4 * g;
+            const f32x4 o = oacc[t][dh] * inv;
+            *reinterpret_cast<uint2*>(dst) = uint2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+        }
+        if (p.lse && g == 0)
+            p.lse[((s.b * p.N + s.n) * p.H + s.h) * L + i] =
+                lt[t] > 0.f ? (msub[t] + __log2f(lt[t])) * kLn2 : -INFINITY;
+    }
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// Exact path for biases holding +-inf: biases are widened and added on the
+// vector ALUs in base-2 units (-inf stays -inf), every access is
+// bounds-checked.  Same lane layout as the fast path; V is staged through
+// buffer 0 with two barriers per block.
+// ---------------------------------------------------------------------------
+__device__ void run_exact(const Params& p, const Slice& s, Smem& sm, int tid) {
+    const int64_t L = p.L;
+    const int lane = tid & 63;
+    const int c = lane & 15, g = lane >> 4;
+
+    bf16x8 qop[kQTiles];
+    for (int t = 0; t < kQTiles; ++t) {
+        int64_t i = s.q0 + 16 * t + c;
+        if (i >= L) i = L - 1;
+        qop[t] = as_bf16x8(load16(p.q + s.slice + i * s.HD + 8 * g));
+    }
     f32x4 oacc[kQTiles][2];
     float mrun[kQTiles], lrun[kQTiles];
     for (int t = 0; t < kQTiles; ++t) {
@@ -124,107 +367,123 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_bf16_d32_kernel(Params p) {
         mrun[t] = -INFINITY;
         lrun[t] = 0.f;
     }
+    const float cq = p.c1;  // log2(e)/sqrt(D)
 
     for (int64_t k0 = 0; k0 < L; k0 += kKB) {
-        // ---- stage V[k0 .. k0+63][0..31] transposed into LDS: vt[d][key] ----
-        {
-            const int key = tid / 4, dc = (tid % 4) * 8;
-            const int64_t j = k0 + key;
-            uint4 val = {0u, 0u, 0u, 0u};
-            if (j < L) val = load16(p.v + slice + j * HD + dc);
-            const uint32_t w[4] = {val.x, val.y, val.z, val.w};
-            __syncthreads();  // previous iteration's readers are done
-            for (int e = 0; e < 8; ++e) vt[(dc + e) * kVtStride + key] = (u16)(w[e / 2] >> (16 * (e % 2)));
-        }
+        const StageRegs r = stage_load(p, s, k0, tid);
+        __syncthreads();  // previous block's readers are done
+        stage_store(sm, 0, r, tid);
+        __syncthreads();
 
-        // ---- S^T = K . Q^T for 4 key tiles x kQTiles query tiles ----
-        f32x4 s[kQTiles][kKT];
+        f32x4 acc[kQTiles][kKT];
         for (int kt = 0; kt < kKT; ++kt) {
-            int64_t j = k0 + 16 * kt + c;  // A[m = key][k = d]: lane (c + 16g) holds k[key c][8g..]
-            if (j >= L) j = L - 1;
-            const bf16x8 kop = as_bf16x8(load16(p.k + slice + j * HD + 8 * g));
-            for (int t = 0; t < kQTiles; ++t)
-                s[t][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[t], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.k[0][(16 * kt + c) * kKStride + 8 * g]));
+            for (int t = 0; t < kQTiles; ++t) acc[t][kt] = mfma(kop, qop[t], f32x4{0.f, 0.f, 0.f, 0.f});
         }
-
-        // ---- scale, biases, masking of keys past L (base-2 units) ----
         for (int kt = 0; kt < kKT; ++kt) {
-            const int64_t jb = k0 + 16 * kt + 4 * g;  // this lane's 4 keys: jb .. jb+3
-            float mb[4] = {0.f, 0.f, 0.f, 0.f};
-            if (mrow)
-                for (int r = 0; r < 4; ++r) mb[r] = jb + r < L ? bf2f(mrow[jb + r]) : 0.f;
+            const int64_t jb = k0 + 16 * kt + 4 * g;
             for (int t = 0; t < kQTiles; ++t) {
-                int64_t i = q0 + 16 * t + c;
+                int64_t i = s.q0 + 16 * t + c;
                 if (i >= L) i = L - 1;
-                for (int r = 0; r < 4; ++r) {
-                    const int64_t j = jb + r;
-                    float bias = mb[r];
-                    if (pbase && j < L) bias += bf2f(pbase[i * L + j]);
-                    s[t][kt][r] = j < L ? fmaf(s[t][kt][r], p.c1, bias * kLog2e) : -INFINITY;
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int64_t j = jb + rr;
+                    float bias = 0.f;
+                    if (s.mrow && j < L) bias += bf2f(s.mrow[j]);
+                    if (s.pbase && j < L) bias += bf2f(s.pbase[i * L + j]);
+                    acc[t][kt][rr] = j < L ? fmaf(acc[t][kt][rr], cq, bias * kLog2e) : -INFINITY;
                 }
             }
         }
-
-        // ---- online softmax per query tile ----
-        bf16x8 pop[kQTiles][2];
+        bf16x8 pmat[kQTiles][2];
         for (int t = 0; t < kQTiles; ++t) {
             float mx = -INFINITY;
             for (int kt = 0; kt < kKT; ++kt)
-                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[t][kt][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = fmaxf(mrun[t], mx);
-            const float msub = mnew == -INFINITY ? 0.f : mnew;
-            const float alpha = __builtin_amdgcn_exp2f(mrun[t] - msub);
-            float sum = 0.f;
+                for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, acc[t][kt][rr]);
+            const float mnew = fmaxf(mrun[t], max_over_groups(mx));
+            const float ms = mnew == -INFINITY ? 0.f : mnew;
+            const float alpha = __builtin_amdgcn_exp2f(mrun[t] - ms);
+            float ls = 0.f;
             for (int kt = 0; kt < kKT; ++kt)
-                for (int r = 0; r < 4; ++r) {
-                    const float pv = __builtin_amdgcn_exp2f(s[t][kt][r] - msub);
-                    s[t][kt][r] = pv;
-                    sum += pv;
+                for (int rr = 0; rr < 4; ++rr) {
+                    const float e = __builtin_amdgcn_exp2f(acc[t][kt][rr] - ms);
+                    acc[t][kt][rr] = e;
+                    ls += e;
                 }
-            lrun[t] = lrun[t] * alpha + sum;  // per-lane partial sum over this lane's keys
+            lrun[t] = lrun[t] * alpha + ls;
             mrun[t] = mnew;
-            for (int dh = 0; dh < 2; ++dh) oacc[t][dh] *= alpha;
-            // B operand of O^T = V^T P^T: element e of 32-key chunk cc is key 32cc + 16(e/4) + 4g + e%4
+            oacc[t][0] *= alpha;
+            oacc[t][1] *= alpha;
             for (int cc = 0; cc < 2; ++cc) {
-                const f32x4 a = s[t][2 * cc], b = s[t][2 * cc + 1];
-                pop[t][cc] = as_bf16x8(uint4{pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(b[0], b[1]), pack2(b[2], b[3])});
+                const f32x4 a = acc[t][2 * cc], b = acc[t][2 * cc + 1];
+                pmat[t][cc] = as_bf16x8(uint4{pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(b[0], b[1]), pack2(b[2], b[3])});
             }
         }
-
-        __syncthreads();  // transposed V visible
-
-        // ---- O^T += V^T . P^T ----
         for (int cc = 0; cc < 2; ++cc)
             for (int dh = 0; dh < 2; ++dh) {
-                // A[m = d][k]: lane (c + 16g) holds V[key(g, e)][16dh + c]
-                const u16* row = vt + (16 * dh + c) * kVtStride + 32 * cc + 4 * g;
+                const u16* row = &sm.vt[0][(16 * dh + c) * kVtStride + 32 * cc + 4 * g];
                 const uint2 lo = *reinterpret_cast<const uint2*>(row);
                 const uint2 hi = *reinterpret_cast<const uint2*>(row + 16);
                 const bf16x8 vop = as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y});
-                for (int t = 0; t < kQTiles; ++t)
-                    oacc[t][dh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[t][cc], oacc[t][dh], 0, 0, 0);
+                for (int t = 0; t < kQTiles; ++t) oacc[t][dh] = mfma(vop, pmat[t][cc], oacc[t][dh]);
             }
     }
-
-    // ---- epilogue: normalise, write O (bf16) and LSE (fp32, natural log) ----
     for (int t = 0; t < kQTiles; ++t) {
-        float l = lrun[t];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        const int64_t i = q0 + 16 * t + c;
+        const float l = sum_over_groups(lrun[t]);
+        const int64_t i = s.q0 + 16 * t + c;
         if (i >= L) continue;
         const float inv = l > 0.f ? 1.f / l : 0.f;
         for (int dh = 0; dh < 2; ++dh) {
-            // lane (c + 16g) holds O^T[d = 16dh + 4g + r][query c], r = 0..3
-            u16* dst = p.out + slice + i * HD + 16 * dh + 4 * g;
+            u16* dst = p.out + s.slice + i * s.HD + 16 * dh + 4 * g;
             const f32x4 o = oacc[t][dh] * inv;
             *reinterpret_cast<uint2*>(dst) = uint2{pack2(o[0], o[1]), pack2(o[2], o[3])};
         }
         if (p.lse && g == 0)
-            p.lse[((b * p.N + n) * p.H + h) * L + i] = l > 0.f ? (mrun[t] + __log2f(l)) * kLn2 : -INFINITY;
+            p.lse[((s.b * p.N + s.n) * p.H + s.h) * L + i] = l > 0.f ? (mrun[t] + __log2f(l)) * kLn2 : -INFINITY;
     }
+}
+
+template <bool PAIR, bool MASK, bool ALIGNED>
+__global__ __launch_bounds__(kWaves * 64) void fwd_bf16_d32_kernel(Params p) {
+    __shared__ __attribute__((aligned(16))) Smem sm;
+
+    int64_t id = logical_block(blockIdx.x, p.total);
+    const int64_t qb = id % p.qblocks;
+    id /= p.qblocks;
+    Slice s;
+    s.n = id % p.N;
+    id /= p.N;
+    s.h = id % p.H;
+    s.b = id / p.H;
+    s.HD = p.H * D;
+    s.slice = ((s.b * p.N + s.n) * p.L * p.H + s.h) * D;  // element (b, n, 0, h, 0)
+    const int tid = threadIdx.x;
+    s.q0 = qb * kBlockQ + (tid >> 6) * kWaveQ;
+    s.mrow = p.mask ? p.mask + (s.b * p.N + s.n) * p.L : nullptr;
+    s.pbase = p.pair ? p.pair + (s.b * p.H + s.h) * p.L * p.L : nullptr;
+
+    if (!run_fast<PAIR, MASK, ALIGNED>(p, s, sm, tid)) {
+        __syncthreads();
+        run_exact(p, s, sm, tid);
+    }
+}
+
+template <bool PAIR, bool MASK, bool ALIGNED>
+hipError_t launch_variant(Params& p, hipStream_t stream) {
+    void* args[] = {&p};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_d32_kernel<PAIR, MASK, ALIGNED>),
+                           dim3((unsigned)p.total), dim3(kWaves * 64), args, 0, stream);
+}
+
+template <bool PAIR, bool MASK>
+hipError_t launch_aligned(Params& p, hipStream_t stream) {
+    return p.L % 8 == 0 ? launch_variant<PAIR, MASK, true>(p, stream) : launch_variant<PAIR, MASK, false>(p, stream);
+}
+
+uint16_t bf16_bits_rne(double x) {
+    const float f = (float)x;
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
 }  // namespace
@@ -243,11 +502,21 @@ hipError_t launch_fwd_bf16_d32(const FwdArgs& a, hipStream_t stream) {
     p.H = a.H;
     p.qblocks = (a.L + kBlockQ - 1) / kBlockQ;
     p.total = a.B * a.N * a.H * p.qblocks;
-    p.c1 = (float)(1.4426950408889634 / std::sqrt((double)D));
+    const double sqd = std::sqrt((double)D);
+    p.c1 = (float)(1.4426950408889634 / sqd);
+    p.lazy_acc = (float)(kLazy * sqd / 1.4426950408889634);
+    const uint16_t hi = bf16_bits_rne(sqd);
+    uint32_t hb = (uint32_t)hi << 16;
+    float hf;
+    std::memcpy(&hf, &hb, 4);
+    const uint16_t lo = bf16_bits_rne(sqd - (double)hf);
+    p.sqd = (uint32_t)hi | ((uint32_t)lo << 16);
     if (p.total > 0x7fffffff) return hipErrorInvalidConfiguration;
-    void* args[] = {&p};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_d32_kernel), dim3((unsigned)p.total),
-                           dim3(kWaves * 64), args, 0, stream);
+    const bool pair = p.pair != nullptr, mask = p.mask != nullptr;
+    if (pair && mask) return launch_aligned<true, true>(p, stream);
+    if (pair) return launch_aligned<true, false>(p, stream);
+    if (mask) return launch_aligned<false, true>(p, stream);
+    return launch_aligned<false, false>(p, stream);
 }
 
 }  // namespace evo
