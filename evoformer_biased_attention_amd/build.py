@@ -24,6 +24,9 @@ HIPCC_FLAGS = [
     "-Wall",
     # Keep the compiler from forming packed fp32 instructions (v_pk_*_f32).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in arch VGPRs: the softmax reads every score, and AGPR
+    # results would cost a v_accvgpr_read per value.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

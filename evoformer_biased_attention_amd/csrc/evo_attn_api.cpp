@@ -47,8 +47,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 thread_local int g_last_hip_error = 0;
 
-bool supported(evo_dtype_t dt, int64_t D) {
-    if (dt == EVO_DTYPE_BF16) return D == 32;
+// The bf16 kernel addresses one (b, n, h) slice and one pair matrix with
+// 32-bit byte offsets.
+constexpr int64_t kMaxOffset = int64_t(1) << 31;
+
+bool supported(evo_dtype_t dt, int64_t L, int64_t H, int64_t D) {
+    if (dt == EVO_DTYPE_BF16) return D == 32 && L * H * D * 2 < kMaxOffset && L * L * 2 < kMaxOffset;
     if (dt == EVO_DTYPE_F32) return D == 8 || D == 16 || D == 32 || D == 64;
     return false;
 }
@@ -84,7 +88,7 @@ extern "C" evo_status_t evo_attn_check(const void* q, const void* k, const void*
         if (eo.overlaps(in) || el.overlaps(in)) return EVO_ERR_ALIASING;
     if (eo.overlaps(el)) return EVO_ERR_ALIASING;
 
-    if (!supported(dtype, D)) return EVO_ERR_UNSUPPORTED;
+    if (!supported(dtype, L, H, D)) return EVO_ERR_UNSUPPORTED;
     return EVO_OK;
 }
 

@@ -17,18 +17,26 @@
 //    accumulator before Q.K^T is accumulated on top.  sqrt(D) is split into a
 //    bf16 high part and a bf16 low part (the two halves of the 32-wide
 //    contraction), so the addition is exact to ~2^-16 relative and the biases
-//    are consumed in their stored bf16 form, one 16-byte row load per lane.
-//    Accumulator units are "sqrt(D) * score"; one fma maps them to the base-2
-//    exponent.  A bias of +-inf would turn the identity's zeros into NaN: a
-//    workgroup that sees a NaN row re-runs the slice on an exact VALU path.
+//    are consumed in their stored bf16 form.  Accumulator units are
+//    "sqrt(D) * score"; one fma maps them to the base-2 exponent.  A bias of
+//    +-inf would turn the identity's zeros into NaN: a workgroup that sees a
+//    NaN row re-runs its slice on an exact VALU path.
 //  * Online softmax with a lazy maximum: the running maximum used for the
 //    exponent is only raised (and the output rescaled) when some score
-//    exceeds it by more than 2^8, so the common iteration costs one per-lane
-//    max and no cross-lane traffic; probabilities stay below 2^8.
-//  * K and V blocks of 64 keys are staged in LDS, double buffered, one
-//    barrier per block; V is written transposed (its contraction index, the
-//    key, must be contiguous per lane).  The pair-bias rows for the next block
-//    are loaded while the current block is processed.
+//    exceeds it by more than 2^8, so the common block costs one per-lane max
+//    and no cross-lane traffic; probabilities stay below 2^8.  The row sum is
+//    taken with v_dot2 over the same bf16 probabilities the P.V product uses.
+//  * Per block of 64 keys the workgroup copies K, V, the 128 x 64 pair-bias
+//    tile of its queries and the mask row straight from global memory into
+//    LDS (buffer loads with the LDS destination bit, no register staging),
+//    one block ahead, double buffered, one barrier per block.  Every copy is
+//    a full-line, 1 KB wave request; the LDS layouts are XOR-swizzled through
+//    the choice of source address per lane so that the operand reads hit
+//    distinct banks.  V stays [key][d] in LDS and is read with the
+//    transposing ds_read_b64_tr_b16.
+//  * Buffer resources (SGPR base + byte range) give 32-bit offsets and return
+//    zeros past the range, so rows and keys beyond L need no compares except
+//    the -inf assignment in the last, partial block.
 //
 // Workgroup = 4 wavefronts x 32 queries = 128 queries of one (b, n, h).
 #include <hip/hip_runtime.h>
@@ -36,6 +44,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 
 #include "evo_attn_launch.h"
 
@@ -56,8 +65,6 @@ constexpr int kWaveQ = 16 * kQTiles;      // 32 queries per wavefront
 constexpr int kBlockQ = kWaves * kWaveQ;  // 128 queries per workgroup
 constexpr int kKB = 64;                   // keys per block
 constexpr int kKT = kKB / 16;             // 16-key tiles per block
-constexpr int kKStride = D + 8;           // LDS row of K (one key), bf16 elements
-constexpr int kVtStride = kKB + 8;        // LDS row of transposed V (one d), bf16 elements
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.f;              // log2 headroom before the running max is raised
@@ -78,9 +85,28 @@ struct Params {
     uint32_t sqd;     // bf16 bits: low half = sqrt(D) high part, high half = low part
 };
 
-struct Smem {
-    u16 k[2][kKB * kKStride];
-    u16 vt[2][D * kVtStride];
+// LDS of the fast path, in 16-byte slots.
+//   k, v: slot 4*key + (chunk ^ ((key >> 2) & 3)), chunk = 8 d-values
+//   pt:   slot 8*row + (chunk ^ (row & 7)), row = query of the workgroup, chunk = 8 keys
+//   mt:   slot chunk (8 keys)
+struct FastSmem {
+    uint4 k[2][kKB * 4];
+    uint4 v[2][kKB * 4];
+    uint4 pt[2][kBlockQ * 8];
+    uint4 mt[2][8];
+};
+
+// LDS of the exact path.
+constexpr int kKStride = D + 8;     // row of K (one key), bf16 elements
+constexpr int kVtStride = kKB + 8;  // row of transposed V (one d), bf16 elements
+struct ExactSmem {
+    u16 k[kKB * kKStride];
+    u16 vt[D * kVtStride];
+};
+
+union Smem {
+    FastSmem f;
+    ExactSmem e;
 };
 
 __device__ inline float bf2f(u16 x) { return __builtin_bit_cast(float, (uint32_t)x << 16); }
@@ -96,6 +122,16 @@ __device__ inline uint4 load16(const u16* p) { return *reinterpret_cast<const ui
 
 __device__ inline f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16) of the 8 bytes at p: within each
+// 16-lane group, lane i receives element e of the 4-element row addressed by
+// lane 4e + i/4 of the group, column i % 4.
+__device__ inline uint2 ds_read_tr(const void* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((__attribute__((address_space(3))) char*)p));
+    return __builtin_bit_cast(uint2, r);
 }
 
 __device__ inline bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
@@ -115,20 +151,27 @@ __device__ inline float sum_over_groups(float x) {
     return x + __shfl_xor(x, 32);
 }
 
-// Eight consecutive bf16 of a bias row starting at key j0 (j0 % 8 == 0);
-// keys >= L read as 0.  ALIGNED: L % 8 == 0, so the 8 keys are all in range
-// or all out of range and a 16-byte load is legal.
-template <bool ALIGNED>
-__device__ inline uint4 load_bias8(const u16* row, int64_t j0, int64_t L) {
-    if (ALIGNED) return j0 < L ? load16(row + j0) : uint4{0u, 0u, 0u, 0u};
-    uint32_t w[4];
-    for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = j0 + 2 * e < L ? row[j0 + 2 * e] : 0u;
-        const uint32_t hi = j0 + 2 * e + 1 < L ? row[j0 + 2 * e + 1] : 0u;
-        w[e] = lo | (hi << 16);
-    }
-    return uint4{w[0], w[1], w[2], w[3]};
+// Buffer resources: base address + byte range in SGPRs, 32-bit per-lane
+// offsets.  A load past the range returns zeros.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+__device__ inline Rsrc make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+
+__device__ inline uint4 bload16(Rsrc r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+// 16 bytes per lane from the buffer straight into LDS: lane l's bytes land at
+// lds + 16*l (lds must be the same for the whole wave).
+__device__ inline void dma16(Rsrc r, const void* lds, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff,
+                                             (int)soff, 0, 0);
+}
+
+// Wait for every outstanding memory operation of this wave.
+__device__ inline void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
 // Workgroups are dealt round-robin over the 8 XCDs.  Renumber them so that
 // each XCD receives one contiguous range of the logical order (b, h, n, query
@@ -146,41 +189,24 @@ struct Slice {
     const u16* pbase;  // pair matrix of (b, h) or nullptr
 };
 
-// Stage K and V keys [k0, k0 + 64) of the slice into LDS buffer `buf`
-// (K as [key][d], V transposed as [d][key]); keys >= L are zero.
-struct StageRegs {
-    uint4 kk, vv;
-};
-
-__device__ inline StageRegs stage_load(const Params& p, const Slice& s, int64_t k0, int tid) {
-    const int key = tid >> 2, dc = (tid & 3) * 8;
-    const int64_t j = k0 + key;
-    StageRegs r{{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-    if (j < p.L) {
-        r.kk = load16(p.k + s.slice + j * s.HD + dc);
-        r.vv = load16(p.v + s.slice + j * s.HD + dc);
-    }
-    return r;
-}
-
-__device__ inline void stage_store(Smem& sm, int buf, const StageRegs& r, int tid) {
-    const int key = tid >> 2, dc = (tid & 3) * 8;
-    *reinterpret_cast<uint4*>(&sm.k[buf][key * kKStride + dc]) = r.kk;
-    const uint32_t w[4] = {r.vv.x, r.vv.y, r.vv.z, r.vv.w};
-    u16* col = &sm.vt[buf][dc * kVtStride + key];
-    for (int e = 0; e < 8; ++e) col[e * kVtStride] = (u16)(w[e / 2] >> (16 * (e % 2)));
-}
-
 // ---------------------------------------------------------------------------
 // Fast path.  Returns false (for the whole workgroup) when some row produced
 // a NaN, i.e. a bias held +-inf; nothing has been written in that case.
+// Requires L % 8 == 0, L * H * D * 2 < 2^31 and L * L * 2 < 2^31.
 // ---------------------------------------------------------------------------
-template <bool PAIR, bool MASK, bool ALIGNED>
-__device__ bool run_fast(const Params& p, const Slice& s, Smem& sm, int tid) {
-    const int64_t L = p.L;
-    const int lane = tid & 63;
+template <bool PAIR, bool MASK>
+__device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid) {
+    const int L = (int)p.L;
+    const int wave = tid >> 6, lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
-    const int nblocks = (int)((L + kKB - 1) / kKB);
+    const int nblocks = (L + kKB - 1) / kKB;
+    const uint32_t rowb = (uint32_t)s.HD * 2;  // bytes between consecutive rows of q, k, v
+    const uint32_t span = (uint32_t)(L - 1) * rowb + D * 2;
+    const Rsrc rq = make_rsrc(p.q + s.slice, span);
+    const Rsrc rk = make_rsrc(p.k + s.slice, span);
+    const Rsrc rv = make_rsrc(p.v + s.slice, span);
+    const Rsrc rp = make_rsrc(PAIR ? s.pbase : p.q, PAIR ? (uint32_t)L * (uint32_t)L * 2u : 0u);
+    const Rsrc rm = make_rsrc(MASK ? s.mrow : p.q, MASK ? (uint32_t)L * 2u : 0u);
 
     // Identity A operand: slot (g, e) stands for key 8*(g%2) + e of a 16-key
     // tile, weighted by the high (g < 2) or low (g >= 2) part of sqrt(D).
@@ -197,26 +223,35 @@ __device__ bool run_fast(const Params& p, const Slice& s, Smem& sm, int tid) {
         ident = as_bf16x8(uint4{w[0], w[1], w[2], w[3]});
     }
 
-    // Q operands (B of S^T = K.Q^T): lane (c + 16g) holds q[query c][8g .. 8g+7].
+    // Q operands (B of S^T = K.Q^T): lane (c + 16g) holds q[query c][8g .. 8g+7];
+    // rows past L read as zero.
     bf16x8 qop[kQTiles];
-    int64_t qrow[kQTiles];
     for (int t = 0; t < kQTiles; ++t) {
-        int64_t i = s.q0 + 16 * t + c;
-        if (i >= L) i = L - 1;
-        qrow[t] = i;
-        qop[t] = as_bf16x8(load16(p.q + s.slice + i * s.HD + 8 * g));
+        const uint32_t i = (uint32_t)(s.q0 + 16 * t + c);
+        qop[t] = as_bf16x8(bload16(rq, i * rowb + 16 * g, 0));
     }
 
-    // bias operands of the current block: pair rows (per query tile) and the mask row
-    uint4 pop_[kQTiles][kKT];
-    uint4 mop[kKT];
-    auto load_bias = [&](int64_t k0) {
-        for (int kt = 0; kt < kKT; ++kt) {
-            const int64_t j0 = k0 + 16 * kt + 8 * (g & 1);
-            if (PAIR)
-                for (int t = 0; t < kQTiles; ++t) pop_[t][kt] = load_bias8<ALIGNED>(s.pbase + qrow[t] * L, j0, L);
-            if (MASK) mop[kt] = load_bias8<ALIGNED>(s.mrow, j0, L);
-        }
+    // ---- copy of one block (keys [64 blk, 64 blk + 64)) into LDS buffer `buf` ----
+    // K, V: wave w fills slots 64w .. 64w+63 (keys 16w .. 16w+15); lane l holds
+    //   key 16w + l/4 at slot position l%4, i.e. chunk (l%4) ^ ((key >> 2) & 3).
+    // pair: wave w fills 1 KB segments 4w .. 4w+3; segment I holds query rows
+    //   8I .. 8I+7, lane l row 8I + l/8 at position l%8, chunk (l%8) ^ (row & 7).
+    //   Query rows past L fall outside the pair range and read as zero.
+    // mask: wave 0 lanes 0..7, 8 keys each.
+    const uint32_t qwg = (uint32_t)(s.q0 - wave * kWaveQ);  // first query of the workgroup
+    const uint32_t kvo = (uint32_t)(16 * wave + (lane >> 2)) * rowb + 16u * ((lane & 3) ^ ((lane >> 4) & 3));
+    uint32_t pvo[4];
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t row = 8u * (4 * wave + j) + (lane >> 3);
+        pvo[j] = (qwg + row) * (uint32_t)L * 2u + 16u * ((lane & 7) ^ (lane >> 3));
+    }
+    auto copy_block = [&](int blk, int buf) {
+        const uint32_t k0 = (uint32_t)blk * kKB;
+        dma16(rk, &sm.k[buf][64 * wave], kvo, k0 * rowb);
+        dma16(rv, &sm.v[buf][64 * wave], kvo, k0 * rowb);
+        if (PAIR)
+            for (int j = 0; j < 4; ++j) dma16(rp, &sm.pt[buf][64 * (4 * wave + j)], pvo[j], k0 * 2u);
+        if (MASK && wave == 0 && lane < 8) dma16(rm, &sm.mt[buf][0], 16u * lane, k0 * 2u);
     };
 
     f32x4 oacc[kQTiles][2];
@@ -229,54 +264,61 @@ __device__ bool run_fast(const Params& p, const Slice& s, Smem& sm, int tid) {
         mthr[t] = -INFINITY;
         lsum[t] = 0.f;
     }
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    {
-        const StageRegs r = stage_load(p, s, 0, tid);
-        stage_store(sm, 0, r, tid);
-    }
-    load_bias(0);
+    copy_block(0, 0);
+    wait_all();
     __syncthreads();
 
-    for (int it = 0; it < nblocks; ++it) {
+    // One block of keys; TAIL marks the last block when L % 64 != 0.
+    auto step = [&](int it, auto tail_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
         const int buf = it & 1;
-        const int64_t k0 = (int64_t)it * kKB;
-        const bool tail = k0 + kKB > L;
-        const bool more = it + 1 < nblocks;
-        StageRegs nxt;
-        if (more) nxt = stage_load(p, s, k0 + kKB, tid);
+        const int k0 = it * kKB;
+        if (it + 1 < nblocks) copy_block(it + 1, buf ^ 1);  // lands while this block is processed
 
         // ---- S^T = sqrt(D)*(pair + mask) + K.Q^T, in accumulator units ----
         bool mask_on = false;
         if (MASK) {
-            uint32_t any = 0;
-            for (int kt = 0; kt < kKT; ++kt) any |= mop[kt].x | mop[kt].y | mop[kt].z | mop[kt].w;
-            mask_on = wave_any(any != 0);
+            const uint4 mw = sm.mt[buf][lane & 7];
+            mask_on = wave_any((mw.x | mw.y | mw.z | mw.w) != 0);
         }
         f32x4 acc[kQTiles][kKT];
         for (int kt = 0; kt < kKT; ++kt) {
-            const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.k[buf][(16 * kt + c) * kKStride + 8 * g]));
+            // A[m = key][k = d]: lane (c + 16g) reads key 16kt + c, chunk g
+            const bf16x8 kop = as_bf16x8(sm.k[buf][64 * kt + 4 * c + (g ^ ((c >> 2) & 3))]);
+            bf16x8 mop;
+            if (MASK && mask_on) mop = as_bf16x8(sm.mt[buf][2 * kt + (g & 1)]);
             for (int t = 0; t < kQTiles; ++t) {
                 f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (PAIR) a = mfma(ident, as_bf16x8(pop_[t][kt]), a);
-                if (MASK && mask_on) a = mfma(ident, as_bf16x8(mop[kt]), a);
+                if (PAIR) {
+                    // B[k = slot][n = query]: pair row of query c, keys 16kt + 8(g%2) .. +7
+                    const int row = wave * kWaveQ + 16 * t + c;
+                    a = mfma(ident, as_bf16x8(sm.pt[buf][8 * row + ((2 * kt + (g & 1)) ^ (c & 7))]), a);
+                }
+                if (MASK && mask_on) a = mfma(ident, mop, a);
                 acc[t][kt] = mfma(kop, qop[t], a);
             }
         }
-        if (more && (PAIR || MASK)) load_bias(k0 + kKB);  // next block's bias rows, overlapping this block's work
-        if (tail)
+        if (TAIL)  // keys past L take no weight
             for (int kt = 0; kt < kKT; ++kt)
                 for (int r = 0; r < 4; ++r)
                     if (k0 + 16 * kt + 4 * g + r >= L)
                         for (int t = 0; t < kQTiles; ++t) acc[t][kt][r] = -INFINITY;
 
         // ---- online softmax with a lazily raised maximum ----
-        bf16x8 pmat[kQTiles][2];
+        float mloc[kQTiles];
+        bool raise = false;
         for (int t = 0; t < kQTiles; ++t) {
-            float mloc = acc[t][0][0];
+            float m = acc[t][0][0];
             for (int kt = 0; kt < kKT; ++kt)
-                for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, acc[t][kt][r]);
-            if (wave_any(mloc > mthr[t])) {
-                const float mnew = fmaxf(mused[t], max_over_groups(mloc));
+                for (int r = 0; r < 4; ++r) m = fmaxf(m, acc[t][kt][r]);
+            mloc[t] = m;
+            raise |= m > mthr[t];
+        }
+        if (wave_any(raise)) {
+            for (int t = 0; t < kQTiles; ++t) {
+                const float mnew = fmaxf(mused[t], max_over_groups(mloc[t]));
                 if (mnew > mused[t]) {
                     const float alpha = __builtin_amdgcn_exp2f((mused[t] - mnew) * p.c1);  // 0 when mused = -inf
                     lsum[t] *= alpha;
@@ -287,35 +329,48 @@ __device__ bool run_fast(const Params& p, const Slice& s, Smem& sm, int tid) {
                     mthr[t] = mnew + p.lazy_acc;
                 }
             }
-            float ls = 0.f;
-            for (int kt = 0; kt < kKT; ++kt)
-                for (int r = 0; r < 4; ++r) {
-                    const float e = __builtin_amdgcn_exp2f(fmaf(acc[t][kt][r], p.c1, -msub[t]));
-                    acc[t][kt][r] = e;
-                    ls += e;
-                }
-            lsum[t] += ls;
-            // B operand of O^T = V^T.P^T: element e of 32-key chunk cc is key 32cc + 16(e/4) + 4g + e%4
-            for (int cc = 0; cc < 2; ++cc) {
-                const f32x4 a = acc[t][2 * cc], b = acc[t][2 * cc + 1];
-                pmat[t][cc] = as_bf16x8(uint4{pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(b[0], b[1]), pack2(b[2], b[3])});
+        }
+        bf16x8 pmat[kQTiles][2];
+        for (int t = 0; t < kQTiles; ++t) {
+            uint32_t w[8];
+            for (int kt = 0; kt < kKT; ++kt) {
+                float e[4];
+                for (int r = 0; r < 4; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(acc[t][kt][r], p.c1, -msub[t]));
+                w[2 * kt] = pack2(e[0], e[1]);
+                w[2 * kt + 1] = pack2(e[2], e[3]);
             }
+            // the row sum is taken over the bf16 probabilities the P.V product uses
+            float ls = lsum[t];
+            for (int j = 0; j < 8; ++j) ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[j]), ones, ls, false);
+            lsum[t] = ls;
+            // B operand of O^T = V^T.P^T: element e of 32-key chunk cc is key 32cc + 16(e/4) + 4g + e%4
+            pmat[t][0] = as_bf16x8(uint4{w[0], w[1], w[2], w[3]});
+            pmat[t][1] = as_bf16x8(uint4{w[4], w[5], w[6], w[7]});
         }
 
         // ---- O^T += V^T . P^T ----
+        // A[m = d][k]: lane (c + 16g) needs V[key(g, e)][16dh + c].  Lane r of
+        // group g addresses key 32cc + 4g + r/4, d-values 16dh + 4(r%4) .. +3
+        // (16-byte chunk 2dh + (r%4)/2, half r%2); the transposing read then
+        // hands lane c the column 16dh + c over keys 32cc + 4g + 0..3, and a
+        // second read does keys 32cc + 16 + 4g + 0..3.
         for (int cc = 0; cc < 2; ++cc)
             for (int dh = 0; dh < 2; ++dh) {
-                // A[m = d][k]: lane (c + 16g) holds V[key(g, e)][16dh + c]
-                const u16* row = &sm.vt[buf][(16 * dh + c) * kVtStride + 32 * cc + 4 * g];
-                const uint2 lo = *reinterpret_cast<const uint2*>(row);
-                const uint2 hi = *reinterpret_cast<const uint2*>(row + 16);
+                const int key = 32 * cc + 4 * g + (c >> 2);          // (key >> 2) & 3 == g
+                const int chunk = (2 * dh + ((c & 3) >> 1)) ^ g;
+                const char* base = reinterpret_cast<const char*>(&sm.v[buf][4 * key + chunk]) + 8 * (c & 1);
+                const uint2 lo = ds_read_tr(base);
+                const uint2 hi = ds_read_tr(base + 16 * 4 * 16);      // 16 keys further
                 const bf16x8 vop = as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y});
                 for (int t = 0; t < kQTiles; ++t) oacc[t][dh] = mfma(vop, pmat[t][cc], oacc[t][dh]);
             }
 
-        if (more) stage_store(sm, buf ^ 1, nxt, tid);
+        wait_all();  // the next block's copies have landed
         __syncthreads();
-    }
+    };
+    for (int it = 0; it + 1 < nblocks; ++it) step(it, std::false_type{});
+    if (L % kKB) step(nblocks - 1, std::true_type{});
+    else step(nblocks - 1, std::false_type{});
 
     // ---- epilogue: normalise, write O (bf16) and LSE (fp32, natural log) ----
     float lt[kQTiles];
@@ -343,12 +398,12 @@ __device__ bool run_fast(const Params& p, const Slice& s, Smem& sm, int tid) {
 }
 
 // ---------------------------------------------------------------------------
-// Exact path for biases holding +-inf: biases are widened and added on the
-// vector ALUs in base-2 units (-inf stays -inf), every access is
-// bounds-checked.  Same lane layout as the fast path; V is staged through
-// buffer 0 with two barriers per block.
+// Exact path: biases are widened and added on the vector ALUs in base-2
+// units (-inf stays -inf), every access is bounds-checked, any L works.  Used
+// for biases holding +-inf and for L % 8 != 0.  Same lane layout as the fast
+// path; K and transposed V are staged through LDS with two barriers per block.
 // ---------------------------------------------------------------------------
-__device__ void run_exact(const Params& p, const Slice& s, Smem& sm, int tid) {
+__device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int tid) {
     const int64_t L = p.L;
     const int lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
@@ -368,16 +423,23 @@ __device__ void run_exact(const Params& p, const Slice& s, Smem& sm, int tid) {
         lrun[t] = 0.f;
     }
     const float cq = p.c1;  // log2(e)/sqrt(D)
+    const int skey = tid >> 2, sdc = (tid & 3) * 8;
 
     for (int64_t k0 = 0; k0 < L; k0 += kKB) {
-        const StageRegs r = stage_load(p, s, k0, tid);
+        uint4 kk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+        if (k0 + skey < L) {
+            kk = load16(p.k + s.slice + (k0 + skey) * s.HD + sdc);
+            vv = load16(p.v + s.slice + (k0 + skey) * s.HD + sdc);
+        }
         __syncthreads();  // previous block's readers are done
-        stage_store(sm, 0, r, tid);
+        *reinterpret_cast<uint4*>(&sm.k[skey * kKStride + sdc]) = kk;
+        const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+        for (int e = 0; e < 8; ++e) sm.vt[(sdc + e) * kVtStride + skey] = (u16)(w[e / 2] >> (16 * (e % 2)));
         __syncthreads();
 
         f32x4 acc[kQTiles][kKT];
         for (int kt = 0; kt < kKT; ++kt) {
-            const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.k[0][(16 * kt + c) * kKStride + 8 * g]));
+            const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.k[(16 * kt + c) * kKStride + 8 * g]));
             for (int t = 0; t < kQTiles; ++t) acc[t][kt] = mfma(kop, qop[t], f32x4{0.f, 0.f, 0.f, 0.f});
         }
         for (int kt = 0; kt < kKT; ++kt) {
@@ -420,7 +482,7 @@ __device__ void run_exact(const Params& p, const Slice& s, Smem& sm, int tid) {
         }
         for (int cc = 0; cc < 2; ++cc)
             for (int dh = 0; dh < 2; ++dh) {
-                const u16* row = &sm.vt[0][(16 * dh + c) * kVtStride + 32 * cc + 4 * g];
+                const u16* row = &sm.vt[(16 * dh + c) * kVtStride + 32 * cc + 4 * g];
                 const uint2 lo = *reinterpret_cast<const uint2*>(row);
                 const uint2 hi = *reinterpret_cast<const uint2*>(row + 16);
                 const bf16x8 vop = as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y});
@@ -442,7 +504,9 @@ __device__ void run_exact(const Params& p, const Slice& s, Smem& sm, int tid) {
     }
 }
 
-template <bool PAIR, bool MASK, bool ALIGNED>
+// FAST: the fast path may run (L % 8 == 0); otherwise every workgroup takes
+// the exact path.
+template <bool PAIR, bool MASK, bool FAST>
 __global__ __launch_bounds__(kWaves * 64) void fwd_bf16_d32_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) Smem sm;
 
@@ -461,21 +525,22 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_bf16_d32_kernel(Params p) {
     s.mrow = p.mask ? p.mask + (s.b * p.N + s.n) * p.L : nullptr;
     s.pbase = p.pair ? p.pair + (s.b * p.H + s.h) * p.L * p.L : nullptr;
 
-    if (!run_fast<PAIR, MASK, ALIGNED>(p, s, sm, tid)) {
+    if (FAST) {
+        if (run_fast<PAIR, MASK>(p, s, sm.f, tid)) return;
         __syncthreads();
-        run_exact(p, s, sm, tid);
     }
+    run_exact(p, s, sm.e, tid);
 }
 
-template <bool PAIR, bool MASK, bool ALIGNED>
+template <bool PAIR, bool MASK, bool FAST>
 hipError_t launch_variant(Params& p, hipStream_t stream) {
     void* args[] = {&p};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_d32_kernel<PAIR, MASK, ALIGNED>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_d32_kernel<PAIR, MASK, FAST>),
                            dim3((unsigned)p.total), dim3(kWaves * 64), args, 0, stream);
 }
 
 template <bool PAIR, bool MASK>
-hipError_t launch_aligned(Params& p, hipStream_t stream) {
+hipError_t launch_biases(Params& p, hipStream_t stream) {
     return p.L % 8 == 0 ? launch_variant<PAIR, MASK, true>(p, stream) : launch_variant<PAIR, MASK, false>(p, stream);
 }
 
@@ -513,10 +578,10 @@ hipError_t launch_fwd_bf16_d32(const FwdArgs& a, hipStream_t stream) {
     p.sqd = (uint32_t)hi | ((uint32_t)lo << 16);
     if (p.total > 0x7fffffff) return hipErrorInvalidConfiguration;
     const bool pair = p.pair != nullptr, mask = p.mask != nullptr;
-    if (pair && mask) return launch_aligned<true, true>(p, stream);
-    if (pair) return launch_aligned<true, false>(p, stream);
-    if (mask) return launch_aligned<false, true>(p, stream);
-    return launch_aligned<false, false>(p, stream);
+    if (pair && mask) return launch_biases<true, true>(p, stream);
+    if (pair) return launch_biases<true, false>(p, stream);
+    if (mask) return launch_biases<false, true>(p, stream);
+    return launch_biases<false, false>(p, stream);
 }
 
 }  // namespace evo

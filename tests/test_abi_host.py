@@ -46,9 +46,9 @@ def test_status_strings():
     assert E.evo_status_string(99) == "unknown status"
 
 
-# Fake device addresses, 1 GiB apart and 256-byte aligned; never dereferenced.
+# Fake device addresses, 1 TiB apart and 256-byte aligned; never dereferenced.
 BASE = 0x7F0000000000
-GIB = 1 << 30
+GIB = 1 << 40  # far enough apart for the largest tensors checked here
 
 
 def addrs(n=8):
@@ -121,6 +121,14 @@ def test_inputs_may_alias_each_other():
                                      (E.EVO_DTYPE_F32, 12), (E.EVO_DTYPE_F32, 128)])
 def test_unsupported(dtype, d):
     assert check(shape=(1, 1, 32, 1, d), dtype=dtype) == E.EVO_ERR_UNSUPPORTED
+
+
+def test_bf16_offset_limits():
+    """The bf16 kernel uses 32-bit byte offsets within a slice and a pair matrix."""
+    assert check(shape=(1, 1, 32767, 1, 32)) == E.EVO_OK
+    assert check(shape=(1, 1, 32768, 1, 32)) == E.EVO_ERR_UNSUPPORTED      # L*L*2 = 2^31
+    big = (1, 1, 1 << 14, 1 << 11, 32)  # L*H*D*2 = 2^31
+    assert check(shape=big, mask_bias=None, pair_bias=None) == E.EVO_ERR_UNSUPPORTED
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
