@@ -89,11 +89,14 @@ struct Params {
 //   k, v: slot 4*key + (chunk ^ ((key >> 2) & 3)), chunk = 8 d-values
 //   pt:   slot 8*row + (chunk ^ (row & 7)), row = query of the workgroup, chunk = 8 keys
 //   mt:   slot chunk (8 keys)
+struct FastBuf {
+    uint4 k[kKB * 4];
+    uint4 v[kKB * 4];
+    uint4 pt[kBlockQ * 8];
+    uint4 mt[8];
+};
 struct FastSmem {
-    uint4 k[2][kKB * 4];
-    uint4 v[2][kKB * 4];
-    uint4 pt[2][kBlockQ * 8];
-    uint4 mt[2][8];
+    FastBuf buf[2];
 };
 
 // LDS of the exact path.
@@ -245,13 +248,13 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
         const uint32_t row = 8u * (4 * wave + j) + (lane >> 3);
         pvo[j] = (qwg + row) * (uint32_t)L * 2u + 16u * ((lane & 7) ^ (lane >> 3));
     }
-    auto copy_block = [&](int blk, int buf) {
+    auto copy_block = [&](int blk, FastBuf* __restrict__ dst) {
         const uint32_t k0 = (uint32_t)blk * kKB;
-        dma16(rk, &sm.k[buf][64 * wave], kvo, k0 * rowb);
-        dma16(rv, &sm.v[buf][64 * wave], kvo, k0 * rowb);
+        dma16(rk, &dst->k[64 * wave], kvo, k0 * rowb);
+        dma16(rv, &dst->v[64 * wave], kvo, k0 * rowb);
         if (PAIR)
-            for (int j = 0; j < 4; ++j) dma16(rp, &sm.pt[buf][64 * (4 * wave + j)], pvo[j], k0 * 2u);
-        if (MASK && wave == 0 && lane < 8) dma16(rm, &sm.mt[buf][0], 16u * lane, k0 * 2u);
+            for (int j = 0; j < 4; ++j) dma16(rp, &dst->pt[64 * (4 * wave + j)], pvo[j], k0 * 2u);
+        if (MASK && wave == 0 && lane < 8) dma16(rm, &dst->mt[0], 16u * lane, k0 * 2u);
     };
 
     f32x4 oacc[kQTiles][2];
@@ -266,40 +269,68 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
     }
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    copy_block(0, 0);
+    copy_block(0, &sm.buf[0]);
     wait_all();
     __syncthreads();
 
-    // One block of keys; TAIL marks the last block when L % 64 != 0.
-    auto step = [&](int it, auto tail_tag) {
-        constexpr bool TAIL = decltype(tail_tag)::value;
-        const int buf = it & 1;
-        const int k0 = it * kKB;
-        if (it + 1 < nblocks) copy_block(it + 1, buf ^ 1);  // lands while this block is processed
-
-        // ---- S^T = sqrt(D)*(pair + mask) + K.Q^T, in accumulator units ----
-        bool mask_on = false;
-        if (MASK) {
-            const uint4 mw = sm.mt[buf][lane & 7];
-            mask_on = wave_any((mw.x | mw.y | mw.z | mw.w) != 0);
-        }
-        f32x4 acc[kQTiles][kKT];
+    // S^T = sqrt(D)*(pair + mask) + K.Q^T for the block in `b`, in accumulator
+    // units; MASKON adds the mask (only blocks whose mask has a nonzero entry).
+    auto scores = [&](const FastBuf* __restrict__ b, f32x4 (&acc)[kQTiles][kKT], auto mask_tag) {
+        constexpr bool MASKON = decltype(mask_tag)::value;
         for (int kt = 0; kt < kKT; ++kt) {
             // A[m = key][k = d]: lane (c + 16g) reads key 16kt + c, chunk g
-            const bf16x8 kop = as_bf16x8(sm.k[buf][64 * kt + 4 * c + (g ^ ((c >> 2) & 3))]);
+            const bf16x8 kop = as_bf16x8(b->k[64 * kt + 4 * c + (g ^ ((c >> 2) & 3))]);
             bf16x8 mop;
-            if (MASK && mask_on) mop = as_bf16x8(sm.mt[buf][2 * kt + (g & 1)]);
+            if (MASKON) mop = as_bf16x8(b->mt[2 * kt + (g & 1)]);
             for (int t = 0; t < kQTiles; ++t) {
                 f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
                 if (PAIR) {
                     // B[k = slot][n = query]: pair row of query c, keys 16kt + 8(g%2) .. +7
                     const int row = wave * kWaveQ + 16 * t + c;
-                    a = mfma(ident, as_bf16x8(sm.pt[buf][8 * row + ((2 * kt + (g & 1)) ^ (c & 7))]), a);
+                    a = mfma(ident, as_bf16x8(b->pt[8 * row + ((2 * kt + (g & 1)) ^ (c & 7))]), a);
                 }
-                if (MASK && mask_on) a = mfma(ident, mop, a);
+                if (MASKON) a = mfma(ident, mop, a);
                 acc[t][kt] = mfma(kop, qop[t], a);
             }
         }
+    };
+
+    // One block of keys; TAIL marks the last block when L % 64 != 0.  Every
+    // LDS read of the block (score operands, then the V operands of P.V) is
+    // issued before the next block's copy into the other buffer: the
+    // compiler orders LDS reads after an LDS-destination load behind that
+    // load's completion, which would expose the global latency here.
+    auto step = [&](int it, const FastBuf* __restrict__ cur, FastBuf* __restrict__ nxt, auto tail_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
+        const int k0 = it * kKB;
+
+        f32x4 acc[kQTiles][kKT];
+        bool mask_on = false;
+        if (MASK) {
+            const uint4 mw = cur->mt[lane & 7];
+            mask_on = wave_any((mw.x | mw.y | mw.z | mw.w) != 0);
+        }
+        if (mask_on) scores(cur, acc, std::true_type{});
+        else scores(cur, acc, std::false_type{});
+
+        // V operands of O^T = V^T . P^T.  A[m = d][k]: lane (c + 16g) needs
+        // V[key(g, e)][16dh + c].  Lane r of group g addresses key 32cc + 4g +
+        // r/4, d-values 16dh + 4(r%4) .. +3 (16-byte chunk 2dh + (r%4)/2, half
+        // r%2); the transposing read then hands lane c the column 16dh + c over
+        // keys 32cc + 4g + 0..3, and a second read does keys 32cc + 16 + 4g + 0..3.
+        bf16x8 vop[2][2];
+        for (int cc = 0; cc < 2; ++cc)
+            for (int dh = 0; dh < 2; ++dh) {
+                const int key = 32 * cc + 4 * g + (c >> 2);          // (key >> 2) & 3 == g
+                const int chunk = (2 * dh + ((c & 3) >> 1)) ^ g;
+                const char* base = reinterpret_cast<const char*>(&cur->v[4 * key + chunk]) + 8 * (c & 1);
+                const uint2 lo = ds_read_tr(base);
+                const uint2 hi = ds_read_tr(base + 16 * 4 * 16);      // 16 keys further
+                vop[cc][dh] = as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y});
+            }
+
+        if (it + 1 < nblocks) copy_block(it + 1, nxt);  // lands while this block is processed
+
         if (TAIL)  // keys past L take no weight
             for (int kt = 0; kt < kKT; ++kt)
                 for (int r = 0; r < 4; ++r)
@@ -349,28 +380,19 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
         }
 
         // ---- O^T += V^T . P^T ----
-        // A[m = d][k]: lane (c + 16g) needs V[key(g, e)][16dh + c].  Lane r of
-        // group g addresses key 32cc + 4g + r/4, d-values 16dh + 4(r%4) .. +3
-        // (16-byte chunk 2dh + (r%4)/2, half r%2); the transposing read then
-        // hands lane c the column 16dh + c over keys 32cc + 4g + 0..3, and a
-        // second read does keys 32cc + 16 + 4g + 0..3.
         for (int cc = 0; cc < 2; ++cc)
-            for (int dh = 0; dh < 2; ++dh) {
-                const int key = 32 * cc + 4 * g + (c >> 2);          // (key >> 2) & 3 == g
-                const int chunk = (2 * dh + ((c & 3) >> 1)) ^ g;
-                const char* base = reinterpret_cast<const char*>(&sm.v[buf][4 * key + chunk]) + 8 * (c & 1);
-                const uint2 lo = ds_read_tr(base);
-                const uint2 hi = ds_read_tr(base + 16 * 4 * 16);      // 16 keys further
-                const bf16x8 vop = as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y});
-                for (int t = 0; t < kQTiles; ++t) oacc[t][dh] = mfma(vop, pmat[t][cc], oacc[t][dh]);
-            }
+            for (int dh = 0; dh < 2; ++dh)
+                for (int t = 0; t < kQTiles; ++t) oacc[t][dh] = mfma(vop[cc][dh], pmat[t][cc], oacc[t][dh]);
 
         wait_all();  // the next block's copies have landed
         __syncthreads();
     };
-    for (int it = 0; it + 1 < nblocks; ++it) step(it, std::false_type{});
-    if (L % kKB) step(nblocks - 1, std::true_type{});
-    else step(nblocks - 1, std::false_type{});
+    for (int it = 0; it + 1 < nblocks; ++it) step(it, &sm.buf[it & 1], &sm.buf[(it & 1) ^ 1], std::false_type{});
+    {
+        const int it = nblocks - 1;
+        if (L % kKB) step(it, &sm.buf[it & 1], &sm.buf[(it & 1) ^ 1], std::true_type{});
+        else step(it, &sm.buf[it & 1], &sm.buf[(it & 1) ^ 1], std::false_type{});
+    }
 
     // ---- epilogue: normalise, write O (bf16) and LSE (fp32, natural log) ----
     float lt[kQTiles];
