@@ -6,13 +6,14 @@ slice, every query), default: triangle attention around the starting node,
 B=1, N=L=384, H=4, D=32, bf16, mask on the last 16 keys, pair bias projected
 from a seeded pair tensor.  Throughput counts the dense work 4*B*N*H*L^2*D.
 
-Timing: W untimed warm-up steps, then exactly K timed steps bracketed by
+Timing: about a second of untimed launches (clock spin-up), W untimed
+warm-up steps, then exactly K timed steps bracketed by
 torch.cuda.synchronize(); inputs are resident in device memory before the
 timed region.  In the default "cold" mode each step reads a different one of R
 copies of the inputs (R chosen so the copies exceed the 256 MB Infinity
 Cache), so every step streams its operands from HBM; "warm" reuses one copy.
-Each launch is bracketed by HIP events on the launch stream; their mean is the
-kernel time used for the roofline.  The fp64 CPU oracle is timed on the host
+A pair of HIP events on the launch stream brackets the K launches; their
+elapsed time / K is the kernel time used for the roofline.  The fp64 CPU oracle is timed on the host
 cores for the cpu_baseline field.
 
 Prints one JSON line.
@@ -77,7 +78,22 @@ def main():
     ap.add_argument("--mode", choices=["cold", "warm"], default="cold")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-time budget of the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-warm", action="store_true", help="skip the secondary warm-cache measurement")
+    ap.add_argument("--spinup-seconds", type=float, default=1.0,
+                    help="untimed launches for this long before the warm-up steps, so the timed steps run at "
+                         "steady-state clocks (a fresh process starts them lower)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed steps, run one plain copy kernel (torch.neg, out=) over this many MiB, "
+                         "a known-size reference for the HBM byte counters")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="read two rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE) and write "
+                         "profiles/traffic_<workload>.json; runs on the host only")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        if args.copy_probe_mib <= 0:
+            raise SystemExit("--summarize-traffic needs the --copy-probe-mib value the counter runs used")
+        summarize_traffic(args.workload, args.copy_probe_mib, *args.summarize_traffic)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -129,22 +145,29 @@ def main():
     if st != E.EVO_OK:
         raise E.EvoAttnError(st)
     log(f"bench: {R} input set(s) of {set_bytes / 2**20:.1f} MiB, warmup {args.warmup}, steps {args.steps}")
+    t_spin = time.perf_counter()
+    while time.perf_counter() - t_spin < args.spinup_seconds:
+        for i in range(20):
+            launch(i % R)
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         launch(i % R)
     torch.cuda.synchronize()
 
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    # Timed region: K launches back to back on the launch stream, one pair of
+    # HIP events around them (events between launches would add a marker
+    # packet and a gap before every kernel).  kernel_us = region / K, so it
+    # includes the short dispatch gaps between consecutive kernels.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        events[i][0].record(stream)
         launch(i % R)
-        events[i][1].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in events]
-    kern_us = 1e3 * float(np.mean(kern_ms))
+    kern_us = 1e3 * ev0.elapsed_time(ev1) / args.steps
     flops = w.flops
     value = flops * args.steps / wall / 1e12
     achieved = flops / (kern_us * 1e-6) / 1e12
@@ -152,16 +175,25 @@ def main():
     log(f"bench: {kern_us:.2f} us/launch (events), {wall / args.steps * 1e6:.2f} us/step (wall), "
         f"{achieved:.1f} TFLOP/s = {100 * achieved / peak:.1f}% of peak")
 
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * 2 ** 20 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     # secondary: the same launches reading one input set (operands may sit in the Infinity Cache)
     warm = None
-    if R > 1:
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
-        for i in range(50):
-            ev[i][0].record(stream)
+    if R > 1 and not args.no_warm:
+        nw = 50
+        ev0.record(stream)
+        for i in range(nw):
             launch(0)
-            ev[i][1].record(stream)
+        ev1.record(stream)
         torch.cuda.synchronize()
-        wu = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        wu = 1e3 * ev0.elapsed_time(ev1) / nw
         warm = {"kernel_us": round(wu, 3), "tflops": round(flops / (wu * 1e-6) / 1e12, 2)}
 
     alg_bytes = algorithmic_bytes(w.shape, w.dtype, w.mask is not None, w.pair is not None)
@@ -197,6 +229,76 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def _counter_means(directory, counter, name_part):
+    """Mean per-dispatch value of one counter over the kernels whose name contains name_part."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                    key = (f, r.get("Dispatch_Id", r.get("Correlation_Id")))
+                    vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernels matching {name_part!r} under {directory}")
+    return sum(vals.values()) / len(vals), len(vals)
+
+
+TRAFFIC_COMMANDS = [
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o tri -- python3 bench.py "
+    "--steps 5 --warmup 1 --no-cpu-baseline --no-warm --spinup-seconds 0 --copy-probe-mib 256",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o tri -- python3 bench.py "
+    "--steps 5 --warmup 1 --no-cpu-baseline --no-warm --spinup-seconds 0 --copy-probe-mib 256",
+    "python3 bench.py --summarize-traffic gpurun_out/prof_fetch gpurun_out/prof_write --copy-probe-mib 256",
+]
+
+
+def summarize_traffic(workload, probe_mib, fetch_dir, write_dir):
+    """HBM traffic per launch of the attention kernel from FETCH_SIZE / WRITE_SIZE (KiB per dispatch).
+
+    Each counter is scaled by the factor that maps what it reads for the copy
+    probe (torch.neg over --copy-probe-mib MiB, reading and writing exactly
+    that many bytes) onto the probe's true byte count.
+    """
+    import synthetic as S
+    w = S.workload(workload)
+    kname, probe_name = "fwd_bf16_d32" if w.dtype == "bf16" else "fwd_f32", "neg_kernel"
+    fk, nfk = _counter_means(fetch_dir, "FETCH_SIZE", kname)
+    wk, nwk = _counter_means(write_dir, "WRITE_SIZE", kname)
+    fp, _ = _counter_means(fetch_dir, "FETCH_SIZE", probe_name)
+    wp, _ = _counter_means(write_dir, "WRITE_SIZE", probe_name)
+    probe_bytes = probe_mib * 2 ** 20
+    f_scale = probe_bytes / (fp * 1024)
+    w_scale = probe_bytes / (wp * 1024)
+    fetch_b = fk * 1024 * f_scale
+    write_b = wk * 1024 * w_scale
+    B, N, L, H, D = w.shape
+    out = {
+        "workload": w.name,
+        "commands": TRAFFIC_COMMANDS,
+        "note": "FETCH_SIZE's formula counts a 128-byte read request as 64 bytes on this device; the copy "
+                "probe (all 128-byte requests) reads back half its size, hence fetch_scale ~2",
+        "kernel_name_contains": kname,
+        "kernel_source_sha256": source_hash(w.dtype),
+        "dispatches": {"fetch": nfk, "write": nwk},
+        "fetch_kib_per_dispatch": round(fk, 1),
+        "write_kib_per_dispatch": round(wk, 1),
+        "copy_probe": {"bytes_read": probe_bytes, "bytes_written": probe_bytes,
+                       "fetch_kib": round(fp, 1), "write_kib": round(wp, 1),
+                       "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
+        "hbm_fetch_bytes_per_launch": int(fetch_b),
+        "hbm_write_bytes_per_launch": int(write_b),
+        "hbm_bytes_per_launch": int(fetch_b + write_b),
+        "algorithmic_bytes": algorithmic_bytes(w.shape, w.dtype, w.mask is not None, w.pair is not None),
+    }
+    path = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
 def cpu_baseline(w, gpu_set, budget_s):
     """The fp64 oracle (oracle/evo_ref.c, OpenMP over slices) on the host cores.
 
@@ -211,7 +313,7 @@ def cpu_baseline(w, gpu_set, budget_s):
     log(f"bench: oracle on {threads} host threads")
     passes, t = 0, 0.0
     ref = None
-    while passes == 0 or (t < budget_s and passes < 20):
+    while passes == 0 or (t < budget_s and passes < 200):
         t0 = time.perf_counter()
         ref = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype=w.dtype, nthreads=threads)
         t += time.perf_counter() - t0

@@ -177,9 +177,12 @@ __device__ inline void dma16(Rsrc r, const void* lds, uint32_t voff, uint32_t so
 __device__ inline void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
 // Workgroups are dealt round-robin over the 8 XCDs.  Renumber them so that
-// each XCD receives one contiguous range of the logical order (b, h, n, query
-// block): the query blocks of one (n, h) share K/V, and all sequences n of one
-// head share the pair bias, within a single XCD's L2.
+// each XCD receives one contiguous range of the logical order (b, n, h, query
+// block).  All workgroups of one sequence n then run on one XCD at about the
+// same time: the query blocks of one (n, h) share K/V, and the heads of a key
+// row share its 128-byte lines (one head's 32 bf16 values are half a line), so
+// each line is fetched from memory into that XCD's L2 once.  The H pair-bias
+// matrices of a batch element stay in every XCD's L2.
 __device__ inline int64_t logical_block(int64_t hw, int64_t total) {
     const int64_t xcd = hw % 8, j = hw / 8;
     const int64_t per = total / 8, extra = total % 8;  // the first `extra` XCDs get one more
@@ -536,10 +539,10 @@ __global__ __launch_bounds__(kWaves * 64) void fwd_bf16_d32_kernel(Params p) {
     const int64_t qb = id % p.qblocks;
     id /= p.qblocks;
     Slice s;
-    s.n = id % p.N;
-    id /= p.N;
     s.h = id % p.H;
-    s.b = id / p.H;
+    id /= p.H;
+    s.n = id % p.N;
+    s.b = id / p.N;
     s.HD = p.H * D;
     s.slice = ((s.b * p.N + s.n) * p.L * p.H + s.h) * D;  // element (b, n, 0, h, 0)
     const int tid = threadIdx.x;
