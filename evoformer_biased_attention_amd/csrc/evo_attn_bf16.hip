@@ -69,6 +69,24 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.f;              // log2 headroom before the running max is raised
 
+// x / d for 0 <= x < 2^31 and 1 <= d < 2^31 as a multiply-high and a shift
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994, section 4): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, x / d = (mulhi(x, m) + x) >> l; the sum
+// cannot overflow because mulhi(x, m) <= x < 2^31.
+struct FastDiv {
+    uint32_t d, m, l;
+};
+
+__device__ inline uint32_t fdiv(uint32_t x, FastDiv f) { return (__umulhi(x, f.m) + x) >> f.l; }
+
+FastDiv make_fastdiv(uint32_t d) {
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d) ++l;
+    const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+    return FastDiv{d, (uint32_t)m, l};
+}
+
 struct Params {
     const u16* q;
     const u16* k;
@@ -78,8 +96,9 @@ struct Params {
     u16* out;
     float* lse;       // nullable
     int64_t N, L, H;
-    int64_t qblocks;  // ceil(L / kBlockQ)
-    int64_t total;    // number of workgroups
+    FastDiv qblocks;  // ceil(L / kBlockQ)
+    FastDiv nd, hd;   // N, H
+    int64_t total;    // number of workgroups, below 2^31
     float c1;         // log2(e) / sqrt(D): accumulator units -> base-2 exponent
     float lazy_acc;   // kLazy in accumulator units
     uint32_t sqd;     // bf16 bits: low half = sqrt(D) high part, high half = low part
@@ -530,19 +549,19 @@ __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int ti
 }
 
 // FAST: the fast path may run (L % 8 == 0); otherwise every workgroup takes
-// the exact path.
+// the exact path.  Three workgroups' LDS fit on a CU; the second launch bound
+// keeps the registers within what three waves per SIMD allow (168 VGPRs).
 template <bool PAIR, bool MASK, bool FAST>
-__global__ __launch_bounds__(kWaves * 64) void fwd_bf16_d32_kernel(Params p) {
+__global__ __launch_bounds__(kWaves * 64, 3) void fwd_bf16_d32_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) Smem sm;
 
-    int64_t id = logical_block(blockIdx.x, p.total);
-    const int64_t qb = id % p.qblocks;
-    id /= p.qblocks;
+    const uint32_t id = (uint32_t)logical_block(blockIdx.x, p.total);
+    const uint32_t r1 = fdiv(id, p.qblocks), r2 = fdiv(r1, p.hd), r3 = fdiv(r2, p.nd);
+    const int64_t qb = id - r1 * p.qblocks.d;
     Slice s;
-    s.h = id % p.H;
-    id /= p.H;
-    s.n = id % p.N;
-    s.b = id / p.N;
+    s.h = r1 - r2 * p.hd.d;
+    s.n = r2 - r3 * p.nd.d;
+    s.b = r3;
     s.HD = p.H * D;
     s.slice = ((s.b * p.N + s.n) * p.L * p.H + s.h) * D;  // element (b, n, 0, h, 0)
     const int tid = threadIdx.x;
@@ -590,8 +609,12 @@ hipError_t launch_fwd_bf16_d32(const FwdArgs& a, hipStream_t stream) {
     p.N = a.N;
     p.L = a.L;
     p.H = a.H;
-    p.qblocks = (a.L + kBlockQ - 1) / kBlockQ;
-    p.total = a.B * a.N * a.H * p.qblocks;
+    const int64_t qblocks = (a.L + kBlockQ - 1) / kBlockQ;
+    p.total = a.B * a.N * a.H * qblocks;
+    if (p.total >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
+    p.qblocks = make_fastdiv((uint32_t)qblocks);
+    p.nd = make_fastdiv((uint32_t)a.N);
+    p.hd = make_fastdiv((uint32_t)a.H);
     const double sqd = std::sqrt((double)D);
     p.c1 = (float)(1.4426950408889634 / sqd);
     p.lazy_acc = (float)(kLazy * sqd / 1.4426950408889634);
@@ -601,7 +624,6 @@ hipError_t launch_fwd_bf16_d32(const FwdArgs& a, hipStream_t stream) {
     std::memcpy(&hf, &hb, 4);
     const uint16_t lo = bf16_bits_rne(sqd - (double)hf);
     p.sqd = (uint32_t)hi | ((uint32_t)lo << 16);
-    if (p.total > 0x7fffffff) return hipErrorInvalidConfiguration;
     const bool pair = p.pair != nullptr, mask = p.mask != nullptr;
     if (pair && mask) return launch_biases<true, true>(p, stream);
     if (pair) return launch_biases<true, false>(p, stream);
