@@ -21,11 +21,15 @@
 //    "sqrt(D) * score"; one fma maps them to the base-2 exponent.  A bias of
 //    +-inf would turn the identity's zeros into NaN: a workgroup that sees a
 //    NaN row re-runs its slice on an exact VALU path.
-//  * Online softmax with a lazy maximum: the running maximum used for the
-//    exponent is only raised (and the output rescaled) when some score
-//    exceeds it by more than 2^8, so the common block costs one per-lane max
-//    and no cross-lane traffic; probabilities stay below 2^8.  The row sum is
-//    taken with v_dot2 over the same bf16 probabilities the P.V product uses.
+//  * Online softmax with a lazy maximum.  The item's first block takes its
+//    row maximum before the exponentials; every later block first uses the
+//    running maximum as it stands and checks the block's row sums, which
+//    bound each of their terms: only when a row sum exceeds 2^12 is the
+//    maximum raised (O and l rescaled) and the block redone.  The common
+//    block thus needs neither a max reduction nor cross-lane traffic, and
+//    probabilities stay below 2^12.  The row sums are formed on the matrix
+//    cores (an all-ones A operand against the same bf16 P that the P.V
+//    product uses), so every lane of a query ends with the full row sum.
 //  * Per block of 64 keys the workgroup copies K, V, the 128 x 64 pair-bias
 //    tile of its queries and the mask row straight from global memory into
 //    LDS (buffer loads with the LDS destination bit, no register staging),
@@ -67,7 +71,7 @@ constexpr int kKB = 64;                   // keys per block
 constexpr int kKT = kKB / 16;             // 16-key tiles per block
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazy = 8.f;              // log2 headroom before the running max is raised
+constexpr float kLazyLimit = 4096.f;      // bound of a block's row sum, and so of every probability
 
 // x / d for 0 <= x < 2^31 and 1 <= d < 2^31 as a multiply-high and a shift
 // (Granlund and Montgomery, "Division by invariant integers using
@@ -100,7 +104,6 @@ struct Params {
     FastDiv nd, hd;   // N, H
     int64_t total;    // number of workgroups, below 2^31
     float c1;         // log2(e) / sqrt(D): accumulator units -> base-2 exponent
-    float lazy_acc;   // kLazy in accumulator units
     uint32_t sqd;     // bf16 bits: low half = sqrt(D) high part, high half = low part
 };
 
@@ -222,7 +225,9 @@ struct Slice {
 template <bool PAIR, bool MASK>
 __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid) {
     const int L = (int)p.L;
-    const int wave = tid >> 6, lane = tid & 63;
+    // the wave index is uniform: keep it (and every LDS address derived from
+    // it, such as the copies' destinations) in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
     const int nblocks = (L + kKB - 1) / kKB;
     const uint32_t rowb = (uint32_t)s.HD * 2;  // bytes between consecutive rows of q, k, v
@@ -280,16 +285,15 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
     };
 
     f32x4 oacc[kQTiles][2];
-    float mused[kQTiles], msub[kQTiles], mthr[kQTiles], lsum[kQTiles];
+    float mused[kQTiles], msub[kQTiles], lsum[kQTiles];
     for (int t = 0; t < kQTiles; ++t) {
         oacc[t][0] = f32x4{0.f, 0.f, 0.f, 0.f};
         oacc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         mused[t] = -INFINITY;
         msub[t] = 0.f;
-        mthr[t] = -INFINITY;
         lsum[t] = 0.f;
     }
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    const bf16x8 ones8 = as_bf16x8(uint4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});  // bf16 1.0
 
     copy_block(0, &sm.buf[0]);
     wait_all();
@@ -299,22 +303,30 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
     // units; MASKON adds the mask (only blocks whose mask has a nonzero entry).
     auto scores = [&](const FastBuf* __restrict__ b, f32x4 (&acc)[kQTiles][kKT], auto mask_tag) {
         constexpr bool MASKON = decltype(mask_tag)::value;
+        // every operand first, then the products in three independent waves
+        // of eight, so that no product waits for the one just issued
+        bf16x8 kop[kKT], pop[kQTiles][kKT], mop[kKT];
         for (int kt = 0; kt < kKT; ++kt) {
             // A[m = key][k = d]: lane (c + 16g) reads key 16kt + c, chunk g
-            const bf16x8 kop = as_bf16x8(b->k[64 * kt + 4 * c + (g ^ ((c >> 2) & 3))]);
-            bf16x8 mop;
-            if (MASKON) mop = as_bf16x8(b->mt[2 * kt + (g & 1)]);
-            for (int t = 0; t < kQTiles; ++t) {
-                f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (PAIR) {
+            kop[kt] = as_bf16x8(b->k[64 * kt + 4 * c + (g ^ ((c >> 2) & 3))]);
+            if (PAIR)
+                for (int t = 0; t < kQTiles; ++t) {
                     // B[k = slot][n = query]: pair row of query c, keys 16kt + 8(g%2) .. +7
                     const int row = wave * kWaveQ + 16 * t + c;
-                    a = mfma(ident, as_bf16x8(b->pt[8 * row + ((2 * kt + (g & 1)) ^ (c & 7))]), a);
+                    pop[t][kt] = as_bf16x8(b->pt[8 * row + ((2 * kt + (g & 1)) ^ (c & 7))]);
                 }
-                if (MASKON) a = mfma(ident, mop, a);
-                acc[t][kt] = mfma(kop, qop[t], a);
-            }
+            if (MASKON) mop[kt] = as_bf16x8(b->mt[2 * kt + (g & 1)]);
         }
+        for (int kt = 0; kt < kKT; ++kt)
+            for (int t = 0; t < kQTiles; ++t) acc[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (PAIR)
+            for (int kt = 0; kt < kKT; ++kt)
+                for (int t = 0; t < kQTiles; ++t) acc[t][kt] = mfma(ident, pop[t][kt], acc[t][kt]);
+        if (MASKON)
+            for (int kt = 0; kt < kKT; ++kt)
+                for (int t = 0; t < kQTiles; ++t) acc[t][kt] = mfma(ident, mop[kt], acc[t][kt]);
+        for (int kt = 0; kt < kKT; ++kt)
+            for (int t = 0; t < kQTiles; ++t) acc[t][kt] = mfma(kop[kt], qop[t], acc[t][kt]);
     };
 
     // One block of keys; TAIL marks the last block when L % 64 != 0.  Every
@@ -360,18 +372,38 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
                         for (int t = 0; t < kQTiles; ++t) acc[t][kt][r] = -INFINITY;
 
         // ---- online softmax with a lazily raised maximum ----
-        float mloc[kQTiles];
-        bool raise = false;
-        for (int t = 0; t < kQTiles; ++t) {
-            float m = acc[t][0][0];
-            for (int kt = 0; kt < kKT; ++kt)
-                for (int r = 0; r < 4; ++r) m = fmaxf(m, acc[t][kt][r]);
-            mloc[t] = m;
-            raise |= m > mthr[t];
-        }
-        if (wave_any(raise)) {
+        // The item's first block takes its maximum before the exponentials.
+        // Later blocks use the running maximum as it stands, and the block's
+        // row sum bounds each of its terms: when no row sum exceeds
+        // kLazyLimit, no probability does either and the block is accepted;
+        // else the maximum is raised and the block redone.
+        bf16x8 pmat[kQTiles][2];
+        float bs[kQTiles];
+        auto probs = [&]() {
             for (int t = 0; t < kQTiles; ++t) {
-                const float mnew = fmaxf(mused[t], max_over_groups(mloc[t]));
+                uint32_t w[8];
+                for (int kt = 0; kt < kKT; ++kt) {
+                    float e[4];
+                    for (int r = 0; r < 4; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(acc[t][kt][r], p.c1, -msub[t]));
+                    w[2 * kt] = pack2(e[0], e[1]);
+                    w[2 * kt + 1] = pack2(e[2], e[3]);
+                }
+                // B operand of O^T = V^T.P^T: element e of 32-key chunk cc is key 32cc + 16(e/4) + 4g + e%4
+                pmat[t][0] = as_bf16x8(uint4{w[0], w[1], w[2], w[3]});
+                pmat[t][1] = as_bf16x8(uint4{w[4], w[5], w[6], w[7]});
+                // the block's row sum over the same bf16 probabilities, on the
+                // matrix cores (an all-ones A operand): every lane of query c
+                // receives the sum over all 64 keys
+                const f32x4 sum4 = mfma(ones8, pmat[t][1], mfma(ones8, pmat[t][0], f32x4{0.f, 0.f, 0.f, 0.f}));
+                bs[t] = sum4[0];
+            }
+        };
+        auto raise_max = [&]() {
+            for (int t = 0; t < kQTiles; ++t) {
+                float m = acc[t][0][0];
+                for (int kt = 0; kt < kKT; ++kt)
+                    for (int r = 0; r < 4; ++r) m = fmaxf(m, acc[t][kt][r]);
+                const float mnew = fmaxf(mused[t], max_over_groups(m));
                 if (mnew > mused[t]) {
                     const float alpha = __builtin_amdgcn_exp2f((mused[t] - mnew) * p.c1);  // 0 when mused = -inf
                     lsum[t] *= alpha;
@@ -379,27 +411,22 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
                     oacc[t][1] *= alpha;
                     mused[t] = mnew;
                     msub[t] = mnew * p.c1;
-                    mthr[t] = mnew + p.lazy_acc;
                 }
             }
-        }
-        bf16x8 pmat[kQTiles][2];
-        for (int t = 0; t < kQTiles; ++t) {
-            uint32_t w[8];
-            for (int kt = 0; kt < kKT; ++kt) {
-                float e[4];
-                for (int r = 0; r < 4; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(acc[t][kt][r], p.c1, -msub[t]));
-                w[2 * kt] = pack2(e[0], e[1]);
-                w[2 * kt + 1] = pack2(e[2], e[3]);
+        };
+        if (it == 0) {
+            raise_max();
+            probs();
+        } else {
+            probs();
+            bool over = false;
+            for (int t = 0; t < kQTiles; ++t) over |= !(bs[t] <= kLazyLimit);  // NaN counts as over
+            if (wave_any(over)) {
+                raise_max();
+                probs();
             }
-            // the row sum is taken over the bf16 probabilities the P.V product uses
-            float ls = lsum[t];
-            for (int j = 0; j < 8; ++j) ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[j]), ones, ls, false);
-            lsum[t] = ls;
-            // B operand of O^T = V^T.P^T: element e of 32-key chunk cc is key 32cc + 16(e/4) + 4g + e%4
-            pmat[t][0] = as_bf16x8(uint4{w[0], w[1], w[2], w[3]});
-            pmat[t][1] = as_bf16x8(uint4{w[4], w[5], w[6], w[7]});
         }
+        for (int t = 0; t < kQTiles; ++t) lsum[t] += bs[t];
 
         // ---- O^T += V^T . P^T ----
         for (int cc = 0; cc < 2; ++cc)
@@ -420,7 +447,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
     float lt[kQTiles];
     bool bad = false;
     for (int t = 0; t < kQTiles; ++t) {
-        lt[t] = sum_over_groups(lsum[t]);
+        lt[t] = lsum[t];  // every lane of query c holds the full row sum
         bad |= lt[t] != lt[t];
     }
     if (__syncthreads_or(bad)) return false;
@@ -617,7 +644,6 @@ hipError_t launch_fwd_bf16_d32(const FwdArgs& a, hipStream_t stream) {
     p.hd = make_fastdiv((uint32_t)a.H);
     const double sqd = std::sqrt((double)D);
     p.c1 = (float)(1.4426950408889634 / sqd);
-    p.lazy_acc = (float)(kLazy * sqd / 1.4426950408889634);
     const uint16_t hi = bf16_bits_rne(sqd);
     uint32_t hb = (uint32_t)hi << 16;
     float hf;
