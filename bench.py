@@ -37,6 +37,7 @@ PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 * 2 ** 20
 METRIC = "biased-attention fwd TFLOP/s + % bf16 MFMA peak, triangle attn N=L=384"
 KERNEL_SOURCES = {"bf16": "evoformer_biased_attention_amd/csrc/evo_attn_bf16.hip",
+                  "f16": "evoformer_biased_attention_amd/csrc/evo_attn_bf16.hip",
                   "f32": "evoformer_biased_attention_amd/csrc/evo_attn_f32.hip"}
 
 
@@ -75,6 +76,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=4, help="named workload 1..5 (default 4)")
+    ap.add_argument("--dtype", choices=["bf16", "f16", "f32"], default=None,
+                    help="store the workload's values in this format instead of its own")
     ap.add_argument("--mode", choices=["cold", "warm"], default="cold")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-time budget of the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -113,7 +116,7 @@ def main():
         sys.exit(1)
 
     log(f"bench: generating workload {args.workload}")
-    w = S.workload(args.workload)
+    w = S.workload(args.workload, dtype=args.dtype)
     B, N, L, H, D = w.shape
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
     dcode = E.torch_dtype_code(tdt)
@@ -263,7 +266,8 @@ def summarize_traffic(workload, probe_mib, fetch_dir, write_dir):
     """
     import synthetic as S
     w = S.workload(workload)
-    kname, probe_name = "fwd_bf16_d32" if w.dtype == "bf16" else "fwd_f32", "neg_kernel"
+    kname = {"bf16": "Bf16Fmt", "f16": "F16Fmt", "f32": "fwd_f32"}[w.dtype]  # in the kernel's demangled name
+    probe_name = "neg_kernel"
     fk, nfk = _counter_means(fetch_dir, "FETCH_SIZE", kname)
     wk, nwk = _counter_means(write_dir, "WRITE_SIZE", kname)
     fp, _ = _counter_means(fetch_dir, "FETCH_SIZE", probe_name)

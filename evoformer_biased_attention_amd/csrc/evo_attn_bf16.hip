@@ -56,8 +56,6 @@ namespace evo {
 namespace {
 
 // bf16 data is moved as integers; __bf16 vectors appear only as MFMA operands.
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
@@ -134,20 +132,58 @@ union Smem {
     ExactSmem e;
 };
 
-__device__ inline float bf2f(u16 x) { return __builtin_bit_cast(float, (uint32_t)x << 16); }
+// The two 16-bit element formats: bfloat16 and IEEE binary16.  Data moves
+// as integers; the vector types appear only as MFMA operands and in the
+// float -> 16-bit conversion.
+struct Bf16Fmt {
+    typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+    typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+    static constexpr bool kF16 = false;
+    static constexpr uint32_t kOnes2 = 0x3f803f80u;  // two 1.0
+    __device__ static float widen(u16 x) { return __builtin_bit_cast(float, (uint32_t)x << 16); }
+    __device__ static f32x4 mfma(v8 a, v8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
+};
+struct F16Fmt {
+    typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+    typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+    static constexpr bool kF16 = true;
+    static constexpr uint32_t kOnes2 = 0x3c003c00u;  // two 1.0
+    __device__ static float widen(u16 x) { return (float)__builtin_bit_cast(_Float16, x); }
+    __device__ static f32x4 mfma(v8 a, v8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+};
 
-// Two floats -> two bf16 (round to nearest even) packed in one dword, low half first.
+// Two floats -> two 16-bit values (round to nearest even) packed in one dword, low half first.
+template <class E>
 __device__ inline uint32_t pack2(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, typename E::v2));
 }
 
-__device__ inline bf16x8 as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8, x); }
+template <class E>
+__device__ inline typename E::v8 as_v8(uint4 x) { return __builtin_bit_cast(typename E::v8, x); }
+
+// binary16 cannot hold a large finite negative mask value: such masks come
+// as -inf, which an identity product would turn into NaN (0 * inf).  They
+// enter the product as the most negative finite value instead, whose
+// weight exp2(-65504 * sqrt(D) * c1) is an exact 0 in fp32.  NaN stays NaN.
+__device__ inline uint4 clamp_neg_inf_f16(uint4 x) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 lo = {(_Float16)-65504.0f, (_Float16)-65504.0f};
+    uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    for (int i = 0; i < 4; ++i)
+        w[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_maximum(__builtin_bit_cast(h2, w[i]), lo));
+    return uint4{w[0], w[1], w[2], w[3]};
+}
+
+// Whether some 16-bit value of x is other than -inf in binary16 (0xfc00).
+__device__ inline bool any_not_neg_inf_f16(uint4 x) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    bool any = false;
+    for (int i = 0; i < 4; ++i) any |= (w[i] & 0xffffu) != 0xfc00u || (w[i] >> 16) != 0xfc00u;
+    return any;
+}
 
 __device__ inline uint4 load16(const u16* p) { return *reinterpret_cast<const uint4*>(p); }
 
-__device__ inline f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 
 // Transposing LDS read (ds_read_b64_tr_b16) of the 8 bytes at p: within each
 // 16-lane group, lane i receives element e of the 4-element row addressed by
@@ -222,8 +258,9 @@ struct Slice {
 // a NaN, i.e. a bias held +-inf; nothing has been written in that case.
 // Requires L % 8 == 0, L * H * D * 2 < 2^31 and L * L * 2 < 2^31.
 // ---------------------------------------------------------------------------
-template <bool PAIR, bool MASK>
+template <class E, bool PAIR, bool MASK>
 __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid) {
+    using V8 = typename E::v8;
     const int L = (int)p.L;
     // the wave index is uniform: keep it (and every LDS address derived from
     // it, such as the copies' destinations) in scalar registers
@@ -240,7 +277,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
 
     // Identity A operand: slot (g, e) stands for key 8*(g%2) + e of a 16-key
     // tile, weighted by the high (g < 2) or low (g >= 2) part of sqrt(D).
-    bf16x8 ident;
+    V8 ident;
     {
         const u16 wt = (u16)(g < 2 ? (p.sqd & 0xffffu) : (p.sqd >> 16));
         uint32_t w[4];
@@ -250,15 +287,15 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
             const uint32_t hi = (c == 8 * (g & 1) + e + 1) ? wt : 0u;
             w[e2] = lo | (hi << 16);
         }
-        ident = as_bf16x8(uint4{w[0], w[1], w[2], w[3]});
+        ident = as_v8<E>(uint4{w[0], w[1], w[2], w[3]});
     }
 
     // Q operands (B of S^T = K.Q^T): lane (c + 16g) holds q[query c][8g .. 8g+7];
     // rows past L read as zero.
-    bf16x8 qop[kQTiles];
+    V8 qop[kQTiles];
     for (int t = 0; t < kQTiles; ++t) {
         const uint32_t i = (uint32_t)(s.q0 + 16 * t + c);
-        qop[t] = as_bf16x8(bload16(rq, i * rowb + 16 * g, 0));
+        qop[t] = as_v8<E>(bload16(rq, i * rowb + 16 * g, 0));
     }
 
     // ---- copy of one block (keys [64 blk, 64 blk + 64)) into LDS buffer `buf` ----
@@ -293,7 +330,10 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
         msub[t] = 0.f;
         lsum[t] = 0.f;
     }
-    const bf16x8 ones8 = as_bf16x8(uint4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});  // bf16 1.0
+    const V8 ones8 = as_v8<E>(uint4{E::kOnes2, E::kOnes2, E::kOnes2, E::kOnes2});  // 1.0
+
+    // binary16 with a mask: every key of the sequence masked by -inf so far
+    bool all_neg_inf = E::kF16 && MASK;
 
     copy_block(0, &sm.buf[0]);
     wait_all();
@@ -305,28 +345,32 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
         constexpr bool MASKON = decltype(mask_tag)::value;
         // every operand first, then the products in three independent waves
         // of eight, so that no product waits for the one just issued
-        bf16x8 kop[kKT], pop[kQTiles][kKT], mop[kKT];
+        V8 kop[kKT], pop[kQTiles][kKT], mop[kKT];
         for (int kt = 0; kt < kKT; ++kt) {
             // A[m = key][k = d]: lane (c + 16g) reads key 16kt + c, chunk g
-            kop[kt] = as_bf16x8(b->k[64 * kt + 4 * c + (g ^ ((c >> 2) & 3))]);
+            kop[kt] = as_v8<E>(b->k[64 * kt + 4 * c + (g ^ ((c >> 2) & 3))]);
             if (PAIR)
                 for (int t = 0; t < kQTiles; ++t) {
                     // B[k = slot][n = query]: pair row of query c, keys 16kt + 8(g%2) .. +7
                     const int row = wave * kWaveQ + 16 * t + c;
-                    pop[t][kt] = as_bf16x8(b->pt[8 * row + ((2 * kt + (g & 1)) ^ (c & 7))]);
+                    pop[t][kt] = as_v8<E>(b->pt[8 * row + ((2 * kt + (g & 1)) ^ (c & 7))]);
                 }
-            if (MASKON) mop[kt] = as_bf16x8(b->mt[2 * kt + (g & 1)]);
+            if (MASKON) {
+                uint4 m = b->mt[2 * kt + (g & 1)];
+                if (E::kF16) m = clamp_neg_inf_f16(m);
+                mop[kt] = as_v8<E>(m);
+            }
         }
         for (int kt = 0; kt < kKT; ++kt)
             for (int t = 0; t < kQTiles; ++t) acc[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (PAIR)
             for (int kt = 0; kt < kKT; ++kt)
-                for (int t = 0; t < kQTiles; ++t) acc[t][kt] = mfma(ident, pop[t][kt], acc[t][kt]);
+                for (int t = 0; t < kQTiles; ++t) acc[t][kt] = E::mfma(ident, pop[t][kt], acc[t][kt]);
         if (MASKON)
             for (int kt = 0; kt < kKT; ++kt)
-                for (int t = 0; t < kQTiles; ++t) acc[t][kt] = mfma(ident, mop[kt], acc[t][kt]);
+                for (int t = 0; t < kQTiles; ++t) acc[t][kt] = E::mfma(ident, mop[kt], acc[t][kt]);
         for (int kt = 0; kt < kKT; ++kt)
-            for (int t = 0; t < kQTiles; ++t) acc[t][kt] = mfma(kop[kt], qop[t], acc[t][kt]);
+            for (int t = 0; t < kQTiles; ++t) acc[t][kt] = E::mfma(kop[kt], qop[t], acc[t][kt]);
     };
 
     // One block of keys; TAIL marks the last block when L % 64 != 0.  Every
@@ -343,6 +387,11 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
         if (MASK) {
             const uint4 mw = cur->mt[lane & 7];
             mask_on = wave_any((mw.x | mw.y | mw.z | mw.w) != 0);
+            // binary16: remember whether any key so far escaped a -inf mask
+            // (chunks past L read as zero and do not count)
+            if (E::kF16)
+                all_neg_inf = all_neg_inf && mask_on &&
+                              !wave_any(k0 + 8 * (lane & 7) < L && any_not_neg_inf_f16(mw));
         }
         if (mask_on) scores(cur, acc, std::true_type{});
         else scores(cur, acc, std::false_type{});
@@ -352,7 +401,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
         // r/4, d-values 16dh + 4(r%4) .. +3 (16-byte chunk 2dh + (r%4)/2, half
         // r%2); the transposing read then hands lane c the column 16dh + c over
         // keys 32cc + 4g + 0..3, and a second read does keys 32cc + 16 + 4g + 0..3.
-        bf16x8 vop[2][2];
+        V8 vop[2][2];
         for (int cc = 0; cc < 2; ++cc)
             for (int dh = 0; dh < 2; ++dh) {
                 const int key = 32 * cc + 4 * g + (c >> 2);          // (key >> 2) & 3 == g
@@ -360,7 +409,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
                 const char* base = reinterpret_cast<const char*>(&cur->v[4 * key + chunk]) + 8 * (c & 1);
                 const uint2 lo = ds_read_tr(base);
                 const uint2 hi = ds_read_tr(base + 16 * 4 * 16);      // 16 keys further
-                vop[cc][dh] = as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y});
+                vop[cc][dh] = as_v8<E>(uint4{lo.x, lo.y, hi.x, hi.y});
             }
 
         if (it + 1 < nblocks) copy_block(it + 1, nxt);  // lands while this block is processed
@@ -377,7 +426,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
         // row sum bounds each of its terms: when no row sum exceeds
         // kLazyLimit, no probability does either and the block is accepted;
         // else the maximum is raised and the block redone.
-        bf16x8 pmat[kQTiles][2];
+        V8 pmat[kQTiles][2];
         float bs[kQTiles];
         auto probs = [&]() {
             for (int t = 0; t < kQTiles; ++t) {
@@ -385,16 +434,16 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
                 for (int kt = 0; kt < kKT; ++kt) {
                     float e[4];
                     for (int r = 0; r < 4; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(acc[t][kt][r], p.c1, -msub[t]));
-                    w[2 * kt] = pack2(e[0], e[1]);
-                    w[2 * kt + 1] = pack2(e[2], e[3]);
+                    w[2 * kt] = pack2<E>(e[0], e[1]);
+                    w[2 * kt + 1] = pack2<E>(e[2], e[3]);
                 }
                 // B operand of O^T = V^T.P^T: element e of 32-key chunk cc is key 32cc + 16(e/4) + 4g + e%4
-                pmat[t][0] = as_bf16x8(uint4{w[0], w[1], w[2], w[3]});
-                pmat[t][1] = as_bf16x8(uint4{w[4], w[5], w[6], w[7]});
+                pmat[t][0] = as_v8<E>(uint4{w[0], w[1], w[2], w[3]});
+                pmat[t][1] = as_v8<E>(uint4{w[4], w[5], w[6], w[7]});
                 // the block's row sum over the same bf16 probabilities, on the
                 // matrix cores (an all-ones A operand): every lane of query c
                 // receives the sum over all 64 keys
-                const f32x4 sum4 = mfma(ones8, pmat[t][1], mfma(ones8, pmat[t][0], f32x4{0.f, 0.f, 0.f, 0.f}));
+                const f32x4 sum4 = E::mfma(ones8, pmat[t][1], E::mfma(ones8, pmat[t][0], f32x4{0.f, 0.f, 0.f, 0.f}));
                 bs[t] = sum4[0];
             }
         };
@@ -431,7 +480,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
         // ---- O^T += V^T . P^T ----
         for (int cc = 0; cc < 2; ++cc)
             for (int dh = 0; dh < 2; ++dh)
-                for (int t = 0; t < kQTiles; ++t) oacc[t][dh] = mfma(vop[cc][dh], pmat[t][cc], oacc[t][dh]);
+                for (int t = 0; t < kQTiles; ++t) oacc[t][dh] = E::mfma(vop[cc][dh], pmat[t][cc], oacc[t][dh]);
 
         wait_all();  // the next block's copies have landed
         __syncthreads();
@@ -450,6 +499,9 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
         lt[t] = lsum[t];  // every lane of query c holds the full row sum
         bad |= lt[t] != lt[t];
     }
+    // a sequence whose keys are all masked by -inf: the exact path returns
+    // out = 0 and lse = -inf for it
+    bad |= all_neg_inf;
     if (__syncthreads_or(bad)) return false;
     for (int t = 0; t < kQTiles; ++t) {
         const int64_t i = s.q0 + 16 * t + c;
@@ -459,7 +511,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
             // lane (c + 16g) holds O^T[d = 16dh + 4g + r][query c], r = 0..3
             u16* dst = p.out + s.slice + i * s.HD + 16 * dh + 4 * g;
             const f32x4 o = oacc[t][dh] * inv;
-            *reinterpret_cast<uint2*>(dst) = uint2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+            *reinterpret_cast<uint2*>(dst) = uint2{pack2<E>(o[0], o[1]), pack2<E>(o[2], o[3])};
         }
         if (p.lse && g == 0)
             p.lse[((s.b * p.N + s.n) * p.H + s.h) * L + i] =
@@ -474,16 +526,18 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
 // for biases holding +-inf and for L % 8 != 0.  Same lane layout as the fast
 // path; K and transposed V are staged through LDS with two barriers per block.
 // ---------------------------------------------------------------------------
+template <class E>
 __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int tid) {
+    using V8 = typename E::v8;
     const int64_t L = p.L;
     const int lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
 
-    bf16x8 qop[kQTiles];
+    V8 qop[kQTiles];
     for (int t = 0; t < kQTiles; ++t) {
         int64_t i = s.q0 + 16 * t + c;
         if (i >= L) i = L - 1;
-        qop[t] = as_bf16x8(load16(p.q + s.slice + i * s.HD + 8 * g));
+        qop[t] = as_v8<E>(load16(p.q + s.slice + i * s.HD + 8 * g));
     }
     f32x4 oacc[kQTiles][2];
     float mrun[kQTiles], lrun[kQTiles];
@@ -510,8 +564,8 @@ __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int ti
 
         f32x4 acc[kQTiles][kKT];
         for (int kt = 0; kt < kKT; ++kt) {
-            const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.k[(16 * kt + c) * kKStride + 8 * g]));
-            for (int t = 0; t < kQTiles; ++t) acc[t][kt] = mfma(kop, qop[t], f32x4{0.f, 0.f, 0.f, 0.f});
+            const V8 kop = as_v8<E>(*reinterpret_cast<const uint4*>(&sm.k[(16 * kt + c) * kKStride + 8 * g]));
+            for (int t = 0; t < kQTiles; ++t) acc[t][kt] = E::mfma(kop, qop[t], f32x4{0.f, 0.f, 0.f, 0.f});
         }
         for (int kt = 0; kt < kKT; ++kt) {
             const int64_t jb = k0 + 16 * kt + 4 * g;
@@ -521,13 +575,13 @@ __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int ti
                 for (int rr = 0; rr < 4; ++rr) {
                     const int64_t j = jb + rr;
                     float bias = 0.f;
-                    if (s.mrow && j < L) bias += bf2f(s.mrow[j]);
-                    if (s.pbase && j < L) bias += bf2f(s.pbase[i * L + j]);
+                    if (s.mrow && j < L) bias += E::widen(s.mrow[j]);
+                    if (s.pbase && j < L) bias += E::widen(s.pbase[i * L + j]);
                     acc[t][kt][rr] = j < L ? fmaf(acc[t][kt][rr], cq, bias * kLog2e) : -INFINITY;
                 }
             }
         }
-        bf16x8 pmat[kQTiles][2];
+        V8 pmat[kQTiles][2];
         for (int t = 0; t < kQTiles; ++t) {
             float mx = -INFINITY;
             for (int kt = 0; kt < kKT; ++kt)
@@ -548,7 +602,7 @@ __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int ti
             oacc[t][1] *= alpha;
             for (int cc = 0; cc < 2; ++cc) {
                 const f32x4 a = acc[t][2 * cc], b = acc[t][2 * cc + 1];
-                pmat[t][cc] = as_bf16x8(uint4{pack2(a[0], a[1]), pack2(a[2], a[3]), pack2(b[0], b[1]), pack2(b[2], b[3])});
+                pmat[t][cc] = as_v8<E>(uint4{pack2<E>(a[0], a[1]), pack2<E>(a[2], a[3]), pack2<E>(b[0], b[1]), pack2<E>(b[2], b[3])});
             }
         }
         for (int cc = 0; cc < 2; ++cc)
@@ -556,8 +610,8 @@ __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int ti
                 const u16* row = &sm.vt[(16 * dh + c) * kVtStride + 32 * cc + 4 * g];
                 const uint2 lo = *reinterpret_cast<const uint2*>(row);
                 const uint2 hi = *reinterpret_cast<const uint2*>(row + 16);
-                const bf16x8 vop = as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y});
-                for (int t = 0; t < kQTiles; ++t) oacc[t][dh] = mfma(vop, pmat[t][cc], oacc[t][dh]);
+                const V8 vop = as_v8<E>(uint4{lo.x, lo.y, hi.x, hi.y});
+                for (int t = 0; t < kQTiles; ++t) oacc[t][dh] = E::mfma(vop, pmat[t][cc], oacc[t][dh]);
             }
     }
     for (int t = 0; t < kQTiles; ++t) {
@@ -568,7 +622,7 @@ __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int ti
         for (int dh = 0; dh < 2; ++dh) {
             u16* dst = p.out + s.slice + i * s.HD + 16 * dh + 4 * g;
             const f32x4 o = oacc[t][dh] * inv;
-            *reinterpret_cast<uint2*>(dst) = uint2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+            *reinterpret_cast<uint2*>(dst) = uint2{pack2<E>(o[0], o[1]), pack2<E>(o[2], o[3])};
         }
         if (p.lse && g == 0)
             p.lse[((s.b * p.N + s.n) * p.H + s.h) * L + i] = l > 0.f ? (mrun[t] + __log2f(l)) * kLn2 : -INFINITY;
@@ -578,8 +632,8 @@ __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int ti
 // FAST: the fast path may run (L % 8 == 0); otherwise every workgroup takes
 // the exact path.  Three workgroups' LDS fit on a CU; the second launch bound
 // keeps the registers within what three waves per SIMD allow (168 VGPRs).
-template <bool PAIR, bool MASK, bool FAST>
-__global__ __launch_bounds__(kWaves * 64, 3) void fwd_bf16_d32_kernel(Params p) {
+template <class E, bool PAIR, bool MASK, bool FAST>
+__global__ __launch_bounds__(kWaves * 64, 3) void fwd_d32_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) Smem sm;
 
     const uint32_t id = (uint32_t)logical_block(blockIdx.x, p.total);
@@ -597,34 +651,42 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_bf16_d32_kernel(Params p) 
     s.pbase = p.pair ? p.pair + (s.b * p.H + s.h) * p.L * p.L : nullptr;
 
     if (FAST) {
-        if (run_fast<PAIR, MASK>(p, s, sm.f, tid)) return;
+        if (run_fast<E, PAIR, MASK>(p, s, sm.f, tid)) return;
         __syncthreads();
     }
-    run_exact(p, s, sm.e, tid);
+    run_exact<E>(p, s, sm.e, tid);
 }
 
-template <bool PAIR, bool MASK, bool FAST>
+template <class E, bool PAIR, bool MASK, bool FAST>
 hipError_t launch_variant(Params& p, hipStream_t stream) {
     void* args[] = {&p};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_bf16_d32_kernel<PAIR, MASK, FAST>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_d32_kernel<E, PAIR, MASK, FAST>),
                            dim3((unsigned)p.total), dim3(kWaves * 64), args, 0, stream);
 }
 
-template <bool PAIR, bool MASK>
+template <class E, bool PAIR, bool MASK>
 hipError_t launch_biases(Params& p, hipStream_t stream) {
-    return p.L % 8 == 0 ? launch_variant<PAIR, MASK, true>(p, stream) : launch_variant<PAIR, MASK, false>(p, stream);
+    return p.L % 8 == 0 ? launch_variant<E, PAIR, MASK, true>(p, stream) : launch_variant<E, PAIR, MASK, false>(p, stream);
 }
 
-uint16_t bf16_bits_rne(double x) {
+// x rounded to nearest even in the 16-bit format, as bits
+uint16_t bits16_rne(double x, bool f16) {
+    if (f16) return __builtin_bit_cast(uint16_t, (_Float16)x);
     const float f = (float)x;
     uint32_t u;
     std::memcpy(&u, &f, 4);
     return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-}  // namespace
+double widen16(uint16_t b, bool f16) {
+    if (f16) return (double)__builtin_bit_cast(_Float16, b);
+    const uint32_t u = (uint32_t)b << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return f;
+}
 
-hipError_t launch_fwd_bf16_d32(const FwdArgs& a, hipStream_t stream) {
+hipError_t launch_fwd_16bit_d32(const FwdArgs& a, hipStream_t stream, bool f16) {
     Params p;
     p.q = static_cast<const u16*>(a.q);
     p.k = static_cast<const u16*>(a.k);
@@ -644,17 +706,26 @@ hipError_t launch_fwd_bf16_d32(const FwdArgs& a, hipStream_t stream) {
     p.hd = make_fastdiv((uint32_t)a.H);
     const double sqd = std::sqrt((double)D);
     p.c1 = (float)(1.4426950408889634 / sqd);
-    const uint16_t hi = bf16_bits_rne(sqd);
-    uint32_t hb = (uint32_t)hi << 16;
-    float hf;
-    std::memcpy(&hf, &hb, 4);
-    const uint16_t lo = bf16_bits_rne(sqd - (double)hf);
+    const uint16_t hi = bits16_rne(sqd, f16);
+    const uint16_t lo = bits16_rne(sqd - widen16(hi, f16), f16);
     p.sqd = (uint32_t)hi | ((uint32_t)lo << 16);
     const bool pair = p.pair != nullptr, mask = p.mask != nullptr;
-    if (pair && mask) return launch_biases<true, true>(p, stream);
-    if (pair) return launch_biases<true, false>(p, stream);
-    if (mask) return launch_biases<false, true>(p, stream);
-    return launch_biases<false, false>(p, stream);
+    if (f16) {
+        if (pair && mask) return launch_biases<F16Fmt, true, true>(p, stream);
+        if (pair) return launch_biases<F16Fmt, true, false>(p, stream);
+        if (mask) return launch_biases<F16Fmt, false, true>(p, stream);
+        return launch_biases<F16Fmt, false, false>(p, stream);
+    }
+    if (pair && mask) return launch_biases<Bf16Fmt, true, true>(p, stream);
+    if (pair) return launch_biases<Bf16Fmt, true, false>(p, stream);
+    if (mask) return launch_biases<Bf16Fmt, false, true>(p, stream);
+    return launch_biases<Bf16Fmt, false, false>(p, stream);
 }
+
+}  // namespace
+
+hipError_t launch_fwd_bf16_d32(const FwdArgs& a, hipStream_t stream) { return launch_fwd_16bit_d32(a, stream, false); }
+
+hipError_t launch_fwd_f16_d32(const FwdArgs& a, hipStream_t stream) { return launch_fwd_16bit_d32(a, stream, true); }
 
 }  // namespace evo

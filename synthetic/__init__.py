@@ -158,10 +158,15 @@ def _projected_pair(rz, rw, L, H, transpose):
     return np.ascontiguousarray(proj.astype(np.float32))[None, None]  # [1,1,H,L,L]
 
 
-def workload(c: int) -> Workload:
-    """Inputs of named workload c (1..5)."""
+def workload(c: int, dtype: str | None = None) -> Workload:
+    """Inputs of named workload c (1..5); `dtype` stores the same drawn values
+    in another format ("f32", "bf16", "f16") instead of the workload's own."""
     w = WORKLOADS[c]
     B, N, L, H, D, dt = w["B"], w["N"], w["L"], w["H"], w["D"], w["dtype"]
+    name = w["name"]
+    if dtype is not None and dtype != dt:
+        name = name.replace(dt, dtype) if dt in name else f"{name}_{dtype}"
+        dt = dtype
     ss = np.random.SeedSequence(1000 + c)
     rq, rk, rv, rmask, rz, rw = [np.random.default_rng(s) for s in ss.spawn(6)]
     q = to_storage(_normal(rq, (B, N, L, H, D)), dt)
@@ -194,7 +199,7 @@ def workload(c: int) -> Workload:
         raise ValueError(c)
     mask = None if mf is None else to_storage(mf, dt)
     pair = None if pair is None else to_storage(pair, dt)
-    return Workload(w["name"], dt, (B, N, L, H, D), q, k, v, mask, pair, meta)
+    return Workload(name, dt, (B, N, L, H, D), q, k, v, mask, pair, meta)
 
 
 def sample_rows(shape, count: int, seed: int = 7) -> np.ndarray:

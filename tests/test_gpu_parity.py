@@ -3,9 +3,14 @@
 Tolerances (floating point):
   f32 path:  max |dO| <= 1e-4, max |dLSE| <= 1e-4
   bf16 path: max |dO| <= 2e-2, mean |dO| <= 2e-3, max |dLSE| <= 1e-2
+  f16 path:  max |dO| <= 1e-2, mean |dO| <= 1e-3, max |dLSE| <= 5e-3
 The bf16 budget is dominated by rounding O to bf16 (half an ulp is 2^-9
 relative) and by rounding the probabilities to bf16 before the P.V product;
 scores themselves are exact products of bf16 values accumulated in fp32.
+binary16 carries 3 more mantissa bits than bf16, so the same two roundings
+are 8 times smaller (half an ulp is 2^-12 relative); its bounds are set at
+half those of bf16, which leaves the same headroom for the fp32 accumulation
+and the output range (|O| < 8).
 
 Outputs are poisoned with NaN before every launch, so an element the kernel
 fails to write shows up as a mismatch.
@@ -23,7 +28,8 @@ import synthetic as S
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": dict(max_o=1e-4, mean_o=1e-4, max_lse=1e-4),
-       "bf16": dict(max_o=2e-2, mean_o=2e-3, max_lse=1e-2)}
+       "bf16": dict(max_o=2e-2, mean_o=2e-3, max_lse=1e-2),
+       "f16": dict(max_o=1e-2, mean_o=1e-3, max_lse=5e-3)}
 THREADS = min(16, oracle.default_threads())
 
 
@@ -185,6 +191,58 @@ def test_neg_inf_mask_rows(torch_dev):
     ro, rl = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype="bf16", nthreads=THREADS)
     assert np.all(o[0, 1] == 0) and np.all(np.isneginf(l[0, 1]))
     compare(o, l, ro, rl, "bf16", "neg-inf mask")
+
+
+# ---------------------------------------------------------------------------
+# binary16 (the same MFMA kernel on f16 operands).  A -1e9 mask is -inf in
+# this format.
+# ---------------------------------------------------------------------------
+RAGGED_F16 = [(1, 1, 1, 1, 32), (2, 3, 17, 2, 32), (1, 2, 64, 1, 32), (2, 2, 129, 3, 32), (1, 2, 200, 4, 32),
+              (1, 2, 257, 2, 32)]
+
+
+@pytest.mark.parametrize("shape", RAGGED_F16, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("bias", ["both", "mask", "none"])
+def test_ragged_f16(torch_dev, shape, bias):
+    B, N, L, H, D = shape
+    w = S.random_problem(B, N, L, H, D, dtype="f16", seed=sum(shape) * 11 + len(bias),
+                         mask="tail" if bias in ("both", "mask") else None,
+                         pair="normal" if bias == "both" else None, mask_frac=0.3)
+    say(f"ragged f16 {shape} bias={bias}")
+    parity_full(torch_dev, w)
+
+
+def test_f16_msa_row_shape(torch_dev):
+    """An MSA-row-like problem in f16: per-sequence tail masks (-inf) and a pair bias."""
+    w = S.random_problem(1, 32, 256, 8, 32, dtype="f16", seed=2024, mask="tail", pair="normal", mask_frac=0.1)
+    parity_full(torch_dev, w)
+
+
+def test_f16_ds4sci_unit_test_shapes(torch_dev):
+    """The guide's unit-test shape with D = 32, in fp16, its primary dtype (section 4)."""
+    w = S.random_problem(1, 256, 256, 4, 32, dtype="f16", seed=4051, mask="tail", pair="normal", mask_frac=0.1)
+    parity_full(torch_dev, w)
+
+
+def test_f16_large_biases_and_random_masks(torch_dev):
+    w = S.random_problem(1, 4, 192, 2, 32, dtype="f16", seed=78, mask="random", pair="normal", mask_frac=0.5,
+                         bias_scale=8.0)
+    parity_full(torch_dev, w)
+
+
+@pytest.mark.parametrize("L", [96, 128])
+def test_f16_fully_masked_sequences(torch_dev, L):
+    """A sequence whose keys are all -inf returns out = 0 and lse = -inf; L = 96 ends in a partial key block."""
+    B, N, H, D = 1, 3, 2, 32
+    w = S.random_problem(B, N, L, H, D, dtype="f16", seed=9 + L, mask="zero", pair="normal")
+    mf = np.zeros((B, N, 1, 1, L), np.float32)
+    mf[0, 0, ..., 10:50] = -1e9
+    mf[0, 1] = -1e9
+    w.mask = S.to_storage(mf, "f16")
+    o, l = run_gpu(torch_dev, w)
+    ro, rl = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype="f16", nthreads=THREADS)
+    assert np.all(o[0, 1] == 0) and np.all(np.isneginf(l[0, 1]))
+    compare(o, l, ro, rl, "f16", f"f16 fully masked L={L}")
 
 
 def test_non_default_stream(torch_dev):
