@@ -52,7 +52,8 @@ thread_local int g_last_hip_error = 0;
 constexpr int64_t kMaxOffset = int64_t(1) << 31;
 
 bool supported(evo_dtype_t dt, int64_t L, int64_t H, int64_t D) {
-    if (dt == EVO_DTYPE_BF16 || dt == EVO_DTYPE_F16) return D == 32 && L * H * D * 2 < kMaxOffset && L * L * 2 < kMaxOffset;
+    if (dt == EVO_DTYPE_BF16 || dt == EVO_DTYPE_F16)
+        return (D == 8 || D == 16 || D == 32) && L * H * D * 2 < kMaxOffset && L * L * 2 < kMaxOffset;
     if (dt == EVO_DTYPE_F32) return D == 8 || D == 16 || D == 32 || D == 64;
     return false;
 }
@@ -99,8 +100,8 @@ extern "C" evo_status_t evo_attn_fwd(const void* q, const void* k, const void* v
     if (st != EVO_OK) return st;
     evo::FwdArgs a{q, k, v, mask_bias, pair_bias, out, lse, shape->B, shape->N, shape->L, shape->H, shape->D};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t err = dtype == EVO_DTYPE_BF16  ? evo::launch_fwd_bf16_d32(a, s)
-                     : dtype == EVO_DTYPE_F16 ? evo::launch_fwd_f16_d32(a, s)
+    hipError_t err = dtype == EVO_DTYPE_BF16  ? evo::launch_fwd_bf16(a, s)
+                     : dtype == EVO_DTYPE_F16 ? evo::launch_fwd_f16(a, s)
                                               : evo::launch_fwd_f32(a, s);
     if (err == hipSuccess) return EVO_OK;
     g_last_hip_error = static_cast<int>(err);

@@ -60,7 +60,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
 
-constexpr int D = 32;
+constexpr int kMaxD = 32;                 // head dimensions 8, 16 and 32 share the 32-wide layouts
+constexpr uint32_t kOOB = 0x80000000u;    // a buffer offset past every range: the load returns zeros
 constexpr int kWaves = 4;
 constexpr int kQTiles = 2;                // 16-query MFMA tiles per wavefront
 constexpr int kWaveQ = 16 * kQTiles;      // 32 queries per wavefront
@@ -120,11 +121,11 @@ struct FastSmem {
 };
 
 // LDS of the exact path.
-constexpr int kKStride = D + 8;     // row of K (one key), bf16 elements
+constexpr int kKStride = kMaxD + 8;  // row of K (one key), 16-bit elements
 constexpr int kVtStride = kKB + 8;  // row of transposed V (one d), bf16 elements
 struct ExactSmem {
     u16 k[kKB * kKStride];
-    u16 vt[D * kVtStride];
+    u16 vt[kMaxD * kVtStride];
 };
 
 union Smem {
@@ -258,9 +259,14 @@ struct Slice {
 // a NaN, i.e. a bias held +-inf; nothing has been written in that case.
 // Requires L % 8 == 0, L * H * D * 2 < 2^31 and L * L * 2 < 2^31.
 // ---------------------------------------------------------------------------
-template <class E, bool PAIR, bool MASK>
+template <class E, int D, bool PAIR, bool MASK>
 __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid) {
     using V8 = typename E::v8;
+    // D < 32: the 16-byte chunks of a row past D read as zero (an offset
+    // beyond the buffer range), which pads Q and K with zero dimensions and V
+    // with zero columns; the d-half of P.V past D is skipped.
+    constexpr int kDC = D / 8;               // 16-byte chunks per row
+    constexpr int kDHT = (D + 15) / 16;      // 16-wide d tiles of the output
     const int L = (int)p.L;
     // the wave index is uniform: keep it (and every LDS address derived from
     // it, such as the copies' destinations) in scalar registers
@@ -268,7 +274,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
     const int c = lane & 15, g = lane >> 4;
     const int nblocks = (L + kKB - 1) / kKB;
     const uint32_t rowb = (uint32_t)s.HD * 2;  // bytes between consecutive rows of q, k, v
-    const uint32_t span = (uint32_t)(L - 1) * rowb + D * 2;
+    const uint32_t span = (uint32_t)(L - 1) * rowb + D * 2;  // below kOOB: the API bounds L * H * D * 2 by 2^31
     const Rsrc rq = make_rsrc(p.q + s.slice, span);
     const Rsrc rk = make_rsrc(p.k + s.slice, span);
     const Rsrc rv = make_rsrc(p.v + s.slice, span);
@@ -295,7 +301,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
     V8 qop[kQTiles];
     for (int t = 0; t < kQTiles; ++t) {
         const uint32_t i = (uint32_t)(s.q0 + 16 * t + c);
-        qop[t] = as_v8<E>(bload16(rq, i * rowb + 16 * g, 0));
+        qop[t] = as_v8<E>(bload16(rq, g < kDC ? i * rowb + 16 * g : kOOB, 0));
     }
 
     // ---- copy of one block (keys [64 blk, 64 blk + 64)) into LDS buffer `buf` ----
@@ -306,7 +312,8 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
     //   Query rows past L fall outside the pair range and read as zero.
     // mask: wave 0 lanes 0..7, 8 keys each.
     const uint32_t qwg = (uint32_t)(s.q0 - wave * kWaveQ);  // first query of the workgroup
-    const uint32_t kvo = (uint32_t)(16 * wave + (lane >> 2)) * rowb + 16u * ((lane & 3) ^ ((lane >> 4) & 3));
+    const uint32_t kvchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+    const uint32_t kvo = kvchunk < kDC ? (uint32_t)(16 * wave + (lane >> 2)) * rowb + 16u * kvchunk : kOOB;
     uint32_t pvo[4];
     for (int j = 0; j < 4; ++j) {
         const uint32_t row = 8u * (4 * wave + j) + (lane >> 3);
@@ -403,7 +410,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
         // keys 32cc + 4g + 0..3, and a second read does keys 32cc + 16 + 4g + 0..3.
         V8 vop[2][2];
         for (int cc = 0; cc < 2; ++cc)
-            for (int dh = 0; dh < 2; ++dh) {
+            for (int dh = 0; dh < kDHT; ++dh) {
                 const int key = 32 * cc + 4 * g + (c >> 2);          // (key >> 2) & 3 == g
                 const int chunk = (2 * dh + ((c & 3) >> 1)) ^ g;
                 const char* base = reinterpret_cast<const char*>(&cur->v[4 * key + chunk]) + 8 * (c & 1);
@@ -479,7 +486,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
 
         // ---- O^T += V^T . P^T ----
         for (int cc = 0; cc < 2; ++cc)
-            for (int dh = 0; dh < 2; ++dh)
+            for (int dh = 0; dh < kDHT; ++dh)
                 for (int t = 0; t < kQTiles; ++t) oacc[t][dh] = E::mfma(vop[cc][dh], pmat[t][cc], oacc[t][dh]);
 
         wait_all();  // the next block's copies have landed
@@ -507,8 +514,9 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
         const int64_t i = s.q0 + 16 * t + c;
         if (i >= L) continue;
         const float inv = lt[t] > 0.f ? 1.f / lt[t] : 0.f;
-        for (int dh = 0; dh < 2; ++dh) {
+        for (int dh = 0; dh < kDHT; ++dh) {
             // lane (c + 16g) holds O^T[d = 16dh + 4g + r][query c], r = 0..3
+            if (16 * dh + 4 * g >= D) continue;
             u16* dst = p.out + s.slice + i * s.HD + 16 * dh + 4 * g;
             const f32x4 o = oacc[t][dh] * inv;
             *reinterpret_cast<uint2*>(dst) = uint2{pack2<E>(o[0], o[1]), pack2<E>(o[2], o[3])};
@@ -526,9 +534,10 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
 // for biases holding +-inf and for L % 8 != 0.  Same lane layout as the fast
 // path; K and transposed V are staged through LDS with two barriers per block.
 // ---------------------------------------------------------------------------
-template <class E>
+template <class E, int D>
 __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int tid) {
     using V8 = typename E::v8;
+    constexpr int kDHT = (D + 15) / 16;  // 16-wide d tiles of the output; dimensions past D are zero
     const int64_t L = p.L;
     const int lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
@@ -537,7 +546,7 @@ __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int ti
     for (int t = 0; t < kQTiles; ++t) {
         int64_t i = s.q0 + 16 * t + c;
         if (i >= L) i = L - 1;
-        qop[t] = as_v8<E>(load16(p.q + s.slice + i * s.HD + 8 * g));
+        qop[t] = as_v8<E>(8 * g < D ? load16(p.q + s.slice + i * s.HD + 8 * g) : uint4{0u, 0u, 0u, 0u});
     }
     f32x4 oacc[kQTiles][2];
     float mrun[kQTiles], lrun[kQTiles];
@@ -552,7 +561,7 @@ __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int ti
 
     for (int64_t k0 = 0; k0 < L; k0 += kKB) {
         uint4 kk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-        if (k0 + skey < L) {
+        if (k0 + skey < L && sdc < D) {
             kk = load16(p.k + s.slice + (k0 + skey) * s.HD + sdc);
             vv = load16(p.v + s.slice + (k0 + skey) * s.HD + sdc);
         }
@@ -606,7 +615,7 @@ __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int ti
             }
         }
         for (int cc = 0; cc < 2; ++cc)
-            for (int dh = 0; dh < 2; ++dh) {
+            for (int dh = 0; dh < kDHT; ++dh) {
                 const u16* row = &sm.vt[(16 * dh + c) * kVtStride + 32 * cc + 4 * g];
                 const uint2 lo = *reinterpret_cast<const uint2*>(row);
                 const uint2 hi = *reinterpret_cast<const uint2*>(row + 16);
@@ -619,7 +628,8 @@ __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int ti
         const int64_t i = s.q0 + 16 * t + c;
         if (i >= L) continue;
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        for (int dh = 0; dh < 2; ++dh) {
+        for (int dh = 0; dh < kDHT; ++dh) {
+            if (16 * dh + 4 * g >= D) continue;
             u16* dst = p.out + s.slice + i * s.HD + 16 * dh + 4 * g;
             const f32x4 o = oacc[t][dh] * inv;
             *reinterpret_cast<uint2*>(dst) = uint2{pack2<E>(o[0], o[1]), pack2<E>(o[2], o[3])};
@@ -632,8 +642,8 @@ __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int ti
 // FAST: the fast path may run (L % 8 == 0); otherwise every workgroup takes
 // the exact path.  Three workgroups' LDS fit on a CU; the second launch bound
 // keeps the registers within what three waves per SIMD allow (168 VGPRs).
-template <class E, bool PAIR, bool MASK, bool FAST>
-__global__ __launch_bounds__(kWaves * 64, 3) void fwd_d32_kernel(Params p) {
+template <class E, int D, bool PAIR, bool MASK, bool FAST>
+__global__ __launch_bounds__(kWaves * 64, 3) void fwd_16bit_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) Smem sm;
 
     const uint32_t id = (uint32_t)logical_block(blockIdx.x, p.total);
@@ -651,22 +661,39 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_d32_kernel(Params p) {
     s.pbase = p.pair ? p.pair + (s.b * p.H + s.h) * p.L * p.L : nullptr;
 
     if (FAST) {
-        if (run_fast<E, PAIR, MASK>(p, s, sm.f, tid)) return;
+        if (run_fast<E, D, PAIR, MASK>(p, s, sm.f, tid)) return;
         __syncthreads();
     }
-    run_exact<E>(p, s, sm.e, tid);
+    run_exact<E, D>(p, s, sm.e, tid);
 }
 
-template <class E, bool PAIR, bool MASK, bool FAST>
+template <class E, int D, bool PAIR, bool MASK, bool FAST>
 hipError_t launch_variant(Params& p, hipStream_t stream) {
     void* args[] = {&p};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_d32_kernel<E, PAIR, MASK, FAST>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_16bit_kernel<E, D, PAIR, MASK, FAST>),
                            dim3((unsigned)p.total), dim3(kWaves * 64), args, 0, stream);
 }
 
-template <class E, bool PAIR, bool MASK>
+template <class E, int D, bool PAIR, bool MASK>
 hipError_t launch_biases(Params& p, hipStream_t stream) {
-    return p.L % 8 == 0 ? launch_variant<E, PAIR, MASK, true>(p, stream) : launch_variant<E, PAIR, MASK, false>(p, stream);
+    return p.L % 8 == 0 ? launch_variant<E, D, PAIR, MASK, true>(p, stream)
+                        : launch_variant<E, D, PAIR, MASK, false>(p, stream);
+}
+
+template <class E, int D>
+hipError_t launch_dim(Params& p, hipStream_t stream) {
+    const bool pair = p.pair != nullptr, mask = p.mask != nullptr;
+    if (pair && mask) return launch_biases<E, D, true, true>(p, stream);
+    if (pair) return launch_biases<E, D, true, false>(p, stream);
+    if (mask) return launch_biases<E, D, false, true>(p, stream);
+    return launch_biases<E, D, false, false>(p, stream);
+}
+
+template <class E>
+hipError_t launch_format(Params& p, int64_t d, hipStream_t stream) {
+    if (d == 8) return launch_dim<E, 8>(p, stream);
+    if (d == 16) return launch_dim<E, 16>(p, stream);
+    return launch_dim<E, 32>(p, stream);
 }
 
 // x rounded to nearest even in the 16-bit format, as bits
@@ -686,7 +713,7 @@ double widen16(uint16_t b, bool f16) {
     return f;
 }
 
-hipError_t launch_fwd_16bit_d32(const FwdArgs& a, hipStream_t stream, bool f16) {
+hipError_t launch_fwd_16bit(const FwdArgs& a, hipStream_t stream, bool f16) {
     Params p;
     p.q = static_cast<const u16*>(a.q);
     p.k = static_cast<const u16*>(a.k);
@@ -704,28 +731,19 @@ hipError_t launch_fwd_16bit_d32(const FwdArgs& a, hipStream_t stream, bool f16) 
     p.qblocks = make_fastdiv((uint32_t)qblocks);
     p.nd = make_fastdiv((uint32_t)a.N);
     p.hd = make_fastdiv((uint32_t)a.H);
-    const double sqd = std::sqrt((double)D);
+    if (a.D != 8 && a.D != 16 && a.D != 32) return hipErrorInvalidValue;
+    const double sqd = std::sqrt((double)a.D);
     p.c1 = (float)(1.4426950408889634 / sqd);
     const uint16_t hi = bits16_rne(sqd, f16);
     const uint16_t lo = bits16_rne(sqd - widen16(hi, f16), f16);
     p.sqd = (uint32_t)hi | ((uint32_t)lo << 16);
-    const bool pair = p.pair != nullptr, mask = p.mask != nullptr;
-    if (f16) {
-        if (pair && mask) return launch_biases<F16Fmt, true, true>(p, stream);
-        if (pair) return launch_biases<F16Fmt, true, false>(p, stream);
-        if (mask) return launch_biases<F16Fmt, false, true>(p, stream);
-        return launch_biases<F16Fmt, false, false>(p, stream);
-    }
-    if (pair && mask) return launch_biases<Bf16Fmt, true, true>(p, stream);
-    if (pair) return launch_biases<Bf16Fmt, true, false>(p, stream);
-    if (mask) return launch_biases<Bf16Fmt, false, true>(p, stream);
-    return launch_biases<Bf16Fmt, false, false>(p, stream);
+    return f16 ? launch_format<F16Fmt>(p, a.D, stream) : launch_format<Bf16Fmt>(p, a.D, stream);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16_d32(const FwdArgs& a, hipStream_t stream) { return launch_fwd_16bit_d32(a, stream, false); }
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) { return launch_fwd_16bit(a, stream, false); }
 
-hipError_t launch_fwd_f16_d32(const FwdArgs& a, hipStream_t stream) { return launch_fwd_16bit_d32(a, stream, true); }
+hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t stream) { return launch_fwd_16bit(a, stream, true); }
 
 }  // namespace evo

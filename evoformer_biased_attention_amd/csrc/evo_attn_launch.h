@@ -18,11 +18,11 @@ struct FwdArgs {
     int64_t B, N, L, H, D;
 };
 
-// bf16 inputs, D = 32: MFMA kernel.  Returns the hipError_t of the launch.
-hipError_t launch_fwd_bf16_d32(const FwdArgs& a, hipStream_t stream);
+// bf16 inputs, D in {8, 16, 32}: MFMA kernel.  Returns the hipError_t of the launch.
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 
-// f16 inputs, D = 32: the same MFMA kernel on binary16 operands.
-hipError_t launch_fwd_f16_d32(const FwdArgs& a, hipStream_t stream);
+// f16 inputs, D in {8, 16, 32}: the same MFMA kernel on binary16 operands.
+hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t stream);
 
 // f32 inputs, D in {8, 16, 32, 64}: vector-ALU kernel.
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);

@@ -83,10 +83,10 @@ typedef enum {
  *   pair_bias   [B,1,H,L,L] or NULL (no pair bias: all zero)
  *   out         output, [B,N,L,H,D], same dtype as q
  *   lse         output, [B,N,H,L] float32, or NULL to skip it
- * Supported today: dtype BF16 or F16 with D = 32 (MFMA path; also needs
- * L * H * D * 2 < 2^31 and L * L * 2 < 2^31, i.e. L <= 32767) and dtype F32
- * with D in {8, 16, 32, 64}; any B, N, H >= 1 and any L >= 1.  Other valid
- * combinations return EVO_ERR_UNSUPPORTED.
+ * Supported today: dtype BF16 or F16 with D in {8, 16, 32} (MFMA path; also
+ * needs L * H * D * 2 < 2^31 and L * L * 2 < 2^31, i.e. L <= 32767) and
+ * dtype F32 with D in {8, 16, 32, 64}; any B, N, H >= 1 and any L >= 1.
+ * Other valid combinations return EVO_ERR_UNSUPPORTED.
  * A query row whose every score is -inf gets out = 0 and lse = -inf.  In
  * F16 a large negative mask value such as -1e9 is -inf, which is how such
  * masks arrive in that format; a -inf bias gives its key exactly zero weight.

@@ -245,6 +245,36 @@ def test_f16_fully_masked_sequences(torch_dev, L):
     compare(o, l, ro, rl, "f16", f"f16 fully masked L={L}")
 
 
+# ---------------------------------------------------------------------------
+# Head dimensions 8 and 16 on the 16-bit path (zero-padded to the 32-wide
+# contraction inside the kernel).
+# ---------------------------------------------------------------------------
+SMALL_D = [(1, 2, 17, 3), (2, 2, 64, 2), (1, 3, 100, 4), (1, 2, 257, 2), (1, 1, 1, 1)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [8, 16])
+@pytest.mark.parametrize("shape", SMALL_D, ids=lambda s: "x".join(map(str, s)))
+def test_small_head_dims(torch_dev, shape, d, dtype):
+    B, N, L, H = shape
+    w = S.random_problem(B, N, L, H, d, dtype=dtype, seed=B * 1000 + N * 100 + L + H + d, mask="tail",
+                         pair="normal", mask_frac=0.3)
+    say(f"small head dim {dtype} {shape} D={d}")
+    parity_full(torch_dev, w)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_ds4sci_unit_test_shape_d8(torch_dev, dtype):
+    """The guide's second unit-test shape (1,512,256,8,8) (section 4)."""
+    import json
+    with open(os.path.join(os.path.dirname(__file__), "golden", "ds4sci_guide_facts.json")) as f:
+        facts = json.load(f)
+    shape = tuple(facts["unit_test"]["shapes_B_N_L_H_D"][1])
+    assert shape == (1, 512, 256, 8, 8)
+    w = S.random_problem(*shape, dtype=dtype, seed=4052, mask="tail", pair="normal", mask_frac=0.1)
+    parity_full(torch_dev, w)
+
+
 def test_non_default_stream(torch_dev):
     torch = torch_dev
     w = S.random_problem(1, 2, 96, 2, 32, dtype="bf16", seed=12, mask="tail", pair="normal")
@@ -259,12 +289,12 @@ def test_errors_write_nothing(torch_dev):
     """Rejected calls return a status and leave the outputs untouched."""
     torch = torch_dev
     import evoformer_biased_attention_amd as E
-    q = torch.zeros((1, 1, 32, 1, 16), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((1, 1, 32, 1, 64), dtype=torch.bfloat16, device="cuda")
     out = torch.full_like(q, 7.0)
-    st = E.evo_attn_fwd(q, q, q, None, None, out, None, (1, 1, 32, 1, 16), E.EVO_DTYPE_BF16,
+    st = E.evo_attn_fwd(q, q, q, None, None, out, None, (1, 1, 32, 1, 64), E.EVO_DTYPE_BF16,
                         torch.cuda.current_stream().cuda_stream)
     assert st == E.EVO_ERR_UNSUPPORTED
-    st = E.evo_attn_fwd(q, q, q, None, None, q, None, (1, 1, 32, 1, 16), E.EVO_DTYPE_BF16, None)
+    st = E.evo_attn_fwd(q, q, q, None, None, q, None, (1, 1, 32, 1, 64), E.EVO_DTYPE_BF16, None)
     assert st == E.EVO_ERR_ALIASING
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
