@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the Evoformer biased-attention forward pass.
+"""fp64 CPU oracle for the Evoformer biased-attention forward and backward passes.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
 CPU-baseline leg may import this package; the product path never does.  It
@@ -10,6 +10,11 @@ hmyw.cn, sections 4, 5.2 and 5.4):
 
     s_j  = q_i . k_j / sqrt(D) + mask[b,n,0,0,j] + pair[b,0,h,i,j]
     out_i = sum_j softmax_j(s) v_j,      lse_i = ln sum_j exp(s_j)
+
+The backward pass (section 5.4: the gradients the training path needs,
+bias gradients only on request) is the chain rule applied to the same
+definition: ``bwd`` returns dq, dk, dv and, when asked, the mask and pair
+gradients, each summed over the axes that bias broadcasts along.
 
 Inputs are numpy arrays holding the stored values: ``float32`` arrays for
 dtype "f32", ``uint16`` bit patterns for "bf16" and "f16".  Outputs are
@@ -60,6 +65,9 @@ def _bind(path):
     lib.evo_ref_fwd.restype = ctypes.c_int
     lib.evo_ref_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, dp, dp,
                                 ctypes.c_int]
+    lib.evo_ref_bwd.restype = ctypes.c_int
+    lib.evo_ref_bwd.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64,
+                                dp, dp, dp, dp, dp, ctypes.c_int]
     lib.evo_ref_rows.restype = ctypes.c_int
     lib.evo_ref_rows.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, vp, i64,
                                  dp, dp, ctypes.c_int]
@@ -140,3 +148,28 @@ def rows(q, k, v, mask=None, pair=None, dtype="bf16", idx=None, nthreads=None, l
     if rc:
         raise RuntimeError(f"evo_ref_rows failed with code {rc}")
     return out, lse
+
+
+def bwd(q, k, v, mask=None, pair=None, dout=None, dtype="bf16", want_dmask=True, want_dpair=True,
+        nthreads=None, lib=None):
+    """Gradients of sum(out * dout) with respect to q, k, v and the biases.
+
+    dout has the inputs' storage format and shape [B,N,L,H,D].  Returns
+    (dq, dk, dv, dmask, dpair) as float64 arrays: dq/dk/dv [B,N,L,H,D], dmask
+    [B,N,1,1,L] (None unless a mask is given and want_dmask), dpair
+    [B,1,H,L,L] (None unless a pair bias is given and want_dpair).
+    """
+    q, k, v, mask, pair, (B, N, L, H, D) = _prep(q, k, v, mask, pair, dtype)
+    dout = np.ascontiguousarray(dout)
+    if dout.dtype != _STORAGE[dtype] or dout.shape != (B, N, L, H, D):
+        raise ValueError(f"dout: expected {_STORAGE[dtype].__name__} {(B, N, L, H, D)}")
+    dq, dk, dv = (np.empty((B, N, L, H, D), np.float64) for _ in range(3))
+    dmask = np.empty((B, N, 1, 1, L), np.float64) if (mask is not None and want_dmask) else None
+    dpair = np.empty((B, 1, H, L, L), np.float64) if (pair is not None and want_dpair) else None
+    rc = (lib or _load()).evo_ref_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(mask), _ptr(pair), _ptr(dout),
+                                      DTYPES[dtype], B, N, L, H, D, dq.ctypes.data, dk.ctypes.data,
+                                      dv.ctypes.data, _ptr(dmask), _ptr(dpair),
+                                      nthreads or default_threads())
+    if rc:
+        raise RuntimeError(f"evo_ref_bwd failed with code {rc}")
+    return dq, dk, dv, dmask, dpair

@@ -179,12 +179,17 @@ int evo_ref_fwd(const void* q, const void* k, const void* v, const void* mask, c
         double* vd = (double*)malloc(sizeof(double) * (size_t)(L * D));
         double* s = (double*)malloc(sizeof(double) * (size_t)L);
         double o_row[1024];
-        if (!kd || !vd || !s) {
+        const int ok = kd && vd && s;
+        if (!ok) {
 #pragma omp atomic write
             failed = 1;
-        } else {
+        }
+        /* every thread reaches the loop (and its closing barrier); one without
+         * scratch memory takes no work */
 #pragma omp for schedule(dynamic, 1)
-            for (int64_t sl = 0; sl < nslices; ++sl) {
+        for (int64_t sl = 0; sl < nslices; ++sl) {
+            if (!ok) continue;
+            {
                 int64_t h = sl % H, n = (sl / H) % N, b = sl / (H * N);
                 widen_slice(&a, b, n, h, kd, vd);
                 for (int64_t i = 0; i < L; ++i) {
@@ -226,21 +231,154 @@ int evo_ref_rows(const void* q, const void* k, const void* v, const void* mask, 
         double* kd = (double*)malloc(sizeof(double) * (size_t)(L * D));
         double* vd = (double*)malloc(sizeof(double) * (size_t)(L * D));
         double* s = (double*)malloc(sizeof(double) * (size_t)L);
-        if (!kd || !vd || !s) {
+        const int ok = kd && vd && s;
+        if (!ok) {
 #pragma omp atomic write
             failed = 1;
-        } else {
+        }
 #pragma omp for schedule(dynamic, 1)
-            for (int64_t r = 0; r < nrows; ++r) {
-                const int64_t* t = rows + 4 * r;
-                widen_slice(&a, t[0], t[1], t[2], kd, vd);
-                double lr = ref_row(&a, kd, vd, t[0], t[1], t[2], t[3], s, out_rows + r * D);
-                if (lse_rows) lse_rows[r] = lr;
-            }
+        for (int64_t r = 0; r < nrows; ++r) {
+            if (!ok) continue;
+            const int64_t* t = rows + 4 * r;
+            widen_slice(&a, t[0], t[1], t[2], kd, vd);
+            double lr = ref_row(&a, kd, vd, t[0], t[1], t[2], t[3], s, out_rows + r * D);
+            if (lse_rows) lse_rows[r] = lr;
         }
         free(kd);
         free(vd);
         free(s);
+    }
+    return failed ? 4 : 0;
+}
+
+/*
+ * Backward pass: the gradients of the forward definition above, in fp64.
+ *
+ * [DSG] S5.4 states that the forward pass keeps the per-row log-sum-exp for
+ * a backward pass and that bias gradients are produced only when asked
+ * for; the gradients themselves follow from the definition by the chain
+ * rule.  With P_ij = exp(s_ij - lse_i) the softmax weights of row i and dO
+ * the incoming gradient of out:
+ *   dv_j        = sum_i P_ij dO_i
+ *   dP_ij       = dO_i . v_j
+ *   delta_i     = sum_e dO_ie out_ie            (= sum_j P_ij dP_ij)
+ *   dS_ij       = P_ij (dP_ij - delta_i)        (gradient of the score)
+ *   dq_i        = sum_j dS_ij k_j / sqrt(D)
+ *   dk_j        = sum_i dS_ij q_i / sqrt(D)
+ *   dmask[b,n,j]    = sum_{h,i} dS[b,n,h,i,j]   (the mask broadcasts over h and i)
+ *   dpair[b,h,i,j]  = sum_n dS[b,n,h,i,j]       (the pair bias broadcasts over n)
+ * out and P are recomputed here from the inputs (not taken from a caller),
+ * so the oracle depends on nothing the GPU produced.  A row whose every
+ * score is -inf has no softmax and contributes nothing.
+ *
+ * dout has the inputs' storage format.  dq, dk, dv: [B,N,L,H,D] doubles;
+ * dmask: [B,N,L] (may be NULL); dpair: [B,H,L,L] (may be NULL).
+ */
+static void slice_backward(const ref_args* a, const void* dout, int64_t b, int64_t n, int64_t h,
+                           const double* kd, const double* vd, double* P, double* dod, double* od,
+                           double* dq, double* dk, double* dv, double* dmask_row, double* dpair_bh) {
+    const int64_t L = a->L, D = a->D;
+    const double scale = 1.0 / sqrt((double)a->D);
+    /* P (row-normalised weights) and out of the slice, through the forward's
+     * own row evaluation: it leaves exp(s_j - m) in the row of P */
+    for (int64_t i = 0; i < L; ++i) {
+        double* Pi = P + i * L;
+        const double lse_i = ref_row(a, kd, vd, b, n, h, i, Pi, od + i * D);
+        if (lse_i == -INFINITY) {
+            for (int64_t j = 0; j < L; ++j) Pi[j] = 0.0;
+        } else {
+            double Z = 0.0;
+            for (int64_t j = 0; j < L; ++j) Z += Pi[j];
+            for (int64_t j = 0; j < L; ++j) Pi[j] /= Z;
+        }
+        for (int64_t e = 0; e < D; ++e) dod[i * D + e] = load(dout, a->dtype, off_qkv(a, b, n, i, h, e));
+    }
+    /* dv, then dS in place of P (after its use for dv), dq, dk and the bias sums */
+    for (int64_t j = 0; j < L; ++j)
+        for (int64_t e = 0; e < D; ++e) {
+            double g = 0.0;
+            for (int64_t i = 0; i < L; ++i) g += P[i * L + j] * dod[i * D + e];
+            dv[off_qkv(a, b, n, j, h, e)] = g;
+        }
+    for (int64_t i = 0; i < L; ++i) {
+        double delta = 0.0;
+        for (int64_t e = 0; e < D; ++e) delta += dod[i * D + e] * od[i * D + e];
+        for (int64_t j = 0; j < L; ++j) {
+            double dp = 0.0;
+            for (int64_t e = 0; e < D; ++e) dp += dod[i * D + e] * vd[j * D + e];
+            P[i * L + j] = P[i * L + j] * (dp - delta); /* now dS_ij */
+        }
+    }
+    for (int64_t i = 0; i < L; ++i)
+        for (int64_t d = 0; d < D; ++d) {
+            double g = 0.0;
+            for (int64_t j = 0; j < L; ++j) g += P[i * L + j] * kd[j * D + d];
+            dq[off_qkv(a, b, n, i, h, d)] = g * scale;
+        }
+    for (int64_t j = 0; j < L; ++j)
+        for (int64_t d = 0; d < D; ++d) {
+            double g = 0.0;
+            for (int64_t r = 0; r < L; ++r) g += P[r * L + j] * load(a->q, a->dtype, off_qkv(a, b, n, r, h, d));
+            dk[off_qkv(a, b, n, j, h, d)] = g * scale;
+        }
+    if (dmask_row)
+        for (int64_t j = 0; j < L; ++j) {
+            double g = 0.0;
+            for (int64_t i = 0; i < L; ++i) g += P[i * L + j];
+            dmask_row[j] += g;
+        }
+    if (dpair_bh)
+        for (int64_t i = 0; i < L; ++i)
+            for (int64_t j = 0; j < L; ++j) dpair_bh[i * L + j] += P[i * L + j];
+}
+
+int evo_ref_bwd(const void* q, const void* k, const void* v, const void* mask, const void* pair, const void* dout,
+                int dtype, int64_t B, int64_t N, int64_t L, int64_t H, int64_t D,
+                double* dq, double* dk, double* dv, double* dmask, double* dpair, int nthreads) {
+    ref_args a = {q, k, v, mask, pair, dtype, B, N, L, H, D};
+    int rc = check_args(&a);
+    if (rc) return rc;
+    if (!dout || !dq || !dk || !dv) return 1;
+    if ((dmask && !mask) || (dpair && !pair)) return 1;
+    if (dmask) memset(dmask, 0, sizeof(double) * (size_t)(B * N * L));
+    if (dpair) memset(dpair, 0, sizeof(double) * (size_t)(B * H * L * L));
+    int failed = 0;
+    /* (b, n) pairs in parallel: each owns its dq/dk/dv slices and its mask
+     * row; the pair-bias gradient, a sum over n, goes through per-thread
+     * partial sums added up at the end */
+#pragma omp parallel num_threads(nthreads > 0 ? nthreads : 1)
+    {
+        double* kd = (double*)malloc(sizeof(double) * (size_t)(L * D));
+        double* vd = (double*)malloc(sizeof(double) * (size_t)(L * D));
+        double* P = (double*)malloc(sizeof(double) * (size_t)(L * L));
+        double* dod = (double*)malloc(sizeof(double) * (size_t)(L * D));
+        double* od = (double*)malloc(sizeof(double) * (size_t)(L * D));
+        double* part = dpair ? (double*)calloc((size_t)(B * H * L * L), sizeof(double)) : NULL;
+        const int ok = kd && vd && P && dod && od && (!dpair || part);
+        if (!ok) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bn = 0; bn < B * N; ++bn) {
+            if (!ok) continue;
+            const int64_t b = bn / N, n = bn % N;
+            for (int64_t h = 0; h < H; ++h) {
+                widen_slice(&a, b, n, h, kd, vd);
+                slice_backward(&a, dout, b, n, h, kd, vd, P, dod, od, dq, dk, dv,
+                               dmask ? dmask + bn * L : NULL, part ? part + (b * H + h) * L * L : NULL);
+            }
+        }
+        /* the loop's closing barrier has passed: every partial is complete */
+#pragma omp critical
+        if (ok && part)
+            for (int64_t e = 0; e < B * H * L * L; ++e) dpair[e] += part[e];
+        free(kd);
+        free(vd);
+        free(P);
+        free(dod);
+        free(od);
+        free(part);
     }
     return failed ? 4 : 0;
 }

@@ -128,6 +128,13 @@ def random_problem(B, N, L, H, D, dtype="bf16", seed=0, mask="tail", pair="norma
                     {"seed": seed, "mask": mask, "pair": pair})
 
 
+def random_dout(shape, dtype="bf16", seed=0, scale=1.0) -> np.ndarray:
+    """Seeded incoming gradient dO for the backward pass: N(0, scale^2) in the
+    storage format, shaped like the output [B, N, L, H, D]."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0x0D0]))
+    return to_storage(scale * _normal(rng, tuple(shape)), dtype)
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads.  Each draws from SeedSequence(1000 + c) spawned
 # into six streams used in a fixed order: q, k, v, mask, pair tensor z, W.

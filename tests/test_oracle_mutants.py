@@ -1,5 +1,8 @@
 """The pins must reject plausible mistakes planted in copies of the oracle source.
 
+Forward mutants face the forward pins; backward mutants (mistakes in the
+gradient code only) face the backward pins.
+
 Each mutant is a textual edit of oracle/evo_ref.c (a dropped term, a wrong
 index, a transposed operand, a wrong constant), compiled with gcc into a
 temporary directory and loaded through the same ctypes interface.  The real
@@ -11,6 +14,7 @@ import os
 import pytest
 
 import oracle
+import oracle_bwd_pins
 import oracle_pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "evo_ref.c")
@@ -40,17 +44,43 @@ MUTANTS = {
     "f16_subnormal_scale": [("(double)frac, -24)", "(double)frac, -23)")],
 }
 
+BWD_MUTANTS = {
+    "bwd_drop_delta": [("P[i * L + j] * (dp - delta);", "P[i * L + j] * dp;")],
+    "bwd_delta_sign": [("P[i * L + j] * (dp - delta);", "P[i * L + j] * (dp + delta);")],
+    "bwd_delta_from_values": [("delta += dod[i * D + e] * od[i * D + e];", "delta += dod[i * D + e] * vd[i * D + e];")],
+    "bwd_dp_from_keys": [("dp += dod[i * D + e] * vd[j * D + e];", "dp += dod[i * D + e] * kd[j * D + e];")],
+    "bwd_dv_transposed_weights": [("g += P[i * L + j] * dod[i * D + e];", "g += P[j * L + i] * dod[i * D + e];")],
+    "bwd_dq_unscaled": [("dq[off_qkv(a, b, n, i, h, d)] = g * scale;", "dq[off_qkv(a, b, n, i, h, d)] = g;")],
+    "bwd_dk_unscaled": [("dk[off_qkv(a, b, n, j, h, d)] = g * scale;", "dk[off_qkv(a, b, n, j, h, d)] = g;")],
+    "bwd_scale_1_over_D": [("const double scale = 1.0 / sqrt((double)a->D);", "const double scale = 1.0 / (double)a->D;")],
+    "bwd_dq_from_values": [("g += P[i * L + j] * kd[j * D + d];", "g += P[i * L + j] * vd[j * D + d];")],
+    "bwd_dk_from_keys": [("load(a->q, a->dtype, off_qkv(a, b, n, r, h, d));", "kd[r * D + d];")],
+    "bwd_dk_transposed": [("g += P[r * L + j] * load", "g += P[j * L + r] * load")],
+    "bwd_unnormalised_weights": [("for (int64_t j = 0; j < L; ++j) Pi[j] /= Z;", "(void)Z;")],
+    "bwd_dmask_by_query": [("for (int64_t i = 0; i < L; ++i) g += P[i * L + j];", "for (int64_t i = 0; i < L; ++i) g += P[j * L + i];")],
+    "bwd_dmask_last_head_only": [("dmask_row[j] += g;", "dmask_row[j] = g;")],
+    "bwd_dpair_transposed": [("dpair_bh[i * L + j] += P[i * L + j];", "dpair_bh[j * L + i] += P[i * L + j];")],
+    "bwd_dpair_last_n_only": [("dpair_bh[i * L + j] += P[i * L + j];", "dpair_bh[i * L + j] = P[i * L + j];")],
+    "bwd_dout_ignores_head": [("off_qkv(a, b, n, i, h, e));", "off_qkv(a, b, n, i, 0, e));")],
+    "bwd_masked_rows_uniform": [("for (int64_t j = 0; j < L; ++j) Pi[j] = 0.0;",
+                                 "for (int64_t j = 0; j < L; ++j) Pi[j] = 1.0 / (double)L;")],
+}
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_pins_reject_mutant(name, tmp_path):
+
+def _compile_mutant(name, edits, tmp_path):
     with open(SRC) as f:
         text = f.read()
-    for old, new in MUTANTS[name]:
+    for old, new in edits:
         assert text.count(old) == 1, f"mutation anchor {old!r} must occur exactly once"
         text = text.replace(old, new)
     src = tmp_path / f"mut_{name}.c"
     src.write_text(text)
-    lib = oracle.load_library(oracle.compile_source(str(src), str(tmp_path / f"libmut_{name}.so")))
+    return oracle.load_library(oracle.compile_source(str(src), str(tmp_path / f"libmut_{name}.so")))
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_mutant(name, tmp_path):
+    lib = _compile_mutant(name, MUTANTS[name], tmp_path)
 
     def ref(q, k, v, mask, pair, dtype):
         return oracle.fwd(q, k, v, mask, pair, dtype=dtype, nthreads=2, lib=lib)
@@ -63,3 +93,21 @@ def test_pins_reject_mutant(name, tmp_path):
             caught_by = pin.__name__
             break
     assert caught_by is not None, f"mutant {name} passed every pin"
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_bwd_pins_reject_mutant(name, tmp_path):
+    lib = _compile_mutant(name, BWD_MUTANTS[name], tmp_path)
+
+    def gref(q, k, v, mask, pair, dout, dtype):
+        # one thread: the per-thread pair partials then hold every n in turn
+        return oracle.bwd(q, k, v, mask, pair, dout, dtype=dtype, nthreads=1, lib=lib)
+
+    caught_by = None
+    for pin in oracle_bwd_pins.ALL_BWD_PINS:
+        try:
+            pin(gref)
+        except (AssertionError, RuntimeError):
+            caught_by = pin.__name__
+            break
+    assert caught_by is not None, f"mutant {name} passed every backward pin"
