@@ -1,8 +1,9 @@
-"""Python binding of libevoattn.so, the MI355X Evoformer biased-attention forward library.
+"""Python binding of libevoattn.so, the MI355X Evoformer biased-attention library (forward and backward).
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C ABI declared in include/evo_attn.h.  The functions keep
-the C names (`evo_attn_fwd`, `evo_attn_check`, `evo_status_string`) and take
+the C names (`evo_attn_fwd`, `evo_attn_bwd`, their `*_check` validators,
+`evo_status_string`) and take
 either raw device addresses (int) or torch tensors, whose `data_ptr()` is
 passed through; PyTorch is used for device memory and streams only.
 
@@ -19,10 +20,11 @@ LIB_PATH = os.path.join(_HERE, "libevoattn.so")
 
 EVO_DTYPE_F32, EVO_DTYPE_BF16, EVO_DTYPE_F16 = 0, 1, 2
 (EVO_OK, EVO_ERR_NULL_POINTER, EVO_ERR_BAD_SHAPE, EVO_ERR_BAD_DTYPE, EVO_ERR_MISALIGNED, EVO_ERR_ALIASING,
- EVO_ERR_UNSUPPORTED, EVO_ERR_HIP) = range(8)
+ EVO_ERR_UNSUPPORTED, EVO_ERR_HIP, EVO_ERR_NO_BIAS) = range(9)
 
 # Symbols declared in include/evo_attn.h.
-EXPORTED = ("evo_attn_fwd", "evo_attn_check", "evo_status_string", "evo_attn_last_hip_error")
+EXPORTED = ("evo_attn_fwd", "evo_attn_check", "evo_attn_bwd", "evo_attn_bwd_check", "evo_status_string",
+            "evo_attn_last_hip_error")
 
 
 class EvoShape(ctypes.Structure):
@@ -56,6 +58,10 @@ def _load():
     lib.evo_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(EvoShape), ctypes.c_int, vp]
     lib.evo_attn_check.restype = ctypes.c_int
     lib.evo_attn_check.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(EvoShape), ctypes.c_int]
+    lib.evo_attn_bwd.restype = ctypes.c_int
+    lib.evo_attn_bwd.argtypes = [vp] * 14 + [ctypes.POINTER(EvoShape), ctypes.c_int, vp]
+    lib.evo_attn_bwd_check.restype = ctypes.c_int
+    lib.evo_attn_bwd_check.argtypes = [vp] * 14 + [ctypes.POINTER(EvoShape), ctypes.c_int]
     lib.evo_status_string.restype = ctypes.c_char_p
     lib.evo_status_string.argtypes = [ctypes.c_int]
     lib.evo_attn_last_hip_error.restype = ctypes.c_int
@@ -106,6 +112,22 @@ def evo_attn_fwd(q, k, v, mask_bias, pair_bias, out, lse, shape, dtype, stream=N
                              _addr(lse), ctypes.byref(_shape(shape)), int(dtype), stream)
 
 
+def evo_attn_bwd_check(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias, dpair_bias, delta,
+                       shape, dtype) -> int:
+    """Host-only validation of the backward call; returns the status code."""
+    return _lib.evo_attn_bwd_check(*[_addr(x) for x in (q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv,
+                                                       dmask_bias, dpair_bias, delta)],
+                                   ctypes.byref(_shape(shape)), int(dtype))
+
+
+def evo_attn_bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias, dpair_bias, delta,
+                 shape, dtype, stream=None) -> int:
+    """Enqueue the backward pass; returns the status code (arguments as in include/evo_attn.h)."""
+    return _lib.evo_attn_bwd(*[_addr(x) for x in (q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv,
+                                                 dmask_bias, dpair_bias, delta)],
+                             ctypes.byref(_shape(shape)), int(dtype), stream)
+
+
 def torch_dtype_code(dt) -> int:
     import torch
     return {torch.float32: EVO_DTYPE_F32, torch.bfloat16: EVO_DTYPE_BF16, torch.float16: EVO_DTYPE_F16}[dt]
@@ -138,3 +160,30 @@ def fwd(q, k, v, mask_bias=None, pair_bias=None, out=None, lse=True, stream=None
     if st != EVO_OK:
         raise EvoAttnError(st)
     return out, lse_t
+
+
+def bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, want_dmask=True, want_dpair=True, stream=None):
+    """torch convenience wrapper around evo_attn_bwd: allocates the gradients and delta with torch.
+
+    out and lse are the forward pass's results for the same inputs.  Returns
+    (dq, dk, dv, dmask_bias or None, dpair_bias or None, delta); a bias
+    gradient is computed only when that bias is given and wanted.
+    Raises EvoAttnError for any status other than EVO_OK.
+    """
+    import torch
+    B, N, L, H, D = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("mask_bias", mask_bias), ("pair_bias", pair_bias),
+                    ("out", out), ("lse", lse), ("dout", dout)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dmask = torch.empty_like(mask_bias) if (mask_bias is not None and want_dmask) else None
+    dpair = torch.empty_like(pair_bias) if (pair_bias is not None and want_dpair) else None
+    delta = torch.empty((B, N, H, L), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = evo_attn_bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask, dpair, delta,
+                      (B, N, L, H, D), torch_dtype_code(q.dtype), stream)
+    if st != EVO_OK:
+        raise EvoAttnError(st)
+    return dq, dk, dv, dmask, dpair, delta

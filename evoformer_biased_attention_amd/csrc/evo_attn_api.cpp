@@ -108,6 +108,73 @@ extern "C" evo_status_t evo_attn_fwd(const void* q, const void* k, const void* v
     return EVO_ERR_HIP;
 }
 
+namespace {
+
+// Gradient support: every dtype with D in {8, 16, 32, 64} (section 5.4 of the
+// guide gives D <= 64 as the backward pass's limit).
+bool bwd_supported(evo_dtype_t dt, int64_t D) {
+    return (dt == EVO_DTYPE_F32 || dt == EVO_DTYPE_BF16 || dt == EVO_DTYPE_F16) &&
+           (D == 8 || D == 16 || D == 32 || D == 64);
+}
+
+}  // namespace
+
+extern "C" evo_status_t evo_attn_bwd_check(const void* q, const void* k, const void* v, const void* mask_bias,
+                                           const void* pair_bias, const void* out, const float* lse,
+                                           const void* dout, const void* dq, const void* dk, const void* dv,
+                                           const void* dmask_bias, const void* dpair_bias, const float* delta,
+                                           const evo_shape_t* shape, evo_dtype_t dtype) {
+    if (!shape || !q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !delta)
+        return EVO_ERR_NULL_POINTER;
+    const int64_t B = shape->B, N = shape->N, L = shape->L, H = shape->H, D = shape->D;
+    if (B < 1 || N < 1 || L < 1 || H < 1 || D < 1) return EVO_ERR_BAD_SHAPE;
+    if (dtype != EVO_DTYPE_F32 && dtype != EVO_DTYPE_BF16 && dtype != EVO_DTYPE_F16) return EVO_ERR_BAD_DTYPE;
+    if ((dmask_bias && !mask_bias) || (dpair_bias && !pair_bias)) return EVO_ERR_NO_BIAS;
+    const int64_t es = elem_size(dtype);
+
+    int64_t qkv = es;
+    for (int64_t s : {B, N, L, H, D}) qkv = mul_checked(qkv, s);
+    int64_t msk = es;
+    for (int64_t s : {B, N, L}) msk = mul_checked(msk, s);
+    int64_t par = es;
+    for (int64_t s : {B, H, L, L}) par = mul_checked(par, s);
+    int64_t row = 4;
+    for (int64_t s : {B, N, H, L}) row = mul_checked(row, s);
+    if (qkv < 0 || msk < 0 || par < 0 || row < 0) return EVO_ERR_BAD_SHAPE;
+
+    for (const void* p : {q, k, v, mask_bias, pair_bias, out, static_cast<const void*>(lse), dout, dq, dk, dv,
+                          dmask_bias, dpair_bias, static_cast<const void*>(delta)})
+        if (p && !aligned16(p)) return EVO_ERR_MISALIGNED;
+
+    const Extent outs[] = {extent(dq, qkv), extent(dk, qkv), extent(dv, qkv), extent(dmask_bias, msk),
+                           extent(dpair_bias, par), extent(delta, row)};
+    const Extent ins[] = {extent(q, qkv),         extent(k, qkv),   extent(v, qkv), extent(mask_bias, msk),
+                          extent(pair_bias, par), extent(out, qkv), extent(lse, row), extent(dout, qkv)};
+    for (size_t a = 0; a < sizeof(outs) / sizeof(outs[0]); ++a) {
+        for (const Extent& in : ins)
+            if (outs[a].overlaps(in)) return EVO_ERR_ALIASING;
+        for (size_t c = a + 1; c < sizeof(outs) / sizeof(outs[0]); ++c)
+            if (outs[a].overlaps(outs[c])) return EVO_ERR_ALIASING;
+    }
+    if (!bwd_supported(dtype, D)) return EVO_ERR_UNSUPPORTED;
+    return EVO_OK;
+}
+
+extern "C" evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v, const void* mask_bias,
+                                     const void* pair_bias, const void* out, const float* lse, const void* dout,
+                                     void* dq, void* dk, void* dv, void* dmask_bias, void* dpair_bias,
+                                     float* delta, const evo_shape_t* shape, evo_dtype_t dtype, void* stream) {
+    const evo_status_t st = evo_attn_bwd_check(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv,
+                                               dmask_bias, dpair_bias, delta, shape, dtype);
+    if (st != EVO_OK) return st;
+    evo::BwdArgs a{q,  k,  v,  mask_bias,  pair_bias,  out,   lse,      dout,     dq,       dk,      dv,
+                   dmask_bias, dpair_bias, delta, shape->B, shape->N, shape->L, shape->H, shape->D};
+    const hipError_t err = evo::launch_bwd(a, static_cast<int>(dtype), static_cast<hipStream_t>(stream));
+    if (err == hipSuccess) return EVO_OK;
+    g_last_hip_error = static_cast<int>(err);
+    return EVO_ERR_HIP;
+}
+
 extern "C" int evo_attn_last_hip_error(void) { return g_last_hip_error; }
 
 extern "C" const char* evo_status_string(evo_status_t status) {
@@ -117,9 +184,10 @@ extern "C" const char* evo_status_string(evo_status_t status) {
     case EVO_ERR_BAD_SHAPE: return "a size is below 1 or a tensor exceeds 2^62 bytes";
     case EVO_ERR_BAD_DTYPE: return "dtype is not an evo_dtype_t value";
     case EVO_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
-    case EVO_ERR_ALIASING: return "out or lse overlaps an input or each other";
+    case EVO_ERR_ALIASING: return "an output overlaps an input or another output";
     case EVO_ERR_UNSUPPORTED: return "dtype / head dimension combination not implemented";
     case EVO_ERR_HIP: return "the HIP runtime reported an error at launch";
+    case EVO_ERR_NO_BIAS: return "a bias gradient was requested for a bias that was not given";
     }
     return "unknown status";
 }

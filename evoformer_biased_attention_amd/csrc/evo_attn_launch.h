@@ -27,4 +27,26 @@ hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t stream);
 // f32 inputs, D in {8, 16, 32, 64}: vector-ALU kernel.
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* mask;   // [B,N,1,1,L] or nullptr
+    const void* pair;   // [B,1,H,L,L] or nullptr
+    const void* out;    // forward output [B,N,L,H,D]
+    const float* lse;   // forward log-sum-exp [B,N,H,L]
+    const void* dout;   // incoming gradient [B,N,L,H,D]
+    void* dq;
+    void* dk;
+    void* dv;
+    void* dmask;        // [B,N,1,1,L] or nullptr (only with mask)
+    void* dpair;        // [B,1,H,L,L] or nullptr (only with pair)
+    float* delta;       // [B,N,H,L], written
+    int64_t B, N, L, H, D;
+};
+
+// Backward pass, dtype 0 = f32, 1 = bf16, 2 = f16, D in {8, 16, 32, 64}:
+// vector-ALU kernels.  Returns the hipError_t of the first failing launch.
+hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t stream);
+
 }  // namespace evo

@@ -1,6 +1,6 @@
 /*
  * evo_attn.h -- C ABI of the MI355X (gfx950) Evoformer biased-attention
- * forward library, libevoattn.so.
+ * library, libevoattn.so: the forward pass and its gradients.
  *
  * Operation.  The page "DeepSpeed DS4Sci_EvoformerAttention 内核实战指南"
  * (hmyw.cn/news/91637) defines it: section 4 gives the reference attention
@@ -66,13 +66,14 @@ typedef struct {
 
 typedef enum {
     EVO_OK = 0,
-    EVO_ERR_NULL_POINTER = 1, /* q, k, v, out or shape is NULL                              */
+    EVO_ERR_NULL_POINTER = 1, /* a required pointer (see each call) is NULL                 */
     EVO_ERR_BAD_SHAPE = 2,    /* a size < 1, or a tensor of more than 2^62 bytes            */
     EVO_ERR_BAD_DTYPE = 3,    /* dtype is not an evo_dtype_t value                          */
     EVO_ERR_MISALIGNED = 4,   /* a tensor pointer is not 16-byte aligned                    */
-    EVO_ERR_ALIASING = 5,     /* out or lse overlaps an input, or out overlaps lse          */
+    EVO_ERR_ALIASING = 5,     /* an output overlaps an input or another output              */
     EVO_ERR_UNSUPPORTED = 6,  /* valid but not implemented (dtype / head dimension)         */
-    EVO_ERR_HIP = 7           /* the HIP runtime reported an error at launch                */
+    EVO_ERR_HIP = 7,          /* the HIP runtime reported an error at launch                */
+    EVO_ERR_NO_BIAS = 8       /* evo_attn_bwd: a bias gradient requested for an absent bias  */
 } evo_status_t;
 
 /*
@@ -104,12 +105,65 @@ evo_status_t evo_attn_check(const void* q, const void* k, const void* v, const v
                             const void* pair_bias, const void* out, const float* lse,
                             const evo_shape_t* shape, evo_dtype_t dtype);
 
+/*
+ * Enqueue the backward pass on `stream`: the gradients of a scalar loss with
+ * respect to q, k, v and, on request, each bias, given dout = d loss / d out.
+ * Section 5.4 of the guide describes this pass: it recomputes the attention
+ * weights from q, k, the biases and the forward pass's log-sum-exp instead of
+ * keeping the [L, L] matrix, uses the per-row quantity delta_i = dout_i . out_i,
+ * and computes a bias gradient only when the caller asks for it.  With
+ * P_ij = exp(s_ij - lse_i) the forward weights and dS_ij = P_ij (dout_i . v_j
+ * - delta_i):
+ *   dq_i = sum_j dS_ij k_j / sqrt(D)        dk_j = sum_i dS_ij q_i / sqrt(D)
+ *   dv_j = sum_i P_ij dout_i
+ *   dmask_bias[b,n,0,0,j] = sum over h and i of dS[b,n,h,i,j]
+ *   dpair_bias[b,0,h,i,j] = sum over n of dS[b,n,h,i,j]
+ * (each bias gradient summed over the axes along which that bias broadcasts).
+ *
+ *   q, k, v, mask_bias, pair_bias   the forward pass's inputs, as for evo_attn_fwd
+ *   out, lse     the forward pass's outputs for those inputs (evo_attn_fwd with
+ *                a non-NULL lse); both required
+ *   dout         [B,N,L,H,D] incoming gradient, element type `dtype`
+ *   dq, dk, dv   [B,N,L,H,D] outputs, element type `dtype`
+ *   dmask_bias   [B,N,1,1,L] output of type `dtype`, or NULL to skip it; only
+ *                with a mask_bias (else EVO_ERR_NO_BIAS)
+ *   dpair_bias   [B,1,H,L,L] output of type `dtype`, or NULL to skip it (and
+ *                its kernel); only with a pair_bias (else EVO_ERR_NO_BIAS)
+ *   delta        [B,N,H,L] float32, written with dout_i . out_i (the saved
+ *                intermediate of section 5.4); required, owned by the caller
+ * Every output is overwritten, never accumulated into.  All arithmetic is
+ * fp32; results are rounded to nearest-even into `dtype` once, at the end.
+ * Sums are formed in a fixed order: the same inputs give bit-identical
+ * gradients on every call.  A row with lse = -inf (every key -inf) receives
+ * and passes on no gradient.
+ * Supported today: every dtype with D in {8, 16, 32, 64} (the guide's limit
+ * for this pass is D <= 64), any B, N, H, L >= 1.  Other valid combinations
+ * return EVO_ERR_UNSUPPORTED.  Required pointers: q, k, v, out, lse, dout, dq,
+ * dk, dv, delta, shape.  Pointer, ownership, alignment, aliasing and error
+ * rules are those of evo_attn_fwd; the outputs (dq, dk, dv, dmask_bias,
+ * dpair_bias, delta) may overlap neither an input nor one another.
+ */
+evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v, const void* mask_bias,
+                          const void* pair_bias, const void* out, const float* lse, const void* dout,
+                          void* dq, void* dk, void* dv, void* dmask_bias, void* dpair_bias, float* delta,
+                          const evo_shape_t* shape, evo_dtype_t dtype, void* stream);
+
+/*
+ * The validation of evo_attn_bwd alone (same arguments minus the stream).
+ * Host-only, like evo_attn_check.
+ */
+evo_status_t evo_attn_bwd_check(const void* q, const void* k, const void* v, const void* mask_bias,
+                                const void* pair_bias, const void* out, const float* lse, const void* dout,
+                                const void* dq, const void* dk, const void* dv, const void* dmask_bias,
+                                const void* dpair_bias, const float* delta, const evo_shape_t* shape,
+                                evo_dtype_t dtype);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* evo_status_string(evo_status_t status);
 
 /*
  * The hipError_t (as an int) that made the calling thread's most recent
- * evo_attn_fwd return EVO_ERR_HIP, or 0 if none has.  Thread-local; never
+ * evo_attn_fwd or evo_attn_bwd return EVO_ERR_HIP, or 0 if none has.  Thread-local; never
  * reset by successful calls.  Lets a caller report the runtime's own reason.
  */
 int evo_attn_last_hip_error(void);

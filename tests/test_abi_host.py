@@ -35,13 +35,13 @@ def test_enum_values_match_header():
     text = _header_text()
     for name in ("EVO_DTYPE_F32", "EVO_DTYPE_BF16", "EVO_DTYPE_F16", "EVO_OK", "EVO_ERR_NULL_POINTER",
                  "EVO_ERR_BAD_SHAPE", "EVO_ERR_BAD_DTYPE", "EVO_ERR_MISALIGNED", "EVO_ERR_ALIASING",
-                 "EVO_ERR_UNSUPPORTED", "EVO_ERR_HIP"):
+                 "EVO_ERR_UNSUPPORTED", "EVO_ERR_HIP", "EVO_ERR_NO_BIAS"):
         m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
         assert m and int(m.group(1)) == getattr(E, name), name
 
 
 def test_status_strings():
-    for s in range(8):
+    for s in range(9):
         assert E.evo_status_string(s) and E.evo_status_string(s) != "unknown status"
     assert E.evo_status_string(99) == "unknown status"
 
@@ -157,3 +157,60 @@ def test_single_hip_runtime_in_process():
             "print(len(maps)); print(sorted(maps))")
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, check=True)
     assert res.stdout.splitlines()[0] == "1", res.stdout
+
+
+# ---------------------------------------------------------------------------
+# evo_attn_bwd_check
+# ---------------------------------------------------------------------------
+BWD_NAMES = ["q", "k", "v", "mask_bias", "pair_bias", "out", "lse", "dout", "dq", "dk", "dv", "dmask_bias",
+             "dpair_bias", "delta"]
+
+
+def bcheck(shape=(1, 2, 64, 4, 32), dtype=E.EVO_DTYPE_BF16, **over):
+    args = dict(zip(BWD_NAMES, addrs(len(BWD_NAMES))))
+    args.update(over)
+    return E.evo_attn_bwd_check(*[args[n] for n in BWD_NAMES], shape, dtype)
+
+
+def test_bwd_valid():
+    for dt in (E.EVO_DTYPE_F32, E.EVO_DTYPE_BF16, E.EVO_DTYPE_F16):
+        for d in (8, 16, 32, 64):
+            assert bcheck(shape=(2, 3, 17, 2, d), dtype=dt) == E.EVO_OK
+    assert bcheck(dmask_bias=None, dpair_bias=None) == E.EVO_OK          # bias gradients are optional
+    assert bcheck(mask_bias=None, pair_bias=None, dmask_bias=None, dpair_bias=None) == E.EVO_OK
+    assert bcheck(shape=(1, 1, 1, 1, 8)) == E.EVO_OK
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "out", "lse", "dout", "dq", "dk", "dv", "delta"])
+def test_bwd_null_required_pointer(name):
+    assert bcheck(**{name: None}) == E.EVO_ERR_NULL_POINTER
+
+
+def test_bwd_bias_gradient_needs_its_bias():
+    assert bcheck(mask_bias=None) == E.EVO_ERR_NO_BIAS
+    assert bcheck(pair_bias=None) == E.EVO_ERR_NO_BIAS
+    assert bcheck(mask_bias=None, dmask_bias=None) == E.EVO_OK
+
+
+@pytest.mark.parametrize("name", BWD_NAMES)
+def test_bwd_misaligned(name):
+    a = dict(zip(BWD_NAMES, addrs(len(BWD_NAMES))))
+    assert bcheck(**{name: a[name] + 4}) == E.EVO_ERR_MISALIGNED
+
+
+def test_bwd_aliasing():
+    a = dict(zip(BWD_NAMES, addrs(len(BWD_NAMES))))
+    for o in ("dq", "dk", "dv", "dmask_bias", "dpair_bias", "delta"):
+        for i in ("q", "k", "v", "mask_bias", "pair_bias", "out", "lse", "dout"):
+            assert bcheck(**{o: a[i]}) == E.EVO_ERR_ALIASING, (o, i)
+    assert bcheck(dk=a["dq"]) == E.EVO_ERR_ALIASING                       # outputs may not share memory
+    assert bcheck(delta=a["dv"] + 512) == E.EVO_ERR_ALIASING
+    assert bcheck(dq=a["q"] + 65536) == E.EVO_OK                          # adjacent, disjoint
+    assert bcheck(k=a["q"], v=a["q"]) == E.EVO_OK                         # inputs may alias
+
+
+def test_bwd_bad_shape_dtype_unsupported():
+    assert bcheck(shape=(1, 0, 8, 1, 32)) == E.EVO_ERR_BAD_SHAPE
+    assert bcheck(dtype=7) == E.EVO_ERR_BAD_DTYPE
+    for d in (4, 24, 128):
+        assert bcheck(shape=(1, 1, 32, 1, d)) == E.EVO_ERR_UNSUPPORTED

@@ -1,0 +1,266 @@
+"""Backward pass: HIP path vs the fp64 oracle, element by element, through the C ABI.
+
+The HIP backward takes the forward pass's out and lse.  Where the forward
+supports the dtype and head dimension they come from the HIP forward (the
+pipeline a caller runs); otherwise (bf16/f16 with D = 64) from the oracle,
+rounded to the storage format.  The oracle recomputes everything from q, k, v,
+the biases and dO in fp64 and never sees a GPU value.
+
+Tolerances, per gradient tensor G, as errors normalised by max|G_ref|:
+  f32:  max <= 1e-4, mean <= 1e-5
+  bf16: max <= 1.6e-2, mean <= 2e-3
+  f16:  max <= 4e-3, mean <= 5e-4
+The backward arithmetic is fp32; the 16-bit budgets come from rounding each
+gradient to the storage format once (half an ulp: 2^-9 relative in bf16,
+2^-12 in f16) and from delta = dO . out using the stored (rounded) out, whose
+error moves every dS_ij of a row by P_ij times that row's delta error.  The
+max bounds allow four ulps of the largest value (bf16 ulp 2^-8, f16 2^-10):
+two for the final rounding and two for delta.  The delta term is the larger
+one where the softmax is peaked (biases of scale 8): one key takes almost all
+the weight, dS_ij = P_ij dO_i . (v_j - out_i) becomes a small difference and
+the rounding of out reaches it undiminished.  The guide's own unit test
+accepts 5e-2 (bf16) and 1e-2 (fp16) on the gradients (section 4).  The mean of the rounding
+error alone reaches a quarter ulp (2^-10 for bf16) when most values sit near
+the maximum, as in a tensor of a few elements, so the mean bounds are twice
+that: the forward's 2e-3 for bf16, and 5e-4 for f16.
+delta = dO . out is computed from the out the backward is given, which
+carries the forward pass's own error (bounded by the forward tolerances:
+max |d out| <= 1e-4 / 2e-2 / 1e-2 for f32 / bf16 / f16); so it is compared
+with dO . out_ref within that bound times sum_e |dO_e|.
+
+Outputs are poisoned with NaN before every launch.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as S
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": dict(max=1e-4, mean=1e-5, out=1e-4),
+       "bf16": dict(max=1.6e-2, mean=2e-3, out=2e-2),
+       "f16": dict(max=4e-3, mean=5e-4, out=1e-2)}
+THREADS = min(16, oracle.default_threads())
+NAMES = ("dq", "dk", "dv", "dmask", "dpair")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import evoformer_biased_attention_amd  # noqa: F401  (fails loudly if the library is missing)
+    return torch
+
+
+def to_dev(torch, x, dtype):
+    if x is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype == "bf16":
+        t = t.view(torch.bfloat16)
+    elif dtype == "f16":
+        t = t.view(torch.float16)
+    return t.to("cuda")
+
+
+def f64(t):
+    return None if t is None else t.float().cpu().numpy().astype(np.float64)
+
+
+def fwd_supported(dtype, D):
+    return D in (8, 16, 32) or (dtype == "f32" and D == 64)
+
+
+def run_bwd(torch, w, dout, want_dmask=True, want_dpair=True, fwd_from_oracle=False, stream=None):
+    """Forward (HIP, or the oracle where the HIP forward lacks the shape), then the HIP backward.
+
+    Returns (grads as float64 numpy [dq, dk, dv, dmask|None, dpair|None], delta, out).
+    """
+    import evoformer_biased_attention_amd as E
+    B, N, L, H, D = w.shape
+    q, k, v = (to_dev(torch, x, w.dtype) for x in (w.q, w.k, w.v))
+    mask, pair = to_dev(torch, w.mask, w.dtype), to_dev(torch, w.pair, w.dtype)
+    do = to_dev(torch, dout, w.dtype)
+    if fwd_from_oracle or not fwd_supported(w.dtype, D):
+        ro, rl = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype=w.dtype, nthreads=THREADS)
+        out = to_dev(torch, S.to_storage(ro.astype(np.float32), w.dtype), w.dtype)
+        lse = torch.from_numpy(rl.astype(np.float32)).to("cuda")
+    else:
+        out, lse = E.fwd(q, k, v, mask, pair)
+    dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+    dmask = torch.full_like(mask, float("nan")) if (mask is not None and want_dmask) else None
+    dpair = torch.full_like(pair, float("nan")) if (pair is not None and want_dpair) else None
+    delta = torch.full((B, N, H, L), float("nan"), dtype=torch.float32, device="cuda")
+    code = E.torch_dtype_code(q.dtype)
+    say(f"  bwd {w.name} shape={w.shape} dtype={w.dtype} mask={mask is not None} pair={pair is not None} "
+        f"dmask={dmask is not None} dpair={dpair is not None}")
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    st = E.evo_attn_bwd(q, k, v, mask, pair, out, lse, do, dq, dk, dv, dmask, dpair, delta, w.shape, code, stream)
+    assert st == E.EVO_OK, E.evo_status_string(st)
+    torch.cuda.synchronize()
+    return [f64(x) for x in (dq, dk, dv, dmask, dpair)], f64(delta), f64(out)
+
+
+def compare_grads(got, want, dtype, what):
+    tol = TOL[dtype]
+    for name, g, r in zip(NAMES, got, want):
+        assert (g is None) == (r is None), f"{what} {name}: presence differs"
+        if g is None:
+            continue
+        assert np.isfinite(g).all(), f"{what} {name}: non-finite values"
+        scale = max(np.abs(r).max(), 1e-30)
+        err = np.abs(g - r) / scale
+        msg = f"{what} {name}: max|d|/max|ref|={err.max():.3e} mean={err.mean():.3e} (max|ref|={scale:.3e})"
+        say("  " + msg)
+        assert err.max() <= tol["max"], msg
+        assert err.mean() <= tol["mean"], msg
+
+
+def compare_delta(delta, w, dout, what):
+    """delta = dO . out, checked against the oracle's out."""
+    ro, _ = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype=w.dtype, nthreads=THREADS)
+    dof = S.storage_to_f32(dout, w.dtype).astype(np.float64)
+    want = np.einsum("bnlhd,bnlhd->bnhl", dof, ro)
+    bound = TOL[w.dtype]["out"] * np.abs(dof).sum(axis=-1).transpose(0, 1, 3, 2) + 1e-6
+    assert (np.abs(delta - want) <= bound).all(), f"{what}: delta off by {np.abs(delta - want).max():.3e}"
+
+
+def parity(torch, w, dout, want_dmask=True, want_dpair=True, **kw):
+    got, delta, _ = run_bwd(torch, w, dout, want_dmask, want_dpair, **kw)
+    want = list(oracle.bwd(w.q, w.k, w.v, w.mask, w.pair, dout, dtype=w.dtype, want_dmask=want_dmask,
+                           want_dpair=want_dpair, nthreads=THREADS))
+    compare_grads(got, want, w.dtype, w.name)
+    compare_delta(delta, w, dout, w.name)
+    return got
+
+
+# ---------------------------------------------------------------------------
+# Ragged shapes: several 64-row tiles and a partial one, every dtype and head
+# dimension, every bias combination.
+# ---------------------------------------------------------------------------
+SHAPES = [(1, 1, 1, 1), (1, 2, 5, 3), (2, 3, 17, 2), (1, 2, 64, 2), (1, 2, 77, 3), (2, 2, 130, 2)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("d", [8, 16, 32, 64])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_bwd_ragged(torch_dev, shape, d, dtype):
+    B, N, L, H = shape
+    w = S.random_problem(B, N, L, H, d, dtype=dtype, seed=B * 1000 + N * 100 + L + H + d, mask="tail",
+                         pair="normal", mask_frac=0.3)
+    dout = S.random_dout(w.shape, dtype, seed=L + d)
+    parity(torch_dev, w, dout)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("bias", ["mask", "pair", "none"])
+def test_bwd_bias_subsets(torch_dev, dtype, bias):
+    w = S.random_problem(1, 3, 90, 2, 32, dtype=dtype, seed=len(bias) * 13, mask="tail" if bias == "mask" else None,
+                         pair="normal" if bias == "pair" else None, mask_frac=0.3)
+    dout = S.random_dout(w.shape, dtype, seed=5)
+    parity(torch_dev, w, dout)
+
+
+def test_bwd_bias_gradients_on_request(torch_dev):
+    """Without dmask/dpair the other gradients are unchanged (and the pair kernel does not run)."""
+    w = S.random_problem(1, 2, 70, 2, 32, dtype="bf16", seed=21, mask="tail", pair="normal")
+    dout = S.random_dout(w.shape, "bf16", seed=22)
+    full = parity(torch_dev, w, dout)
+    part = parity(torch_dev, w, dout, want_dmask=False, want_dpair=False)
+    assert part[3] is None and part[4] is None
+    for a, b in zip(full[:3], part[:3]):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_bwd_deterministic(torch_dev):
+    """Sums are formed in a fixed order: two calls agree bit for bit."""
+    w = S.random_problem(1, 5, 100, 2, 32, dtype="bf16", seed=23, mask="tail", pair="normal")
+    dout = S.random_dout(w.shape, "bf16", seed=24)
+    a, da, _ = run_bwd(torch_dev, w, dout)
+    b, db, _ = run_bwd(torch_dev, w, dout)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    np.testing.assert_array_equal(da, db)
+
+
+def test_bwd_large_biases_random_masks(torch_dev):
+    w = S.random_problem(1, 4, 150, 2, 32, dtype="bf16", seed=25, mask="random", pair="normal", mask_frac=0.5,
+                         bias_scale=8.0)
+    parity(torch_dev, w, S.random_dout(w.shape, "bf16", seed=26))
+
+
+@pytest.mark.parametrize("L", [40, 96])
+def test_bwd_f16_fully_masked_sequence(torch_dev, L):
+    """f16 turns -1e9 into -inf: a sequence with every key removed gets and passes on no gradient."""
+    B, N, H, D = 1, 3, 2, 32
+    w = S.random_problem(B, N, L, H, D, dtype="f16", seed=27 + L, mask="zero", pair="normal")
+    mf = np.zeros((B, N, 1, 1, L), np.float32)
+    mf[0, 0, ..., 10:30] = -1e9
+    mf[0, 1] = -1e9
+    w.mask = S.to_storage(mf, "f16")
+    dout = S.random_dout(w.shape, "f16", seed=28)
+    got = parity(torch_dev, w, dout)
+    for g in got[:4]:
+        assert np.all(g[0, 1] == 0)
+
+
+def test_bwd_oracle_forward_inputs(torch_dev):
+    """The backward accepts out/lse from any forward: oracle values give the same gradients to the bound."""
+    w = S.random_problem(1, 2, 80, 2, 32, dtype="bf16", seed=29, mask="tail", pair="normal")
+    dout = S.random_dout(w.shape, "bf16", seed=30)
+    parity(torch_dev, w, dout, fwd_from_oracle=True)
+
+
+def test_bwd_non_default_stream(torch_dev):
+    torch = torch_dev
+    w = S.random_problem(1, 2, 96, 2, 32, dtype="bf16", seed=31, mask="tail", pair="normal")
+    dout = S.random_dout(w.shape, "bf16", seed=32)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        got, _, _ = run_bwd(torch, w, dout, stream=s.cuda_stream)
+    want = list(oracle.bwd(w.q, w.k, w.v, w.mask, w.pair, dout, dtype="bf16", nthreads=THREADS))
+    compare_grads(got, want, "bf16", "side stream")
+
+
+def test_bwd_errors_write_nothing(torch_dev):
+    torch = torch_dev
+    import evoformer_biased_attention_amd as E
+    shp = (1, 1, 32, 1, 24)
+    q = torch.zeros(shp, dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((1, 1, 1, 32), dtype=torch.float32, device="cuda")
+    outs = [torch.full_like(q, 7.0) for _ in range(3)]
+    delta = torch.full_like(lse, 7.0)
+    st = E.evo_attn_bwd(q, q, q, None, None, q, lse, q, *outs, None, None, delta, shp, E.EVO_DTYPE_BF16, None)
+    assert st == E.EVO_ERR_UNSUPPORTED
+    st = E.evo_attn_bwd(q, q, q, None, q, q, lse, q, *outs, None, outs[0], delta, (1, 1, 32, 1, 32),
+                        E.EVO_DTYPE_BF16, None)
+    assert st != E.EVO_OK
+    torch.cuda.synchronize()
+    assert all(bool((o == 7.0).all()) for o in outs) and bool((delta == 7.0).all())
+
+
+# ---------------------------------------------------------------------------
+# Named workloads at full size (the oracle's full backward finishes in seconds
+# for these): the guide's unit-test shape and the triangle-attention problem.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("c", [1, 2, 4])
+def test_bwd_workload_full(torch_dev, c):
+    w = S.workload(c)
+    say(f"workload {c} backward: full oracle comparison")
+    parity(torch_dev, w, S.random_dout(w.shape, w.dtype, seed=100 + c))
+
+
+def test_bwd_ds4sci_unit_test_shape(torch_dev):
+    """The guide's unit test checks every gradient on (1,256,256,4,32) with both biases (section 4)."""
+    w = S.random_problem(1, 256, 256, 4, 32, dtype="f16", seed=4053, mask="tail", pair="normal", mask_frac=0.1)
+    parity(torch_dev, w, S.random_dout(w.shape, "f16", seed=4054))
