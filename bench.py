@@ -79,6 +79,8 @@ def main():
     ap.add_argument("--dtype", choices=["bf16", "f16", "f32"], default=None,
                     help="store the workload's values in this format instead of its own")
     ap.add_argument("--mode", choices=["cold", "warm"], default="cold")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
+                    help="fwd (default): the forward pass; bwd: one evo_attn_bwd call per step, every gradient")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-time budget of the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-warm", action="store_true", help="skip the secondary warm-cache measurement")
@@ -126,6 +128,9 @@ def main():
             return None
         t = torch.from_numpy(np.ascontiguousarray(x))
         return (t if w.dtype == "f32" else t.view(tdt)).to("cuda")
+
+    if args.which == "bwd":
+        return bench_bwd(args, w, dev, torch, E, S)
 
     base = [dev(x) for x in (w.q, w.k, w.v, w.mask, w.pair)]
     set_bytes = sum(t.numel() * t.element_size() for t in base if t is not None) * 4 // 3 + B * N * H * L * 4
@@ -229,6 +234,106 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, sets[0], args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+BWD_METRIC = "biased-attention bwd TFLOP/s (dq, dk, dv, mask and pair gradients), triangle attn N=L=384"
+
+
+def bench_bwd(args, w, dev, torch, E, S):
+    """One step = one evo_attn_bwd call: dq, dk, dv, the mask gradient and the
+    pair gradient (a sum over N), from the forward pass's out and lse.
+    Throughput counts the backward's dense work 10*B*N*H*L^2*D: the score
+    recomputation Q.K^T, dP = dO.V^T, dV = P^T.dO, dQ = dS.K and dK = dS^T.Q."""
+    B, N, L, H, D = w.shape
+    dcode = {"f32": E.EVO_DTYPE_F32, "bf16": E.EVO_DTYPE_BF16, "f16": E.EVO_DTYPE_F16}[w.dtype]
+    dout = S.random_dout(w.shape, w.dtype, seed=2026)
+    base = [dev(x) for x in (w.q, w.k, w.v, w.mask, w.pair, dout)]
+    out, lse = E.fwd(*base[:5])
+    base += [out, lse]
+    in_bytes = sum(t.numel() * t.element_size() for t in base if t is not None)
+    set_bytes = 2 * in_bytes
+    R = 1 if args.mode == "warm" else max(2, math.ceil(2.5 * MALL_BYTES / set_bytes))
+    sets = []
+    for r in range(R):
+        ins = [t if (t is None or r == 0) else t.clone() for t in base]
+        q, k, v, m, p, do, o, l = ins
+        grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+                 None if m is None else torch.empty_like(m), None if p is None else torch.empty_like(p),
+                 torch.empty((B, N, H, L), dtype=torch.float32, device="cuda")]
+        sets.append((ins, grads))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def launch(r):
+        (q, k, v, m, p, do, o, l), (dq, dk, dv, dm, dp, delta) = sets[r]
+        return E.evo_attn_bwd(q, k, v, m, p, o, l, do, dq, dk, dv, dm, dp, delta, w.shape, dcode, sh)
+
+    st = launch(0)
+    if st != E.EVO_OK:
+        raise E.EvoAttnError(st)
+    log(f"bench bwd: {R} input set(s) of {set_bytes / 2**20:.1f} MiB, warmup {args.warmup}, steps {args.steps}")
+    t_spin = time.perf_counter()
+    while time.perf_counter() - t_spin < args.spinup_seconds:
+        for i in range(5):
+            launch(i % R)
+        torch.cuda.synchronize()
+    for i in range(args.warmup):
+        launch(i % R)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        launch(i % R)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pass_us = 1e3 * ev0.elapsed_time(ev1) / args.steps
+    flops = 10 * B * N * H * L * L * D
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (pass_us * 1e-6) / 1e12
+    log(f"bench bwd: {pass_us:.2f} us/pass (events), {achieved:.2f} TFLOP/s")
+    result = {
+        "metric": BWD_METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; see synthetic/)",
+        "config": {"workload": w.name, "variant": w.meta.get("variant"), "B": B, "N": N, "L": L, "H": H, "D": D,
+                   "mask": w.mask is not None, "pair_bias": w.pair is not None, "mode": args.mode,
+                   "input_sets": R, "flop_per_step": flops, "kernels_per_step": 3 if w.pair is not None else 2},
+        # the three kernels run fp32 arithmetic on the vector ALUs: priced against the fp32 vector peak
+        "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_F32_TFLOPS, 4), "traffic": None, "scope": "whole pass"},
+        "pass_us": round(pass_us, 3),
+    }
+    if not args.no_cpu_baseline:
+        import numpy as np
+        import oracle
+        threads = len(os.sched_getaffinity(0))
+        passes, t = 0, 0.0
+        while passes == 0 or (t < args.cpu_seconds and passes < 50):
+            t0 = time.perf_counter()
+            ref = oracle.bwd(w.q, w.k, w.v, w.mask, w.pair, dout, dtype=w.dtype, nthreads=threads)
+            t += time.perf_counter() - t0
+            passes += 1
+        got = [None if g is None else g.float().cpu().numpy() for g in sets[0][1][:5]]
+        err = {n: float(np.abs(g - r).max() / np.abs(r).max())
+               for n, g, r in zip(("dq", "dk", "dv", "dmask", "dpair"), got, ref) if g is not None}
+        result["cpu_baseline"] = {"value": round(flops * passes / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+                                  "kind": "oracle",
+                                  "sample": f"{passes} full backward pass(es) over workload {w.name} in fp64, "
+                                            f"{t:.1f} s",
+                                  "parity_vs_gpu_max_err_over_max_ref": err}
     print(json.dumps(result), flush=True)
 
 
