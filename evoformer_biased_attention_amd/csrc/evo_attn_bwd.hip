@@ -308,8 +308,9 @@ __global__ __launch_bounds__(kLanes) void bwd_dpair_kernel(Params<T> p) {
         if (c < jcnt) T::st(out, c, acc[c]);
 }
 
+// stages: a mask of kStageDq | kStageDkDv | kStageDpair, the kernels to run here
 template <class T, int D>
-hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_all(const BwdArgs& a, unsigned stages, hipStream_t stream) {
     using S = typename T::S;
     Params<T> p;
     p.q = static_cast<const S*>(a.q);
@@ -339,39 +340,57 @@ hipError_t launch_all(const BwdArgs& a, hipStream_t stream) {
     const int64_t g_pair = a.B * a.H * p.blocks_l * p.groups_j;
     if (g_dq > 0x7fffffff || g_kv > 0x7fffffff || g_pair > 0x7fffffff) return hipErrorInvalidConfiguration;
 
-    // delta is written by the first kernel and read by the other two, which
+    // delta is written by the dq kernel and read by the other two, which
     // follow it on the same stream.
     void* args[] = {&p};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_kernel<T, D>), dim3(unsigned(g_dq)),
-                                   dim3(kLanes), args, 0, stream);
-    if (e != hipSuccess) return e;
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<T, D>), dim3(unsigned(g_kv)), dim3(kLanes),
-                        args, 0, stream);
-    if (e != hipSuccess || !a.dpair) return e;
-    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dpair_kernel<T, D>), dim3(unsigned(g_pair)),
-                           dim3(kLanes), args, 0, stream);
+    hipError_t e = hipSuccess;
+    if (stages & kStageDq)
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_kernel<T, D>), dim3(unsigned(g_dq)), dim3(kLanes),
+                            args, 0, stream);
+    if (e == hipSuccess && (stages & kStageDkDv))
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<T, D>), dim3(unsigned(g_kv)),
+                            dim3(kLanes), args, 0, stream);
+    if (e == hipSuccess && (stages & kStageDpair) && a.dpair)
+        e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dpair_kernel<T, D>), dim3(unsigned(g_pair)),
+                            dim3(kLanes), args, 0, stream);
+    return e;
 }
 
 template <class T>
-hipError_t launch_dim(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_dim(const BwdArgs& a, unsigned stages, hipStream_t stream) {
     switch (a.D) {
-    case 8: return launch_all<T, 8>(a, stream);
-    case 16: return launch_all<T, 16>(a, stream);
-    case 32: return launch_all<T, 32>(a, stream);
-    case 64: return launch_all<T, 64>(a, stream);
+    case 8: return launch_all<T, 8>(a, stages, stream);
+    case 16: return launch_all<T, 16>(a, stages, stream);
+    case 32: return launch_all<T, 32>(a, stages, stream);
+    case 64: return launch_all<T, 64>(a, stages, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_valu(const BwdArgs& a, int dtype, unsigned stages, hipStream_t stream) {
+    if (!stages) return hipSuccess;
+    switch (dtype) {
+    case 0: return launch_dim<TF32>(a, stages, stream);
+    case 1: return launch_dim<TBF16>(a, stages, stream);
+    case 2: return launch_dim<TF16>(a, stages, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
+// The matrix-core kernels take the stages they implement for the shapes
+// they accept (16-bit formats, D <= 32, L % 8 == 0); the vector-ALU kernels
+// take the rest.  The dq stage goes first in either case: it writes delta.
 hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t stream) {
-    switch (dtype) {
-    case 0: return launch_dim<TF32>(a, stream);
-    case 1: return launch_dim<TBF16>(a, stream);
-    case 2: return launch_dim<TF16>(a, stream);
-    default: return hipErrorInvalidValue;
-    }
+    const unsigned mfma = bwd_mfma_eligible(a, dtype) ? kBwdMfmaStages : 0u;
+    hipError_t e = hipSuccess;
+    if (mfma & kStageDq) e = launch_bwd_mfma(a, dtype, kStageDq, stream);
+    else e = launch_valu(a, dtype, kStageDq, stream);
+    if (e != hipSuccess) return e;
+    if (mfma & ~kStageDq) e = launch_bwd_mfma(a, dtype, mfma & ~kStageDq, stream);
+    if (e != hipSuccess) return e;
+    return launch_valu(a, dtype, (kStageDkDv | kStageDpair) & ~mfma, stream);
 }
 
 }  // namespace evo

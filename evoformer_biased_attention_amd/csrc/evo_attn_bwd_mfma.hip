@@ -1,0 +1,407 @@
+// Backward pass on the matrix cores (bf16 / f16, head dimension 8, 16 or 32).
+//
+// The gradients (page "DeepSpeed DS4Sci_EvoformerAttention 内核实战指南",
+// hmyw.cn, sections 4 and 5.4: the backward pass recomputes the weights from
+// the saved log-sum-exp and uses delta_i = dO_i . out_i) are, with
+// P_ij = exp(s_ij - lse_i) and dS_ij = P_ij (dO_i . v_j - delta_i):
+//   dq_i = sum_j dS_ij k_j / sqrt(D),  dk_j = sum_i dS_ij q_i / sqrt(D),
+//   dv_j = sum_i P_ij dO_i, dmask = sum over h, i of dS, dpair = sum over n of dS.
+//
+// Every product runs on v_mfma_f32_16x16x32_{bf16,f16} (fp32 accumulation);
+// the weights and dS enter the second products rounded to the input format.
+// The result of a 16x16 MFMA leaves column n of the tile in lanes n, n+16,
+// n+32, n+48, which is where the B operand of the next MFMA expects column n:
+// a product whose result's row index is the next product's contraction index
+// chains without any data exchange.  Hence two orientations:
+//   bwd_dq_mfma   scores transposed (S^T = K.Q^T, one query per lane column):
+//                 dQ^T = K^T . dS^T contracts over keys.  Also writes delta.
+//   bwd_dkdv_mfma scores upright (S = Q.K^T, one key per lane column):
+//                 dV^T = dO^T . P and dK^T = Q^T . dS contract over queries;
+//                 the workgroup visits every head, so dmask is complete.
+// The contraction index of a chained product is permuted (element e of a
+// 32-wide chunk is row 16(e/4) + 4g + e%4 of the result tiles); the other
+// operand is read through the transposing LDS read ds_read_b64_tr_b16 in the
+// same order.
+//
+// Operand tiles move from global memory to LDS with buffer loads that write
+// LDS directly, one block ahead, double buffered; buffer resources return
+// zeros past their range, which pads rows past L and dimensions past D.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
+#include "evo_attn_launch.h"
+
+namespace evo {
+namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16;
+
+constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every range: loads return zeros
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWaves = 4;
+constexpr int kWaveRows = 32;                // queries (dq kernel) or keys (dk/dv kernel) per wavefront
+constexpr int kBlockRows = kWaves * kWaveRows;
+constexpr int kKB = 64;                      // keys (dq kernel) or queries (dk/dv kernel) per LDS block
+constexpr int kKT = kKB / 16;
+
+struct Bf16Fmt {
+    typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+    typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+    __device__ static float widen(u16 x) { return __builtin_bit_cast(float, (uint32_t)x << 16); }
+    __device__ static f32x4 mfma(v8 a, v8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
+};
+struct F16Fmt {
+    typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+    typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+    __device__ static float widen(u16 x) { return (float)__builtin_bit_cast(_Float16, x); }
+    __device__ static f32x4 mfma(v8 a, v8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+};
+
+// two floats -> two 16-bit values (nearest even), low half first
+template <class E>
+__device__ inline uint32_t pack2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, typename E::v2));
+}
+
+template <class E>
+__device__ inline typename E::v8 as_v8(uint4 x) { return __builtin_bit_cast(typename E::v8, x); }
+
+// the two 16-bit values of a dword, widened
+template <class E>
+__device__ inline f32x2 unpack2(uint32_t w) { return f32x2{E::widen((u16)(w & 0xffffu)), E::widen((u16)(w >> 16))}; }
+
+// ds_read_b64_tr_b16 of the 8 bytes at p: in each 16-lane group, lane i
+// receives element e (e = 0..3) from column i % 4 of the 4-element row that
+// lane 4e + i/4 addressed.  With lane a addressing row R0 + a/4, columns
+// 4(a%4) .. +3 of a row-major matrix, lane i gets column i of rows R0 .. R0+3.
+__device__ inline uint2 ds_read_tr(const void* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((__attribute__((address_space(3))) char*)p));
+    return __builtin_bit_cast(uint2, r);
+}
+
+__device__ inline float sum_over_groups(float x) {
+    x += __shfl_xor(x, 16);
+    return x + __shfl_xor(x, 32);
+}
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+__device__ inline Rsrc make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ inline uint4 bload16(Rsrc r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+// 16 bytes per lane straight into LDS: lane l's bytes land at lds + 16 l
+__device__ inline void dma16(Rsrc r, const void* lds, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff,
+                                             (int)soff, 0, 0);
+}
+
+__device__ inline void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+
+// x / d with a multiply-high and a shift (Granlund and Montgomery, PLDI
+// 1994, section 4), for 0 <= x < 2^31 and 1 <= d < 2^31.
+struct FastDiv {
+    uint32_t d, m, l;
+};
+
+__device__ inline uint32_t fdiv(uint32_t x, FastDiv f) { return (__umulhi(x, f.m) + x) >> f.l; }
+
+FastDiv make_fastdiv(uint32_t d) {
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d) ++l;
+    const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+    return FastDiv{d, (uint32_t)m, l};
+}
+
+// Workgroups are dealt round-robin over the 8 XCDs; renumber them so that
+// each XCD runs one contiguous range of the logical order, whose neighbours
+// share operand lines in that XCD's L2.
+__device__ inline int64_t logical_block(int64_t hw, int64_t total) {
+    const int64_t xcd = hw % 8, j = hw / 8;
+    const int64_t per = total / 8, extra = total % 8;
+    return xcd < extra ? xcd * (per + 1) + j : extra * (per + 1) + (xcd - extra) * per + j;
+}
+
+struct Params {
+    const u16 *q, *k, *v, *mask, *pair, *out, *dout;
+    const float* lse;
+    u16 *dq, *dk, *dv, *dmask, *dpair;
+    float* delta;
+    int64_t N, L, H;
+    FastDiv rblocks;  // ceil(L / 128): row blocks of the dq and dk/dv kernels
+    FastDiv nd, hd;   // N, H
+    int64_t total;    // workgroups of the launch
+    float c1;         // log2(e) / sqrt(D): raw q.k -> base-2 exponent
+    float scale;      // 1 / sqrt(D)
+};
+
+// Per-row constant of the exponent: lse * log2(e), or +inf for a row without
+// softmax (lse = -inf) so that every weight of the row is exactly zero.
+__device__ inline float lse_base2(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
+
+// ---------------------------------------------------------------------------
+// dq (and delta).  Workgroup = 128 queries of one (b, n, h); wave w owns
+// queries 32w .. 32w+31 as two 16-query tiles.  LDS per 64-key block:
+//   k, v: slot 4*key + (chunk ^ ((key >> 2) & 3)), chunk = 8 d-values
+//   pt:   slot 8*row + (chunk ^ (row & 7)), row = query of the workgroup, chunk = 8 keys
+//   mt:   slot chunk (8 keys)
+// ---------------------------------------------------------------------------
+struct DqBuf {
+    uint4 k[kKB * 4];
+    uint4 v[kKB * 4];
+    uint4 pt[kBlockRows * 8];
+    uint4 mt[8];
+};
+
+template <class E, int D, bool PAIR, bool MASK>
+__global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
+    using V8 = typename E::v8;
+    constexpr int kDC = D / 8;           // 16-byte chunks per row
+    constexpr int kDHT = (D + 15) / 16;  // 16-wide d tiles
+    __shared__ __attribute__((aligned(16))) DqBuf sm[2];
+
+    const uint32_t id = (uint32_t)logical_block(blockIdx.x, p.total);
+    const uint32_t r1 = fdiv(id, p.rblocks), r2 = fdiv(r1, p.hd), r3 = fdiv(r2, p.nd);
+    const int64_t qb = id - r1 * p.rblocks.d;
+    const int64_t h = r1 - r2 * p.hd.d, n = r2 - r3 * p.nd.d, b = r3;
+    const int L = (int)p.L;
+    const int64_t HD = p.H * D;
+    const int64_t slice = ((b * p.N + n) * p.L * p.H + h) * D;
+    const int64_t rowbase = ((b * p.N + n) * p.H + h) * p.L;  // lse / delta index of query 0
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int c = lane & 15, g = lane >> 4;
+    const int nblocks = (L + kKB - 1) / kKB;
+    const uint32_t rowb = (uint32_t)HD * 2;
+    const uint32_t span = (uint32_t)(L - 1) * rowb + D * 2;
+    const Rsrc rq = make_rsrc(p.q + slice, span);
+    const Rsrc rk = make_rsrc(p.k + slice, span);
+    const Rsrc rv = make_rsrc(p.v + slice, span);
+    const Rsrc rdo = make_rsrc(p.dout + slice, span);
+    const Rsrc ro = make_rsrc(p.out + slice, span);
+    const Rsrc rp = make_rsrc(PAIR ? p.pair + (b * p.H + h) * p.L * p.L : p.q, PAIR ? (uint32_t)L * (uint32_t)L * 2u : 0u);
+    const Rsrc rm = make_rsrc(MASK ? p.mask + (b * p.N + n) * p.L : p.q, MASK ? (uint32_t)L * 2u : 0u);
+
+    const int q0 = (int)qb * kBlockRows + wave * kWaveRows;
+    // B operands of S^T = K.Q^T and dP^T = V.dO^T: lane (c + 16g) holds row
+    // (query c of the tile), d-values 8g .. 8g+7; rows past L and chunks past D read as zero
+    V8 qop[2], dop[2];
+    float delta[2], lse2[2];
+    for (int t = 0; t < 2; ++t) {
+        const int i = q0 + 16 * t + c;
+        const uint32_t off = g < kDC ? (uint32_t)i * rowb + 16u * g : kOOB;
+        const uint4 qq = bload16(rq, off, 0), dd = bload16(rdo, off, 0), oo = bload16(ro, off, 0);
+        qop[t] = as_v8<E>(qq);
+        dop[t] = as_v8<E>(dd);
+        const uint32_t dw[4] = {dd.x, dd.y, dd.z, dd.w}, ow[4] = {oo.x, oo.y, oo.z, oo.w};
+        float part = 0.f;
+        for (int e = 0; e < 4; ++e) {
+            const f32x2 a = unpack2<E>(dw[e]), o = unpack2<E>(ow[e]);
+            part = fmaf(a[0], o[0], part);
+            part = fmaf(a[1], o[1], part);
+        }
+        delta[t] = sum_over_groups(part);
+        lse2[t] = i < L ? lse_base2(p.lse[rowbase + i]) : INFINITY;
+        if (g == 0 && i < L) p.delta[rowbase + i] = delta[t];
+    }
+
+    // copies of one 64-key block (same addressing as the forward kernel)
+    const uint32_t qwg = (uint32_t)(qb * kBlockRows);
+    const uint32_t kvchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+    const uint32_t kvo = kvchunk < kDC ? (uint32_t)(16 * wave + (lane >> 2)) * rowb + 16u * kvchunk : kOOB;
+    uint32_t pvo[4];
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t row = 8u * (4 * wave + j) + (lane >> 3);
+        pvo[j] = (qwg + row) * (uint32_t)L * 2u + 16u * ((lane & 7) ^ (lane >> 3));
+    }
+    auto copy_block = [&](int blk, DqBuf* __restrict__ dst) {
+        const uint32_t k0 = (uint32_t)blk * kKB;
+        dma16(rk, &dst->k[64 * wave], kvo, k0 * rowb);
+        dma16(rv, &dst->v[64 * wave], kvo, k0 * rowb);
+        if (PAIR)
+            for (int j = 0; j < 4; ++j) dma16(rp, &dst->pt[64 * (4 * wave + j)], pvo[j], k0 * 2u);
+        if (MASK && wave == 0 && lane < 8) dma16(rm, &dst->mt[0], 16u * lane, k0 * 2u);
+    };
+
+    f32x4 dqacc[2][2];
+    for (int t = 0; t < 2; ++t) dqacc[t][0] = dqacc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    copy_block(0, &sm[0]);
+    wait_all();
+    __syncthreads();
+
+    auto step = [&](int it, const DqBuf* __restrict__ cur, DqBuf* __restrict__ nxt, auto tail_tag) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
+        const int k0 = it * kKB;
+        // A operands: K and V rows (key 16kt + c, chunk g) and transposed K
+        // for dQ^T = K^T.dS^T (column 16dh + c over keys 32cc + 4g + 0..3 and
+        // 32cc + 16 + 4g + 0..3)
+        V8 kop[kKT], vop[kKT], ktr[2][2];
+        for (int kt = 0; kt < kKT; ++kt) {
+            kop[kt] = as_v8<E>(cur->k[64 * kt + 4 * c + (g ^ ((c >> 2) & 3))]);
+            vop[kt] = as_v8<E>(cur->v[64 * kt + 4 * c + (g ^ ((c >> 2) & 3))]);
+        }
+        for (int cc = 0; cc < 2; ++cc)
+            for (int dh = 0; dh < kDHT; ++dh) {
+                const int key = 32 * cc + 4 * g + (c >> 2);
+                const int chunk = (2 * dh + ((c & 3) >> 1)) ^ g;
+                const char* base = reinterpret_cast<const char*>(&cur->k[4 * key + chunk]) + 8 * (c & 1);
+                const uint2 lo = ds_read_tr(base);
+                const uint2 hi = ds_read_tr(base + 16 * 4 * 16);
+                ktr[cc][dh] = as_v8<E>(uint4{lo.x, lo.y, hi.x, hi.y});
+            }
+        // biases of lane (c + 16g): keys 16kt + 4g + 0..3 (8 bytes), query c of each tile
+        uint2 pb[2][kKT], mb[kKT];
+        for (int kt = 0; kt < kKT; ++kt) {
+            const int chunk = 2 * kt + (g >> 1);
+            if (MASK) mb[kt] = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(&cur->mt[chunk]) + 8 * (g & 1));
+            if (PAIR)
+                for (int t = 0; t < 2; ++t) {
+                    const int row = wave * kWaveRows + 16 * t + c;
+                    pb[t][kt] = *reinterpret_cast<const uint2*>(
+                        reinterpret_cast<const char*>(&cur->pt[8 * row + (chunk ^ (c & 7))]) + 8 * (g & 1));
+                }
+        }
+
+        if (it + 1 < nblocks) copy_block(it + 1, nxt);
+
+        f32x4 s[2][kKT], dp[2][kKT];
+        for (int kt = 0; kt < kKT; ++kt)
+            for (int t = 0; t < 2; ++t) {
+                s[t][kt] = E::mfma(kop[kt], qop[t], f32x4{0.f, 0.f, 0.f, 0.f});
+                dp[t][kt] = E::mfma(vop[kt], dop[t], f32x4{0.f, 0.f, 0.f, 0.f});
+            }
+        V8 dsop[2][2];
+        for (int t = 0; t < 2; ++t) {
+            uint32_t w[8];
+            for (int kt = 0; kt < kKT; ++kt) {
+                float bias[4] = {0.f, 0.f, 0.f, 0.f};
+                if (MASK) {
+                    const f32x2 m01 = unpack2<E>(mb[kt].x), m23 = unpack2<E>(mb[kt].y);
+                    bias[0] = m01[0], bias[1] = m01[1], bias[2] = m23[0], bias[3] = m23[1];
+                }
+                if (PAIR) {
+                    const f32x2 a01 = unpack2<E>(pb[t][kt].x), a23 = unpack2<E>(pb[t][kt].y);
+                    bias[0] += a01[0], bias[1] += a01[1], bias[2] += a23[0], bias[3] += a23[1];
+                }
+                float ds[4];
+                for (int r = 0; r < 4; ++r) {
+                    float x = fmaf(s[t][kt][r], p.c1, fmaf(bias[r], kLog2e, -lse2[t]));
+                    if (TAIL && k0 + 16 * kt + 4 * g + r >= L) x = -INFINITY;  // keys past L take no weight
+                    ds[r] = __builtin_amdgcn_exp2f(x) * (dp[t][kt][r] - delta[t]);
+                }
+                w[2 * kt] = pack2<E>(ds[0], ds[1]);
+                w[2 * kt + 1] = pack2<E>(ds[2], ds[3]);
+            }
+            // element e of 32-key chunk cc is key 32cc + 16(e/4) + 4g + e%4
+            dsop[t][0] = as_v8<E>(uint4{w[0], w[1], w[2], w[3]});
+            dsop[t][1] = as_v8<E>(uint4{w[4], w[5], w[6], w[7]});
+        }
+        for (int cc = 0; cc < 2; ++cc)
+            for (int dh = 0; dh < kDHT; ++dh)
+                for (int t = 0; t < 2; ++t) dqacc[t][dh] = E::mfma(ktr[cc][dh], dsop[t][cc], dqacc[t][dh]);
+
+        wait_all();
+        __syncthreads();
+    };
+    for (int it = 0; it + 1 < nblocks; ++it) step(it, &sm[it & 1], &sm[(it & 1) ^ 1], std::false_type{});
+    {
+        const int it = nblocks - 1;
+        if (L % kKB) step(it, &sm[it & 1], &sm[(it & 1) ^ 1], std::true_type{});
+        else step(it, &sm[it & 1], &sm[(it & 1) ^ 1], std::false_type{});
+    }
+
+    // lane (c + 16g) holds dQ^T[d = 16dh + 4g + r][query c]
+    for (int t = 0; t < 2; ++t) {
+        const int64_t i = q0 + 16 * t + c;
+        if (i >= L) continue;
+        for (int dh = 0; dh < kDHT; ++dh) {
+            if (16 * dh + 4 * g >= D) continue;
+            const f32x4 o = dqacc[t][dh] * p.scale;
+            *reinterpret_cast<uint2*>(p.dq + slice + i * HD + 16 * dh + 4 * g) = uint2{pack2<E>(o[0], o[1]), pack2<E>(o[2], o[3])};
+        }
+    }
+}
+
+template <class E, int D, bool PAIR, bool MASK>
+hipError_t launch_dq(Params& p, int64_t B, hipStream_t stream) {
+    const int64_t rblocks = (p.L + kBlockRows - 1) / kBlockRows;
+    p.total = B * p.N * p.H * rblocks;
+    if (p.total >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
+    p.rblocks = make_fastdiv((uint32_t)rblocks);
+    void* args[] = {&p};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_mfma<E, D, PAIR, MASK>), dim3((unsigned)p.total),
+                           dim3(kWaves * 64), args, 0, stream);
+}
+
+template <class E, int D>
+hipError_t launch_dim(const BwdArgs& a, unsigned stages, hipStream_t stream) {
+    Params p;
+    p.q = static_cast<const u16*>(a.q);
+    p.k = static_cast<const u16*>(a.k);
+    p.v = static_cast<const u16*>(a.v);
+    p.mask = static_cast<const u16*>(a.mask);
+    p.pair = static_cast<const u16*>(a.pair);
+    p.out = static_cast<const u16*>(a.out);
+    p.dout = static_cast<const u16*>(a.dout);
+    p.lse = a.lse;
+    p.dq = static_cast<u16*>(a.dq);
+    p.dk = static_cast<u16*>(a.dk);
+    p.dv = static_cast<u16*>(a.dv);
+    p.dmask = static_cast<u16*>(a.dmask);
+    p.dpair = static_cast<u16*>(a.dpair);
+    p.delta = a.delta;
+    p.N = a.N;
+    p.L = a.L;
+    p.H = a.H;
+    p.nd = make_fastdiv((uint32_t)a.N);
+    p.hd = make_fastdiv((uint32_t)a.H);
+    p.c1 = (float)(1.4426950408889634 / std::sqrt((double)D));
+    p.scale = (float)(1.0 / std::sqrt((double)D));
+    const bool pair = a.pair != nullptr, mask = a.mask != nullptr;
+    hipError_t e = hipSuccess;
+    if (stages & kStageDq) {
+        if (pair && mask) e = launch_dq<E, D, true, true>(p, a.B, stream);
+        else if (pair) e = launch_dq<E, D, true, false>(p, a.B, stream);
+        else if (mask) e = launch_dq<E, D, false, true>(p, a.B, stream);
+        else e = launch_dq<E, D, false, false>(p, a.B, stream);
+    }
+    return e;
+}
+
+template <class E>
+hipError_t launch_format(const BwdArgs& a, unsigned stages, hipStream_t stream) {
+    switch (a.D) {
+    case 8: return launch_dim<E, 8>(a, stages, stream);
+    case 16: return launch_dim<E, 16>(a, stages, stream);
+    case 32: return launch_dim<E, 32>(a, stages, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+const unsigned kBwdMfmaStages = kStageDq;
+
+bool bwd_mfma_eligible(const BwdArgs& a, int dtype) {
+    constexpr int64_t kMax = int64_t(1) << 31;
+    return (dtype == 1 || dtype == 2) && (a.D == 8 || a.D == 16 || a.D == 32) && a.L % 8 == 0 &&
+           a.L * a.H * a.D * 2 < kMax && a.L * a.L * 2 < kMax && a.N < kMax && a.H < kMax;
+}
+
+hipError_t launch_bwd_mfma(const BwdArgs& a, int dtype, unsigned stages, hipStream_t stream) {
+    return dtype == 2 ? launch_format<F16Fmt>(a, stages, stream) : launch_format<Bf16Fmt>(a, stages, stream);
+}
+
+}  // namespace evo

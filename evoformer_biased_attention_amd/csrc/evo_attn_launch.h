@@ -45,8 +45,19 @@ struct BwdArgs {
     int64_t B, N, L, H, D;
 };
 
-// Backward pass, dtype 0 = f32, 1 = bf16, 2 = f16, D in {8, 16, 32, 64}:
-// vector-ALU kernels.  Returns the hipError_t of the first failing launch.
+// Backward pass, dtype 0 = f32, 1 = bf16, 2 = f16, D in {8, 16, 32, 64}.
+// Returns the hipError_t of the first failing launch.
 hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t stream);
+
+// The backward's three stages (each a kernel that owns its outputs).
+constexpr unsigned kStageDq = 1;     // dq, and delta (read by the other two)
+constexpr unsigned kStageDkDv = 2;   // dk, dv, dmask
+constexpr unsigned kStageDpair = 4;  // dpair
+
+// Matrix-core backward: the stages it implements, whether it accepts the
+// arguments, and a launch of some of those stages in stage order.
+extern const unsigned kBwdMfmaStages;
+bool bwd_mfma_eligible(const BwdArgs& a, int dtype);
+hipError_t launch_bwd_mfma(const BwdArgs& a, int dtype, unsigned stages, hipStream_t stream);
 
 }  // namespace evo
