@@ -214,7 +214,9 @@ __device__ inline float sum_over_groups(float x) {
 }
 
 // Buffer resources: base address + byte range in SGPRs, 32-bit per-lane
-// offsets.  A load past the range returns zeros.
+// offsets.  A load past the range returns zeros.  Every offset is passed in
+// the per-lane part (the scalar offset stays 0), so the range check sees the
+// whole offset.
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 
 __device__ inline Rsrc make_rsrc(const void* base, uint32_t bytes) {
@@ -321,11 +323,11 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
     }
     auto copy_block = [&](int blk, FastBuf* __restrict__ dst) {
         const uint32_t k0 = (uint32_t)blk * kKB;
-        dma16(rk, &dst->k[64 * wave], kvo, k0 * rowb);
-        dma16(rv, &dst->v[64 * wave], kvo, k0 * rowb);
+        dma16(rk, &dst->k[64 * wave], kvo + k0 * rowb, 0);
+        dma16(rv, &dst->v[64 * wave], kvo + k0 * rowb, 0);
         if (PAIR)
-            for (int j = 0; j < 4; ++j) dma16(rp, &dst->pt[64 * (4 * wave + j)], pvo[j], k0 * 2u);
-        if (MASK && wave == 0 && lane < 8) dma16(rm, &dst->mt[0], 16u * lane, k0 * 2u);
+            for (int j = 0; j < 4; ++j) dma16(rp, &dst->pt[64 * (4 * wave + j)], pvo[j] + k0 * 2u, 0);
+        if (MASK && wave == 0 && lane < 8) dma16(rm, &dst->mt[0], 16u * lane + k0 * 2u, 0);
     };
 
     f32x4 oacc[kQTiles][2];

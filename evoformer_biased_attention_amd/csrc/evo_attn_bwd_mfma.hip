@@ -91,6 +91,10 @@ __device__ inline float sum_over_groups(float x) {
     return x + __shfl_xor(x, 32);
 }
 
+// Buffer resources: base + byte range in SGPRs.  A load past the range
+// returns zeros.  Every offset is passed in the per-lane part (the scalar
+// offset stays 0), so the range check sees the whole offset; offsets past
+// the range stay below 2^32 (kOOB plus less than 2^31).
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 
 __device__ inline Rsrc make_rsrc(const void* base, uint32_t bytes) {
@@ -227,11 +231,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
     }
     auto copy_block = [&](int blk, DqBuf* __restrict__ dst) {
         const uint32_t k0 = (uint32_t)blk * kKB;
-        dma16(rk, &dst->k[64 * wave], kvo, k0 * rowb);
-        dma16(rv, &dst->v[64 * wave], kvo, k0 * rowb);
+        dma16(rk, &dst->k[64 * wave], kvo + k0 * rowb, 0);
+        dma16(rv, &dst->v[64 * wave], kvo + k0 * rowb, 0);
         if (PAIR)
-            for (int j = 0; j < 4; ++j) dma16(rp, &dst->pt[64 * (4 * wave + j)], pvo[j], k0 * 2u);
-        if (MASK && wave == 0 && lane < 8) dma16(rm, &dst->mt[0], 16u * lane, k0 * 2u);
+            for (int j = 0; j < 4; ++j) dma16(rp, &dst->pt[64 * (4 * wave + j)], pvo[j] + k0 * 2u, 0);
+        if (MASK && wave == 0 && lane < 8) dma16(rm, &dst->mt[0], 16u * lane + k0 * 2u, 0);
     };
 
     f32x4 dqacc[2][2];
@@ -334,6 +338,239 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// dk, dv and dmask.  Workgroup = 128 keys of one (b, n); wave w owns keys
+// 32w .. 32w+31 as two 16-key tiles and keeps their K and V rows (B
+// operands of S = Q.K^T and dP = dO.V^T) in registers.  The workgroup walks
+// every (head, 64-query block) pair in order; LDS per step:
+//   q, dO: slot 4*row + (chunk ^ ((row >> 2) & 3)), row = query of the block, chunk = 8 d-values
+//   pt:    slot 16*row + (chunk ^ 2(row & 7)), row = query of the block, chunk = 8 of the 128 keys
+//   ls:    lse * log2(e) of the block's queries (+inf past L or for a row without softmax)
+//   dl:    delta of the block's queries
+// Queries past L read as zero rows with ls = +inf, so they add nothing; keys
+// past L are computed on zero rows and never stored.
+// ---------------------------------------------------------------------------
+struct KvBuf {
+    uint4 q[kKB * 4];
+    uint4 dout[kKB * 4];
+    uint4 pt[kKB * 16];
+    float ls[kKB];
+    float dl[kKB];
+};
+
+template <class E, int D, bool PAIR, bool MASK>
+__global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
+    using V8 = typename E::v8;
+    constexpr int kDC = D / 8;
+    constexpr int kDHT = (D + 15) / 16;
+    __shared__ __attribute__((aligned(16))) KvBuf sm[2];
+
+    const uint32_t id = (uint32_t)logical_block(blockIdx.x, p.total);
+    const uint32_t r1 = fdiv(id, p.rblocks), r2 = fdiv(r1, p.nd);
+    const int64_t kb = id - r1 * p.rblocks.d;
+    const int64_t n = r1 - r2 * p.nd.d, b = r2;
+    const int L = (int)p.L, H = (int)p.H;
+    const int64_t HD = p.H * D;
+    const int64_t bn = b * p.N + n;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int c = lane & 15, g = lane >> 4;
+    const int nqb = (L + kKB - 1) / kKB;  // query blocks per head
+    const int nsteps = H * nqb;
+    const uint32_t rowb = (uint32_t)HD * 2;
+    const uint32_t span = (uint32_t)L * rowb;  // below 2^31: the launcher bounds L * H * D * 2
+    const int64_t base = bn * p.L * HD;        // element (b, n, 0, 0, 0)
+    const Rsrc rq = make_rsrc(p.q + base, span);
+    const Rsrc rk = make_rsrc(p.k + base, span);
+    const Rsrc rv = make_rsrc(p.v + base, span);
+    const Rsrc rdo = make_rsrc(p.dout + base, span);
+    const int kw0 = (int)kb * kBlockRows + wave * kWaveRows;  // first key of the wave
+
+    // per-key mask term (base 2), constant over heads and queries
+    float mk[2] = {0.f, 0.f};
+    if (MASK)
+        for (int t = 0; t < 2; ++t) {
+            const int j = kw0 + 16 * t + c;
+            mk[t] = j < L ? E::widen(p.mask[bn * p.L + j]) * kLog2e : 0.f;
+        }
+
+    // copies of step `it` (head it / nqb, queries 64 (it % nqb) ..)
+    const uint32_t qdchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+    const uint32_t qdo = qdchunk < kDC ? (uint32_t)(16 * wave + (lane >> 2)) * rowb + 16u * qdchunk : kOOB;
+    uint32_t pvo[4];
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t row = (uint32_t)(16 * wave + 4 * j + (lane >> 4));
+        pvo[j] = row * (uint32_t)L * 2u + (uint32_t)kb * kBlockRows * 2u + 16u * ((lane & 15) ^ (2 * (row & 7)));
+    }
+    float lsv = 0.f, dlv = 0.f;  // wave 0: this lane's query of the step being copied
+    auto copy_block = [&](int it, KvBuf* __restrict__ dst) {
+        const int h = it / nqb, q0 = (it - h * nqb) * kKB;
+        const uint32_t hoff = (uint32_t)h * D * 2u;
+        dma16(rq, &dst->q[64 * wave], qdo + (uint32_t)q0 * rowb + hoff, 0);
+        dma16(rdo, &dst->dout[64 * wave], qdo + (uint32_t)q0 * rowb + hoff, 0);
+        if (PAIR) {
+            const Rsrc rp = make_rsrc(p.pair + (b * p.H + h) * p.L * p.L, (uint32_t)L * (uint32_t)L * 2u);
+            for (int j = 0; j < 4; ++j)
+                dma16(rp, &dst->pt[64 * (4 * wave + j)], pvo[j] + (uint32_t)q0 * (uint32_t)L * 2u, 0);
+        }
+        if (wave == 0) {
+            const int i = q0 + lane;
+            const int64_t row = (bn * p.H + h) * p.L + i;
+            lsv = i < L ? lse_base2(p.lse[row]) : INFINITY;
+            dlv = i < L ? p.delta[row] : 0.f;
+        }
+    };
+    auto put_rows = [&](KvBuf* __restrict__ dst) {
+        if (wave == 0) {
+            dst->ls[lane] = lsv;
+            dst->dl[lane] = dlv;
+        }
+    };
+
+    V8 kop[2], vop[2];
+    f32x4 dkacc[2][2], dvacc[2][2];
+    float dm[2] = {0.f, 0.f};
+
+    copy_block(0, &sm[0]);
+    put_rows(&sm[0]);
+    wait_all();
+    __syncthreads();
+
+    for (int it = 0; it < nsteps; ++it) {
+        const KvBuf* __restrict__ cur = &sm[it & 1];
+        KvBuf* __restrict__ nxt = &sm[(it & 1) ^ 1];
+        const int h = it / nqb, qbk = it - h * nqb;
+        if (qbk == 0) {
+            for (int t = 0; t < 2; ++t) {
+                const uint32_t j = (uint32_t)(kw0 + 16 * t + c);
+                const uint32_t off = g < kDC ? j * rowb + 16u * g : kOOB;
+                kop[t] = as_v8<E>(bload16(rk, off + (uint32_t)h * D * 2u, 0));
+                vop[t] = as_v8<E>(bload16(rv, off + (uint32_t)h * D * 2u, 0));
+                for (int dh = 0; dh < 2; ++dh) dkacc[t][dh] = dvacc[t][dh] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        // A operands: Q and dO rows (query 16qt + c, chunk g); transposed Q and dO
+        // for the products over queries (column 16dh + c over queries 32cc + 4g
+        // + 0..3 and 32cc + 16 + 4g + 0..3)
+        V8 aq[kKT], ado[kKT], qtr[2][2], dotr[2][2];
+        for (int qt = 0; qt < kKT; ++qt) {
+            aq[qt] = as_v8<E>(cur->q[64 * qt + 4 * c + (g ^ ((c >> 2) & 3))]);
+            ado[qt] = as_v8<E>(cur->dout[64 * qt + 4 * c + (g ^ ((c >> 2) & 3))]);
+        }
+        for (int cc = 0; cc < 2; ++cc)
+            for (int dh = 0; dh < kDHT; ++dh) {
+                const int row = 32 * cc + 4 * g + (c >> 2);
+                const int chunk = (2 * dh + ((c & 3) >> 1)) ^ g;
+                const int off = 16 * (4 * row + chunk) + 8 * (c & 1);
+                const char* bq = reinterpret_cast<const char*>(cur->q) + off;
+                const char* bd = reinterpret_cast<const char*>(cur->dout) + off;
+                const uint2 ql = ds_read_tr(bq), qh = ds_read_tr(bq + 16 * 4 * 16);
+                const uint2 dl = ds_read_tr(bd), dhh = ds_read_tr(bd + 16 * 4 * 16);
+                qtr[cc][dh] = as_v8<E>(uint4{ql.x, ql.y, qh.x, qh.y});
+                dotr[cc][dh] = as_v8<E>(uint4{dl.x, dl.y, dhh.x, dhh.y});
+            }
+        // pair bias of lane (c + 16g): queries 16qt + 4g + 0..3, key 16t + c of the wave
+        uint2 pb[kKT][2];
+        if (PAIR)
+            for (int qt = 0; qt < kKT; ++qt)
+                for (int t = 0; t < 2; ++t) {
+                    const int row = 16 * qt + 4 * g + (c >> 2);
+                    const int chunk = 4 * wave + 2 * t + ((c & 3) >> 1);
+                    pb[qt][t] = ds_read_tr(reinterpret_cast<const char*>(&cur->pt[16 * row + (chunk ^ (2 * (row & 7)))]) +
+                                           8 * (c & 1));
+                }
+        float4 lsq[kKT], dlq[kKT];
+        for (int qt = 0; qt < kKT; ++qt) {
+            lsq[qt] = *reinterpret_cast<const float4*>(&cur->ls[16 * qt + 4 * g]);
+            dlq[qt] = *reinterpret_cast<const float4*>(&cur->dl[16 * qt + 4 * g]);
+        }
+
+        if (it + 1 < nsteps) copy_block(it + 1, nxt);
+
+        f32x4 sc[kKT][2], dp[kKT][2];
+        for (int qt = 0; qt < kKT; ++qt)
+            for (int t = 0; t < 2; ++t) {
+                sc[qt][t] = E::mfma(aq[qt], kop[t], f32x4{0.f, 0.f, 0.f, 0.f});
+                dp[qt][t] = E::mfma(ado[qt], vop[t], f32x4{0.f, 0.f, 0.f, 0.f});
+            }
+        // lane (c + 16g) holds S[query 16qt + 4g + r][key 16t + c]
+        V8 pm[2][2], dsm[2][2];
+        for (int t = 0; t < 2; ++t) {
+            uint32_t wp[8], wd[8];
+            for (int qt = 0; qt < kKT; ++qt) {
+                const float lsr[4] = {lsq[qt].x, lsq[qt].y, lsq[qt].z, lsq[qt].w};
+                const float dlr[4] = {dlq[qt].x, dlq[qt].y, dlq[qt].z, dlq[qt].w};
+                float bias[4] = {0.f, 0.f, 0.f, 0.f};
+                if (PAIR) {
+                    const f32x2 a01 = unpack2<E>(pb[qt][t].x), a23 = unpack2<E>(pb[qt][t].y);
+                    bias[0] = a01[0], bias[1] = a01[1], bias[2] = a23[0], bias[3] = a23[1];
+                }
+                float pr[4], ds[4];
+                for (int r = 0; r < 4; ++r) {
+                    const float x = fmaf(sc[qt][t][r], p.c1, fmaf(bias[r], kLog2e, mk[t] - lsr[r]));
+                    pr[r] = __builtin_amdgcn_exp2f(x);
+                    ds[r] = pr[r] * (dp[qt][t][r] - dlr[r]);
+                    dm[t] += ds[r];
+                }
+                wp[2 * qt] = pack2<E>(pr[0], pr[1]);
+                wp[2 * qt + 1] = pack2<E>(pr[2], pr[3]);
+                wd[2 * qt] = pack2<E>(ds[0], ds[1]);
+                wd[2 * qt + 1] = pack2<E>(ds[2], ds[3]);
+            }
+            // element e of 32-query chunk cc is query 32cc + 16(e/4) + 4g + e%4
+            pm[t][0] = as_v8<E>(uint4{wp[0], wp[1], wp[2], wp[3]});
+            pm[t][1] = as_v8<E>(uint4{wp[4], wp[5], wp[6], wp[7]});
+            dsm[t][0] = as_v8<E>(uint4{wd[0], wd[1], wd[2], wd[3]});
+            dsm[t][1] = as_v8<E>(uint4{wd[4], wd[5], wd[6], wd[7]});
+        }
+        for (int cc = 0; cc < 2; ++cc)
+            for (int dh = 0; dh < kDHT; ++dh)
+                for (int t = 0; t < 2; ++t) {
+                    dvacc[t][dh] = E::mfma(dotr[cc][dh], pm[t][cc], dvacc[t][dh]);
+                    dkacc[t][dh] = E::mfma(qtr[cc][dh], dsm[t][cc], dkacc[t][dh]);
+                }
+
+        if (it + 1 < nsteps) put_rows(nxt);
+        wait_all();
+        __syncthreads();
+
+        if (qbk == nqb - 1) {
+            // lane (c + 16g) holds dK^T, dV^T[d = 16dh + 4g + r][key 16t + c]
+            for (int t = 0; t < 2; ++t) {
+                const int64_t j = kw0 + 16 * t + c;
+                if (j >= L) continue;
+                for (int dh = 0; dh < kDHT; ++dh) {
+                    if (16 * dh + 4 * g >= D) continue;
+                    const int64_t o = base + j * HD + (int64_t)h * D + 16 * dh + 4 * g;
+                    const f32x4 dk = dkacc[t][dh] * p.scale, dv = dvacc[t][dh];
+                    *reinterpret_cast<uint2*>(p.dk + o) = uint2{pack2<E>(dk[0], dk[1]), pack2<E>(dk[2], dk[3])};
+                    *reinterpret_cast<uint2*>(p.dv + o) = uint2{pack2<E>(dv[0], dv[1]), pack2<E>(dv[2], dv[3])};
+                }
+            }
+        }
+    }
+    if (MASK && p.dmask)
+        for (int t = 0; t < 2; ++t) {
+            const float tot = sum_over_groups(dm[t]);
+            const int j = kw0 + 16 * t + c;
+            if (g == 0 && j < L) {
+                const uint32_t w = pack2<E>(tot, 0.f);
+                p.dmask[bn * p.L + j] = (u16)(w & 0xffffu);
+            }
+        }
+}
+
+template <class E, int D, bool PAIR, bool MASK>
+hipError_t launch_dkdv(Params& p, int64_t B, hipStream_t stream) {
+    const int64_t rblocks = (p.L + kBlockRows - 1) / kBlockRows;
+    p.total = B * p.N * rblocks;
+    if (p.total >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
+    p.rblocks = make_fastdiv((uint32_t)rblocks);
+    void* args[] = {&p};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_mfma<E, D, PAIR, MASK>), dim3((unsigned)p.total),
+                           dim3(kWaves * 64), args, 0, stream);
+}
+
 template <class E, int D, bool PAIR, bool MASK>
 hipError_t launch_dq(Params& p, int64_t B, hipStream_t stream) {
     const int64_t rblocks = (p.L + kBlockRows - 1) / kBlockRows;
@@ -377,6 +614,12 @@ hipError_t launch_dim(const BwdArgs& a, unsigned stages, hipStream_t stream) {
         else if (mask) e = launch_dq<E, D, false, true>(p, a.B, stream);
         else e = launch_dq<E, D, false, false>(p, a.B, stream);
     }
+    if (e == hipSuccess && (stages & kStageDkDv)) {
+        if (pair && mask) e = launch_dkdv<E, D, true, true>(p, a.B, stream);
+        else if (pair) e = launch_dkdv<E, D, true, false>(p, a.B, stream);
+        else if (mask) e = launch_dkdv<E, D, false, true>(p, a.B, stream);
+        else e = launch_dkdv<E, D, false, false>(p, a.B, stream);
+    }
     return e;
 }
 
@@ -392,7 +635,7 @@ hipError_t launch_format(const BwdArgs& a, unsigned stages, hipStream_t stream) 
 
 }  // namespace
 
-const unsigned kBwdMfmaStages = kStageDq;
+const unsigned kBwdMfmaStages = kStageDq | kStageDkDv;
 
 bool bwd_mfma_eligible(const BwdArgs& a, int dtype) {
     constexpr int64_t kMax = int64_t(1) << 31;

@@ -264,3 +264,33 @@ def test_bwd_ds4sci_unit_test_shape(torch_dev):
     """The guide's unit test checks every gradient on (1,256,256,4,32) with both biases (section 4)."""
     w = S.random_problem(1, 256, 256, 4, 32, dtype="f16", seed=4053, mask="tail", pair="normal", mask_frac=0.1)
     parity(torch_dev, w, S.random_dout(w.shape, "f16", seed=4054))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("L", [200, 72])
+def test_bwd_rows_past_L_read_as_zero(torch_dev, dtype, L):
+    """Rows past L are never read from memory: with NaN right after every input and L not a multiple of
+    the 64-row block, every gradient stays finite and matches the oracle."""
+    torch = torch_dev
+    import evoformer_biased_attention_amd as E
+    B, N, H, D = 1, 2, 2, 32
+    w = S.random_problem(B, N, L, H, D, dtype=dtype, seed=43 + L, mask="tail", pair="normal", mask_frac=0.2)
+    dout = S.random_dout(w.shape, dtype, seed=44)
+    extra = 128 * H * D + 128 * L
+
+    def dev(x):
+        t = to_dev(torch, x, dtype)
+        buf = torch.full((t.numel() + extra,), float("nan"), dtype=t.dtype, device="cuda")
+        buf[: t.numel()] = t.reshape(-1)
+        return buf[: t.numel()].view(t.shape)
+
+    q, k, v, m, p, do = (dev(x) for x in (w.q, w.k, w.v, w.mask, w.pair, dout))
+    out, lse = E.fwd(q, k, v, m, p)
+    o2 = torch.full((out.numel() + extra,), float("nan"), dtype=out.dtype, device="cuda")
+    o2[: out.numel()] = out.reshape(-1)
+    out = o2[: out.numel()].view(out.shape)
+    grads = E.bwd(q, k, v, m, p, out, lse, do)[:5]
+    torch.cuda.synchronize()
+    got = [f64(g) for g in grads]
+    want = list(oracle.bwd(w.q, w.k, w.v, w.mask, w.pair, dout, dtype=dtype, nthreads=THREADS))
+    compare_grads(got, want, dtype, f"NaN after every input, L={L}")

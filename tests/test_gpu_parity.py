@@ -300,3 +300,29 @@ def test_errors_write_nothing(torch_dev):
     assert bool((out == 7.0).all())
     with pytest.raises(E.EvoAttnError):
         E.fwd(q, q, q)
+
+
+def nan_tailed(torch, x, dtype, extra):
+    """x on the device at the very end of its allocation's useful part: `extra` NaN elements follow it."""
+    t = to_dev(torch, x, dtype)
+    buf = torch.full((t.numel() + extra,), float("nan"), dtype=t.dtype, device="cuda")
+    buf[: t.numel()] = t.reshape(-1)
+    return buf[: t.numel()].view(t.shape)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_rows_past_L_read_as_zero(torch_dev, dtype):
+    """Operand rows past L are never read from memory: with NaN right after every input (L = 200 ends in a
+    partial 64-key block), the outputs stay finite and match the oracle."""
+    torch = torch_dev
+    import evoformer_biased_attention_amd as E
+    B, N, L, H, D = 1, 2, 200, 2, 32
+    w = S.random_problem(B, N, L, H, D, dtype=dtype, seed=41, mask="tail", pair="normal", mask_frac=0.2)
+    extra = 128 * H * D + 128 * L
+    q, k, v, m, p = (nan_tailed(torch, x, dtype, extra) for x in (w.q, w.k, w.v, w.mask, w.pair))
+    out, lse = E.fwd(q, k, v, m, p)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy().astype(np.float64)
+    l = lse.cpu().numpy().astype(np.float64)
+    ro, rl = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype=dtype, nthreads=THREADS)
+    compare(o, l, ro, rl, dtype, "NaN after every input")
