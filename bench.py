@@ -311,9 +311,12 @@ def bench_bwd(args, w, dev, torch, E, S):
         "config": {"workload": w.name, "variant": w.meta.get("variant"), "B": B, "N": N, "L": L, "H": H, "D": D,
                    "mask": w.mask is not None, "pair_bias": w.pair is not None, "mode": args.mode,
                    "input_sets": R, "flop_per_step": flops, "kernels_per_step": 3 if w.pair is not None else 2},
-        # the three kernels run fp32 arithmetic on the vector ALUs: priced against the fp32 vector peak
-        "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_F32_TFLOPS, 4), "traffic": None, "scope": "whole pass"},
+        # 16-bit inputs: every product on the matrix cores, priced against the dense bf16/f16 MFMA peak;
+        # f32 inputs: vector-ALU kernels, priced against the fp32 vector peak
+        "roofline": {"bound": "mfma" if w.dtype != "f32" else "alu", "achieved": round(achieved, 3),
+                     "peak": PEAK_BF16_TFLOPS if w.dtype != "f32" else PEAK_F32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / (PEAK_BF16_TFLOPS if w.dtype != "f32" else PEAK_F32_TFLOPS), 4),
+                     "traffic": None, "scope": "whole pass"},
         "pass_us": round(pass_us, 3),
     }
     if not args.no_cpu_baseline:

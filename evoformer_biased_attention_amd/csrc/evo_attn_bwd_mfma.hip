@@ -571,6 +571,142 @@ hipError_t launch_dkdv(Params& p, int64_t B, hipStream_t stream) {
                            dim3(kWaves * 64), args, 0, stream);
 }
 
+// ---------------------------------------------------------------------------
+// dpair.  Workgroup = one (b, h) tile of 16 kZQ queries x 16 kZK keys; its kZW
+// waves split the N axis (wave w takes n = w, w + kZW, ...), each computing
+// the whole tile per n with scores transposed (S^T = K.Q^T: lane c + 16g
+// holds keys 4g + 0..3 of a key tile for query c of a query tile) and
+// accumulating dS in registers.  The operands of one n come straight from
+// global memory into registers, those of the wave's next n loaded while the
+// current one is processed.  The kZW partial sums are then added in wave
+// order through LDS, so the result does not depend on scheduling.
+// ---------------------------------------------------------------------------
+constexpr int kZW = 8;  // waves per dpair workgroup
+constexpr int kZQ = 2;  // 16-query tiles per dpair workgroup
+constexpr int kZK = 2;  // 16-key tiles per dpair workgroup
+
+template <class E, int D, bool MASK>
+__global__ __launch_bounds__(kZW * 64, 1) void bwd_dpair_mfma(Params p) {
+    using V8 = typename E::v8;
+    constexpr int kDC = D / 8;
+    constexpr int kAcc = kZQ * kZK * 4;  // accumulators per lane
+    __shared__ float red[kZW][kAcc][64];
+
+    // tile order (b, h, query tile, key tile), key tile fastest
+    const uint32_t id = (uint32_t)logical_block(blockIdx.x, p.total);
+    const uint32_t r1 = fdiv(id, p.nd), r2 = fdiv(r1, p.rblocks), r3 = fdiv(r2, p.hd);
+    const int64_t kt0 = id - r1 * p.nd.d;   // nd holds the number of key tiles here
+    const int64_t qt0 = r1 - r2 * p.rblocks.d;
+    const int64_t h = r2 - r3 * p.hd.d, b = r3;
+    const int L = (int)p.L;
+    const int64_t N = p.N, HD = p.H * D;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int c = lane & 15, g = lane >> 4;
+    const int i0 = (int)qt0 * 16 * kZQ, j0 = (int)kt0 * 16 * kZK;
+    const uint32_t rowb = (uint32_t)HD * 2;
+    const uint32_t span = (uint32_t)(L - 1) * rowb + D * 2;
+
+    // pair bias (base 2) of lane c + 16g: query i0 + 16qt + c, keys j0 + 16kt + 4g + 0..3
+    float pb[kZQ][kZK][4];
+    {
+        const u16* pm = p.pair + (b * p.H + h) * p.L * p.L;
+        for (int qt = 0; qt < kZQ; ++qt)
+            for (int kt = 0; kt < kZK; ++kt) {
+                const int i = i0 + 16 * qt + c, j = j0 + 16 * kt + 4 * g;
+                uint2 w = {0u, 0u};
+                if (i < L && j < L) w = *reinterpret_cast<const uint2*>(pm + (int64_t)i * L + j);
+                const f32x2 a = unpack2<E>(w.x), bb = unpack2<E>(w.y);
+                pb[qt][kt][0] = a[0] * kLog2e, pb[qt][kt][1] = a[1] * kLog2e;
+                pb[qt][kt][2] = bb[0] * kLog2e, pb[qt][kt][3] = bb[1] * kLog2e;
+            }
+    }
+
+    struct Ops {
+        V8 k[kZK], v[kZK], q[kZQ], d[kZQ];
+        float ls[kZQ], dl[kZQ];
+        uint2 mk[kZK];
+    };
+    auto load = [&](int64_t n) {
+        Ops o;
+        const int64_t slice = ((b * N + n) * p.L * p.H + h) * D;
+        const Rsrc rk = make_rsrc(p.k + slice, span), rv = make_rsrc(p.v + slice, span);
+        const Rsrc rq = make_rsrc(p.q + slice, span), rd = make_rsrc(p.dout + slice, span);
+        for (int kt = 0; kt < kZK; ++kt) {
+            const uint32_t off = g < kDC ? (uint32_t)(j0 + 16 * kt + c) * rowb + 16u * g : kOOB;
+            o.k[kt] = as_v8<E>(bload16(rk, off, 0));
+            o.v[kt] = as_v8<E>(bload16(rv, off, 0));
+            const int j = j0 + 16 * kt + 4 * g;
+            o.mk[kt] = (MASK && j < L) ? *reinterpret_cast<const uint2*>(p.mask + (b * N + n) * p.L + j) : uint2{0u, 0u};
+        }
+        for (int qt = 0; qt < kZQ; ++qt) {
+            const int i = i0 + 16 * qt + c;
+            const uint32_t off = g < kDC ? (uint32_t)i * rowb + 16u * g : kOOB;
+            o.q[qt] = as_v8<E>(bload16(rq, off, 0));
+            o.d[qt] = as_v8<E>(bload16(rd, off, 0));
+            const int64_t row = ((b * N + n) * p.H + h) * p.L + i;
+            o.ls[qt] = i < L ? lse_base2(p.lse[row]) : INFINITY;
+            o.dl[qt] = i < L ? p.delta[row] : 0.f;
+        }
+        return o;
+    };
+
+    f32x4 acc[kZQ][kZK];
+    for (int qt = 0; qt < kZQ; ++qt)
+        for (int kt = 0; kt < kZK; ++kt) acc[qt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (wave < N) {
+        Ops cur = load(wave);
+        for (int64_t n = wave; n < N; n += kZW) {
+            const Ops nxt = load(n + kZW < N ? n + kZW : n);
+            for (int kt = 0; kt < kZK; ++kt) {
+                float m2[4] = {0.f, 0.f, 0.f, 0.f};
+                if (MASK) {
+                    const f32x2 a = unpack2<E>(cur.mk[kt].x), bb = unpack2<E>(cur.mk[kt].y);
+                    m2[0] = a[0] * kLog2e, m2[1] = a[1] * kLog2e, m2[2] = bb[0] * kLog2e, m2[3] = bb[1] * kLog2e;
+                }
+                for (int qt = 0; qt < kZQ; ++qt) {
+                    const f32x4 sc = E::mfma(cur.k[kt], cur.q[qt], f32x4{0.f, 0.f, 0.f, 0.f});
+                    const f32x4 dp = E::mfma(cur.v[kt], cur.d[qt], f32x4{0.f, 0.f, 0.f, 0.f});
+                    for (int r = 0; r < 4; ++r) {
+                        const float x = fmaf(sc[r], p.c1, pb[qt][kt][r]) + (m2[r] - cur.ls[qt]);
+                        acc[qt][kt][r] = fmaf(__builtin_amdgcn_exp2f(x), dp[r] - cur.dl[qt], acc[qt][kt][r]);
+                    }
+                }
+            }
+            cur = nxt;
+        }
+    }
+
+    // add the waves' partial sums in wave order
+    for (int qt = 0; qt < kZQ; ++qt)
+        for (int kt = 0; kt < kZK; ++kt)
+            for (int r = 0; r < 4; ++r) red[wave][(qt * kZK + kt) * 4 + r][lane] = acc[qt][kt][r];
+    __syncthreads();
+    if (tid < 64 * kZQ * kZK) {
+        const int l = tid & 63, f = tid >> 6, qt = f / kZK, kt = f % kZK;
+        float tot[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < kZW; ++w)
+            for (int r = 0; r < 4; ++r) tot[r] += red[w][4 * f + r][l];
+        const int i = i0 + 16 * qt + (l & 15), j = j0 + 16 * kt + 4 * (l >> 4);
+        if (i < L && j < L)
+            *reinterpret_cast<uint2*>(p.dpair + ((b * p.H + h) * p.L + i) * p.L + j) =
+                uint2{pack2<E>(tot[0], tot[1]), pack2<E>(tot[2], tot[3])};
+    }
+}
+
+template <class E, int D, bool MASK>
+hipError_t launch_dpair(Params p, int64_t B, hipStream_t stream) {
+    const int64_t qtiles = (p.L + 16 * kZQ - 1) / (16 * kZQ), ktiles = (p.L + 16 * kZK - 1) / (16 * kZK);
+    p.total = B * p.H * qtiles * ktiles;
+    if (p.total >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
+    p.rblocks = make_fastdiv((uint32_t)qtiles);
+    p.nd = make_fastdiv((uint32_t)ktiles);  // the dpair kernel decodes key tiles with this divisor
+    void* args[] = {&p};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dpair_mfma<E, D, MASK>), dim3((unsigned)p.total),
+                           dim3(kZW * 64), args, 0, stream);
+}
+
 template <class E, int D, bool PAIR, bool MASK>
 hipError_t launch_dq(Params& p, int64_t B, hipStream_t stream) {
     const int64_t rblocks = (p.L + kBlockRows - 1) / kBlockRows;
@@ -620,6 +756,8 @@ hipError_t launch_dim(const BwdArgs& a, unsigned stages, hipStream_t stream) {
         else if (mask) e = launch_dkdv<E, D, false, true>(p, a.B, stream);
         else e = launch_dkdv<E, D, false, false>(p, a.B, stream);
     }
+    if (e == hipSuccess && (stages & kStageDpair) && a.dpair)
+        e = mask ? launch_dpair<E, D, true>(p, a.B, stream) : launch_dpair<E, D, false>(p, a.B, stream);
     return e;
 }
 
@@ -635,7 +773,7 @@ hipError_t launch_format(const BwdArgs& a, unsigned stages, hipStream_t stream) 
 
 }  // namespace
 
-const unsigned kBwdMfmaStages = kStageDq | kStageDkDv;
+const unsigned kBwdMfmaStages = kStageDq | kStageDkDv | kStageDpair;
 
 bool bwd_mfma_eligible(const BwdArgs& a, int dtype) {
     constexpr int64_t kMax = int64_t(1) << 31;
