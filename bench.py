@@ -81,6 +81,7 @@ def main():
     ap.add_argument("--mode", choices=["cold", "warm"], default="cold")
     ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
                     help="fwd (default): the forward pass; bwd: one evo_attn_bwd call per step, every gradient")
+    ap.add_argument("--no-workspace", action="store_true", help="bwd: run without the pair-gradient workspace")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-time budget of the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-warm", action="store_true", help="skip the secondary warm-cache measurement")
@@ -262,13 +263,17 @@ def bench_bwd(args, w, dev, torch, E, S):
                  None if m is None else torch.empty_like(m), None if p is None else torch.empty_like(p),
                  torch.empty((B, N, H, L), dtype=torch.float32, device="cuda")]
         sets.append((ins, grads))
+    # one workspace serves every step: the steps run one after another on one stream
+    ws_bytes = E.evo_attn_bwd_workspace_size(w.shape, dcode) if not args.no_workspace else 0
+    ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda") if ws_bytes else None
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
     def launch(r):
         (q, k, v, m, p, do, o, l), (dq, dk, dv, dm, dp, delta) = sets[r]
-        return E.evo_attn_bwd(q, k, v, m, p, o, l, do, dq, dk, dv, dm, dp, delta, w.shape, dcode, sh)
+        return E.evo_attn_bwd(q, k, v, m, p, o, l, do, dq, dk, dv, dm, dp, delta, w.shape, dcode, sh,
+                              workspace=ws, workspace_bytes=ws_bytes)
 
     st = launch(0)
     if st != E.EVO_OK:
@@ -310,7 +315,7 @@ def bench_bwd(args, w, dev, torch, E, S):
         "data": "synthetic (seeded; see synthetic/)",
         "config": {"workload": w.name, "variant": w.meta.get("variant"), "B": B, "N": N, "L": L, "H": H, "D": D,
                    "mask": w.mask is not None, "pair_bias": w.pair is not None, "mode": args.mode,
-                   "input_sets": R, "flop_per_step": flops, "kernels_per_step": 3 if w.pair is not None else 2},
+                   "input_sets": R, "flop_per_step": flops, "workspace_bytes": ws_bytes},
         # 16-bit inputs: every product on the matrix cores, priced against the dense bf16/f16 MFMA peak;
         # f32 inputs: vector-ALU kernels, priced against the fp32 vector peak
         "roofline": {"bound": "mfma" if w.dtype != "f32" else "alu", "achieved": round(achieved, 3),

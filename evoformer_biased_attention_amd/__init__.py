@@ -23,8 +23,8 @@ EVO_DTYPE_F32, EVO_DTYPE_BF16, EVO_DTYPE_F16 = 0, 1, 2
  EVO_ERR_UNSUPPORTED, EVO_ERR_HIP, EVO_ERR_NO_BIAS) = range(9)
 
 # Symbols declared in include/evo_attn.h.
-EXPORTED = ("evo_attn_fwd", "evo_attn_check", "evo_attn_bwd", "evo_attn_bwd_check", "evo_status_string",
-            "evo_attn_last_hip_error")
+EXPORTED = ("evo_attn_fwd", "evo_attn_check", "evo_attn_bwd", "evo_attn_bwd_check", "evo_attn_bwd_workspace_size",
+            "evo_status_string", "evo_attn_last_hip_error")
 
 
 class EvoShape(ctypes.Structure):
@@ -59,9 +59,11 @@ def _load():
     lib.evo_attn_check.restype = ctypes.c_int
     lib.evo_attn_check.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(EvoShape), ctypes.c_int]
     lib.evo_attn_bwd.restype = ctypes.c_int
-    lib.evo_attn_bwd.argtypes = [vp] * 14 + [ctypes.POINTER(EvoShape), ctypes.c_int, vp]
+    lib.evo_attn_bwd.argtypes = [vp] * 15 + [ctypes.c_size_t, ctypes.POINTER(EvoShape), ctypes.c_int, vp]
     lib.evo_attn_bwd_check.restype = ctypes.c_int
-    lib.evo_attn_bwd_check.argtypes = [vp] * 14 + [ctypes.POINTER(EvoShape), ctypes.c_int]
+    lib.evo_attn_bwd_check.argtypes = [vp] * 15 + [ctypes.c_size_t, ctypes.POINTER(EvoShape), ctypes.c_int]
+    lib.evo_attn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.evo_attn_bwd_workspace_size.argtypes = [ctypes.POINTER(EvoShape), ctypes.c_int]
     lib.evo_status_string.restype = ctypes.c_char_p
     lib.evo_status_string.argtypes = [ctypes.c_int]
     lib.evo_attn_last_hip_error.restype = ctypes.c_int
@@ -113,19 +115,24 @@ def evo_attn_fwd(q, k, v, mask_bias, pair_bias, out, lse, shape, dtype, stream=N
 
 
 def evo_attn_bwd_check(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias, dpair_bias, delta,
-                       shape, dtype) -> int:
+                       shape, dtype, workspace=None, workspace_bytes=0) -> int:
     """Host-only validation of the backward call; returns the status code."""
     return _lib.evo_attn_bwd_check(*[_addr(x) for x in (q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv,
-                                                       dmask_bias, dpair_bias, delta)],
-                                   ctypes.byref(_shape(shape)), int(dtype))
+                                                       dmask_bias, dpair_bias, delta, workspace)],
+                                   int(workspace_bytes), ctypes.byref(_shape(shape)), int(dtype))
+
+
+def evo_attn_bwd_workspace_size(shape, dtype) -> int:
+    """Bytes of workspace for the fastest backward on this shape (0: none used)."""
+    return int(_lib.evo_attn_bwd_workspace_size(ctypes.byref(_shape(shape)), int(dtype)))
 
 
 def evo_attn_bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias, dpair_bias, delta,
-                 shape, dtype, stream=None) -> int:
+                 shape, dtype, stream=None, workspace=None, workspace_bytes=0) -> int:
     """Enqueue the backward pass; returns the status code (arguments as in include/evo_attn.h)."""
     return _lib.evo_attn_bwd(*[_addr(x) for x in (q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv,
-                                                 dmask_bias, dpair_bias, delta)],
-                             ctypes.byref(_shape(shape)), int(dtype), stream)
+                                                 dmask_bias, dpair_bias, delta, workspace)],
+                             int(workspace_bytes), ctypes.byref(_shape(shape)), int(dtype), stream)
 
 
 def torch_dtype_code(dt) -> int:
@@ -162,8 +169,10 @@ def fwd(q, k, v, mask_bias=None, pair_bias=None, out=None, lse=True, stream=None
     return out, lse_t
 
 
-def bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, want_dmask=True, want_dpair=True, stream=None):
-    """torch convenience wrapper around evo_attn_bwd: allocates the gradients and delta with torch.
+def bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, want_dmask=True, want_dpair=True, stream=None,
+        workspace=True):
+    """torch convenience wrapper around evo_attn_bwd: allocates the gradients, delta and (unless
+    workspace=False) the recommended workspace with torch.
 
     out and lse are the forward pass's results for the same inputs.  Returns
     (dq, dk, dv, dmask_bias or None, dpair_bias or None, delta); a bias
@@ -180,10 +189,16 @@ def bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, want_dmask=True, want_dpa
     dmask = torch.empty_like(mask_bias) if (mask_bias is not None and want_dmask) else None
     dpair = torch.empty_like(pair_bias) if (pair_bias is not None and want_dpair) else None
     delta = torch.empty((B, N, H, L), dtype=torch.float32, device=q.device)
+    code = torch_dtype_code(q.dtype)
+    ws, ws_bytes = None, 0
+    if workspace and dpair is not None:
+        ws_bytes = evo_attn_bwd_workspace_size((B, N, L, H, D), code)
+        if ws_bytes:
+            ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     st = evo_attn_bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask, dpair, delta,
-                      (B, N, L, H, D), torch_dtype_code(q.dtype), stream)
+                      (B, N, L, H, D), code, stream, workspace=ws, workspace_bytes=ws_bytes)
     if st != EVO_OK:
         raise EvoAttnError(st)
     return dq, dk, dv, dmask, dpair, delta

@@ -123,7 +123,8 @@ extern "C" evo_status_t evo_attn_bwd_check(const void* q, const void* k, const v
                                            const void* pair_bias, const void* out, const float* lse,
                                            const void* dout, const void* dq, const void* dk, const void* dv,
                                            const void* dmask_bias, const void* dpair_bias, const float* delta,
-                                           const evo_shape_t* shape, evo_dtype_t dtype) {
+                                           const void* workspace, size_t workspace_bytes, const evo_shape_t* shape,
+                                           evo_dtype_t dtype) {
     if (!shape || !q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !delta)
         return EVO_ERR_NULL_POINTER;
     const int64_t B = shape->B, N = shape->N, L = shape->L, H = shape->H, D = shape->D;
@@ -142,12 +143,14 @@ extern "C" evo_status_t evo_attn_bwd_check(const void* q, const void* k, const v
     for (int64_t s : {B, N, H, L}) row = mul_checked(row, s);
     if (qkv < 0 || msk < 0 || par < 0 || row < 0) return EVO_ERR_BAD_SHAPE;
 
+    if (workspace && workspace_bytes > static_cast<size_t>(kMaxBytes)) return EVO_ERR_BAD_SHAPE;
     for (const void* p : {q, k, v, mask_bias, pair_bias, out, static_cast<const void*>(lse), dout, dq, dk, dv,
-                          dmask_bias, dpair_bias, static_cast<const void*>(delta)})
+                          dmask_bias, dpair_bias, static_cast<const void*>(delta), workspace})
         if (p && !aligned16(p)) return EVO_ERR_MISALIGNED;
 
-    const Extent outs[] = {extent(dq, qkv), extent(dk, qkv), extent(dv, qkv), extent(dmask_bias, msk),
-                           extent(dpair_bias, par), extent(delta, row)};
+    const Extent outs[] = {extent(dq, qkv),        extent(dk, qkv),   extent(dv, qkv),
+                           extent(dmask_bias, msk), extent(dpair_bias, par), extent(delta, row),
+                           extent(workspace, workspace ? static_cast<int64_t>(workspace_bytes) : 0)};
     const Extent ins[] = {extent(q, qkv),         extent(k, qkv),   extent(v, qkv), extent(mask_bias, msk),
                           extent(pair_bias, par), extent(out, qkv), extent(lse, row), extent(dout, qkv)};
     for (size_t a = 0; a < sizeof(outs) / sizeof(outs[0]); ++a) {
@@ -160,15 +163,48 @@ extern "C" evo_status_t evo_attn_bwd_check(const void* q, const void* k, const v
     return EVO_OK;
 }
 
+namespace {
+
+// Workspace chunks the call can use: what the matrix-core path wants, capped
+// by what the given workspace holds (0: none).
+int64_t usable_chunks(const evo_shape_t* s, evo_dtype_t dtype, size_t workspace_bytes) {
+    evo::BwdArgs probe{};
+    probe.B = s->B, probe.N = s->N, probe.L = s->L, probe.H = s->H, probe.D = s->D;
+    if (!evo::bwd_mfma_eligible(probe, static_cast<int>(dtype))) return 0;
+    const int64_t want = evo::bwd_dpair_chunks(s->B, s->N, s->L, s->H);
+    const int64_t per = s->B * s->H * s->L * s->L * 4;  // bytes of one chunk's partial sums
+    const int64_t fit = static_cast<int64_t>(workspace_bytes / static_cast<size_t>(per));
+    const int64_t c = want < fit ? want : fit;
+    return c >= 2 ? c : 0;
+}
+
+}  // namespace
+
+extern "C" size_t evo_attn_bwd_workspace_size(const evo_shape_t* shape, evo_dtype_t dtype) {
+    if (!shape || shape->B < 1 || shape->N < 1 || shape->L < 1 || shape->H < 1 || shape->D < 1) return 0;
+    int64_t par = 4;
+    for (int64_t s : {shape->B, shape->H, shape->L, shape->L}) par = mul_checked(par, s);
+    if (par < 0) return 0;
+    const int64_t c = usable_chunks(shape, dtype, ~static_cast<size_t>(0) >> 2);
+    const int64_t bytes = mul_checked(par, c);
+    return bytes < 0 ? 0 : static_cast<size_t>(bytes);
+}
+
 extern "C" evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v, const void* mask_bias,
                                      const void* pair_bias, const void* out, const float* lse, const void* dout,
                                      void* dq, void* dk, void* dv, void* dmask_bias, void* dpair_bias,
-                                     float* delta, const evo_shape_t* shape, evo_dtype_t dtype, void* stream) {
+                                     float* delta, void* workspace, size_t workspace_bytes, const evo_shape_t* shape,
+                                     evo_dtype_t dtype, void* stream) {
     const evo_status_t st = evo_attn_bwd_check(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv,
-                                               dmask_bias, dpair_bias, delta, shape, dtype);
+                                               dmask_bias, dpair_bias, delta, workspace, workspace_bytes, shape,
+                                               dtype);
     if (st != EVO_OK) return st;
-    evo::BwdArgs a{q,  k,  v,  mask_bias,  pair_bias,  out,   lse,      dout,     dq,       dk,      dv,
-                   dmask_bias, dpair_bias, delta, shape->B, shape->N, shape->L, shape->H, shape->D};
+    evo::BwdArgs a{q,  k,  v,  mask_bias,  pair_bias,  out,   lse,     dout,    dq,      dk,      dv,
+                   dmask_bias, dpair_bias, delta, nullptr, 0, shape->B, shape->N, shape->L, shape->H, shape->D};
+    if (workspace && dpair_bias) {
+        a.ws_chunks = usable_chunks(shape, dtype, workspace_bytes);
+        if (a.ws_chunks) a.ws = static_cast<float*>(workspace);
+    }
     const hipError_t err = evo::launch_bwd(a, static_cast<int>(dtype), static_cast<hipStream_t>(stream));
     if (err == hipSuccess) return EVO_OK;
     g_last_hip_error = static_cast<int>(err);

@@ -707,6 +707,195 @@ hipError_t launch_dpair(Params p, int64_t B, hipStream_t stream) {
                            dim3(kZW * 64), args, 0, stream);
 }
 
+// ---------------------------------------------------------------------------
+// dpair with a workspace.  Workgroup = one (b, h) tile of 64 queries x 64 keys
+// and one chunk of the N axis; all four waves take the same n at a time, so
+// the chunk's Q, dO, K and V rows for the tile are copied into LDS once per n
+// and shared (one block ahead, double buffered).  Wave w owns queries 16w ..
+// 16w+15 against all 64 keys, scores transposed (lane c + 16g holds keys
+// 16kt + 4g + 0..3 of query 16w + c).  Each workgroup writes its chunk's
+// partial sum (fp32) to the workspace; bwd_dpair_reduce then adds the chunks
+// in chunk order.  LDS per step, with the swizzle of the dq kernel:
+//   q, dout, k, v: slot 4*row + (chunk ^ ((row >> 2) & 3)), row of the tile, chunk = 8 d-values
+//   mt: the tile's 64 mask values; ls, dl: lse * log2(e) and delta of the tile's queries
+// ---------------------------------------------------------------------------
+struct PairBuf {
+    uint4 q[64 * 4];
+    uint4 dout[64 * 4];
+    uint4 k[64 * 4];
+    uint4 v[64 * 4];
+    uint4 mt[8];
+    float ls[64];
+    float dl[64];
+};
+
+struct PartParams {
+    Params p;
+    float* ws;        // [chunks][B][H][L][L] fp32
+    int64_t chunks;   // N is split into this many contiguous ranges
+    FastDiv tiles;    // 64 x 64 tiles per (b, h): ceil(L/64)^2
+    FastDiv tdim;     // ceil(L/64)
+    FastDiv chd;      // chunks
+    int64_t bh;       // B * H
+};
+
+template <class E, int D, bool MASK>
+__global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) {
+    using V8 = typename E::v8;
+    constexpr int kDC = D / 8;
+    const Params& p = pp.p;
+    __shared__ __attribute__((aligned(16))) PairBuf sm[2];
+
+    // order (b, h, chunk, query tile, key tile): the tiles of one (b, h, chunk)
+    // run on one XCD together and share each n's rows in its L2
+    const uint32_t id = (uint32_t)logical_block(blockIdx.x, p.total);
+    const uint32_t r1 = fdiv(id, pp.tiles), r2 = fdiv(r1, pp.chd), r3 = fdiv(r2, p.hd);
+    const uint32_t tile = id - r1 * pp.tiles.d;
+    const uint32_t ti = fdiv(tile, pp.tdim), tj = tile - ti * pp.tdim.d;
+    const int64_t chunk = r1 - r2 * pp.chd.d, h = r2 - r3 * p.hd.d, b = r3;
+    const int L = (int)p.L;
+    const int64_t N = p.N, HD = p.H * D;
+    const int64_t n0 = chunk * N / pp.chunks, n1 = (chunk + 1) * N / pp.chunks;
+    const int i0 = (int)ti * 64, j0 = (int)tj * 64;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int c = lane & 15, g = lane >> 4;
+    const uint32_t rowb = (uint32_t)HD * 2;
+    const uint32_t span = (uint32_t)(L - 1) * rowb + D * 2;
+
+    // pair bias (base 2) of lane c + 16g: query i0 + 16 wave + c, keys j0 + 16kt + 4g + 0..3
+    float pb[kKT][4];
+    {
+        const u16* pm = p.pair + (b * p.H + h) * p.L * p.L;
+        const int i = i0 + 16 * wave + c;
+        for (int kt = 0; kt < kKT; ++kt) {
+            const int j = j0 + 16 * kt + 4 * g;
+            uint2 w = {0u, 0u};
+            if (i < L && j < L) w = *reinterpret_cast<const uint2*>(pm + (int64_t)i * L + j);
+            const f32x2 a = unpack2<E>(w.x), bb = unpack2<E>(w.y);
+            pb[kt][0] = a[0] * kLog2e, pb[kt][1] = a[1] * kLog2e, pb[kt][2] = bb[0] * kLog2e, pb[kt][3] = bb[1] * kLog2e;
+        }
+    }
+
+    // copies of step n: rows 16 wave + lane/4 of the tile, chunk (lane & 3) ^ ((lane >> 4) & 3)
+    const uint32_t dchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+    const uint32_t trow = (uint32_t)(16 * wave + (lane >> 2));
+    const uint32_t qoff = dchunk < kDC ? ((uint32_t)i0 + trow) * rowb + 16u * dchunk : kOOB;
+    const uint32_t koff = dchunk < kDC ? ((uint32_t)j0 + trow) * rowb + 16u * dchunk : kOOB;
+    float lsv = 0.f, dlv = 0.f;
+    auto copy_step = [&](int64_t n, PairBuf* __restrict__ dst) {
+        const int64_t slice = ((b * N + n) * p.L * p.H + h) * D;
+        dma16(make_rsrc(p.q + slice, span), &dst->q[64 * wave], qoff, 0);
+        dma16(make_rsrc(p.dout + slice, span), &dst->dout[64 * wave], qoff, 0);
+        dma16(make_rsrc(p.k + slice, span), &dst->k[64 * wave], koff, 0);
+        dma16(make_rsrc(p.v + slice, span), &dst->v[64 * wave], koff, 0);
+        if (MASK && wave == 0 && lane < 8)
+            dma16(make_rsrc(p.mask + (b * N + n) * p.L, (uint32_t)L * 2u), &dst->mt[0], (uint32_t)j0 * 2u + 16u * lane, 0);
+        if (wave == 1) {
+            const int i = i0 + lane;
+            const int64_t row = ((b * N + n) * p.H + h) * p.L + i;
+            lsv = i < L ? lse_base2(p.lse[row]) : INFINITY;
+            dlv = i < L ? p.delta[row] : 0.f;
+        }
+    };
+    auto put_rows = [&](PairBuf* __restrict__ dst) {
+        if (wave == 1) {
+            dst->ls[lane] = lsv;
+            dst->dl[lane] = dlv;
+        }
+    };
+
+    f32x4 acc[kKT];
+    for (int kt = 0; kt < kKT; ++kt) acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    copy_step(n0, &sm[0]);
+    put_rows(&sm[0]);
+    wait_all();
+    __syncthreads();
+    for (int64_t n = n0; n < n1; ++n) {
+        const int it = (int)(n - n0);
+        const PairBuf* __restrict__ cur = &sm[it & 1];
+        PairBuf* __restrict__ nxt = &sm[(it & 1) ^ 1];
+        const int sw = g ^ ((c >> 2) & 3);
+        const V8 qop = as_v8<E>(cur->q[64 * wave + 4 * c + sw]);
+        const V8 dop = as_v8<E>(cur->dout[64 * wave + 4 * c + sw]);
+        V8 kop[kKT], vop[kKT];
+        uint2 mb[kKT];
+        for (int kt = 0; kt < kKT; ++kt) {
+            kop[kt] = as_v8<E>(cur->k[64 * kt + 4 * c + sw]);
+            vop[kt] = as_v8<E>(cur->v[64 * kt + 4 * c + sw]);
+            if (MASK) mb[kt] = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(&cur->mt[2 * kt + (g >> 1)]) + 8 * (g & 1));
+        }
+        const float lsq = cur->ls[16 * wave + c], dlq = cur->dl[16 * wave + c];
+        if (n + 1 < n1) copy_step(n + 1, nxt);
+        for (int kt = 0; kt < kKT; ++kt) {
+            const f32x4 sc = E::mfma(kop[kt], qop, f32x4{0.f, 0.f, 0.f, 0.f});
+            const f32x4 dp = E::mfma(vop[kt], dop, f32x4{0.f, 0.f, 0.f, 0.f});
+            float m2[4] = {0.f, 0.f, 0.f, 0.f};
+            if (MASK) {
+                const f32x2 a = unpack2<E>(mb[kt].x), bb = unpack2<E>(mb[kt].y);
+                m2[0] = a[0] * kLog2e, m2[1] = a[1] * kLog2e, m2[2] = bb[0] * kLog2e, m2[3] = bb[1] * kLog2e;
+            }
+            for (int r = 0; r < 4; ++r) {
+                const float x = fmaf(sc[r], p.c1, pb[kt][r]) + (m2[r] - lsq);
+                acc[kt][r] = fmaf(__builtin_amdgcn_exp2f(x), dp[r] - dlq, acc[kt][r]);
+            }
+        }
+        if (n + 1 < n1) put_rows(nxt);
+        wait_all();
+        __syncthreads();
+    }
+
+    // lane c + 16g: query i0 + 16 wave + c, keys j0 + 16kt + 4g + 0..3
+    const int i = i0 + 16 * wave + c;
+    if (i < L)
+        for (int kt = 0; kt < kKT; ++kt) {
+            const int j = j0 + 16 * kt + 4 * g;
+            if (j < L)
+                *reinterpret_cast<f32x4*>(pp.ws + ((chunk * pp.bh + b * p.H + h) * p.L + i) * p.L + j) = acc[kt];
+        }
+}
+
+// dpair[e] = sum over the workspace's chunks of their partial sums, in chunk
+// order; four consecutive elements per thread (B*H*L*L is a multiple of 8).
+template <class E>
+__global__ __launch_bounds__(256) void bwd_dpair_reduce(const float* __restrict__ ws, u16* __restrict__ dpair,
+                                                        int64_t quads, int64_t chunks) {
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= quads) return;
+    f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int64_t ch = 0; ch < chunks; ++ch) t += reinterpret_cast<const f32x4*>(ws)[ch * quads + q];
+    reinterpret_cast<uint2*>(dpair)[q] = uint2{pack2<E>(t[0], t[1]), pack2<E>(t[2], t[3])};
+}
+
+template <class E, int D, bool MASK>
+hipError_t launch_dpair_ws(const Params& base, int64_t B, float* ws, int64_t chunks, hipStream_t stream) {
+    PartParams pp;
+    pp.p = base;
+    const int64_t tdim = (base.L + 63) / 64;
+    pp.p.total = B * base.H * chunks * tdim * tdim;
+    if (pp.p.total >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
+    pp.ws = ws;
+    pp.chunks = chunks;
+    pp.tiles = make_fastdiv((uint32_t)(tdim * tdim));
+    pp.tdim = make_fastdiv((uint32_t)tdim);
+    pp.chd = make_fastdiv((uint32_t)chunks);
+    pp.bh = B * base.H;
+    void* args[] = {&pp};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dpair_part<E, D, MASK>),
+                                   dim3((unsigned)pp.p.total), dim3(kWaves * 64), args, 0, stream);
+    if (e != hipSuccess) return e;
+    const int64_t quads = B * base.H * base.L * base.L / 4;
+    const int64_t blocks = (quads + 255) / 256;
+    if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
+    const float* wsc = ws;
+    u16* out = base.dpair;
+    int64_t ch = chunks;
+    void* rargs[] = {&wsc, &out, (void*)&quads, &ch};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dpair_reduce<E>), dim3((unsigned)blocks), dim3(256),
+                           rargs, 0, stream);
+}
+
 template <class E, int D, bool PAIR, bool MASK>
 hipError_t launch_dq(Params& p, int64_t B, hipStream_t stream) {
     const int64_t rblocks = (p.L + kBlockRows - 1) / kBlockRows;
@@ -756,8 +945,13 @@ hipError_t launch_dim(const BwdArgs& a, unsigned stages, hipStream_t stream) {
         else if (mask) e = launch_dkdv<E, D, false, true>(p, a.B, stream);
         else e = launch_dkdv<E, D, false, false>(p, a.B, stream);
     }
-    if (e == hipSuccess && (stages & kStageDpair) && a.dpair)
-        e = mask ? launch_dpair<E, D, true>(p, a.B, stream) : launch_dpair<E, D, false>(p, a.B, stream);
+    if (e == hipSuccess && (stages & kStageDpair) && a.dpair) {
+        if (a.ws && a.ws_chunks >= 1)
+            e = mask ? launch_dpair_ws<E, D, true>(p, a.B, a.ws, a.ws_chunks, stream)
+                     : launch_dpair_ws<E, D, false>(p, a.B, a.ws, a.ws_chunks, stream);
+        else
+            e = mask ? launch_dpair<E, D, true>(p, a.B, stream) : launch_dpair<E, D, false>(p, a.B, stream);
+    }
     return e;
 }
 
@@ -774,6 +968,14 @@ hipError_t launch_format(const BwdArgs& a, unsigned stages, hipStream_t stream) 
 }  // namespace
 
 const unsigned kBwdMfmaStages = kStageDq | kStageDkDv | kStageDpair;
+
+int64_t bwd_dpair_chunks(int64_t B, int64_t N, int64_t L, int64_t H) {
+    // about 2048 workgroups (eight per CU), at least 8 values of n per chunk
+    const int64_t tdim = (L + 63) / 64, tiles = B * H * tdim * tdim;
+    int64_t c = (2048 + tiles - 1) / tiles;
+    if (c > N / 8) c = N / 8;
+    return c < 2 ? 0 : c;
+}
 
 bool bwd_mfma_eligible(const BwdArgs& a, int dtype) {
     constexpr int64_t kMax = int64_t(1) << 31;

@@ -42,6 +42,8 @@ struct BwdArgs {
     void* dmask;        // [B,N,1,1,L] or nullptr (only with mask)
     void* dpair;        // [B,1,H,L,L] or nullptr (only with pair)
     float* delta;       // [B,N,H,L], written
+    float* ws;          // workspace for the pair gradient's partial sums, or nullptr
+    int64_t ws_chunks;  // N-chunks the workspace holds ([ws_chunks][B][H][L][L] fp32)
     int64_t B, N, L, H, D;
 };
 
@@ -58,6 +60,9 @@ constexpr unsigned kStageDpair = 4;  // dpair
 // arguments, and a launch of some of those stages in stage order.
 extern const unsigned kBwdMfmaStages;
 bool bwd_mfma_eligible(const BwdArgs& a, int dtype);
+// The number of N-chunks whose pair-gradient partial sums the matrix-core
+// path would like in its workspace (0: no workspace wanted).
+int64_t bwd_dpair_chunks(int64_t B, int64_t N, int64_t L, int64_t H);
 hipError_t launch_bwd_mfma(const BwdArgs& a, int dtype, unsigned stages, hipStream_t stream);
 
 }  // namespace evo

@@ -42,6 +42,7 @@
 #ifndef EVO_ATTN_H
 #define EVO_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -131,6 +132,15 @@ evo_status_t evo_attn_check(const void* q, const void* k, const void* v, const v
  *                its kernel); only with a pair_bias (else EVO_ERR_NO_BIAS)
  *   delta        [B,N,H,L] float32, written with dout_i . out_i (the saved
  *                intermediate of section 5.4); required, owned by the caller
+ *   workspace, workspace_bytes
+ *                optional device scratch for the pair gradient: the pass may
+ *                split the N axis of that sum over more workgroups and keep
+ *                the partial sums there (fp32; they are added in a fixed
+ *                order, so results stay deterministic).  Query the size with
+ *                evo_attn_bwd_workspace_size.  NULL (or fewer bytes than one
+ *                split needs) runs the pass without it, more slowly for small
+ *                B*H*L^2.  Owned by the caller, contents undefined after the
+ *                call; calls that share a workspace must not overlap in time.
  * Every output is overwritten, never accumulated into.  All arithmetic is
  * fp32; results are rounded to nearest-even into `dtype` once, at the end.
  * Sums are formed in a fixed order: the same inputs give bit-identical
@@ -141,12 +151,20 @@ evo_status_t evo_attn_check(const void* q, const void* k, const void* v, const v
  * return EVO_ERR_UNSUPPORTED.  Required pointers: q, k, v, out, lse, dout, dq,
  * dk, dv, delta, shape.  Pointer, ownership, alignment, aliasing and error
  * rules are those of evo_attn_fwd; the outputs (dq, dk, dv, dmask_bias,
- * dpair_bias, delta) may overlap neither an input nor one another.
+ * dpair_bias, delta) and the workspace may overlap neither an input nor one
+ * another.  workspace_bytes above 2^62 is EVO_ERR_BAD_SHAPE.
  */
 evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v, const void* mask_bias,
                           const void* pair_bias, const void* out, const float* lse, const void* dout,
                           void* dq, void* dk, void* dv, void* dmask_bias, void* dpair_bias, float* delta,
-                          const evo_shape_t* shape, evo_dtype_t dtype, void* stream);
+                          void* workspace, size_t workspace_bytes, const evo_shape_t* shape, evo_dtype_t dtype,
+                          void* stream);
+
+/*
+ * Bytes of workspace with which evo_attn_bwd runs fastest for this shape and
+ * dtype (0: it uses none).  Host-only; returns 0 for an invalid shape.
+ */
+size_t evo_attn_bwd_workspace_size(const evo_shape_t* shape, evo_dtype_t dtype);
 
 /*
  * The validation of evo_attn_bwd alone (same arguments minus the stream).
@@ -155,8 +173,8 @@ evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v, const voi
 evo_status_t evo_attn_bwd_check(const void* q, const void* k, const void* v, const void* mask_bias,
                                 const void* pair_bias, const void* out, const float* lse, const void* dout,
                                 const void* dq, const void* dk, const void* dv, const void* dmask_bias,
-                                const void* dpair_bias, const float* delta, const evo_shape_t* shape,
-                                evo_dtype_t dtype);
+                                const void* dpair_bias, const float* delta, const void* workspace,
+                                size_t workspace_bytes, const evo_shape_t* shape, evo_dtype_t dtype);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* evo_status_string(evo_status_t status);

@@ -21,7 +21,8 @@ def _header_text():
 
 
 def test_header_declares_exactly_the_exported_names():
-    decls = set(re.findall(r"^\s*(?:const\s+char\s*\*|evo_status_t|int)\s+(evo_\w+)\s*\(", _header_text(), re.M))
+    decls = set(re.findall(r"^\s*(?:const\s+char\s*\*|evo_status_t|int|size_t)\s+(evo_\w+)\s*\(", _header_text(),
+                           re.M))
     assert decls == set(E.EXPORTED)
 
 
@@ -163,13 +164,14 @@ def test_single_hip_runtime_in_process():
 # evo_attn_bwd_check
 # ---------------------------------------------------------------------------
 BWD_NAMES = ["q", "k", "v", "mask_bias", "pair_bias", "out", "lse", "dout", "dq", "dk", "dv", "dmask_bias",
-             "dpair_bias", "delta"]
+             "dpair_bias", "delta", "workspace"]
 
 
-def bcheck(shape=(1, 2, 64, 4, 32), dtype=E.EVO_DTYPE_BF16, **over):
+def bcheck(shape=(1, 2, 64, 4, 32), dtype=E.EVO_DTYPE_BF16, workspace_bytes=1 << 20, **over):
     args = dict(zip(BWD_NAMES, addrs(len(BWD_NAMES))))
     args.update(over)
-    return E.evo_attn_bwd_check(*[args[n] for n in BWD_NAMES], shape, dtype)
+    return E.evo_attn_bwd_check(*[args[n] for n in BWD_NAMES[:-1]], shape, dtype, workspace=args["workspace"],
+                                workspace_bytes=workspace_bytes)
 
 
 def test_bwd_valid():
@@ -200,7 +202,7 @@ def test_bwd_misaligned(name):
 
 def test_bwd_aliasing():
     a = dict(zip(BWD_NAMES, addrs(len(BWD_NAMES))))
-    for o in ("dq", "dk", "dv", "dmask_bias", "dpair_bias", "delta"):
+    for o in ("dq", "dk", "dv", "dmask_bias", "dpair_bias", "delta", "workspace"):
         for i in ("q", "k", "v", "mask_bias", "pair_bias", "out", "lse", "dout"):
             assert bcheck(**{o: a[i]}) == E.EVO_ERR_ALIASING, (o, i)
     assert bcheck(dk=a["dq"]) == E.EVO_ERR_ALIASING                       # outputs may not share memory
@@ -214,3 +216,27 @@ def test_bwd_bad_shape_dtype_unsupported():
     assert bcheck(dtype=7) == E.EVO_ERR_BAD_DTYPE
     for d in (4, 24, 128):
         assert bcheck(shape=(1, 1, 32, 1, d)) == E.EVO_ERR_UNSUPPORTED
+
+
+def test_bwd_workspace_rules():
+    a = dict(zip(BWD_NAMES, addrs(len(BWD_NAMES))))
+    assert bcheck(workspace=None, workspace_bytes=0) == E.EVO_OK            # the workspace is optional
+    assert bcheck(workspace=None, workspace_bytes=1 << 40) == E.EVO_OK      # size ignored without a pointer
+    assert bcheck(workspace_bytes=0) == E.EVO_OK
+    assert bcheck(workspace=a["workspace"] + 8) == E.EVO_ERR_MISALIGNED
+    assert bcheck(workspace=a["dq"] + 4096) == E.EVO_ERR_ALIASING           # inside dq
+    assert bcheck(workspace=a["dq"] - 4096, workspace_bytes=8192) == E.EVO_ERR_ALIASING  # runs into dq
+    assert bcheck(workspace_bytes=(1 << 62) + 16) == E.EVO_ERR_BAD_SHAPE
+
+
+def test_bwd_workspace_size():
+    """The size is a whole number of fp32 [B,H,L,L] partial-sum planes, at least two, or 0."""
+    plane = lambda B, H, L: B * H * L * L * 4
+    ws = E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 32), E.EVO_DTYPE_BF16)
+    assert ws > 0 and ws % plane(1, 4, 384) == 0 and ws // plane(1, 4, 384) >= 2
+    assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 32), E.EVO_DTYPE_F16) == ws
+    assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 32), E.EVO_DTYPE_F32) == 0    # vector-ALU path
+    assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 64), E.EVO_DTYPE_BF16) == 0   # vector-ALU path
+    assert E.evo_attn_bwd_workspace_size((1, 8, 384, 4, 32), E.EVO_DTYPE_BF16) == 0     # N too small to split
+    assert E.evo_attn_bwd_workspace_size((1, 384, 100, 4, 32), E.EVO_DTYPE_BF16) == 0   # L % 8 != 0
+    assert E.evo_attn_bwd_workspace_size((0, 384, 384, 4, 32), E.EVO_DTYPE_BF16) == 0

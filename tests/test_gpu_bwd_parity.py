@@ -80,8 +80,9 @@ def fwd_supported(dtype, D):
     return D in (8, 16, 32) or (dtype == "f32" and D == 64)
 
 
-def run_bwd(torch, w, dout, want_dmask=True, want_dpair=True, fwd_from_oracle=False, stream=None):
-    """Forward (HIP, or the oracle where the HIP forward lacks the shape), then the HIP backward.
+def run_bwd(torch, w, dout, want_dmask=True, want_dpair=True, fwd_from_oracle=False, stream=None, use_ws=True):
+    """Forward (HIP, or the oracle where the HIP forward lacks the shape), then the HIP backward, with the
+    recommended workspace (NaN-filled) unless use_ws is False.
 
     Returns (grads as float64 numpy [dq, dk, dv, dmask|None, dpair|None], delta, out).
     """
@@ -101,11 +102,14 @@ def run_bwd(torch, w, dout, want_dmask=True, want_dpair=True, fwd_from_oracle=Fa
     dpair = torch.full_like(pair, float("nan")) if (pair is not None and want_dpair) else None
     delta = torch.full((B, N, H, L), float("nan"), dtype=torch.float32, device="cuda")
     code = E.torch_dtype_code(q.dtype)
+    ws_bytes = E.evo_attn_bwd_workspace_size(w.shape, code) if use_ws else 0
+    ws = torch.full((ws_bytes // 4,), float("nan"), dtype=torch.float32, device="cuda") if ws_bytes else None
     say(f"  bwd {w.name} shape={w.shape} dtype={w.dtype} mask={mask is not None} pair={pair is not None} "
-        f"dmask={dmask is not None} dpair={dpair is not None}")
+        f"dmask={dmask is not None} dpair={dpair is not None} workspace={ws_bytes}")
     if stream is None:
         stream = torch.cuda.current_stream().cuda_stream
-    st = E.evo_attn_bwd(q, k, v, mask, pair, out, lse, do, dq, dk, dv, dmask, dpair, delta, w.shape, code, stream)
+    st = E.evo_attn_bwd(q, k, v, mask, pair, out, lse, do, dq, dk, dv, dmask, dpair, delta, w.shape, code, stream,
+                        workspace=ws, workspace_bytes=ws_bytes)
     assert st == E.EVO_OK, E.evo_status_string(st)
     torch.cuda.synchronize()
     return [f64(x) for x in (dq, dk, dv, dmask, dpair)], f64(delta), f64(out)
@@ -136,6 +140,7 @@ def compare_delta(delta, w, dout, what):
 
 
 def parity(torch, w, dout, want_dmask=True, want_dpair=True, **kw):
+    """HIP backward vs the oracle's; returns the HIP gradients."""
     got, delta, _ = run_bwd(torch, w, dout, want_dmask, want_dpair, **kw)
     want = list(oracle.bwd(w.q, w.k, w.v, w.mask, w.pair, dout, dtype=w.dtype, want_dmask=want_dmask,
                            want_dpair=want_dpair, nthreads=THREADS))
@@ -294,3 +299,34 @@ def test_bwd_rows_past_L_read_as_zero(torch_dev, dtype, L):
     got = [f64(g) for g in grads]
     want = list(oracle.bwd(w.q, w.k, w.v, w.mask, w.pair, dout, dtype=dtype, nthreads=THREADS))
     compare_grads(got, want, dtype, f"NaN after every input, L={L}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("L", [64, 72, 136, 200])
+def test_bwd_pair_gradient_split_over_n(torch_dev, dtype, L):
+    """N large enough for the workspace path (the N axis of the pair gradient split over workgroups and the
+    partial sums added in order), L with partial 64-row tiles; the same gradients without a workspace."""
+    import evoformer_biased_attention_amd as E
+    w = S.random_problem(1, 24, L, 3, 32, dtype=dtype, seed=L + 7, mask="tail", pair="normal", mask_frac=0.2)
+    assert E.evo_attn_bwd_workspace_size(w.shape, E.torch_dtype_code(
+        torch_dev.bfloat16 if dtype == "bf16" else torch_dev.float16)) > 0
+    dout = S.random_dout(w.shape, dtype, seed=L + 8)
+    split = parity(torch_dev, w, dout)
+    single = parity(torch_dev, w, dout, use_ws=False)
+    for a, b in zip(split[:4], single[:4]):
+        np.testing.assert_array_equal(a, b)   # only the pair gradient takes another route
+
+
+def test_bwd_workspace_deterministic(torch_dev):
+    w = S.random_problem(1, 40, 96, 2, 32, dtype="bf16", seed=61, mask="tail", pair="normal")
+    dout = S.random_dout(w.shape, "bf16", seed=62)
+    a, _, _ = run_bwd(torch_dev, w, dout)
+    b, _, _ = run_bwd(torch_dev, w, dout)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("c", [2, 4])
+def test_bwd_workload_without_workspace(torch_dev, c):
+    w = S.workload(c)
+    parity(torch_dev, w, S.random_dout(w.shape, w.dtype, seed=100 + c), use_ws=False)
