@@ -82,6 +82,9 @@ def main():
     ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
                     help="fwd (default): the forward pass; bwd: one evo_attn_bwd call per step, every gradient")
     ap.add_argument("--no-workspace", action="store_true", help="bwd: run without the pair-gradient workspace")
+    ap.add_argument("--layout", choices=["dense", "transposed"], default="dense",
+                    help="fwd: transposed stores Q/K/V/O as X[B, L, N, H, D] and reads them in place through "
+                         "evo_attn_fwd_strided (triangle attention around the ending node without a copy)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-time budget of the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-warm", action="store_true", help="skip the secondary warm-cache measurement")
@@ -134,10 +137,14 @@ def main():
         return bench_bwd(args, w, dev, torch, E, S)
 
     base = [dev(x) for x in (w.q, w.k, w.v, w.mask, w.pair)]
+    if args.layout == "transposed":
+        # X[B, L, N, H, D] in memory; the kernel sees its [B, N, L, H, D] view
+        base[:3] = [t.permute(0, 2, 1, 3, 4).contiguous().permute(0, 2, 1, 3, 4) for t in base[:3]]
     set_bytes = sum(t.numel() * t.element_size() for t in base if t is not None) * 4 // 3 + B * N * H * L * 4
     R = 1 if args.mode == "warm" else max(2, math.ceil(2.5 * MALL_BYTES / set_bytes))
     sets = []
     for r in range(R):
+        # clone keeps the strides (preserve_format), so every copy has the chosen layout
         ins = [t if (t is None or r == 0) else t.clone() for t in base]
         out = torch.empty_like(base[0])
         lse = torch.empty((B, N, H, L), dtype=torch.float32, device="cuda")
@@ -145,10 +152,13 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+    layouts = [E.layout_of(s_[0], s_[1], s_[2], s_[5], s_[3], s_[4]) for s_ in sets]
 
     def launch(r):
         q, k, v, m, p, o, l = sets[r]
-        return E.evo_attn_fwd(q, k, v, m, p, o, l, w.shape, dcode, sh)
+        if args.layout == "dense":
+            return E.evo_attn_fwd(q, k, v, m, p, o, l, w.shape, dcode, sh)
+        return E.evo_attn_fwd_strided(q, k, v, m, p, o, l, layouts[r], w.shape, dcode, sh)
 
     st = launch(0)
     if st != E.EVO_OK:
@@ -222,7 +232,7 @@ def main():
         "data": "synthetic (seeded; see synthetic/)",
         "config": {"workload": w.name, "variant": w.meta.get("variant"), "B": B, "N": N, "L": L, "H": H, "D": D,
                    "mask": w.mask is not None, "pair_bias": w.pair is not None, "mode": args.mode,
-                   "input_sets": R, "flop_per_step": flops},
+                   "input_sets": R, "flop_per_step": flops, "layout": args.layout},
         "pct_of_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic},

@@ -23,13 +23,22 @@ EVO_DTYPE_F32, EVO_DTYPE_BF16, EVO_DTYPE_F16 = 0, 1, 2
  EVO_ERR_UNSUPPORTED, EVO_ERR_HIP, EVO_ERR_NO_BIAS) = range(9)
 
 # Symbols declared in include/evo_attn.h.
-EXPORTED = ("evo_attn_fwd", "evo_attn_check", "evo_attn_bwd", "evo_attn_bwd_check", "evo_attn_bwd_workspace_size",
+EXPORTED = ("evo_attn_fwd", "evo_attn_check", "evo_attn_fwd_strided", "evo_attn_check_strided",
+            "evo_attn_dense_layout", "evo_attn_bwd", "evo_attn_bwd_check", "evo_attn_bwd_workspace_size",
             "evo_status_string", "evo_attn_last_hip_error")
 
 
 class EvoShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("N", ctypes.c_int64), ("L", ctypes.c_int64), ("H", ctypes.c_int64),
                 ("D", ctypes.c_int64)]
+
+
+class EvoLayout(ctypes.Structure):
+    """evo_layout_t: element strides (q, k, v, out: b, n, l, h; biases; lse rows)."""
+    _fields_ = [("q", ctypes.c_int64 * 4), ("k", ctypes.c_int64 * 4), ("v", ctypes.c_int64 * 4),
+                ("out", ctypes.c_int64 * 4), ("mask_b", ctypes.c_int64), ("mask_n", ctypes.c_int64),
+                ("pair_b", ctypes.c_int64), ("pair_h", ctypes.c_int64), ("pair_i", ctypes.c_int64),
+                ("lse_row", ctypes.c_int64)]
 
 
 class EvoAttnError(RuntimeError):
@@ -58,6 +67,13 @@ def _load():
     lib.evo_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(EvoShape), ctypes.c_int, vp]
     lib.evo_attn_check.restype = ctypes.c_int
     lib.evo_attn_check.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(EvoShape), ctypes.c_int]
+    lib.evo_attn_fwd_strided.restype = ctypes.c_int
+    lib.evo_attn_fwd_strided.argtypes = [vp] * 7 + [ctypes.POINTER(EvoLayout), ctypes.POINTER(EvoShape), ctypes.c_int,
+                                                    vp]
+    lib.evo_attn_check_strided.restype = ctypes.c_int
+    lib.evo_attn_check_strided.argtypes = [vp] * 7 + [ctypes.POINTER(EvoLayout), ctypes.POINTER(EvoShape), ctypes.c_int]
+    lib.evo_attn_dense_layout.restype = None
+    lib.evo_attn_dense_layout.argtypes = [ctypes.POINTER(EvoShape), ctypes.POINTER(EvoLayout)]
     lib.evo_attn_bwd.restype = ctypes.c_int
     lib.evo_attn_bwd.argtypes = [vp] * 15 + [ctypes.c_size_t, ctypes.POINTER(EvoShape), ctypes.c_int, vp]
     lib.evo_attn_bwd_check.restype = ctypes.c_int
@@ -133,6 +149,48 @@ def evo_attn_bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmas
     return _lib.evo_attn_bwd(*[_addr(x) for x in (q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv,
                                                  dmask_bias, dpair_bias, delta, workspace)],
                              int(workspace_bytes), ctypes.byref(_shape(shape)), int(dtype), stream)
+
+
+def evo_attn_dense_layout(shape) -> EvoLayout:
+    """The dense layout of `shape` (what evo_attn_fwd assumes)."""
+    lay = EvoLayout()
+    _lib.evo_attn_dense_layout(ctypes.byref(_shape(shape)), ctypes.byref(lay))
+    return lay
+
+
+def evo_attn_check_strided(q, k, v, mask_bias, pair_bias, out, lse, layout, shape, dtype) -> int:
+    """Host-only validation of the strided call; returns the status code."""
+    return _lib.evo_attn_check_strided(_addr(q), _addr(k), _addr(v), _addr(mask_bias), _addr(pair_bias), _addr(out),
+                                       _addr(lse), ctypes.byref(layout), ctypes.byref(_shape(shape)), int(dtype))
+
+
+def evo_attn_fwd_strided(q, k, v, mask_bias, pair_bias, out, lse, layout, shape, dtype, stream=None) -> int:
+    """Enqueue the forward pass on strided tensors; returns the status code."""
+    return _lib.evo_attn_fwd_strided(_addr(q), _addr(k), _addr(v), _addr(mask_bias), _addr(pair_bias), _addr(out),
+                                     _addr(lse), ctypes.byref(layout), ctypes.byref(_shape(shape)), int(dtype), stream)
+
+
+def layout_of(q, k, v, out, mask_bias=None, pair_bias=None, lse_row=None) -> EvoLayout:
+    """evo_layout_t from torch tensors viewed as [B,N,L,H,D] (d contiguous), [B,N,1,1,L] and [B,1,H,L,L]
+    (keys contiguous); lse_row defaults to L."""
+    lay = EvoLayout()
+    L = q.shape[2]
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if t.stride(4) != 1:
+            raise ValueError(f"{name}: the head dimension must be contiguous")
+        getattr(lay, name)[:] = [t.stride(0), t.stride(1), t.stride(2), t.stride(3)]
+    if mask_bias is not None:
+        if mask_bias.stride(4) != 1:
+            raise ValueError("mask_bias: keys must be contiguous")
+        lay.mask_b, lay.mask_n = mask_bias.stride(0), mask_bias.stride(1)
+    if pair_bias is not None:
+        if pair_bias.stride(4) != 1:
+            raise ValueError("pair_bias: keys must be contiguous")
+        lay.pair_b, lay.pair_h, lay.pair_i = pair_bias.stride(0), pair_bias.stride(2), pair_bias.stride(3)
+    else:
+        lay.pair_i = L
+    lay.lse_row = L if lse_row is None else int(lse_row)
+    return lay
 
 
 def torch_dtype_code(dt) -> int:

@@ -12,7 +12,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
+#include <initializer_list>
+#include <utility>
 
 #include "evo_attn_launch.h"
 
@@ -47,50 +50,168 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 thread_local int g_last_hip_error = 0;
 
-// The 16-bit (bf16, f16) kernel addresses one (b, n, h) slice and one pair
-// matrix with 32-bit byte offsets.
+// The 16-bit (bf16, f16) kernel addresses the rows of one (b, n, h) slice
+// and of one pair matrix with 32-bit byte offsets, including rows up to 128
+// past L (which must land beyond the range, not wrap).
 constexpr int64_t kMaxOffset = int64_t(1) << 31;
+constexpr int64_t kMaxOffset32 = int64_t(1) << 32;
 
-bool supported(evo_dtype_t dt, int64_t L, int64_t H, int64_t D) {
-    if (dt == EVO_DTYPE_BF16 || dt == EVO_DTYPE_F16)
-        return (D == 8 || D == 16 || D == 32) && L * H * D * 2 < kMaxOffset && L * L * 2 < kMaxOffset;
-    if (dt == EVO_DTYPE_F32) return D == 8 || D == 16 || D == 32 || D == 64;
-    return false;
+// Whether rows of `row_elems` elements, es bytes each, keep every offset of
+// the 16-bit kernel in 32 bits: the last row's end below 2^31 (the buffer
+// range) and row L + 128 below 2^32.
+bool rows_fit(int64_t L, int64_t row_elems, int64_t last_row_bytes) {
+    const int64_t row = mul_checked(row_elems, 2);
+    const int64_t lo = mul_checked(L - 1, row), hi = mul_checked(L + 128, row);
+    return row >= 0 && lo >= 0 && lo + last_row_bytes < kMaxOffset && hi >= 0 && hi < kMaxOffset32;
+}
+
+bool dim_supported(evo_dtype_t dt, int64_t D) {
+    if (dt == EVO_DTYPE_BF16 || dt == EVO_DTYPE_F16) return D == 8 || D == 16 || D == 32;
+    return dt == EVO_DTYPE_F32 && (D == 8 || D == 16 || D == 32 || D == 64);
+}
+
+bool offsets_fit(evo_dtype_t dt, const evo_shape_t& s, const evo_layout_t& lay) {
+    if (dt == EVO_DTYPE_F32) return true;
+    const int64_t L = s.L, D = s.D;
+    return rows_fit(L, lay.q[2], D * 2) && rows_fit(L, lay.k[2], D * 2) && rows_fit(L, lay.v[2], D * 2) &&
+           rows_fit(L, lay.pair_i, L * 2);
+}
+
+// Largest element offset + 1 over axes {(size, stride)}, or -1 past 2^62.
+int64_t span_elems(std::initializer_list<std::pair<int64_t, int64_t>> axes) {
+    int64_t e = 1;
+    for (const auto& a : axes) {
+        const int64_t t = mul_checked(a.first - 1, a.second);
+        if (t < 0 || e > kMaxBytes - t) return -1;
+        e += t;
+    }
+    return e;
+}
+
+// Whether distinct (b, n, l, h, d) of a [B,N,L,H,D] tensor with these strides
+// (d contiguous) have distinct offsets: taken in increasing stride order, each
+// axis of size > 1 must step past everything the faster axes cover.
+bool no_self_overlap(const int64_t* st, const evo_shape_t& s) {
+    std::pair<int64_t, int64_t> ax[4] = {{st[0], s.B}, {st[1], s.N}, {st[2], s.L}, {st[3], s.H}};
+    std::sort(ax, ax + 4);
+    int64_t e = s.D;
+    for (const auto& a : ax) {
+        if (a.second <= 1) continue;
+        if (a.first < e) return false;
+        const int64_t t = mul_checked(a.second - 1, a.first);
+        if (t < 0 || e > kMaxBytes - t) return false;
+        e += t;
+    }
+    return true;
 }
 
 }  // namespace
 
-extern "C" evo_status_t evo_attn_check(const void* q, const void* k, const void* v, const void* mask_bias,
-                                       const void* pair_bias, const void* out, const float* lse,
-                                       const evo_shape_t* shape, evo_dtype_t dtype) {
-    if (!shape || !q || !k || !v || !out) return EVO_ERR_NULL_POINTER;
-    const int64_t B = shape->B, N = shape->N, L = shape->L, H = shape->H, D = shape->D;
+extern "C" void evo_attn_dense_layout(const evo_shape_t* shape, evo_layout_t* layout) {
+    if (!shape || !layout) return;
+    // a stride that overflows becomes -1, which the checks reject
+    const int64_t N = shape->N, L = shape->L, H = shape->H, D = shape->D;
+    const int64_t hd = mul_checked(H, D), lhd = mul_checked(L, hd), ll = mul_checked(L, L);
+    const int64_t dense[4] = {mul_checked(N, lhd), lhd, hd, D};
+    for (int a = 0; a < 4; ++a) layout->q[a] = layout->k[a] = layout->v[a] = layout->out[a] = dense[a];
+    layout->mask_b = mul_checked(N, L);
+    layout->mask_n = L;
+    layout->pair_b = mul_checked(H, ll);
+    layout->pair_h = ll;
+    layout->pair_i = L;
+    layout->lse_row = L;
+}
+
+extern "C" evo_status_t evo_attn_check_strided(const void* q, const void* k, const void* v, const void* mask_bias,
+                                               const void* pair_bias, const void* out, const float* lse,
+                                               const evo_layout_t* layout, const evo_shape_t* shape,
+                                               evo_dtype_t dtype) {
+    if (!shape || !layout || !q || !k || !v || !out) return EVO_ERR_NULL_POINTER;
+    const evo_shape_t& s = *shape;
+    const evo_layout_t& lay = *layout;
+    const int64_t B = s.B, N = s.N, L = s.L, H = s.H, D = s.D;
     if (B < 1 || N < 1 || L < 1 || H < 1 || D < 1) return EVO_ERR_BAD_SHAPE;
     if (dtype != EVO_DTYPE_F32 && dtype != EVO_DTYPE_BF16 && dtype != EVO_DTYPE_F16) return EVO_ERR_BAD_DTYPE;
     const int64_t es = elem_size(dtype);
 
-    // Byte sizes of every tensor, each bounded by 2^62.
-    int64_t qkv = es;
-    for (int64_t s : {B, N, L, H, D}) qkv = mul_checked(qkv, s);
-    int64_t msk = es;
-    for (int64_t s : {B, N, L}) msk = mul_checked(msk, s);
-    int64_t par = es;
-    for (int64_t s : {B, H, L, L}) par = mul_checked(par, s);
-    int64_t lsb = 4;
-    for (int64_t s : {B, N, H, L}) lsb = mul_checked(lsb, s);
-    if (qkv < 0 || msk < 0 || par < 0 || lsb < 0) return EVO_ERR_BAD_SHAPE;
+    // strides: non-negative; pair rows and lse rows at least L apart
+    const int64_t* qkvo[4] = {lay.q, lay.k, lay.v, lay.out};
+    for (const int64_t* t : qkvo)
+        for (int a = 0; a < 4; ++a)
+            if (t[a] < 0) return EVO_ERR_BAD_SHAPE;
+    if (lay.mask_b < 0 || lay.mask_n < 0 || lay.pair_b < 0 || lay.pair_h < 0) return EVO_ERR_BAD_SHAPE;
+    if (pair_bias && lay.pair_i < L) return EVO_ERR_BAD_SHAPE;
+    if (lse && lay.lse_row < L) return EVO_ERR_BAD_SHAPE;
+
+    // byte extents, each below 2^62
+    int64_t ext[4];
+    for (int t = 0; t < 4; ++t) {
+        const int64_t e = span_elems({{B, qkvo[t][0]}, {N, qkvo[t][1]}, {L, qkvo[t][2]}, {H, qkvo[t][3]}, {D, 1}});
+        ext[t] = e < 0 ? -1 : mul_checked(e, es);
+    }
+    const int64_t me = span_elems({{B, lay.mask_b}, {N, lay.mask_n}, {L, 1}});
+    const int64_t pe = span_elems({{B, lay.pair_b}, {H, lay.pair_h}, {L, lay.pair_i}, {L, 1}});
+    const int64_t bnh = mul_checked(mul_checked(B, N), H);
+    const int64_t le = bnh < 0 ? -1 : span_elems({{bnh, lay.lse_row}, {L, 1}});
+    const int64_t msk = me < 0 ? -1 : mul_checked(me, es), par = pe < 0 ? -1 : mul_checked(pe, es);
+    const int64_t lsb = le < 0 ? -1 : mul_checked(le, 4);
+    for (int64_t x : {ext[0], ext[1], ext[2], ext[3], msk, par, lsb})
+        if (x < 0) return EVO_ERR_BAD_SHAPE;
 
     for (const void* p : {q, k, v, mask_bias, pair_bias, out, static_cast<const void*>(lse)})
         if (p && !aligned16(p)) return EVO_ERR_MISALIGNED;
 
-    const Extent eo = extent(out, qkv), el = extent(lse, lsb);
-    for (const Extent& in : {extent(q, qkv), extent(k, qkv), extent(v, qkv), extent(mask_bias, msk),
+    // outputs: out's strides must not map two elements to one address, and
+    // out and lse may overlap neither an input nor each other
+    if (!no_self_overlap(lay.out, s)) return EVO_ERR_ALIASING;
+    const Extent eo = extent(out, ext[3]), el = extent(lse, lsb);
+    for (const Extent& in : {extent(q, ext[0]), extent(k, ext[1]), extent(v, ext[2]), extent(mask_bias, msk),
                              extent(pair_bias, par)})
         if (eo.overlaps(in) || el.overlaps(in)) return EVO_ERR_ALIASING;
     if (eo.overlaps(el)) return EVO_ERR_ALIASING;
 
-    if (!supported(dtype, L, H, D)) return EVO_ERR_UNSUPPORTED;
+    if (!dim_supported(dtype, D)) return EVO_ERR_UNSUPPORTED;
+    // rows of q, k, v and out start 16-byte aligned (the kernels move rows in
+    // 16-byte pieces); bias strides need no alignment (unaligned ones take the
+    // exact path)
+    for (const int64_t* t : qkvo)
+        for (int a = 0; a < 4; ++a)
+            if ((t[a] * es) % 16) return EVO_ERR_MISALIGNED;
+    if (!offsets_fit(dtype, s, lay)) return EVO_ERR_UNSUPPORTED;
     return EVO_OK;
+}
+
+extern "C" evo_status_t evo_attn_check(const void* q, const void* k, const void* v, const void* mask_bias,
+                                       const void* pair_bias, const void* out, const float* lse,
+                                       const evo_shape_t* shape, evo_dtype_t dtype) {
+    if (!shape) return EVO_ERR_NULL_POINTER;
+    evo_layout_t lay;
+    evo_attn_dense_layout(shape, &lay);
+    return evo_attn_check_strided(q, k, v, mask_bias, pair_bias, out, lse, &lay, shape, dtype);
+}
+
+extern "C" evo_status_t evo_attn_fwd_strided(const void* q, const void* k, const void* v, const void* mask_bias,
+                                             const void* pair_bias, void* out, float* lse, const evo_layout_t* layout,
+                                             const evo_shape_t* shape, evo_dtype_t dtype, void* stream) {
+    const evo_status_t st = evo_attn_check_strided(q, k, v, mask_bias, pair_bias, out, lse, layout, shape, dtype);
+    if (st != EVO_OK) return st;
+    evo::FwdArgs a{q, k, v, mask_bias, pair_bias, out, lse, shape->B, shape->N, shape->L, shape->H, shape->D, {}};
+    for (int i = 0; i < 4; ++i) {
+        a.st.q[i] = layout->q[i];
+        a.st.k[i] = layout->k[i];
+        a.st.v[i] = layout->v[i];
+        a.st.o[i] = layout->out[i];
+    }
+    a.st.mb = layout->mask_b, a.st.mn = layout->mask_n;
+    a.st.pb = layout->pair_b, a.st.ph = layout->pair_h, a.st.pi = layout->pair_i;
+    a.st.lrow = layout->lse_row;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t err = dtype == EVO_DTYPE_BF16  ? evo::launch_fwd_bf16(a, s)
+                           : dtype == EVO_DTYPE_F16 ? evo::launch_fwd_f16(a, s)
+                                                    : evo::launch_fwd_f32(a, s);
+    if (err == hipSuccess) return EVO_OK;
+    g_last_hip_error = static_cast<int>(err);
+    return EVO_ERR_HIP;
 }
 
 extern "C" evo_status_t evo_attn_fwd(const void* q, const void* k, const void* v, const void* mask_bias,
@@ -98,14 +219,9 @@ extern "C" evo_status_t evo_attn_fwd(const void* q, const void* k, const void* v
                                      evo_dtype_t dtype, void* stream) {
     const evo_status_t st = evo_attn_check(q, k, v, mask_bias, pair_bias, out, lse, shape, dtype);
     if (st != EVO_OK) return st;
-    evo::FwdArgs a{q, k, v, mask_bias, pair_bias, out, lse, shape->B, shape->N, shape->L, shape->H, shape->D};
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t err = dtype == EVO_DTYPE_BF16  ? evo::launch_fwd_bf16(a, s)
-                     : dtype == EVO_DTYPE_F16 ? evo::launch_fwd_f16(a, s)
-                                              : evo::launch_fwd_f32(a, s);
-    if (err == hipSuccess) return EVO_OK;
-    g_last_hip_error = static_cast<int>(err);
-    return EVO_ERR_HIP;
+    evo_layout_t lay;
+    evo_attn_dense_layout(shape, &lay);
+    return evo_attn_fwd_strided(q, k, v, mask_bias, pair_bias, out, lse, &lay, shape, dtype, stream);
 }
 
 namespace {

@@ -102,6 +102,7 @@ struct Params {
     FastDiv qblocks;  // ceil(L / kBlockQ)
     FastDiv nd, hd;   // N, H
     int64_t total;    // number of workgroups, below 2^31
+    Strides st;       // element strides of every tensor
     float c1;         // log2(e) / sqrt(D): accumulator units -> base-2 exponent
     uint32_t sqd;     // bf16 bits: low half = sqrt(D) high part, high half = low part
 };
@@ -251,9 +252,12 @@ __device__ inline int64_t logical_block(int64_t hw, int64_t total) {
 }
 
 struct Slice {
-    int64_t b, n, h, slice, HD, q0;
+    int64_t b, n, h, q0;
+    int64_t qb, kb, vb, ob;         // element offsets of (b, n, 0, h, 0) in q, k, v, out
+    int64_t ql, kl, vl, ol, pi;     // row strides (elements) of q, k, v, out and the pair matrix
     const u16* mrow;   // mask row of (b, n) or nullptr
     const u16* pbase;  // pair matrix of (b, h) or nullptr
+    float* lrow;       // lse row of (b, n, h) or nullptr
 };
 
 // ---------------------------------------------------------------------------
@@ -275,12 +279,14 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
     const int nblocks = (L + kKB - 1) / kKB;
-    const uint32_t rowb = (uint32_t)s.HD * 2;  // bytes between consecutive rows of q, k, v
-    const uint32_t span = (uint32_t)(L - 1) * rowb + D * 2;  // below kOOB: the API bounds L * H * D * 2 by 2^31
-    const Rsrc rq = make_rsrc(p.q + s.slice, span);
-    const Rsrc rk = make_rsrc(p.k + s.slice, span);
-    const Rsrc rv = make_rsrc(p.v + s.slice, span);
-    const Rsrc rp = make_rsrc(PAIR ? s.pbase : p.q, PAIR ? (uint32_t)L * (uint32_t)L * 2u : 0u);
+    // bytes between consecutive rows of q, k, v and the pair matrix; every
+    // row span is below kOOB (the launcher checks)
+    const uint32_t rowq = (uint32_t)s.ql * 2, rowk = (uint32_t)s.kl * 2, rowv = (uint32_t)s.vl * 2;
+    const uint32_t rowp = (uint32_t)s.pi * 2;
+    const Rsrc rq = make_rsrc(p.q + s.qb, (uint32_t)(L - 1) * rowq + D * 2);
+    const Rsrc rk = make_rsrc(p.k + s.kb, (uint32_t)(L - 1) * rowk + D * 2);
+    const Rsrc rv = make_rsrc(p.v + s.vb, (uint32_t)(L - 1) * rowv + D * 2);
+    const Rsrc rp = make_rsrc(PAIR ? s.pbase : p.q, PAIR ? (uint32_t)(L - 1) * rowp + (uint32_t)L * 2u : 0u);
     const Rsrc rm = make_rsrc(MASK ? s.mrow : p.q, MASK ? (uint32_t)L * 2u : 0u);
 
     // Identity A operand: slot (g, e) stands for key 8*(g%2) + e of a 16-key
@@ -303,7 +309,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
     V8 qop[kQTiles];
     for (int t = 0; t < kQTiles; ++t) {
         const uint32_t i = (uint32_t)(s.q0 + 16 * t + c);
-        qop[t] = as_v8<E>(bload16(rq, g < kDC ? i * rowb + 16 * g : kOOB, 0));
+        qop[t] = as_v8<E>(bload16(rq, g < kDC ? i * rowq + 16 * g : kOOB, 0));
     }
 
     // ---- copy of one block (keys [64 blk, 64 blk + 64)) into LDS buffer `buf` ----
@@ -315,16 +321,19 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
     // mask: wave 0 lanes 0..7, 8 keys each.
     const uint32_t qwg = (uint32_t)(s.q0 - wave * kWaveQ);  // first query of the workgroup
     const uint32_t kvchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
-    const uint32_t kvo = kvchunk < kDC ? (uint32_t)(16 * wave + (lane >> 2)) * rowb + 16u * kvchunk : kOOB;
+    const uint32_t krow = (uint32_t)(16 * wave + (lane >> 2));
+    const uint32_t ko = kvchunk < kDC ? krow * rowk + 16u * kvchunk : kOOB;
+    const uint32_t vo = kvchunk < kDC ? krow * rowv + 16u * kvchunk : kOOB;
     uint32_t pvo[4];
     for (int j = 0; j < 4; ++j) {
         const uint32_t row = 8u * (4 * wave + j) + (lane >> 3);
-        pvo[j] = (qwg + row) * (uint32_t)L * 2u + 16u * ((lane & 7) ^ (lane >> 3));
+        // rows past L start beyond the range (the pair row stride is at least L)
+        pvo[j] = (qwg + row) * rowp + 16u * ((lane & 7) ^ (lane >> 3));
     }
     auto copy_block = [&](int blk, FastBuf* __restrict__ dst) {
         const uint32_t k0 = (uint32_t)blk * kKB;
-        dma16(rk, &dst->k[64 * wave], kvo + k0 * rowb, 0);
-        dma16(rv, &dst->v[64 * wave], kvo + k0 * rowb, 0);
+        dma16(rk, &dst->k[64 * wave], ko + k0 * rowk, 0);
+        dma16(rv, &dst->v[64 * wave], vo + k0 * rowv, 0);
         if (PAIR)
             for (int j = 0; j < 4; ++j) dma16(rp, &dst->pt[64 * (4 * wave + j)], pvo[j] + k0 * 2u, 0);
         if (MASK && wave == 0 && lane < 8) dma16(rm, &dst->mt[0], 16u * lane + k0 * 2u, 0);
@@ -519,13 +528,11 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
         for (int dh = 0; dh < kDHT; ++dh) {
             // lane (c + 16g) holds O^T[d = 16dh + 4g + r][query c], r = 0..3
             if (16 * dh + 4 * g >= D) continue;
-            u16* dst = p.out + s.slice + i * s.HD + 16 * dh + 4 * g;
+            u16* dst = p.out + s.ob + i * s.ol + 16 * dh + 4 * g;
             const f32x4 o = oacc[t][dh] * inv;
             *reinterpret_cast<uint2*>(dst) = uint2{pack2<E>(o[0], o[1]), pack2<E>(o[2], o[3])};
         }
-        if (p.lse && g == 0)
-            p.lse[((s.b * p.N + s.n) * p.H + s.h) * L + i] =
-                lt[t] > 0.f ? (msub[t] + __log2f(lt[t])) * kLn2 : -INFINITY;
+        if (s.lrow && g == 0) s.lrow[i] = lt[t] > 0.f ? (msub[t] + __log2f(lt[t])) * kLn2 : -INFINITY;
     }
     return true;
 }
@@ -548,7 +555,7 @@ __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int ti
     for (int t = 0; t < kQTiles; ++t) {
         int64_t i = s.q0 + 16 * t + c;
         if (i >= L) i = L - 1;
-        qop[t] = as_v8<E>(8 * g < D ? load16(p.q + s.slice + i * s.HD + 8 * g) : uint4{0u, 0u, 0u, 0u});
+        qop[t] = as_v8<E>(8 * g < D ? load16(p.q + s.qb + i * s.ql + 8 * g) : uint4{0u, 0u, 0u, 0u});
     }
     f32x4 oacc[kQTiles][2];
     float mrun[kQTiles], lrun[kQTiles];
@@ -564,8 +571,8 @@ __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int ti
     for (int64_t k0 = 0; k0 < L; k0 += kKB) {
         uint4 kk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
         if (k0 + skey < L && sdc < D) {
-            kk = load16(p.k + s.slice + (k0 + skey) * s.HD + sdc);
-            vv = load16(p.v + s.slice + (k0 + skey) * s.HD + sdc);
+            kk = load16(p.k + s.kb + (k0 + skey) * s.kl + sdc);
+            vv = load16(p.v + s.vb + (k0 + skey) * s.vl + sdc);
         }
         __syncthreads();  // previous block's readers are done
         *reinterpret_cast<uint4*>(&sm.k[skey * kKStride + sdc]) = kk;
@@ -587,7 +594,7 @@ __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int ti
                     const int64_t j = jb + rr;
                     float bias = 0.f;
                     if (s.mrow && j < L) bias += E::widen(s.mrow[j]);
-                    if (s.pbase && j < L) bias += E::widen(s.pbase[i * L + j]);
+                    if (s.pbase && j < L) bias += E::widen(s.pbase[i * s.pi + j]);
                     acc[t][kt][rr] = j < L ? fmaf(acc[t][kt][rr], cq, bias * kLog2e) : -INFINITY;
                 }
             }
@@ -632,12 +639,11 @@ __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int ti
         const float inv = l > 0.f ? 1.f / l : 0.f;
         for (int dh = 0; dh < kDHT; ++dh) {
             if (16 * dh + 4 * g >= D) continue;
-            u16* dst = p.out + s.slice + i * s.HD + 16 * dh + 4 * g;
+            u16* dst = p.out + s.ob + i * s.ol + 16 * dh + 4 * g;
             const f32x4 o = oacc[t][dh] * inv;
             *reinterpret_cast<uint2*>(dst) = uint2{pack2<E>(o[0], o[1]), pack2<E>(o[2], o[3])};
         }
-        if (p.lse && g == 0)
-            p.lse[((s.b * p.N + s.n) * p.H + s.h) * L + i] = l > 0.f ? (mrun[t] + __log2f(l)) * kLn2 : -INFINITY;
+        if (s.lrow && g == 0) s.lrow[i] = l > 0.f ? (mrun[t] + __log2f(l)) * kLn2 : -INFINITY;
     }
 }
 
@@ -655,12 +661,17 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_16bit_kernel(Params p) {
     s.h = r1 - r2 * p.hd.d;
     s.n = r2 - r3 * p.nd.d;
     s.b = r3;
-    s.HD = p.H * D;
-    s.slice = ((s.b * p.N + s.n) * p.L * p.H + s.h) * D;  // element (b, n, 0, h, 0)
+    const Strides& st = p.st;
+    s.qb = s.b * st.q[0] + s.n * st.q[1] + s.h * st.q[3];
+    s.kb = s.b * st.k[0] + s.n * st.k[1] + s.h * st.k[3];
+    s.vb = s.b * st.v[0] + s.n * st.v[1] + s.h * st.v[3];
+    s.ob = s.b * st.o[0] + s.n * st.o[1] + s.h * st.o[3];
+    s.ql = st.q[2], s.kl = st.k[2], s.vl = st.v[2], s.ol = st.o[2], s.pi = st.pi;
     const int tid = threadIdx.x;
     s.q0 = qb * kBlockQ + (tid >> 6) * kWaveQ;
-    s.mrow = p.mask ? p.mask + (s.b * p.N + s.n) * p.L : nullptr;
-    s.pbase = p.pair ? p.pair + (s.b * p.H + s.h) * p.L * p.L : nullptr;
+    s.mrow = p.mask ? p.mask + s.b * st.mb + s.n * st.mn : nullptr;
+    s.pbase = p.pair ? p.pair + s.b * st.pb + s.h * st.ph : nullptr;
+    s.lrow = p.lse ? p.lse + ((s.b * p.N + s.n) * p.H + s.h) * st.lrow : nullptr;
 
     if (FAST) {
         if (run_fast<E, D, PAIR, MASK>(p, s, sm.f, tid)) return;
@@ -676,10 +687,14 @@ hipError_t launch_variant(Params& p, hipStream_t stream) {
                            dim3((unsigned)p.total), dim3(kWaves * 64), args, 0, stream);
 }
 
+// The fast path copies bias rows in 16-byte pieces: it needs L % 8 == 0 and
+// bias rows that start 16-byte aligned.
 template <class E, int D, bool PAIR, bool MASK>
 hipError_t launch_biases(Params& p, hipStream_t stream) {
-    return p.L % 8 == 0 ? launch_variant<E, D, PAIR, MASK, true>(p, stream)
-                        : launch_variant<E, D, PAIR, MASK, false>(p, stream);
+    const bool aligned = (!PAIR || (p.st.pb % 8 == 0 && p.st.ph % 8 == 0 && p.st.pi % 8 == 0)) &&
+                         (!MASK || (p.st.mb % 8 == 0 && p.st.mn % 8 == 0));
+    return p.L % 8 == 0 && aligned ? launch_variant<E, D, PAIR, MASK, true>(p, stream)
+                                   : launch_variant<E, D, PAIR, MASK, false>(p, stream);
 }
 
 template <class E, int D>
@@ -724,6 +739,7 @@ hipError_t launch_fwd_16bit(const FwdArgs& a, hipStream_t stream, bool f16) {
     p.pair = static_cast<const u16*>(a.pair);
     p.out = static_cast<u16*>(a.out);
     p.lse = a.lse;
+    p.st = a.st;
     p.N = a.N;
     p.L = a.L;
     p.H = a.H;

@@ -979,8 +979,11 @@ int64_t bwd_dpair_chunks(int64_t B, int64_t N, int64_t L, int64_t H) {
 
 bool bwd_mfma_eligible(const BwdArgs& a, int dtype) {
     constexpr int64_t kMax = int64_t(1) << 31;
+    // 32-bit byte offsets: rows of a slice and of a pair matrix end below
+    // 2^31, and rows up to 128 past L stay below 2^32
     return (dtype == 1 || dtype == 2) && (a.D == 8 || a.D == 16 || a.D == 32) && a.L % 8 == 0 &&
-           a.L * a.H * a.D * 2 < kMax && a.L * a.L * 2 < kMax && a.N < kMax && a.H < kMax;
+           a.L * a.H * a.D * 2 < kMax && a.L * a.L * 2 < kMax && (a.L + 128) * a.H * a.D * 2 < 2 * kMax &&
+           (a.L + 128) * a.L * 2 < 2 * kMax && a.N < kMax && a.H < kMax;
 }
 
 hipError_t launch_bwd_mfma(const BwdArgs& a, int dtype, unsigned stages, hipStream_t stream) {

@@ -22,12 +22,22 @@ namespace {
 constexpr int kQ = 64;  // queries per workgroup (one wavefront)
 constexpr int kK = 64;  // keys per LDS block
 
+struct F32Params {
+    const float *q, *k, *v, *mask, *pair;
+    float *out, *lse;
+    int64_t N, L, H, qblocks;
+    Strides st;
+    float scale;
+};
+
 template <int D>
-__global__ __launch_bounds__(kQ) void fwd_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
-                                                     const float* __restrict__ v, const float* __restrict__ mask,
-                                                     const float* __restrict__ pair, float* __restrict__ out,
-                                                     float* __restrict__ lse, int64_t N, int64_t L, int64_t H,
-                                                     int64_t qblocks, float scale) {
+__global__ __launch_bounds__(kQ) void fwd_f32_kernel(F32Params p) {
+    const float* __restrict__ q = p.q;
+    const float* __restrict__ k = p.k;
+    const float* __restrict__ v = p.v;
+    const int64_t N = p.N, L = p.L, H = p.H, qblocks = p.qblocks;
+    const float scale = p.scale;
+    const Strides& st = p.st;
     __shared__ float ks[kK][D + 1];
     __shared__ float vs[kK][D + 1];
 
@@ -43,17 +53,18 @@ __global__ __launch_bounds__(kQ) void fwd_f32_kernel(const float* __restrict__ q
     const int lane = threadIdx.x;
     const int64_t i = qb * kQ + lane;
     const bool active = i < L;
-    const int64_t HD = H * D;
-    const int64_t slice = ((b * N + n) * L * H + h) * D;  // element (b, n, 0, h, 0)
+    const int64_t qbase = b * st.q[0] + n * st.q[1] + h * st.q[3];
+    const int64_t kbase = b * st.k[0] + n * st.k[1] + h * st.k[3];
+    const int64_t vbase = b * st.v[0] + n * st.v[1] + h * st.v[3];
 
     float qr[D], acc[D];
     const int64_t irow = active ? i : L - 1;
     for (int d = 0; d < D; ++d) {
-        qr[d] = q[slice + irow * HD + d];
+        qr[d] = q[qbase + irow * st.q[2] + d];
         acc[d] = 0.f;
     }
-    const float* mrow = mask ? mask + (b * N + n) * L : nullptr;
-    const float* prow = pair ? pair + ((b * H + h) * L + irow) * L : nullptr;
+    const float* mrow = p.mask ? p.mask + b * st.mb + n * st.mn : nullptr;
+    const float* prow = p.pair ? p.pair + b * st.pb + h * st.ph + irow * st.pi : nullptr;
 
     float m = -INFINITY, l = 0.f;
     for (int64_t k0 = 0; k0 < L; k0 += kK) {
@@ -63,8 +74,8 @@ __global__ __launch_bounds__(kQ) void fwd_f32_kernel(const float* __restrict__ q
             const int j = e / D, d = e % D;
             float kv = 0.f, vv = 0.f;
             if (j < cnt) {
-                kv = k[slice + (k0 + j) * HD + d];
-                vv = v[slice + (k0 + j) * HD + d];
+                kv = k[kbase + (k0 + j) * st.k[2] + d];
+                vv = v[vbase + (k0 + j) * st.v[2] + d];
             }
             ks[j][d] = kv;
             vs[j][d] = vv;
@@ -87,8 +98,9 @@ __global__ __launch_bounds__(kQ) void fwd_f32_kernel(const float* __restrict__ q
     }
     if (!active) return;
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    for (int d = 0; d < D; ++d) out[slice + i * HD + d] = acc[d] * inv;
-    if (lse) lse[((b * N + n) * H + h) * L + i] = l > 0.f ? m + logf(l) : -INFINITY;
+    float* orow = p.out + b * st.o[0] + n * st.o[1] + h * st.o[3] + i * st.o[2];
+    for (int d = 0; d < D; ++d) orow[d] = acc[d] * inv;
+    if (p.lse) p.lse[((b * N + n) * H + h) * st.lrow + i] = l > 0.f ? m + logf(l) : -INFINITY;
 }
 
 template <int D>
@@ -96,16 +108,18 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
     const int64_t qblocks = (a.L + kQ - 1) / kQ;
     const int64_t blocks = a.B * a.N * a.H * qblocks;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const float* q = static_cast<const float*>(a.q);
-    const float* k = static_cast<const float*>(a.k);
-    const float* v = static_cast<const float*>(a.v);
-    const float* mask = static_cast<const float*>(a.mask);
-    const float* pair = static_cast<const float*>(a.pair);
-    float* out = static_cast<float*>(a.out);
-    float* lse = a.lse;
-    int64_t N = a.N, L = a.L, H = a.H;
-    float scale = (float)(1.0 / std::sqrt((double)D));
-    void* args[] = {&q, &k, &v, &mask, &pair, &out, &lse, &N, &L, &H, (void*)&qblocks, &scale};
+    F32Params p;
+    p.q = static_cast<const float*>(a.q);
+    p.k = static_cast<const float*>(a.k);
+    p.v = static_cast<const float*>(a.v);
+    p.mask = static_cast<const float*>(a.mask);
+    p.pair = static_cast<const float*>(a.pair);
+    p.out = static_cast<float*>(a.out);
+    p.lse = a.lse;
+    p.N = a.N, p.L = a.L, p.H = a.H, p.qblocks = qblocks;
+    p.st = a.st;
+    p.scale = (float)(1.0 / std::sqrt((double)D));
+    void* args[] = {&p};
     return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_f32_kernel<D>), dim3((unsigned)blocks), dim3(kQ),
                            args, 0, stream);
 }

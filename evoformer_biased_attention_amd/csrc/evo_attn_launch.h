@@ -7,6 +7,17 @@
 
 namespace evo {
 
+// Element strides of the forward pass's tensors.  q, k, v, out: the b, n,
+// l (row) and h axes; the d axis is contiguous.  Biases: keys contiguous.
+// The C ABI checks that every stride except lrow is a multiple of 16 bytes
+// and that every row span fits 2^31 bytes.
+struct Strides {
+    int64_t q[4], k[4], v[4], o[4];  // b, n, l, h
+    int64_t mb, mn;                  // mask row of (b, n)
+    int64_t pb, ph, pi;              // pair matrix of (b, h), its query rows
+    int64_t lrow;                    // lse: elements between consecutive (b, n, h) rows, >= L
+};
+
 struct FwdArgs {
     const void* q;
     const void* k;
@@ -14,8 +25,9 @@ struct FwdArgs {
     const void* mask;  // [B,N,1,1,L] or nullptr
     const void* pair;  // [B,1,H,L,L] or nullptr
     void* out;
-    float* lse;        // [B,N,H,L] or nullptr
+    float* lse;        // [B,N,H,L] (rows lrow apart) or nullptr
     int64_t B, N, L, H, D;
+    Strides st;
 };
 
 // bf16 inputs, D in {8, 16, 32}: MFMA kernel.  Returns the hipError_t of the launch.

@@ -85,9 +85,12 @@ typedef enum {
  *   pair_bias   [B,1,H,L,L] or NULL (no pair bias: all zero)
  *   out         output, [B,N,L,H,D], same dtype as q
  *   lse         output, [B,N,H,L] float32, or NULL to skip it
- * Supported today: dtype BF16 or F16 with D in {8, 16, 32} (MFMA path; also
- * needs L * H * D * 2 < 2^31 and L * L * 2 < 2^31, i.e. L <= 32767) and
- * dtype F32 with D in {8, 16, 32, 64}; any B, N, H >= 1 and any L >= 1.
+ * Supported today: dtype BF16 or F16 with D in {8, 16, 32} (MFMA path; it
+ * addresses one head's rows of a slice and the rows of a pair matrix with
+ * 32-bit byte offsets, so it needs (L - 1) * H * D * 2 + 2 D < 2^31 and
+ * (L - 1) * L * 2 + 2 L < 2^31 (L <= 32767), and rows up to L + 128 below
+ * 2^32: (L + 128) * H * D * 2 < 2^32, (L + 128) * L * 2 < 2^32) and dtype
+ * F32 with D in {8, 16, 32, 64}; any B, N, H >= 1 and any L >= 1.
  * Other valid combinations return EVO_ERR_UNSUPPORTED.
  * A query row whose every score is -inf gets out = 0 and lse = -inf.  In
  * F16 a large negative mask value such as -1e9 is -inf, which is how such
@@ -96,6 +99,52 @@ typedef enum {
 evo_status_t evo_attn_fwd(const void* q, const void* k, const void* v, const void* mask_bias,
                           const void* pair_bias, void* out, float* lse, const evo_shape_t* shape,
                           evo_dtype_t dtype, void* stream);
+
+/*
+ * Element strides of every tensor, for callers whose tensors are views (a
+ * transposed pair representation, an MSA tensor read column-wise, a padded
+ * LSE).  Section 5.3 of the guide: triangle attention around the ending node
+ * and MSA column attention attend along the other axis of the same tensor as
+ * their row-wise counterparts; with these strides they read it in place.
+ *   q, k, v, out   strides of the b, n, l and h axes of [B,N,L,H,D]; the d
+ *                  axis is contiguous (stride 1).  Example: Q of ending-node
+ *                  attention as a view of X[B, L_i, L_j, H, D] (n = j, l = i):
+ *                  {L*L*H*D, H*D, L*H*D, D}.
+ *   mask_b, mask_n strides of mask_bias [B,N,1,1,L]; keys contiguous
+ *   pair_b, pair_h, pair_i
+ *                  strides of pair_bias [B,1,H,L,L] (pair_i: between query
+ *                  rows, >= L); keys contiguous
+ *   lse_row        elements between the lse rows of consecutive (b, n, h),
+ *                  >= L (the guide's padded layout is ceil(L/32)*32, section 5.4)
+ * Every stride other than lse_row must be a multiple of 16 bytes
+ * (EVO_ERR_MISALIGNED) and non-negative (EVO_ERR_BAD_SHAPE); out's strides
+ * must give distinct elements distinct addresses (EVO_ERR_ALIASING).
+ */
+typedef struct {
+    int64_t q[4], k[4], v[4], out[4];
+    int64_t mask_b, mask_n;
+    int64_t pair_b, pair_h, pair_i;
+    int64_t lse_row;
+} evo_layout_t;
+
+/* Fill *layout with the dense layout of *shape (what evo_attn_fwd assumes). */
+void evo_attn_dense_layout(const evo_shape_t* shape, evo_layout_t* layout);
+
+/*
+ * evo_attn_fwd with explicit strides (see evo_layout_t); every other rule is
+ * that of evo_attn_fwd.  Extents for the aliasing check run from each
+ * pointer to its tensor's last element.  For bf16 and f16 the row strides of
+ * q, k, v and the pair bias must also keep (L + 128) rows below 2^32 bytes
+ * (else EVO_ERR_UNSUPPORTED).
+ */
+evo_status_t evo_attn_fwd_strided(const void* q, const void* k, const void* v, const void* mask_bias,
+                                  const void* pair_bias, void* out, float* lse, const evo_layout_t* layout,
+                                  const evo_shape_t* shape, evo_dtype_t dtype, void* stream);
+
+/* The validation of evo_attn_fwd_strided alone; host-only. */
+evo_status_t evo_attn_check_strided(const void* q, const void* k, const void* v, const void* mask_bias,
+                                    const void* pair_bias, const void* out, const float* lse,
+                                    const evo_layout_t* layout, const evo_shape_t* shape, evo_dtype_t dtype);
 
 /*
  * The validation of evo_attn_fwd alone, with the same arguments minus the

@@ -21,7 +21,7 @@ def _header_text():
 
 
 def test_header_declares_exactly_the_exported_names():
-    decls = set(re.findall(r"^\s*(?:const\s+char\s*\*|evo_status_t|int|size_t)\s+(evo_\w+)\s*\(", _header_text(),
+    decls = set(re.findall(r"^\s*(?:const\s+char\s*\*|evo_status_t|int|size_t|void)\s+(evo_\w+)\s*\(", _header_text(),
                            re.M))
     assert decls == set(E.EXPORTED)
 
@@ -132,8 +132,12 @@ def test_bf16_offset_limits():
     """The bf16 kernel uses 32-bit byte offsets within a slice and a pair matrix."""
     assert check(shape=(1, 1, 32767, 1, 32)) == E.EVO_OK
     assert check(shape=(1, 1, 32768, 1, 32)) == E.EVO_ERR_UNSUPPORTED      # L*L*2 = 2^31
-    big = (1, 1, 1 << 14, 1 << 11, 32)  # L*H*D*2 = 2^31
+    # one head's rows of a slice must end below 2^31 bytes: (L-1)*H*D*2 + 2D
+    fits = (1, 1, 1 << 14, 1 << 11, 32)       # (2^14 - 1) * 2^17 + 64 < 2^31
+    assert check(shape=fits, mask_bias=None, pair_bias=None) == E.EVO_OK
+    big = (1, 1, 1 << 14, 1 << 12, 32)        # (2^14 - 1) * 2^18 + 64 > 2^31
     assert check(shape=big, mask_bias=None, pair_bias=None) == E.EVO_ERR_UNSUPPORTED
+    assert check(shape=big, mask_bias=None, pair_bias=None, dtype=E.EVO_DTYPE_F32) == E.EVO_OK
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
@@ -240,3 +244,94 @@ def test_bwd_workspace_size():
     assert E.evo_attn_bwd_workspace_size((1, 8, 384, 4, 32), E.EVO_DTYPE_BF16) == 0     # N too small to split
     assert E.evo_attn_bwd_workspace_size((1, 384, 100, 4, 32), E.EVO_DTYPE_BF16) == 0   # L % 8 != 0
     assert E.evo_attn_bwd_workspace_size((0, 384, 384, 4, 32), E.EVO_DTYPE_BF16) == 0
+
+
+# ---------------------------------------------------------------------------
+# evo_attn_check_strided
+# ---------------------------------------------------------------------------
+def scheck(layout, shape=(1, 8, 64, 4, 32), dtype=E.EVO_DTYPE_BF16, **over):
+    q, k, v, m, p, o, l = addrs(7)
+    args = dict(q=q, k=k, v=v, mask_bias=m, pair_bias=p, out=o, lse=l)
+    args.update(over)
+    return E.evo_attn_check_strided(args["q"], args["k"], args["v"], args["mask_bias"], args["pair_bias"],
+                                    args["out"], args["lse"], layout, shape, dtype)
+
+
+def transposed_layout(B, N, L, H, D):
+    """Q/K/V/O of ending-node attention as views of X[B, L_i(=L), L_j(=N), H, D]: n = j, l = i."""
+    lay = E.evo_attn_dense_layout((B, N, L, H, D))
+    for name in ("q", "k", "v", "out"):
+        getattr(lay, name)[:] = [L * N * H * D, H * D, N * H * D, D]
+    return lay
+
+
+def test_dense_layout_values():
+    lay = E.evo_attn_dense_layout((2, 3, 5, 4, 8))
+    assert list(lay.q) == [3 * 5 * 4 * 8, 5 * 4 * 8, 4 * 8, 8] == list(lay.out)
+    assert (lay.mask_b, lay.mask_n, lay.pair_b, lay.pair_h, lay.pair_i, lay.lse_row) == (15, 5, 100, 25, 5, 5)
+
+
+def test_strided_valid():
+    shape = (1, 8, 64, 4, 32)
+    assert scheck(E.evo_attn_dense_layout(shape)) == E.EVO_OK
+    assert scheck(transposed_layout(*shape)) == E.EVO_OK
+    lay = E.evo_attn_dense_layout(shape)
+    lay.lse_row = 96                                # padded lse rows
+    lay.pair_i = 72                                 # padded pair rows
+    assert scheck(lay) == E.EVO_OK
+
+
+def test_strided_rules():
+    shape = (1, 8, 64, 4, 32)
+    lay = E.evo_attn_dense_layout(shape)
+    lay.lse_row = 63
+    assert scheck(lay) == E.EVO_ERR_BAD_SHAPE       # lse rows overlap
+    assert scheck(lay, lse=None) == E.EVO_OK        # no lse: its stride is ignored
+    lay = E.evo_attn_dense_layout(shape)
+    lay.pair_i = 60
+    assert scheck(lay) == E.EVO_ERR_BAD_SHAPE       # pair rows shorter than L
+    lay = E.evo_attn_dense_layout(shape)
+    lay.q[2] = 132                                  # 264 bytes: not a multiple of 16
+    assert scheck(lay) == E.EVO_ERR_MISALIGNED
+    lay = E.evo_attn_dense_layout(shape)
+    lay.k[1] = -8
+    assert scheck(lay) == E.EVO_ERR_BAD_SHAPE
+    lay = E.evo_attn_dense_layout(shape)
+    lay.out[3] = 16                                 # heads 16 apart with D = 32: elements collide
+    assert scheck(lay) == E.EVO_ERR_ALIASING
+    lay = E.evo_attn_dense_layout(shape)
+    lay.out[1] = 0                                  # every n on the same rows
+    assert scheck(lay) == E.EVO_ERR_ALIASING
+    lay = E.evo_attn_dense_layout(shape)
+    lay.q[1] = 0                                    # inputs may repeat: the same Q for every n
+    assert scheck(lay) == E.EVO_OK
+    lay = E.evo_attn_dense_layout(shape)
+    lay.mask_n = 68                                 # unaligned bias rows are accepted (exact path)
+    lay.pair_i = 66
+    assert scheck(lay) == E.EVO_OK
+
+
+def test_strided_aliasing_uses_the_strided_extent():
+    shape = (1, 8, 64, 4, 32)
+    lay = transposed_layout(*shape)
+    q, *_ = addrs(1)
+    assert scheck(lay, out=q + 4096) == E.EVO_ERR_ALIASING
+
+
+def test_strided_32bit_row_limits():
+    """bf16: rows up to L + 128 must stay below 2^32 bytes of offset."""
+    shape = (1, 2, 8, 1, 32)
+    lay = E.evo_attn_dense_layout(shape)
+    for name in ("q", "k", "v", "out"):
+        getattr(lay, name)[:] = [1 << 30, 1 << 29, 1 << 25, 32]   # row stride 2^26 bytes
+    assert scheck(lay, shape=shape, mask_bias=None, pair_bias=None) == E.EVO_ERR_UNSUPPORTED
+    assert scheck(lay, shape=shape, mask_bias=None, pair_bias=None, dtype=E.EVO_DTYPE_F32) == E.EVO_OK
+    for name in ("q", "k", "v", "out"):
+        getattr(lay, name)[:] = [1 << 24, 1 << 23, 1 << 18, 32]
+    assert scheck(lay, shape=shape, mask_bias=None, pair_bias=None) == E.EVO_OK
+
+
+def test_dense_entry_matches_strided_with_dense_layout():
+    for shape in ((1, 2, 64, 4, 32), (2, 3, 17, 2, 16), (1, 1, 1, 1, 8)):
+        for dt in (E.EVO_DTYPE_BF16, E.EVO_DTYPE_F16, E.EVO_DTYPE_F32):
+            assert check(shape=shape, dtype=dt) == scheck(E.evo_attn_dense_layout(shape), shape=shape, dtype=dt)
