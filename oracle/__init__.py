@@ -11,6 +11,10 @@ hmyw.cn, sections 4, 5.2 and 5.4):
     s_j  = q_i . k_j / sqrt(D) + mask[b,n,0,0,j] + pair[b,0,h,i,j]
     out_i = sum_j softmax_j(s) v_j,      lse_i = ln sum_j exp(s_j)
 
+Triangle multiplication (``trimul``) is the second operation: per channel,
+a product through the third node of a [B, C, L, L] pair tensor (see
+``evo_ref_trimul`` in evo_ref.c for the reading and its source).
+
 The backward pass (section 5.4: the gradients the training path needs,
 bias gradients only on request) is the chain rule applied to the same
 definition: ``bwd`` returns dq, dk, dv and, when asked, the mask and pair
@@ -68,6 +72,8 @@ def _bind(path):
     lib.evo_ref_bwd.restype = ctypes.c_int
     lib.evo_ref_bwd.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64,
                                 dp, dp, dp, dp, dp, ctypes.c_int]
+    lib.evo_ref_trimul.restype = ctypes.c_int
+    lib.evo_ref_trimul.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, dp, ctypes.c_int]
     lib.evo_ref_rows.restype = ctypes.c_int
     lib.evo_ref_rows.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64, vp, i64,
                                  dp, dp, ctypes.c_int]
@@ -173,3 +179,26 @@ def bwd(q, k, v, mask=None, pair=None, dout=None, dtype="bf16", want_dmask=True,
     if rc:
         raise RuntimeError(f"evo_ref_bwd failed with code {rc}")
     return dq, dk, dv, dmask, dpair
+
+
+TRIMUL_DIRECTIONS = {"outgoing": 0, "incoming": 1}
+
+
+def trimul(a, w, dtype="bf16", direction="outgoing", nthreads=None, lib=None):
+    """x[b,c,i,j] = sum_k a[b,c,i,k] w[b,c,j,k] (outgoing) or sum_k a[b,c,k,i] w[b,c,k,j] (incoming).
+
+    a, w: [B, C, L, L] storage arrays; returns x [B, C, L, L] float64.
+    """
+    if dtype not in DTYPES:
+        raise ValueError(f"dtype must be one of {sorted(DTYPES)}")
+    st = _STORAGE[dtype]
+    a, w = np.ascontiguousarray(a), np.ascontiguousarray(w)
+    if a.ndim != 4 or a.shape[2] != a.shape[3] or a.shape != w.shape or a.dtype != st or w.dtype != st:
+        raise ValueError(f"a, w: expected {st.__name__} [B, C, L, L] of one shape")
+    B, C, L, _ = a.shape
+    x = np.empty((B, C, L, L), np.float64)
+    rc = (lib or _load()).evo_ref_trimul(a.ctypes.data, w.ctypes.data, DTYPES[dtype], B, C, L,
+                                         TRIMUL_DIRECTIONS[direction], x.ctypes.data, nthreads or default_threads())
+    if rc:
+        raise RuntimeError(f"evo_ref_trimul failed with code {rc}")
+    return x

@@ -382,3 +382,42 @@ int evo_ref_bwd(const void* q, const void* k, const void* v, const void* mask, c
     }
     return failed ? 4 : 0;
 }
+
+/*
+ * Triangle multiplication: the cubic contraction at the core of the triangle
+ * multiplicative update.  [CUEQ] (the cuEquivariance / NIM article, its
+ * "accelerating triangle operations" section) names triangle multiplication
+ * beside triangle attention as the O(N^3) hot spot of pair-representation
+ * models and motivates it by transitivity: when i is near k and k is near j,
+ * i and j are related.  Its formula is not printed there; this is the plain
+ * reading of "a product through the third node k", per channel c, in the two
+ * orientations (edges leaving or entering i and j):
+ *   outgoing (direction 0):  x[b,c,i,j] = sum_k a[b,c,i,k] * w[b,c,j,k]
+ *   incoming (direction 1):  x[b,c,i,j] = sum_k a[b,c,k,i] * w[b,c,k,j]
+ * a, w and x are [B, C, L, L]; the sums are exact products of the widened
+ * stored values accumulated in fp64.  x: [B, C, L, L] doubles.
+ * Returns 0, 1 for a NULL pointer, 2 for a bad dtype, 3 for a bad shape or
+ * direction.
+ */
+int evo_ref_trimul(const void* a, const void* w, int dtype, int64_t B, int64_t C, int64_t L, int direction,
+                   double* x, int nthreads) {
+    if (!a || !w || !x) return 1;
+    if (dtype < REF_F32 || dtype > REF_F16) return 2;
+    if (B < 1 || C < 1 || L < 1 || (direction != 0 && direction != 1)) return 3;
+    const int64_t planes = B * C, LL = L * L;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t bc = 0; bc < planes; ++bc) {
+        const int64_t base = bc * LL;
+        for (int64_t i = 0; i < L; ++i)
+            for (int64_t j = 0; j < L; ++j) {
+                double sum = 0.0;
+                for (int64_t k = 0; k < L; ++k) {
+                    const int64_t ia = direction == 0 ? i * L + k : k * L + i;
+                    const int64_t iw = direction == 0 ? j * L + k : k * L + j;
+                    sum += load(a, dtype, base + ia) * load(w, dtype, base + iw);
+                }
+                x[base + i * L + j] = sum;
+            }
+    }
+    return 0;
+}

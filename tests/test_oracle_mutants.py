@@ -1,7 +1,8 @@
 """The pins must reject plausible mistakes planted in copies of the oracle source.
 
 Forward mutants face the forward pins; backward mutants (mistakes in the
-gradient code only) face the backward pins.
+gradient code only) face the backward pins; triangle-multiplication mutants
+face its pins.
 
 Each mutant is a textual edit of oracle/evo_ref.c (a dropped term, a wrong
 index, a transposed operand, a wrong constant), compiled with gcc into a
@@ -16,6 +17,7 @@ import pytest
 import oracle
 import oracle_bwd_pins
 import oracle_pins
+import oracle_trimul_pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "evo_ref.c")
 
@@ -111,3 +113,36 @@ def test_bwd_pins_reject_mutant(name, tmp_path):
             caught_by = pin.__name__
             break
     assert caught_by is not None, f"mutant {name} passed every backward pin"
+
+
+TRIMUL_MUTANTS = {
+    "tm_a_as_incoming": [("const int64_t ia = direction == 0 ? i * L + k : k * L + i;",
+                          "const int64_t ia = k * L + i;")],
+    "tm_w_transposed": [("const int64_t iw = direction == 0 ? j * L + k : k * L + j;",
+                         "const int64_t iw = direction == 0 ? k * L + j : j * L + k;")],
+    "tm_out_transposed": [("x[base + i * L + j] = sum;", "x[base + j * L + i] = sum;")],
+    "tm_channel_ignored": [("const int64_t base = bc * LL;", "const int64_t base = (bc / C) * C * LL;")],
+    "tm_a_times_a": [("sum += load(a, dtype, base + ia) * load(w, dtype, base + iw);",
+                      "sum += load(a, dtype, base + ia) * load(a, dtype, base + iw);")],
+    "tm_directions_swapped": [("const int64_t ia = direction == 0 ?", "const int64_t ia = direction == 1 ?"),
+                              ("const int64_t iw = direction == 0 ?", "const int64_t iw = direction == 1 ?")],
+    "tm_last_k_dropped": [("for (int64_t k = 0; k < L; ++k) {\n                    const int64_t ia",
+                           "for (int64_t k = 0; k + 1 < L; ++k) {\n                    const int64_t ia")],
+}
+
+
+@pytest.mark.parametrize("name", sorted(TRIMUL_MUTANTS))
+def test_trimul_pins_reject_mutant(name, tmp_path):
+    lib = _compile_mutant(name, TRIMUL_MUTANTS[name], tmp_path)
+
+    def tref(a, w, dtype, direction):
+        return oracle.trimul(a, w, dtype=dtype, direction=direction, nthreads=1, lib=lib)
+
+    caught_by = None
+    for pin in oracle_trimul_pins.ALL_TRIMUL_PINS:
+        try:
+            pin(tref)
+        except (AssertionError, RuntimeError):
+            caught_by = pin.__name__
+            break
+    assert caught_by is not None, f"mutant {name} passed every triangle-multiplication pin"
