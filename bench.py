@@ -82,6 +82,9 @@ def main():
     ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
                     help="fwd (default): the forward pass; bwd: one evo_attn_bwd call per step, every gradient")
     ap.add_argument("--no-workspace", action="store_true", help="bwd: run without the pair-gradient workspace")
+    ap.add_argument("--op", choices=["attention", "trimul"], default="attention",
+                    help="trimul: time evo_trimul on the named triangle-multiplication size instead")
+    ap.add_argument("--direction", choices=["outgoing", "incoming"], default="outgoing", help="trimul orientation")
     ap.add_argument("--layout", choices=["dense", "transposed"], default="dense",
                     help="fwd: transposed stores Q/K/V/O as X[B, L, N, H, D] and reads them in place through "
                          "evo_attn_fwd_strided (triangle attention around the ending node without a copy)")
@@ -120,6 +123,9 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}), flush=True)
         sys.exit(1)
+
+    if args.op == "trimul":
+        return bench_trimul(args, torch, E, S)
 
     log(f"bench: generating workload {args.workload}")
     w = S.workload(args.workload, dtype=args.dtype)
@@ -245,6 +251,100 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, sets[0], args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+TRIMUL_METRIC = "triangle multiplication TFLOP/s (x[c,i,j] = sum_k a[c,i,k] w[c,j,k]), bf16, L=384, C=128"
+
+
+def bench_trimul(args, torch, E, S):
+    """One step = one evo_trimul call over the named size (B=1, C=128, L=384).  Work 2*B*C*L^3; algorithmic
+    bytes 3*B*C*L^2*2 (a and w read once, x written once), so the call is bound by HBM (128 FLOP/B, below
+    the 315 FLOP/B ridge)."""
+    import numpy as np
+    c = dict(S.TRIMUL_WORKLOAD)
+    if args.dtype:
+        c["dtype"] = args.dtype
+    B, C, L, dt = c["B"], c["C"], c["L"], c["dtype"]
+    if dt not in ("bf16", "f16"):
+        raise SystemExit("trimul runs in bf16 or f16")
+    a, w = S.trimul_problem(B, C, L, dt, seed=384)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float16
+    base = [torch.from_numpy(x).view(tdt).to("cuda") for x in (a, w)]
+    set_bytes = 3 * B * C * L * L * 2
+    R = 1 if args.mode == "warm" else max(2, math.ceil(2.5 * MALL_BYTES / set_bytes))
+    sets = [([t if r == 0 else t.clone() for t in base], torch.empty_like(base[0])) for r in range(R)]
+    code = E.torch_dtype_code(tdt)
+    d = {"outgoing": E.EVO_TRIMUL_OUTGOING, "incoming": E.EVO_TRIMUL_INCOMING}[args.direction]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def launch(r):
+        (ta, tw), x = sets[r]
+        return E.evo_trimul(ta, tw, x, (B, C, L), d, code, sh)
+
+    st = launch(0)
+    if st != E.EVO_OK:
+        raise E.EvoAttnError(st)
+    t_spin = time.perf_counter()
+    while time.perf_counter() - t_spin < args.spinup_seconds:
+        for i in range(20):
+            launch(i % R)
+        torch.cuda.synchronize()
+    for i in range(args.warmup):
+        launch(i % R)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        launch(i % R)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_us = 1e3 * ev0.elapsed_time(ev1) / args.steps
+    flops = 2 * B * C * L ** 3
+    alg_bytes = set_bytes
+    gbs = alg_bytes / (kern_us * 1e-6) / 1e9
+    log(f"bench trimul: {kern_us:.2f} us/launch, {flops / (kern_us * 1e-6) / 1e12:.1f} TFLOP/s, {gbs:.0f} GB/s")
+    result = {
+        "metric": TRIMUL_METRIC.replace("sum_k a[c,i,k] w[c,j,k]", "sum_k a[c,i,k] w[c,j,k]" if d == 0
+                                        else "sum_k a[c,k,i] w[c,k,j]"),
+        "value": round(flops * args.steps / wall / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic (seeded; see synthetic/)",
+        "config": {"workload": c["name"], "direction": args.direction, "B": B, "C": C, "L": L, "mode": args.mode,
+                   "input_sets": R, "flop_per_step": flops},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+        "kernel_us": round(kern_us, 3),
+        "mfma": {"tflops": round(flops / (kern_us * 1e-6) / 1e12, 2),
+                 "frac_of_bf16_peak": round(flops / (kern_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = len(os.sched_getaffinity(0))
+        ch, t = 0, 0.0
+        while ch == 0 or (t < args.cpu_seconds and ch < C):
+            t0 = time.perf_counter()
+            ref = oracle.trimul(a[:, ch:ch + 1], w[:, ch:ch + 1], dt, args.direction, nthreads=threads)
+            t += time.perf_counter() - t0
+            ch += 1
+        got = sets[0][1][:, :1].float().cpu().numpy()
+        ref0 = oracle.trimul(a[:, :1], w[:, :1], dt, args.direction, nthreads=threads)
+        result["cpu_baseline"] = {"value": round(2 * B * ch * L ** 3 / t / 1e12, 6), "unit": "TFLOP/s",
+                                  "cores": threads, "kind": "oracle",
+                                  "sample": f"{ch} of {C} channels of {c['name']} in fp64, {t:.1f} s",
+                                  "parity_vs_gpu_channel0_max_err_over_max_ref":
+                                      float(np.abs(got - ref0).max() / np.abs(ref0).max())}
     print(json.dumps(result), flush=True)
 
 

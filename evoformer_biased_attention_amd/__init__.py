@@ -25,7 +25,8 @@ EVO_DTYPE_F32, EVO_DTYPE_BF16, EVO_DTYPE_F16 = 0, 1, 2
 # Symbols declared in include/evo_attn.h.
 EXPORTED = ("evo_attn_fwd", "evo_attn_check", "evo_attn_fwd_strided", "evo_attn_check_strided",
             "evo_attn_dense_layout", "evo_attn_bwd", "evo_attn_bwd_check", "evo_attn_bwd_workspace_size",
-            "evo_status_string", "evo_attn_last_hip_error")
+            "evo_trimul", "evo_trimul_check", "evo_status_string", "evo_attn_last_hip_error")
+EVO_TRIMUL_OUTGOING, EVO_TRIMUL_INCOMING = 0, 1
 
 
 class EvoShape(ctypes.Structure):
@@ -39,6 +40,10 @@ class EvoLayout(ctypes.Structure):
                 ("out", ctypes.c_int64 * 4), ("mask_b", ctypes.c_int64), ("mask_n", ctypes.c_int64),
                 ("pair_b", ctypes.c_int64), ("pair_h", ctypes.c_int64), ("pair_i", ctypes.c_int64),
                 ("lse_row", ctypes.c_int64)]
+
+
+class EvoTrimulShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("C", ctypes.c_int64), ("L", ctypes.c_int64)]
 
 
 class EvoAttnError(RuntimeError):
@@ -80,6 +85,10 @@ def _load():
     lib.evo_attn_bwd_check.argtypes = [vp] * 15 + [ctypes.c_size_t, ctypes.POINTER(EvoShape), ctypes.c_int]
     lib.evo_attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.evo_attn_bwd_workspace_size.argtypes = [ctypes.POINTER(EvoShape), ctypes.c_int]
+    lib.evo_trimul.restype = ctypes.c_int
+    lib.evo_trimul.argtypes = [vp, vp, vp, ctypes.POINTER(EvoTrimulShape), ctypes.c_int, ctypes.c_int, vp]
+    lib.evo_trimul_check.restype = ctypes.c_int
+    lib.evo_trimul_check.argtypes = [vp, vp, vp, ctypes.POINTER(EvoTrimulShape), ctypes.c_int, ctypes.c_int]
     lib.evo_status_string.restype = ctypes.c_char_p
     lib.evo_status_string.argtypes = [ctypes.c_int]
     lib.evo_attn_last_hip_error.restype = ctypes.c_int
@@ -260,3 +269,32 @@ def bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, want_dmask=True, want_dpa
     if st != EVO_OK:
         raise EvoAttnError(st)
     return dq, dk, dv, dmask, dpair, delta
+
+
+def evo_trimul_check(a, w, x, shape, direction, dtype) -> int:
+    """Host-only validation of the triangle multiplication; shape is (B, C, L)."""
+    return _lib.evo_trimul_check(_addr(a), _addr(w), _addr(x), ctypes.byref(EvoTrimulShape(*[int(v) for v in shape])),
+                                 int(direction), int(dtype))
+
+
+def evo_trimul(a, w, x, shape, direction, dtype, stream=None) -> int:
+    """Enqueue the triangle multiplication (include/evo_attn.h); returns the status code."""
+    return _lib.evo_trimul(_addr(a), _addr(w), _addr(x), ctypes.byref(EvoTrimulShape(*[int(v) for v in shape])),
+                           int(direction), int(dtype), stream)
+
+
+def trimul(a, w, direction="outgoing", out=None, stream=None):
+    """torch wrapper: a, w contiguous [B, C, L, L] device tensors; returns x of the same shape and dtype."""
+    import torch
+    for name, t in (("a", a), ("w", w)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    x = torch.empty_like(a) if out is None else out
+    B, C, L, _ = a.shape
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device).cuda_stream
+    d = {"outgoing": EVO_TRIMUL_OUTGOING, "incoming": EVO_TRIMUL_INCOMING}[direction]
+    st = evo_trimul(a, w, x, (B, C, L), d, torch_dtype_code(a.dtype), stream)
+    if st != EVO_OK:
+        raise EvoAttnError(st)
+    return x

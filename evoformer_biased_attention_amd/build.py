@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libevoattn.so")
 SOURCES = ["evo_attn_api.cpp", "evo_attn_f32.hip", "evo_attn_bf16.hip", "evo_attn_bwd.hip",
-           "evo_attn_bwd_mfma.hip"]
+           "evo_attn_bwd_mfma.hip", "evo_trimul.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -327,6 +327,40 @@ extern "C" evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v
     return EVO_ERR_HIP;
 }
 
+extern "C" evo_status_t evo_trimul_check(const void* a, const void* w, const void* x,
+                                         const evo_trimul_shape_t* shape, evo_trimul_direction_t direction,
+                                         evo_dtype_t dtype) {
+    if (!shape || !a || !w || !x) return EVO_ERR_NULL_POINTER;
+    if (shape->B < 1 || shape->C < 1 || shape->L < 1) return EVO_ERR_BAD_SHAPE;
+    if (direction != EVO_TRIMUL_OUTGOING && direction != EVO_TRIMUL_INCOMING) return EVO_ERR_BAD_SHAPE;
+    if (dtype != EVO_DTYPE_F32 && dtype != EVO_DTYPE_BF16 && dtype != EVO_DTYPE_F16) return EVO_ERR_BAD_DTYPE;
+    int64_t bytes = elem_size(dtype);
+    for (int64_t s : {shape->B, shape->C, shape->L, shape->L}) bytes = mul_checked(bytes, s);
+    if (bytes < 0) return EVO_ERR_BAD_SHAPE;
+    for (const void* p : {a, w, x})
+        if (!aligned16(p)) return EVO_ERR_MISALIGNED;
+    const Extent ex = extent(x, bytes);
+    if (ex.overlaps(extent(a, bytes)) || ex.overlaps(extent(w, bytes))) return EVO_ERR_ALIASING;
+    // matrix-core kernel: 16-bit formats, L a multiple of 8, one plane's rows
+    // (up to L + 128 of them) addressed with 32-bit byte offsets
+    const int64_t L = shape->L;
+    if (dtype == EVO_DTYPE_F32 || L % 8 || L * L * 2 >= kMaxOffset || (L + 128) * L * 2 >= kMaxOffset32)
+        return EVO_ERR_UNSUPPORTED;
+    return EVO_OK;
+}
+
+extern "C" evo_status_t evo_trimul(const void* a, const void* w, void* x, const evo_trimul_shape_t* shape,
+                                   evo_trimul_direction_t direction, evo_dtype_t dtype, void* stream) {
+    const evo_status_t st = evo_trimul_check(a, w, x, shape, direction, dtype);
+    if (st != EVO_OK) return st;
+    const hipError_t err = evo::launch_trimul(a, w, x, shape->B * shape->C, shape->L,
+                                              direction == EVO_TRIMUL_INCOMING, dtype == EVO_DTYPE_F16,
+                                              static_cast<hipStream_t>(stream));
+    if (err == hipSuccess) return EVO_OK;
+    g_last_hip_error = static_cast<int>(err);
+    return EVO_ERR_HIP;
+}
+
 extern "C" int evo_attn_last_hip_error(void) { return g_last_hip_error; }
 
 extern "C" const char* evo_status_string(evo_status_t status) {

@@ -77,4 +77,8 @@ bool bwd_mfma_eligible(const BwdArgs& a, int dtype);
 int64_t bwd_dpair_chunks(int64_t B, int64_t N, int64_t L, int64_t H);
 hipError_t launch_bwd_mfma(const BwdArgs& a, int dtype, unsigned stages, hipStream_t stream);
 
+// Triangle multiplication, 16-bit formats, [planes][L][L] operands, L % 8 == 0.
+hipError_t launch_trimul(const void* a, const void* w, void* x, int64_t planes, int64_t L, int incoming, int f16,
+                         hipStream_t stream);
+
 }  // namespace evo

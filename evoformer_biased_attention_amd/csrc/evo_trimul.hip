@@ -1,0 +1,245 @@
+// Triangle multiplication on the matrix cores (bf16 / f16, fp32 accumulation).
+//
+// The cubic contraction of the triangle multiplicative update, per channel
+// (page "Accelerated molecular modeling with NVIDIA cuEquivariance and NVIDIA
+// NIM microservices", open-lab.net, the triangle-operations section names
+// it beside triangle attention as the O(N^3) hot spot; the two orientations
+// are the plain reading of a product through the third node):
+//   outgoing:  x[b,c,i,j] = sum_k a[b,c,i,k] w[b,c,j,k]      (X = A . W^T)
+//   incoming:  x[b,c,i,j] = sum_k a[b,c,k,i] w[b,c,k,j]      (X = A^T . W)
+// a, w, x are [B, C, L, L]; every (b, c) plane is an independent L x L x L
+// matrix product.
+//
+// Design (v_mfma_f32_16x16x32_{bf16,f16}, wave64):
+//  * The product is formed transposed, X^T tile = W-side operand (rows j) x
+//    A-side operand (columns i): a 16x16 result leaves j = 4g + 0..3 and
+//    i = c in lane c + 16g, so every lane stores 4 consecutive j of one row i
+//    (8 bytes).
+//  * Workgroup = 4 waves, a 128 x 128 tile of one plane (wave w: j rows
+//    64(w/2) .., i columns 64(w%2) ..; 4 x 4 MFMA tiles, 64 accumulators).
+//    The contraction runs over k in steps of 64; both operand tiles of a
+//    step are copied from global memory straight into LDS one step ahead
+//    (double buffered, one barrier per step).
+//  * outgoing: the tiles are [row][k] (rows i or j, 8 chunks of 8 k), read
+//    as 16-byte row chunks.  incoming: the tiles are [k][column] (16 chunks
+//    of 8 columns), read with the transposing ds_read_b64_tr_b16; both
+//    operands put k = 32kc + 16(e/4) + 4g + e%4 in element e of lane group g.
+//  * Buffer resources of one plane return zeros for rows past L; chunks of k
+//    past L get an offset past the range.  Hence L % 8 == 0.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "evo_attn_launch.h"
+
+namespace evo {
+namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16;
+
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int kTile = 128;  // output tile (i and j) per workgroup
+constexpr int kKS = 64;     // contraction step
+
+struct Bf16T {
+    typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+    typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+    __device__ static f32x4 mfma(v8 a, v8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
+};
+struct F16T {
+    typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+    typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+    __device__ static f32x4 mfma(v8 a, v8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+};
+
+template <class E>
+__device__ inline uint32_t pack2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, typename E::v2));
+}
+
+template <class E>
+__device__ inline typename E::v8 as_v8(uint4 x) { return __builtin_bit_cast(typename E::v8, x); }
+
+// ds_read_b64_tr_b16: with lane a of a 16-lane group addressing row R0 + a/4,
+// columns 4(a%4) .. +3 of a row-major 16-bit matrix, lane i receives column i
+// of rows R0 .. R0+3.
+__device__ inline uint2 ds_read_tr(const void* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((__attribute__((address_space(3))) char*)p));
+    return __builtin_bit_cast(uint2, r);
+}
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+__device__ inline Rsrc make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from the buffer into LDS (lane l at lds + 16 l); the
+// whole offset is per lane, so the range check sees it
+__device__ inline void dma16(Rsrc r, const void* lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, 0, 0, 0);
+}
+
+__device__ inline void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
+
+__device__ inline int64_t logical_block(int64_t hw, int64_t total) {
+    const int64_t xcd = hw % 8, j = hw / 8;
+    const int64_t per = total / 8, extra = total % 8;
+    return xcd < extra ? xcd * (per + 1) + j : extra * (per + 1) + (xcd - extra) * per + j;
+}
+
+struct TmParams {
+    const u16* a;
+    const u16* w;
+    u16* x;
+    int64_t L;
+    int64_t tdim;   // ceil(L / 128)
+    int64_t total;  // planes * tdim^2
+};
+
+// LDS per step: one tile of each operand, 16 KB each.
+//   outgoing, [row][k]: slot 8*row + (chunk ^ (row & 7)), 128 rows, chunk = 8 k
+//   incoming, [k][col]: slot 16*k + (chunk ^ 2(k & 7)), 64 rows of k, chunk = 8 columns
+struct TmBuf {
+    uint4 a[1024];
+    uint4 w[1024];
+};
+
+template <class E, bool INCOMING>
+__global__ __launch_bounds__(256, 2) void trimul_kernel(TmParams p) {
+    using V8 = typename E::v8;
+    __shared__ __attribute__((aligned(16))) TmBuf sm[2];
+
+    const int64_t id = logical_block(blockIdx.x, p.total);
+    const int64_t per_plane = p.tdim * p.tdim;
+    const int64_t plane = id / per_plane, t = id - plane * per_plane;
+    const int i0 = (int)(t % p.tdim) * kTile, j0 = (int)(t / p.tdim) * kTile;
+    const int L = (int)p.L;
+    const int64_t pbase = plane * p.L * p.L;
+    const uint32_t range = (uint32_t)L * (uint32_t)L * 2u;
+    const Rsrc ra = make_rsrc(p.a + pbase, range), rw = make_rsrc(p.w + pbase, range);
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int c = lane & 15, g = lane >> 4;
+    const int wm = wave >> 1, wn = wave & 1;  // the wave's j rows 64 wm .., i columns 64 wn ..
+    const int nsteps = (L + kKS - 1) / kKS;
+
+    // per-lane copy offsets of step 0 (k0 added per step)
+    uint32_t offa[4], offw[4];
+    for (int q = 0; q < 4; ++q) {
+        if (!INCOMING) {
+            // segment 4 wave + q: rows 8 (4 wave + q) + lane/8, slot lane % 8 holds chunk (lane%8) ^ (row & 7)
+            const int row = 8 * (4 * wave + q) + (lane >> 3);
+            const int chunk = (lane & 7) ^ (row & 7);
+            offa[q] = (uint32_t)(i0 + row) * (uint32_t)L * 2u + 16u * chunk;
+            offw[q] = (uint32_t)(j0 + row) * (uint32_t)L * 2u + 16u * chunk;
+        } else {
+            // segment 4 wave + q: k rows 4 (4 wave + q) + lane/16, slot lane % 16 holds chunk (lane%16) ^ 2(k & 7)
+            const int kr = 4 * (4 * wave + q) + (lane >> 4);
+            const int chunk = (lane & 15) ^ (2 * (kr & 7));
+            offa[q] = (uint32_t)kr * (uint32_t)L * 2u + (uint32_t)i0 * 2u + 16u * chunk;
+            offw[q] = (uint32_t)kr * (uint32_t)L * 2u + (uint32_t)j0 * 2u + 16u * chunk;
+        }
+    }
+    auto copy_step = [&](int st, TmBuf* __restrict__ dst) {
+        const int k0 = st * kKS;
+        for (int q = 0; q < 4; ++q) {
+            uint32_t oa, ow;
+            if (!INCOMING) {
+                // k of this lane's chunk: past L reads zero
+                const int row = 8 * (4 * wave + q) + (lane >> 3);
+                const int kk = k0 + 8 * ((lane & 7) ^ (row & 7));
+                oa = kk < L ? offa[q] + (uint32_t)k0 * 2u : kOOB;
+                ow = kk < L ? offw[q] + (uint32_t)k0 * 2u : kOOB;
+            } else {
+                oa = offa[q] + (uint32_t)k0 * (uint32_t)L * 2u;  // k rows past L start beyond the range
+                ow = offw[q] + (uint32_t)k0 * (uint32_t)L * 2u;
+            }
+            dma16(ra, &dst->a[64 * (4 * wave + q)], oa);
+            dma16(rw, &dst->w[64 * (4 * wave + q)], ow);
+        }
+    };
+
+    f32x4 acc[4][4];  // [m tile (j)][n tile (i)]
+    for (int mt = 0; mt < 4; ++mt)
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    copy_step(0, &sm[0]);
+    wait_all();
+    __syncthreads();
+    for (int st = 0; st < nsteps; ++st) {
+        const TmBuf* __restrict__ cur = &sm[st & 1];
+        // every LDS read of the step first: the compiler orders an LDS read
+        // that follows a copy into LDS behind that copy's completion
+        V8 aop[2][4], bop[2][4];  // A operand: W side (rows j); B operand: A side (columns i)
+        for (int kc = 0; kc < 2; ++kc)
+            for (int q = 0; q < 4; ++q) {
+                if (!INCOMING) {
+                    const int rj = 64 * wm + 16 * q + c, ri = 64 * wn + 16 * q + c, chunk = 4 * kc + g;
+                    aop[kc][q] = as_v8<E>(cur->w[8 * rj + (chunk ^ (rj & 7))]);
+                    bop[kc][q] = as_v8<E>(cur->a[8 * ri + (chunk ^ (ri & 7))]);
+                } else {
+                    // lane c + 16g addresses k row 32kc + 4g + c/4 (and 16 further), columns 4(c%4) .. +3 of
+                    // the 16-column group; it receives column c of k rows 32kc + 4g + 0..3 and + 16
+                    const int kr = 32 * kc + 4 * g + (c >> 2);
+                    const int colj = 64 * wm + 16 * q + 4 * (c & 3), coli = 64 * wn + 16 * q + 4 * (c & 3);
+                    const char* bw = reinterpret_cast<const char*>(cur->w);
+                    const char* ba = reinterpret_cast<const char*>(cur->a);
+                    auto addr = [&](const char* base, int k, int col) {
+                        return base + 16 * (16 * k + ((col >> 3) ^ (2 * (k & 7)))) + 2 * (col & 7);
+                    };
+                    const uint2 wl = ds_read_tr(addr(bw, kr, colj)), wh = ds_read_tr(addr(bw, kr + 16, colj));
+                    const uint2 al = ds_read_tr(addr(ba, kr, coli)), ah = ds_read_tr(addr(ba, kr + 16, coli));
+                    aop[kc][q] = as_v8<E>(uint4{wl.x, wl.y, wh.x, wh.y});
+                    bop[kc][q] = as_v8<E>(uint4{al.x, al.y, ah.x, ah.y});
+                }
+            }
+        if (st + 1 < nsteps) copy_step(st + 1, &sm[(st & 1) ^ 1]);
+        for (int kc = 0; kc < 2; ++kc)
+            for (int mt = 0; mt < 4; ++mt)
+                for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = E::mfma(aop[kc][mt], bop[kc][nt], acc[mt][nt]);
+        wait_all();
+        __syncthreads();
+    }
+
+    // lane c + 16g holds X^T[j = 64 wm + 16 mt + 4g + r][i = 64 wn + 16 nt + c]
+    for (int nt = 0; nt < 4; ++nt) {
+        const int i = i0 + 64 * wn + 16 * nt + c;
+        if (i >= L) continue;
+        for (int mt = 0; mt < 4; ++mt) {
+            const int j = j0 + 64 * wm + 16 * mt + 4 * g;
+            if (j >= L) continue;
+            *reinterpret_cast<uint2*>(p.x + pbase + (int64_t)i * L + j) =
+                uint2{pack2<E>(acc[mt][nt][0], acc[mt][nt][1]), pack2<E>(acc[mt][nt][2], acc[mt][nt][3])};
+        }
+    }
+}
+
+template <class E, bool INCOMING>
+hipError_t launch(TmParams& p, hipStream_t stream) {
+    void* args[] = {&p};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&trimul_kernel<E, INCOMING>), dim3((unsigned)p.total),
+                           dim3(256), args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_trimul(const void* a, const void* w, void* x, int64_t planes, int64_t L, int incoming, int f16,
+                         hipStream_t stream) {
+    TmParams p;
+    p.a = static_cast<const u16*>(a);
+    p.w = static_cast<const u16*>(w);
+    p.x = static_cast<u16*>(x);
+    p.L = L;
+    p.tdim = (L + kTile - 1) / kTile;
+    p.total = planes * p.tdim * p.tdim;
+    if (p.total >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
+    if (f16) return incoming ? launch<F16T, true>(p, stream) : launch<F16T, false>(p, stream);
+    return incoming ? launch<Bf16T, true>(p, stream) : launch<Bf16T, false>(p, stream);
+}
+
+}  // namespace evo

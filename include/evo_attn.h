@@ -225,6 +225,41 @@ evo_status_t evo_attn_bwd_check(const void* q, const void* k, const void* v, con
                                 const void* dpair_bias, const float* delta, const void* workspace,
                                 size_t workspace_bytes, const evo_shape_t* shape, evo_dtype_t dtype);
 
+/*
+ * Triangle multiplication: the cubic contraction of the triangle
+ * multiplicative update, per channel c.  The page "Accelerated molecular
+ * modeling with NVIDIA cuEquivariance and NVIDIA NIM microservices"
+ * (open-lab.net), in its section on triangle operations, names it with
+ * triangle attention as the O(N^3) hot spot of pair-representation models,
+ * motivated by transitivity (i near k and k near j relate i and j); the
+ * formula below is the plain reading of a product through the third node k,
+ * in its two orientations:
+ *   EVO_TRIMUL_OUTGOING:  x[b,c,i,j] = sum_k a[b,c,i,k] * w[b,c,j,k]
+ *   EVO_TRIMUL_INCOMING:  x[b,c,i,j] = sum_k a[b,c,k,i] * w[b,c,k,j]
+ * a, w and x are dense [B, C, L, L] tensors of `dtype` (channel-major: each
+ * (b, c) plane is an L x L row-major matrix), device memory owned by the
+ * caller; x may overlap neither input.  Products are accumulated in fp32 and
+ * x is rounded to nearest-even once.  The layer normalisations, projections
+ * and gates around this contraction in a model are O(L^2) per channel and
+ * not part of this call.
+ * Supported today: BF16 and F16 with L % 8 == 0, L <= 32767 and
+ * (L + 128) * L * 2 < 2^32; any B, C >= 1.  Other valid calls return
+ * EVO_ERR_UNSUPPORTED.  Errors as for evo_attn_fwd (a bad direction is
+ * EVO_ERR_BAD_SHAPE); nothing is written on error.
+ */
+typedef enum { EVO_TRIMUL_OUTGOING = 0, EVO_TRIMUL_INCOMING = 1 } evo_trimul_direction_t;
+
+typedef struct {
+    int64_t B, C, L;
+} evo_trimul_shape_t;
+
+evo_status_t evo_trimul(const void* a, const void* w, void* x, const evo_trimul_shape_t* shape,
+                        evo_trimul_direction_t direction, evo_dtype_t dtype, void* stream);
+
+/* The validation of evo_trimul alone; host-only. */
+evo_status_t evo_trimul_check(const void* a, const void* w, const void* x, const evo_trimul_shape_t* shape,
+                              evo_trimul_direction_t direction, evo_dtype_t dtype);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* evo_status_string(evo_status_t status);
 

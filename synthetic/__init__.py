@@ -135,6 +135,16 @@ def random_dout(shape, dtype="bf16", seed=0, scale=1.0) -> np.ndarray:
     return to_storage(scale * _normal(rng, tuple(shape)), dtype)
 
 
+def trimul_problem(B, C, L, dtype="bf16", seed=0, scale=1.0):
+    """Seeded operands of the triangle multiplication: a, w ~ N(0, scale^2), [B, C, L, L] in the storage format.
+    The named size is TRIMUL_WORKLOAD (a pair representation of 384 residues with 128 channels)."""
+    ra, rw = [np.random.default_rng(s) for s in np.random.SeedSequence([seed, 0x7A1]).spawn(2)]
+    return (to_storage(scale * _normal(ra, (B, C, L, L)), dtype), to_storage(scale * _normal(rw, (B, C, L, L)), dtype))
+
+
+TRIMUL_WORKLOAD = dict(name="trimul_bf16_384x128", B=1, C=128, L=384, dtype="bf16")
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads.  Each draws from SeedSequence(1000 + c) spawned
 # into six streams used in a fixed order: q, k, v, mask, pair tensor z, W.

@@ -335,3 +335,37 @@ def test_dense_entry_matches_strided_with_dense_layout():
     for shape in ((1, 2, 64, 4, 32), (2, 3, 17, 2, 16), (1, 1, 1, 1, 8)):
         for dt in (E.EVO_DTYPE_BF16, E.EVO_DTYPE_F16, E.EVO_DTYPE_F32):
             assert check(shape=shape, dtype=dt) == scheck(E.evo_attn_dense_layout(shape), shape=shape, dtype=dt)
+
+
+# ---------------------------------------------------------------------------
+# evo_trimul_check
+# ---------------------------------------------------------------------------
+def tcheck(shape=(1, 4, 64), direction=E.EVO_TRIMUL_OUTGOING, dtype=E.EVO_DTYPE_BF16, **over):
+    a, w, x = addrs(3)
+    args = dict(a=a, w=w, x=x)
+    args.update(over)
+    return E.evo_trimul_check(args["a"], args["w"], args["x"], shape, direction, dtype)
+
+
+def test_trimul_valid():
+    for d in (E.EVO_TRIMUL_OUTGOING, E.EVO_TRIMUL_INCOMING):
+        for dt in (E.EVO_DTYPE_BF16, E.EVO_DTYPE_F16):
+            for shape in ((1, 1, 8), (2, 3, 72), (1, 128, 384)):
+                assert tcheck(shape=shape, direction=d, dtype=dt) == E.EVO_OK
+    a, *_ = addrs(1)
+    assert tcheck(w=a) == E.EVO_OK                          # the operands may be one tensor
+
+
+def test_trimul_errors():
+    for name in ("a", "w", "x"):
+        assert tcheck(**{name: None}) == E.EVO_ERR_NULL_POINTER
+    assert tcheck(shape=(1, 0, 64)) == E.EVO_ERR_BAD_SHAPE
+    assert tcheck(direction=2) == E.EVO_ERR_BAD_SHAPE
+    assert tcheck(dtype=5) == E.EVO_ERR_BAD_DTYPE
+    a, w, x = addrs(3)
+    assert tcheck(x=a) == E.EVO_ERR_ALIASING
+    assert tcheck(x=w + 64 * 64 * 2 * 4 - 16) == E.EVO_ERR_ALIASING   # starts inside w's last 16 bytes
+    assert tcheck(x=x + 8) == E.EVO_ERR_MISALIGNED
+    assert tcheck(shape=(1, 4, 100)) == E.EVO_ERR_UNSUPPORTED          # L % 8 != 0
+    assert tcheck(dtype=E.EVO_DTYPE_F32) == E.EVO_ERR_UNSUPPORTED
+    assert tcheck(shape=(1, 1, 32768)) == E.EVO_ERR_UNSUPPORTED        # L * L * 2 = 2^31
