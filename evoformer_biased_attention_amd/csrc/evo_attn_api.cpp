@@ -66,7 +66,7 @@ bool rows_fit(int64_t L, int64_t row_elems, int64_t last_row_bytes) {
 }
 
 bool dim_supported(evo_dtype_t dt, int64_t D) {
-    if (dt == EVO_DTYPE_BF16 || dt == EVO_DTYPE_F16) return D == 8 || D == 16 || D == 32;
+    if (dt == EVO_DTYPE_BF16 || dt == EVO_DTYPE_F16) return D == 8 || D == 16 || D == 32 || D == 64;
     return dt == EVO_DTYPE_F32 && (D == 8 || D == 16 || D == 32 || D == 64);
 }
 

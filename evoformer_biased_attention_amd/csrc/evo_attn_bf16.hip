@@ -1,4 +1,5 @@
-// bf16 forward kernel for head dimension 32 on gfx950 (MI355X).
+// 16-bit (bf16, f16) forward kernel on gfx950 (MI355X): head dimensions 8, 16
+// and 32 on the fast path below, 64 on the exact path.
 //
 // Operation (page "DeepSpeed DS4Sci_EvoformerAttention 内核实战指南",
 // hmyw.cn, sections 4, 5.2 and 5.4): for each (b, n, h) slice and query i,
@@ -122,11 +123,13 @@ struct FastSmem {
 };
 
 // LDS of the exact path.
-constexpr int kKStride = kMaxD + 8;  // row of K (one key), 16-bit elements
-constexpr int kVtStride = kKB + 8;  // row of transposed V (one d), bf16 elements
+// The exact path also serves D = 64 (two 32-wide halves of the contraction).
+constexpr int kExactMaxD = 64;
+constexpr int kKStride = kExactMaxD + 8;  // row of K (one key), 16-bit elements
+constexpr int kVtStride = kKB + 8;        // row of transposed V (one d), 16-bit elements
 struct ExactSmem {
     u16 k[kKB * kKStride];
-    u16 vt[kMaxD * kVtStride];
+    u16 vt[kExactMaxD * kVtStride];
 };
 
 union Smem {
@@ -547,21 +550,24 @@ template <class E, int D>
 __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int tid) {
     using V8 = typename E::v8;
     constexpr int kDHT = (D + 15) / 16;  // 16-wide d tiles of the output; dimensions past D are zero
+    constexpr int kDH = (D + 31) / 32;   // 32-wide halves of the contraction over d
     const int64_t L = p.L;
     const int lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
 
-    V8 qop[kQTiles];
+    V8 qop[kQTiles][kDH];
     for (int t = 0; t < kQTiles; ++t) {
         int64_t i = s.q0 + 16 * t + c;
         if (i >= L) i = L - 1;
-        qop[t] = as_v8<E>(8 * g < D ? load16(p.q + s.qb + i * s.ql + 8 * g) : uint4{0u, 0u, 0u, 0u});
+        for (int hh = 0; hh < kDH; ++hh) {
+            const int d0 = 32 * hh + 8 * g;
+            qop[t][hh] = as_v8<E>(d0 < D ? load16(p.q + s.qb + i * s.ql + d0) : uint4{0u, 0u, 0u, 0u});
+        }
     }
-    f32x4 oacc[kQTiles][2];
+    f32x4 oacc[kQTiles][kDHT];
     float mrun[kQTiles], lrun[kQTiles];
     for (int t = 0; t < kQTiles; ++t) {
-        oacc[t][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        oacc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int dh = 0; dh < kDHT; ++dh) oacc[t][dh] = f32x4{0.f, 0.f, 0.f, 0.f};
         mrun[t] = -INFINITY;
         lrun[t] = 0.f;
     }
@@ -569,21 +575,32 @@ __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int ti
     const int skey = tid >> 2, sdc = (tid & 3) * 8;
 
     for (int64_t k0 = 0; k0 < L; k0 += kKB) {
-        uint4 kk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-        if (k0 + skey < L && sdc < D) {
-            kk = load16(p.k + s.kb + (k0 + skey) * s.kl + sdc);
-            vv = load16(p.v + s.vb + (k0 + skey) * s.vl + sdc);
+        // each thread stages kDH 16-byte chunks of one key row: d-values 32 hh + sdc .. +7
+        uint4 kk[kDH], vv[kDH];
+        for (int hh = 0; hh < kDH; ++hh) {
+            kk[hh] = vv[hh] = uint4{0u, 0u, 0u, 0u};
+            if (k0 + skey < L && 32 * hh + sdc < D) {
+                kk[hh] = load16(p.k + s.kb + (k0 + skey) * s.kl + 32 * hh + sdc);
+                vv[hh] = load16(p.v + s.vb + (k0 + skey) * s.vl + 32 * hh + sdc);
+            }
         }
         __syncthreads();  // previous block's readers are done
-        *reinterpret_cast<uint4*>(&sm.k[skey * kKStride + sdc]) = kk;
-        const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-        for (int e = 0; e < 8; ++e) sm.vt[(sdc + e) * kVtStride + skey] = (u16)(w[e / 2] >> (16 * (e % 2)));
+        for (int hh = 0; hh < kDH; ++hh) {
+            *reinterpret_cast<uint4*>(&sm.k[skey * kKStride + 32 * hh + sdc]) = kk[hh];
+            const uint32_t w[4] = {vv[hh].x, vv[hh].y, vv[hh].z, vv[hh].w};
+            for (int e = 0; e < 8; ++e)
+                sm.vt[(32 * hh + sdc + e) * kVtStride + skey] = (u16)(w[e / 2] >> (16 * (e % 2)));
+        }
         __syncthreads();
 
         f32x4 acc[kQTiles][kKT];
         for (int kt = 0; kt < kKT; ++kt) {
-            const V8 kop = as_v8<E>(*reinterpret_cast<const uint4*>(&sm.k[(16 * kt + c) * kKStride + 8 * g]));
-            for (int t = 0; t < kQTiles; ++t) acc[t][kt] = E::mfma(kop, qop[t], f32x4{0.f, 0.f, 0.f, 0.f});
+            for (int t = 0; t < kQTiles; ++t) acc[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int hh = 0; hh < kDH; ++hh) {
+                const V8 kop =
+                    as_v8<E>(*reinterpret_cast<const uint4*>(&sm.k[(16 * kt + c) * kKStride + 32 * hh + 8 * g]));
+                for (int t = 0; t < kQTiles; ++t) acc[t][kt] = E::mfma(kop, qop[t][hh], acc[t][kt]);
+            }
         }
         for (int kt = 0; kt < kKT; ++kt) {
             const int64_t jb = k0 + 16 * kt + 4 * g;
@@ -616,8 +633,7 @@ __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int ti
                 }
             lrun[t] = lrun[t] * alpha + ls;
             mrun[t] = mnew;
-            oacc[t][0] *= alpha;
-            oacc[t][1] *= alpha;
+            for (int dh = 0; dh < kDHT; ++dh) oacc[t][dh] *= alpha;
             for (int cc = 0; cc < 2; ++cc) {
                 const f32x4 a = acc[t][2 * cc], b = acc[t][2 * cc + 1];
                 pmat[t][cc] = as_v8<E>(uint4{pack2<E>(a[0], a[1]), pack2<E>(a[2], a[3]), pack2<E>(b[0], b[1]), pack2<E>(b[2], b[3])});
@@ -673,7 +689,7 @@ __global__ __launch_bounds__(kWaves * 64, 3) void fwd_16bit_kernel(Params p) {
     s.pbase = p.pair ? p.pair + s.b * st.pb + s.h * st.ph : nullptr;
     s.lrow = p.lse ? p.lse + ((s.b * p.N + s.n) * p.H + s.h) * st.lrow : nullptr;
 
-    if (FAST) {
+    if constexpr (FAST) {
         if (run_fast<E, D, PAIR, MASK>(p, s, sm.f, tid)) return;
         __syncthreads();
     }
@@ -706,10 +722,21 @@ hipError_t launch_dim(Params& p, hipStream_t stream) {
     return launch_biases<E, D, false, false>(p, stream);
 }
 
+// D = 64: the matrix-core exact path (its fast-path layouts are 32 wide)
+template <class E>
+hipError_t launch_d64(Params& p, hipStream_t stream) {
+    const bool pair = p.pair != nullptr, mask = p.mask != nullptr;
+    if (pair && mask) return launch_variant<E, 64, true, true, false>(p, stream);
+    if (pair) return launch_variant<E, 64, true, false, false>(p, stream);
+    if (mask) return launch_variant<E, 64, false, true, false>(p, stream);
+    return launch_variant<E, 64, false, false, false>(p, stream);
+}
+
 template <class E>
 hipError_t launch_format(Params& p, int64_t d, hipStream_t stream) {
     if (d == 8) return launch_dim<E, 8>(p, stream);
     if (d == 16) return launch_dim<E, 16>(p, stream);
+    if (d == 64) return launch_d64<E>(p, stream);
     return launch_dim<E, 32>(p, stream);
 }
 
@@ -749,7 +776,7 @@ hipError_t launch_fwd_16bit(const FwdArgs& a, hipStream_t stream, bool f16) {
     p.qblocks = make_fastdiv((uint32_t)qblocks);
     p.nd = make_fastdiv((uint32_t)a.N);
     p.hd = make_fastdiv((uint32_t)a.H);
-    if (a.D != 8 && a.D != 16 && a.D != 32) return hipErrorInvalidValue;
+    if (a.D != 8 && a.D != 16 && a.D != 32 && a.D != 64) return hipErrorInvalidValue;
     const double sqd = std::sqrt((double)a.D);
     p.c1 = (float)(1.4426950408889634 / sqd);
     const uint16_t hi = bits16_rne(sqd, f16);

@@ -30,10 +30,10 @@ struct FwdArgs {
     Strides st;
 };
 
-// bf16 inputs, D in {8, 16, 32}: MFMA kernel.  Returns the hipError_t of the launch.
+// bf16 inputs, D in {8, 16, 32, 64}: MFMA kernel.  Returns the hipError_t of the launch.
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 
-// f16 inputs, D in {8, 16, 32}: the same MFMA kernel on binary16 operands.
+// f16 inputs, D in {8, 16, 32, 64}: the same MFMA kernel on binary16 operands.
 hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t stream);
 
 // f32 inputs, D in {8, 16, 32, 64}: vector-ALU kernel.

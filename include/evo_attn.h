@@ -85,7 +85,7 @@ typedef enum {
  *   pair_bias   [B,1,H,L,L] or NULL (no pair bias: all zero)
  *   out         output, [B,N,L,H,D], same dtype as q
  *   lse         output, [B,N,H,L] float32, or NULL to skip it
- * Supported today: dtype BF16 or F16 with D in {8, 16, 32} (MFMA path; it
+ * Supported today: dtype BF16 or F16 with D in {8, 16, 32, 64} (MFMA path; it
  * addresses one head's rows of a slice and the rows of a pair matrix with
  * 32-bit byte offsets, so it needs (L - 1) * H * D * 2 + 2 D < 2^31 and
  * (L - 1) * L * 2 + 2 L < 2^31 (L <= 32767), and rows up to L + 128 below

@@ -67,7 +67,7 @@ def check(shape=(1, 2, 64, 4, 32), dtype=E.EVO_DTYPE_BF16, **over):
 def test_valid_bf16_f16_and_f32():
     assert check() == E.EVO_OK
     assert check(dtype=E.EVO_DTYPE_F16) == E.EVO_OK
-    for d in (8, 16, 32):
+    for d in (8, 16, 32, 64):
         assert check(shape=(2, 3, 17, 2, d)) == E.EVO_OK
         assert check(shape=(2, 3, 17, 2, d), dtype=E.EVO_DTYPE_F16) == E.EVO_OK
     assert check(mask_bias=None, pair_bias=None, lse=None) == E.EVO_OK
@@ -122,7 +122,7 @@ def test_inputs_may_alias_each_other():
     assert check(k=q, v=q) == E.EVO_OK  # self-attention on one tensor is legal: inputs are read-only
 
 
-@pytest.mark.parametrize("dtype,d", [(E.EVO_DTYPE_BF16, 64), (E.EVO_DTYPE_BF16, 24), (E.EVO_DTYPE_F16, 64),
+@pytest.mark.parametrize("dtype,d", [(E.EVO_DTYPE_BF16, 128), (E.EVO_DTYPE_BF16, 24), (E.EVO_DTYPE_F16, 128),
                                      (E.EVO_DTYPE_F16, 4), (E.EVO_DTYPE_F32, 12), (E.EVO_DTYPE_F32, 128)])
 def test_unsupported(dtype, d):
     assert check(shape=(1, 1, 32, 1, d), dtype=dtype) == E.EVO_ERR_UNSUPPORTED

@@ -289,12 +289,12 @@ def test_errors_write_nothing(torch_dev):
     """Rejected calls return a status and leave the outputs untouched."""
     torch = torch_dev
     import evoformer_biased_attention_amd as E
-    q = torch.zeros((1, 1, 32, 1, 64), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((1, 1, 32, 1, 128), dtype=torch.bfloat16, device="cuda")
     out = torch.full_like(q, 7.0)
-    st = E.evo_attn_fwd(q, q, q, None, None, out, None, (1, 1, 32, 1, 64), E.EVO_DTYPE_BF16,
+    st = E.evo_attn_fwd(q, q, q, None, None, out, None, (1, 1, 32, 1, 128), E.EVO_DTYPE_BF16,
                         torch.cuda.current_stream().cuda_stream)
     assert st == E.EVO_ERR_UNSUPPORTED
-    st = E.evo_attn_fwd(q, q, q, None, None, q, None, (1, 1, 32, 1, 64), E.EVO_DTYPE_BF16, None)
+    st = E.evo_attn_fwd(q, q, q, None, None, q, None, (1, 1, 32, 1, 128), E.EVO_DTYPE_BF16, None)
     assert st == E.EVO_ERR_ALIASING
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
@@ -326,3 +326,24 @@ def test_rows_past_L_read_as_zero(torch_dev, dtype):
     l = lse.cpu().numpy().astype(np.float64)
     ro, rl = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype=dtype, nthreads=THREADS)
     compare(o, l, ro, rl, dtype, "NaN after every input")
+
+
+# ---------------------------------------------------------------------------
+# Head dimension 64 on the 16-bit path (the exact path's two 32-wide halves).
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1), (1, 2, 17, 3), (2, 2, 64, 2), (1, 3, 100, 4), (1, 2, 257, 2)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_head_dim_64(torch_dev, shape, dtype):
+    B, N, L, H = shape
+    w = S.random_problem(B, N, L, H, 64, dtype=dtype, seed=B * 100 + N * 10 + L + H, mask="tail", pair="normal",
+                         mask_frac=0.3)
+    say(f"head dim 64 {dtype} {shape}")
+    parity_full(torch_dev, w)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_head_dim_64_msa_row_shape(torch_dev, dtype):
+    """An MSA-row problem with the largest head dimension the guide's backward allows (section 5.4: D <= 64)."""
+    w = S.random_problem(1, 16, 256, 4, 64, dtype=dtype, seed=64, mask="tail", pair="normal", mask_frac=0.1)
+    parity_full(torch_dev, w)
