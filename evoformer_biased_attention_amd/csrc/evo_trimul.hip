@@ -17,6 +17,8 @@
 //    (8 bytes).
 //  * Workgroup = 4 waves, a 128 x 128 tile of one plane (wave w: j rows
 //    64(w/2) .., i columns 64(w%2) ..; 4 x 4 MFMA tiles, 64 accumulators).
+//    The result leaves through LDS so that every store is a 16-byte piece of
+//    a whole 128-byte row segment, written non-temporally.
 //    The contraction runs over k in steps of 64; both operand tiles of a
 //    step are copied from global memory straight into LDS one step ahead
 //    (double buffered, one barrier per step).
@@ -41,7 +43,6 @@ typedef uint16_t u16;
 
 constexpr uint32_t kOOB = 0x80000000u;
 constexpr int kTile = 128;  // output tile (i and j) per workgroup
-constexpr int kKS = 64;     // contraction step
 
 struct Bf16T {
     typedef __bf16 v8 __attribute__((ext_vector_type(8)));
@@ -101,18 +102,28 @@ struct TmParams {
     int64_t total;  // planes * tdim^2
 };
 
-// LDS per step: one tile of each operand, 16 KB each.
-//   outgoing, [row][k]: slot 8*row + (chunk ^ (row & 7)), 128 rows, chunk = 8 k
-//   incoming, [k][col]: slot 16*k + (chunk ^ 2(k & 7)), 64 rows of k, chunk = 8 columns
+// LDS per step: one tile of each operand, 128 x KS 16-bit values each.
+//   outgoing, [row][k]: CPR = KS/8 chunks of 8 k per row; slot CPR*row + (chunk ^ swz(row)),
+//     swz = row & 7 for KS = 64, (row >> 2) & 3 for KS = 32 (rows sharing a bank group differ in slot)
+//   incoming, [k][col]: KS rows of k, 16 chunks of 8 columns; slot 16*k + (chunk ^ 2(k & 7))
+template <int KS>
 struct TmBuf {
-    uint4 a[1024];
-    uint4 w[1024];
+    uint4 a[16 * KS];
+    uint4 w[16 * KS];
 };
 
-template <class E, bool INCOMING>
-__global__ __launch_bounds__(256, 2) void trimul_kernel(TmParams p) {
+template <int KS>
+__device__ inline int tm_swz(int row) {
+    return KS == 64 ? (row & 7) : ((row >> 2) & 3);
+}
+
+template <class E, bool INCOMING, int KS>
+__global__ __launch_bounds__(256, KS == 64 ? 2 : 3) void trimul_kernel(TmParams p) {
     using V8 = typename E::v8;
-    __shared__ __attribute__((aligned(16))) TmBuf sm[2];
+    constexpr int CPR = KS / 8;        // outgoing: 16-byte chunks per tile row
+    constexpr int SEG = KS / 16;       // 1 KB copy segments per wave per operand per step
+    constexpr int KC = KS / 32;        // 32-wide contraction chunks per step
+    __shared__ __attribute__((aligned(16))) TmBuf<KS> sm[2];
 
     const int64_t id = logical_block(blockIdx.x, p.total);
     const int64_t per_plane = p.tdim * p.tdim;
@@ -126,41 +137,41 @@ __global__ __launch_bounds__(256, 2) void trimul_kernel(TmParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;  // the wave's j rows 64 wm .., i columns 64 wn ..
-    const int nsteps = (L + kKS - 1) / kKS;
+    const int nsteps = (L + KS - 1) / KS;
 
-    // per-lane copy offsets of step 0 (k0 added per step)
-    uint32_t offa[4], offw[4];
-    for (int q = 0; q < 4; ++q) {
+    // per-lane copy offsets of step 0 (k0 added per step); segment s = SEG wave + q
+    uint32_t offa[SEG], offw[SEG];
+    int kofs[SEG];  // outgoing: k of this lane's chunk within the step
+    for (int q = 0; q < SEG; ++q) {
+        const int seg = SEG * wave + q;
         if (!INCOMING) {
-            // segment 4 wave + q: rows 8 (4 wave + q) + lane/8, slot lane % 8 holds chunk (lane%8) ^ (row & 7)
-            const int row = 8 * (4 * wave + q) + (lane >> 3);
-            const int chunk = (lane & 7) ^ (row & 7);
+            const int row = seg * (64 / CPR) + lane / CPR;
+            const int chunk = (lane % CPR) ^ tm_swz<KS>(row);
+            kofs[q] = 8 * chunk;
             offa[q] = (uint32_t)(i0 + row) * (uint32_t)L * 2u + 16u * chunk;
             offw[q] = (uint32_t)(j0 + row) * (uint32_t)L * 2u + 16u * chunk;
         } else {
-            // segment 4 wave + q: k rows 4 (4 wave + q) + lane/16, slot lane % 16 holds chunk (lane%16) ^ 2(k & 7)
-            const int kr = 4 * (4 * wave + q) + (lane >> 4);
+            const int kr = 4 * seg + (lane >> 4);
             const int chunk = (lane & 15) ^ (2 * (kr & 7));
+            kofs[q] = 0;
             offa[q] = (uint32_t)kr * (uint32_t)L * 2u + (uint32_t)i0 * 2u + 16u * chunk;
             offw[q] = (uint32_t)kr * (uint32_t)L * 2u + (uint32_t)j0 * 2u + 16u * chunk;
         }
     }
-    auto copy_step = [&](int st, TmBuf* __restrict__ dst) {
-        const int k0 = st * kKS;
-        for (int q = 0; q < 4; ++q) {
+    auto copy_step = [&](int st, TmBuf<KS>* __restrict__ dst) {
+        const int k0 = st * KS;
+        for (int q = 0; q < SEG; ++q) {
             uint32_t oa, ow;
             if (!INCOMING) {
-                // k of this lane's chunk: past L reads zero
-                const int row = 8 * (4 * wave + q) + (lane >> 3);
-                const int kk = k0 + 8 * ((lane & 7) ^ (row & 7));
-                oa = kk < L ? offa[q] + (uint32_t)k0 * 2u : kOOB;
-                ow = kk < L ? offw[q] + (uint32_t)k0 * 2u : kOOB;
+                const bool in = k0 + kofs[q] < L;  // chunks of k past L read zero
+                oa = in ? offa[q] + (uint32_t)k0 * 2u : kOOB;
+                ow = in ? offw[q] + (uint32_t)k0 * 2u : kOOB;
             } else {
                 oa = offa[q] + (uint32_t)k0 * (uint32_t)L * 2u;  // k rows past L start beyond the range
                 ow = offw[q] + (uint32_t)k0 * (uint32_t)L * 2u;
             }
-            dma16(ra, &dst->a[64 * (4 * wave + q)], oa);
-            dma16(rw, &dst->w[64 * (4 * wave + q)], ow);
+            dma16(ra, &dst->a[64 * (SEG * wave + q)], oa);
+            dma16(rw, &dst->w[64 * (SEG * wave + q)], ow);
         }
     };
 
@@ -172,16 +183,16 @@ __global__ __launch_bounds__(256, 2) void trimul_kernel(TmParams p) {
     wait_all();
     __syncthreads();
     for (int st = 0; st < nsteps; ++st) {
-        const TmBuf* __restrict__ cur = &sm[st & 1];
+        const TmBuf<KS>* __restrict__ cur = &sm[st & 1];
         // every LDS read of the step first: the compiler orders an LDS read
         // that follows a copy into LDS behind that copy's completion
-        V8 aop[2][4], bop[2][4];  // A operand: W side (rows j); B operand: A side (columns i)
-        for (int kc = 0; kc < 2; ++kc)
+        V8 aop[KC][4], bop[KC][4];  // A operand: w side (rows j); B operand: a side (columns i)
+        for (int kc = 0; kc < KC; ++kc)
             for (int q = 0; q < 4; ++q) {
                 if (!INCOMING) {
                     const int rj = 64 * wm + 16 * q + c, ri = 64 * wn + 16 * q + c, chunk = 4 * kc + g;
-                    aop[kc][q] = as_v8<E>(cur->w[8 * rj + (chunk ^ (rj & 7))]);
-                    bop[kc][q] = as_v8<E>(cur->a[8 * ri + (chunk ^ (ri & 7))]);
+                    aop[kc][q] = as_v8<E>(cur->w[CPR * rj + (chunk ^ tm_swz<KS>(rj))]);
+                    bop[kc][q] = as_v8<E>(cur->a[CPR * ri + (chunk ^ tm_swz<KS>(ri))]);
                 } else {
                     // lane c + 16g addresses k row 32kc + 4g + c/4 (and 16 further), columns 4(c%4) .. +3 of
                     // the 16-column group; it receives column c of k rows 32kc + 4g + 0..3 and + 16
@@ -199,31 +210,42 @@ __global__ __launch_bounds__(256, 2) void trimul_kernel(TmParams p) {
                 }
             }
         if (st + 1 < nsteps) copy_step(st + 1, &sm[(st & 1) ^ 1]);
-        for (int kc = 0; kc < 2; ++kc)
+        for (int kc = 0; kc < KC; ++kc)
             for (int mt = 0; mt < 4; ++mt)
                 for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = E::mfma(aop[kc][mt], bop[kc][nt], acc[mt][nt]);
         wait_all();
         __syncthreads();
     }
 
-    // lane c + 16g holds X^T[j = 64 wm + 16 mt + 4g + r][i = 64 wn + 16 nt + c]
-    for (int nt = 0; nt < 4; ++nt) {
-        const int i = i0 + 64 * wn + 16 * nt + c;
-        if (i >= L) continue;
-        for (int mt = 0; mt < 4; ++mt) {
-            const int j = j0 + 64 * wm + 16 * mt + 4 * g;
-            if (j >= L) continue;
-            *reinterpret_cast<uint2*>(p.x + pbase + (int64_t)i * L + j) =
+    // Epilogue through LDS: lane c + 16g holds X^T[j = 64 wm + 16 mt + 4g + r][i = 64 wn + 16 nt + c]; each
+    // wave writes its 64 x 64 block of x as [i][j] rows (padded to 72 against bank conflicts), then stores
+    // whole 128-byte row segments, 16 bytes per lane.  The operand buffers are free (the loop ended with a
+    // barrier) and each wave reads back only what it wrote.
+    constexpr int kRow = 72;
+    static_assert(4 * 64 * kRow * 2 <= (int)sizeof(sm), "epilogue tile fits the operand buffers");
+    u16* tile = reinterpret_cast<u16*>(&sm[0]) + wave * 64 * kRow;
+    for (int nt = 0; nt < 4; ++nt)
+        for (int mt = 0; mt < 4; ++mt)
+            *reinterpret_cast<uint2*>(tile + (16 * nt + c) * kRow + 16 * mt + 4 * g) =
                 uint2{pack2<E>(acc[mt][nt][0], acc[mt][nt][1]), pack2<E>(acc[mt][nt][2], acc[mt][nt][3])};
-        }
+    // x is not read again here: streaming (non-temporal) stores
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const int ib = i0 + 64 * wn, jc = j0 + 64 * wm + 8 * (lane & 7);
+    for (int pass = 0; pass < 8; ++pass) {
+        const int row = 8 * pass + (lane >> 3);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(tile + row * kRow + 8 * (lane & 7));
+        if (ib + row < L && jc < L)
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p.x + pbase + (int64_t)(ib + row) * L + jc));
     }
 }
+
+constexpr int kKStep = 64;  // contraction step (a 32-wide step measured no faster and leaves too little LDS for the epilogue)
 
 template <class E, bool INCOMING>
 hipError_t launch(TmParams& p, hipStream_t stream) {
     void* args[] = {&p};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&trimul_kernel<E, INCOMING>), dim3((unsigned)p.total),
-                           dim3(256), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&trimul_kernel<E, INCOMING, kKStep>),
+                           dim3((unsigned)p.total), dim3(256), args, 0, stream);
 }
 
 }  // namespace
