@@ -85,6 +85,9 @@ def main():
     ap.add_argument("--op", choices=["attention", "trimul"], default="attention",
                     help="trimul: time evo_trimul on the named triangle-multiplication size instead")
     ap.add_argument("--direction", choices=["outgoing", "incoming"], default="outgoing", help="trimul orientation")
+    ap.add_argument("--sweep", choices=["ds4sci"], default=None,
+                    help="ds4sci: forward and backward over batch 1..16 at N=L=256, H=4, D=32, fp16 "
+                         "(the DS4Sci guide's benchmark shape); prints one JSON line with every batch")
     ap.add_argument("--layout", choices=["dense", "transposed"], default="dense",
                     help="fwd: transposed stores Q/K/V/O as X[B, L, N, H, D] and reads them in place through "
                          "evo_attn_fwd_strided (triangle attention around the ending node without a copy)")
@@ -126,6 +129,8 @@ def main():
 
     if args.op == "trimul":
         return bench_trimul(args, torch, E, S)
+    if args.sweep:
+        return bench_sweep(args, torch, E, S)
 
     log(f"bench: generating workload {args.workload}")
     w = S.workload(args.workload, dtype=args.dtype)
@@ -452,6 +457,111 @@ def bench_bwd(args, w, dev, torch, E, S):
                                   "sample": f"{passes} full backward pass(es) over workload {w.name} in fp64, "
                                             f"{t:.1f} s",
                                   "parity_vs_gpu_max_err_over_max_ref": err}
+    print(json.dumps(result), flush=True)
+
+
+SWEEP_METRIC = "biased-attention fwd+bwd TFLOP/s over batch 1..16, N=L=256, H=4, D=32, fp16"
+
+
+def _event_time_us(torch, launch, R, steps, warmup):
+    """Average time per launch (HIP events around `steps` back-to-back launches), inputs rotating over R sets."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        launch(i % R)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(steps):
+        launch(i % R)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return 1e3 * ev0.elapsed_time(ev1) / steps
+
+
+def bench_sweep(args, torch, E, S):
+    """The DS4Sci guide's benchmark shape (section 4 of its page): N=L=256,
+    H=4, D=32, fp16, with a mask and a pair bias, batch 1 to 16.  Per batch:
+    the forward (4*B*N*H*L^2*D flops) and the backward (10*B*N*H*L^2*D) each
+    timed with HIP events over the launch stream, inputs rotated over enough
+    copies to miss the Infinity Cache.  `value` is the fwd+bwd throughput at
+    batch 16.  The guide prints no MI355X or absolute figure for this shape, so
+    vs_baseline is null."""
+    batches = [1, 2, 4, 8, 16]
+    N, L, H, D, dt = 256, 256, 4, 32, "f16"
+    log(f"sweep: generating B={batches[-1]} N={N} L={L} H={H} D={D} {dt}")
+    w = S.random_problem(batches[-1], N, L, H, D, dtype=dt, seed=4781, mask="tail", pair="normal")
+    dout = S.random_dout(w.shape, dt, seed=2026)
+    dcode = E.EVO_DTYPE_F16
+
+    def dev(x):
+        return torch.from_numpy(x).view(torch.float16).to("cuda")
+
+    full = [dev(x) for x in (w.q, w.k, w.v, w.mask, w.pair, dout)]
+    stream_h = torch.cuda.current_stream().cuda_stream
+    rows = []
+    t_total = {"fwd": 0.0, "bwd": 0.0}
+    for B in batches:
+        shape = (B, N, L, H, D)
+        base = [t[:B].contiguous() for t in full]
+        in_bytes = sum(t.numel() * t.element_size() for t in base)
+        R = max(2, math.ceil(2.5 * MALL_BYTES / (2 * in_bytes)))
+        sets = []
+        for r in range(R):
+            q, k, v, m, p, do = base if r == 0 else [t.clone() for t in base]
+            o, l = E.fwd(q, k, v, m, p)
+            grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(m),
+                     torch.empty_like(p), torch.empty((B, N, H, L), dtype=torch.float32, device="cuda")]
+            sets.append(((q, k, v, m, p, do, o, l), grads))
+        ws_bytes = E.evo_attn_bwd_workspace_size(shape, dcode)
+        ws = torch.empty(max(ws_bytes, 4) // 4, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+
+        def fwd(r):
+            (q, k, v, m, p, _, o, l), _g = sets[r]
+            return E.evo_attn_fwd(q, k, v, m, p, o, l, shape, dcode, stream_h)
+
+        def bwd(r):
+            (q, k, v, m, p, do, o, l), (dq, dk, dv, dm, dp, delta) = sets[r]
+            return E.evo_attn_bwd(q, k, v, m, p, o, l, do, dq, dk, dv, dm, dp, delta, shape, dcode, stream_h,
+                                  workspace=ws, workspace_bytes=ws_bytes)
+
+        for f in (fwd, bwd):
+            st = f(0)
+            if st != E.EVO_OK:
+                raise E.EvoAttnError(st)
+        steps = max(10, args.steps // B)
+        fu = _event_time_us(torch, fwd, R, steps, max(3, args.warmup // B))
+        bu = _event_time_us(torch, bwd, R, steps, max(3, args.warmup // B))
+        ff, bf = 4 * B * N * H * L * L * D, 10 * B * N * H * L * L * D
+        rows.append({"B": B, "fwd_us": round(fu, 2), "fwd_tflops": round(ff / fu / 1e6, 2),
+                     "bwd_us": round(bu, 2), "bwd_tflops": round(bf / bu / 1e6, 2),
+                     "fwd_bwd_tflops": round((ff + bf) / (fu + bu) / 1e6, 2), "input_sets": R})
+        log(f"sweep: B={B} fwd {fu:.1f} us ({rows[-1]['fwd_tflops']} TFLOP/s), "
+            f"bwd {bu:.1f} us ({rows[-1]['bwd_tflops']} TFLOP/s)")
+        t_total["fwd"], t_total["bwd"] = fu, bu
+        del sets, ws
+        torch.cuda.empty_cache()
+    last = rows[-1]
+    result = {
+        "metric": SWEEP_METRIC,
+        "value": last["fwd_bwd_tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round((t_total["fwd"] + t_total["bwd"]) / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic (seeded; see synthetic/)",
+        "config": {"workload": "ds4sci_benchmark_256x256_h4_d32_f16", "N": N, "L": L, "H": H, "D": D,
+                   "batches": batches, "mask": True, "pair_bias": True, "mode": "cold"},
+        "roofline": {"bound": "mfma", "achieved": last["fwd_bwd_tflops"], "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(last["fwd_bwd_tflops"] / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "scope": "forward + backward at batch 16"},
+        "sweep": rows,
+    }
     print(json.dumps(result), flush=True)
 
 
