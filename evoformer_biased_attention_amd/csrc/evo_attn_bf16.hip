@@ -1,5 +1,5 @@
-// 16-bit (bf16, f16) forward kernel on gfx950 (MI355X): head dimensions 8, 16
-// and 32 on the fast path below, 64 on the exact path.
+// 16-bit (bf16, f16) forward kernel on gfx950 (MI355X): head dimensions 8, 16,
+// 32 and 64.
 //
 // Operation (page "DeepSpeed DS4Sci_EvoformerAttention 内核实战指南",
 // hmyw.cn, sections 4, 5.2 and 5.4): for each (b, n, h) slice and query i,
@@ -31,6 +31,9 @@
 //    probabilities stay below 2^12.  The row sums are formed on the matrix
 //    cores (an all-ones A operand against the same bf16 P that the P.V
 //    product uses), so every lane of a query ends with the full row sum.
+//  * D = 64 runs as two 32-wide halves: two products per score tile over the
+//    two halves of Q and K, and four 16-wide output tiles; K and V sit in LDS
+//    as two 32-wide half tiles in the D = 32 layout.
 //  * Per block of 64 keys the workgroup copies K, V, the 128 x 64 pair-bias
 //    tile of its queries and the mask row straight from global memory into
 //    LDS (buffer loads with the LDS destination bit, no register staging),
@@ -61,7 +64,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
 
-constexpr int kMaxD = 32;                 // head dimensions 8, 16 and 32 share the 32-wide layouts
 constexpr uint32_t kOOB = 0x80000000u;    // a buffer offset past every range: the load returns zeros
 constexpr int kWaves = 4;
 constexpr int kQTiles = 2;                // 16-query MFMA tiles per wavefront
@@ -108,18 +110,21 @@ struct Params {
     uint32_t sqd;     // bf16 bits: low half = sqrt(D) high part, high half = low part
 };
 
-// LDS of the fast path, in 16-byte slots.
-//   k, v: slot 4*key + (chunk ^ ((key >> 2) & 3)), chunk = 8 d-values
+// LDS of the fast path, in 16-byte slots; DH = 32-wide halves of the head
+// dimension (1, or 2 for D = 64).
+//   k, v: half hh, slot 4*key + (chunk ^ ((key >> 2) & 3)), chunk = 8 d-values of the half
 //   pt:   slot 8*row + (chunk ^ (row & 7)), row = query of the workgroup, chunk = 8 keys
 //   mt:   slot chunk (8 keys)
+template <int DH>
 struct FastBuf {
-    uint4 k[kKB * 4];
-    uint4 v[kKB * 4];
+    uint4 k[DH][kKB * 4];
+    uint4 v[DH][kKB * 4];
     uint4 pt[kBlockQ * 8];
     uint4 mt[8];
 };
+template <int DH>
 struct FastSmem {
-    FastBuf buf[2];
+    FastBuf<DH> buf[2];
 };
 
 // LDS of the exact path.
@@ -132,8 +137,9 @@ struct ExactSmem {
     u16 vt[kExactMaxD * kVtStride];
 };
 
+template <int DH>
 union Smem {
-    FastSmem f;
+    FastSmem<DH> f;
     ExactSmem e;
 };
 
@@ -269,12 +275,14 @@ struct Slice {
 // Requires L % 8 == 0, L * H * D * 2 < 2^31 and L * L * 2 < 2^31.
 // ---------------------------------------------------------------------------
 template <class E, int D, bool PAIR, bool MASK>
-__device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid) {
+__device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32>& sm, int tid) {
     using V8 = typename E::v8;
+    using Buf = FastBuf<(D + 31) / 32>;
     // D < 32: the 16-byte chunks of a row past D read as zero (an offset
     // beyond the buffer range), which pads Q and K with zero dimensions and V
-    // with zero columns; the d-half of P.V past D is skipped.
+    // with zero columns; the d-tile of P.V past D is skipped.
     constexpr int kDC = D / 8;               // 16-byte chunks per row
+    constexpr int kDH = (D + 31) / 32;       // 32-wide halves of the contraction over d
     constexpr int kDHT = (D + 15) / 16;      // 16-wide d tiles of the output
     const int L = (int)p.L;
     // the wave index is uniform: keep it (and every LDS address derived from
@@ -307,17 +315,18 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
         ident = as_v8<E>(uint4{w[0], w[1], w[2], w[3]});
     }
 
-    // Q operands (B of S^T = K.Q^T): lane (c + 16g) holds q[query c][8g .. 8g+7];
-    // rows past L read as zero.
-    V8 qop[kQTiles];
+    // Q operands (B of S^T = K.Q^T): lane (c + 16g) holds q[query c][32hh + 8g
+    // .. 32hh + 8g + 7] for half hh; rows past L read as zero.
+    V8 qop[kQTiles][kDH];
     for (int t = 0; t < kQTiles; ++t) {
         const uint32_t i = (uint32_t)(s.q0 + 16 * t + c);
-        qop[t] = as_v8<E>(bload16(rq, g < kDC ? i * rowq + 16 * g : kOOB, 0));
+        for (int hh = 0; hh < kDH; ++hh)
+            qop[t][hh] = as_v8<E>(bload16(rq, 4 * hh + g < kDC ? i * rowq + 64 * hh + 16 * g : kOOB, 0));
     }
 
     // ---- copy of one block (keys [64 blk, 64 blk + 64)) into LDS buffer `buf` ----
-    // K, V: wave w fills slots 64w .. 64w+63 (keys 16w .. 16w+15); lane l holds
-    //   key 16w + l/4 at slot position l%4, i.e. chunk (l%4) ^ ((key >> 2) & 3).
+    // K, V: wave w fills slots 64w .. 64w+63 of each half (keys 16w .. 16w+15);
+    //   lane l holds key 16w + l/4 at slot position l%4, i.e. chunk (l%4) ^ ((key >> 2) & 3).
     // pair: wave w fills 1 KB segments 4w .. 4w+3; segment I holds query rows
     //   8I .. 8I+7, lane l row 8I + l/8 at position l%8, chunk (l%8) ^ (row & 7).
     //   Query rows past L fall outside the pair range and read as zero.
@@ -325,28 +334,33 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
     const uint32_t qwg = (uint32_t)(s.q0 - wave * kWaveQ);  // first query of the workgroup
     const uint32_t kvchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
     const uint32_t krow = (uint32_t)(16 * wave + (lane >> 2));
-    const uint32_t ko = kvchunk < kDC ? krow * rowk + 16u * kvchunk : kOOB;
-    const uint32_t vo = kvchunk < kDC ? krow * rowv + 16u * kvchunk : kOOB;
+    uint32_t ko[kDH], vo[kDH];
+    for (int hh = 0; hh < kDH; ++hh) {
+        const bool in = 4 * hh + (int)kvchunk < kDC;
+        ko[hh] = in ? krow * rowk + 64u * hh + 16u * kvchunk : kOOB;
+        vo[hh] = in ? krow * rowv + 64u * hh + 16u * kvchunk : kOOB;
+    }
     uint32_t pvo[4];
     for (int j = 0; j < 4; ++j) {
         const uint32_t row = 8u * (4 * wave + j) + (lane >> 3);
         // rows past L start beyond the range (the pair row stride is at least L)
         pvo[j] = (qwg + row) * rowp + 16u * ((lane & 7) ^ (lane >> 3));
     }
-    auto copy_block = [&](int blk, FastBuf* __restrict__ dst) {
+    auto copy_block = [&](int blk, Buf* __restrict__ dst) {
         const uint32_t k0 = (uint32_t)blk * kKB;
-        dma16(rk, &dst->k[64 * wave], ko + k0 * rowk, 0);
-        dma16(rv, &dst->v[64 * wave], vo + k0 * rowv, 0);
+        for (int hh = 0; hh < kDH; ++hh) {
+            dma16(rk, &dst->k[hh][64 * wave], ko[hh] + k0 * rowk, 0);
+            dma16(rv, &dst->v[hh][64 * wave], vo[hh] + k0 * rowv, 0);
+        }
         if (PAIR)
             for (int j = 0; j < 4; ++j) dma16(rp, &dst->pt[64 * (4 * wave + j)], pvo[j] + k0 * 2u, 0);
         if (MASK && wave == 0 && lane < 8) dma16(rm, &dst->mt[0], 16u * lane + k0 * 2u, 0);
     };
 
-    f32x4 oacc[kQTiles][2];
+    f32x4 oacc[kQTiles][kDHT];
     float mused[kQTiles], msub[kQTiles], lsum[kQTiles];
     for (int t = 0; t < kQTiles; ++t) {
-        oacc[t][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        oacc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int dh = 0; dh < kDHT; ++dh) oacc[t][dh] = f32x4{0.f, 0.f, 0.f, 0.f};
         mused[t] = -INFINITY;
         msub[t] = 0.f;
         lsum[t] = 0.f;
@@ -362,14 +376,14 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
 
     // S^T = sqrt(D)*(pair + mask) + K.Q^T for the block in `b`, in accumulator
     // units; MASKON adds the mask (only blocks whose mask has a nonzero entry).
-    auto scores = [&](const FastBuf* __restrict__ b, f32x4 (&acc)[kQTiles][kKT], auto mask_tag) {
+    auto scores = [&](const Buf* __restrict__ b, f32x4 (&acc)[kQTiles][kKT], auto mask_tag) {
         constexpr bool MASKON = decltype(mask_tag)::value;
         // every operand first, then the products in three independent waves
         // of eight, so that no product waits for the one just issued
-        V8 kop[kKT], pop[kQTiles][kKT], mop[kKT];
+        V8 kop[kKT][kDH], pop[kQTiles][kKT], mop[kKT];
         for (int kt = 0; kt < kKT; ++kt) {
-            // A[m = key][k = d]: lane (c + 16g) reads key 16kt + c, chunk g
-            kop[kt] = as_v8<E>(b->k[64 * kt + 4 * c + (g ^ ((c >> 2) & 3))]);
+            // A[m = key][k = d]: lane (c + 16g) reads key 16kt + c, chunk g of each half
+            for (int hh = 0; hh < kDH; ++hh) kop[kt][hh] = as_v8<E>(b->k[hh][64 * kt + 4 * c + (g ^ ((c >> 2) & 3))]);
             if (PAIR)
                 for (int t = 0; t < kQTiles; ++t) {
                     // B[k = slot][n = query]: pair row of query c, keys 16kt + 8(g%2) .. +7
@@ -390,8 +404,9 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
         if (MASKON)
             for (int kt = 0; kt < kKT; ++kt)
                 for (int t = 0; t < kQTiles; ++t) acc[t][kt] = E::mfma(ident, mop[kt], acc[t][kt]);
-        for (int kt = 0; kt < kKT; ++kt)
-            for (int t = 0; t < kQTiles; ++t) acc[t][kt] = E::mfma(kop[kt], qop[t], acc[t][kt]);
+        for (int hh = 0; hh < kDH; ++hh)
+            for (int kt = 0; kt < kKT; ++kt)
+                for (int t = 0; t < kQTiles; ++t) acc[t][kt] = E::mfma(kop[kt][hh], qop[t][hh], acc[t][kt]);
     };
 
     // One block of keys; TAIL marks the last block when L % 64 != 0.  Every
@@ -399,7 +414,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
     // issued before the next block's copy into the other buffer: the
     // compiler orders LDS reads after an LDS-destination load behind that
     // load's completion, which would expose the global latency here.
-    auto step = [&](int it, const FastBuf* __restrict__ cur, FastBuf* __restrict__ nxt, auto tail_tag) {
+    auto step = [&](int it, const Buf* __restrict__ cur, Buf* __restrict__ nxt, auto tail_tag) {
         constexpr bool TAIL = decltype(tail_tag)::value;
         const int k0 = it * kKB;
 
@@ -419,15 +434,16 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
 
         // V operands of O^T = V^T . P^T.  A[m = d][k]: lane (c + 16g) needs
         // V[key(g, e)][16dh + c].  Lane r of group g addresses key 32cc + 4g +
-        // r/4, d-values 16dh + 4(r%4) .. +3 (16-byte chunk 2dh + (r%4)/2, half
-        // r%2); the transposing read then hands lane c the column 16dh + c over
-        // keys 32cc + 4g + 0..3, and a second read does keys 32cc + 16 + 4g + 0..3.
-        V8 vop[2][2];
+        // r/4, d-values 16dh + 4(r%4) .. +3 (16-byte chunk 2dh + (r%4)/2 of
+        // the half, byte half r%2); the transposing read then hands lane c the
+        // column 16dh + c over keys 32cc + 4g + 0..3, and a second read does
+        // keys 32cc + 16 + 4g + 0..3.
+        V8 vop[2][kDHT];
         for (int cc = 0; cc < 2; ++cc)
             for (int dh = 0; dh < kDHT; ++dh) {
                 const int key = 32 * cc + 4 * g + (c >> 2);          // (key >> 2) & 3 == g
-                const int chunk = (2 * dh + ((c & 3) >> 1)) ^ g;
-                const char* base = reinterpret_cast<const char*>(&cur->v[4 * key + chunk]) + 8 * (c & 1);
+                const int chunk = (2 * (dh & 1) + ((c & 3) >> 1)) ^ g;
+                const char* base = reinterpret_cast<const char*>(&cur->v[dh >> 1][4 * key + chunk]) + 8 * (c & 1);
                 const uint2 lo = ds_read_tr(base);
                 const uint2 hi = ds_read_tr(base + 16 * 4 * 16);      // 16 keys further
                 vop[cc][dh] = as_v8<E>(uint4{lo.x, lo.y, hi.x, hi.y});
@@ -477,8 +493,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem& sm, int tid)
                 if (mnew > mused[t]) {
                     const float alpha = __builtin_amdgcn_exp2f((mused[t] - mnew) * p.c1);  // 0 when mused = -inf
                     lsum[t] *= alpha;
-                    oacc[t][0] *= alpha;
-                    oacc[t][1] *= alpha;
+                    for (int dh = 0; dh < kDHT; ++dh) oacc[t][dh] *= alpha;
                     mused[t] = mnew;
                     msub[t] = mnew * p.c1;
                 }
@@ -664,11 +679,12 @@ __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int ti
 }
 
 // FAST: the fast path may run (L % 8 == 0); otherwise every workgroup takes
-// the exact path.  Three workgroups' LDS fit on a CU; the second launch bound
-// keeps the registers within what three waves per SIMD allow (168 VGPRs).
+// the exact path.  D <= 32: three workgroups' LDS fit on a CU, and the second
+// launch bound keeps the registers within what three waves per SIMD allow
+// (168 VGPRs).  D = 64: two workgroups per CU (64 KB of LDS each), 256 VGPRs.
 template <class E, int D, bool PAIR, bool MASK, bool FAST>
-__global__ __launch_bounds__(kWaves * 64, 3) void fwd_16bit_kernel(Params p) {
-    __shared__ __attribute__((aligned(16))) Smem sm;
+__global__ __launch_bounds__(kWaves * 64, D > 32 ? 2 : 3) void fwd_16bit_kernel(Params p) {
+    __shared__ __attribute__((aligned(16))) Smem<(D + 31) / 32> sm;
 
     const uint32_t id = (uint32_t)logical_block(blockIdx.x, p.total);
     const uint32_t r1 = fdiv(id, p.qblocks), r2 = fdiv(r1, p.hd), r3 = fdiv(r2, p.nd);
@@ -722,21 +738,11 @@ hipError_t launch_dim(Params& p, hipStream_t stream) {
     return launch_biases<E, D, false, false>(p, stream);
 }
 
-// D = 64: the matrix-core exact path (its fast-path layouts are 32 wide)
-template <class E>
-hipError_t launch_d64(Params& p, hipStream_t stream) {
-    const bool pair = p.pair != nullptr, mask = p.mask != nullptr;
-    if (pair && mask) return launch_variant<E, 64, true, true, false>(p, stream);
-    if (pair) return launch_variant<E, 64, true, false, false>(p, stream);
-    if (mask) return launch_variant<E, 64, false, true, false>(p, stream);
-    return launch_variant<E, 64, false, false, false>(p, stream);
-}
-
 template <class E>
 hipError_t launch_format(Params& p, int64_t d, hipStream_t stream) {
     if (d == 8) return launch_dim<E, 8>(p, stream);
     if (d == 16) return launch_dim<E, 16>(p, stream);
-    if (d == 64) return launch_d64<E>(p, stream);
+    if (d == 64) return launch_dim<E, 64>(p, stream);
     return launch_dim<E, 32>(p, stream);
 }
 

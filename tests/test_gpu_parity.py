@@ -329,10 +329,13 @@ def test_rows_past_L_read_as_zero(torch_dev, dtype):
 
 
 # ---------------------------------------------------------------------------
-# Head dimension 64 on the 16-bit path (the exact path's two 32-wide halves).
+# Head dimension 64 on the 16-bit path: two 32-wide halves of the contraction,
+# on the fast path for L % 8 == 0 (64, 136, 200, 256) and on the exact path
+# otherwise (1, 17, 100, 257).
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("shape", [(1, 1, 1, 1), (1, 2, 17, 3), (2, 2, 64, 2), (1, 3, 100, 4), (1, 2, 257, 2)],
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1), (1, 2, 17, 3), (2, 2, 64, 2), (1, 3, 100, 4), (1, 2, 257, 2),
+                                   (1, 3, 136, 2), (2, 2, 200, 3)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_head_dim_64(torch_dev, shape, dtype):
     B, N, L, H = shape
@@ -347,3 +350,41 @@ def test_head_dim_64_msa_row_shape(torch_dev, dtype):
     """An MSA-row problem with the largest head dimension the guide's backward allows (section 5.4: D <= 64)."""
     w = S.random_problem(1, 16, 256, 4, 64, dtype=dtype, seed=64, mask="tail", pair="normal", mask_frac=0.1)
     parity_full(torch_dev, w)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_head_dim_64_masked_and_peaked(torch_dev, dtype):
+    """D = 64 with -inf masks (a partly and a fully masked sequence) and biases of scale 8."""
+    B, N, L, H, D = 1, 3, 128, 2, 64
+    w = S.random_problem(B, N, L, H, D, dtype=dtype, seed=640, mask="zero", pair="normal", bias_scale=8.0)
+    mf = np.zeros((B, N, 1, 1, L), np.float32)
+    mf[0, 0, ..., 10:50] = -np.inf
+    mf[0, 1] = -np.inf
+    w.mask = S.to_storage(mf, dtype)
+    o, l = run_gpu(torch_dev, w)
+    ro, rl = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype=dtype, nthreads=THREADS)
+    assert np.all(o[0, 1] == 0) and np.all(np.isneginf(l[0, 1]))
+    compare(o, l, ro, rl, dtype, "head dim 64, masked and peaked")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_head_dim_64_neg_inf_pair_bias(torch_dev, dtype):
+    """-inf in the pair bias at D = 64 (one key of a row, part of a row, a whole row): the identity product
+    turns it into NaN, and the workgroups that meet it redo their slice on the exact path."""
+    B, N, L, H, D = 1, 2, 96, 2, 64
+    w = S.random_problem(B, N, L, H, D, dtype=dtype, seed=641, mask="tail", pair="normal")
+    pf = S.storage_to_f32(w.pair, dtype).copy()
+    pf[0, 0, 1, 5, 7] = -np.inf
+    pf[0, 0, 0, 70, :40] = -np.inf
+    pf[0, 0, 1, 20, :] = -np.inf
+    w.pair = S.to_storage(pf, dtype)
+    o, l = run_gpu(torch_dev, w)
+    ro, rl = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype=dtype, nthreads=THREADS)
+    compare(o, l, ro, rl, dtype, "head dim 64, infinite pair bias")
+
+
+def test_head_dim_64_workload_size(torch_dev):
+    """Triangle attention at N = L = 384, H = 4 with D = 64 (bf16), on 4096 sampled rows."""
+    w = S.random_problem(1, 384, 384, 4, 64, dtype="bf16", seed=642, mask="tail", pair="normal")
+    say("head dim 64 at N = L = 384, sampled rows")
+    parity_sampled(torch_dev, w)
