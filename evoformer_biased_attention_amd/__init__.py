@@ -25,6 +25,7 @@ EVO_DTYPE_F32, EVO_DTYPE_BF16, EVO_DTYPE_F16 = 0, 1, 2
 # Symbols declared in include/evo_attn.h.
 EXPORTED = ("evo_attn_fwd", "evo_attn_check", "evo_attn_fwd_strided", "evo_attn_check_strided",
             "evo_attn_dense_layout", "evo_attn_bwd", "evo_attn_bwd_check", "evo_attn_bwd_workspace_size",
+            "evo_attn_bwd_strided", "evo_attn_bwd_check_strided",
             "evo_trimul", "evo_trimul_check", "evo_status_string", "evo_attn_last_hip_error")
 EVO_TRIMUL_OUTGOING, EVO_TRIMUL_INCOMING = 0, 1
 
@@ -85,6 +86,12 @@ def _load():
     lib.evo_attn_bwd_check.argtypes = [vp] * 15 + [ctypes.c_size_t, ctypes.POINTER(EvoShape), ctypes.c_int]
     lib.evo_attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.evo_attn_bwd_workspace_size.argtypes = [ctypes.POINTER(EvoShape), ctypes.c_int]
+    lib.evo_attn_bwd_strided.restype = ctypes.c_int
+    lib.evo_attn_bwd_strided.argtypes = [vp] * 15 + [ctypes.c_size_t, ctypes.POINTER(EvoLayout),
+                                                     ctypes.POINTER(EvoShape), ctypes.c_int, vp]
+    lib.evo_attn_bwd_check_strided.restype = ctypes.c_int
+    lib.evo_attn_bwd_check_strided.argtypes = [vp] * 15 + [ctypes.c_size_t, ctypes.POINTER(EvoLayout),
+                                                           ctypes.POINTER(EvoShape), ctypes.c_int]
     lib.evo_trimul.restype = ctypes.c_int
     lib.evo_trimul.argtypes = [vp, vp, vp, ctypes.POINTER(EvoTrimulShape), ctypes.c_int, ctypes.c_int, vp]
     lib.evo_trimul_check.restype = ctypes.c_int
@@ -158,6 +165,24 @@ def evo_attn_bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmas
     return _lib.evo_attn_bwd(*[_addr(x) for x in (q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv,
                                                  dmask_bias, dpair_bias, delta, workspace)],
                              int(workspace_bytes), ctypes.byref(_shape(shape)), int(dtype), stream)
+
+
+def evo_attn_bwd_check_strided(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias, dpair_bias,
+                               delta, layout, shape, dtype, workspace=None, workspace_bytes=0) -> int:
+    """Host-only validation of the strided backward call; returns the status code."""
+    return _lib.evo_attn_bwd_check_strided(*[_addr(x) for x in (q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk,
+                                                               dv, dmask_bias, dpair_bias, delta, workspace)],
+                                           int(workspace_bytes), ctypes.byref(layout), ctypes.byref(_shape(shape)),
+                                           int(dtype))
+
+
+def evo_attn_bwd_strided(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias, dpair_bias, delta,
+                         layout, shape, dtype, stream=None, workspace=None, workspace_bytes=0) -> int:
+    """Enqueue the backward pass on strided tensors; each gradient has its tensor's layout."""
+    return _lib.evo_attn_bwd_strided(*[_addr(x) for x in (q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv,
+                                                         dmask_bias, dpair_bias, delta, workspace)],
+                                     int(workspace_bytes), ctypes.byref(layout), ctypes.byref(_shape(shape)),
+                                     int(dtype), stream)
 
 
 def evo_attn_dense_layout(shape) -> EvoLayout:
@@ -236,26 +261,39 @@ def fwd(q, k, v, mask_bias=None, pair_bias=None, out=None, lse=True, stream=None
     return out, lse_t
 
 
+def _lse_row(lse, B, N, H, L):
+    """Row stride of an lse-like tensor [B,N,H,L] whose (b, n, h) rows are equally spaced."""
+    if tuple(lse.shape) != (B, N, H, L) or lse.stride(3) != 1:
+        raise ValueError("lse must be [B,N,H,L] with contiguous rows")
+    # size-1 axes have arbitrary strides: take the row step from the first axis that moves
+    row = lse.stride(2) if H > 1 else lse.stride(1) if N > 1 else lse.stride(0) if B > 1 else L
+    if (N > 1 and lse.stride(1) != H * row) or (B > 1 and lse.stride(0) != N * H * row):
+        raise ValueError("lse rows must be equally spaced")
+    return row
+
+
 def bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, want_dmask=True, want_dpair=True, stream=None,
         workspace=True):
-    """torch convenience wrapper around evo_attn_bwd: allocates the gradients, delta and (unless
-    workspace=False) the recommended workspace with torch.
+    """torch convenience wrapper around evo_attn_bwd_strided: allocates the gradients (each with the
+    strides of its tensor, so views such as the transposed tensors of ending-node or column attention
+    get gradients in the same views), delta (with lse's row stride) and, unless workspace=False, the
+    recommended workspace, with torch.
 
-    out and lse are the forward pass's results for the same inputs.  Returns
-    (dq, dk, dv, dmask_bias or None, dpair_bias or None, delta); a bias
-    gradient is computed only when that bias is given and wanted.
-    Raises EvoAttnError for any status other than EVO_OK.
+    out and lse are the forward pass's results for the same inputs; dout must have out's strides.
+    Returns (dq, dk, dv, dmask_bias or None, dpair_bias or None, delta); a bias gradient is computed
+    only when that bias is given and wanted.  Raises EvoAttnError for any status other than EVO_OK.
     """
     import torch
     B, N, L, H, D = q.shape
-    for name, t in (("q", q), ("k", k), ("v", v), ("mask_bias", mask_bias), ("pair_bias", pair_bias),
-                    ("out", out), ("lse", lse), ("dout", dout)):
-        if t is not None and not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    dmask = torch.empty_like(mask_bias) if (mask_bias is not None and want_dmask) else None
-    dpair = torch.empty_like(pair_bias) if (pair_bias is not None and want_dpair) else None
-    delta = torch.empty((B, N, H, L), dtype=torch.float32, device=q.device)
+    if tuple(dout.stride()) != tuple(out.stride()):
+        raise ValueError("dout must have the strides of out")
+    row = _lse_row(lse, B, N, H, L)
+    lay = layout_of(q, k, v, out, mask_bias, pair_bias, lse_row=row)
+    like = lambda t: torch.empty_strided(t.size(), t.stride(), dtype=t.dtype, device=t.device)
+    dq, dk, dv = like(q), like(k), like(v)
+    dmask = like(mask_bias) if (mask_bias is not None and want_dmask) else None
+    dpair = like(pair_bias) if (pair_bias is not None and want_dpair) else None
+    delta = torch.empty((B, N, H, row), dtype=torch.float32, device=q.device)[..., :L]
     code = torch_dtype_code(q.dtype)
     ws, ws_bytes = None, 0
     if workspace and dpair is not None:
@@ -264,8 +302,8 @@ def bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, want_dmask=True, want_dpa
             ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = evo_attn_bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask, dpair, delta,
-                      (B, N, L, H, D), code, stream, workspace=ws, workspace_bytes=ws_bytes)
+    st = evo_attn_bwd_strided(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask, dpair, delta, lay,
+                              (B, N, L, H, D), code, stream, workspace=ws, workspace_bytes=ws_bytes)
     if st != EVO_OK:
         raise EvoAttnError(st)
     return dq, dk, dv, dmask, dpair, delta

@@ -88,14 +88,15 @@ int64_t span_elems(std::initializer_list<std::pair<int64_t, int64_t>> axes) {
     return e;
 }
 
-// Whether distinct (b, n, l, h, d) of a [B,N,L,H,D] tensor with these strides
-// (d contiguous) have distinct offsets: taken in increasing stride order, each
-// axis of size > 1 must step past everything the faster axes cover.
-bool no_self_overlap(const int64_t* st, const evo_shape_t& s) {
-    std::pair<int64_t, int64_t> ax[4] = {{st[0], s.B}, {st[1], s.N}, {st[2], s.L}, {st[3], s.H}};
-    std::sort(ax, ax + 4);
-    int64_t e = s.D;
-    for (const auto& a : ax) {
+// Whether distinct indices of a tensor with axes {(stride, size)} and a
+// contiguous innermost run of `inner` elements have distinct offsets: taken in
+// increasing stride order, each axis of size > 1 must step past everything the
+// faster axes cover.
+bool disjoint_axes(std::pair<int64_t, int64_t>* ax, int count, int64_t inner) {
+    std::sort(ax, ax + count);
+    int64_t e = inner;
+    for (int i = 0; i < count; ++i) {
+        const auto& a = ax[i];
         if (a.second <= 1) continue;
         if (a.first < e) return false;
         const int64_t t = mul_checked(a.second - 1, a.first);
@@ -103,6 +104,27 @@ bool no_self_overlap(const int64_t* st, const evo_shape_t& s) {
         e += t;
     }
     return true;
+}
+
+// The same for a [B,N,L,H,D] tensor with strides st (b, n, l, h; d contiguous).
+bool no_self_overlap(const int64_t* st, const evo_shape_t& s) {
+    std::pair<int64_t, int64_t> ax[4] = {{st[0], s.B}, {st[1], s.N}, {st[2], s.L}, {st[3], s.H}};
+    return disjoint_axes(ax, 4, s.D);
+}
+
+// evo_layout_t -> the kernels' stride set
+evo::Strides strides_of(const evo_layout_t& lay) {
+    evo::Strides st{};
+    for (int i = 0; i < 4; ++i) {
+        st.q[i] = lay.q[i];
+        st.k[i] = lay.k[i];
+        st.v[i] = lay.v[i];
+        st.o[i] = lay.out[i];
+    }
+    st.mb = lay.mask_b, st.mn = lay.mask_n;
+    st.pb = lay.pair_b, st.ph = lay.pair_h, st.pi = lay.pair_i;
+    st.lrow = lay.lse_row;
+    return st;
 }
 
 }  // namespace
@@ -195,16 +217,8 @@ extern "C" evo_status_t evo_attn_fwd_strided(const void* q, const void* k, const
                                              const evo_shape_t* shape, evo_dtype_t dtype, void* stream) {
     const evo_status_t st = evo_attn_check_strided(q, k, v, mask_bias, pair_bias, out, lse, layout, shape, dtype);
     if (st != EVO_OK) return st;
-    evo::FwdArgs a{q, k, v, mask_bias, pair_bias, out, lse, shape->B, shape->N, shape->L, shape->H, shape->D, {}};
-    for (int i = 0; i < 4; ++i) {
-        a.st.q[i] = layout->q[i];
-        a.st.k[i] = layout->k[i];
-        a.st.v[i] = layout->v[i];
-        a.st.o[i] = layout->out[i];
-    }
-    a.st.mb = layout->mask_b, a.st.mn = layout->mask_n;
-    a.st.pb = layout->pair_b, a.st.ph = layout->pair_h, a.st.pi = layout->pair_i;
-    a.st.lrow = layout->lse_row;
+    const evo::FwdArgs a{q,        k,        v,        mask_bias, pair_bias,          out, lse,
+                         shape->B, shape->N, shape->L, shape->H,  shape->D, strides_of(*layout)};
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t err = dtype == EVO_DTYPE_BF16  ? evo::launch_fwd_bf16(a, s)
                            : dtype == EVO_DTYPE_F16 ? evo::launch_fwd_f16(a, s)
@@ -235,40 +249,70 @@ bool bwd_supported(evo_dtype_t dt, int64_t D) {
 
 }  // namespace
 
-extern "C" evo_status_t evo_attn_bwd_check(const void* q, const void* k, const void* v, const void* mask_bias,
-                                           const void* pair_bias, const void* out, const float* lse,
-                                           const void* dout, const void* dq, const void* dk, const void* dv,
-                                           const void* dmask_bias, const void* dpair_bias, const float* delta,
-                                           const void* workspace, size_t workspace_bytes, const evo_shape_t* shape,
-                                           evo_dtype_t dtype) {
-    if (!shape || !q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !delta)
+extern "C" evo_status_t evo_attn_bwd_check_strided(const void* q, const void* k, const void* v,
+                                                   const void* mask_bias, const void* pair_bias, const void* out,
+                                                   const float* lse, const void* dout, const void* dq, const void* dk,
+                                                   const void* dv, const void* dmask_bias, const void* dpair_bias,
+                                                   const float* delta, const void* workspace,
+                                                   size_t workspace_bytes, const evo_layout_t* layout,
+                                                   const evo_shape_t* shape, evo_dtype_t dtype) {
+    if (!shape || !layout || !q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !delta)
         return EVO_ERR_NULL_POINTER;
-    const int64_t B = shape->B, N = shape->N, L = shape->L, H = shape->H, D = shape->D;
+    const evo_shape_t& s = *shape;
+    const evo_layout_t& lay = *layout;
+    const int64_t B = s.B, N = s.N, L = s.L, H = s.H, D = s.D;
     if (B < 1 || N < 1 || L < 1 || H < 1 || D < 1) return EVO_ERR_BAD_SHAPE;
     if (dtype != EVO_DTYPE_F32 && dtype != EVO_DTYPE_BF16 && dtype != EVO_DTYPE_F16) return EVO_ERR_BAD_DTYPE;
     if ((dmask_bias && !mask_bias) || (dpair_bias && !pair_bias)) return EVO_ERR_NO_BIAS;
     const int64_t es = elem_size(dtype);
 
-    int64_t qkv = es;
-    for (int64_t s : {B, N, L, H, D}) qkv = mul_checked(qkv, s);
-    int64_t msk = es;
-    for (int64_t s : {B, N, L}) msk = mul_checked(msk, s);
-    int64_t par = es;
-    for (int64_t s : {B, H, L, L}) par = mul_checked(par, s);
-    int64_t row = 4;
-    for (int64_t s : {B, N, H, L}) row = mul_checked(row, s);
-    if (qkv < 0 || msk < 0 || par < 0 || row < 0) return EVO_ERR_BAD_SHAPE;
+    // strides: non-negative; pair rows and lse / delta rows at least L apart
+    const int64_t* qkvo[4] = {lay.q, lay.k, lay.v, lay.out};
+    for (const int64_t* t : qkvo)
+        for (int a = 0; a < 4; ++a)
+            if (t[a] < 0) return EVO_ERR_BAD_SHAPE;
+    if (lay.mask_b < 0 || lay.mask_n < 0 || lay.pair_b < 0 || lay.pair_h < 0) return EVO_ERR_BAD_SHAPE;
+    if (pair_bias && lay.pair_i < L) return EVO_ERR_BAD_SHAPE;
+    if (lay.lse_row < L) return EVO_ERR_BAD_SHAPE;
+
+    // byte extents, each below 2^62; a gradient spans what its tensor spans
+    int64_t ext[4];
+    for (int t = 0; t < 4; ++t) {
+        const int64_t e = span_elems({{B, qkvo[t][0]}, {N, qkvo[t][1]}, {L, qkvo[t][2]}, {H, qkvo[t][3]}, {D, 1}});
+        ext[t] = e < 0 ? -1 : mul_checked(e, es);
+    }
+    const int64_t me = span_elems({{B, lay.mask_b}, {N, lay.mask_n}, {L, 1}});
+    const int64_t pe = span_elems({{B, lay.pair_b}, {H, lay.pair_h}, {L, lay.pair_i}, {L, 1}});
+    const int64_t bnh = mul_checked(mul_checked(B, N), H);
+    const int64_t le = bnh < 0 ? -1 : span_elems({{bnh, lay.lse_row}, {L, 1}});
+    const int64_t msk = me < 0 ? -1 : mul_checked(me, es), par = pe < 0 ? -1 : mul_checked(pe, es);
+    const int64_t row = le < 0 ? -1 : mul_checked(le, 4);
+    for (int64_t x : {ext[0], ext[1], ext[2], ext[3], msk, par, row})
+        if (x < 0) return EVO_ERR_BAD_SHAPE;
 
     if (workspace && workspace_bytes > static_cast<size_t>(kMaxBytes)) return EVO_ERR_BAD_SHAPE;
     for (const void* p : {q, k, v, mask_bias, pair_bias, out, static_cast<const void*>(lse), dout, dq, dk, dv,
                           dmask_bias, dpair_bias, static_cast<const void*>(delta), workspace})
         if (p && !aligned16(p)) return EVO_ERR_MISALIGNED;
 
-    const Extent outs[] = {extent(dq, qkv),        extent(dk, qkv),   extent(dv, qkv),
-                           extent(dmask_bias, msk), extent(dpair_bias, par), extent(delta, row),
+    // outputs: no two elements of one gradient at one address, and no output
+    // overlapping an input or another output
+    if (!no_self_overlap(lay.q, s) || !no_self_overlap(lay.k, s) || !no_self_overlap(lay.v, s))
+        return EVO_ERR_ALIASING;
+    if (dmask_bias) {
+        std::pair<int64_t, int64_t> ax[2] = {{lay.mask_b, B}, {lay.mask_n, N}};
+        if (!disjoint_axes(ax, 2, L)) return EVO_ERR_ALIASING;
+    }
+    if (dpair_bias) {
+        std::pair<int64_t, int64_t> ax[3] = {{lay.pair_b, B}, {lay.pair_h, H}, {lay.pair_i, L}};
+        if (!disjoint_axes(ax, 3, L)) return EVO_ERR_ALIASING;
+    }
+    const Extent outs[] = {extent(dq, ext[0]),     extent(dk, ext[1]),          extent(dv, ext[2]),
+                           extent(dmask_bias, msk), extent(dpair_bias, par),     extent(delta, row),
                            extent(workspace, workspace ? static_cast<int64_t>(workspace_bytes) : 0)};
-    const Extent ins[] = {extent(q, qkv),         extent(k, qkv),   extent(v, qkv), extent(mask_bias, msk),
-                          extent(pair_bias, par), extent(out, qkv), extent(lse, row), extent(dout, qkv)};
+    const Extent ins[] = {extent(q, ext[0]),         extent(k, ext[1]),   extent(v, ext[2]),
+                          extent(mask_bias, msk),    extent(pair_bias, par), extent(out, ext[3]),
+                          extent(lse, row),          extent(dout, ext[3])};
     for (size_t a = 0; a < sizeof(outs) / sizeof(outs[0]); ++a) {
         for (const Extent& in : ins)
             if (outs[a].overlaps(in)) return EVO_ERR_ALIASING;
@@ -276,19 +320,35 @@ extern "C" evo_status_t evo_attn_bwd_check(const void* q, const void* k, const v
             if (outs[a].overlaps(outs[c])) return EVO_ERR_ALIASING;
     }
     if (!bwd_supported(dtype, D)) return EVO_ERR_UNSUPPORTED;
+    // rows of q, k, v and out (and so of their gradients) start 16-byte aligned
+    for (const int64_t* t : qkvo)
+        for (int a = 0; a < 4; ++a)
+            if ((t[a] * es) % 16) return EVO_ERR_MISALIGNED;
     return EVO_OK;
+}
+
+extern "C" evo_status_t evo_attn_bwd_check(const void* q, const void* k, const void* v, const void* mask_bias,
+                                           const void* pair_bias, const void* out, const float* lse,
+                                           const void* dout, const void* dq, const void* dk, const void* dv,
+                                           const void* dmask_bias, const void* dpair_bias, const float* delta,
+                                           const void* workspace, size_t workspace_bytes, const evo_shape_t* shape,
+                                           evo_dtype_t dtype) {
+    if (!shape) return EVO_ERR_NULL_POINTER;
+    evo_layout_t lay;
+    evo_attn_dense_layout(shape, &lay);
+    return evo_attn_bwd_check_strided(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias,
+                                      dpair_bias, delta, workspace, workspace_bytes, &lay, shape, dtype);
 }
 
 namespace {
 
-// Workspace chunks the call can use: what the matrix-core path wants, capped
-// by what the given workspace holds (0: none).
-int64_t usable_chunks(const evo_shape_t* s, evo_dtype_t dtype, size_t workspace_bytes) {
-    evo::BwdArgs probe{};
-    probe.B = s->B, probe.N = s->N, probe.L = s->L, probe.H = s->H, probe.D = s->D;
-    if (!evo::bwd_mfma_eligible(probe, static_cast<int>(dtype))) return 0;
-    const int64_t want = evo::bwd_dpair_chunks(s->B, s->N, s->L, s->H);
-    const int64_t per = s->B * s->H * s->L * s->L * 4;  // bytes of one chunk's partial sums
+// Workspace chunks a call can use: what the matrix-core path wants, capped by
+// what the given workspace holds (0: none).  `a` carries the shape, the
+// biases present and the strides.
+int64_t usable_chunks(const evo::BwdArgs& a, evo_dtype_t dtype, size_t workspace_bytes) {
+    if (!evo::bwd_mfma_eligible(a, static_cast<int>(dtype))) return 0;
+    const int64_t want = evo::bwd_dpair_chunks(a.B, a.N, a.L, a.H);
+    const int64_t per = a.B * a.H * a.L * a.L * 4;  // bytes of one chunk's partial sums
     const int64_t fit = static_cast<int64_t>(workspace_bytes / static_cast<size_t>(per));
     const int64_t c = want < fit ? want : fit;
     return c >= 2 ? c : 0;
@@ -301,9 +361,37 @@ extern "C" size_t evo_attn_bwd_workspace_size(const evo_shape_t* shape, evo_dtyp
     int64_t par = 4;
     for (int64_t s : {shape->B, shape->H, shape->L, shape->L}) par = mul_checked(par, s);
     if (par < 0) return 0;
-    const int64_t c = usable_chunks(shape, dtype, ~static_cast<size_t>(0) >> 2);
+    evo_layout_t lay;
+    evo_attn_dense_layout(shape, &lay);
+    evo::BwdArgs probe{};
+    probe.B = shape->B, probe.N = shape->N, probe.L = shape->L, probe.H = shape->H, probe.D = shape->D;
+    probe.st = strides_of(lay);
+    const int64_t c = usable_chunks(probe, dtype, ~static_cast<size_t>(0) >> 2);
     const int64_t bytes = mul_checked(par, c);
     return bytes < 0 ? 0 : static_cast<size_t>(bytes);
+}
+
+extern "C" evo_status_t evo_attn_bwd_strided(const void* q, const void* k, const void* v, const void* mask_bias,
+                                             const void* pair_bias, const void* out, const float* lse,
+                                             const void* dout, void* dq, void* dk, void* dv, void* dmask_bias,
+                                             void* dpair_bias, float* delta, void* workspace, size_t workspace_bytes,
+                                             const evo_layout_t* layout, const evo_shape_t* shape, evo_dtype_t dtype,
+                                             void* stream) {
+    const evo_status_t st = evo_attn_bwd_check_strided(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv,
+                                                       dmask_bias, dpair_bias, delta, workspace, workspace_bytes,
+                                                       layout, shape, dtype);
+    if (st != EVO_OK) return st;
+    evo::BwdArgs a{q,  k,  v,  mask_bias,  pair_bias,  out,   lse,     dout,    dq,      dk,      dv,
+                   dmask_bias, dpair_bias, delta, nullptr, 0, shape->B, shape->N, shape->L, shape->H, shape->D,
+                   strides_of(*layout)};
+    if (workspace && dpair_bias) {
+        a.ws_chunks = usable_chunks(a, dtype, workspace_bytes);
+        if (a.ws_chunks) a.ws = static_cast<float*>(workspace);
+    }
+    const hipError_t err = evo::launch_bwd(a, static_cast<int>(dtype), static_cast<hipStream_t>(stream));
+    if (err == hipSuccess) return EVO_OK;
+    g_last_hip_error = static_cast<int>(err);
+    return EVO_ERR_HIP;
 }
 
 extern "C" evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v, const void* mask_bias,
@@ -311,20 +399,11 @@ extern "C" evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v
                                      void* dq, void* dk, void* dv, void* dmask_bias, void* dpair_bias,
                                      float* delta, void* workspace, size_t workspace_bytes, const evo_shape_t* shape,
                                      evo_dtype_t dtype, void* stream) {
-    const evo_status_t st = evo_attn_bwd_check(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv,
-                                               dmask_bias, dpair_bias, delta, workspace, workspace_bytes, shape,
-                                               dtype);
-    if (st != EVO_OK) return st;
-    evo::BwdArgs a{q,  k,  v,  mask_bias,  pair_bias,  out,   lse,     dout,    dq,      dk,      dv,
-                   dmask_bias, dpair_bias, delta, nullptr, 0, shape->B, shape->N, shape->L, shape->H, shape->D};
-    if (workspace && dpair_bias) {
-        a.ws_chunks = usable_chunks(shape, dtype, workspace_bytes);
-        if (a.ws_chunks) a.ws = static_cast<float*>(workspace);
-    }
-    const hipError_t err = evo::launch_bwd(a, static_cast<int>(dtype), static_cast<hipStream_t>(stream));
-    if (err == hipSuccess) return EVO_OK;
-    g_last_hip_error = static_cast<int>(err);
-    return EVO_ERR_HIP;
+    if (!shape) return EVO_ERR_NULL_POINTER;
+    evo_layout_t lay;
+    evo_attn_dense_layout(shape, &lay);
+    return evo_attn_bwd_strided(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias, dpair_bias,
+                                delta, workspace, workspace_bytes, &lay, shape, dtype, stream);
 }
 
 extern "C" evo_status_t evo_trimul_check(const void* a, const void* w, const void* x,

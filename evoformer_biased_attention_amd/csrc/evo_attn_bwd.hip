@@ -74,6 +74,7 @@ struct Params {
     int64_t blocks_l;  // ceil(L / 64)
     int64_t groups_j;  // ceil(L / kJG)
     float scale;       // 1 / sqrt(D)
+    Strides st;        // element strides; each gradient shares its tensor's (dout: out's, delta: lse's)
 };
 
 // exp(s - lse) for a live row; rows whose lse is -inf have no softmax and
@@ -87,8 +88,8 @@ __device__ inline float weight(float s, float lse_i) {
 // ---------------------------------------------------------------------------
 template <class T, int D>
 __global__ __launch_bounds__(kLanes) void bwd_dq_kernel(Params<T> p) {
-    __shared__ float ks[kBlk][D + 1];
-    __shared__ float vs[kBlk][D + 1];
+    __shared__ float kt[kBlk][D + 1];
+    __shared__ float vt[kBlk][D + 1];
     __shared__ float ms[kBlk];
     __shared__ float pt[kLanes][kBlk + 1];  // pair tile: [query in block][key in block]
 
@@ -99,27 +100,29 @@ __global__ __launch_bounds__(kLanes) void bwd_dq_kernel(Params<T> p) {
     id /= p.H;
     const int64_t n = id % p.N;
     const int64_t b = id / p.N;
-    const int64_t L = p.L, HD = p.H * D;
+    const int64_t L = p.L;
+    const Strides& st = p.st;
     const int lane = threadIdx.x;
     const int64_t i = qb * kLanes + lane;
     const bool active = i < L;
     const int64_t irow = active ? i : L - 1;
-    const int64_t slice = ((b * p.N + n) * L * p.H + h) * D;  // element (b, n, 0, h, 0)
+    // elements (b, n, 0, h, 0) of q, k, v and out / dout
+    const int64_t qs = b * st.q[0] + n * st.q[1] + h * st.q[3], ks = b * st.k[0] + n * st.k[1] + h * st.k[3];
+    const int64_t vs = b * st.v[0] + n * st.v[1] + h * st.v[3], os = b * st.o[0] + n * st.o[1] + h * st.o[3];
 
     float qr[D], dor[D], acc[D];
     float delta = 0.f;
     for (int d = 0; d < D; ++d) {
-        const int64_t o = slice + irow * HD + d;
-        qr[d] = T::ld(p.q, o);
-        dor[d] = T::ld(p.dout, o);
-        delta = fmaf(dor[d], T::ld(p.out, o), delta);
+        qr[d] = T::ld(p.q, qs + irow * st.q[2] + d);
+        dor[d] = T::ld(p.dout, os + irow * st.o[2] + d);
+        delta = fmaf(dor[d], T::ld(p.out, os + irow * st.o[2] + d), delta);
         acc[d] = 0.f;
     }
-    const int64_t row = ((b * p.N + n) * p.H + h) * L + irow;
+    const int64_t row = ((b * p.N + n) * p.H + h) * st.lrow + irow;
     const float lse_i = p.lse[row];
     if (active) p.delta[row] = delta;
-    const typename T::S* mrow = p.mask ? p.mask + (b * p.N + n) * L : nullptr;
-    const typename T::S* pmat = p.pair ? p.pair + (b * p.H + h) * L * L : nullptr;
+    const typename T::S* mrow = p.mask ? p.mask + b * st.mb + n * st.mn : nullptr;
+    const typename T::S* pmat = p.pair ? p.pair + b * st.pb + h * st.ph : nullptr;
 
     for (int64_t k0 = 0; k0 < L; k0 += kBlk) {
         const int cnt = int(L - k0 < kBlk ? L - k0 : kBlk);
@@ -127,31 +130,31 @@ __global__ __launch_bounds__(kLanes) void bwd_dq_kernel(Params<T> p) {
         for (int e = lane; e < kBlk * D; e += kLanes) {
             const int j = e / D, d = e % D;
             const bool in = j < cnt;
-            ks[j][d] = in ? T::ld(p.k, slice + (k0 + j) * HD + d) : 0.f;
-            vs[j][d] = in ? T::ld(p.v, slice + (k0 + j) * HD + d) : 0.f;
+            kt[j][d] = in ? T::ld(p.k, ks + (k0 + j) * st.k[2] + d) : 0.f;
+            vt[j][d] = in ? T::ld(p.v, vs + (k0 + j) * st.v[2] + d) : 0.f;
         }
         ms[lane] = (mrow && lane < cnt) ? T::ld(mrow, k0 + lane) : 0.f;
         if (pmat)
             for (int e = lane; e < kLanes * kBlk; e += kLanes) {
                 const int r = e / kBlk, c = e % kBlk;
                 const int64_t gi = qb * kLanes + r;
-                pt[r][c] = (gi < L && c < cnt) ? T::ld(pmat, gi * L + k0 + c) : 0.f;
+                pt[r][c] = (gi < L && c < cnt) ? T::ld(pmat, gi * st.pi + k0 + c) : 0.f;
             }
         __syncthreads();
         for (int j = 0; j < cnt; ++j) {
             float dot = 0.f, dp = 0.f;
             for (int d = 0; d < D; ++d) {
-                dot = fmaf(qr[d], ks[j][d], dot);
-                dp = fmaf(dor[d], vs[j][d], dp);
+                dot = fmaf(qr[d], kt[j][d], dot);
+                dp = fmaf(dor[d], vt[j][d], dp);
             }
             float s = dot * p.scale + ms[j];
             if (pmat) s += pt[lane][j];
             const float ds = weight(s, lse_i) * (dp - delta);
-            for (int d = 0; d < D; ++d) acc[d] = fmaf(ds, ks[j][d], acc[d]);
+            for (int d = 0; d < D; ++d) acc[d] = fmaf(ds, kt[j][d], acc[d]);
         }
     }
     if (!active) return;
-    for (int d = 0; d < D; ++d) T::st(p.dq, slice + i * HD + d, acc[d] * p.scale);
+    for (int d = 0; d < D; ++d) T::st(p.dq, qs + i * st.q[2] + d, acc[d] * p.scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -161,7 +164,7 @@ __global__ __launch_bounds__(kLanes) void bwd_dq_kernel(Params<T> p) {
 // ---------------------------------------------------------------------------
 template <class T, int D>
 __global__ __launch_bounds__(kLanes) void bwd_dkdv_kernel(Params<T> p) {
-    __shared__ float qs[kBlk][D + 1];
+    __shared__ float qt[kBlk][D + 1];
     __shared__ float dos[kBlk][D + 1];
     __shared__ float ls[kBlk];
     __shared__ float dl[kBlk];
@@ -172,23 +175,26 @@ __global__ __launch_bounds__(kLanes) void bwd_dkdv_kernel(Params<T> p) {
     id /= p.blocks_l;
     const int64_t n = id % p.N;
     const int64_t b = id / p.N;
-    const int64_t L = p.L, H = p.H, HD = H * D;
+    const int64_t L = p.L, H = p.H;
+    const Strides& st = p.st;
     const int lane = threadIdx.x;
     const int64_t j = kb * kLanes + lane;
     const bool active = j < L;
     const int64_t jrow = active ? j : L - 1;
-    const float mask_j = p.mask ? T::ld(p.mask, (b * p.N + n) * L + jrow) : 0.f;
+    const int64_t mrow = b * st.mb + n * st.mn;
+    const float mask_j = p.mask ? T::ld(p.mask, mrow + jrow) : 0.f;
     float dmask = 0.f;
 
     for (int64_t h = 0; h < H; ++h) {
-        const int64_t slice = ((b * p.N + n) * L * H + h) * D;
-        const float* lrow = p.lse + ((b * p.N + n) * H + h) * L;
-        const float* drow = p.delta + ((b * p.N + n) * H + h) * L;
-        const typename T::S* pmat = p.pair ? p.pair + (b * H + h) * L * L : nullptr;
+        const int64_t qs = b * st.q[0] + n * st.q[1] + h * st.q[3], ks = b * st.k[0] + n * st.k[1] + h * st.k[3];
+        const int64_t vs = b * st.v[0] + n * st.v[1] + h * st.v[3], os = b * st.o[0] + n * st.o[1] + h * st.o[3];
+        const float* lrow = p.lse + ((b * p.N + n) * H + h) * st.lrow;
+        const float* drow = p.delta + ((b * p.N + n) * H + h) * st.lrow;
+        const typename T::S* pmat = p.pair ? p.pair + b * st.pb + h * st.ph : nullptr;
         float kr[D], vr[D], dk[D], dv[D];
         for (int d = 0; d < D; ++d) {
-            kr[d] = T::ld(p.k, slice + jrow * HD + d);
-            vr[d] = T::ld(p.v, slice + jrow * HD + d);
+            kr[d] = T::ld(p.k, ks + jrow * st.k[2] + d);
+            vr[d] = T::ld(p.v, vs + jrow * st.v[2] + d);
             dk[d] = 0.f;
             dv[d] = 0.f;
         }
@@ -198,8 +204,8 @@ __global__ __launch_bounds__(kLanes) void bwd_dkdv_kernel(Params<T> p) {
             for (int e = lane; e < kBlk * D; e += kLanes) {
                 const int r = e / D, d = e % D;
                 const bool in = r < cnt;
-                qs[r][d] = in ? T::ld(p.q, slice + (i0 + r) * HD + d) : 0.f;
-                dos[r][d] = in ? T::ld(p.dout, slice + (i0 + r) * HD + d) : 0.f;
+                qt[r][d] = in ? T::ld(p.q, qs + (i0 + r) * st.q[2] + d) : 0.f;
+                dos[r][d] = in ? T::ld(p.dout, os + (i0 + r) * st.o[2] + d) : 0.f;
             }
             ls[lane] = lane < cnt ? lrow[i0 + lane] : -INFINITY;
             dl[lane] = lane < cnt ? drow[i0 + lane] : 0.f;
@@ -207,7 +213,7 @@ __global__ __launch_bounds__(kLanes) void bwd_dkdv_kernel(Params<T> p) {
                 for (int e = lane; e < kBlk * kLanes; e += kLanes) {
                     const int r = e / kLanes, c = e % kLanes;
                     const int64_t gj = kb * kLanes + c;
-                    pt[r][c] = (r < cnt && gj < L) ? T::ld(pmat, (i0 + r) * L + gj) : 0.f;
+                    pt[r][c] = (r < cnt && gj < L) ? T::ld(pmat, (i0 + r) * st.pi + gj) : 0.f;
                 }
             __syncthreads();
             for (int r = 0; r < cnt; ++r) {
@@ -215,7 +221,7 @@ __global__ __launch_bounds__(kLanes) void bwd_dkdv_kernel(Params<T> p) {
                 if (lse_i == -INFINITY) continue;  // a row without softmax: no gradient flows
                 float dot = 0.f, dp = 0.f;
                 for (int d = 0; d < D; ++d) {
-                    dot = fmaf(qs[r][d], kr[d], dot);
+                    dot = fmaf(qt[r][d], kr[d], dot);
                     dp = fmaf(dos[r][d], vr[d], dp);
                 }
                 float s = dot * p.scale + mask_j;
@@ -224,18 +230,18 @@ __global__ __launch_bounds__(kLanes) void bwd_dkdv_kernel(Params<T> p) {
                 const float ds = w * (dp - dl[r]);
                 for (int d = 0; d < D; ++d) {
                     dv[d] = fmaf(w, dos[r][d], dv[d]);
-                    dk[d] = fmaf(ds, qs[r][d], dk[d]);
+                    dk[d] = fmaf(ds, qt[r][d], dk[d]);
                 }
                 dmask += ds;
             }
         }
         if (active)
             for (int d = 0; d < D; ++d) {
-                T::st(p.dk, slice + j * HD + d, dk[d] * p.scale);
-                T::st(p.dv, slice + j * HD + d, dv[d]);
+                T::st(p.dk, ks + j * st.k[2] + d, dk[d] * p.scale);
+                T::st(p.dv, vs + j * st.v[2] + d, dv[d]);
             }
     }
-    if (active && p.dmask) T::st(p.dmask, (b * p.N + n) * L + j, dmask);
+    if (active && p.dmask) T::st(p.dmask, mrow + j, dmask);
 }
 
 // ---------------------------------------------------------------------------
@@ -245,8 +251,8 @@ __global__ __launch_bounds__(kLanes) void bwd_dkdv_kernel(Params<T> p) {
 // ---------------------------------------------------------------------------
 template <class T, int D>
 __global__ __launch_bounds__(kLanes) void bwd_dpair_kernel(Params<T> p) {
-    __shared__ float ks[kJG][D + 1];
-    __shared__ float vs[kJG][D + 1];
+    __shared__ float kt[kJG][D + 1];
+    __shared__ float vt[kJG][D + 1];
     __shared__ float ms[kJG];
 
     int64_t id = blockIdx.x;
@@ -256,14 +262,16 @@ __global__ __launch_bounds__(kLanes) void bwd_dpair_kernel(Params<T> p) {
     id /= p.blocks_l;
     const int64_t h = id % p.H;
     const int64_t b = id / p.H;
-    const int64_t L = p.L, H = p.H, HD = H * D;
+    const int64_t L = p.L, H = p.H;
+    const Strides& st = p.st;
     const int lane = threadIdx.x;
     const int64_t i = ib * kLanes + lane;
     const bool active = i < L;
     const int64_t irow = active ? i : L - 1;
     const int64_t j0 = jg * kJG;
     const int jcnt = int(L - j0 < kJG ? L - j0 : kJG);
-    const typename T::S* prow = p.pair + ((b * H + h) * L + irow) * L + j0;
+    const int64_t pmat = b * st.pb + h * st.ph;
+    const typename T::S* prow = p.pair + pmat + irow * st.pi + j0;
 
     float pr[kJG], acc[kJG];
 #pragma unroll
@@ -272,37 +280,38 @@ __global__ __launch_bounds__(kLanes) void bwd_dpair_kernel(Params<T> p) {
         acc[c] = 0.f;
     }
     for (int64_t n = 0; n < p.N; ++n) {
-        const int64_t slice = ((b * p.N + n) * L * H + h) * D;
+        const int64_t qs = b * st.q[0] + n * st.q[1] + h * st.q[3], ks = b * st.k[0] + n * st.k[1] + h * st.k[3];
+        const int64_t vs = b * st.v[0] + n * st.v[1] + h * st.v[3], os = b * st.o[0] + n * st.o[1] + h * st.o[3];
         float qr[D], dor[D];
         for (int d = 0; d < D; ++d) {
-            qr[d] = T::ld(p.q, slice + irow * HD + d);
-            dor[d] = T::ld(p.dout, slice + irow * HD + d);
+            qr[d] = T::ld(p.q, qs + irow * st.q[2] + d);
+            dor[d] = T::ld(p.dout, os + irow * st.o[2] + d);
         }
-        const int64_t row = ((b * p.N + n) * H + h) * L + irow;
+        const int64_t row = ((b * p.N + n) * H + h) * st.lrow + irow;
         const float lse_i = p.lse[row];
         const float delta = p.delta[row];
         __syncthreads();
         for (int e = lane; e < kJG * D; e += kLanes) {
             const int c = e / D, d = e % D;
             const bool in = c < jcnt;
-            ks[c][d] = in ? T::ld(p.k, slice + (j0 + c) * HD + d) : 0.f;
-            vs[c][d] = in ? T::ld(p.v, slice + (j0 + c) * HD + d) : 0.f;
+            kt[c][d] = in ? T::ld(p.k, ks + (j0 + c) * st.k[2] + d) : 0.f;
+            vt[c][d] = in ? T::ld(p.v, vs + (j0 + c) * st.v[2] + d) : 0.f;
         }
-        if (lane < kJG) ms[lane] = (p.mask && lane < jcnt) ? T::ld(p.mask, (b * p.N + n) * L + j0 + lane) : 0.f;
+        if (lane < kJG) ms[lane] = (p.mask && lane < jcnt) ? T::ld(p.mask, b * st.mb + n * st.mn + j0 + lane) : 0.f;
         __syncthreads();
 #pragma unroll
         for (int c = 0; c < kJG; ++c) {
             float dot = 0.f, dp = 0.f;
             for (int d = 0; d < D; ++d) {
-                dot = fmaf(qr[d], ks[c][d], dot);
-                dp = fmaf(dor[d], vs[c][d], dp);
+                dot = fmaf(qr[d], kt[c][d], dot);
+                dp = fmaf(dor[d], vt[c][d], dp);
             }
             const float s = dot * p.scale + ms[c] + pr[c];
             acc[c] = fmaf(weight(s, lse_i), dp - delta, acc[c]);
         }
     }
     if (!active) return;
-    typename T::S* out = p.dpair + ((b * H + h) * L + i) * L + j0;
+    typename T::S* out = p.dpair + pmat + i * st.pi + j0;
 #pragma unroll
     for (int c = 0; c < kJG; ++c)
         if (c < jcnt) T::st(out, c, acc[c]);
@@ -334,6 +343,7 @@ hipError_t launch_all(const BwdArgs& a, unsigned stages, hipStream_t stream) {
     p.blocks_l = (a.L + kLanes - 1) / kLanes;
     p.groups_j = (a.L + kJG - 1) / kJG;
     p.scale = float(1.0 / std::sqrt(double(D)));
+    p.st = a.st;
 
     const int64_t g_dq = a.B * a.N * a.H * p.blocks_l;
     const int64_t g_kv = a.B * a.N * p.blocks_l;

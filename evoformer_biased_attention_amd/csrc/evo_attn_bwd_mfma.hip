@@ -148,6 +148,7 @@ struct Params {
     int64_t total;    // workgroups of the launch
     float c1;         // log2(e) / sqrt(D): raw q.k -> base-2 exponent
     float scale;      // 1 / sqrt(D)
+    Strides st;       // element strides; each gradient shares its tensor's (dout: out's, delta: lse's)
 };
 
 // Per-row constant of the exponent: lse * log2(e), or +inf for a row without
@@ -180,22 +181,28 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
     const int64_t qb = id - r1 * p.rblocks.d;
     const int64_t h = r1 - r2 * p.hd.d, n = r2 - r3 * p.nd.d, b = r3;
     const int L = (int)p.L;
-    const int64_t HD = p.H * D;
-    const int64_t slice = ((b * p.N + n) * p.L * p.H + h) * D;
-    const int64_t rowbase = ((b * p.N + n) * p.H + h) * p.L;  // lse / delta index of query 0
+    const Strides& st = p.st;
+    // element offsets of (b, n, 0, h, 0) in q, k, v and out / dout
+    const int64_t qs = b * st.q[0] + n * st.q[1] + h * st.q[3];
+    const int64_t ks = b * st.k[0] + n * st.k[1] + h * st.k[3];
+    const int64_t vs = b * st.v[0] + n * st.v[1] + h * st.v[3];
+    const int64_t os = b * st.o[0] + n * st.o[1] + h * st.o[3];
+    const int64_t rowbase = ((b * p.N + n) * p.H + h) * st.lrow;  // lse / delta index of query 0
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
     const int nblocks = (L + kKB - 1) / kKB;
-    const uint32_t rowb = (uint32_t)HD * 2;
-    const uint32_t span = (uint32_t)(L - 1) * rowb + D * 2;
-    const Rsrc rq = make_rsrc(p.q + slice, span);
-    const Rsrc rk = make_rsrc(p.k + slice, span);
-    const Rsrc rv = make_rsrc(p.v + slice, span);
-    const Rsrc rdo = make_rsrc(p.dout + slice, span);
-    const Rsrc ro = make_rsrc(p.out + slice, span);
-    const Rsrc rp = make_rsrc(PAIR ? p.pair + (b * p.H + h) * p.L * p.L : p.q, PAIR ? (uint32_t)L * (uint32_t)L * 2u : 0u);
-    const Rsrc rm = make_rsrc(MASK ? p.mask + (b * p.N + n) * p.L : p.q, MASK ? (uint32_t)L * 2u : 0u);
+    // bytes between consecutive rows; every offset below stays in 32 bits (the launcher checks)
+    const uint32_t rowq = (uint32_t)st.q[2] * 2, rowk = (uint32_t)st.k[2] * 2, rowv = (uint32_t)st.v[2] * 2;
+    const uint32_t rowo = (uint32_t)st.o[2] * 2, rowp = (uint32_t)st.pi * 2;
+    const uint32_t last = (uint32_t)(L - 1);
+    const Rsrc rq = make_rsrc(p.q + qs, last * rowq + D * 2);
+    const Rsrc rk = make_rsrc(p.k + ks, last * rowk + D * 2);
+    const Rsrc rv = make_rsrc(p.v + vs, last * rowv + D * 2);
+    const Rsrc rdo = make_rsrc(p.dout + os, last * rowo + D * 2);
+    const Rsrc ro = make_rsrc(p.out + os, last * rowo + D * 2);
+    const Rsrc rp = make_rsrc(PAIR ? p.pair + b * st.pb + h * st.ph : p.q, PAIR ? last * rowp + (uint32_t)L * 2u : 0u);
+    const Rsrc rm = make_rsrc(MASK ? p.mask + b * st.mb + n * st.mn : p.q, MASK ? (uint32_t)L * 2u : 0u);
 
     const int q0 = (int)qb * kBlockRows + wave * kWaveRows;
     // B operands of S^T = K.Q^T and dP^T = V.dO^T: lane (c + 16g) holds row
@@ -204,8 +211,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
     float delta[2], lse2[2];
     for (int t = 0; t < 2; ++t) {
         const int i = q0 + 16 * t + c;
-        const uint32_t off = g < kDC ? (uint32_t)i * rowb + 16u * g : kOOB;
-        const uint4 qq = bload16(rq, off, 0), dd = bload16(rdo, off, 0), oo = bload16(ro, off, 0);
+        const uint32_t offq = g < kDC ? (uint32_t)i * rowq + 16u * g : kOOB;
+        const uint32_t offo = g < kDC ? (uint32_t)i * rowo + 16u * g : kOOB;
+        const uint4 qq = bload16(rq, offq, 0), dd = bload16(rdo, offo, 0), oo = bload16(ro, offo, 0);
         qop[t] = as_v8<E>(qq);
         dop[t] = as_v8<E>(dd);
         const uint32_t dw[4] = {dd.x, dd.y, dd.z, dd.w}, ow[4] = {oo.x, oo.y, oo.z, oo.w};
@@ -223,16 +231,19 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
     // copies of one 64-key block (same addressing as the forward kernel)
     const uint32_t qwg = (uint32_t)(qb * kBlockRows);
     const uint32_t kvchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
-    const uint32_t kvo = kvchunk < kDC ? (uint32_t)(16 * wave + (lane >> 2)) * rowb + 16u * kvchunk : kOOB;
+    const uint32_t kvrow = (uint32_t)(16 * wave + (lane >> 2));
+    const uint32_t ko = kvchunk < kDC ? kvrow * rowk + 16u * kvchunk : kOOB;
+    const uint32_t vo = kvchunk < kDC ? kvrow * rowv + 16u * kvchunk : kOOB;
     uint32_t pvo[4];
     for (int j = 0; j < 4; ++j) {
+        // rows past L start beyond the pair range (its row stride is at least L)
         const uint32_t row = 8u * (4 * wave + j) + (lane >> 3);
-        pvo[j] = (qwg + row) * (uint32_t)L * 2u + 16u * ((lane & 7) ^ (lane >> 3));
+        pvo[j] = (qwg + row) * rowp + 16u * ((lane & 7) ^ (lane >> 3));
     }
     auto copy_block = [&](int blk, DqBuf* __restrict__ dst) {
         const uint32_t k0 = (uint32_t)blk * kKB;
-        dma16(rk, &dst->k[64 * wave], kvo + k0 * rowb, 0);
-        dma16(rv, &dst->v[64 * wave], kvo + k0 * rowb, 0);
+        dma16(rk, &dst->k[64 * wave], ko + k0 * rowk, 0);
+        dma16(rv, &dst->v[64 * wave], vo + k0 * rowv, 0);
         if (PAIR)
             for (int j = 0; j < 4; ++j) dma16(rp, &dst->pt[64 * (4 * wave + j)], pvo[j] + k0 * 2u, 0);
         if (MASK && wave == 0 && lane < 8) dma16(rm, &dst->mt[0], 16u * lane + k0 * 2u, 0);
@@ -333,7 +344,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
         for (int dh = 0; dh < kDHT; ++dh) {
             if (16 * dh + 4 * g >= D) continue;
             const f32x4 o = dqacc[t][dh] * p.scale;
-            *reinterpret_cast<uint2*>(p.dq + slice + i * HD + 16 * dh + 4 * g) = uint2{pack2<E>(o[0], o[1]), pack2<E>(o[2], o[3])};
+            *reinterpret_cast<uint2*>(p.dq + qs + i * st.q[2] + 16 * dh + 4 * g) =
+                uint2{pack2<E>(o[0], o[1]), pack2<E>(o[2], o[3])};
         }
     }
 }
@@ -370,52 +382,61 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
     const int64_t kb = id - r1 * p.rblocks.d;
     const int64_t n = r1 - r2 * p.nd.d, b = r2;
     const int L = (int)p.L, H = (int)p.H;
-    const int64_t HD = p.H * D;
+    const Strides& st = p.st;
     const int64_t bn = b * p.N + n;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
     const int nqb = (L + kKB - 1) / kKB;  // query blocks per head
     const int nsteps = H * nqb;
-    const uint32_t rowb = (uint32_t)HD * 2;
-    const uint32_t span = (uint32_t)L * rowb;  // below 2^31: the launcher bounds L * H * D * 2
-    const int64_t base = bn * p.L * HD;        // element (b, n, 0, 0, 0)
-    const Rsrc rq = make_rsrc(p.q + base, span);
-    const Rsrc rk = make_rsrc(p.k + base, span);
-    const Rsrc rv = make_rsrc(p.v + base, span);
-    const Rsrc rdo = make_rsrc(p.dout + base, span);
+    // element offsets of (b, n, 0, 0, 0) in q, k, v and out / dout; bytes
+    // between rows and between heads.  A buffer covers every head of the
+    // sequence; its offsets stay in 32 bits (the launcher checks).
+    const int64_t qbn = b * st.q[0] + n * st.q[1], kbn = b * st.k[0] + n * st.k[1];
+    const int64_t vbn = b * st.v[0] + n * st.v[1], obn = b * st.o[0] + n * st.o[1];
+    const uint32_t rowq = (uint32_t)st.q[2] * 2, rowk = (uint32_t)st.k[2] * 2, rowv = (uint32_t)st.v[2] * 2;
+    const uint32_t rowo = (uint32_t)st.o[2] * 2, rowp = (uint32_t)st.pi * 2;
+    const uint32_t hq = (uint32_t)st.q[3] * 2, hk = (uint32_t)st.k[3] * 2, hv = (uint32_t)st.v[3] * 2;
+    const uint32_t ho = (uint32_t)st.o[3] * 2;
+    const uint32_t last = (uint32_t)(L - 1), lasth = (uint32_t)(H - 1);
+    const Rsrc rq = make_rsrc(p.q + qbn, last * rowq + lasth * hq + D * 2);
+    const Rsrc rk = make_rsrc(p.k + kbn, last * rowk + lasth * hk + D * 2);
+    const Rsrc rv = make_rsrc(p.v + vbn, last * rowv + lasth * hv + D * 2);
+    const Rsrc rdo = make_rsrc(p.dout + obn, last * rowo + lasth * ho + D * 2);
     const int kw0 = (int)kb * kBlockRows + wave * kWaveRows;  // first key of the wave
+    const int64_t mrow = b * st.mb + n * st.mn;                // mask row of (b, n)
 
     // per-key mask term (base 2), constant over heads and queries
     float mk[2] = {0.f, 0.f};
     if (MASK)
         for (int t = 0; t < 2; ++t) {
             const int j = kw0 + 16 * t + c;
-            mk[t] = j < L ? E::widen(p.mask[bn * p.L + j]) * kLog2e : 0.f;
+            mk[t] = j < L ? E::widen(p.mask[mrow + j]) * kLog2e : 0.f;
         }
 
     // copies of step `it` (head it / nqb, queries 64 (it % nqb) ..)
     const uint32_t qdchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
-    const uint32_t qdo = qdchunk < kDC ? (uint32_t)(16 * wave + (lane >> 2)) * rowb + 16u * qdchunk : kOOB;
+    const uint32_t qdrow = (uint32_t)(16 * wave + (lane >> 2));
+    const uint32_t qoff = qdchunk < kDC ? qdrow * rowq + 16u * qdchunk : kOOB;
+    const uint32_t dooff = qdchunk < kDC ? qdrow * rowo + 16u * qdchunk : kOOB;
     uint32_t pvo[4];
     for (int j = 0; j < 4; ++j) {
+        // rows past L start beyond the pair range (its row stride is at least L)
         const uint32_t row = (uint32_t)(16 * wave + 4 * j + (lane >> 4));
-        pvo[j] = row * (uint32_t)L * 2u + (uint32_t)kb * kBlockRows * 2u + 16u * ((lane & 15) ^ (2 * (row & 7)));
+        pvo[j] = row * rowp + (uint32_t)kb * kBlockRows * 2u + 16u * ((lane & 15) ^ (2 * (row & 7)));
     }
     float lsv = 0.f, dlv = 0.f;  // wave 0: this lane's query of the step being copied
     auto copy_block = [&](int it, KvBuf* __restrict__ dst) {
         const int h = it / nqb, q0 = (it - h * nqb) * kKB;
-        const uint32_t hoff = (uint32_t)h * D * 2u;
-        dma16(rq, &dst->q[64 * wave], qdo + (uint32_t)q0 * rowb + hoff, 0);
-        dma16(rdo, &dst->dout[64 * wave], qdo + (uint32_t)q0 * rowb + hoff, 0);
+        dma16(rq, &dst->q[64 * wave], qoff + (uint32_t)q0 * rowq + (uint32_t)h * hq, 0);
+        dma16(rdo, &dst->dout[64 * wave], dooff + (uint32_t)q0 * rowo + (uint32_t)h * ho, 0);
         if (PAIR) {
-            const Rsrc rp = make_rsrc(p.pair + (b * p.H + h) * p.L * p.L, (uint32_t)L * (uint32_t)L * 2u);
-            for (int j = 0; j < 4; ++j)
-                dma16(rp, &dst->pt[64 * (4 * wave + j)], pvo[j] + (uint32_t)q0 * (uint32_t)L * 2u, 0);
+            const Rsrc rp = make_rsrc(p.pair + b * st.pb + h * st.ph, last * rowp + (uint32_t)L * 2u);
+            for (int j = 0; j < 4; ++j) dma16(rp, &dst->pt[64 * (4 * wave + j)], pvo[j] + (uint32_t)q0 * rowp, 0);
         }
         if (wave == 0) {
             const int i = q0 + lane;
-            const int64_t row = (bn * p.H + h) * p.L + i;
+            const int64_t row = (bn * p.H + h) * st.lrow + i;
             lsv = i < L ? lse_base2(p.lse[row]) : INFINITY;
             dlv = i < L ? p.delta[row] : 0.f;
         }
@@ -443,9 +464,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
         if (qbk == 0) {
             for (int t = 0; t < 2; ++t) {
                 const uint32_t j = (uint32_t)(kw0 + 16 * t + c);
-                const uint32_t off = g < kDC ? j * rowb + 16u * g : kOOB;
-                kop[t] = as_v8<E>(bload16(rk, off + (uint32_t)h * D * 2u, 0));
-                vop[t] = as_v8<E>(bload16(rv, off + (uint32_t)h * D * 2u, 0));
+                kop[t] = as_v8<E>(bload16(rk, g < kDC ? j * rowk + (uint32_t)h * hk + 16u * g : kOOB, 0));
+                vop[t] = as_v8<E>(bload16(rv, g < kDC ? j * rowv + (uint32_t)h * hv + 16u * g : kOOB, 0));
                 for (int dh = 0; dh < 2; ++dh) dkacc[t][dh] = dvacc[t][dh] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
@@ -541,10 +561,12 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
                 if (j >= L) continue;
                 for (int dh = 0; dh < kDHT; ++dh) {
                     if (16 * dh + 4 * g >= D) continue;
-                    const int64_t o = base + j * HD + (int64_t)h * D + 16 * dh + 4 * g;
+                    const int64_t d0 = 16 * dh + 4 * g;
                     const f32x4 dk = dkacc[t][dh] * p.scale, dv = dvacc[t][dh];
-                    *reinterpret_cast<uint2*>(p.dk + o) = uint2{pack2<E>(dk[0], dk[1]), pack2<E>(dk[2], dk[3])};
-                    *reinterpret_cast<uint2*>(p.dv + o) = uint2{pack2<E>(dv[0], dv[1]), pack2<E>(dv[2], dv[3])};
+                    *reinterpret_cast<uint2*>(p.dk + kbn + j * st.k[2] + h * st.k[3] + d0) =
+                        uint2{pack2<E>(dk[0], dk[1]), pack2<E>(dk[2], dk[3])};
+                    *reinterpret_cast<uint2*>(p.dv + vbn + j * st.v[2] + h * st.v[3] + d0) =
+                        uint2{pack2<E>(dv[0], dv[1]), pack2<E>(dv[2], dv[3])};
                 }
             }
         }
@@ -555,7 +577,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
             const int j = kw0 + 16 * t + c;
             if (g == 0 && j < L) {
                 const uint32_t w = pack2<E>(tot, 0.f);
-                p.dmask[bn * p.L + j] = (u16)(w & 0xffffu);
+                p.dmask[mrow + j] = (u16)(w & 0xffffu);
             }
         }
 }
@@ -599,23 +621,26 @@ __global__ __launch_bounds__(kZW * 64, 1) void bwd_dpair_mfma(Params p) {
     const int64_t qt0 = r1 - r2 * p.rblocks.d;
     const int64_t h = r2 - r3 * p.hd.d, b = r3;
     const int L = (int)p.L;
-    const int64_t N = p.N, HD = p.H * D;
+    const int64_t N = p.N;
+    const Strides& st = p.st;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
     const int i0 = (int)qt0 * 16 * kZQ, j0 = (int)kt0 * 16 * kZK;
-    const uint32_t rowb = (uint32_t)HD * 2;
-    const uint32_t span = (uint32_t)(L - 1) * rowb + D * 2;
+    const uint32_t rowq = (uint32_t)st.q[2] * 2, rowk = (uint32_t)st.k[2] * 2, rowv = (uint32_t)st.v[2] * 2;
+    const uint32_t rowo = (uint32_t)st.o[2] * 2;
+    const uint32_t last = (uint32_t)(L - 1);
+    const int64_t pmat = b * st.pb + h * st.ph;  // pair matrix of (b, h)
 
     // pair bias (base 2) of lane c + 16g: query i0 + 16qt + c, keys j0 + 16kt + 4g + 0..3
     float pb[kZQ][kZK][4];
     {
-        const u16* pm = p.pair + (b * p.H + h) * p.L * p.L;
+        const u16* pm = p.pair + pmat;
         for (int qt = 0; qt < kZQ; ++qt)
             for (int kt = 0; kt < kZK; ++kt) {
                 const int i = i0 + 16 * qt + c, j = j0 + 16 * kt + 4 * g;
                 uint2 w = {0u, 0u};
-                if (i < L && j < L) w = *reinterpret_cast<const uint2*>(pm + (int64_t)i * L + j);
+                if (i < L && j < L) w = *reinterpret_cast<const uint2*>(pm + (int64_t)i * st.pi + j);
                 const f32x2 a = unpack2<E>(w.x), bb = unpack2<E>(w.y);
                 pb[qt][kt][0] = a[0] * kLog2e, pb[qt][kt][1] = a[1] * kLog2e;
                 pb[qt][kt][2] = bb[0] * kLog2e, pb[qt][kt][3] = bb[1] * kLog2e;
@@ -629,22 +654,23 @@ __global__ __launch_bounds__(kZW * 64, 1) void bwd_dpair_mfma(Params p) {
     };
     auto load = [&](int64_t n) {
         Ops o;
-        const int64_t slice = ((b * N + n) * p.L * p.H + h) * D;
-        const Rsrc rk = make_rsrc(p.k + slice, span), rv = make_rsrc(p.v + slice, span);
-        const Rsrc rq = make_rsrc(p.q + slice, span), rd = make_rsrc(p.dout + slice, span);
+        const Rsrc rk = make_rsrc(p.k + b * st.k[0] + n * st.k[1] + h * st.k[3], last * rowk + D * 2);
+        const Rsrc rv = make_rsrc(p.v + b * st.v[0] + n * st.v[1] + h * st.v[3], last * rowv + D * 2);
+        const Rsrc rq = make_rsrc(p.q + b * st.q[0] + n * st.q[1] + h * st.q[3], last * rowq + D * 2);
+        const Rsrc rd = make_rsrc(p.dout + b * st.o[0] + n * st.o[1] + h * st.o[3], last * rowo + D * 2);
         for (int kt = 0; kt < kZK; ++kt) {
-            const uint32_t off = g < kDC ? (uint32_t)(j0 + 16 * kt + c) * rowb + 16u * g : kOOB;
-            o.k[kt] = as_v8<E>(bload16(rk, off, 0));
-            o.v[kt] = as_v8<E>(bload16(rv, off, 0));
-            const int j = j0 + 16 * kt + 4 * g;
-            o.mk[kt] = (MASK && j < L) ? *reinterpret_cast<const uint2*>(p.mask + (b * N + n) * p.L + j) : uint2{0u, 0u};
+            const uint32_t j = (uint32_t)(j0 + 16 * kt + c);
+            o.k[kt] = as_v8<E>(bload16(rk, g < kDC ? j * rowk + 16u * g : kOOB, 0));
+            o.v[kt] = as_v8<E>(bload16(rv, g < kDC ? j * rowv + 16u * g : kOOB, 0));
+            const int jm = j0 + 16 * kt + 4 * g;
+            o.mk[kt] = (MASK && jm < L) ? *reinterpret_cast<const uint2*>(p.mask + b * st.mb + n * st.mn + jm)
+                                        : uint2{0u, 0u};
         }
         for (int qt = 0; qt < kZQ; ++qt) {
             const int i = i0 + 16 * qt + c;
-            const uint32_t off = g < kDC ? (uint32_t)i * rowb + 16u * g : kOOB;
-            o.q[qt] = as_v8<E>(bload16(rq, off, 0));
-            o.d[qt] = as_v8<E>(bload16(rd, off, 0));
-            const int64_t row = ((b * N + n) * p.H + h) * p.L + i;
+            o.q[qt] = as_v8<E>(bload16(rq, g < kDC ? (uint32_t)i * rowq + 16u * g : kOOB, 0));
+            o.d[qt] = as_v8<E>(bload16(rd, g < kDC ? (uint32_t)i * rowo + 16u * g : kOOB, 0));
+            const int64_t row = ((b * N + n) * p.H + h) * st.lrow + i;
             o.ls[qt] = i < L ? lse_base2(p.lse[row]) : INFINITY;
             o.dl[qt] = i < L ? p.delta[row] : 0.f;
         }
@@ -690,7 +716,7 @@ __global__ __launch_bounds__(kZW * 64, 1) void bwd_dpair_mfma(Params p) {
             for (int r = 0; r < 4; ++r) tot[r] += red[w][4 * f + r][l];
         const int i = i0 + 16 * qt + (l & 15), j = j0 + 16 * kt + 4 * (l >> 4);
         if (i < L && j < L)
-            *reinterpret_cast<uint2*>(p.dpair + ((b * p.H + h) * p.L + i) * p.L + j) =
+            *reinterpret_cast<uint2*>(p.dpair + pmat + (int64_t)i * st.pi + j) =
                 uint2{pack2<E>(tot[0], tot[1]), pack2<E>(tot[2], tot[3])};
     }
 }
@@ -754,24 +780,26 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
     const uint32_t ti = fdiv(tile, pp.tdim), tj = tile - ti * pp.tdim.d;
     const int64_t chunk = r1 - r2 * pp.chd.d, h = r2 - r3 * p.hd.d, b = r3;
     const int L = (int)p.L;
-    const int64_t N = p.N, HD = p.H * D;
+    const int64_t N = p.N;
+    const Strides& st = p.st;
     const int64_t n0 = chunk * N / pp.chunks, n1 = (chunk + 1) * N / pp.chunks;
     const int i0 = (int)ti * 64, j0 = (int)tj * 64;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
-    const uint32_t rowb = (uint32_t)HD * 2;
-    const uint32_t span = (uint32_t)(L - 1) * rowb + D * 2;
+    const uint32_t rowq = (uint32_t)st.q[2] * 2, rowk = (uint32_t)st.k[2] * 2, rowv = (uint32_t)st.v[2] * 2;
+    const uint32_t rowo = (uint32_t)st.o[2] * 2;
+    const uint32_t last = (uint32_t)(L - 1);
 
     // pair bias (base 2) of lane c + 16g: query i0 + 16 wave + c, keys j0 + 16kt + 4g + 0..3
     float pb[kKT][4];
     {
-        const u16* pm = p.pair + (b * p.H + h) * p.L * p.L;
+        const u16* pm = p.pair + b * st.pb + h * st.ph;
         const int i = i0 + 16 * wave + c;
         for (int kt = 0; kt < kKT; ++kt) {
             const int j = j0 + 16 * kt + 4 * g;
             uint2 w = {0u, 0u};
-            if (i < L && j < L) w = *reinterpret_cast<const uint2*>(pm + (int64_t)i * L + j);
+            if (i < L && j < L) w = *reinterpret_cast<const uint2*>(pm + (int64_t)i * st.pi + j);
             const f32x2 a = unpack2<E>(w.x), bb = unpack2<E>(w.y);
             pb[kt][0] = a[0] * kLog2e, pb[kt][1] = a[1] * kLog2e, pb[kt][2] = bb[0] * kLog2e, pb[kt][3] = bb[1] * kLog2e;
         }
@@ -780,20 +808,24 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
     // copies of step n: rows 16 wave + lane/4 of the tile, chunk (lane & 3) ^ ((lane >> 4) & 3)
     const uint32_t dchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
     const uint32_t trow = (uint32_t)(16 * wave + (lane >> 2));
-    const uint32_t qoff = dchunk < kDC ? ((uint32_t)i0 + trow) * rowb + 16u * dchunk : kOOB;
-    const uint32_t koff = dchunk < kDC ? ((uint32_t)j0 + trow) * rowb + 16u * dchunk : kOOB;
+    const bool din = dchunk < kDC;
+    const uint32_t qoff = din ? ((uint32_t)i0 + trow) * rowq + 16u * dchunk : kOOB;
+    const uint32_t dooff = din ? ((uint32_t)i0 + trow) * rowo + 16u * dchunk : kOOB;
+    const uint32_t koff = din ? ((uint32_t)j0 + trow) * rowk + 16u * dchunk : kOOB;
+    const uint32_t voff = din ? ((uint32_t)j0 + trow) * rowv + 16u * dchunk : kOOB;
     float lsv = 0.f, dlv = 0.f;
     auto copy_step = [&](int64_t n, PairBuf* __restrict__ dst) {
-        const int64_t slice = ((b * N + n) * p.L * p.H + h) * D;
-        dma16(make_rsrc(p.q + slice, span), &dst->q[64 * wave], qoff, 0);
-        dma16(make_rsrc(p.dout + slice, span), &dst->dout[64 * wave], qoff, 0);
-        dma16(make_rsrc(p.k + slice, span), &dst->k[64 * wave], koff, 0);
-        dma16(make_rsrc(p.v + slice, span), &dst->v[64 * wave], koff, 0);
+        dma16(make_rsrc(p.q + b * st.q[0] + n * st.q[1] + h * st.q[3], last * rowq + D * 2), &dst->q[64 * wave], qoff, 0);
+        dma16(make_rsrc(p.dout + b * st.o[0] + n * st.o[1] + h * st.o[3], last * rowo + D * 2), &dst->dout[64 * wave],
+              dooff, 0);
+        dma16(make_rsrc(p.k + b * st.k[0] + n * st.k[1] + h * st.k[3], last * rowk + D * 2), &dst->k[64 * wave], koff, 0);
+        dma16(make_rsrc(p.v + b * st.v[0] + n * st.v[1] + h * st.v[3], last * rowv + D * 2), &dst->v[64 * wave], voff, 0);
         if (MASK && wave == 0 && lane < 8)
-            dma16(make_rsrc(p.mask + (b * N + n) * p.L, (uint32_t)L * 2u), &dst->mt[0], (uint32_t)j0 * 2u + 16u * lane, 0);
+            dma16(make_rsrc(p.mask + b * st.mb + n * st.mn, (uint32_t)L * 2u), &dst->mt[0], (uint32_t)j0 * 2u + 16u * lane,
+                  0);
         if (wave == 1) {
             const int i = i0 + lane;
-            const int64_t row = ((b * N + n) * p.H + h) * p.L + i;
+            const int64_t row = ((b * N + n) * p.H + h) * st.lrow + i;
             lsv = i < L ? lse_base2(p.lse[row]) : INFINITY;
             dlv = i < L ? p.delta[row] : 0.f;
         }
@@ -856,16 +888,27 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
         }
 }
 
-// dpair[e] = sum over the workspace's chunks of their partial sums, in chunk
-// order; four consecutive elements per thread (B*H*L*L is a multiple of 8).
+// dpair[b,h,i,j] = sum over the workspace's chunks of their partial sums, in
+// chunk order; four consecutive keys per thread (L is a multiple of 8, the
+// pair strides multiples of 8 elements).  The workspace is dense [B][H][L][L].
+struct ReduceParams {
+    const float* ws;
+    u16* dpair;
+    int64_t quads, chunks;  // B*H*L*L / 4; N-chunks
+    int64_t L, H;
+    int64_t pb, ph, pi;     // strides of dpair
+};
+
 template <class E>
-__global__ __launch_bounds__(256) void bwd_dpair_reduce(const float* __restrict__ ws, u16* __restrict__ dpair,
-                                                        int64_t quads, int64_t chunks) {
+__global__ __launch_bounds__(256) void bwd_dpair_reduce(ReduceParams r) {
     const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (q >= quads) return;
+    if (q >= r.quads) return;
     f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int64_t ch = 0; ch < chunks; ++ch) t += reinterpret_cast<const f32x4*>(ws)[ch * quads + q];
-    reinterpret_cast<uint2*>(dpair)[q] = uint2{pack2<E>(t[0], t[1]), pack2<E>(t[2], t[3])};
+    for (int64_t ch = 0; ch < r.chunks; ++ch) t += reinterpret_cast<const f32x4*>(r.ws)[ch * r.quads + q];
+    const int64_t rq = r.L / 4, row = q / rq, j = 4 * (q - row * rq);  // row = (b * H + h) * L + i
+    const int64_t bh = row / r.L, i = row - bh * r.L, b = bh / r.H, h = bh - b * r.H;
+    *reinterpret_cast<uint2*>(r.dpair + b * r.pb + h * r.ph + i * r.pi + j) =
+        uint2{pack2<E>(t[0], t[1]), pack2<E>(t[2], t[3])};
 }
 
 template <class E, int D, bool MASK>
@@ -885,13 +928,17 @@ hipError_t launch_dpair_ws(const Params& base, int64_t B, float* ws, int64_t chu
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dpair_part<E, D, MASK>),
                                    dim3((unsigned)pp.p.total), dim3(kWaves * 64), args, 0, stream);
     if (e != hipSuccess) return e;
-    const int64_t quads = B * base.H * base.L * base.L / 4;
-    const int64_t blocks = (quads + 255) / 256;
+    ReduceParams r;
+    r.ws = ws;
+    r.dpair = base.dpair;
+    r.quads = B * base.H * base.L * base.L / 4;
+    r.chunks = chunks;
+    r.L = base.L;
+    r.H = base.H;
+    r.pb = base.st.pb, r.ph = base.st.ph, r.pi = base.st.pi;
+    const int64_t blocks = (r.quads + 255) / 256;
     if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
-    const float* wsc = ws;
-    u16* out = base.dpair;
-    int64_t ch = chunks;
-    void* rargs[] = {&wsc, &out, (void*)&quads, &ch};
+    void* rargs[] = {&r};
     return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dpair_reduce<E>), dim3((unsigned)blocks), dim3(256),
                            rargs, 0, stream);
 }
@@ -931,6 +978,7 @@ hipError_t launch_dim(const BwdArgs& a, unsigned stages, hipStream_t stream) {
     p.hd = make_fastdiv((uint32_t)a.H);
     p.c1 = (float)(1.4426950408889634 / std::sqrt((double)D));
     p.scale = (float)(1.0 / std::sqrt((double)D));
+    p.st = a.st;
     const bool pair = a.pair != nullptr, mask = a.mask != nullptr;
     hipError_t e = hipSuccess;
     if (stages & kStageDq) {
@@ -977,13 +1025,35 @@ int64_t bwd_dpair_chunks(int64_t B, int64_t N, int64_t L, int64_t H) {
     return c < 2 ? 0 : c;
 }
 
+namespace {
+
+// Rows of one tensor, `row` elements apart with `head` elements between heads,
+// as the matrix-core kernels address them: one buffer per sequence covering
+// every head, 32-bit byte offsets.  The last element ends below 2^31, rows up
+// to 128 past L stay below 2^32, and each row spans every head, so that rows
+// past L fall beyond the buffer and read as zero.
+bool rows_fit32(int64_t L, int64_t H, int64_t D, int64_t row, int64_t head) {
+    constexpr int64_t kMax = int64_t(1) << 31, kLim = int64_t(1) << 40;
+    if (row < 0 || head < 0 || row >= kLim || head >= kLim || L >= kLim || H >= kLim) return false;
+    if (row < (H - 1) * head + D) return false;
+    const int64_t end = ((L - 1) * row + (H - 1) * head + D) * 2, past = ((L + 128) * row + (H - 1) * head) * 2;
+    return end < kMax && past < 2 * kMax;
+}
+
+}  // namespace
+
 bool bwd_mfma_eligible(const BwdArgs& a, int dtype) {
     constexpr int64_t kMax = int64_t(1) << 31;
-    // 32-bit byte offsets: rows of a slice and of a pair matrix end below
-    // 2^31, and rows up to 128 past L stay below 2^32
-    return (dtype == 1 || dtype == 2) && (a.D == 8 || a.D == 16 || a.D == 32) && a.L % 8 == 0 &&
-           a.L * a.H * a.D * 2 < kMax && a.L * a.L * 2 < kMax && (a.L + 128) * a.H * a.D * 2 < 2 * kMax &&
-           (a.L + 128) * a.L * 2 < 2 * kMax && a.N < kMax && a.H < kMax;
+    const Strides& s = a.st;
+    const int64_t L = a.L, H = a.H, D = a.D;
+    if (!(dtype == 1 || dtype == 2) || !(D == 8 || D == 16 || D == 32) || L % 8 != 0 || a.N >= kMax || H >= kMax)
+        return false;
+    for (const int64_t* t : {s.q, s.k, s.v, s.o})
+        if (t[2] % 8 || t[3] % 8 || !rows_fit32(L, H, D, t[2], t[3])) return false;
+    // biases are copied in 16-byte pieces; pair rows at least L apart (the C ABI checks)
+    if (a.pair && (s.pb % 8 || s.ph % 8 || s.pi % 8 || !rows_fit32(L, 1, L, s.pi, 0))) return false;
+    if (a.mask && (s.mb % 8 || s.mn % 8)) return false;
+    return true;
 }
 
 hipError_t launch_bwd_mfma(const BwdArgs& a, int dtype, unsigned stages, hipStream_t stream) {

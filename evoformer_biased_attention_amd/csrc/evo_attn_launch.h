@@ -7,10 +7,12 @@
 
 namespace evo {
 
-// Element strides of the forward pass's tensors.  q, k, v, out: the b, n,
-// l (row) and h axes; the d axis is contiguous.  Biases: keys contiguous.
-// The C ABI checks that every stride except lrow is a multiple of 16 bytes
-// and that every row span fits 2^31 bytes.
+// Element strides of the attention tensors.  q, k, v, out: the b, n, l (row)
+// and h axes; the d axis is contiguous.  Biases: keys contiguous.  The C ABI
+// checks that the q, k, v and out strides are multiples of 16 bytes.  In the
+// backward pass each gradient shares the strides of the tensor it belongs to
+// (dout those of out, dq of q, dk of k, dv of v, dmask of the mask, dpair of
+// the pair bias, delta the lse rows).
 struct Strides {
     int64_t q[4], k[4], v[4], o[4];  // b, n, l, h
     int64_t mb, mn;                  // mask row of (b, n)
@@ -46,17 +48,18 @@ struct BwdArgs {
     const void* mask;   // [B,N,1,1,L] or nullptr
     const void* pair;   // [B,1,H,L,L] or nullptr
     const void* out;    // forward output [B,N,L,H,D]
-    const float* lse;   // forward log-sum-exp [B,N,H,L]
+    const float* lse;   // forward log-sum-exp [B,N,H,L] (rows lrow apart)
     const void* dout;   // incoming gradient [B,N,L,H,D]
     void* dq;
     void* dk;
     void* dv;
     void* dmask;        // [B,N,1,1,L] or nullptr (only with mask)
     void* dpair;        // [B,1,H,L,L] or nullptr (only with pair)
-    float* delta;       // [B,N,H,L], written
+    float* delta;       // [B,N,H,L] (rows lrow apart), written
     float* ws;          // workspace for the pair gradient's partial sums, or nullptr
     int64_t ws_chunks;  // N-chunks the workspace holds ([ws_chunks][B][H][L][L] fp32)
     int64_t B, N, L, H, D;
+    Strides st;         // element strides of every tensor and of its gradient
 };
 
 // Backward pass, dtype 0 = f32, 1 = bf16, 2 = f16, D in {8, 16, 32, 64}.

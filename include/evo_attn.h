@@ -211,7 +211,8 @@ evo_status_t evo_attn_bwd(const void* q, const void* k, const void* v, const voi
 
 /*
  * Bytes of workspace with which evo_attn_bwd runs fastest for this shape and
- * dtype (0: it uses none).  Host-only; returns 0 for an invalid shape.
+ * dtype (0: it uses none), for the dense layout; a strided call uses as much
+ * of it as its layout allows.  Host-only; returns 0 for an invalid shape.
  */
 size_t evo_attn_bwd_workspace_size(const evo_shape_t* shape, evo_dtype_t dtype);
 
@@ -224,6 +225,36 @@ evo_status_t evo_attn_bwd_check(const void* q, const void* k, const void* v, con
                                 const void* dq, const void* dk, const void* dv, const void* dmask_bias,
                                 const void* dpair_bias, const float* delta, const void* workspace,
                                 size_t workspace_bytes, const evo_shape_t* shape, evo_dtype_t dtype);
+
+/*
+ * evo_attn_bwd on strided views (see evo_layout_t): training of ending-node
+ * triangle attention and MSA column attention in place, without transposed
+ * copies (section 5.3 of the guide).  Every gradient has the layout of the
+ * tensor it belongs to: dout and out share layout->out, dq, dk and dv share
+ * layout->q, ->k and ->v, dmask_bias shares the mask strides, dpair_bias the
+ * pair strides, and delta the lse row stride (rows of layout->lse_row floats,
+ * >= L).  Every other rule is that of evo_attn_bwd, plus: q, k, v and out
+ * strides multiples of 16 bytes (EVO_ERR_MISALIGNED); each written gradient's
+ * strides giving distinct elements distinct addresses, and the extents (first
+ * to last element) of outputs, workspace and inputs pairwise disjoint
+ * (EVO_ERR_ALIASING).  Layouts the matrix-core kernels cannot address with
+ * 32-bit offsets (or whose rows do not span every head, or whose bias strides
+ * are not multiples of 16 bytes) run on the vector-ALU kernels: slower, same
+ * results.
+ */
+evo_status_t evo_attn_bwd_strided(const void* q, const void* k, const void* v, const void* mask_bias,
+                                  const void* pair_bias, const void* out, const float* lse, const void* dout,
+                                  void* dq, void* dk, void* dv, void* dmask_bias, void* dpair_bias, float* delta,
+                                  void* workspace, size_t workspace_bytes, const evo_layout_t* layout,
+                                  const evo_shape_t* shape, evo_dtype_t dtype, void* stream);
+
+/* The validation of evo_attn_bwd_strided alone; host-only. */
+evo_status_t evo_attn_bwd_check_strided(const void* q, const void* k, const void* v, const void* mask_bias,
+                                        const void* pair_bias, const void* out, const float* lse, const void* dout,
+                                        const void* dq, const void* dk, const void* dv, const void* dmask_bias,
+                                        const void* dpair_bias, const float* delta, const void* workspace,
+                                        size_t workspace_bytes, const evo_layout_t* layout,
+                                        const evo_shape_t* shape, evo_dtype_t dtype);
 
 /*
  * Triangle multiplication: the cubic contraction of the triangle

@@ -338,6 +338,79 @@ def test_dense_entry_matches_strided_with_dense_layout():
 
 
 # ---------------------------------------------------------------------------
+# evo_attn_bwd_check_strided: each gradient has the layout of its tensor
+# ---------------------------------------------------------------------------
+def bscheck(layout, shape=(1, 8, 64, 4, 32), dtype=E.EVO_DTYPE_BF16, workspace_bytes=1 << 20, **over):
+    args = dict(zip(BWD_NAMES, addrs(len(BWD_NAMES))))
+    args.update(over)
+    return E.evo_attn_bwd_check_strided(*[args[n] for n in BWD_NAMES[:-1]], layout, shape, dtype,
+                                        workspace=args["workspace"], workspace_bytes=workspace_bytes)
+
+
+def test_bwd_strided_valid():
+    shape = (1, 8, 64, 4, 32)
+    for dt in (E.EVO_DTYPE_F32, E.EVO_DTYPE_BF16, E.EVO_DTYPE_F16):
+        assert bscheck(E.evo_attn_dense_layout(shape), dtype=dt) == E.EVO_OK
+        assert bscheck(transposed_layout(*shape), dtype=dt) == E.EVO_OK
+    lay = E.evo_attn_dense_layout(shape)
+    lay.lse_row, lay.pair_i = 96, 72                # padded lse / delta rows and pair rows
+    assert bscheck(lay) == E.EVO_ERR_ALIASING       # the padded rows run into the next head's matrix
+    lay.pair_h, lay.pair_b = 64 * 72, 4 * 64 * 72
+    assert bscheck(lay) == E.EVO_OK
+
+
+def test_bwd_strided_rules():
+    shape = (1, 8, 64, 4, 32)
+    lay = E.evo_attn_dense_layout(shape)
+    lay.lse_row = 63
+    assert bscheck(lay) == E.EVO_ERR_BAD_SHAPE      # lse and delta are required: their rows must not overlap
+    lay = E.evo_attn_dense_layout(shape)
+    lay.pair_i = 60
+    assert bscheck(lay) == E.EVO_ERR_BAD_SHAPE
+    lay = E.evo_attn_dense_layout(shape)
+    lay.v[:] = [8 * 64 * 200, 64 * 200, 200, 36]    # heads 72 bytes apart
+    assert bscheck(lay) == E.EVO_ERR_MISALIGNED
+    lay = E.evo_attn_dense_layout(shape)
+    lay.mask_b = -1
+    assert bscheck(lay) == E.EVO_ERR_BAD_SHAPE
+    # a repeated input is fine for the forward, but its gradient would collide
+    lay = E.evo_attn_dense_layout(shape)
+    lay.q[1] = 0
+    assert scheck(lay) == E.EVO_OK and bscheck(lay) == E.EVO_ERR_ALIASING
+    lay = E.evo_attn_dense_layout(shape)
+    lay.mask_n = 0                                  # one mask row for every n
+    assert bscheck(lay) == E.EVO_ERR_ALIASING
+    assert bscheck(lay, dmask_bias=None) == E.EVO_OK
+    lay = E.evo_attn_dense_layout(shape)
+    lay.pair_h = 0                                  # one pair matrix for every head
+    assert bscheck(lay) == E.EVO_ERR_ALIASING
+    assert bscheck(lay, dpair_bias=None) == E.EVO_OK
+    lay = E.evo_attn_dense_layout(shape)
+    lay.out[3] = 16                                 # dout shares out's strides: heads collide
+    assert bscheck(lay) == E.EVO_OK                 # out and dout are read, never written
+
+
+def test_bwd_strided_aliasing_uses_the_strided_extent():
+    shape = (1, 8, 64, 4, 32)
+    lay = transposed_layout(*shape)
+    a = dict(zip(BWD_NAMES, addrs(len(BWD_NAMES))))
+    assert bscheck(lay, dq=a["q"] + 4096) == E.EVO_ERR_ALIASING
+    assert bscheck(lay, dk=a["dq"] + 8192) == E.EVO_ERR_ALIASING
+    lay.lse_row = 96
+    lse_bytes = ((1 * 8 * 4 - 1) * 96 + 64) * 4     # first to last element of the padded lse rows
+    assert bscheck(lay, delta=a["lse"] + lse_bytes - 16) == E.EVO_ERR_ALIASING
+    assert bscheck(lay, delta=a["lse"] + lse_bytes) == E.EVO_OK
+
+
+def test_bwd_dense_entry_matches_strided_with_dense_layout():
+    for shape in ((1, 2, 64, 4, 32), (2, 3, 17, 2, 16), (1, 1, 1, 1, 8), (1, 2, 64, 2, 64)):
+        for dt in (E.EVO_DTYPE_BF16, E.EVO_DTYPE_F16, E.EVO_DTYPE_F32):
+            assert bcheck(shape=shape, dtype=dt) == bscheck(E.evo_attn_dense_layout(shape), shape=shape, dtype=dt)
+            assert bcheck(shape=shape, dtype=dt, dq=None) == bscheck(E.evo_attn_dense_layout(shape), shape=shape,
+                                                                     dtype=dt, dq=None)
+
+
+# ---------------------------------------------------------------------------
 # evo_trimul_check
 # ---------------------------------------------------------------------------
 def tcheck(shape=(1, 4, 64), direction=E.EVO_TRIMUL_OUTGOING, dtype=E.EVO_DTYPE_BF16, **over):
