@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import synthetic as S
-from test_gpu_parity import THREADS, compare, say, to_dev
+from test_gpu_parity import THREADS, compare, parity_sampled, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -126,3 +126,29 @@ def test_dense_layout_through_strided_entry_is_identical(torch_dev, dtype):
     assert st == E.EVO_OK
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_transposed_layout_at_workload_size(torch_dev):
+    """Workload 5 (ending node, N = L = 768, bf16) with Q/K/V/O stored as X[B, L, N, H, D]: the launch that
+    `bench.py --workload 5 --layout transposed` times, checked on 4096 sampled rows."""
+    torch = torch_dev
+    w = S.workload(5)
+    B, N, L, H, D = w.shape
+    X = {n: np.ascontiguousarray(getattr(w, n).transpose(0, 2, 1, 3, 4)) for n in ("q", "k", "v")}
+    view = lambda t: t.permute(0, 2, 1, 3, 4)
+    xq, xk, xv = (to_dev(torch, X[n], "bf16") for n in ("q", "k", "v"))
+    xo = torch.full_like(xq, float("nan"))
+    o, l, _ = gpu_strided(torch, view(xq), view(xk), view(xv), None, to_dev(torch, w.pair, "bf16"), view(xo))
+    idx = S.sample_rows(w.shape, 4096, seed=11)
+    ro, rl = oracle.rows(w.q, w.k, w.v, w.mask, w.pair, dtype="bf16", idx=idx, nthreads=THREADS)
+    b, n, h, i = idx.T
+    compare(o[b, n, i, h, :], l[b, n, h, i], ro, rl, "bf16", "workload 5, transposed layout (sampled rows)")
+    assert np.isfinite(o).all() and np.isfinite(l).all()
+
+
+def test_ds4sci_benchmark_shape_batch16_f16(torch_dev):
+    """The largest batch of the DS4Sci benchmark sweep (16 x 256 x 256, H = 4, D = 32, fp16, mask and pair
+    bias), in the dense launch `bench.py --sweep ds4sci` times, on 4096 sampled rows."""
+    w = S.random_problem(16, 256, 256, 4, 32, dtype="f16", seed=4781, mask="tail", pair="normal")
+    say("ds4sci benchmark shape, batch 16, f16")
+    parity_sampled(torch_dev, w)
