@@ -157,14 +157,16 @@ __device__ inline float lse_base2(float lse) { return lse == -INFINITY ? INFINIT
 
 // ---------------------------------------------------------------------------
 // dq (and delta).  Workgroup = 128 queries of one (b, n, h); wave w owns
-// queries 32w .. 32w+31 as two 16-query tiles.  LDS per 64-key block:
-//   k, v: slot 4*key + (chunk ^ ((key >> 2) & 3)), chunk = 8 d-values
+// queries 32w .. 32w+31 as two 16-query tiles.  LDS per 64-key block, d-rows
+// in 32-wide halves hh (two for D = 64):
+//   k, v: half hh, slot 4*key + (chunk ^ ((key >> 2) & 3)), chunk = 8 d-values
 //   pt:   slot 8*row + (chunk ^ (row & 7)), row = query of the workgroup, chunk = 8 keys
 //   mt:   slot chunk (8 keys)
 // ---------------------------------------------------------------------------
+template <int DH>
 struct DqBuf {
-    uint4 k[kKB * 4];
-    uint4 v[kKB * 4];
+    uint4 k[DH][kKB * 4];
+    uint4 v[DH][kKB * 4];
     uint4 pt[kBlockRows * 8];
     uint4 mt[8];
 };
@@ -173,8 +175,10 @@ template <class E, int D, bool PAIR, bool MASK>
 __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
     using V8 = typename E::v8;
     constexpr int kDC = D / 8;           // 16-byte chunks per row
+    constexpr int kDH = (D + 31) / 32;   // 32-wide halves of a row
     constexpr int kDHT = (D + 15) / 16;  // 16-wide d tiles
-    __shared__ __attribute__((aligned(16))) DqBuf sm[2];
+    using Buf = DqBuf<kDH>;
+    __shared__ __attribute__((aligned(16))) Buf sm[2];
 
     const uint32_t id = (uint32_t)logical_block(blockIdx.x, p.total);
     const uint32_t r1 = fdiv(id, p.rblocks), r2 = fdiv(r1, p.hd), r3 = fdiv(r2, p.nd);
@@ -206,22 +210,26 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
 
     const int q0 = (int)qb * kBlockRows + wave * kWaveRows;
     // B operands of S^T = K.Q^T and dP^T = V.dO^T: lane (c + 16g) holds row
-    // (query c of the tile), d-values 8g .. 8g+7; rows past L and chunks past D read as zero
-    V8 qop[2], dop[2];
+    // (query c of the tile), d-values 32hh + 8g .. +7 of half hh; rows past L
+    // and chunks past D read as zero
+    V8 qop[2][kDH], dop[2][kDH];
     float delta[2], lse2[2];
     for (int t = 0; t < 2; ++t) {
         const int i = q0 + 16 * t + c;
-        const uint32_t offq = g < kDC ? (uint32_t)i * rowq + 16u * g : kOOB;
-        const uint32_t offo = g < kDC ? (uint32_t)i * rowo + 16u * g : kOOB;
-        const uint4 qq = bload16(rq, offq, 0), dd = bload16(rdo, offo, 0), oo = bload16(ro, offo, 0);
-        qop[t] = as_v8<E>(qq);
-        dop[t] = as_v8<E>(dd);
-        const uint32_t dw[4] = {dd.x, dd.y, dd.z, dd.w}, ow[4] = {oo.x, oo.y, oo.z, oo.w};
         float part = 0.f;
-        for (int e = 0; e < 4; ++e) {
-            const f32x2 a = unpack2<E>(dw[e]), o = unpack2<E>(ow[e]);
-            part = fmaf(a[0], o[0], part);
-            part = fmaf(a[1], o[1], part);
+        for (int hh = 0; hh < kDH; ++hh) {
+            const bool in = 4 * hh + g < kDC;
+            const uint32_t offq = in ? (uint32_t)i * rowq + 64u * hh + 16u * g : kOOB;
+            const uint32_t offo = in ? (uint32_t)i * rowo + 64u * hh + 16u * g : kOOB;
+            const uint4 qq = bload16(rq, offq, 0), dd = bload16(rdo, offo, 0), oo = bload16(ro, offo, 0);
+            qop[t][hh] = as_v8<E>(qq);
+            dop[t][hh] = as_v8<E>(dd);
+            const uint32_t dw[4] = {dd.x, dd.y, dd.z, dd.w}, ow[4] = {oo.x, oo.y, oo.z, oo.w};
+            for (int e = 0; e < 4; ++e) {
+                const f32x2 a = unpack2<E>(dw[e]), o = unpack2<E>(ow[e]);
+                part = fmaf(a[0], o[0], part);
+                part = fmaf(a[1], o[1], part);
+            }
         }
         delta[t] = sum_over_groups(part);
         lse2[t] = i < L ? lse_base2(p.lse[rowbase + i]) : INFINITY;
@@ -232,46 +240,54 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
     const uint32_t qwg = (uint32_t)(qb * kBlockRows);
     const uint32_t kvchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
     const uint32_t kvrow = (uint32_t)(16 * wave + (lane >> 2));
-    const uint32_t ko = kvchunk < kDC ? kvrow * rowk + 16u * kvchunk : kOOB;
-    const uint32_t vo = kvchunk < kDC ? kvrow * rowv + 16u * kvchunk : kOOB;
+    uint32_t ko[kDH], vo[kDH];
+    for (int hh = 0; hh < kDH; ++hh) {
+        const bool in = 4 * hh + (int)kvchunk < kDC;
+        ko[hh] = in ? kvrow * rowk + 64u * hh + 16u * kvchunk : kOOB;
+        vo[hh] = in ? kvrow * rowv + 64u * hh + 16u * kvchunk : kOOB;
+    }
     uint32_t pvo[4];
     for (int j = 0; j < 4; ++j) {
         // rows past L start beyond the pair range (its row stride is at least L)
         const uint32_t row = 8u * (4 * wave + j) + (lane >> 3);
         pvo[j] = (qwg + row) * rowp + 16u * ((lane & 7) ^ (lane >> 3));
     }
-    auto copy_block = [&](int blk, DqBuf* __restrict__ dst) {
+    auto copy_block = [&](int blk, Buf* __restrict__ dst) {
         const uint32_t k0 = (uint32_t)blk * kKB;
-        dma16(rk, &dst->k[64 * wave], ko + k0 * rowk, 0);
-        dma16(rv, &dst->v[64 * wave], vo + k0 * rowv, 0);
+        for (int hh = 0; hh < kDH; ++hh) {
+            dma16(rk, &dst->k[hh][64 * wave], ko[hh] + k0 * rowk, 0);
+            dma16(rv, &dst->v[hh][64 * wave], vo[hh] + k0 * rowv, 0);
+        }
         if (PAIR)
             for (int j = 0; j < 4; ++j) dma16(rp, &dst->pt[64 * (4 * wave + j)], pvo[j] + k0 * 2u, 0);
         if (MASK && wave == 0 && lane < 8) dma16(rm, &dst->mt[0], 16u * lane + k0 * 2u, 0);
     };
 
-    f32x4 dqacc[2][2];
-    for (int t = 0; t < 2; ++t) dqacc[t][0] = dqacc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 dqacc[2][kDHT];
+    for (int t = 0; t < 2; ++t)
+        for (int dh = 0; dh < kDHT; ++dh) dqacc[t][dh] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     copy_block(0, &sm[0]);
     wait_all();
     __syncthreads();
 
-    auto step = [&](int it, const DqBuf* __restrict__ cur, DqBuf* __restrict__ nxt, auto tail_tag) {
+    auto step = [&](int it, const Buf* __restrict__ cur, Buf* __restrict__ nxt, auto tail_tag) {
         constexpr bool TAIL = decltype(tail_tag)::value;
         const int k0 = it * kKB;
         // A operands: K and V rows (key 16kt + c, chunk g) and transposed K
         // for dQ^T = K^T.dS^T (column 16dh + c over keys 32cc + 4g + 0..3 and
         // 32cc + 16 + 4g + 0..3)
-        V8 kop[kKT], vop[kKT], ktr[2][2];
-        for (int kt = 0; kt < kKT; ++kt) {
-            kop[kt] = as_v8<E>(cur->k[64 * kt + 4 * c + (g ^ ((c >> 2) & 3))]);
-            vop[kt] = as_v8<E>(cur->v[64 * kt + 4 * c + (g ^ ((c >> 2) & 3))]);
-        }
+        V8 kop[kKT][kDH], vop[kKT][kDH], ktr[2][kDHT];
+        for (int kt = 0; kt < kKT; ++kt)
+            for (int hh = 0; hh < kDH; ++hh) {
+                kop[kt][hh] = as_v8<E>(cur->k[hh][64 * kt + 4 * c + (g ^ ((c >> 2) & 3))]);
+                vop[kt][hh] = as_v8<E>(cur->v[hh][64 * kt + 4 * c + (g ^ ((c >> 2) & 3))]);
+            }
         for (int cc = 0; cc < 2; ++cc)
             for (int dh = 0; dh < kDHT; ++dh) {
                 const int key = 32 * cc + 4 * g + (c >> 2);
-                const int chunk = (2 * dh + ((c & 3) >> 1)) ^ g;
-                const char* base = reinterpret_cast<const char*>(&cur->k[4 * key + chunk]) + 8 * (c & 1);
+                const int chunk = (2 * (dh & 1) + ((c & 3) >> 1)) ^ g;
+                const char* base = reinterpret_cast<const char*>(&cur->k[dh >> 1][4 * key + chunk]) + 8 * (c & 1);
                 const uint2 lo = ds_read_tr(base);
                 const uint2 hi = ds_read_tr(base + 16 * 4 * 16);
                 ktr[cc][dh] = as_v8<E>(uint4{lo.x, lo.y, hi.x, hi.y});
@@ -294,8 +310,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
         f32x4 s[2][kKT], dp[2][kKT];
         for (int kt = 0; kt < kKT; ++kt)
             for (int t = 0; t < 2; ++t) {
-                s[t][kt] = E::mfma(kop[kt], qop[t], f32x4{0.f, 0.f, 0.f, 0.f});
-                dp[t][kt] = E::mfma(vop[kt], dop[t], f32x4{0.f, 0.f, 0.f, 0.f});
+                s[t][kt] = dp[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int hh = 0; hh < kDH; ++hh) {
+                    s[t][kt] = E::mfma(kop[kt][hh], qop[t][hh], s[t][kt]);
+                    dp[t][kt] = E::mfma(vop[kt][hh], dop[t][hh], dp[t][kt]);
+                }
             }
         V8 dsop[2][2];
         for (int t = 0; t < 2; ++t) {
@@ -351,31 +370,49 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
 }
 
 // ---------------------------------------------------------------------------
-// dk, dv and dmask.  Workgroup = 128 keys of one (b, n); wave w owns keys
-// 32w .. 32w+31 as two 16-key tiles and keeps their K and V rows (B
-// operands of S = Q.K^T and dP = dO.V^T) in registers.  The workgroup walks
-// every (head, 64-query block) pair in order; LDS per step:
-//   q, dO: slot 4*row + (chunk ^ ((row >> 2) & 3)), row = query of the block, chunk = 8 d-values
-//   pt:    slot 16*row + (chunk ^ 2(row & 7)), row = query of the block, chunk = 8 of the 128 keys
+// dk, dv and dmask.  Workgroup = 64 KT keys of one (b, n); wave w owns keys
+// 16 KT w .. as KT 16-key tiles and keeps their K and V rows (B operands of
+// S = Q.K^T and dP = dO.V^T) in registers.  The workgroup walks every (head,
+// QS-query block) pair in order.  KT = 2, QS = 64 for head dimensions up to
+// 32; KT = 1, QS = 32 for D = 64 (two 32-wide halves of every row), which
+// keeps the operands of one step within the registers of two waves per SIMD.
+// LDS per step, d-rows in 32-wide halves hh:
+//   q, dO: half hh, slot 4*row + (chunk ^ ((row >> 2) & 3)), row = query of the block, chunk = 8 d-values
+//   pt:    slot (8 KT)*row + (chunk ^ 2(row & (4 KT - 1))), chunk = 8 of the workgroup's keys
 //   ls:    lse * log2(e) of the block's queries (+inf past L or for a row without softmax)
 //   dl:    delta of the block's queries
 // Queries past L read as zero rows with ls = +inf, so they add nothing; keys
 // past L are computed on zero rows and never stored.
 // ---------------------------------------------------------------------------
+template <int QS, int DH, int KT>
 struct KvBuf {
-    uint4 q[kKB * 4];
-    uint4 dout[kKB * 4];
-    uint4 pt[kKB * 16];
-    float ls[kKB];
-    float dl[kKB];
+    uint4 q[DH][QS * 4];
+    uint4 dout[DH][QS * 4];
+    uint4 pt[QS * 8 * KT];
+    float ls[QS];
+    float dl[QS];
+};
+
+template <int D>
+struct DkdvShape {
+    static constexpr int KT = D > 32 ? 1 : 2;   // 16-key tiles per wave
+    static constexpr int QS = D > 32 ? 32 : 64;  // queries per step
+    static constexpr int BK = kWaves * 16 * KT;  // keys per workgroup
 };
 
 template <class E, int D, bool PAIR, bool MASK>
 __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
     using V8 = typename E::v8;
     constexpr int kDC = D / 8;
-    constexpr int kDHT = (D + 15) / 16;
-    __shared__ __attribute__((aligned(16))) KvBuf sm[2];
+    constexpr int kDH = (D + 31) / 32;        // 32-wide halves of a row
+    constexpr int kDHT = (D + 15) / 16;       // 16-wide d tiles
+    constexpr int KT = DkdvShape<D>::KT, QS = DkdvShape<D>::QS, BK = DkdvShape<D>::BK;
+    constexpr int QT = QS / 16, CC = QS / 32; // 16-query tiles and 32-query chunks of a step
+    constexpr int CPR = 8 * KT;               // 16-byte pair chunks per row of the tile
+    constexpr int RPI = 64 / CPR;             // pair rows per wave-wide copy
+    constexpr int PCW = QS / RPI / kWaves;    // pair copies per wave and step
+    constexpr int RG = QS / 16;               // 16-row groups of a half (q and dO copies)
+    __shared__ __attribute__((aligned(16))) KvBuf<QS, kDH, KT> sm[2];
 
     const uint32_t id = (uint32_t)logical_block(blockIdx.x, p.total);
     const uint32_t r1 = fdiv(id, p.rblocks), r2 = fdiv(r1, p.nd);
@@ -387,7 +424,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
-    const int nqb = (L + kKB - 1) / kKB;  // query blocks per head
+    const int nqb = (L + QS - 1) / QS;  // query blocks per head
     const int nsteps = H * nqb;
     // element offsets of (b, n, 0, 0, 0) in q, k, v and out / dout; bytes
     // between rows and between heads.  A buffer covers every head of the
@@ -403,54 +440,61 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
     const Rsrc rk = make_rsrc(p.k + kbn, last * rowk + lasth * hk + D * 2);
     const Rsrc rv = make_rsrc(p.v + vbn, last * rowv + lasth * hv + D * 2);
     const Rsrc rdo = make_rsrc(p.dout + obn, last * rowo + lasth * ho + D * 2);
-    const int kw0 = (int)kb * kBlockRows + wave * kWaveRows;  // first key of the wave
-    const int64_t mrow = b * st.mb + n * st.mn;                // mask row of (b, n)
+    const int kw0 = (int)kb * BK + wave * 16 * KT;  // first key of the wave
+    const int64_t mrow = b * st.mb + n * st.mn;     // mask row of (b, n)
 
     // per-key mask term (base 2), constant over heads and queries
-    float mk[2] = {0.f, 0.f};
-    if (MASK)
-        for (int t = 0; t < 2; ++t) {
-            const int j = kw0 + 16 * t + c;
-            mk[t] = j < L ? E::widen(p.mask[mrow + j]) * kLog2e : 0.f;
-        }
+    float mk[KT];
+    for (int t = 0; t < KT; ++t) {
+        const int j = kw0 + 16 * t + c;
+        mk[t] = MASK && j < L ? E::widen(p.mask[mrow + j]) * kLog2e : 0.f;
+    }
 
-    // copies of step `it` (head it / nqb, queries 64 (it % nqb) ..)
+    // copies of step `it` (head it / nqb, queries QS (it % nqb) ..).  q and
+    // dO: wave w fills 16-row group w % RG of half w / RG; lane l holds row
+    // 16 (w % RG) + l/4 at slot position l%4, chunk (l%4) ^ ((row >> 2) & 3).
+    const int qhh = wave / RG, qrg = wave % RG;
     const uint32_t qdchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
-    const uint32_t qdrow = (uint32_t)(16 * wave + (lane >> 2));
-    const uint32_t qoff = qdchunk < kDC ? qdrow * rowq + 16u * qdchunk : kOOB;
-    const uint32_t dooff = qdchunk < kDC ? qdrow * rowo + 16u * qdchunk : kOOB;
-    uint32_t pvo[4];
-    for (int j = 0; j < 4; ++j) {
+    const uint32_t qdrow = (uint32_t)(16 * qrg + (lane >> 2));
+    const bool qdin = 4 * qhh + (int)qdchunk < kDC;
+    const uint32_t qoff = qdin ? qdrow * rowq + 64u * qhh + 16u * qdchunk : kOOB;
+    const uint32_t dooff = qdin ? qdrow * rowo + 64u * qhh + 16u * qdchunk : kOOB;
+    // pair tile: rows of CPR chunks; wave w fills copies PCW w .. PCW w + PCW - 1,
+    // RPI rows each; lane l holds row RPI I + l / CPR at position l % CPR
+    uint32_t pvo[PCW];
+    for (int j = 0; j < PCW; ++j) {
         // rows past L start beyond the pair range (its row stride is at least L)
-        const uint32_t row = (uint32_t)(16 * wave + 4 * j + (lane >> 4));
-        pvo[j] = row * rowp + (uint32_t)kb * kBlockRows * 2u + 16u * ((lane & 15) ^ (2 * (row & 7)));
+        const uint32_t row = (uint32_t)(RPI * (PCW * wave + j) + lane / CPR);
+        pvo[j] = row * rowp + (uint32_t)kb * BK * 2u + 16u * ((lane % CPR) ^ (2 * (row & (CPR / 2 - 1))));
     }
     float lsv = 0.f, dlv = 0.f;  // wave 0: this lane's query of the step being copied
-    auto copy_block = [&](int it, KvBuf* __restrict__ dst) {
-        const int h = it / nqb, q0 = (it - h * nqb) * kKB;
-        dma16(rq, &dst->q[64 * wave], qoff + (uint32_t)q0 * rowq + (uint32_t)h * hq, 0);
-        dma16(rdo, &dst->dout[64 * wave], dooff + (uint32_t)q0 * rowo + (uint32_t)h * ho, 0);
+    auto copy_block = [&](int it, KvBuf<QS, kDH, KT>* __restrict__ dst) {
+        const int h = it / nqb, q0 = (it - h * nqb) * QS;
+        dma16(rq, &dst->q[qhh][64 * qrg], qoff + (uint32_t)q0 * rowq + (uint32_t)h * hq, 0);
+        dma16(rdo, &dst->dout[qhh][64 * qrg], dooff + (uint32_t)q0 * rowo + (uint32_t)h * ho, 0);
         if (PAIR) {
             const Rsrc rp = make_rsrc(p.pair + b * st.pb + h * st.ph, last * rowp + (uint32_t)L * 2u);
-            for (int j = 0; j < 4; ++j) dma16(rp, &dst->pt[64 * (4 * wave + j)], pvo[j] + (uint32_t)q0 * rowp, 0);
+            for (int j = 0; j < PCW; ++j)
+                dma16(rp, &dst->pt[64 * (PCW * wave + j)], pvo[j] + (uint32_t)q0 * rowp, 0);
         }
-        if (wave == 0) {
+        if (wave == 0 && lane < QS) {
             const int i = q0 + lane;
             const int64_t row = (bn * p.H + h) * st.lrow + i;
             lsv = i < L ? lse_base2(p.lse[row]) : INFINITY;
             dlv = i < L ? p.delta[row] : 0.f;
         }
     };
-    auto put_rows = [&](KvBuf* __restrict__ dst) {
-        if (wave == 0) {
+    auto put_rows = [&](KvBuf<QS, kDH, KT>* __restrict__ dst) {
+        if (wave == 0 && lane < QS) {
             dst->ls[lane] = lsv;
             dst->dl[lane] = dlv;
         }
     };
 
-    V8 kop[2], vop[2];
-    f32x4 dkacc[2][2], dvacc[2][2];
-    float dm[2] = {0.f, 0.f};
+    V8 kop[KT][kDH], vop[KT][kDH];
+    f32x4 dkacc[KT][kDHT], dvacc[KT][kDHT];
+    float dm[KT];
+    for (int t = 0; t < KT; ++t) dm[t] = 0.f;
 
     copy_block(0, &sm[0]);
     put_rows(&sm[0]);
@@ -458,66 +502,74 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
     __syncthreads();
 
     for (int it = 0; it < nsteps; ++it) {
-        const KvBuf* __restrict__ cur = &sm[it & 1];
-        KvBuf* __restrict__ nxt = &sm[(it & 1) ^ 1];
+        const KvBuf<QS, kDH, KT>* __restrict__ cur = &sm[it & 1];
+        KvBuf<QS, kDH, KT>* __restrict__ nxt = &sm[(it & 1) ^ 1];
         const int h = it / nqb, qbk = it - h * nqb;
         if (qbk == 0) {
-            for (int t = 0; t < 2; ++t) {
+            for (int t = 0; t < KT; ++t) {
                 const uint32_t j = (uint32_t)(kw0 + 16 * t + c);
-                kop[t] = as_v8<E>(bload16(rk, g < kDC ? j * rowk + (uint32_t)h * hk + 16u * g : kOOB, 0));
-                vop[t] = as_v8<E>(bload16(rv, g < kDC ? j * rowv + (uint32_t)h * hv + 16u * g : kOOB, 0));
-                for (int dh = 0; dh < 2; ++dh) dkacc[t][dh] = dvacc[t][dh] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int hh = 0; hh < kDH; ++hh) {
+                    const bool in = 4 * hh + g < kDC;
+                    kop[t][hh] = as_v8<E>(bload16(rk, in ? j * rowk + (uint32_t)h * hk + 64u * hh + 16u * g : kOOB, 0));
+                    vop[t][hh] = as_v8<E>(bload16(rv, in ? j * rowv + (uint32_t)h * hv + 64u * hh + 16u * g : kOOB, 0));
+                }
+                for (int dh = 0; dh < kDHT; ++dh) dkacc[t][dh] = dvacc[t][dh] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
-        // A operands: Q and dO rows (query 16qt + c, chunk g); transposed Q and dO
-        // for the products over queries (column 16dh + c over queries 32cc + 4g
-        // + 0..3 and 32cc + 16 + 4g + 0..3)
-        V8 aq[kKT], ado[kKT], qtr[2][2], dotr[2][2];
-        for (int qt = 0; qt < kKT; ++qt) {
-            aq[qt] = as_v8<E>(cur->q[64 * qt + 4 * c + (g ^ ((c >> 2) & 3))]);
-            ado[qt] = as_v8<E>(cur->dout[64 * qt + 4 * c + (g ^ ((c >> 2) & 3))]);
-        }
-        for (int cc = 0; cc < 2; ++cc)
+        // A operands: Q and dO rows (query 16qt + c, chunk g of each half);
+        // transposed Q and dO for the products over queries (column 16dh + c
+        // over queries 32cc + 4g + 0..3 and 32cc + 16 + 4g + 0..3)
+        V8 aq[QT][kDH], ado[QT][kDH], qtr[CC][kDHT], dotr[CC][kDHT];
+        for (int qt = 0; qt < QT; ++qt)
+            for (int hh = 0; hh < kDH; ++hh) {
+                aq[qt][hh] = as_v8<E>(cur->q[hh][64 * qt + 4 * c + (g ^ ((c >> 2) & 3))]);
+                ado[qt][hh] = as_v8<E>(cur->dout[hh][64 * qt + 4 * c + (g ^ ((c >> 2) & 3))]);
+            }
+        for (int cc = 0; cc < CC; ++cc)
             for (int dh = 0; dh < kDHT; ++dh) {
                 const int row = 32 * cc + 4 * g + (c >> 2);
-                const int chunk = (2 * dh + ((c & 3) >> 1)) ^ g;
+                const int chunk = (2 * (dh & 1) + ((c & 3) >> 1)) ^ g;
                 const int off = 16 * (4 * row + chunk) + 8 * (c & 1);
-                const char* bq = reinterpret_cast<const char*>(cur->q) + off;
-                const char* bd = reinterpret_cast<const char*>(cur->dout) + off;
+                const char* bq = reinterpret_cast<const char*>(cur->q[dh >> 1]) + off;
+                const char* bd = reinterpret_cast<const char*>(cur->dout[dh >> 1]) + off;
                 const uint2 ql = ds_read_tr(bq), qh = ds_read_tr(bq + 16 * 4 * 16);
                 const uint2 dl = ds_read_tr(bd), dhh = ds_read_tr(bd + 16 * 4 * 16);
                 qtr[cc][dh] = as_v8<E>(uint4{ql.x, ql.y, qh.x, qh.y});
                 dotr[cc][dh] = as_v8<E>(uint4{dl.x, dl.y, dhh.x, dhh.y});
             }
         // pair bias of lane (c + 16g): queries 16qt + 4g + 0..3, key 16t + c of the wave
-        uint2 pb[kKT][2];
+        uint2 pb[QT][KT];
         if (PAIR)
-            for (int qt = 0; qt < kKT; ++qt)
-                for (int t = 0; t < 2; ++t) {
+            for (int qt = 0; qt < QT; ++qt)
+                for (int t = 0; t < KT; ++t) {
                     const int row = 16 * qt + 4 * g + (c >> 2);
-                    const int chunk = 4 * wave + 2 * t + ((c & 3) >> 1);
-                    pb[qt][t] = ds_read_tr(reinterpret_cast<const char*>(&cur->pt[16 * row + (chunk ^ (2 * (row & 7)))]) +
-                                           8 * (c & 1));
+                    const int chunk = 2 * KT * wave + 2 * t + ((c & 3) >> 1);
+                    pb[qt][t] = ds_read_tr(
+                        reinterpret_cast<const char*>(&cur->pt[CPR * row + (chunk ^ (2 * (row & (CPR / 2 - 1))))]) +
+                        8 * (c & 1));
                 }
-        float4 lsq[kKT], dlq[kKT];
-        for (int qt = 0; qt < kKT; ++qt) {
+        float4 lsq[QT], dlq[QT];
+        for (int qt = 0; qt < QT; ++qt) {
             lsq[qt] = *reinterpret_cast<const float4*>(&cur->ls[16 * qt + 4 * g]);
             dlq[qt] = *reinterpret_cast<const float4*>(&cur->dl[16 * qt + 4 * g]);
         }
 
         if (it + 1 < nsteps) copy_block(it + 1, nxt);
 
-        f32x4 sc[kKT][2], dp[kKT][2];
-        for (int qt = 0; qt < kKT; ++qt)
-            for (int t = 0; t < 2; ++t) {
-                sc[qt][t] = E::mfma(aq[qt], kop[t], f32x4{0.f, 0.f, 0.f, 0.f});
-                dp[qt][t] = E::mfma(ado[qt], vop[t], f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 sc[QT][KT], dp[QT][KT];
+        for (int qt = 0; qt < QT; ++qt)
+            for (int t = 0; t < KT; ++t) {
+                sc[qt][t] = dp[qt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int hh = 0; hh < kDH; ++hh) {
+                    sc[qt][t] = E::mfma(aq[qt][hh], kop[t][hh], sc[qt][t]);
+                    dp[qt][t] = E::mfma(ado[qt][hh], vop[t][hh], dp[qt][t]);
+                }
             }
         // lane (c + 16g) holds S[query 16qt + 4g + r][key 16t + c]
-        V8 pm[2][2], dsm[2][2];
-        for (int t = 0; t < 2; ++t) {
-            uint32_t wp[8], wd[8];
-            for (int qt = 0; qt < kKT; ++qt) {
+        V8 pm[KT][CC], dsm[KT][CC];
+        for (int t = 0; t < KT; ++t) {
+            uint32_t wp[2 * QT], wd[2 * QT];
+            for (int qt = 0; qt < QT; ++qt) {
                 const float lsr[4] = {lsq[qt].x, lsq[qt].y, lsq[qt].z, lsq[qt].w};
                 const float dlr[4] = {dlq[qt].x, dlq[qt].y, dlq[qt].z, dlq[qt].w};
                 float bias[4] = {0.f, 0.f, 0.f, 0.f};
@@ -538,14 +590,14 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
                 wd[2 * qt + 1] = pack2<E>(ds[2], ds[3]);
             }
             // element e of 32-query chunk cc is query 32cc + 16(e/4) + 4g + e%4
-            pm[t][0] = as_v8<E>(uint4{wp[0], wp[1], wp[2], wp[3]});
-            pm[t][1] = as_v8<E>(uint4{wp[4], wp[5], wp[6], wp[7]});
-            dsm[t][0] = as_v8<E>(uint4{wd[0], wd[1], wd[2], wd[3]});
-            dsm[t][1] = as_v8<E>(uint4{wd[4], wd[5], wd[6], wd[7]});
+            for (int cc = 0; cc < CC; ++cc) {
+                pm[t][cc] = as_v8<E>(uint4{wp[4 * cc], wp[4 * cc + 1], wp[4 * cc + 2], wp[4 * cc + 3]});
+                dsm[t][cc] = as_v8<E>(uint4{wd[4 * cc], wd[4 * cc + 1], wd[4 * cc + 2], wd[4 * cc + 3]});
+            }
         }
-        for (int cc = 0; cc < 2; ++cc)
+        for (int cc = 0; cc < CC; ++cc)
             for (int dh = 0; dh < kDHT; ++dh)
-                for (int t = 0; t < 2; ++t) {
+                for (int t = 0; t < KT; ++t) {
                     dvacc[t][dh] = E::mfma(dotr[cc][dh], pm[t][cc], dvacc[t][dh]);
                     dkacc[t][dh] = E::mfma(qtr[cc][dh], dsm[t][cc], dkacc[t][dh]);
                 }
@@ -556,7 +608,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
 
         if (qbk == nqb - 1) {
             // lane (c + 16g) holds dK^T, dV^T[d = 16dh + 4g + r][key 16t + c]
-            for (int t = 0; t < 2; ++t) {
+            for (int t = 0; t < KT; ++t) {
                 const int64_t j = kw0 + 16 * t + c;
                 if (j >= L) continue;
                 for (int dh = 0; dh < kDHT; ++dh) {
@@ -572,7 +624,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
         }
     }
     if (MASK && p.dmask)
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < KT; ++t) {
             const float tot = sum_over_groups(dm[t]);
             const int j = kw0 + 16 * t + c;
             if (g == 0 && j < L) {
@@ -584,7 +636,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
 
 template <class E, int D, bool PAIR, bool MASK>
 hipError_t launch_dkdv(Params& p, int64_t B, hipStream_t stream) {
-    const int64_t rblocks = (p.L + kBlockRows - 1) / kBlockRows;
+    const int64_t rblocks = (p.L + DkdvShape<D>::BK - 1) / DkdvShape<D>::BK;
     p.total = B * p.N * rblocks;
     if (p.total >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
     p.rblocks = make_fastdiv((uint32_t)rblocks);
@@ -611,6 +663,7 @@ template <class E, int D, bool MASK>
 __global__ __launch_bounds__(kZW * 64, 1) void bwd_dpair_mfma(Params p) {
     using V8 = typename E::v8;
     constexpr int kDC = D / 8;
+    constexpr int kDH = (D + 31) / 32;  // 32-wide halves of a row
     constexpr int kAcc = kZQ * kZK * 4;  // accumulators per lane
     __shared__ float red[kZW][kAcc][64];
 
@@ -648,7 +701,7 @@ __global__ __launch_bounds__(kZW * 64, 1) void bwd_dpair_mfma(Params p) {
     }
 
     struct Ops {
-        V8 k[kZK], v[kZK], q[kZQ], d[kZQ];
+        V8 k[kZK][kDH], v[kZK][kDH], q[kZQ][kDH], d[kZQ][kDH];
         float ls[kZQ], dl[kZQ];
         uint2 mk[kZK];
     };
@@ -660,16 +713,22 @@ __global__ __launch_bounds__(kZW * 64, 1) void bwd_dpair_mfma(Params p) {
         const Rsrc rd = make_rsrc(p.dout + b * st.o[0] + n * st.o[1] + h * st.o[3], last * rowo + D * 2);
         for (int kt = 0; kt < kZK; ++kt) {
             const uint32_t j = (uint32_t)(j0 + 16 * kt + c);
-            o.k[kt] = as_v8<E>(bload16(rk, g < kDC ? j * rowk + 16u * g : kOOB, 0));
-            o.v[kt] = as_v8<E>(bload16(rv, g < kDC ? j * rowv + 16u * g : kOOB, 0));
+            for (int hh = 0; hh < kDH; ++hh) {
+                const bool in = 4 * hh + g < kDC;
+                o.k[kt][hh] = as_v8<E>(bload16(rk, in ? j * rowk + 64u * hh + 16u * g : kOOB, 0));
+                o.v[kt][hh] = as_v8<E>(bload16(rv, in ? j * rowv + 64u * hh + 16u * g : kOOB, 0));
+            }
             const int jm = j0 + 16 * kt + 4 * g;
             o.mk[kt] = (MASK && jm < L) ? *reinterpret_cast<const uint2*>(p.mask + b * st.mb + n * st.mn + jm)
                                         : uint2{0u, 0u};
         }
         for (int qt = 0; qt < kZQ; ++qt) {
             const int i = i0 + 16 * qt + c;
-            o.q[qt] = as_v8<E>(bload16(rq, g < kDC ? (uint32_t)i * rowq + 16u * g : kOOB, 0));
-            o.d[qt] = as_v8<E>(bload16(rd, g < kDC ? (uint32_t)i * rowo + 16u * g : kOOB, 0));
+            for (int hh = 0; hh < kDH; ++hh) {
+                const bool in = 4 * hh + g < kDC;
+                o.q[qt][hh] = as_v8<E>(bload16(rq, in ? (uint32_t)i * rowq + 64u * hh + 16u * g : kOOB, 0));
+                o.d[qt][hh] = as_v8<E>(bload16(rd, in ? (uint32_t)i * rowo + 64u * hh + 16u * g : kOOB, 0));
+            }
             const int64_t row = ((b * N + n) * p.H + h) * st.lrow + i;
             o.ls[qt] = i < L ? lse_base2(p.lse[row]) : INFINITY;
             o.dl[qt] = i < L ? p.delta[row] : 0.f;
@@ -692,8 +751,11 @@ __global__ __launch_bounds__(kZW * 64, 1) void bwd_dpair_mfma(Params p) {
                     m2[0] = a[0] * kLog2e, m2[1] = a[1] * kLog2e, m2[2] = bb[0] * kLog2e, m2[3] = bb[1] * kLog2e;
                 }
                 for (int qt = 0; qt < kZQ; ++qt) {
-                    const f32x4 sc = E::mfma(cur.k[kt], cur.q[qt], f32x4{0.f, 0.f, 0.f, 0.f});
-                    const f32x4 dp = E::mfma(cur.v[kt], cur.d[qt], f32x4{0.f, 0.f, 0.f, 0.f});
+                    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int hh = 0; hh < kDH; ++hh) {
+                        sc = E::mfma(cur.k[kt][hh], cur.q[qt][hh], sc);
+                        dp = E::mfma(cur.v[kt][hh], cur.d[qt][hh], dp);
+                    }
                     for (int r = 0; r < 4; ++r) {
                         const float x = fmaf(sc[r], p.c1, pb[qt][kt][r]) + (m2[r] - cur.ls[qt]);
                         acc[qt][kt][r] = fmaf(__builtin_amdgcn_exp2f(x), dp[r] - cur.dl[qt], acc[qt][kt][r]);
@@ -745,11 +807,12 @@ hipError_t launch_dpair(Params p, int64_t B, hipStream_t stream) {
 //   q, dout, k, v: slot 4*row + (chunk ^ ((row >> 2) & 3)), row of the tile, chunk = 8 d-values
 //   mt: the tile's 64 mask values; ls, dl: lse * log2(e) and delta of the tile's queries
 // ---------------------------------------------------------------------------
+template <int DH>
 struct PairBuf {
-    uint4 q[64 * 4];
-    uint4 dout[64 * 4];
-    uint4 k[64 * 4];
-    uint4 v[64 * 4];
+    uint4 q[DH][64 * 4];
+    uint4 dout[DH][64 * 4];
+    uint4 k[DH][64 * 4];
+    uint4 v[DH][64 * 4];
     uint4 mt[8];
     float ls[64];
     float dl[64];
@@ -769,8 +832,10 @@ template <class E, int D, bool MASK>
 __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) {
     using V8 = typename E::v8;
     constexpr int kDC = D / 8;
+    constexpr int kDH = (D + 31) / 32;  // 32-wide halves of a row (each its own LDS tile)
+    using Buf = PairBuf<kDH>;
     const Params& p = pp.p;
-    __shared__ __attribute__((aligned(16))) PairBuf sm[2];
+    __shared__ __attribute__((aligned(16))) Buf sm[2];
 
     // order (b, h, chunk, query tile, key tile): the tiles of one (b, h, chunk)
     // run on one XCD together and share each n's rows in its L2
@@ -808,18 +873,26 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
     // copies of step n: rows 16 wave + lane/4 of the tile, chunk (lane & 3) ^ ((lane >> 4) & 3)
     const uint32_t dchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
     const uint32_t trow = (uint32_t)(16 * wave + (lane >> 2));
-    const bool din = dchunk < kDC;
-    const uint32_t qoff = din ? ((uint32_t)i0 + trow) * rowq + 16u * dchunk : kOOB;
-    const uint32_t dooff = din ? ((uint32_t)i0 + trow) * rowo + 16u * dchunk : kOOB;
-    const uint32_t koff = din ? ((uint32_t)j0 + trow) * rowk + 16u * dchunk : kOOB;
-    const uint32_t voff = din ? ((uint32_t)j0 + trow) * rowv + 16u * dchunk : kOOB;
+    uint32_t qoff[kDH], dooff[kDH], koff[kDH], voff[kDH];
+    for (int hh = 0; hh < kDH; ++hh) {
+        const bool din = 4 * hh + (int)dchunk < kDC;
+        qoff[hh] = din ? ((uint32_t)i0 + trow) * rowq + 64u * hh + 16u * dchunk : kOOB;
+        dooff[hh] = din ? ((uint32_t)i0 + trow) * rowo + 64u * hh + 16u * dchunk : kOOB;
+        koff[hh] = din ? ((uint32_t)j0 + trow) * rowk + 64u * hh + 16u * dchunk : kOOB;
+        voff[hh] = din ? ((uint32_t)j0 + trow) * rowv + 64u * hh + 16u * dchunk : kOOB;
+    }
     float lsv = 0.f, dlv = 0.f;
-    auto copy_step = [&](int64_t n, PairBuf* __restrict__ dst) {
-        dma16(make_rsrc(p.q + b * st.q[0] + n * st.q[1] + h * st.q[3], last * rowq + D * 2), &dst->q[64 * wave], qoff, 0);
-        dma16(make_rsrc(p.dout + b * st.o[0] + n * st.o[1] + h * st.o[3], last * rowo + D * 2), &dst->dout[64 * wave],
-              dooff, 0);
-        dma16(make_rsrc(p.k + b * st.k[0] + n * st.k[1] + h * st.k[3], last * rowk + D * 2), &dst->k[64 * wave], koff, 0);
-        dma16(make_rsrc(p.v + b * st.v[0] + n * st.v[1] + h * st.v[3], last * rowv + D * 2), &dst->v[64 * wave], voff, 0);
+    auto copy_step = [&](int64_t n, Buf* __restrict__ dst) {
+        const Rsrc rq = make_rsrc(p.q + b * st.q[0] + n * st.q[1] + h * st.q[3], last * rowq + D * 2);
+        const Rsrc rd = make_rsrc(p.dout + b * st.o[0] + n * st.o[1] + h * st.o[3], last * rowo + D * 2);
+        const Rsrc rk = make_rsrc(p.k + b * st.k[0] + n * st.k[1] + h * st.k[3], last * rowk + D * 2);
+        const Rsrc rv = make_rsrc(p.v + b * st.v[0] + n * st.v[1] + h * st.v[3], last * rowv + D * 2);
+        for (int hh = 0; hh < kDH; ++hh) {
+            dma16(rq, &dst->q[hh][64 * wave], qoff[hh], 0);
+            dma16(rd, &dst->dout[hh][64 * wave], dooff[hh], 0);
+            dma16(rk, &dst->k[hh][64 * wave], koff[hh], 0);
+            dma16(rv, &dst->v[hh][64 * wave], voff[hh], 0);
+        }
         if (MASK && wave == 0 && lane < 8)
             dma16(make_rsrc(p.mask + b * st.mb + n * st.mn, (uint32_t)L * 2u), &dst->mt[0], (uint32_t)j0 * 2u + 16u * lane,
                   0);
@@ -830,7 +903,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
             dlv = i < L ? p.delta[row] : 0.f;
         }
     };
-    auto put_rows = [&](PairBuf* __restrict__ dst) {
+    auto put_rows = [&](Buf* __restrict__ dst) {
         if (wave == 1) {
             dst->ls[lane] = lsv;
             dst->dl[lane] = dlv;
@@ -846,23 +919,30 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
     __syncthreads();
     for (int64_t n = n0; n < n1; ++n) {
         const int it = (int)(n - n0);
-        const PairBuf* __restrict__ cur = &sm[it & 1];
-        PairBuf* __restrict__ nxt = &sm[(it & 1) ^ 1];
+        const Buf* __restrict__ cur = &sm[it & 1];
+        Buf* __restrict__ nxt = &sm[(it & 1) ^ 1];
         const int sw = g ^ ((c >> 2) & 3);
-        const V8 qop = as_v8<E>(cur->q[64 * wave + 4 * c + sw]);
-        const V8 dop = as_v8<E>(cur->dout[64 * wave + 4 * c + sw]);
-        V8 kop[kKT], vop[kKT];
+        V8 qop[kDH], dop[kDH], kop[kKT][kDH], vop[kKT][kDH];
+        for (int hh = 0; hh < kDH; ++hh) {
+            qop[hh] = as_v8<E>(cur->q[hh][64 * wave + 4 * c + sw]);
+            dop[hh] = as_v8<E>(cur->dout[hh][64 * wave + 4 * c + sw]);
+        }
         uint2 mb[kKT];
         for (int kt = 0; kt < kKT; ++kt) {
-            kop[kt] = as_v8<E>(cur->k[64 * kt + 4 * c + sw]);
-            vop[kt] = as_v8<E>(cur->v[64 * kt + 4 * c + sw]);
+            for (int hh = 0; hh < kDH; ++hh) {
+                kop[kt][hh] = as_v8<E>(cur->k[hh][64 * kt + 4 * c + sw]);
+                vop[kt][hh] = as_v8<E>(cur->v[hh][64 * kt + 4 * c + sw]);
+            }
             if (MASK) mb[kt] = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(&cur->mt[2 * kt + (g >> 1)]) + 8 * (g & 1));
         }
         const float lsq = cur->ls[16 * wave + c], dlq = cur->dl[16 * wave + c];
         if (n + 1 < n1) copy_step(n + 1, nxt);
         for (int kt = 0; kt < kKT; ++kt) {
-            const f32x4 sc = E::mfma(kop[kt], qop, f32x4{0.f, 0.f, 0.f, 0.f});
-            const f32x4 dp = E::mfma(vop[kt], dop, f32x4{0.f, 0.f, 0.f, 0.f});
+            f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int hh = 0; hh < kDH; ++hh) {
+                sc = E::mfma(kop[kt][hh], qop[hh], sc);
+                dp = E::mfma(vop[kt][hh], dop[hh], dp);
+            }
             float m2[4] = {0.f, 0.f, 0.f, 0.f};
             if (MASK) {
                 const f32x2 a = unpack2<E>(mb[kt].x), bb = unpack2<E>(mb[kt].y);
@@ -1009,6 +1089,7 @@ hipError_t launch_format(const BwdArgs& a, unsigned stages, hipStream_t stream) 
     case 8: return launch_dim<E, 8>(a, stages, stream);
     case 16: return launch_dim<E, 16>(a, stages, stream);
     case 32: return launch_dim<E, 32>(a, stages, stream);
+    case 64: return launch_dim<E, 64>(a, stages, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1046,7 +1127,8 @@ bool bwd_mfma_eligible(const BwdArgs& a, int dtype) {
     constexpr int64_t kMax = int64_t(1) << 31;
     const Strides& s = a.st;
     const int64_t L = a.L, H = a.H, D = a.D;
-    if (!(dtype == 1 || dtype == 2) || !(D == 8 || D == 16 || D == 32) || L % 8 != 0 || a.N >= kMax || H >= kMax)
+    if (!(dtype == 1 || dtype == 2) || !(D == 8 || D == 16 || D == 32 || D == 64) || L % 8 != 0 || a.N >= kMax ||
+        H >= kMax)
         return false;
     for (const int64_t* t : {s.q, s.k, s.v, s.o})
         if (t[2] % 8 || t[3] % 8 || !rows_fit32(L, H, D, t[2], t[3])) return false;

@@ -330,3 +330,65 @@ def test_bwd_workspace_deterministic(torch_dev):
 def test_bwd_workload_without_workspace(torch_dev, c):
     w = S.workload(c)
     parity(torch_dev, w, S.random_dout(w.shape, w.dtype, seed=100 + c), use_ws=False)
+
+
+# ---------------------------------------------------------------------------
+# Head dimension 64 on the matrix cores (L % 8 == 0): dq and the pair gradient
+# in two 32-wide halves, dk/dv with 16-key tiles and 32-query steps.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("shape", [(1, 2, 64, 2), (1, 3, 136, 2), (2, 2, 200, 3), (1, 2, 40, 4)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_bwd_head_dim_64_matrix_cores(torch_dev, shape, dtype):
+    B, N, L, H = shape
+    w = S.random_problem(B, N, L, H, 64, dtype=dtype, seed=6400 + B * 100 + N * 10 + L + H, mask="tail",
+                         pair="normal", mask_frac=0.3)
+    parity(torch_dev, w, S.random_dout(w.shape, dtype, seed=L + 64))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_bwd_head_dim_64_split_over_n(torch_dev, dtype):
+    """D = 64 with the workspace (pair gradient split over N) and without: only dpair takes another route."""
+    import evoformer_biased_attention_amd as E
+    w = S.random_problem(1, 24, 136, 2, 64, dtype=dtype, seed=6464, mask="tail", pair="normal", mask_frac=0.2)
+    assert E.evo_attn_bwd_workspace_size(w.shape, E.EVO_DTYPE_BF16 if dtype == "bf16" else E.EVO_DTYPE_F16) > 0
+    dout = S.random_dout(w.shape, dtype, seed=6465)
+    split = parity(torch_dev, w, dout)
+    single = parity(torch_dev, w, dout, use_ws=False)
+    for a, b in zip(split[:4], single[:4]):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_bwd_head_dim_64_larger(torch_dev):
+    """D = 64 at N = 128, L = 256, H = 4 (bf16, mask and pair bias): four 64-key dk/dv workgroups per
+    sequence, eight 32-query steps per head."""
+    w = S.random_problem(1, 128, 256, 4, 64, dtype="bf16", seed=6466, mask="tail", pair="normal", mask_frac=0.1)
+    parity(torch_dev, w, S.random_dout(w.shape, "bf16", seed=6467))
+
+
+@pytest.mark.parametrize("L", [200, 72])
+def test_bwd_head_dim_64_rows_past_L_read_as_zero(torch_dev, L):
+    """As test_bwd_rows_past_L_read_as_zero, at D = 64: NaN right after every input."""
+    torch = torch_dev
+    import evoformer_biased_attention_amd as E
+    B, N, H, D, dtype = 1, 2, 2, 64, "bf16"
+    w = S.random_problem(B, N, L, H, D, dtype=dtype, seed=6468 + L, mask="tail", pair="normal", mask_frac=0.2)
+    dout = S.random_dout(w.shape, dtype, seed=6469)
+    extra = 128 * H * D + 128 * L
+
+    def dev(x):
+        t = to_dev(torch, x, dtype)
+        buf = torch.full((t.numel() + extra,), float("nan"), dtype=t.dtype, device="cuda")
+        buf[: t.numel()] = t.reshape(-1)
+        return buf[: t.numel()].view(t.shape)
+
+    q, k, v, m, p, do = (dev(x) for x in (w.q, w.k, w.v, w.mask, w.pair, dout))
+    out, lse = E.fwd(q, k, v, m, p)
+    o2 = torch.full((out.numel() + extra,), float("nan"), dtype=out.dtype, device="cuda")
+    o2[: out.numel()] = out.reshape(-1)
+    out = o2[: out.numel()].view(out.shape)
+    grads = E.bwd(q, k, v, m, p, out, lse, do)[:5]
+    torch.cuda.synchronize()
+    got = [f64(g) for g in grads]
+    want = list(oracle.bwd(w.q, w.k, w.v, w.mask, w.pair, dout, dtype=dtype, nthreads=THREADS))
+    compare_grads(got, want, dtype, f"D = 64, NaN after every input, L={L}")
