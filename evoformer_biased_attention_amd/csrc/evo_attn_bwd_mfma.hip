@@ -373,9 +373,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
 // dk, dv and dmask.  Workgroup = 64 KT keys of one (b, n); wave w owns keys
 // 16 KT w .. as KT 16-key tiles and keeps their K and V rows (B operands of
 // S = Q.K^T and dP = dO.V^T) in registers.  The workgroup walks every (head,
-// QS-query block) pair in order.  KT = 2, QS = 64 for head dimensions up to
-// 32; KT = 1, QS = 32 for D = 64 (two 32-wide halves of every row), which
-// keeps the operands of one step within the registers of two waves per SIMD.
+// QS-query block) pair in order.  KT = 1 (one 16-key tile per wave, which
+// keeps a step within the registers of three waves per SIMD); QS = 64 for
+// head dimensions up to 32, QS = 32 for D = 64 (two 32-wide halves of every
+// row), so that each step's q and dO tiles are one wave-wide copy per wave.
 // LDS per step, d-rows in 32-wide halves hh:
 //   q, dO: half hh, slot 4*row + (chunk ^ ((row >> 2) & 3)), row = query of the block, chunk = 8 d-values
 //   pt:    slot (8 KT)*row + (chunk ^ 2(row & (4 KT - 1))), chunk = 8 of the workgroup's keys
@@ -395,7 +396,7 @@ struct KvBuf {
 
 template <int D>
 struct DkdvShape {
-    static constexpr int KT = D > 32 ? 1 : 2;   // 16-key tiles per wave
+    static constexpr int KT = 1;                 // 16-key tiles per wave
     static constexpr int QS = D > 32 ? 32 : 64;  // queries per step
     static constexpr int BK = kWaves * 16 * KT;  // keys per workgroup
 };
@@ -412,6 +413,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
     constexpr int RPI = 64 / CPR;             // pair rows per wave-wide copy
     constexpr int PCW = QS / RPI / kWaves;    // pair copies per wave and step
     constexpr int RG = QS / 16;               // 16-row groups of a half (q and dO copies)
+    // the q and dO copies take one wave-wide copy per wave and tensor
+    static_assert(QS * 4 * kDH == 64 * kWaves, "q/dO tile must be one wave-wide copy per wave");
+    static_assert(PCW >= 1 && PCW * RPI * kWaves == QS, "pair tile must split evenly over the waves");
     __shared__ __attribute__((aligned(16))) KvBuf<QS, kDH, KT> sm[2];
 
     const uint32_t id = (uint32_t)logical_block(blockIdx.x, p.total);
