@@ -860,9 +860,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
     const uint32_t rowo = (uint32_t)st.o[2] * 2;
     const uint32_t last = (uint32_t)(L - 1);
 
-    // pair bias (base 2) of lane c + 16g: query i0 + 16 wave + c, keys j0 + 16kt + 4g + 0..3
-    float pb[kKT][4];
+    // pair bias of lane c + 16g (query i0 + 16 wave + c, keys j0 + 16kt + 4g
+    // + 0..3) times sqrt(D): the accumulator input of every S^T product, so
+    // that S^T comes out as q.k + sqrt(D) pair, which the exponent's factor
+    // log2(e) / sqrt(D) maps to q.k log2(e) / sqrt(D) + pair log2(e)
+    f32x4 pbs[kKT];
     {
+        const float sqd = __builtin_sqrtf((float)D);
         const u16* pm = p.pair + b * st.pb + h * st.ph;
         const int i = i0 + 16 * wave + c;
         for (int kt = 0; kt < kKT; ++kt) {
@@ -870,7 +874,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
             uint2 w = {0u, 0u};
             if (i < L && j < L) w = *reinterpret_cast<const uint2*>(pm + (int64_t)i * st.pi + j);
             const f32x2 a = unpack2<E>(w.x), bb = unpack2<E>(w.y);
-            pb[kt][0] = a[0] * kLog2e, pb[kt][1] = a[1] * kLog2e, pb[kt][2] = bb[0] * kLog2e, pb[kt][3] = bb[1] * kLog2e;
+            pbs[kt] = f32x4{a[0] * sqd, a[1] * sqd, bb[0] * sqd, bb[1] * sqd};
         }
     }
 
@@ -942,18 +946,18 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
         const float lsq = cur->ls[16 * wave + c], dlq = cur->dl[16 * wave + c];
         if (n + 1 < n1) copy_step(n + 1, nxt);
         for (int kt = 0; kt < kKT; ++kt) {
-            f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 sc = pbs[kt], dp = f32x4{0.f, 0.f, 0.f, 0.f};
             for (int hh = 0; hh < kDH; ++hh) {
                 sc = E::mfma(kop[kt][hh], qop[hh], sc);
                 dp = E::mfma(vop[kt][hh], dop[hh], dp);
             }
-            float m2[4] = {0.f, 0.f, 0.f, 0.f};
+            float mraw[4] = {0.f, 0.f, 0.f, 0.f};
             if (MASK) {
                 const f32x2 a = unpack2<E>(mb[kt].x), bb = unpack2<E>(mb[kt].y);
-                m2[0] = a[0] * kLog2e, m2[1] = a[1] * kLog2e, m2[2] = bb[0] * kLog2e, m2[3] = bb[1] * kLog2e;
+                mraw[0] = a[0], mraw[1] = a[1], mraw[2] = bb[0], mraw[3] = bb[1];
             }
             for (int r = 0; r < 4; ++r) {
-                const float x = fmaf(sc[r], p.c1, pb[kt][r]) + (m2[r] - lsq);
+                const float x = fmaf(sc[r], p.c1, MASK ? fmaf(mraw[r], kLog2e, -lsq) : -lsq);
                 acc[kt][r] = fmaf(__builtin_amdgcn_exp2f(x), dp[r] - dlq, acc[kt][r]);
             }
         }
