@@ -185,11 +185,13 @@ __device__ inline uint4 clamp_neg_inf_f16(uint4 x) {
     return uint4{w[0], w[1], w[2], w[3]};
 }
 
-// Whether some 16-bit value of x is other than -inf in binary16 (0xfc00).
-__device__ inline bool any_not_neg_inf_f16(uint4 x) {
+// Whether one of the first n 16-bit values of x is other than -inf in
+// binary16 (0xfc00).
+__device__ inline bool any_not_neg_inf_f16(uint4 x, int n) {
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
     bool any = false;
-    for (int i = 0; i < 4; ++i) any |= (w[i] & 0xffffu) != 0xfc00u || (w[i] >> 16) != 0xfc00u;
+    for (int i = 0; i < 4; ++i)
+        any |= (2 * i < n && (w[i] & 0xffffu) != 0xfc00u) || (2 * i + 1 < n && (w[i] >> 16) != 0xfc00u);
     return any;
 }
 
@@ -269,12 +271,31 @@ struct Slice {
     float* lrow;       // lse row of (b, n, h) or nullptr
 };
 
+// 16 bytes at byte offset `off` of a buffer of `range` bytes, any 2-byte
+// alignment.  A chunk that starts inside the range and ends past it is read
+// element by element, so that its elements inside the range keep their
+// values (the range check of a wider load may drop more than the part
+// outside); a chunk wholly past the range reads as zeros either way.
+__device__ inline uint4 bload16_any(Rsrc r, uint32_t off, uint32_t range) {
+    if (off >= range || off + 16u <= range) return bload16(r, off, 0);
+    uint32_t w[4];
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, (int)(off + 4 * e), 0, 0);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, (int)(off + 4 * e + 2), 0, 0);
+        w[e] = lo | (hi << 16);
+    }
+    return uint4{w[0], w[1], w[2], w[3]};
+}
+
 // ---------------------------------------------------------------------------
 // Fast path.  Returns false (for the whole workgroup) when some row produced
 // a NaN, i.e. a bias held +-inf; nothing has been written in that case.
-// Requires L % 8 == 0, L * H * D * 2 < 2^31 and L * L * 2 < 2^31.
+// Requires L * H * D * 2 < 2^31 and L * L * 2 < 2^31.  STAGED: the bias rows
+// are not 16-byte aligned (L % 8 != 0, or unaligned bias strides); their
+// tiles then go global -> registers -> LDS, with unaligned 16-byte loads,
+// instead of straight into LDS.
 // ---------------------------------------------------------------------------
-template <class E, int D, bool PAIR, bool MASK>
+template <class E, int D, bool PAIR, bool MASK, bool STAGED>
 __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32>& sm, int tid) {
     using V8 = typename E::v8;
     using Buf = FastBuf<(D + 31) / 32>;
@@ -297,7 +318,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
     const Rsrc rq = make_rsrc(p.q + s.qb, (uint32_t)(L - 1) * rowq + D * 2);
     const Rsrc rk = make_rsrc(p.k + s.kb, (uint32_t)(L - 1) * rowk + D * 2);
     const Rsrc rv = make_rsrc(p.v + s.vb, (uint32_t)(L - 1) * rowv + D * 2);
-    const Rsrc rp = make_rsrc(PAIR ? s.pbase : p.q, PAIR ? (uint32_t)(L - 1) * rowp + (uint32_t)L * 2u : 0u);
+    const Rsrc rp = make_rsrc(PAIR ? s.pbase : p.q, PAIR ? (uint32_t)(L - 1) * rowp + (uint32_t)L * 2u : 0u);  // prange
     const Rsrc rm = make_rsrc(MASK ? s.mrow : p.q, MASK ? (uint32_t)L * 2u : 0u);
 
     // Identity A operand: slot (g, e) stands for key 8*(g%2) + e of a 16-key
@@ -346,15 +367,32 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
         // rows past L start beyond the range (the pair row stride is at least L)
         pvo[j] = (qwg + row) * rowp + 16u * ((lane & 7) ^ (lane >> 3));
     }
+    // STAGED: the pair and mask chunks in flight between a block's copy and
+    // its landing in LDS
+    uint4 pstage[4], mstage;
+    const uint32_t prange = PAIR ? (uint32_t)(L - 1) * rowp + (uint32_t)L * 2u : 0u;
     auto copy_block = [&](int blk, Buf* __restrict__ dst) {
         const uint32_t k0 = (uint32_t)blk * kKB;
         for (int hh = 0; hh < kDH; ++hh) {
             dma16(rk, &dst->k[hh][64 * wave], ko[hh] + k0 * rowk, 0);
             dma16(rv, &dst->v[hh][64 * wave], vo[hh] + k0 * rowv, 0);
         }
+        if (STAGED) {
+            if (PAIR)
+                for (int j = 0; j < 4; ++j) pstage[j] = bload16_any(rp, pvo[j] + k0 * 2u, prange);
+            if (MASK && wave == 0 && lane < 8) mstage = bload16_any(rm, 16u * lane + k0 * 2u, (uint32_t)L * 2u);
+        } else {
+            if (PAIR)
+                for (int j = 0; j < 4; ++j) dma16(rp, &dst->pt[64 * (4 * wave + j)], pvo[j] + k0 * 2u, 0);
+            if (MASK && wave == 0 && lane < 8) dma16(rm, &dst->mt[0], 16u * lane + k0 * 2u, 0);
+        }
+    };
+    // STAGED: the staged chunks into the slots the direct copies would fill
+    auto land_block = [&](Buf* __restrict__ dst) {
+        if (!STAGED) return;
         if (PAIR)
-            for (int j = 0; j < 4; ++j) dma16(rp, &dst->pt[64 * (4 * wave + j)], pvo[j] + k0 * 2u, 0);
-        if (MASK && wave == 0 && lane < 8) dma16(rm, &dst->mt[0], 16u * lane + k0 * 2u, 0);
+            for (int j = 0; j < 4; ++j) dst->pt[64 * (4 * wave + j) + lane] = pstage[j];
+        if (MASK && wave == 0 && lane < 8) dst->mt[lane] = mstage;
     };
 
     f32x4 oacc[kQTiles][kDHT];
@@ -371,6 +409,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
     bool all_neg_inf = E::kF16 && MASK;
 
     copy_block(0, &sm.buf[0]);
+    land_block(&sm.buf[0]);
     wait_all();
     __syncthreads();
 
@@ -424,10 +463,10 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
             const uint4 mw = cur->mt[lane & 7];
             mask_on = wave_any((mw.x | mw.y | mw.z | mw.w) != 0);
             // binary16: remember whether any key so far escaped a -inf mask
-            // (chunks past L read as zero and do not count)
+            // (keys past L read as zero or as the next row and do not count)
             if (E::kF16)
                 all_neg_inf = all_neg_inf && mask_on &&
-                              !wave_any(k0 + 8 * (lane & 7) < L && any_not_neg_inf_f16(mw));
+                              !wave_any(any_not_neg_inf_f16(mw, L - k0 - 8 * (lane & 7)));
         }
         if (mask_on) scores(cur, acc, std::true_type{});
         else scores(cur, acc, std::false_type{});
@@ -518,6 +557,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
             for (int dh = 0; dh < kDHT; ++dh)
                 for (int t = 0; t < kQTiles; ++t) oacc[t][dh] = E::mfma(vop[cc][dh], pmat[t][cc], oacc[t][dh]);
 
+        if (it + 1 < nblocks) land_block(nxt);
         wait_all();  // the next block's copies have landed
         __syncthreads();
     };
@@ -558,7 +598,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
 // ---------------------------------------------------------------------------
 // Exact path: biases are widened and added on the vector ALUs in base-2
 // units (-inf stays -inf), every access is bounds-checked, any L works.  Used
-// for biases holding +-inf and for L % 8 != 0.  Same lane layout as the fast
+// for biases holding +-inf.  Same lane layout as the fast
 // path; K and transposed V are staged through LDS with two barriers per block.
 // ---------------------------------------------------------------------------
 template <class E, int D>
@@ -678,11 +718,10 @@ __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int ti
     }
 }
 
-// FAST: the fast path may run (L % 8 == 0); otherwise every workgroup takes
-// the exact path.  D <= 32: three workgroups' LDS fit on a CU, and the second
+// STAGED: the fast path copies the bias tiles through registers.  D <= 32: three workgroups' LDS fit on a CU, and the second
 // launch bound keeps the registers within what three waves per SIMD allow
 // (168 VGPRs).  D = 64: two workgroups per CU (64 KB of LDS each), 256 VGPRs.
-template <class E, int D, bool PAIR, bool MASK, bool FAST>
+template <class E, int D, bool PAIR, bool MASK, bool STAGED>
 __global__ __launch_bounds__(kWaves * 64, D > 32 ? 2 : 3) void fwd_16bit_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) Smem<(D + 31) / 32> sm;
 
@@ -705,28 +744,26 @@ __global__ __launch_bounds__(kWaves * 64, D > 32 ? 2 : 3) void fwd_16bit_kernel(
     s.pbase = p.pair ? p.pair + s.b * st.pb + s.h * st.ph : nullptr;
     s.lrow = p.lse ? p.lse + ((s.b * p.N + s.n) * p.H + s.h) * st.lrow : nullptr;
 
-    if constexpr (FAST) {
-        if (run_fast<E, D, PAIR, MASK>(p, s, sm.f, tid)) return;
-        __syncthreads();
-    }
+    if (run_fast<E, D, PAIR, MASK, STAGED>(p, s, sm.f, tid)) return;
+    __syncthreads();
     run_exact<E, D>(p, s, sm.e, tid);
 }
 
-template <class E, int D, bool PAIR, bool MASK, bool FAST>
+template <class E, int D, bool PAIR, bool MASK, bool STAGED>
 hipError_t launch_variant(Params& p, hipStream_t stream) {
     void* args[] = {&p};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_16bit_kernel<E, D, PAIR, MASK, FAST>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_16bit_kernel<E, D, PAIR, MASK, STAGED>),
                            dim3((unsigned)p.total), dim3(kWaves * 64), args, 0, stream);
 }
 
-// The fast path copies bias rows in 16-byte pieces: it needs L % 8 == 0 and
-// bias rows that start 16-byte aligned.
+// The direct copies of bias rows into LDS need 16-byte aligned rows (L % 8
+// == 0 and aligned bias strides); other rows are staged through registers.
 template <class E, int D, bool PAIR, bool MASK>
 hipError_t launch_biases(Params& p, hipStream_t stream) {
     const bool aligned = (!PAIR || (p.st.pb % 8 == 0 && p.st.ph % 8 == 0 && p.st.pi % 8 == 0)) &&
                          (!MASK || (p.st.mb % 8 == 0 && p.st.mn % 8 == 0));
-    return p.L % 8 == 0 && aligned ? launch_variant<E, D, PAIR, MASK, true>(p, stream)
-                                   : launch_variant<E, D, PAIR, MASK, false>(p, stream);
+    return p.L % 8 == 0 && aligned ? launch_variant<E, D, PAIR, MASK, false>(p, stream)
+                                   : launch_variant<E, D, PAIR, MASK, true>(p, stream);
 }
 
 template <class E, int D>

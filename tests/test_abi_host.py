@@ -306,7 +306,7 @@ def test_strided_rules():
     lay.q[1] = 0                                    # inputs may repeat: the same Q for every n
     assert scheck(lay) == E.EVO_OK
     lay = E.evo_attn_dense_layout(shape)
-    lay.mask_n = 68                                 # unaligned bias rows are accepted (exact path)
+    lay.mask_n = 68                                 # unaligned bias rows are accepted (staged copies)
     lay.pair_i = 66
     assert scheck(lay) == E.EVO_OK
 

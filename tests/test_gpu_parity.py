@@ -193,6 +193,55 @@ def test_neg_inf_mask_rows(torch_dev):
     compare(o, l, ro, rl, "bf16", "neg-inf mask")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("L", [77, 96])
+def test_neg_inf_pair_bias_exact_path(torch_dev, L, dtype):
+    """-inf in the pair bias (one key, part of a row, a whole row, the last element): the identity product
+    turns it into NaN and those workgroups redo their slice on the exact path, for staged (L = 77) and
+    direct (L = 96) bias copies."""
+    w = S.random_problem(1, 2, L, 2, 32, dtype=dtype, seed=900 + L, mask="tail", pair="normal")
+    pf = S.storage_to_f32(w.pair, dtype).copy()
+    pf[0, 0, 1, 5, 7] = -np.inf
+    pf[0, 0, 0, 70, :40] = -np.inf
+    pf[0, 0, 1, 20, :] = -np.inf
+    pf[0, 0, 0, L - 1, L - 1] = -np.inf
+    w.pair = S.to_storage(pf, dtype)
+    o, l = run_gpu(torch_dev, w)
+    ro, rl = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype=dtype, nthreads=THREADS)
+    compare(o, l, ro, rl, dtype, f"infinite pair bias, L={L}")
+
+
+# ---------------------------------------------------------------------------
+# L % 8 != 0: bias rows are not 16-byte aligned, and the kernel stages the
+# bias tiles through registers with unaligned loads; a chunk that crosses the
+# end of its buffer is read element by element.  Large biases on the last
+# element of every pair matrix and mask row (and on the first key of the
+# last pair row) make a dropped or shifted value show.
+# ---------------------------------------------------------------------------
+def with_edge_biases(w):
+    pf = S.storage_to_f32(w.pair, w.dtype).copy()
+    pf[..., -1, -1] = 6.0
+    pf[..., -1, 0] = -4.0
+    mf = S.storage_to_f32(w.mask, w.dtype).copy()
+    mf[..., -1] = 3.0
+    w.pair, w.mask = S.to_storage(pf, w.dtype), S.to_storage(mf, w.dtype)
+    return w
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("L", [3, 9, 31, 63, 66, 99, 130, 250])
+def test_odd_L_edge_biases(torch_dev, L, dtype):
+    w = with_edge_biases(S.random_problem(1, 2, L, 3, 32, dtype=dtype, seed=600 + L, mask="tail", pair="normal"))
+    parity_full(torch_dev, w)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [8, 16, 64])
+def test_odd_L_edge_biases_other_head_dims(torch_dev, d, dtype):
+    w = with_edge_biases(S.random_problem(2, 2, 75, 2, d, dtype=dtype, seed=700 + d, mask="tail", pair="normal"))
+    parity_full(torch_dev, w)
+
+
 # ---------------------------------------------------------------------------
 # binary16 (the same MFMA kernel on f16 operands).  A -1e9 mask is -inf in
 # this format.
@@ -230,9 +279,10 @@ def test_f16_large_biases_and_random_masks(torch_dev):
     parity_full(torch_dev, w)
 
 
-@pytest.mark.parametrize("L", [96, 128])
+@pytest.mark.parametrize("L", [96, 99, 128])
 def test_f16_fully_masked_sequences(torch_dev, L):
-    """A sequence whose keys are all -inf returns out = 0 and lse = -inf; L = 96 ends in a partial key block."""
+    """A sequence whose keys are all -inf returns out = 0 and lse = -inf; L = 96 ends in a partial key block,
+    L = 99 in a partial 8-key chunk (the keys past L must not count as unmasked)."""
     B, N, H, D = 1, 3, 2, 32
     w = S.random_problem(B, N, L, H, D, dtype="f16", seed=9 + L, mask="zero", pair="normal")
     mf = np.zeros((B, N, 1, 1, L), np.float32)
@@ -330,8 +380,8 @@ def test_rows_past_L_read_as_zero(torch_dev, dtype):
 
 # ---------------------------------------------------------------------------
 # Head dimension 64 on the 16-bit path: two 32-wide halves of the contraction,
-# on the fast path for L % 8 == 0 (64, 136, 200, 256) and on the exact path
-# otherwise (1, 17, 100, 257).
+# with bias tiles copied straight into LDS for L % 8 == 0 (64, 136, 200, 256)
+# and staged through registers otherwise (1, 17, 100, 257).
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("shape", [(1, 1, 1, 1), (1, 2, 17, 3), (2, 2, 64, 2), (1, 3, 100, 4), (1, 2, 257, 2),

@@ -98,7 +98,7 @@ def test_padded_lse_rows(torch_dev, L):
 
 @pytest.mark.parametrize("pad", [8, 3])
 def test_padded_pair_rows(torch_dev, pad):
-    """Pair rows L + pad apart (a slice of a wider tensor); pad = 3 leaves the rows unaligned (exact path)."""
+    """Pair rows L + pad apart (a slice of a wider tensor); pad = 3 leaves the rows unaligned (staged copies)."""
     torch = torch_dev
     B, N, L, H, D = 1, 4, 96, 2, 32
     w = S.random_problem(B, N, L, H, D, dtype="bf16", seed=90 + pad, mask="tail", pair="normal")
@@ -110,6 +110,32 @@ def test_padded_pair_rows(torch_dev, pad):
     o, l, _ = gpu_strided(torch, q, k, v, m, pair, out)
     ro, rl = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype="bf16", nthreads=THREADS)
     compare(o, l, ro, rl, "bf16", f"pair rows L+{pad}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("L", [77, 96])
+def test_unaligned_bias_rows(torch_dev, L, dtype):
+    """Pair rows L + 1 apart and mask rows L + 3 apart (slices of wider tensors): the bias rows start at
+    every 2-byte alignment, also for L % 8 == 0.  Large biases sit on the last element of each row."""
+    torch = torch_dev
+    B, N, H, D = 2, 3, 2, 32
+    w = S.random_problem(B, N, L, H, D, dtype=dtype, seed=1200 + L, mask="tail", pair="normal")
+    pf = S.storage_to_f32(w.pair, dtype).copy()
+    pf[..., :, -1] = 5.0
+    mf = S.storage_to_f32(w.mask, dtype).copy()
+    mf[..., -1] = 3.0
+    w.pair, w.mask = S.to_storage(pf, dtype), S.to_storage(mf, dtype)
+    wide_p = np.zeros((B, 1, H, L, L + 1), np.uint16)
+    wide_p[..., :L] = w.pair
+    wide_m = np.zeros((B, N, 1, 1, L + 3), np.uint16)
+    wide_m[..., :L] = w.mask
+    pair = to_dev(torch, wide_p, dtype)[..., :L]
+    mask = to_dev(torch, wide_m, dtype)[..., :L]
+    q, k, v = (to_dev(torch, x, dtype) for x in (w.q, w.k, w.v))
+    out = torch.full_like(q, float("nan"))
+    o, l, _ = gpu_strided(torch, q, k, v, mask, pair, out)
+    ro, rl = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype=dtype, nthreads=THREADS)
+    compare(o, l, ro, rl, dtype, f"unaligned bias rows L={L}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
