@@ -420,10 +420,10 @@ extern "C" evo_status_t evo_trimul_check(const void* a, const void* w, const voi
         if (!aligned16(p)) return EVO_ERR_MISALIGNED;
     const Extent ex = extent(x, bytes);
     if (ex.overlaps(extent(a, bytes)) || ex.overlaps(extent(w, bytes))) return EVO_ERR_ALIASING;
-    // matrix-core kernel: 16-bit formats, L a multiple of 8, one plane's rows
-    // (up to L + 128 of them) addressed with 32-bit byte offsets
+    // matrix-core kernel: 16-bit formats, one plane's rows (up to L + 128 of
+    // them) addressed with 32-bit byte offsets
     const int64_t L = shape->L;
-    if (dtype == EVO_DTYPE_F32 || L % 8 || L * L * 2 >= kMaxOffset || (L + 128) * L * 2 >= kMaxOffset32)
+    if (dtype == EVO_DTYPE_F32 || L * L * 2 >= kMaxOffset || (L + 128) * L * 2 >= kMaxOffset32)
         return EVO_ERR_UNSUPPORTED;
     return EVO_OK;
 }

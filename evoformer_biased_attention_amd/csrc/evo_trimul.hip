@@ -27,7 +27,15 @@
 //    of 8 columns), read with the transposing ds_read_b64_tr_b16; both
 //    operands put k = 32kc + 16(e/4) + 4g + e%4 in element e of lane group g.
 //  * Buffer resources of one plane return zeros for rows past L; chunks of k
-//    past L get an offset past the range.  Hence L % 8 == 0.
+//    past L get an offset past the range.
+//  * L % 8 != 0: rows are no longer 16-byte aligned, so the operand chunks
+//    go global -> registers -> LDS (unaligned 16-byte loads, into the slots
+//    the direct copies would fill).  A chunk that starts inside the plane's
+//    range and ends past it is read element by element; outgoing chunks that
+//    cross k = L have their elements past L cleared (they hold the next
+//    row); incoming chunks past column L only feed outputs that are not
+//    stored.  The epilogue writes the last partial 8-wide piece of each
+//    output row element by element.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -87,6 +95,33 @@ __device__ inline void dma16(Rsrc r, const void* lds, uint32_t voff) {
 
 __device__ inline void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
+__device__ inline uint4 bload16(Rsrc r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// 16 bytes at byte offset `off` of a buffer of `range` bytes, any 2-byte
+// alignment.  A chunk that starts inside the range and ends past it is read
+// element by element, so that its elements inside the range keep their
+// values (the range check of a wider load may drop more than the part
+// outside); a chunk wholly past the range reads as zeros either way.
+__device__ inline uint4 bload16_any(Rsrc r, uint32_t off, uint32_t range) {
+    if (off >= range || off + 16u <= range) return bload16(r, off);
+    uint32_t w[4];
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, (int)(off + 4 * e), 0, 0);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, (int)(off + 4 * e + 2), 0, 0);
+        w[e] = lo | (hi << 16);
+    }
+    return uint4{w[0], w[1], w[2], w[3]};
+}
+
+// x with its 16-bit elements e >= n cleared
+__device__ inline uint4 keep_first(uint4 x, int n) {
+    uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    for (int i = 0; i < 4; ++i) w[i] &= (2 * i < n ? 0xffffu : 0u) | (2 * i + 1 < n ? 0xffff0000u : 0u);
+    return uint4{w[0], w[1], w[2], w[3]};
+}
+
 __device__ inline int64_t logical_block(int64_t hw, int64_t total) {
     const int64_t xcd = hw % 8, j = hw / 8;
     const int64_t per = total / 8, extra = total % 8;
@@ -117,7 +152,7 @@ __device__ inline int tm_swz(int row) {
     return KS == 64 ? (row & 7) : ((row >> 2) & 3);
 }
 
-template <class E, bool INCOMING, int KS>
+template <class E, bool INCOMING, int KS, bool STAGED>
 __global__ __launch_bounds__(256, KS == 64 ? 2 : 3) void trimul_kernel(TmParams p) {
     using V8 = typename E::v8;
     constexpr int CPR = KS / 8;        // outgoing: 16-byte chunks per tile row
@@ -158,6 +193,7 @@ __global__ __launch_bounds__(256, KS == 64 ? 2 : 3) void trimul_kernel(TmParams 
             offw[q] = (uint32_t)kr * (uint32_t)L * 2u + (uint32_t)j0 * 2u + 16u * chunk;
         }
     }
+    uint4 sa[SEG], sw[SEG];  // STAGED: chunks between their load and their landing in LDS
     auto copy_step = [&](int st, TmBuf<KS>* __restrict__ dst) {
         const int k0 = st * KS;
         for (int q = 0; q < SEG; ++q) {
@@ -170,8 +206,27 @@ __global__ __launch_bounds__(256, KS == 64 ? 2 : 3) void trimul_kernel(TmParams 
                 oa = offa[q] + (uint32_t)k0 * (uint32_t)L * 2u;  // k rows past L start beyond the range
                 ow = offw[q] + (uint32_t)k0 * (uint32_t)L * 2u;
             }
-            dma16(ra, &dst->a[64 * (SEG * wave + q)], oa);
-            dma16(rw, &dst->w[64 * (SEG * wave + q)], ow);
+            if (!STAGED) {
+                dma16(ra, &dst->a[64 * (SEG * wave + q)], oa);
+                dma16(rw, &dst->w[64 * (SEG * wave + q)], ow);
+            } else {
+                sa[q] = bload16_any(ra, oa, range);
+                sw[q] = bload16_any(rw, ow, range);
+                if (!INCOMING && k0 + KS > L) {  // the step that reaches k = L
+                    const int valid = L - (k0 + kofs[q]);
+                    if (valid < 8) {
+                        sa[q] = keep_first(sa[q], valid);
+                        sw[q] = keep_first(sw[q], valid);
+                    }
+                }
+            }
+        }
+    };
+    auto land_step = [&](TmBuf<KS>* __restrict__ dst) {
+        if (!STAGED) return;
+        for (int q = 0; q < SEG; ++q) {
+            dst->a[64 * (SEG * wave + q) + lane] = sa[q];
+            dst->w[64 * (SEG * wave + q) + lane] = sw[q];
         }
     };
 
@@ -180,6 +235,7 @@ __global__ __launch_bounds__(256, KS == 64 ? 2 : 3) void trimul_kernel(TmParams 
         for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     copy_step(0, &sm[0]);
+    land_step(&sm[0]);
     wait_all();
     __syncthreads();
     for (int st = 0; st < nsteps; ++st) {
@@ -213,6 +269,7 @@ __global__ __launch_bounds__(256, KS == 64 ? 2 : 3) void trimul_kernel(TmParams 
         for (int kc = 0; kc < KC; ++kc)
             for (int mt = 0; mt < 4; ++mt)
                 for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = E::mfma(aop[kc][mt], bop[kc][nt], acc[mt][nt]);
+        if (st + 1 < nsteps) land_step(&sm[(st & 1) ^ 1]);
         wait_all();
         __syncthreads();
     }
@@ -234,8 +291,16 @@ __global__ __launch_bounds__(256, KS == 64 ? 2 : 3) void trimul_kernel(TmParams 
     for (int pass = 0; pass < 8; ++pass) {
         const int row = 8 * pass + (lane >> 3);
         const u32x4 v = *reinterpret_cast<const u32x4*>(tile + row * kRow + 8 * (lane & 7));
-        if (ib + row < L && jc < L)
-            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p.x + pbase + (int64_t)(ib + row) * L + jc));
+        if (ib + row < L && jc < L) {
+            u16* dst = p.x + pbase + (int64_t)(ib + row) * L + jc;
+            if (!STAGED || jc + 8 <= L) {
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));  // unaligned when STAGED
+            } else {
+                const u16* e = reinterpret_cast<const u16*>(tile + row * kRow + 8 * (lane & 7));
+                for (int q = 0; q < 8; ++q)
+                    if (jc + q < L) dst[q] = e[q];
+            }
+        }
     }
 }
 
@@ -244,8 +309,9 @@ constexpr int kKStep = 64;  // contraction step (a 32-wide step measured no fast
 template <class E, bool INCOMING>
 hipError_t launch(TmParams& p, hipStream_t stream) {
     void* args[] = {&p};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&trimul_kernel<E, INCOMING, kKStep>),
-                           dim3((unsigned)p.total), dim3(256), args, 0, stream);
+    const void* k = p.L % 8 ? reinterpret_cast<const void*>(&trimul_kernel<E, INCOMING, kKStep, true>)
+                            : reinterpret_cast<const void*>(&trimul_kernel<E, INCOMING, kKStep, false>);
+    return hipLaunchKernel(k, dim3((unsigned)p.total), dim3(256), args, 0, stream);
 }
 
 }  // namespace

@@ -273,8 +273,8 @@ evo_status_t evo_attn_bwd_check_strided(const void* q, const void* k, const void
  * x is rounded to nearest-even once.  The layer normalisations, projections
  * and gates around this contraction in a model are O(L^2) per channel and
  * not part of this call.
- * Supported today: BF16 and F16 with L % 8 == 0, L <= 32767 and
- * (L + 128) * L * 2 < 2^32; any B, C >= 1.  Other valid calls return
+ * Supported today: BF16 and F16 with L <= 32767 and (L + 128) * L * 2 <
+ * 2^32; any B, C >= 1.  Other valid calls return
  * EVO_ERR_UNSUPPORTED.  Errors as for evo_attn_fwd (a bad direction is
  * EVO_ERR_BAD_SHAPE); nothing is written on error.
  */

@@ -423,7 +423,7 @@ def tcheck(shape=(1, 4, 64), direction=E.EVO_TRIMUL_OUTGOING, dtype=E.EVO_DTYPE_
 def test_trimul_valid():
     for d in (E.EVO_TRIMUL_OUTGOING, E.EVO_TRIMUL_INCOMING):
         for dt in (E.EVO_DTYPE_BF16, E.EVO_DTYPE_F16):
-            for shape in ((1, 1, 8), (2, 3, 72), (1, 128, 384)):
+            for shape in ((1, 1, 8), (2, 3, 72), (1, 128, 384), (1, 1, 1), (2, 3, 99)):
                 assert tcheck(shape=shape, direction=d, dtype=dt) == E.EVO_OK
     a, *_ = addrs(1)
     assert tcheck(w=a) == E.EVO_OK                          # the operands may be one tensor
@@ -439,6 +439,5 @@ def test_trimul_errors():
     assert tcheck(x=a) == E.EVO_ERR_ALIASING
     assert tcheck(x=w + 64 * 64 * 2 * 4 - 16) == E.EVO_ERR_ALIASING   # starts inside w's last 16 bytes
     assert tcheck(x=x + 8) == E.EVO_ERR_MISALIGNED
-    assert tcheck(shape=(1, 4, 100)) == E.EVO_ERR_UNSUPPORTED          # L % 8 != 0
     assert tcheck(dtype=E.EVO_DTYPE_F32) == E.EVO_ERR_UNSUPPORTED
     assert tcheck(shape=(1, 1, 32768)) == E.EVO_ERR_UNSUPPORTED        # L * L * 2 = 2^31

@@ -57,8 +57,9 @@ def run(torch, a, w, dtype, direction, extra=0):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("direction", ["outgoing", "incoming"])
-@pytest.mark.parametrize("L", [8, 16, 64, 72, 128, 136, 200, 264])
+@pytest.mark.parametrize("L", [1, 3, 8, 16, 31, 64, 72, 99, 128, 130, 136, 200, 257, 264])
 def test_trimul_ragged(torch_dev, L, direction, dtype):
+    """L % 8 != 0 (1, 3, 31, 99, 130, 257) stages the operands through registers."""
     a, w = S.trimul_problem(2, 3, L, dtype, seed=L)
     compare(run(torch_dev, a, w, dtype, direction), oracle.trimul(a, w, dtype, direction, nthreads=THREADS), dtype,
             f"L={L} {direction}")
@@ -76,10 +77,12 @@ def test_trimul_workload_sampled_channels(torch_dev, direction):
 
 
 @pytest.mark.parametrize("direction", ["outgoing", "incoming"])
-def test_trimul_rows_past_L_read_as_zero(torch_dev, direction):
-    """NaN right after both inputs, L = 72 (partial 128 tile and partial 64 contraction step)."""
-    a, w = S.trimul_problem(1, 2, 72, "bf16", seed=5)
-    x = run(torch_dev, a, w, "bf16", direction, extra=256 * 72)
+@pytest.mark.parametrize("L", [72, 77])
+def test_trimul_rows_past_L_read_as_zero(torch_dev, direction, L):
+    """NaN right after both inputs, L = 72 (partial 128 tile and partial 64 contraction step) and L = 77
+    (staged copies: the last chunk of the plane crosses the end of the range)."""
+    a, w = S.trimul_problem(1, 2, L, "bf16", seed=5)
+    x = run(torch_dev, a, w, "bf16", direction, extra=256 * L)
     compare(x, oracle.trimul(a, w, "bf16", direction, nthreads=THREADS), "bf16", f"NaN tail {direction}")
 
 
@@ -94,9 +97,9 @@ def test_trimul_same_operand(torch_dev):
 def test_trimul_errors_write_nothing(torch_dev):
     torch = torch_dev
     import evoformer_biased_attention_amd as E
-    a = torch.zeros((1, 2, 100, 100), dtype=torch.bfloat16, device="cuda")
+    a = torch.zeros((1, 2, 100, 100), dtype=torch.float32, device="cuda")
     x = torch.full_like(a, 7.0)
-    assert E.evo_trimul(a, a, x, (1, 2, 100), 0, E.EVO_DTYPE_BF16) == E.EVO_ERR_UNSUPPORTED
-    assert E.evo_trimul(a, a, a, (1, 2, 100), 0, E.EVO_DTYPE_BF16) == E.EVO_ERR_ALIASING
+    assert E.evo_trimul(a, a, x, (1, 2, 100), 0, E.EVO_DTYPE_F32) == E.EVO_ERR_UNSUPPORTED
+    assert E.evo_trimul(a, a, a, (1, 2, 100), 0, E.EVO_DTYPE_F32) == E.EVO_ERR_ALIASING
     torch.cuda.synchronize()
     assert bool((x == 7.0).all())
