@@ -348,7 +348,7 @@ namespace {
 int64_t usable_chunks(const evo::BwdArgs& a, evo_dtype_t dtype, size_t workspace_bytes) {
     if (!evo::bwd_mfma_eligible(a, static_cast<int>(dtype))) return 0;
     const int64_t want = evo::bwd_dpair_chunks(a.B, a.N, a.L, a.H);
-    const int64_t per = a.B * a.H * a.L * a.L * 4;  // bytes of one chunk's partial sums
+    const int64_t per = a.B * a.H * a.L * evo::bwd_ws_row(a.L) * 4;  // bytes of one chunk's partial sums
     const int64_t fit = static_cast<int64_t>(workspace_bytes / static_cast<size_t>(per));
     const int64_t c = want < fit ? want : fit;
     return c >= 2 ? c : 0;
@@ -359,7 +359,7 @@ int64_t usable_chunks(const evo::BwdArgs& a, evo_dtype_t dtype, size_t workspace
 extern "C" size_t evo_attn_bwd_workspace_size(const evo_shape_t* shape, evo_dtype_t dtype) {
     if (!shape || shape->B < 1 || shape->N < 1 || shape->L < 1 || shape->H < 1 || shape->D < 1) return 0;
     int64_t par = 4;
-    for (int64_t s : {shape->B, shape->H, shape->L, shape->L}) par = mul_checked(par, s);
+    for (int64_t s : {shape->B, shape->H, shape->L, evo::bwd_ws_row(shape->L)}) par = mul_checked(par, s);
     if (par < 0) return 0;
     evo_layout_t lay;
     evo_attn_dense_layout(shape, &lay);

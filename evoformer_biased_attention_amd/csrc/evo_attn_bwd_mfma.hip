@@ -113,6 +113,48 @@ __device__ inline void dma16(Rsrc r, const void* lds, uint32_t voff, uint32_t so
 
 __device__ inline void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 
+// 16 bytes at byte offset `off` of a buffer of `range` bytes, any 2-byte
+// alignment.  A chunk that starts inside the range and ends past it is read
+// element by element, so that its elements inside the range keep their
+// values (the range check of a wider load may drop more than the part
+// outside); a chunk wholly past the range reads as zeros either way.
+__device__ inline uint4 bload16_any(Rsrc r, uint32_t off, uint32_t range) {
+    if (off >= range || off + 16u <= range) return bload16(r, off, 0);
+    uint32_t w[4];
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, (int)(off + 4 * e), 0, 0);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, (int)(off + 4 * e + 2), 0, 0);
+        w[e] = lo | (hi << 16);
+    }
+    return uint4{w[0], w[1], w[2], w[3]};
+}
+
+// Four consecutive 16-bit values at p of which the first n lie inside their
+// row (n >= 1; the rest read as zero), at any 2-byte alignment.
+__device__ inline uint2 load4(const u16* p, int n) {
+    uint2 v = {0u, 0u};
+    if (n >= 4) {
+        __builtin_memcpy(&v, p, 8);
+    } else {
+        uint32_t e[3] = {0u, 0u, 0u};
+        for (int q = 0; q < 3; ++q)
+            if (q < n) e[q] = p[q];
+        v = uint2{e[0] | (e[1] << 16), e[2]};
+    }
+    return v;
+}
+
+// The first n (>= 1) of four packed 16-bit values to p, at any 2-byte alignment.
+__device__ inline void store4(u16* p, uint2 v, int n) {
+    if (n >= 4) {
+        __builtin_memcpy(p, &v, 8);
+    } else {
+        const u16 e[3] = {(u16)(v.x & 0xffffu), (u16)(v.x >> 16), (u16)(v.y & 0xffffu)};
+        for (int q = 0; q < 3; ++q)
+            if (q < n) p[q] = e[q];
+    }
+}
+
 // x / d with a multiply-high and a shift (Granlund and Montgomery, PLDI
 // 1994, section 4), for 0 <= x < 2^31 and 1 <= d < 2^31.
 struct FastDiv {
@@ -171,7 +213,10 @@ struct DqBuf {
     uint4 mt[8];
 };
 
-template <class E, int D, bool PAIR, bool MASK>
+// STAGED: bias rows not 16-byte aligned (L % 8 != 0 or unaligned bias
+// strides); their tiles go global -> registers -> LDS through unaligned
+// 16-byte loads, into the slots the direct copies would fill.
+template <class E, int D, bool PAIR, bool MASK, bool STAGED>
 __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
     using V8 = typename E::v8;
     constexpr int kDC = D / 8;           // 16-byte chunks per row
@@ -252,15 +297,29 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
         const uint32_t row = 8u * (4 * wave + j) + (lane >> 3);
         pvo[j] = (qwg + row) * rowp + 16u * ((lane & 7) ^ (lane >> 3));
     }
+    uint4 pstage[4], mstage;  // STAGED: chunks between their load and their landing in LDS
+    const uint32_t prange = PAIR ? last * rowp + (uint32_t)L * 2u : 0u;
     auto copy_block = [&](int blk, Buf* __restrict__ dst) {
         const uint32_t k0 = (uint32_t)blk * kKB;
         for (int hh = 0; hh < kDH; ++hh) {
             dma16(rk, &dst->k[hh][64 * wave], ko[hh] + k0 * rowk, 0);
             dma16(rv, &dst->v[hh][64 * wave], vo[hh] + k0 * rowv, 0);
         }
+        if (STAGED) {
+            if (PAIR)
+                for (int j = 0; j < 4; ++j) pstage[j] = bload16_any(rp, pvo[j] + k0 * 2u, prange);
+            if (MASK && wave == 0 && lane < 8) mstage = bload16_any(rm, 16u * lane + k0 * 2u, (uint32_t)L * 2u);
+        } else {
+            if (PAIR)
+                for (int j = 0; j < 4; ++j) dma16(rp, &dst->pt[64 * (4 * wave + j)], pvo[j] + k0 * 2u, 0);
+            if (MASK && wave == 0 && lane < 8) dma16(rm, &dst->mt[0], 16u * lane + k0 * 2u, 0);
+        }
+    };
+    auto land_block = [&](Buf* __restrict__ dst) {
+        if (!STAGED) return;
         if (PAIR)
-            for (int j = 0; j < 4; ++j) dma16(rp, &dst->pt[64 * (4 * wave + j)], pvo[j] + k0 * 2u, 0);
-        if (MASK && wave == 0 && lane < 8) dma16(rm, &dst->mt[0], 16u * lane + k0 * 2u, 0);
+            for (int j = 0; j < 4; ++j) dst->pt[64 * (4 * wave + j) + lane] = pstage[j];
+        if (MASK && wave == 0 && lane < 8) dst->mt[lane] = mstage;
     };
 
     f32x4 dqacc[2][kDHT];
@@ -268,6 +327,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
         for (int dh = 0; dh < kDHT; ++dh) dqacc[t][dh] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     copy_block(0, &sm[0]);
+    land_block(&sm[0]);
     wait_all();
     __syncthreads();
 
@@ -346,6 +406,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
             for (int dh = 0; dh < kDHT; ++dh)
                 for (int t = 0; t < 2; ++t) dqacc[t][dh] = E::mfma(ktr[cc][dh], dsop[t][cc], dqacc[t][dh]);
 
+        if (it + 1 < nblocks) land_block(nxt);
         wait_all();
         __syncthreads();
     };
@@ -401,7 +462,7 @@ struct DkdvShape {
     static constexpr int BK = kWaves * 16 * KT;  // keys per workgroup
 };
 
-template <class E, int D, bool PAIR, bool MASK>
+template <class E, int D, bool PAIR, bool MASK, bool STAGED>
 __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
     using V8 = typename E::v8;
     constexpr int kDC = D / 8;
@@ -472,14 +533,18 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
         pvo[j] = row * rowp + (uint32_t)kb * BK * 2u + 16u * ((lane % CPR) ^ (2 * (row & (CPR / 2 - 1))));
     }
     float lsv = 0.f, dlv = 0.f;  // wave 0: this lane's query of the step being copied
+    uint4 pstage[PCW];           // STAGED: pair chunks between their load and their landing in LDS
     auto copy_block = [&](int it, KvBuf<QS, kDH, KT>* __restrict__ dst) {
         const int h = it / nqb, q0 = (it - h * nqb) * QS;
         dma16(rq, &dst->q[qhh][64 * qrg], qoff + (uint32_t)q0 * rowq + (uint32_t)h * hq, 0);
         dma16(rdo, &dst->dout[qhh][64 * qrg], dooff + (uint32_t)q0 * rowo + (uint32_t)h * ho, 0);
         if (PAIR) {
-            const Rsrc rp = make_rsrc(p.pair + b * st.pb + h * st.ph, last * rowp + (uint32_t)L * 2u);
-            for (int j = 0; j < PCW; ++j)
-                dma16(rp, &dst->pt[64 * (PCW * wave + j)], pvo[j] + (uint32_t)q0 * rowp, 0);
+            const uint32_t prange = last * rowp + (uint32_t)L * 2u;
+            const Rsrc rp = make_rsrc(p.pair + b * st.pb + h * st.ph, prange);
+            for (int j = 0; j < PCW; ++j) {
+                if (STAGED) pstage[j] = bload16_any(rp, pvo[j] + (uint32_t)q0 * rowp, prange);
+                else dma16(rp, &dst->pt[64 * (PCW * wave + j)], pvo[j] + (uint32_t)q0 * rowp, 0);
+            }
         }
         if (wave == 0 && lane < QS) {
             const int i = q0 + lane;
@@ -493,6 +558,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
             dst->ls[lane] = lsv;
             dst->dl[lane] = dlv;
         }
+        if (STAGED && PAIR)
+            for (int j = 0; j < PCW; ++j) dst->pt[64 * (PCW * wave + j) + lane] = pstage[j];
     };
 
     V8 kop[KT][kDH], vop[KT][kDH];
@@ -638,14 +705,14 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
         }
 }
 
-template <class E, int D, bool PAIR, bool MASK>
+template <class E, int D, bool PAIR, bool MASK, bool STAGED>
 hipError_t launch_dkdv(Params& p, int64_t B, hipStream_t stream) {
     const int64_t rblocks = (p.L + DkdvShape<D>::BK - 1) / DkdvShape<D>::BK;
     p.total = B * p.N * rblocks;
     if (p.total >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
     p.rblocks = make_fastdiv((uint32_t)rblocks);
     void* args[] = {&p};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_mfma<E, D, PAIR, MASK>), dim3((unsigned)p.total),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_mfma<E, D, PAIR, MASK, STAGED>), dim3((unsigned)p.total),
                            dim3(kWaves * 64), args, 0, stream);
 }
 
@@ -697,7 +764,7 @@ __global__ __launch_bounds__(kZW * 64, 1) void bwd_dpair_mfma(Params p) {
             for (int kt = 0; kt < kZK; ++kt) {
                 const int i = i0 + 16 * qt + c, j = j0 + 16 * kt + 4 * g;
                 uint2 w = {0u, 0u};
-                if (i < L && j < L) w = *reinterpret_cast<const uint2*>(pm + (int64_t)i * st.pi + j);
+                if (i < L && j < L) w = load4(pm + (int64_t)i * st.pi + j, L - j);
                 const f32x2 a = unpack2<E>(w.x), bb = unpack2<E>(w.y);
                 pb[qt][kt][0] = a[0] * kLog2e, pb[qt][kt][1] = a[1] * kLog2e;
                 pb[qt][kt][2] = bb[0] * kLog2e, pb[qt][kt][3] = bb[1] * kLog2e;
@@ -723,8 +790,7 @@ __global__ __launch_bounds__(kZW * 64, 1) void bwd_dpair_mfma(Params p) {
                 o.v[kt][hh] = as_v8<E>(bload16(rv, in ? j * rowv + 64u * hh + 16u * g : kOOB, 0));
             }
             const int jm = j0 + 16 * kt + 4 * g;
-            o.mk[kt] = (MASK && jm < L) ? *reinterpret_cast<const uint2*>(p.mask + b * st.mb + n * st.mn + jm)
-                                        : uint2{0u, 0u};
+            o.mk[kt] = (MASK && jm < L) ? load4(p.mask + b * st.mb + n * st.mn + jm, L - jm) : uint2{0u, 0u};
         }
         for (int qt = 0; qt < kZQ; ++qt) {
             const int i = i0 + 16 * qt + c;
@@ -782,8 +848,8 @@ __global__ __launch_bounds__(kZW * 64, 1) void bwd_dpair_mfma(Params p) {
             for (int r = 0; r < 4; ++r) tot[r] += red[w][4 * f + r][l];
         const int i = i0 + 16 * qt + (l & 15), j = j0 + 16 * kt + 4 * (l >> 4);
         if (i < L && j < L)
-            *reinterpret_cast<uint2*>(p.dpair + pmat + (int64_t)i * st.pi + j) =
-                uint2{pack2<E>(tot[0], tot[1]), pack2<E>(tot[2], tot[3])};
+            store4(p.dpair + pmat + (int64_t)i * st.pi + j, uint2{pack2<E>(tot[0], tot[1]), pack2<E>(tot[2], tot[3])},
+                   L - j);
     }
 }
 
@@ -824,7 +890,7 @@ struct PairBuf {
 
 struct PartParams {
     Params p;
-    float* ws;        // [chunks][B][H][L][L] fp32
+    float* ws;        // [chunks][B][H][L][bwd_ws_row(L)] fp32
     int64_t chunks;   // N is split into this many contiguous ranges
     FastDiv tiles;    // 64 x 64 tiles per (b, h): ceil(L/64)^2
     FastDiv tdim;     // ceil(L/64)
@@ -832,7 +898,7 @@ struct PartParams {
     int64_t bh;       // B * H
 };
 
-template <class E, int D, bool MASK>
+template <class E, int D, bool MASK, bool STAGED>
 __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) {
     using V8 = typename E::v8;
     constexpr int kDC = D / 8;
@@ -872,7 +938,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
         for (int kt = 0; kt < kKT; ++kt) {
             const int j = j0 + 16 * kt + 4 * g;
             uint2 w = {0u, 0u};
-            if (i < L && j < L) w = *reinterpret_cast<const uint2*>(pm + (int64_t)i * st.pi + j);
+            if (i < L && j < L) w = load4(pm + (int64_t)i * st.pi + j, L - j);
             const f32x2 a = unpack2<E>(w.x), bb = unpack2<E>(w.y);
             pbs[kt] = f32x4{a[0] * sqd, a[1] * sqd, bb[0] * sqd, bb[1] * sqd};
         }
@@ -890,6 +956,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
         voff[hh] = din ? ((uint32_t)j0 + trow) * rowv + 64u * hh + 16u * dchunk : kOOB;
     }
     float lsv = 0.f, dlv = 0.f;
+    uint4 mstage;  // STAGED: the mask chunk between its load and its landing in LDS
     auto copy_step = [&](int64_t n, Buf* __restrict__ dst) {
         const Rsrc rq = make_rsrc(p.q + b * st.q[0] + n * st.q[1] + h * st.q[3], last * rowq + D * 2);
         const Rsrc rd = make_rsrc(p.dout + b * st.o[0] + n * st.o[1] + h * st.o[3], last * rowo + D * 2);
@@ -901,9 +968,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
             dma16(rk, &dst->k[hh][64 * wave], koff[hh], 0);
             dma16(rv, &dst->v[hh][64 * wave], voff[hh], 0);
         }
-        if (MASK && wave == 0 && lane < 8)
-            dma16(make_rsrc(p.mask + b * st.mb + n * st.mn, (uint32_t)L * 2u), &dst->mt[0], (uint32_t)j0 * 2u + 16u * lane,
-                  0);
+        if (MASK && wave == 0 && lane < 8) {
+            const Rsrc rm = make_rsrc(p.mask + b * st.mb + n * st.mn, (uint32_t)L * 2u);
+            if (STAGED) mstage = bload16_any(rm, (uint32_t)j0 * 2u + 16u * lane, (uint32_t)L * 2u);
+            else dma16(rm, &dst->mt[0], (uint32_t)j0 * 2u + 16u * lane, 0);
+        }
         if (wave == 1) {
             const int i = i0 + lane;
             const int64_t row = ((b * N + n) * p.H + h) * st.lrow + i;
@@ -916,6 +985,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
             dst->ls[lane] = lsv;
             dst->dl[lane] = dlv;
         }
+        if (STAGED && MASK && wave == 0 && lane < 8) dst->mt[lane] = mstage;
     };
 
     f32x4 acc[kKT];
@@ -972,17 +1042,18 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
         for (int kt = 0; kt < kKT; ++kt) {
             const int j = j0 + 16 * kt + 4 * g;
             if (j < L)
-                *reinterpret_cast<f32x4*>(pp.ws + ((chunk * pp.bh + b * p.H + h) * p.L + i) * p.L + j) = acc[kt];
+                *reinterpret_cast<f32x4*>(pp.ws + ((chunk * pp.bh + b * p.H + h) * p.L + i) * bwd_ws_row(p.L) + j) =
+                    acc[kt];
         }
 }
 
 // dpair[b,h,i,j] = sum over the workspace's chunks of their partial sums, in
-// chunk order; four consecutive keys per thread (L is a multiple of 8, the
-// pair strides multiples of 8 elements).  The workspace is dense [B][H][L][L].
+// chunk order; four consecutive keys per thread.  The workspace is dense
+// [B][H][L][bwd_ws_row(L)]; keys past L are skipped.
 struct ReduceParams {
     const float* ws;
     u16* dpair;
-    int64_t quads, chunks;  // B*H*L*L / 4; N-chunks
+    int64_t quads, chunks;  // B*H*L*bwd_ws_row(L) / 4; N-chunks
     int64_t L, H;
     int64_t pb, ph, pi;     // strides of dpair
 };
@@ -993,13 +1064,14 @@ __global__ __launch_bounds__(256) void bwd_dpair_reduce(ReduceParams r) {
     if (q >= r.quads) return;
     f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int64_t ch = 0; ch < r.chunks; ++ch) t += reinterpret_cast<const f32x4*>(r.ws)[ch * r.quads + q];
-    const int64_t rq = r.L / 4, row = q / rq, j = 4 * (q - row * rq);  // row = (b * H + h) * L + i
+    const int64_t rq = bwd_ws_row(r.L) / 4, row = q / rq, j = 4 * (q - row * rq);  // row = (b * H + h) * L + i
+    if (j >= r.L) return;
     const int64_t bh = row / r.L, i = row - bh * r.L, b = bh / r.H, h = bh - b * r.H;
-    *reinterpret_cast<uint2*>(r.dpair + b * r.pb + h * r.ph + i * r.pi + j) =
-        uint2{pack2<E>(t[0], t[1]), pack2<E>(t[2], t[3])};
+    store4(r.dpair + b * r.pb + h * r.ph + i * r.pi + j, uint2{pack2<E>(t[0], t[1]), pack2<E>(t[2], t[3])},
+           (int)(r.L - j));
 }
 
-template <class E, int D, bool MASK>
+template <class E, int D, bool MASK, bool STAGED>
 hipError_t launch_dpair_ws(const Params& base, int64_t B, float* ws, int64_t chunks, hipStream_t stream) {
     PartParams pp;
     pp.p = base;
@@ -1013,13 +1085,13 @@ hipError_t launch_dpair_ws(const Params& base, int64_t B, float* ws, int64_t chu
     pp.chd = make_fastdiv((uint32_t)chunks);
     pp.bh = B * base.H;
     void* args[] = {&pp};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dpair_part<E, D, MASK>),
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dpair_part<E, D, MASK, STAGED>),
                                    dim3((unsigned)pp.p.total), dim3(kWaves * 64), args, 0, stream);
     if (e != hipSuccess) return e;
     ReduceParams r;
     r.ws = ws;
     r.dpair = base.dpair;
-    r.quads = B * base.H * base.L * base.L / 4;
+    r.quads = B * base.H * base.L * bwd_ws_row(base.L) / 4;
     r.chunks = chunks;
     r.L = base.L;
     r.H = base.H;
@@ -1031,14 +1103,14 @@ hipError_t launch_dpair_ws(const Params& base, int64_t B, float* ws, int64_t chu
                            rargs, 0, stream);
 }
 
-template <class E, int D, bool PAIR, bool MASK>
+template <class E, int D, bool PAIR, bool MASK, bool STAGED>
 hipError_t launch_dq(Params& p, int64_t B, hipStream_t stream) {
     const int64_t rblocks = (p.L + kBlockRows - 1) / kBlockRows;
     p.total = B * p.N * p.H * rblocks;
     if (p.total >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
     p.rblocks = make_fastdiv((uint32_t)rblocks);
     void* args[] = {&p};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_mfma<E, D, PAIR, MASK>), dim3((unsigned)p.total),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_mfma<E, D, PAIR, MASK, STAGED>), dim3((unsigned)p.total),
                            dim3(kWaves * 64), args, 0, stream);
 }
 
@@ -1068,25 +1140,41 @@ hipError_t launch_dim(const BwdArgs& a, unsigned stages, hipStream_t stream) {
     p.scale = (float)(1.0 / std::sqrt((double)D));
     p.st = a.st;
     const bool pair = a.pair != nullptr, mask = a.mask != nullptr;
+    // bias rows copied in 16-byte pieces straight into LDS need 16-byte
+    // alignment; other rows are staged through registers
+    const Strides& s = a.st;
+    const bool staged = a.L % 8 || (pair && (s.pb % 8 || s.ph % 8 || s.pi % 8)) || (mask && (s.mb % 8 || s.mn % 8));
     hipError_t e = hipSuccess;
     if (stages & kStageDq) {
-        if (pair && mask) e = launch_dq<E, D, true, true>(p, a.B, stream);
-        else if (pair) e = launch_dq<E, D, true, false>(p, a.B, stream);
-        else if (mask) e = launch_dq<E, D, false, true>(p, a.B, stream);
-        else e = launch_dq<E, D, false, false>(p, a.B, stream);
+        if (staged) {
+            if (pair && mask) e = launch_dq<E, D, true, true, true>(p, a.B, stream);
+            else if (pair) e = launch_dq<E, D, true, false, true>(p, a.B, stream);
+            else if (mask) e = launch_dq<E, D, false, true, true>(p, a.B, stream);
+            else e = launch_dq<E, D, false, false, true>(p, a.B, stream);
+        } else {
+            if (pair && mask) e = launch_dq<E, D, true, true, false>(p, a.B, stream);
+            else if (pair) e = launch_dq<E, D, true, false, false>(p, a.B, stream);
+            else if (mask) e = launch_dq<E, D, false, true, false>(p, a.B, stream);
+            else e = launch_dq<E, D, false, false, false>(p, a.B, stream);
+        }
     }
     if (e == hipSuccess && (stages & kStageDkDv)) {
-        if (pair && mask) e = launch_dkdv<E, D, true, true>(p, a.B, stream);
-        else if (pair) e = launch_dkdv<E, D, true, false>(p, a.B, stream);
-        else if (mask) e = launch_dkdv<E, D, false, true>(p, a.B, stream);
-        else e = launch_dkdv<E, D, false, false>(p, a.B, stream);
+        // the dk/dv kernel reads the mask per key, so only the pair tile is staged
+        if (pair && mask) e = staged ? launch_dkdv<E, D, true, true, true>(p, a.B, stream)
+                                     : launch_dkdv<E, D, true, true, false>(p, a.B, stream);
+        else if (pair) e = staged ? launch_dkdv<E, D, true, false, true>(p, a.B, stream)
+                                  : launch_dkdv<E, D, true, false, false>(p, a.B, stream);
+        else if (mask) e = launch_dkdv<E, D, false, true, false>(p, a.B, stream);
+        else e = launch_dkdv<E, D, false, false, false>(p, a.B, stream);
     }
     if (e == hipSuccess && (stages & kStageDpair) && a.dpair) {
-        if (a.ws && a.ws_chunks >= 1)
-            e = mask ? launch_dpair_ws<E, D, true>(p, a.B, a.ws, a.ws_chunks, stream)
-                     : launch_dpair_ws<E, D, false>(p, a.B, a.ws, a.ws_chunks, stream);
-        else
+        if (a.ws && a.ws_chunks >= 1) {
+            if (mask) e = staged ? launch_dpair_ws<E, D, true, true>(p, a.B, a.ws, a.ws_chunks, stream)
+                                 : launch_dpair_ws<E, D, true, false>(p, a.B, a.ws, a.ws_chunks, stream);
+            else e = launch_dpair_ws<E, D, false, false>(p, a.B, a.ws, a.ws_chunks, stream);
+        } else {
             e = mask ? launch_dpair<E, D, true>(p, a.B, stream) : launch_dpair<E, D, false>(p, a.B, stream);
+        }
     }
     return e;
 }
@@ -1135,14 +1223,13 @@ bool bwd_mfma_eligible(const BwdArgs& a, int dtype) {
     constexpr int64_t kMax = int64_t(1) << 31;
     const Strides& s = a.st;
     const int64_t L = a.L, H = a.H, D = a.D;
-    if (!(dtype == 1 || dtype == 2) || !(D == 8 || D == 16 || D == 32 || D == 64) || L % 8 != 0 || a.N >= kMax ||
-        H >= kMax)
+    if (!(dtype == 1 || dtype == 2) || !(D == 8 || D == 16 || D == 32 || D == 64) || a.N >= kMax || H >= kMax)
         return false;
     for (const int64_t* t : {s.q, s.k, s.v, s.o})
         if (t[2] % 8 || t[3] % 8 || !rows_fit32(L, H, D, t[2], t[3])) return false;
-    // biases are copied in 16-byte pieces; pair rows at least L apart (the C ABI checks)
-    if (a.pair && (s.pb % 8 || s.ph % 8 || s.pi % 8 || !rows_fit32(L, 1, L, s.pi, 0))) return false;
-    if (a.mask && (s.mb % 8 || s.mn % 8)) return false;
+    // pair rows at least L apart (the C ABI checks); unaligned bias rows are
+    // staged through registers
+    if (a.pair && !rows_fit32(L, 1, L, s.pi, 0)) return false;
     return true;
 }
 

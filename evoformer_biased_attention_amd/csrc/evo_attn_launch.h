@@ -78,9 +78,13 @@ bool bwd_mfma_eligible(const BwdArgs& a, int dtype);
 // The number of N-chunks whose pair-gradient partial sums the matrix-core
 // path would like in its workspace (0: no workspace wanted).
 int64_t bwd_dpair_chunks(int64_t B, int64_t N, int64_t L, int64_t H);
+// Row length (fp32 elements) of those partial sums: L rounded up to a
+// multiple of 4, so that every 4-key group of a row is one aligned 16-byte
+// piece of its own row.  One chunk holds B * H * L rows.
+__host__ __device__ inline int64_t bwd_ws_row(int64_t L) { return (L + 3) / 4 * 4; }
 hipError_t launch_bwd_mfma(const BwdArgs& a, int dtype, unsigned stages, hipStream_t stream);
 
-// Triangle multiplication, 16-bit formats, [planes][L][L] operands, L % 8 == 0.
+// Triangle multiplication, 16-bit formats, [planes][L][L] operands.
 hipError_t launch_trimul(const void* a, const void* w, void* x, int64_t planes, int64_t L, int incoming, int f16,
                          hipStream_t stream);
 

@@ -234,15 +234,18 @@ def test_bwd_workspace_rules():
 
 
 def test_bwd_workspace_size():
-    """The size is a whole number of fp32 [B,H,L,L] partial-sum planes, at least two, or 0."""
-    plane = lambda B, H, L: B * H * L * L * 4
+    """The size is a whole number of fp32 [B,H,L,ceil4(L)] partial-sum planes (rows padded to a multiple of
+    4 keys), at least two, or 0."""
+    plane = lambda B, H, L: B * H * L * ((L + 3) // 4 * 4) * 4
     ws = E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 32), E.EVO_DTYPE_BF16)
     assert ws > 0 and ws % plane(1, 4, 384) == 0 and ws // plane(1, 4, 384) >= 2
     assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 32), E.EVO_DTYPE_F16) == ws
     assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 32), E.EVO_DTYPE_F32) == 0    # vector-ALU path
     assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 64), E.EVO_DTYPE_BF16) == ws  # matrix cores for D = 64 too
     assert E.evo_attn_bwd_workspace_size((1, 8, 384, 4, 32), E.EVO_DTYPE_BF16) == 0     # N too small to split
-    assert E.evo_attn_bwd_workspace_size((1, 384, 100, 4, 32), E.EVO_DTYPE_BF16) == 0   # L % 8 != 0
+    for L in (100, 383, 99):                                                          # any L on the matrix cores
+        ws_l = E.evo_attn_bwd_workspace_size((1, 384, L, 4, 32), E.EVO_DTYPE_BF16)
+        assert ws_l > 0 and ws_l % plane(1, 4, L) == 0 and ws_l // plane(1, 4, L) >= 2
     assert E.evo_attn_bwd_workspace_size((0, 384, 384, 4, 32), E.EVO_DTYPE_BF16) == 0
 
 

@@ -23,6 +23,9 @@ accepts 5e-2 (bf16) and 1e-2 (fp16) on the gradients (section 4).  The mean of t
 error alone reaches a quarter ulp (2^-10 for bf16) when most values sit near
 the maximum, as in a tensor of a few elements, so the mean bounds are twice
 that: the forward's 2e-3 for bf16, and 5e-4 for f16.
+With a single key (L = 1), P = 1 and dS = dO . v - dO . out with out = v, so
+dq, dk and both bias gradients vanish identically; those are checked against
+the fp32 error bound of that cancellation instead (single_key_bound).
 delta = dO . out is computed from the out the backward is given, which
 carries the forward pass's own error (bounded by the forward tolerances:
 max |d out| <= 1e-4 / 2e-2 / 1e-2 for f32 / bf16 / f16); so it is compared
@@ -164,7 +167,40 @@ def test_bwd_ragged(torch_dev, shape, d, dtype):
     w = S.random_problem(B, N, L, H, d, dtype=dtype, seed=B * 1000 + N * 100 + L + H + d, mask="tail",
                          pair="normal", mask_frac=0.3)
     dout = S.random_dout(w.shape, dtype, seed=L + d)
-    parity(torch_dev, w, dout)
+    if L == 1:
+        single_key(torch_dev, w, dout)
+    else:
+        parity(torch_dev, w, dout)
+
+
+def single_key(torch, w, dout):
+    """L = 1: dv = dO (P = 1) is compared as usual.  dq, dk, dmask and dpair vanish identically (the oracle
+    returns exact zeros); the kernel's dS is the fp32 difference of two evaluations of the same D-term dot
+    product dO . v, so |dS| <= 2 gamma_D sum_d |dO_d v_d| with gamma_D = D u / (1 - D u), u = 2^-24.  Each
+    gradient multiplies that by its fan-in: |k| / sqrt(D) per element for dq, |q| / sqrt(D) for dk, the H
+    heads for dmask and the N sequences for dpair; rounding to the storage format cannot enlarge a bound
+    that is representable."""
+    got, delta, _ = run_bwd(torch, w, dout)
+    want = oracle.bwd(w.q, w.k, w.v, w.mask, w.pair, dout, dtype=w.dtype, nthreads=THREADS)
+    B, N, L, H, D = w.shape
+    for name, r in zip(NAMES, want):
+        if name != "dv":
+            assert r is None or not r.any(), f"oracle {name} is not identically zero for one key"
+    compare_grads([None, None, got[2], None, None], [None, None, want[2], None, None], w.dtype, w.name)
+    f = lambda x: S.storage_to_f32(x, w.dtype).astype(np.float64)
+    u = 2.0 ** -24
+    gamma = D * u / (1 - D * u)
+    ds = 2 * gamma * np.abs(f(dout) * f(w.v)).sum(axis=-1)        # [B,N,1,H] bound on |dS|
+    bounds = {"dq": ds[..., None] * np.abs(f(w.k)) / np.sqrt(D),
+              "dk": ds[..., None] * np.abs(f(w.q)) / np.sqrt(D),
+              "dmask": ds.sum(axis=-1).reshape(B, N, 1, 1, 1),
+              "dpair": ds.sum(axis=1).reshape(B, 1, H, 1, 1)}
+    for name, g in zip(NAMES, got):
+        if name in bounds and g is not None:
+            excess = np.abs(g) - bounds[name]
+            say(f"  {w.name} {name}: max|g|={np.abs(g).max():.3e} within the cancellation bound: {(excess <= 0).all()}")
+            assert (excess <= 0).all(), f"{w.name} {name}: exceeds the cancellation bound by {excess.max():.3e}"
+    compare_delta(delta, w, dout, w.name)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
@@ -315,6 +351,43 @@ def test_bwd_pair_gradient_split_over_n(torch_dev, dtype, L):
     single = parity(torch_dev, w, dout, use_ws=False)
     for a, b in zip(split[:4], single[:4]):
         np.testing.assert_array_equal(a, b)   # only the pair gradient takes another route
+
+
+# ---------------------------------------------------------------------------
+# L % 8 != 0 on the matrix cores: the bias tiles are staged through registers,
+# the pair gradient's workspace rows are padded to a multiple of 4 keys, and
+# the last partial group of 4 keys of every bias and bias-gradient row is read
+# and written element by element.  Large biases sit on the last element of
+# every pair matrix and mask row (and on the first key of the last pair row).
+# ---------------------------------------------------------------------------
+def with_edge_biases(w):
+    pf = S.storage_to_f32(w.pair, w.dtype).copy()
+    pf[..., -1, -1] = 4.0
+    pf[..., -1, 0] = -3.0
+    mf = S.storage_to_f32(w.mask, w.dtype).copy()
+    mf[..., -1] = 2.0
+    w.pair, w.mask = S.to_storage(pf, w.dtype), S.to_storage(mf, w.dtype)
+    return w
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("L", [9, 63, 99, 130])
+def test_bwd_odd_L_split_over_n(torch_dev, dtype, L):
+    """With and without the workspace; only the pair gradient takes another route."""
+    w = with_edge_biases(S.random_problem(1, 24, L, 3, 32, dtype=dtype, seed=L + 70, mask="tail", pair="normal",
+                                          mask_frac=0.2))
+    dout = S.random_dout(w.shape, dtype, seed=L + 71)
+    split = parity(torch_dev, w, dout)
+    single = parity(torch_dev, w, dout, use_ws=False)
+    for a, b in zip(split[:4], single[:4]):
+        np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [8, 16, 64])
+def test_bwd_odd_L_other_head_dims(torch_dev, d, dtype):
+    w = with_edge_biases(S.random_problem(1, 16, 77, 2, d, dtype=dtype, seed=d + 90, mask="tail", pair="normal"))
+    parity(torch_dev, w, S.random_dout(w.shape, dtype, seed=d + 91))
 
 
 def test_bwd_workspace_deterministic(torch_dev):
