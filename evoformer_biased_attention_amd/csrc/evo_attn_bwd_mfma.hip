@@ -442,7 +442,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
 //   q, dO: half hh, slot 4*row + (chunk ^ ((row >> 2) & 3)), row = query of the block, chunk = 8 d-values
 //   pt:    slot (8 KT)*row + (chunk ^ 2(row & (4 KT - 1))), chunk = 8 of the workgroup's keys
 //   ls:    lse * log2(e) of the block's queries (+inf past L or for a row without softmax)
-//   dl:    delta of the block's queries
+//   dl:    -delta of the block's queries (the accumulator input of dP)
 // Queries past L read as zero rows with ls = +inf, so they add nothing; keys
 // past L are computed on zero rows and never stored.
 // ---------------------------------------------------------------------------
@@ -550,7 +550,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
             const int i = q0 + lane;
             const int64_t row = (bn * p.H + h) * st.lrow + i;
             lsv = i < L ? lse_base2(p.lse[row]) : INFINITY;
-            dlv = i < L ? p.delta[row] : 0.f;
+            dlv = i < L ? -p.delta[row] : 0.f;  // negated: the accumulator input of dP
         }
     };
     auto put_rows = [&](KvBuf<QS, kDH, KT>* __restrict__ dst) {
@@ -630,7 +630,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
         f32x4 sc[QT][KT], dp[QT][KT];
         for (int qt = 0; qt < QT; ++qt)
             for (int t = 0; t < KT; ++t) {
-                sc[qt][t] = dp[qt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                sc[qt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                dp[qt][t] = f32x4{dlq[qt].x, dlq[qt].y, dlq[qt].z, dlq[qt].w};  // -delta: dP - delta comes out
                 for (int hh = 0; hh < kDH; ++hh) {
                     sc[qt][t] = E::mfma(aq[qt][hh], kop[t][hh], sc[qt][t]);
                     dp[qt][t] = E::mfma(ado[qt][hh], vop[t][hh], dp[qt][t]);
@@ -642,7 +643,6 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
             uint32_t wp[2 * QT], wd[2 * QT];
             for (int qt = 0; qt < QT; ++qt) {
                 const float lsr[4] = {lsq[qt].x, lsq[qt].y, lsq[qt].z, lsq[qt].w};
-                const float dlr[4] = {dlq[qt].x, dlq[qt].y, dlq[qt].z, dlq[qt].w};
                 float bias[4] = {0.f, 0.f, 0.f, 0.f};
                 if (PAIR) {
                     const f32x2 a01 = unpack2<E>(pb[qt][t].x), a23 = unpack2<E>(pb[qt][t].y);
@@ -652,7 +652,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
                 for (int r = 0; r < 4; ++r) {
                     const float x = fmaf(sc[qt][t][r], p.c1, fmaf(bias[r], kLog2e, mk[t] - lsr[r]));
                     pr[r] = __builtin_amdgcn_exp2f(x);
-                    ds[r] = pr[r] * (dp[qt][t][r] - dlr[r]);
+                    ds[r] = pr[r] * dp[qt][t][r];
                     dm[t] += ds[r];
                 }
                 wp[2 * qt] = pack2<E>(pr[0], pr[1]);
@@ -821,14 +821,15 @@ __global__ __launch_bounds__(kZW * 64, 1) void bwd_dpair_mfma(Params p) {
                     m2[0] = a[0] * kLog2e, m2[1] = a[1] * kLog2e, m2[2] = bb[0] * kLog2e, m2[3] = bb[1] * kLog2e;
                 }
                 for (int qt = 0; qt < kZQ; ++qt) {
-                    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+                    const float ndl = -cur.dl[qt];  // dP starts from -delta
+                    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{ndl, ndl, ndl, ndl};
                     for (int hh = 0; hh < kDH; ++hh) {
                         sc = E::mfma(cur.k[kt][hh], cur.q[qt][hh], sc);
                         dp = E::mfma(cur.v[kt][hh], cur.d[qt][hh], dp);
                     }
                     for (int r = 0; r < 4; ++r) {
                         const float x = fmaf(sc[r], p.c1, pb[qt][kt][r]) + (m2[r] - cur.ls[qt]);
-                        acc[qt][kt][r] = fmaf(__builtin_amdgcn_exp2f(x), dp[r] - cur.dl[qt], acc[qt][kt][r]);
+                        acc[qt][kt][r] = fmaf(__builtin_amdgcn_exp2f(x), dp[r], acc[qt][kt][r]);
                     }
                 }
             }
@@ -875,7 +876,7 @@ hipError_t launch_dpair(Params p, int64_t B, hipStream_t stream) {
 // partial sum (fp32) to the workspace; bwd_dpair_reduce then adds the chunks
 // in chunk order.  LDS per step, with the swizzle of the dq kernel:
 //   q, dout, k, v: slot 4*row + (chunk ^ ((row >> 2) & 3)), row of the tile, chunk = 8 d-values
-//   mt: the tile's 64 mask values; ls, dl: lse * log2(e) and delta of the tile's queries
+//   mt: the tile's 64 mask values; ls, dl: lse * log2(e) and -delta of the tile's queries
 // ---------------------------------------------------------------------------
 template <int DH>
 struct PairBuf {
@@ -977,7 +978,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
             const int i = i0 + lane;
             const int64_t row = ((b * N + n) * p.H + h) * st.lrow + i;
             lsv = i < L ? lse_base2(p.lse[row]) : INFINITY;
-            dlv = i < L ? p.delta[row] : 0.f;
+            dlv = i < L ? -p.delta[row] : 0.f;  // negated: the accumulator input of dP
         }
     };
     auto put_rows = [&](Buf* __restrict__ dst) {
@@ -1016,7 +1017,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
         const float lsq = cur->ls[16 * wave + c], dlq = cur->dl[16 * wave + c];
         if (n + 1 < n1) copy_step(n + 1, nxt);
         for (int kt = 0; kt < kKT; ++kt) {
-            f32x4 sc = pbs[kt], dp = f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 sc = pbs[kt], dp = f32x4{dlq, dlq, dlq, dlq};  // -delta: dP - delta comes out
             for (int hh = 0; hh < kDH; ++hh) {
                 sc = E::mfma(kop[kt][hh], qop[hh], sc);
                 dp = E::mfma(vop[kt][hh], dop[hh], dp);
@@ -1028,7 +1029,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
             }
             for (int r = 0; r < 4; ++r) {
                 const float x = fmaf(sc[r], p.c1, MASK ? fmaf(mraw[r], kLog2e, -lsq) : -lsq);
-                acc[kt][r] = fmaf(__builtin_amdgcn_exp2f(x), dp[r] - dlq, acc[kt][r]);
+                acc[kt][r] = fmaf(__builtin_amdgcn_exp2f(x), dp[r], acc[kt][r]);
             }
         }
         if (n + 1 < n1) put_rows(nxt);
