@@ -309,6 +309,92 @@ def bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, want_dmask=True, want_dpa
     return dq, dk, dv, dmask, dpair, delta
 
 
+# ---------------------------------------------------------------------------
+# Differentiable call.  The pages' interface takes Q, K, V and a list of at
+# most two biases (None where a bias is absent), the first broadcast like
+# [B, N, 1, 1, L] (one key mask per sequence), the second like
+# [B, 1, H, L, L] (one pair bias per head), and returns O; gradients flow to
+# Q, K, V and to each bias that requires one.  Both passes are the C ABI's
+# (evo_attn_fwd_strided, evo_attn_bwd_strided), so views such as the
+# transposed tensors of ending-node or column attention need no copies.
+# ---------------------------------------------------------------------------
+def _check_biases(q, biases):
+    """(mask_bias, pair_bias) from the bias list; raises ValueError for a list of more than two or a bias of
+    the wrong shape, dtype or device, before anything is launched."""
+    biases = list(biases) if biases is not None else []
+    if len(biases) > 2:
+        raise ValueError("at most two biases: [mask_bias [B,N,1,1,L], pair_bias [B,1,H,L,L]]")
+    biases += [None] * (2 - len(biases))
+    B, N, L, H, D = q.shape
+    want = {0: (B, N, 1, 1, L), 1: (B, 1, H, L, L)}
+    for i, b in enumerate(biases):
+        if b is None:
+            continue
+        if tuple(b.shape) != want[i]:
+            raise ValueError(f"bias {i} must have shape {want[i]}, not {tuple(b.shape)}")
+        if b.dtype != q.dtype or b.device != q.device:
+            raise ValueError(f"bias {i} must have q's dtype and device")
+        if b.stride(4) != 1:
+            raise ValueError(f"bias {i}: keys must be contiguous")
+    return biases[0], biases[1]
+
+
+_FN = None
+
+
+def _function():
+    """The torch.autograd.Function (built on first use, so that importing this package needs no torch)."""
+    global _FN
+    if _FN is not None:
+        return _FN
+    import torch
+
+    class EvoformerAttentionFn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, mask_bias, pair_bias):
+            B, N, L, H, D = q.shape
+            out = torch.empty_like(q)  # q's strides when q is dense, else contiguous
+            if out.stride(4) != 1:
+                out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+            lse = torch.empty((B, N, H, L), dtype=torch.float32, device=q.device)
+            lay = layout_of(q, k, v, out, mask_bias, pair_bias)
+            st = evo_attn_fwd_strided(q, k, v, mask_bias, pair_bias, out, lse, lay, (B, N, L, H, D),
+                                      torch_dtype_code(q.dtype), torch.cuda.current_stream(q.device).cuda_stream)
+            if st != EVO_OK:
+                raise EvoAttnError(st)
+            ctx.save_for_backward(q, k, v, mask_bias, pair_bias, out, lse)
+            return out
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, mask_bias, pair_bias, out, lse = ctx.saved_tensors
+            if tuple(dout.stride()) != tuple(out.stride()):
+                d = torch.empty_strided(out.size(), out.stride(), dtype=out.dtype, device=out.device)
+                d.copy_(dout)
+                dout = d
+            need = ctx.needs_input_grad
+            dq, dk, dv, dm, dp, _ = bwd(q, k, v, mask_bias, pair_bias, out, lse, dout,
+                                        want_dmask=mask_bias is not None and need[3],
+                                        want_dpair=pair_bias is not None and need[4])
+            return dq, dk, dv, dm, dp
+
+    _FN = EvoformerAttentionFn
+    return _FN
+
+
+def evoformer_attention(q, k, v, biases=()):
+    """O = softmax(Q K^T / sqrt(D) + mask_bias + pair_bias) V over the keys of each (b, n, h), differentiable.
+
+    q, k, v: [B, N, L, H, D] device tensors (head dimension contiguous; any other strides, e.g. a
+    transposed view); biases: a list of at most two tensors or None, [mask_bias [B,N,1,1,L],
+    pair_bias [B,1,H,L,L]], of q's dtype (keys contiguous).  Returns O, [B,N,L,H,D], in q's dtype.
+    Gradients reach q, k, v and every bias with requires_grad; a bias gradient is computed only then.
+    Raises ValueError for a bad bias list and EvoAttnError for a status other than EVO_OK.
+    """
+    mask_bias, pair_bias = _check_biases(q, biases)
+    return _function().apply(q, k, v, mask_bias, pair_bias)
+
+
 def evo_trimul_check(a, w, x, shape, direction, dtype) -> int:
     """Host-only validation of the triangle multiplication; shape is (B, C, L)."""
     return _lib.evo_trimul_check(_addr(a), _addr(w), _addr(x), ctypes.byref(EvoTrimulShape(*[int(v) for v in shape])),

@@ -444,3 +444,21 @@ def test_trimul_errors():
     assert tcheck(x=x + 8) == E.EVO_ERR_MISALIGNED
     assert tcheck(dtype=E.EVO_DTYPE_F32) == E.EVO_ERR_UNSUPPORTED
     assert tcheck(shape=(1, 1, 32768)) == E.EVO_ERR_UNSUPPORTED        # L * L * 2 = 2^31
+
+
+# ---------------------------------------------------------------------------
+# evoformer_attention: the bias list is checked on the host before any launch
+# ---------------------------------------------------------------------------
+def test_evoformer_attention_bias_list_checks():
+    import torch
+    q = torch.zeros(1, 2, 5, 3, 8, dtype=torch.bfloat16)
+    mask = torch.zeros(1, 2, 1, 1, 5, dtype=torch.bfloat16)
+    pair = torch.zeros(1, 1, 3, 5, 5, dtype=torch.bfloat16)
+    bad = [[mask, pair, None],                                   # more than two
+           [torch.zeros(1, 2, 1, 1, 4, dtype=torch.bfloat16)],   # wrong mask shape
+           [None, torch.zeros(1, 3, 1, 5, 5, dtype=torch.bfloat16)],  # pair in the mask's place of heads
+           [None, pair.float()],                                 # another dtype
+           [torch.zeros(1, 2, 1, 1, 10, dtype=torch.bfloat16)[..., ::2]]]  # keys not contiguous
+    for biases in bad:
+        with pytest.raises(ValueError):
+            E.evoformer_attention(q, q, q, biases)
