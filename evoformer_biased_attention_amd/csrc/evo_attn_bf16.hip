@@ -291,7 +291,7 @@ __device__ inline uint4 bload16_any(Rsrc r, uint32_t off, uint32_t range) {
 // Fast path.  Returns false (for the whole workgroup) when some row produced
 // a NaN, i.e. a bias held +-inf; nothing has been written in that case.
 // Requires L * H * D * 2 < 2^31 and L * L * 2 < 2^31.  STAGED: the bias rows
-// are not 16-byte aligned (L % 8 != 0, or unaligned bias strides); their
+// are not 16-byte aligned (bias strides not multiples of 8 elements); their
 // tiles then go global -> registers -> LDS, with unaligned 16-byte loads,
 // instead of straight into LDS.
 // ---------------------------------------------------------------------------
@@ -318,8 +318,14 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
     const Rsrc rq = make_rsrc(p.q + s.qb, (uint32_t)(L - 1) * rowq + D * 2);
     const Rsrc rk = make_rsrc(p.k + s.kb, (uint32_t)(L - 1) * rowk + D * 2);
     const Rsrc rv = make_rsrc(p.v + s.vb, (uint32_t)(L - 1) * rowv + D * 2);
-    const Rsrc rp = make_rsrc(PAIR ? s.pbase : p.q, PAIR ? (uint32_t)(L - 1) * rowp + (uint32_t)L * 2u : 0u);  // prange
-    const Rsrc rm = make_rsrc(MASK ? s.mrow : p.q, MASK ? (uint32_t)L * 2u : 0u);
+    // Bias buffers.  Direct copies (aligned rows): the range ends at the
+    // 16-byte boundary after the last element, so that the last row's final
+    // chunk is read whole even when L % 8 != 0 (its elements past the row are
+    // keys past L; that granule lies in the page of the last element).
+    // STAGED: the exact range, which the element-wise reads at its end need.
+    const uint32_t pbytes = (uint32_t)(L - 1) * rowp + (uint32_t)L * 2u, mbytes = (uint32_t)L * 2u;
+    const Rsrc rp = make_rsrc(PAIR ? s.pbase : p.q, PAIR ? (STAGED ? pbytes : (pbytes + 15u) & ~15u) : 0u);
+    const Rsrc rm = make_rsrc(MASK ? s.mrow : p.q, MASK ? (STAGED ? mbytes : (mbytes + 15u) & ~15u) : 0u);
 
     // Identity A operand: slot (g, e) stands for key 8*(g%2) + e of a 16-key
     // tile, weighted by the high (g < 2) or low (g >= 2) part of sqrt(D).
@@ -370,7 +376,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
     // STAGED: the pair and mask chunks in flight between a block's copy and
     // its landing in LDS
     uint4 pstage[4], mstage;
-    const uint32_t prange = PAIR ? (uint32_t)(L - 1) * rowp + (uint32_t)L * 2u : 0u;
+    const uint32_t prange = PAIR ? pbytes : 0u;
     auto copy_block = [&](int blk, Buf* __restrict__ dst) {
         const uint32_t k0 = (uint32_t)blk * kKB;
         for (int hh = 0; hh < kDH; ++hh) {
@@ -380,7 +386,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
         if (STAGED) {
             if (PAIR)
                 for (int j = 0; j < 4; ++j) pstage[j] = bload16_any(rp, pvo[j] + k0 * 2u, prange);
-            if (MASK && wave == 0 && lane < 8) mstage = bload16_any(rm, 16u * lane + k0 * 2u, (uint32_t)L * 2u);
+            if (MASK && wave == 0 && lane < 8) mstage = bload16_any(rm, 16u * lane + k0 * 2u, mbytes);
         } else {
             if (PAIR)
                 for (int j = 0; j < 4; ++j) dma16(rp, &dst->pt[64 * (4 * wave + j)], pvo[j] + k0 * 2u, 0);
@@ -756,14 +762,17 @@ hipError_t launch_variant(Params& p, hipStream_t stream) {
                            dim3((unsigned)p.total), dim3(kWaves * 64), args, 0, stream);
 }
 
-// The direct copies of bias rows into LDS need 16-byte aligned rows (L % 8
-// == 0 and aligned bias strides); other rows are staged through registers.
+// The direct copies of bias rows into LDS need rows that start 16-byte
+// aligned (bias strides multiples of 8 elements; the tensors themselves are
+// 16-byte aligned), for any L; other rows are staged through registers.  A
+// caller with L % 8 != 0 gets the direct copies by passing biases whose rows
+// are padded to a multiple of 8 elements.
 template <class E, int D, bool PAIR, bool MASK>
 hipError_t launch_biases(Params& p, hipStream_t stream) {
     const bool aligned = (!PAIR || (p.st.pb % 8 == 0 && p.st.ph % 8 == 0 && p.st.pi % 8 == 0)) &&
                          (!MASK || (p.st.mb % 8 == 0 && p.st.mn % 8 == 0));
-    return p.L % 8 == 0 && aligned ? launch_variant<E, D, PAIR, MASK, false>(p, stream)
-                                   : launch_variant<E, D, PAIR, MASK, true>(p, stream);
+    return aligned ? launch_variant<E, D, PAIR, MASK, false>(p, stream)
+                   : launch_variant<E, D, PAIR, MASK, true>(p, stream);
 }
 
 template <class E, int D>

@@ -129,6 +129,14 @@ __device__ inline uint4 bload16_any(Rsrc r, uint32_t off, uint32_t range) {
     return uint4{w[0], w[1], w[2], w[3]};
 }
 
+// Byte range of a bias buffer of `bytes` bytes.  Direct copies need rows
+// that start 16-byte aligned; their range ends at the 16-byte boundary after
+// the last element, so that the last row's final chunk is read whole also
+// when L % 8 != 0 (its elements past the row are keys past L, never used;
+// that granule lies in the page of the last element).  Staged copies keep
+// the exact range, which their element-wise reads at its end need.
+__device__ inline uint32_t bias_range(uint32_t bytes, bool staged) { return staged ? bytes : (bytes + 15u) & ~15u; }
+
 // Four consecutive 16-bit values at p of which the first n lie inside their
 // row (n >= 1; the rest read as zero), at any 2-byte alignment.
 __device__ inline uint2 load4(const u16* p, int n) {
@@ -213,8 +221,8 @@ struct DqBuf {
     uint4 mt[8];
 };
 
-// STAGED: bias rows not 16-byte aligned (L % 8 != 0 or unaligned bias
-// strides); their tiles go global -> registers -> LDS through unaligned
+// STAGED: bias rows not 16-byte aligned (bias strides not multiples of 8
+// elements); their tiles go global -> registers -> LDS through unaligned
 // 16-byte loads, into the slots the direct copies would fill.
 template <class E, int D, bool PAIR, bool MASK, bool STAGED>
 __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
@@ -250,8 +258,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
     const Rsrc rv = make_rsrc(p.v + vs, last * rowv + D * 2);
     const Rsrc rdo = make_rsrc(p.dout + os, last * rowo + D * 2);
     const Rsrc ro = make_rsrc(p.out + os, last * rowo + D * 2);
-    const Rsrc rp = make_rsrc(PAIR ? p.pair + b * st.pb + h * st.ph : p.q, PAIR ? last * rowp + (uint32_t)L * 2u : 0u);
-    const Rsrc rm = make_rsrc(MASK ? p.mask + b * st.mb + n * st.mn : p.q, MASK ? (uint32_t)L * 2u : 0u);
+    // bias buffers: direct copies read whole 16-byte granules at the end (bias_range)
+    const Rsrc rp = make_rsrc(PAIR ? p.pair + b * st.pb + h * st.ph : p.q,
+                              PAIR ? bias_range(last * rowp + (uint32_t)L * 2u, STAGED) : 0u);
+    const Rsrc rm = make_rsrc(MASK ? p.mask + b * st.mb + n * st.mn : p.q, MASK ? bias_range((uint32_t)L * 2u, STAGED) : 0u);
 
     const int q0 = (int)qb * kBlockRows + wave * kWaveRows;
     // B operands of S^T = K.Q^T and dP^T = V.dO^T: lane (c + 16g) holds row
@@ -540,7 +550,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
         dma16(rdo, &dst->dout[qhh][64 * qrg], dooff + (uint32_t)q0 * rowo + (uint32_t)h * ho, 0);
         if (PAIR) {
             const uint32_t prange = last * rowp + (uint32_t)L * 2u;
-            const Rsrc rp = make_rsrc(p.pair + b * st.pb + h * st.ph, prange);
+            const Rsrc rp = make_rsrc(p.pair + b * st.pb + h * st.ph, bias_range(prange, STAGED));
             for (int j = 0; j < PCW; ++j) {
                 if (STAGED) pstage[j] = bload16_any(rp, pvo[j] + (uint32_t)q0 * rowp, prange);
                 else dma16(rp, &dst->pt[64 * (PCW * wave + j)], pvo[j] + (uint32_t)q0 * rowp, 0);
@@ -970,7 +980,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
             dma16(rv, &dst->v[hh][64 * wave], voff[hh], 0);
         }
         if (MASK && wave == 0 && lane < 8) {
-            const Rsrc rm = make_rsrc(p.mask + b * st.mb + n * st.mn, (uint32_t)L * 2u);
+            const Rsrc rm = make_rsrc(p.mask + b * st.mb + n * st.mn, bias_range((uint32_t)L * 2u, STAGED));
             if (STAGED) mstage = bload16_any(rm, (uint32_t)j0 * 2u + 16u * lane, (uint32_t)L * 2u);
             else dma16(rm, &dst->mt[0], (uint32_t)j0 * 2u + 16u * lane, 0);
         }
@@ -1141,10 +1151,10 @@ hipError_t launch_dim(const BwdArgs& a, unsigned stages, hipStream_t stream) {
     p.scale = (float)(1.0 / std::sqrt((double)D));
     p.st = a.st;
     const bool pair = a.pair != nullptr, mask = a.mask != nullptr;
-    // bias rows copied in 16-byte pieces straight into LDS need 16-byte
-    // alignment; other rows are staged through registers
+    // bias rows copied in 16-byte pieces straight into LDS need rows that
+    // start 16-byte aligned (any L); other rows are staged through registers
     const Strides& s = a.st;
-    const bool staged = a.L % 8 || (pair && (s.pb % 8 || s.ph % 8 || s.pi % 8)) || (mask && (s.mb % 8 || s.mn % 8));
+    const bool staged = (pair && (s.pb % 8 || s.ph % 8 || s.pi % 8)) || (mask && (s.mb % 8 || s.mn % 8));
     hipError_t e = hipSuccess;
     if (stages & kStageDq) {
         if (staged) {

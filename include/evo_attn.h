@@ -116,9 +116,17 @@ evo_status_t evo_attn_fwd(const void* q, const void* k, const void* v, const voi
  *                  rows, >= L); keys contiguous
  *   lse_row        elements between the lse rows of consecutive (b, n, h),
  *                  >= L (the guide's padded layout is ceil(L/32)*32, section 5.4)
- * Every stride other than lse_row must be a multiple of 16 bytes
- * (EVO_ERR_MISALIGNED) and non-negative (EVO_ERR_BAD_SHAPE); out's strides
- * must give distinct elements distinct addresses (EVO_ERR_ALIASING).
+ * The strides of q, k, v and out must be multiples of 16 bytes
+ * (EVO_ERR_MISALIGNED); every stride must be non-negative (EVO_ERR_BAD_SHAPE);
+ * out's strides must give distinct elements distinct addresses
+ * (EVO_ERR_ALIASING).  Bias strides may take any value.  Bias rows that start
+ * 16-byte aligned (mask and pair strides multiples of 8 elements) are copied
+ * straight into on-chip memory, for any L; other rows (such as dense biases
+ * with L % 8 != 0) take a slower staged copy.  A caller with L % 8 != 0 can
+ * keep the fast copies by padding the bias rows to a multiple of 8 elements:
+ * the padding is read (as keys past L, never weighted) but not written, and
+ * padding that holds NaN or inf only sends the affected work to the exact
+ * path.
  */
 typedef struct {
     int64_t q[4], k[4], v[4], out[4];

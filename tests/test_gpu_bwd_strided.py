@@ -168,6 +168,36 @@ def test_unaligned_bias_rows(torch_dev, L, use_ws):
     assert torch.isnan(full[..., L:, :]).all() and torch.isnan(full[..., :L, L:]).all()
 
 
+@pytest.mark.parametrize("use_ws", [True, False], ids=["workspace", "no_workspace"])
+@pytest.mark.parametrize("L,fill", [(77, 0.0), (99, float("nan"))], ids=["77-zeros", "99-nan"])
+def test_padded_bias_rows_any_L(torch_dev, L, fill, use_ws):
+    """L % 8 != 0 with the pair and mask rows (and so their gradients' rows) padded to a multiple of 8
+    elements: the bias tiles are copied straight into LDS, each row's last chunk read whole with its
+    padding (NaN in one case), and the gradients leave the padding alone."""
+    torch = torch_dev
+    B, N, H, D = 1, 24, 2, 32
+    dtype = "bf16"
+    Lp = (L + 7) // 8 * 8
+    w = S.random_problem(B, N, L, H, D, dtype=dtype, seed=L + 800, mask="tail", pair="normal")
+    dout = S.random_dout(w.shape, dtype, seed=L + 801)
+    fill_bits = S.to_storage(np.full(1, fill, np.float32), dtype)[0]
+    wide = np.full((B, 1, H, L, Lp), fill_bits, np.uint16)
+    wide[..., :L] = w.pair
+    pair_full = to_dev(torch, wide, dtype)
+    pair = pair_full[..., :L]
+    wide_m = np.full((B, N, 1, 1, Lp), fill_bits, np.uint16)
+    wide_m[..., :L] = w.mask
+    mask = to_dev(torch, wide_m, dtype)[..., :L]
+    q, k, v, do = (to_dev(torch, x, dtype) for x in (w.q, w.k, w.v, dout))
+    dpair_store = torch.empty_like(pair_full).reshape(-1)
+    got, delta, raw = strided_bwd(torch, q, k, v, mask, pair, do, use_ws=use_ws, pair_storage=dpair_store)
+    want = oracle.bwd(w.q, w.k, w.v, w.mask, w.pair, dout, dtype=dtype, nthreads=THREADS)
+    compare_grads(got, want, dtype, f"padded bias rows L={L} fill={fill}, workspace={use_ws}")
+    compare_delta(delta, w, dout, "padded bias rows")
+    full = dpair_store.view(B, 1, H, L, Lp).float()
+    assert torch.isnan(full[..., L:]).all()
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_head_major_layout_runs_and_matches(torch_dev, dtype):
     """Q/K/V/dO as views of [B, N, H, L, D] (heads outermost): rows do not span every head, so the 16-bit

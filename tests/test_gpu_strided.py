@@ -138,6 +138,32 @@ def test_unaligned_bias_rows(torch_dev, L, dtype):
     compare(o, l, ro, rl, dtype, f"unaligned bias rows L={L}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("L,fill", [(77, 0.0), (99, 0.0), (130, 0.0), (77, float("nan")), (77, float("inf"))],
+                         ids=["77-zeros", "99-zeros", "130-zeros", "77-nan", "77-inf"])
+def test_padded_bias_rows_any_L(torch_dev, L, fill, dtype):
+    """L % 8 != 0 with bias rows padded to a multiple of 8 elements: the rows start 16-byte aligned, so
+    the bias tiles are copied straight into LDS and each row's last chunk is read whole, padding (keys
+    past L) included.  Padding that holds NaN or inf turns the identity product's zeros into NaN; the
+    workgroups that meet it redo their slice on the exact path, with the same results."""
+    torch = torch_dev
+    B, N, H, D = 1, 3, 2, 32
+    Lp = (L + 7) // 8 * 8
+    w = S.random_problem(B, N, L, H, D, dtype=dtype, seed=L + 700, mask="tail", pair="normal")
+    fill_bits = S.to_storage(np.full(1, fill, np.float32), dtype)[0]
+    wide_p = np.full((B, 1, H, L, Lp), fill_bits, np.uint16)
+    wide_p[..., :L] = w.pair
+    wide_m = np.full((B, N, 1, 1, Lp), fill_bits, np.uint16)
+    wide_m[..., :L] = w.mask
+    pair = to_dev(torch, wide_p, dtype)[..., :L]
+    mask = to_dev(torch, wide_m, dtype)[..., :L]
+    q, k, v = (to_dev(torch, x, dtype) for x in (w.q, w.k, w.v))
+    out = torch.full_like(q, float("nan"))
+    o, l, _ = gpu_strided(torch, q, k, v, mask, pair, out)
+    ro, rl = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype=dtype, nthreads=THREADS)
+    compare(o, l, ro, rl, dtype, f"padded bias rows L={L} fill={fill}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_dense_layout_through_strided_entry_is_identical(torch_dev, dtype):
     torch = torch_dev
