@@ -581,13 +581,14 @@ def _counter_means(directory, counter, name_part):
     return sum(vals.values()) / len(vals), len(vals)
 
 
-TRAFFIC_COMMANDS = [
-    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof_fetch -o tri -- python3 bench.py "
-    "--steps 5 --warmup 1 --no-cpu-baseline --no-warm --spinup-seconds 0 --copy-probe-mib 256",
-    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof_write -o tri -- python3 bench.py "
-    "--steps 5 --warmup 1 --no-cpu-baseline --no-warm --spinup-seconds 0 --copy-probe-mib 256",
-    "python3 bench.py --summarize-traffic gpurun_out/prof_fetch gpurun_out/prof_write --copy-probe-mib 256",
-]
+def traffic_commands(fetch_dir, write_dir, probe_mib):
+    """The three commands behind a traffic summary: one counter run per counter (each writes its CSV under
+    the given directory), then this summary."""
+    run = (f"-o tri -- python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-warm --spinup-seconds 0 "
+           f"--copy-probe-mib {probe_mib}")
+    return [f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} {run}",
+            f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} {run}",
+            f"python3 bench.py --summarize-traffic {fetch_dir} {write_dir} --copy-probe-mib {probe_mib}"]
 
 
 def summarize_traffic(workload, probe_mib, fetch_dir, write_dir):
@@ -613,7 +614,7 @@ def summarize_traffic(workload, probe_mib, fetch_dir, write_dir):
     B, N, L, H, D = w.shape
     out = {
         "workload": w.name,
-        "commands": TRAFFIC_COMMANDS,
+        "commands": traffic_commands(fetch_dir, write_dir, probe_mib),
         "note": "FETCH_SIZE's formula counts a 128-byte read request as 64 bytes on this device; the copy "
                 "probe (all 128-byte requests) reads back half its size, hence fetch_scale ~2",
         "kernel_name_contains": kname,
