@@ -390,8 +390,9 @@ hipError_t launch_valu(const BwdArgs& a, int dtype, unsigned stages, hipStream_t
 }  // namespace
 
 // The matrix-core kernels take the stages they implement for the shapes
-// they accept (16-bit formats, D <= 32, L % 8 == 0); the vector-ALU kernels
-// take the rest.  The dq stage goes first in either case: it writes delta.
+// they accept (16-bit formats, D in {8, 16, 32, 64}, q/k/v/out rows 16-byte
+// aligned, any L); the vector-ALU kernels take the rest (fp32).  The dq
+// stage goes first in either case: it writes delta.
 hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t stream) {
     const unsigned mfma = bwd_mfma_eligible(a, dtype) ? kBwdMfmaStages : 0u;
     hipError_t e = hipSuccess;
