@@ -15,8 +15,10 @@
 //    A-side operand (columns i): a 16x16 result leaves j = 4g + 0..3 and
 //    i = c in lane c + 16g, so every lane stores 4 consecutive j of one row i
 //    (8 bytes).
-//  * Workgroup = 4 waves, a 128 x 128 tile of one plane (wave w: j rows
-//    64(w/2) .., i columns 64(w%2) ..; 4 x 4 MFMA tiles, 64 accumulators).
+//  * Workgroup = 8 waves, a 128 x 128 tile of one plane (wave w: j rows
+//    64(w%2) .., i columns 32(w/2) ..; 4 x 2 MFMA tiles, 32 accumulators),
+//    two workgroups per CU.  Four waves with 64 x 64 each measured 6 % slower:
+//    the steps are latency-bound and more waves hide more of it.
 //    The result leaves through LDS so that every store is a 16-byte piece of
 //    a whole 128-byte row segment, written non-temporally.
 //    The contraction runs over k in steps of 64; both operand tiles of a
@@ -152,12 +154,16 @@ __device__ inline int tm_swz(int row) {
     return KS == 64 ? (row & 7) : ((row >> 2) & 3);
 }
 
+constexpr int kNW = 8;  // waves per workgroup
+// Two workgroups per CU (64 KB of LDS each), so the launch bound asks for
+// four waves per SIMD (at most 128 VGPRs).
 template <class E, bool INCOMING, int KS, bool STAGED>
-__global__ __launch_bounds__(256, KS == 64 ? 2 : 3) void trimul_kernel(TmParams p) {
+__global__ __launch_bounds__(64 * kNW, 4) void trimul_kernel(TmParams p) {
     using V8 = typename E::v8;
-    constexpr int CPR = KS / 8;        // outgoing: 16-byte chunks per tile row
-    constexpr int SEG = KS / 16;       // 1 KB copy segments per wave per operand per step
-    constexpr int KC = KS / 32;        // 32-wide contraction chunks per step
+    constexpr int CPR = KS / 8;              // outgoing: 16-byte chunks per tile row
+    constexpr int SEG = KS * 4 / 16 / kNW;   // 1 KB copy segments per wave per operand per step
+    constexpr int KC = KS / 32;              // 32-wide contraction chunks per step
+    constexpr int NT = 2;                    // 16-wide i tiles per wave (j tiles: 4)
     __shared__ __attribute__((aligned(16))) TmBuf<KS> sm[2];
 
     const int64_t id = logical_block(blockIdx.x, p.total);
@@ -171,7 +177,7 @@ __global__ __launch_bounds__(256, KS == 64 ? 2 : 3) void trimul_kernel(TmParams 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
-    const int wm = wave >> 1, wn = wave & 1;  // the wave's j rows 64 wm .., i columns 64 wn ..
+    const int wm = wave & 1, wn = wave >> 1;  // the wave's j rows 64 wm .., i columns 16 NT wn ..
     const int nsteps = (L + KS - 1) / KS;
 
     // per-lane copy offsets of step 0 (k0 added per step); segment s = SEG wave + q
@@ -230,9 +236,9 @@ __global__ __launch_bounds__(256, KS == 64 ? 2 : 3) void trimul_kernel(TmParams 
         }
     };
 
-    f32x4 acc[4][4];  // [m tile (j)][n tile (i)]
+    f32x4 acc[4][NT];  // [m tile (j)][n tile (i)]
     for (int mt = 0; mt < 4; ++mt)
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     copy_step(0, &sm[0]);
     land_step(&sm[0]);
@@ -246,49 +252,51 @@ __global__ __launch_bounds__(256, KS == 64 ? 2 : 3) void trimul_kernel(TmParams 
         for (int kc = 0; kc < KC; ++kc)
             for (int q = 0; q < 4; ++q) {
                 if (!INCOMING) {
-                    const int rj = 64 * wm + 16 * q + c, ri = 64 * wn + 16 * q + c, chunk = 4 * kc + g;
+                    const int rj = 64 * wm + 16 * q + c, ri = 16 * NT * wn + 16 * q + c, chunk = 4 * kc + g;
                     aop[kc][q] = as_v8<E>(cur->w[CPR * rj + (chunk ^ tm_swz<KS>(rj))]);
-                    bop[kc][q] = as_v8<E>(cur->a[CPR * ri + (chunk ^ tm_swz<KS>(ri))]);
+                    if (q < NT) bop[kc][q] = as_v8<E>(cur->a[CPR * ri + (chunk ^ tm_swz<KS>(ri))]);
                 } else {
                     // lane c + 16g addresses k row 32kc + 4g + c/4 (and 16 further), columns 4(c%4) .. +3 of
                     // the 16-column group; it receives column c of k rows 32kc + 4g + 0..3 and + 16
                     const int kr = 32 * kc + 4 * g + (c >> 2);
-                    const int colj = 64 * wm + 16 * q + 4 * (c & 3), coli = 64 * wn + 16 * q + 4 * (c & 3);
+                    const int colj = 64 * wm + 16 * q + 4 * (c & 3), coli = 16 * NT * wn + 16 * q + 4 * (c & 3);
                     const char* bw = reinterpret_cast<const char*>(cur->w);
                     const char* ba = reinterpret_cast<const char*>(cur->a);
                     auto addr = [&](const char* base, int k, int col) {
                         return base + 16 * (16 * k + ((col >> 3) ^ (2 * (k & 7)))) + 2 * (col & 7);
                     };
                     const uint2 wl = ds_read_tr(addr(bw, kr, colj)), wh = ds_read_tr(addr(bw, kr + 16, colj));
-                    const uint2 al = ds_read_tr(addr(ba, kr, coli)), ah = ds_read_tr(addr(ba, kr + 16, coli));
                     aop[kc][q] = as_v8<E>(uint4{wl.x, wl.y, wh.x, wh.y});
-                    bop[kc][q] = as_v8<E>(uint4{al.x, al.y, ah.x, ah.y});
+                    if (q < NT) {
+                        const uint2 al = ds_read_tr(addr(ba, kr, coli)), ah = ds_read_tr(addr(ba, kr + 16, coli));
+                        bop[kc][q] = as_v8<E>(uint4{al.x, al.y, ah.x, ah.y});
+                    }
                 }
             }
         if (st + 1 < nsteps) copy_step(st + 1, &sm[(st & 1) ^ 1]);
         for (int kc = 0; kc < KC; ++kc)
             for (int mt = 0; mt < 4; ++mt)
-                for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = E::mfma(aop[kc][mt], bop[kc][nt], acc[mt][nt]);
+                for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = E::mfma(aop[kc][mt], bop[kc][nt], acc[mt][nt]);
         if (st + 1 < nsteps) land_step(&sm[(st & 1) ^ 1]);
         wait_all();
         __syncthreads();
     }
 
-    // Epilogue through LDS: lane c + 16g holds X^T[j = 64 wm + 16 mt + 4g + r][i = 64 wn + 16 nt + c]; each
-    // wave writes its 64 x 64 block of x as [i][j] rows (padded to 72 against bank conflicts), then stores
+    // Epilogue through LDS: lane c + 16g holds X^T[j = 64 wm + 16 mt + 4g + r][i = 32 wn + 16 nt + c]; each
+    // wave writes its 32 (i) x 64 (j) block of x as [i][j] rows (padded to 72 against bank conflicts), then stores
     // whole 128-byte row segments, 16 bytes per lane.  The operand buffers are free (the loop ended with a
     // barrier) and each wave reads back only what it wrote.
     constexpr int kRow = 72;
-    static_assert(4 * 64 * kRow * 2 <= (int)sizeof(sm), "epilogue tile fits the operand buffers");
-    u16* tile = reinterpret_cast<u16*>(&sm[0]) + wave * 64 * kRow;
-    for (int nt = 0; nt < 4; ++nt)
+    static_assert(kNW * 16 * NT * kRow * 2 <= (int)sizeof(sm), "epilogue tile fits the operand buffers");
+    u16* tile = reinterpret_cast<u16*>(&sm[0]) + wave * 16 * NT * kRow;
+    for (int nt = 0; nt < NT; ++nt)
         for (int mt = 0; mt < 4; ++mt)
             *reinterpret_cast<uint2*>(tile + (16 * nt + c) * kRow + 16 * mt + 4 * g) =
                 uint2{pack2<E>(acc[mt][nt][0], acc[mt][nt][1]), pack2<E>(acc[mt][nt][2], acc[mt][nt][3])};
     // x is not read again here: streaming (non-temporal) stores
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const int ib = i0 + 64 * wn, jc = j0 + 64 * wm + 8 * (lane & 7);
-    for (int pass = 0; pass < 8; ++pass) {
+    const int ib = i0 + 16 * NT * wn, jc = j0 + 64 * wm + 8 * (lane & 7);
+    for (int pass = 0; pass < 2 * NT; ++pass) {
         const int row = 8 * pass + (lane >> 3);
         const u32x4 v = *reinterpret_cast<const u32x4*>(tile + row * kRow + 8 * (lane & 7));
         if (ib + row < L && jc < L) {
@@ -304,14 +312,14 @@ __global__ __launch_bounds__(256, KS == 64 ? 2 : 3) void trimul_kernel(TmParams 
     }
 }
 
-constexpr int kKStep = 64;  // contraction step (a 32-wide step measured no faster and leaves too little LDS for the epilogue)
+constexpr int kKStep = 64;  // contraction step (a 32-wide step with three workgroups per CU measured no faster overall)
 
 template <class E, bool INCOMING>
 hipError_t launch(TmParams& p, hipStream_t stream) {
     void* args[] = {&p};
     const void* k = p.L % 8 ? reinterpret_cast<const void*>(&trimul_kernel<E, INCOMING, kKStep, true>)
                             : reinterpret_cast<const void*>(&trimul_kernel<E, INCOMING, kKStep, false>);
-    return hipLaunchKernel(k, dim3((unsigned)p.total), dim3(256), args, 0, stream);
+    return hipLaunchKernel(k, dim3((unsigned)p.total), dim3(64 * kNW), args, 0, stream);
 }
 
 }  // namespace
