@@ -310,6 +310,23 @@ def pin_row_shift(ref):
     np.testing.assert_allclose(l2[0, :, 0, 2], l[0, :, 0, 2] + 0.75, rtol=1e-6)
 
 
+def pin_all_keys_finite_mask(ref):
+    """Every key of a sequence masked by the same finite -1e9 (stored exactly: f32, and bf16's nearest
+    value): softmax is invariant under a constant shift, so out equals the unmasked result and lse moves
+    by exactly the mask value (fp64 keeps the score differences next to 1e9 to ~1e-7)."""
+    for dtype in ("f32", "bf16"):
+        w = random_problem(1, 3, 11, 2, 8, dtype=dtype, seed=31, mask="zero", pair="normal")
+        o0, l0 = ref(w.q, w.k, w.v, w.mask, w.pair, dtype)
+        mf = np.zeros(storage_to_f32(w.mask, dtype).shape, np.float32)
+        mf[0, 1] = -1e9
+        masked = to_storage(mf, dtype)
+        c = float(storage_to_f32(masked, dtype)[0, 1, 0, 0, 0])  # the stored value of -1e9
+        o1, l1 = ref(w.q, w.k, w.v, masked, w.pair, dtype)
+        np.testing.assert_allclose(o1, o0, rtol=0, atol=1e-6)
+        np.testing.assert_allclose(l1[0, 1], l0[0, 1] + c, rtol=0, atol=1e-6)
+        np.testing.assert_array_equal(l1[0, [0, 2]], l0[0, [0, 2]])
+
+
 def pin_heads_independent(ref):
     """Changing head 0's inputs leaves head 1's outputs bit-identical."""
     w = _pb()
@@ -376,4 +393,5 @@ ALL_PINS = [
     pin_uniform_values, pin_one_boosted_key, pin_two_keys_sigmoid, pin_weights_via_onehot_values,
     pin_zero_bias_is_plain_attention, pin_permute_n, pin_permute_keys, pin_permute_queries,
     pin_row_shift, pin_heads_independent, pin_split_batch, pin_dtype_widening, pin_all_keys_neg_inf,
+    pin_all_keys_finite_mask,
 ]
