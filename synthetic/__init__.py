@@ -92,7 +92,9 @@ def random_problem(B, N, L, H, D, dtype="bf16", seed=0, mask="tail", pair="norma
     mask: None | "tail" (per-sequence random tail of up to mask_frac*L keys set
           to -1e9) | "random" (each key removed with probability mask_frac) |
           "normal" (N(0, bias_scale^2) values, no removal) | "zero".
-    pair: None | "normal" (N(0, bias_scale^2)) | "zero".
+    pair: None | "normal" (N(0, bias_scale^2)) | "zero" | "int8" (k / 32 for
+          uniform int8 k: exact in every storage format and cheap to draw for
+          pair matrices of ~10^9 elements, filled in bands of rows).
     """
     ss = np.random.SeedSequence(seed)
     rq, rk, rv, rm, rp = [np.random.default_rng(s) for s in ss.spawn(5)]
@@ -122,6 +124,15 @@ def random_problem(B, N, L, H, D, dtype="bf16", seed=0, mask="tail", pair="norma
             p = to_storage(bias_scale * _normal(rp, (B, 1, H, L, L)), dtype)
         elif pair == "zero":
             p = to_storage(np.zeros((B, 1, H, L, L), np.float32), dtype)
+        elif pair == "int8":
+            p = np.empty((B, 1, H, L, L), np.float32 if dtype == "f32" else np.uint16)
+            band = 2048
+            for b in range(B):
+                for h in range(H):
+                    for r0 in range(0, L, band):
+                        r1 = min(L, r0 + band)
+                        k8 = rp.integers(-128, 128, size=(r1 - r0, L), dtype=np.int8)
+                        p[b, 0, h, r0:r1] = to_storage(k8.astype(np.float32) / 32, dtype)
         else:
             raise ValueError(pair)
     return Workload(f"random_{B}x{N}x{L}x{H}x{D}_{dtype}", dtype, (B, N, L, H, D), q, k, v, m, p,

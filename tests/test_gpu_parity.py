@@ -121,6 +121,16 @@ def test_workload_full_oracle(torch_dev, c):
     parity_full(torch_dev, S.workload(c))
 
 
+@pytest.mark.parametrize("L", [32760, 32767])
+def test_longest_pair_rows(torch_dev, L):
+    """The longest sequences whose pair matrix keeps every byte offset of the 16-bit kernel in 32 bits
+    ((L - 1) * 2L + 2L < 2^31; L = 32768 is rejected): L = 32760 has 16-byte aligned rows (direct copies),
+    L = 32767 does not (rows staged through registers).  One 2 GiB pair matrix, 512 blocks of keys per row."""
+    say(f"longest pair rows: L = {L}")
+    w = S.random_problem(1, 1, L, 1, 32, dtype="bf16", seed=L, mask="tail", pair="int8")
+    parity_sampled(torch_dev, w, count=256)
+
+
 @pytest.mark.parametrize("c", [3, 5])
 def test_workload_sampled_rows(torch_dev, c):
     say(f"workload {c}: sampled-row oracle comparison")

@@ -30,6 +30,17 @@ def test_deterministic():
         np.testing.assert_array_equal(x, y)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_int8_pair_bias_is_exact(dtype):
+    w = S.random_problem(2, 1, 37, 3, 8, dtype=dtype, seed=11, pair="int8")
+    pf = S.storage_to_f32(w.pair, dtype).astype(np.float64)
+    k = pf * 32
+    np.testing.assert_array_equal(k, np.round(k))          # every value is k / 32 exactly
+    assert k.min() >= -128 and k.max() <= 127
+    assert len(np.unique(k)) > 200                          # and the int8 range is used
+    np.testing.assert_array_equal(w.pair, S.random_problem(2, 1, 37, 3, 8, dtype=dtype, seed=11, pair="int8").pair)
+
+
 @pytest.mark.parametrize("c", [1, 2, 4])
 def test_workload_recipes(c):
     w = S.workload(c)
