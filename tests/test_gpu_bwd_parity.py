@@ -301,6 +301,15 @@ def test_bwd_workload_full(torch_dev, c):
     parity(torch_dev, w, S.random_dout(w.shape, w.dtype, seed=100 + c))
 
 
+@pytest.mark.parametrize("L", [4096, 4093])
+def test_bwd_long_rows(torch_dev, L):
+    """Rows of 64 blocks of keys: L = 4096 (aligned bias rows) and L = 4093 (bias rows staged through
+    registers, a partial group of 4 keys at every row's end), four sequences sharing one pair matrix."""
+    w = S.random_problem(1, 4, L, 1, 32, dtype="bf16", seed=4000 + L, mask="tail", pair="normal", mask_frac=0.1)
+    say(f"long rows backward: L = {L}")
+    parity(torch_dev, w, S.random_dout(w.shape, "bf16", seed=L))
+
+
 def test_bwd_ds4sci_unit_test_shape(torch_dev):
     """The guide's unit test checks every gradient on (1,256,256,4,32) with both biases (section 4)."""
     w = S.random_problem(1, 256, 256, 4, 32, dtype="f16", seed=4053, mask="tail", pair="normal", mask_frac=0.1)
