@@ -272,6 +272,17 @@ def _lse_row(lse, B, N, H, L):
     return row
 
 
+def _self_overlapping(t) -> bool:
+    """Whether two distinct indices of t share an address (a broadcast view such as expand()'s stride 0)."""
+    axes = sorted((st, n) for st, n in zip(t.stride(), t.shape) if n > 1)
+    reach = 1
+    for st, n in axes:
+        if st < reach:
+            return True
+        reach += (n - 1) * st
+    return False
+
+
 def bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, want_dmask=True, want_dpair=True, stream=None,
         workspace=True):
     """torch convenience wrapper around evo_attn_bwd_strided: allocates the gradients (each with the
@@ -281,10 +292,15 @@ def bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, want_dmask=True, want_dpa
 
     out and lse are the forward pass's results for the same inputs; dout must have out's strides.
     Returns (dq, dk, dv, dmask_bias or None, dpair_bias or None, delta); a bias gradient is computed
-    only when that bias is given and wanted.  Raises EvoAttnError for any status other than EVO_OK.
+    only when that bias is given and wanted.  A wanted bias gradient needs a bias whose elements have
+    distinct addresses (a broadcast view's gradient would collide with itself): ValueError otherwise.
+    Raises EvoAttnError for any status other than EVO_OK.
     """
     import torch
     B, N, L, H, D = q.shape
+    for name, t, want in (("mask_bias", mask_bias, want_dmask), ("pair_bias", pair_bias, want_dpair)):
+        if t is not None and want and _self_overlapping(t):
+            raise ValueError(f"{name} is a broadcast view: its gradient needs a bias with distinct elements")
     if tuple(dout.stride()) != tuple(out.stride()):
         raise ValueError("dout must have the strides of out")
     row = _lse_row(lse, B, N, H, L)
@@ -392,6 +408,13 @@ def evoformer_attention(q, k, v, biases=()):
     Raises ValueError for a bad bias list and EvoAttnError for a status other than EVO_OK.
     """
     mask_bias, pair_bias = _check_biases(q, biases)
+    # A broadcast bias (e.g. a mask expand()ed over N) that needs a gradient is
+    # materialised first: its gradient then has one element per position, and
+    # autograd sums it back over the broadcast axes.
+    if mask_bias is not None and mask_bias.requires_grad and _self_overlapping(mask_bias):
+        mask_bias = mask_bias.contiguous()
+    if pair_bias is not None and pair_bias.requires_grad and _self_overlapping(pair_bias):
+        pair_bias = pair_bias.contiguous()
     return _function().apply(q, k, v, mask_bias, pair_bias)
 
 

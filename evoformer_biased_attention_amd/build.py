@@ -36,10 +36,7 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP/C++ source of the library into libevoattn.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,6 +47,28 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP/C++ source of the library into libevoattn.so (always recompiles).
+
+    Each source becomes an object of its own, compiled in parallel (at most MAX_JOBS, default the
+    CPU count, at most 16), and the objects are linked into the library."""
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = os.path.join(os.path.dirname(PKG), "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    jobs = max(1, min(16, int(os.environ.get("MAX_JOBS", os.cpu_count() or 1)), len(SOURCES)))
+    # the largest sources first, so that they do not start last
+    order = sorted(range(len(SOURCES)), key=lambda i: -os.path.getsize(os.path.join(CSRC, SOURCES[i])))
+    with ThreadPoolExecutor(jobs) as ex:
+        futs = [ex.submit(_run, [hipcc(), *compile_flags, "-c", "-o", objs[i], os.path.join(CSRC, SOURCES[i])],
+                          verbose) for i in order]
+        for f in futs:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -70,11 +70,13 @@ bool dim_supported(evo_dtype_t dt, int64_t D) {
     return dt == EVO_DTYPE_F32 && (D == 8 || D == 16 || D == 32 || D == 64);
 }
 
-bool offsets_fit(evo_dtype_t dt, const evo_shape_t& s, const evo_layout_t& lay) {
+// The pair rows count only when a pair bias is given: without one the kernel
+// forms no pair offset.
+bool offsets_fit(evo_dtype_t dt, const evo_shape_t& s, const evo_layout_t& lay, bool pair) {
     if (dt == EVO_DTYPE_F32) return true;
     const int64_t L = s.L, D = s.D;
     return rows_fit(L, lay.q[2], D * 2) && rows_fit(L, lay.k[2], D * 2) && rows_fit(L, lay.v[2], D * 2) &&
-           rows_fit(L, lay.pair_i, L * 2);
+           (!pair || rows_fit(L, lay.pair_i, L * 2));
 }
 
 // Largest element offset + 1 over axes {(size, stride)}, or -1 past 2^62.
@@ -199,7 +201,7 @@ extern "C" evo_status_t evo_attn_check_strided(const void* q, const void* k, con
     for (const int64_t* t : qkvo)
         for (int a = 0; a < 4; ++a)
             if ((t[a] * es) % 16) return EVO_ERR_MISALIGNED;
-    if (!offsets_fit(dtype, s, lay)) return EVO_ERR_UNSUPPORTED;
+    if (!offsets_fit(dtype, s, lay, pair_bias != nullptr)) return EVO_ERR_UNSUPPORTED;
     return EVO_OK;
 }
 

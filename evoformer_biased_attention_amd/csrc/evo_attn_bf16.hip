@@ -288,8 +288,9 @@ __device__ inline uint4 bload16_any(Rsrc r, uint32_t off, uint32_t range) {
 }
 
 // ---------------------------------------------------------------------------
-// Fast path.  Returns false (for the whole workgroup) when some row produced
-// a NaN, i.e. a bias held +-inf; nothing has been written in that case.
+// Fast path.  Returns false (for the whole workgroup) when some row sum ended
+// outside [2^-8, inf) (a bias of +-inf, or a row whose keys all carry one
+// huge finite bias); nothing has been written in that case.
 // Requires L * H * D * 2 < 2^31 and L * L * 2 < 2^31.  STAGED: the bias rows
 // are not 16-byte aligned (bias strides not multiples of 8 elements); their
 // tiles then go global -> registers -> LDS, with unaligned 16-byte loads,
@@ -579,7 +580,12 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
     bool bad = false;
     for (int t = 0; t < kQTiles; ++t) {
         lt[t] = lsum[t];  // every lane of query c holds the full row sum
-        bad |= lt[t] != lt[t];
+        // The key that sets the running maximum adds exp2 of the rounding
+        // error of msub, about 1, so a sound row sum lies in [2^-8, inf).
+        // Outside it: NaN (an infinite bias), or a row whose largest score
+        // is so large in magnitude (a huge finite bias on every key) that
+        // this rounding error itself under- or overflows the exponential.
+        bad |= !(lt[t] >= 0x1p-8f && lt[t] < INFINITY);
     }
     // a sequence whose keys are all masked by -inf: the exact path returns
     // out = 0 and lse = -inf for it

@@ -88,9 +88,10 @@ typedef enum {
  * Supported today: dtype BF16 or F16 with D in {8, 16, 32, 64} (MFMA path; it
  * addresses one head's rows of a slice and the rows of a pair matrix with
  * 32-bit byte offsets, so it needs (L - 1) * H * D * 2 + 2 D < 2^31 and
- * (L - 1) * L * 2 + 2 L < 2^31 (L <= 32767), and rows up to L + 128 below
- * 2^32: (L + 128) * H * D * 2 < 2^32, (L + 128) * L * 2 < 2^32) and dtype
- * F32 with D in {8, 16, 32, 64}; any B, N, H >= 1 and any L >= 1.
+ * rows up to L + 128 below 2^32, (L + 128) * H * D * 2 < 2^32, and, when a
+ * pair bias is given, (L - 1) * L * 2 + 2 L < 2^31 (L <= 32767) and
+ * (L + 128) * L * 2 < 2^32) and dtype F32 with D in {8, 16, 32, 64}; any
+ * B, N, H >= 1 and any L >= 1.
  * Other valid combinations return EVO_ERR_UNSUPPORTED.
  * A query row whose every score is -inf gets out = 0 and lse = -inf.  In
  * F16 a large negative mask value such as -1e9 is -inf, which is how such
@@ -142,8 +143,8 @@ void evo_attn_dense_layout(const evo_shape_t* shape, evo_layout_t* layout);
  * evo_attn_fwd with explicit strides (see evo_layout_t); every other rule is
  * that of evo_attn_fwd.  Extents for the aliasing check run from each
  * pointer to its tensor's last element.  For bf16 and f16 the row strides of
- * q, k, v and the pair bias must also keep (L + 128) rows below 2^32 bytes
- * (else EVO_ERR_UNSUPPORTED).
+ * q, k, v and (when given) the pair bias must also keep (L + 128) rows below
+ * 2^32 bytes (else EVO_ERR_UNSUPPORTED).
  */
 evo_status_t evo_attn_fwd_strided(const void* q, const void* k, const void* v, const void* mask_bias,
                                   const void* pair_bias, void* out, float* lse, const evo_layout_t* layout,

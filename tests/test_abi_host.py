@@ -140,6 +140,15 @@ def test_bf16_offset_limits():
     assert check(shape=big, mask_bias=None, pair_bias=None, dtype=E.EVO_DTYPE_F32) == E.EVO_OK
 
 
+def test_no_pair_bias_lifts_the_pair_row_limit():
+    """Without a pair bias the kernel forms no pair offset: MSA column attention over more than 32767
+    sequences is accepted, with or without a mask; with a pair bias the same L is rejected."""
+    assert check(shape=(1, 1, 40000, 1, 32), mask_bias=None, pair_bias=None) == E.EVO_OK
+    assert check(shape=(1, 1, 40000, 1, 32), pair_bias=None) == E.EVO_OK
+    assert check(shape=(1, 1, 40000, 1, 32), dtype=E.EVO_DTYPE_F16, pair_bias=None) == E.EVO_OK
+    assert check(shape=(1, 1, 40000, 1, 32)) == E.EVO_ERR_UNSUPPORTED
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     """The product path has no fallback: a missing library is an ImportError."""
     import importlib.util

@@ -48,14 +48,49 @@ def run(torch, w, dout, grad_mask=True, grad_pair=True):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("L", [64, 77])
-def test_autograd_matches_oracle(torch_dev, L, dtype):
-    w = S.random_problem(1, 4, L, 2, 32, dtype=dtype, seed=L + 500, mask="tail", pair="normal")
+@pytest.mark.parametrize("D", [32, 64])
+def test_autograd_matches_oracle(torch_dev, D, L, dtype):
+    """D = 64 chains the 16-bit forward (two 32-wide halves) into the matrix-core backward."""
+    w = S.random_problem(1, 4, L, 2, D, dtype=dtype, seed=L + 500 + D, mask="tail", pair="normal")
     dout = S.random_dout(w.shape, dtype, seed=L + 501)
     o, grads = run(torch_dev, w, dout)
     ro, rl = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype=dtype, nthreads=THREADS)
-    compare(o, None, ro, None, dtype, f"autograd forward L={L}")
+    compare(o, None, ro, None, dtype, f"autograd forward L={L} D={D}")
     want = oracle.bwd(w.q, w.k, w.v, w.mask, w.pair, dout, dtype=dtype, nthreads=THREADS)
-    compare_grads(grads, list(want), dtype, f"autograd L={L}")
+    compare_grads(grads, list(want), dtype, f"autograd L={L} D={D}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_autograd_broadcast_mask(torch_dev, dtype):
+    """A mask given once per batch element and expand()ed over N (stride 0), requiring a gradient: the call
+    materialises it, and the gradient that reaches the [B,1,1,1,L] leaf is the oracle's mask gradient
+    summed over N."""
+    torch = torch_dev
+    import evoformer_biased_attention_amd as E
+    B, N, L, H, D = 1, 5, 72, 2, 32
+    w = S.random_problem(B, N, L, H, D, dtype=dtype, seed=540, mask=None, pair="normal")
+    mf = np.zeros((B, 1, 1, 1, L), np.float32)
+    mf[..., L - 9:] = -1e9
+    mf[..., :5] = np.float32(0.75)
+    base = S.to_storage(mf, dtype)
+    w.mask = np.ascontiguousarray(np.broadcast_to(base, (B, N, 1, 1, L)))
+    dout = S.random_dout(w.shape, dtype, seed=541)
+    q, k, v = (leaf(torch, x, dtype) for x in (w.q, w.k, w.v))
+    mleaf = leaf(torch, base, dtype)
+    pair = leaf(torch, w.pair, dtype, False)
+    out = E.evoformer_attention(q, k, v, [mleaf.expand(B, N, 1, 1, L), pair])
+    (out.float() * to_dev(torch, dout, dtype).float()).sum().backward()
+    torch.cuda.synchronize()
+    ro, _ = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype=dtype, nthreads=THREADS)
+    compare(f64(out.detach()), None, ro, None, dtype, "broadcast mask, forward")
+    want = oracle.bwd(w.q, w.k, w.v, w.mask, w.pair, dout, dtype=dtype, nthreads=THREADS)
+    got = [f64(q.grad), f64(k.grad), f64(v.grad), f64(mleaf.grad)]
+    compare_grads(got, [want[0], want[1], want[2], want[3].sum(axis=1, keepdims=True)], dtype,
+                  "broadcast mask")
+    # the low-level wrapper refuses to write a gradient into a broadcast view
+    with pytest.raises(ValueError):
+        E.bwd(q.detach(), k.detach(), v.detach(), mleaf.detach().expand(B, N, 1, 1, L), None, out.detach(),
+              torch.zeros((B, N, H, L), dtype=torch.float32, device="cuda"), to_dev(torch, dout, dtype))
 
 
 def test_autograd_bias_gradients_only_on_request(torch_dev):

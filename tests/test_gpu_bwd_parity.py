@@ -1,10 +1,11 @@
 """Backward pass: HIP path vs the fp64 oracle, element by element, through the C ABI.
 
-The HIP backward takes the forward pass's out and lse.  Where the forward
-supports the dtype and head dimension they come from the HIP forward (the
-pipeline a caller runs); otherwise (bf16/f16 with D = 64) from the oracle,
-rounded to the storage format.  The oracle recomputes everything from q, k, v,
-the biases and dO in fp64 and never sees a GPU value.
+The HIP backward takes the forward pass's out and lse, from the HIP forward
+(the pipeline a caller runs) unless a test asks for the oracle's, rounded to
+the storage format.  The oracle recomputes everything from q, k, v, the biases
+and dO in fp64 and never sees a GPU value.  Every comparison prints its
+normalised errors, and the largest per dtype and gradient is printed when the
+module ends (the measured margin under each bound).
 
 Tolerances, per gradient tensor G, as errors normalised by max|G_ref|:
   f32:  max <= 1e-4, mean <= 1e-5
@@ -80,7 +81,19 @@ def f64(t):
 
 
 def fwd_supported(dtype, D):
-    return D in (8, 16, 32) or (dtype == "f32" and D == 64)
+    return D in (8, 16, 32, 64)
+
+
+# largest normalised error seen per (dtype, gradient), printed when the module ends
+WORST = {}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def report_worst():
+    yield
+    for (dtype, name), (mx, mean, what) in sorted(WORST.items()):
+        say(f"largest {dtype} {name}: max|d|/max|ref|={mx:.3e} (bound {TOL[dtype]['max']:.1e}, {what}); "
+            f"largest mean {mean:.3e} (bound {TOL[dtype]['mean']:.1e})")
 
 
 def run_bwd(torch, w, dout, want_dmask=True, want_dpair=True, fwd_from_oracle=False, stream=None, use_ws=True):
@@ -129,6 +142,9 @@ def compare_grads(got, want, dtype, what):
         err = np.abs(g - r) / scale
         msg = f"{what} {name}: max|d|/max|ref|={err.max():.3e} mean={err.mean():.3e} (max|ref|={scale:.3e})"
         say("  " + msg)
+        prev = WORST.get((dtype, name), (0.0, 0.0, ""))
+        WORST[(dtype, name)] = (max(prev[0], err.max()), max(prev[1], err.mean()),
+                                what if err.max() > prev[0] else prev[2])
         assert err.max() <= tol["max"], msg
         assert err.mean() <= tol["mean"], msg
 
