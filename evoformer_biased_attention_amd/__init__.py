@@ -20,13 +20,14 @@ LIB_PATH = os.path.join(_HERE, "libevoattn.so")
 
 EVO_DTYPE_F32, EVO_DTYPE_BF16, EVO_DTYPE_F16 = 0, 1, 2
 (EVO_OK, EVO_ERR_NULL_POINTER, EVO_ERR_BAD_SHAPE, EVO_ERR_BAD_DTYPE, EVO_ERR_MISALIGNED, EVO_ERR_ALIASING,
- EVO_ERR_UNSUPPORTED, EVO_ERR_HIP, EVO_ERR_NO_BIAS) = range(9)
+ EVO_ERR_UNSUPPORTED, EVO_ERR_HIP, EVO_ERR_NO_BIAS, EVO_ERR_SCRATCH) = range(10)
 
 # Symbols declared in include/evo_attn.h.
 EXPORTED = ("evo_attn_fwd", "evo_attn_check", "evo_attn_fwd_strided", "evo_attn_check_strided",
             "evo_attn_dense_layout", "evo_attn_bwd", "evo_attn_bwd_check", "evo_attn_bwd_workspace_size",
             "evo_attn_bwd_strided", "evo_attn_bwd_check_strided",
-            "evo_trimul", "evo_trimul_check", "evo_status_string", "evo_attn_last_hip_error")
+            "evo_trimul", "evo_trimul_check", "evo_status_string", "evo_attn_last_hip_error",
+            "evo_attn_bwd_noalloc", "evo_attn_bwd_noalloc_scratch_bytes", "evo_attn_bwd_noalloc_last_hip_error")
 EVO_TRIMUL_OUTGOING, EVO_TRIMUL_INCOMING = 0, 1
 
 
@@ -100,6 +101,12 @@ def _load():
     lib.evo_status_string.argtypes = [ctypes.c_int]
     lib.evo_attn_last_hip_error.restype = ctypes.c_int
     lib.evo_attn_last_hip_error.argtypes = []
+    lib.evo_attn_bwd_noalloc.restype = ctypes.c_int
+    lib.evo_attn_bwd_noalloc.argtypes = [vp] * 14 + [ctypes.POINTER(EvoShape), ctypes.c_int, vp]
+    lib.evo_attn_bwd_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    lib.evo_attn_bwd_noalloc_scratch_bytes.argtypes = []
+    lib.evo_attn_bwd_noalloc_last_hip_error.restype = ctypes.c_int
+    lib.evo_attn_bwd_noalloc_last_hip_error.argtypes = []
     return lib
 
 
@@ -165,6 +172,20 @@ def evo_attn_bwd(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmas
     return _lib.evo_attn_bwd(*[_addr(x) for x in (q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv,
                                                  dmask_bias, dpair_bias, delta, workspace)],
                              int(workspace_bytes), ctypes.byref(_shape(shape)), int(dtype), stream)
+
+
+def evo_attn_bwd_noalloc(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias, dpair_bias, delta,
+                         shape, dtype, stream=None) -> int:
+    """Enqueue the backward pass with the library's static scratch instead of a workspace (no allocation);
+    returns the status code (EVO_ERR_SCRATCH when the shape needs more than the static buffer holds)."""
+    return _lib.evo_attn_bwd_noalloc(*[_addr(x) for x in (q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv,
+                                                         dmask_bias, dpair_bias, delta)],
+                                     ctypes.byref(_shape(shape)), int(dtype), stream)
+
+
+def evo_attn_bwd_noalloc_scratch_bytes() -> int:
+    """Bytes of the static scratch array evo_attn_bwd_noalloc uses on each GPU."""
+    return int(_lib.evo_attn_bwd_noalloc_scratch_bytes())
 
 
 def evo_attn_bwd_check_strided(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv, dmask_bias, dpair_bias,

@@ -455,6 +455,7 @@ extern "C" const char* evo_status_string(evo_status_t status) {
     case EVO_ERR_UNSUPPORTED: return "dtype / head dimension combination not implemented";
     case EVO_ERR_HIP: return "the HIP runtime reported an error at launch";
     case EVO_ERR_NO_BIAS: return "a bias gradient was requested for a bias that was not given";
+    case EVO_ERR_SCRATCH: return "the shape needs more scratch than the library's static buffer holds";
     }
     return "unknown status";
 }

@@ -74,7 +74,9 @@ typedef enum {
     EVO_ERR_ALIASING = 5,     /* an output overlaps an input or another output              */
     EVO_ERR_UNSUPPORTED = 6,  /* valid but not implemented (dtype / head dimension)         */
     EVO_ERR_HIP = 7,          /* the HIP runtime reported an error at launch                */
-    EVO_ERR_NO_BIAS = 8       /* evo_attn_bwd: a bias gradient requested for an absent bias  */
+    EVO_ERR_NO_BIAS = 8,      /* evo_attn_bwd: a bias gradient requested for an absent bias  */
+    EVO_ERR_SCRATCH = 9       /* evo_attn_bwd_noalloc: the shape needs more scratch than the
+                                 library's static buffer holds                              */
 } evo_status_t;
 
 /*
@@ -299,6 +301,34 @@ evo_status_t evo_trimul(const void* a, const void* w, void* x, const evo_trimul_
 /* The validation of evo_trimul alone; host-only. */
 evo_status_t evo_trimul_check(const void* a, const void* w, const void* x, const evo_trimul_shape_t* shape,
                               evo_trimul_direction_t direction, evo_dtype_t dtype);
+
+/*
+ * evo_attn_bwd without a caller workspace and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Arguments and
+ * results are those of evo_attn_bwd with the workspace it recommends
+ * (evo_attn_bwd_workspace_size): the pair gradient's partial sums go to a
+ * static device array of the library instead, of
+ * evo_attn_bwd_noalloc_scratch_bytes() bytes (40 MiB) on every GPU the library
+ * runs on, held until the process ends.  A shape (with a pair gradient
+ * requested) whose recommended workspace exceeds that returns EVO_ERR_SCRATCH
+ * before anything is enqueued; use evo_attn_bwd with a workspace of your own
+ * there.  The call makes no hipMalloc or hipFree; its first call on a device
+ * looks up that device's array address (hipGetSymbolAddress).  Calls on one
+ * GPU share its array: calls that overlap in time on one GPU race on it.
+ * Results are bit-identical to evo_attn_bwd's with the recommended workspace.
+ */
+evo_status_t evo_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* mask_bias,
+                                  const void* pair_bias, const void* out, const float* lse, const void* dout,
+                                  void* dq, void* dk, void* dv, void* dmask_bias, void* dpair_bias, float* delta,
+                                  const evo_shape_t* shape, evo_dtype_t dtype, void* stream);
+
+/* Size in bytes of the static scratch array evo_attn_bwd_noalloc uses on each GPU. */
+size_t evo_attn_bwd_noalloc_scratch_bytes(void);
+
+/* The hipError_t (as an int) of the calling thread's last evo_attn_bwd_noalloc
+ * failure in its own set-up (the scratch address lookup), or 0. */
+int evo_attn_bwd_noalloc_last_hip_error(void);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* evo_status_string(evo_status_t status);

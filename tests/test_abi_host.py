@@ -36,13 +36,13 @@ def test_enum_values_match_header():
     text = _header_text()
     for name in ("EVO_DTYPE_F32", "EVO_DTYPE_BF16", "EVO_DTYPE_F16", "EVO_OK", "EVO_ERR_NULL_POINTER",
                  "EVO_ERR_BAD_SHAPE", "EVO_ERR_BAD_DTYPE", "EVO_ERR_MISALIGNED", "EVO_ERR_ALIASING",
-                 "EVO_ERR_UNSUPPORTED", "EVO_ERR_HIP", "EVO_ERR_NO_BIAS"):
+                 "EVO_ERR_UNSUPPORTED", "EVO_ERR_HIP", "EVO_ERR_NO_BIAS", "EVO_ERR_SCRATCH"):
         m = re.search(rf"\b{name}\s*=\s*(\d+)", text)
         assert m and int(m.group(1)) == getattr(E, name), name
 
 
 def test_status_strings():
-    for s in range(9):
+    for s in range(10):
         assert E.evo_status_string(s) and E.evo_status_string(s) != "unknown status"
     assert E.evo_status_string(99) == "unknown status"
 
@@ -229,6 +229,31 @@ def test_bwd_bad_shape_dtype_unsupported():
     assert bcheck(dtype=7) == E.EVO_ERR_BAD_DTYPE
     for d in (4, 24, 128):
         assert bcheck(shape=(1, 1, 32, 1, d)) == E.EVO_ERR_UNSUPPORTED
+
+
+def test_bwd_noalloc_host_checks():
+    """evo_attn_bwd_noalloc validates on the host before any HIP call: bad arguments return the backward's
+    status codes, and a shape whose recommended workspace exceeds the static scratch returns EVO_ERR_SCRATCH
+    (no GPU is touched on either path)."""
+    a = dict(zip(BWD_NAMES, addrs(len(BWD_NAMES))))
+    names = [n for n in BWD_NAMES if n != "workspace"]
+
+    def call(shape=(1, 2, 64, 4, 32), dtype=E.EVO_DTYPE_BF16, **over):
+        args = dict(a)
+        args.update(over)
+        return E.evo_attn_bwd_noalloc(*[args[n] for n in names], shape, dtype, None)
+
+    cap = E.evo_attn_bwd_noalloc_scratch_bytes()
+    assert cap == 40 << 20
+    # the N = L = 384 triangle-attention shape fits (35.4 MB of partial sums)
+    assert 0 < E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 32), E.EVO_DTYPE_BF16) <= cap
+    assert call(q=None) == E.EVO_ERR_NULL_POINTER
+    assert call(dq=a["q"]) == E.EVO_ERR_ALIASING
+    assert call(mask_bias=None) == E.EVO_ERR_NO_BIAS
+    big = (1, 32, 640, 10, 32)  # 1000 tiles of 64 x 64, three N-chunks: 49.2 MB
+    assert E.evo_attn_bwd_workspace_size(big, E.EVO_DTYPE_BF16) > cap
+    assert call(shape=big) == E.EVO_ERR_SCRATCH
+    assert "static buffer" in E.evo_status_string(E.EVO_ERR_SCRATCH)
 
 
 def test_bwd_workspace_rules():
