@@ -43,91 +43,20 @@
 #include <cstdint>
 
 #include "evo_attn_launch.h"
+#include "gfx950_common.h"
 
 namespace evo {
 namespace {
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint16_t u16;
+using namespace gfx;
 
-constexpr uint32_t kOOB = 0x80000000u;
 constexpr int kTile = 128;  // output tile (i and j) per workgroup
-
-struct Bf16T {
-    typedef __bf16 v8 __attribute__((ext_vector_type(8)));
-    typedef __bf16 v2 __attribute__((ext_vector_type(2)));
-    __device__ static f32x4 mfma(v8 a, v8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
-};
-struct F16T {
-    typedef _Float16 v8 __attribute__((ext_vector_type(8)));
-    typedef _Float16 v2 __attribute__((ext_vector_type(2)));
-    __device__ static f32x4 mfma(v8 a, v8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
-};
-
-template <class E>
-__device__ inline uint32_t pack2(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, typename E::v2));
-}
-
-template <class E>
-__device__ inline typename E::v8 as_v8(uint4 x) { return __builtin_bit_cast(typename E::v8, x); }
-
-// ds_read_b64_tr_b16: with lane a of a 16-lane group addressing row R0 + a/4,
-// columns 4(a%4) .. +3 of a row-major 16-bit matrix, lane i receives column i
-// of rows R0 .. R0+3.
-__device__ inline uint2 ds_read_tr(const void* p) {
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((__attribute__((address_space(3))) char*)p));
-    return __builtin_bit_cast(uint2, r);
-}
-
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-
-__device__ inline Rsrc make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// 16 bytes per lane from the buffer into LDS (lane l at lds + 16 l); the
-// whole offset is per lane, so the range check sees it
-__device__ inline void dma16(Rsrc r, const void* lds, uint32_t voff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, 0, 0, 0);
-}
-
-__device__ inline void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
-
-__device__ inline uint4 bload16(Rsrc r, uint32_t off) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
-}
-
-// 16 bytes at byte offset `off` of a buffer of `range` bytes, any 2-byte
-// alignment.  A chunk that starts inside the range and ends past it is read
-// element by element, so that its elements inside the range keep their
-// values (the range check of a wider load may drop more than the part
-// outside); a chunk wholly past the range reads as zeros either way.
-__device__ inline uint4 bload16_any(Rsrc r, uint32_t off, uint32_t range) {
-    if (off >= range || off + 16u <= range) return bload16(r, off);
-    uint32_t w[4];
-    for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, (int)(off + 4 * e), 0, 0);
-        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, (int)(off + 4 * e + 2), 0, 0);
-        w[e] = lo | (hi << 16);
-    }
-    return uint4{w[0], w[1], w[2], w[3]};
-}
 
 // x with its 16-bit elements e >= n cleared
 __device__ inline uint4 keep_first(uint4 x, int n) {
     uint32_t w[4] = {x.x, x.y, x.z, x.w};
     for (int i = 0; i < 4; ++i) w[i] &= (2 * i < n ? 0xffffu : 0u) | (2 * i + 1 < n ? 0xffff0000u : 0u);
     return uint4{w[0], w[1], w[2], w[3]};
-}
-
-__device__ inline int64_t logical_block(int64_t hw, int64_t total) {
-    const int64_t xcd = hw % 8, j = hw / 8;
-    const int64_t per = total / 8, extra = total % 8;
-    return xcd < extra ? xcd * (per + 1) + j : extra * (per + 1) + (xcd - extra) * per + j;
 }
 
 struct TmParams {
@@ -334,8 +263,8 @@ hipError_t launch_trimul(const void* a, const void* w, void* x, int64_t planes, 
     p.tdim = (L + kTile - 1) / kTile;
     p.total = planes * p.tdim * p.tdim;
     if (p.total >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
-    if (f16) return incoming ? launch<F16T, true>(p, stream) : launch<F16T, false>(p, stream);
-    return incoming ? launch<Bf16T, true>(p, stream) : launch<Bf16T, false>(p, stream);
+    if (f16) return incoming ? launch<F16Fmt, true>(p, stream) : launch<F16Fmt, false>(p, stream);
+    return incoming ? launch<Bf16Fmt, true>(p, stream) : launch<Bf16Fmt, false>(p, stream);
 }
 
 }  // namespace evo
