@@ -5,7 +5,7 @@
 // flight to hide its latency, timed with HIP events over the whole grid (and
 // with the shader clock inside each wave, which gives cycles per instruction).
 //
-// Usage: micro [test ...]   tests: mfma exp fma cvt mix coissue lds dma hbm
+// Usage: micro [test ...]   tests: mfma exp fma cvt mix coissue lds dma dmaissue hbm
 // (no argument: all).  One JSON object per line on stdout.
 #include <hip/hip_runtime.h>
 
@@ -134,7 +134,10 @@ __global__ void k_mix(float* out, int iters, long long* clk) {
 }
 
 // Two kinds of waves in one workgroup of 8: waves 0-3 run MFMAs, waves 4-7
-// exponentials (wave w runs on SIMD w % 4, so each SIMD holds one of each).
+// vector work (wave w runs on SIMD w % 4, so each SIMD holds one of each).
+// KIND of the vector work: 0 exponentials, 1 fma, 2 the softmax mix (per 8
+// values: 8 fma, 8 exponentials, 4 bf16 conversions).
+template <int KIND>
 __global__ void k_coissue(float* out, int iters_mfma, int iters_exp, long long* clk) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     float s = 0.f;
@@ -149,8 +152,19 @@ __global__ void k_coissue(float* out, int iters_mfma, int iters_exp, long long* 
     } else {
         float x[kChains];
         for (int c = 0; c < kChains; ++c) x[c] = 0.01f * (lane + c);
-        for (int i = 0; i < iters_exp; ++i)
-            for (int c = 0; c < kChains; ++c) x[c] = __builtin_amdgcn_exp2f(-x[c]);
+        for (int i = 0; i < iters_exp; ++i) {
+            if (KIND == 0)
+                for (int c = 0; c < kChains; ++c) x[c] = __builtin_amdgcn_exp2f(-x[c]);
+            else if (KIND == 1)
+                for (int c = 0; c < kChains; ++c) x[c] = fmaf(x[c], 0.999f, 0.001f);
+            else {
+                for (int c = 0; c < kChains; ++c) x[c] = __builtin_amdgcn_exp2f(fmaf(x[c], -0.9f, 0.01f));
+                for (int c = 0; c < kChains; c += 2) {
+                    const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x[c], x[c + 1]}, bf16x2));
+                    x[c] = __builtin_bit_cast(float, w & 0xffff0000u);
+                }
+            }
+        }
         for (int c = 0; c < kChains; ++c) s += x[c];
     }
     const long long t1 = clock64();
@@ -199,6 +213,49 @@ __global__ void k_dma(const uint4* src, uint32_t bytes, float* out, int iters, l
     __syncthreads();
     out[blockIdx.x * blockDim.x + tid] = (float)buf[tid & 7][tid].x;
     if (lane == 0) clk[(blockIdx.x * blockDim.x + tid) / 64] = t1 - t0;
+}
+
+// Issue cost of global -> LDS copies: each wave issues 8 copy requests back
+// to back (16 bytes per lane, 1 KB per request, L2-resident source), timing
+// the issue alone with the shader clock; MODE 0: a new LDS address (M0) per
+// request, 1: one M0 for all eight, 2: plain loads into registers instead.
+template <int MODE>
+__global__ void k_dma_issue(const uint4* src, uint32_t bytes, float* out, long long* clk) {
+    __shared__ uint4 buf[8][1024];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(src), (short)0, (int)bytes, 0x00020000);
+    const uint32_t base = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&buf[0][64 * (wave & 15)]);
+    const uint32_t seg = bytes / 1024;
+    uint4 acc = {0u, 0u, 0u, 0u};
+    long long total = 0;
+    for (int rep = 0; rep < 16; ++rep) {
+        const uint32_t off0 = ((uint32_t)(blockIdx.x * 64 + rep * 8 + wave) % seg) * 1024 + 16 * lane;
+        const long long t0 = clock64();
+        if (MODE == 2) {
+            uint4 v[8];
+            for (int u = 0; u < 8; ++u)
+                v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off0 + u * 4096), 0, 0));
+            const long long t1 = clock64();
+            total += t1 - t0;
+            for (int u = 0; u < 8; ++u) acc.x ^= v[u].x ^ v[u].w;
+        } else {
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t m0 = MODE == 0 ? base + (uint32_t)u * 16384u : base;
+                asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                             :
+                             : "s"(m0), "v"(off0 + u * 4096), "s"(r)
+                             : "memory", "m0");
+            }
+            const long long t1 = clock64();
+            total += t1 - t0;
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();
+    out[blockIdx.x * blockDim.x + tid] = (float)(buf[tid & 7][tid].x + acc.x);
+    if (lane == 0) clk[(blockIdx.x * blockDim.x + tid) / 64] = total;
 }
 
 // HBM streaming copy: grid-stride loop of 16-byte loads and stores.
@@ -309,12 +366,14 @@ void test_mix() {
     mix_one<4>();
 }
 
-void test_coissue() {
-    // alone: MFMA waves only (exp loop of 0), exp waves only (MFMA loop of 0), then both
+template <int KIND>
+void coissue_one(const char* kind) {
+    // alone: MFMA waves only (vector loop of 0), vector waves only (MFMA loop of 0), then both
     const int blocks = g_cus, threads = 512;
-    for (auto cfg : {std::pair<int, int>{4096, 0}, {0, 4096}, {4096, 4096}}) {
+    const int vec_iters = KIND == 0 ? 4096 : KIND == 1 ? 16384 : 2048;
+    for (auto cfg : {std::pair<int, int>{4096, 0}, {0, vec_iters}, {4096, vec_iters}}) {
         const double ms = timed([&] {
-            hipLaunchKernelGGL(k_coissue, dim3(blocks), dim3(threads), 0, 0, g_out, cfg.first, cfg.second, g_clk);
+            hipLaunchKernelGGL(k_coissue<KIND>, dim3(blocks), dim3(threads), 0, 0, g_out, cfg.first, cfg.second, g_clk);
         });
         const int waves = blocks * threads / 64;
         std::vector<long long> h(waves);
@@ -322,11 +381,16 @@ void test_coissue() {
         double cm = 0, ce = 0;
         for (int i = 0; i < waves; ++i) ((i % 8) < 4 ? cm : ce) += (double)h[i];
         cm /= waves / 2, ce /= waves / 2;
-        printf("{\"test\": \"coissue\", \"mfma_per_wave\": %d, \"exp_per_wave\": %d, \"ms\": %.4f, "
-               "\"mfma_wave_clk\": %.0f, \"exp_wave_clk\": %.0f}\n",
-               cfg.first * kChains, cfg.second * kChains, ms, cm, ce);
+        printf("{\"test\": \"coissue_%s\", \"mfma_per_wave\": %d, \"vector_iters_per_wave\": %d, \"ms\": %.4f, "
+               "\"mfma_wave_clk\": %.0f, \"vector_wave_clk\": %.0f}\n",
+               kind, cfg.first * kChains, cfg.second, ms, cm, ce);
         fflush(stdout);
     }
+}
+void test_coissue() {
+    coissue_one<0>("exp");
+    coissue_one<1>("fma");
+    coissue_one<2>("softmax_mix");
 }
 
 void test_lds() {
@@ -364,6 +428,28 @@ void test_dma() {
     CHECK(hipFree(src));
 }
 
+template <int MODE>
+void dma_issue_one(const char* mode, const uint4* src, uint32_t bytes) {
+    for (int w : {1, 4, 8, 16}) {
+        const int threads = 64 * w, blocks = g_cus;
+        timed([&] { hipLaunchKernelGGL(k_dma_issue<MODE>, dim3(blocks), dim3(threads), 0, 0, src, bytes, g_out, g_clk); });
+        const double clk = mean_clk(blocks * w);
+        printf("{\"test\": \"dma_issue\", \"mode\": \"%s\", \"waves_per_cu\": %d, "
+               "\"shader_clk_per_8_requests\": %.0f}\n", mode, w, clk / 16);
+        fflush(stdout);
+    }
+}
+void test_dma_issue() {
+    const uint32_t bytes = 4u << 20;
+    uint4* src;
+    CHECK(hipMalloc(&src, bytes));
+    CHECK(hipMemset(src, 1, bytes));
+    dma_issue_one<0>("lds_new_m0", src, bytes);
+    dma_issue_one<1>("lds_same_m0", src, bytes);
+    dma_issue_one<2>("to_registers", src, bytes);
+    CHECK(hipFree(src));
+}
+
 void test_hbm() {
     const size_t bytes = size_t(1) << 30;  // 1 GiB read + 1 GiB written
     uint4 *src, *dst;
@@ -398,7 +484,7 @@ int main(int argc, char** argv) {
     CHECK(hipMalloc(&g_clk, sizeof(long long) * kMaxThreads / 64));
     std::vector<std::string> tests;
     for (int i = 1; i < argc; ++i) tests.push_back(argv[i]);
-    if (tests.empty()) tests = {"mfma", "exp", "fma", "cvt", "mix", "coissue", "lds", "dma", "hbm"};
+    if (tests.empty()) tests = {"mfma", "exp", "fma", "cvt", "mix", "coissue", "lds", "dma", "dmaissue", "hbm"};
     for (const auto& t : tests) {
         if (t == "mfma") test_mfma();
         else if (t == "exp") test_exp();
@@ -409,6 +495,7 @@ int main(int argc, char** argv) {
         else if (t == "lds") test_lds();
         else if (t == "dma") test_dma();
         else if (t == "hbm") test_hbm();
+        else if (t == "dmaissue") test_dma_issue();
         else {
             fprintf(stderr, "unknown test %s\n", t.c_str());
             return 2;
