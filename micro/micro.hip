@@ -109,9 +109,9 @@ __global__ void k_cvt(float* out, int iters, long long* clk) {
 }
 
 // Per iteration: one MFMA (four rotating accumulators) and E independent
-// exponentials in the same wave: does the wave issue the exponentials while
-// the matrix core works?
-template <int E>
+// exponentials (FMA: fma instead) in the same wave: does the wave issue the
+// vector instructions while the matrix core works?
+template <int E, bool FMA = false>
 __global__ void k_mix(float* out, int iters, long long* clk) {
     const int lane = threadIdx.x & 63;
     const bf16x8 a = bf16_operand(lane, 1), b = bf16_operand(lane, 2);
@@ -123,7 +123,10 @@ __global__ void k_mix(float* out, int iters, long long* clk) {
     for (int i = 0; i < iters; i += 4)
         for (int c = 0; c < 4; ++c) {
             acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
-            for (int e = 0; e < E; ++e) x[(c * E + e) % kChains] = __builtin_amdgcn_exp2f(-x[(c * E + e) % kChains]);
+            for (int e = 0; e < E; ++e) {
+                float& y = x[(c * E + e) % kChains];
+                y = FMA ? fmaf(y, 0.999f, 0.001f) : __builtin_amdgcn_exp2f(-y);
+            }
         }
     const long long t1 = clock64();
     float s = 0.f;
@@ -346,16 +349,16 @@ void test_cvt() {
     for (int w : {1, 2, 4}) run_rate("v_cvt_pk_bf16_f32", "cvt/s", 128.0 * kChains, w, 4096, k_cvt, 128);
 }
 
-template <int E>
+template <int E, bool FMA = false>
 void mix_one() {
     for (int w : {1, 2}) {
         const int threads = 256 * w, blocks = g_cus, iters = 8192;
-        const double ms = timed([&] { hipLaunchKernelGGL(k_mix<E>, dim3(blocks), dim3(threads), 0, 0, g_out, iters, g_clk); });
+        const double ms = timed([&] { hipLaunchKernelGGL((k_mix<E, FMA>), dim3(blocks), dim3(threads), 0, 0, g_out, iters, g_clk); });
         const int waves = blocks * threads / 64;
         const double clk = mean_clk(waves);
-        printf("{\"test\": \"mfma_plus_exp\", \"exp_per_mfma\": %d, \"waves_per_simd\": %d, \"ms\": %.4f, "
+        printf("{\"test\": \"mfma_plus_%s\", \"vector_per_mfma\": %d, \"waves_per_simd\": %d, \"ms\": %.4f, "
                "\"clk_per_iter_per_wave\": %.3f, \"simd_clk_per_iter\": %.3f}\n",
-               E, w, ms, clk / iters, clk / iters / w);
+               FMA ? "fma" : "exp", E, w, ms, clk / iters, clk / iters / w);
         fflush(stdout);
     }
 }
@@ -364,6 +367,10 @@ void test_mix() {
     mix_one<1>();
     mix_one<2>();
     mix_one<4>();
+    mix_one<1, true>();
+    mix_one<2, true>();
+    mix_one<4, true>();
+    mix_one<8, true>();
 }
 
 template <int KIND>
