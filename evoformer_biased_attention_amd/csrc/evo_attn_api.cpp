@@ -200,7 +200,7 @@ extern "C" evo_status_t evo_attn_check_strided(const void* q, const void* k, con
     // exact path)
     for (const int64_t* t : qkvo)
         for (int a = 0; a < 4; ++a)
-            if ((t[a] * es) % 16) return EVO_ERR_MISALIGNED;
+            if ((t[a] % 16) * es % 16) return EVO_ERR_MISALIGNED;  // t[a] >= 0; no overflow for any stride
     if (!offsets_fit(dtype, s, lay, pair_bias != nullptr)) return EVO_ERR_UNSUPPORTED;
     return EVO_OK;
 }
@@ -325,7 +325,7 @@ extern "C" evo_status_t evo_attn_bwd_check_strided(const void* q, const void* k,
     // rows of q, k, v and out (and so of their gradients) start 16-byte aligned
     for (const int64_t* t : qkvo)
         for (int a = 0; a < 4; ++a)
-            if ((t[a] * es) % 16) return EVO_ERR_MISALIGNED;
+            if ((t[a] % 16) * es % 16) return EVO_ERR_MISALIGNED;  // t[a] >= 0; no overflow for any stride
     return EVO_OK;
 }
 
@@ -350,7 +350,9 @@ namespace {
 int64_t usable_chunks(const evo::BwdArgs& a, evo_dtype_t dtype, size_t workspace_bytes) {
     if (!evo::bwd_mfma_eligible(a, static_cast<int>(dtype))) return 0;
     const int64_t want = evo::bwd_dpair_chunks(a.B, a.N, a.L, a.H);
-    const int64_t per = a.B * a.H * a.L * evo::bwd_ws_row(a.L) * 4;  // bytes of one chunk's partial sums
+    int64_t per = 4;  // bytes of one chunk's partial sums
+    for (int64_t s : {a.B, a.H, a.L, evo::bwd_ws_row(a.L)}) per = mul_checked(per, s);
+    if (per <= 0) return 0;
     const int64_t fit = static_cast<int64_t>(workspace_bytes / static_cast<size_t>(per));
     const int64_t c = want < fit ? want : fit;
     return c >= 2 ? c : 0;
@@ -361,7 +363,9 @@ int64_t usable_chunks(const evo::BwdArgs& a, evo_dtype_t dtype, size_t workspace
 extern "C" size_t evo_attn_bwd_workspace_size(const evo_shape_t* shape, evo_dtype_t dtype) {
     if (!shape || shape->B < 1 || shape->N < 1 || shape->L < 1 || shape->H < 1 || shape->D < 1) return 0;
     int64_t par = 4;
-    for (int64_t s : {shape->B, shape->H, shape->L, evo::bwd_ws_row(shape->L)}) par = mul_checked(par, s);
+    for (int64_t s : {shape->B, shape->H, shape->L}) par = mul_checked(par, s);
+    if (par < 0) return 0;  // beyond 2^62 bytes; L is now below 2^62, so its rounded row length fits
+    par = mul_checked(par, evo::bwd_ws_row(shape->L));
     if (par < 0) return 0;
     evo_layout_t lay;
     evo_attn_dense_layout(shape, &lay);
