@@ -13,8 +13,11 @@ timed region.  In the default "cold" mode each step reads a different one of R
 copies of the inputs (R chosen so the copies exceed the 256 MB Infinity
 Cache), so every step streams its operands from HBM; "warm" reuses one copy.
 A pair of HIP events on the launch stream brackets the K launches; their
-elapsed time / K is the kernel time used for the roofline.  The fp64 CPU oracle is timed on the host
-cores for the cpu_baseline field.
+elapsed time / K is the kernel time used for the roofline.  After the timed
+region, 100 more launches, each between its own pair of events, give the
+distribution of single-launch times (median, min, p90).  The fp64 CPU oracle
+is timed on the host cores for the cpu_baseline field.  The line also names
+the host CPU model, the GPU and the ROCm / HIP / PyTorch versions.
 
 Prints one JSON line.
 """
@@ -32,6 +35,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, AMD public specification
+# What a loop of independent v_mfma_f32_16x16x32_bf16 sustains on this part, two
+# waves per SIMD on all 256 CUs (micro/micro.hip; profiles/micro_peaks_gfx950.md)
+MEASURED_BF16_MFMA_TFLOPS = 1905.0
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 * 2 ** 20
@@ -41,8 +47,55 @@ KERNEL_SOURCES = {"bf16": "evoformer_biased_attention_amd/csrc/evo_attn_bf16.hip
                   "f32": "evoformer_biased_attention_amd/csrc/evo_attn_f32.hip"}
 
 
+def metric_name(base, workload_name):
+    """The headline metric names the triangle workload (N=L=384); other workloads name themselves."""
+    return base if workload_name == "tri_start_bf16_384" else base.split(", triangle attn")[0] + ", " + workload_name
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def launch_stats(torch, launch, R, n=100):
+    """Distribution of single-launch times: n launches, each bracketed by its own pair of HIP events on the
+    launch stream (the marker packets add a little to each), inputs rotating over the R sets as in the timed
+    region."""
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        launch(i % R)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(1e3 * a.elapsed_time(b) for a, b in evs)
+    pick = lambda q: t[min(n - 1, int(round(q * (n - 1))))]
+    return {"n": n, "median_us": round(pick(0.5), 3), "min_us": round(t[0], 3), "p90_us": round(pick(0.9), 3),
+            "max_us": round(t[-1], 3), "mean_us": round(sum(t) / n, 3)}
+
+
+def environment(torch):
+    """Host CPU model, GPU, and the versions of the tools behind the numbers."""
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    rocm = None
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        if os.path.exists(path):
+            with open(path) as f:
+                rocm = f.read().strip()
+            break
+    props = torch.cuda.get_device_properties(0)
+    return {"cpu_model": cpu, "host_threads": len(os.sched_getaffinity(0)), "gpu": props.name or None,
+            "gcn_arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count,
+            "rocm": rocm, "hip_runtime": torch.version.hip, "torch": torch.__version__,
+            "python": sys.version.split()[0]}
 
 
 def source_hash(dtype):
@@ -214,6 +267,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    stats = launch_stats(torch, launch, R)
+    log(f"bench: single launches median {stats['median_us']} us, min {stats['min_us']}, p90 {stats['p90_us']}")
+
     # secondary: the same launches reading one input set (operands may sit in the Infinity Cache)
     warm = None
     if R > 1 and not args.no_warm:
@@ -229,7 +285,7 @@ def main():
     alg_bytes = algorithmic_bytes(w.shape, w.dtype, w.mask is not None, w.pair is not None)
     traffic = measured_traffic(w.name, w.dtype)
     result = {
-        "metric": METRIC,
+        "metric": metric_name(METRIC, w.name),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -247,11 +303,16 @@ def main():
         "pct_of_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic},
+        "measured_mfma_peak": None if w.dtype == "f32" else {
+            "tflops": MEASURED_BF16_MFMA_TFLOPS, "frac": round(achieved / MEASURED_BF16_MFMA_TFLOPS, 4),
+            "source": "profiles/micro_peaks_gfx950.md"},
         "kernel_us": round(kern_us, 3),
+        "launch_us": stats,
         "hbm": {"algorithmic_bytes": alg_bytes,
                 "achieved_GBps": round(alg_bytes / (kern_us * 1e-6) / 1e9, 1),
                 "frac_of_8TBps": round(alg_bytes / (kern_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
         "warm": warm,
+        "env": environment(torch),
     }
 
     if not args.no_cpu_baseline:
@@ -308,6 +369,7 @@ def bench_trimul(args, torch, E, S):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_us = 1e3 * ev0.elapsed_time(ev1) / args.steps
+    stats = launch_stats(torch, launch, R)
     flops = 2 * B * C * L ** 3
     alg_bytes = set_bytes
     gbs = alg_bytes / (kern_us * 1e-6) / 1e9
@@ -333,6 +395,8 @@ def bench_trimul(args, torch, E, S):
         "kernel_us": round(kern_us, 3),
         "mfma": {"tflops": round(flops / (kern_us * 1e-6) / 1e12, 2),
                  "frac_of_bf16_peak": round(flops / (kern_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "launch_us": stats,
+        "env": environment(torch),
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -411,12 +475,13 @@ def bench_bwd(args, w, dev, torch, E, S):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     pass_us = 1e3 * ev0.elapsed_time(ev1) / args.steps
+    stats = launch_stats(torch, launch, R, n=60)
     flops = 10 * B * N * H * L * L * D
     value = flops * args.steps / wall / 1e12
     achieved = flops / (pass_us * 1e-6) / 1e12
     log(f"bench bwd: {pass_us:.2f} us/pass (events), {achieved:.2f} TFLOP/s")
     result = {
-        "metric": BWD_METRIC,
+        "metric": metric_name(BWD_METRIC, w.name),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -437,7 +502,12 @@ def bench_bwd(args, w, dev, torch, E, S):
                      "peak": PEAK_BF16_TFLOPS if w.dtype != "f32" else PEAK_F32_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / (PEAK_BF16_TFLOPS if w.dtype != "f32" else PEAK_F32_TFLOPS), 4),
                      "traffic": None, "scope": "whole pass"},
+        "measured_mfma_peak": None if w.dtype == "f32" else {
+            "tflops": MEASURED_BF16_MFMA_TFLOPS, "frac": round(achieved / MEASURED_BF16_MFMA_TFLOPS, 4),
+            "source": "profiles/micro_peaks_gfx950.md"},
         "pass_us": round(pass_us, 3),
+        "launch_us": stats,
+        "env": environment(torch),
     }
     if not args.no_cpu_baseline:
         import numpy as np

@@ -20,8 +20,11 @@
 //    contraction), so the addition is exact to ~2^-16 relative and the biases
 //    are consumed in their stored bf16 form.  Accumulator units are
 //    "sqrt(D) * score"; one fma maps them to the base-2 exponent.  A bias of
-//    +-inf would turn the identity's zeros into NaN: a workgroup that sees a
-//    NaN row re-runs its slice on an exact VALU path.
+//    +-inf would turn the identity's zeros into NaN, so -inf in the mask is
+//    first clamped to a finite value whose weight is still exactly zero (see
+//    clamp_neg_inf_bf16 / clamp_neg_inf_f16); any other infinity (+inf, or
+//    -inf in the pair bias) makes a NaN row, and a workgroup that sees one
+//    re-runs its slice on an exact VALU path.
 //  * Online softmax with a lazy maximum.  The item's first block takes its
 //    row maximum before the exponentials; every later block first uses the
 //    running maximum as it stands and checks the block's row sums, which
@@ -131,6 +134,35 @@ __device__ inline uint4 clamp_neg_inf_f16(uint4 x) {
     for (int i = 0; i < 4; ++i)
         w[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_maximum(__builtin_bit_cast(h2, w[i]), lo));
     return uint4{w[0], w[1], w[2], w[3]};
+}
+
+// bfloat16 masks of -inf stay on the fast path too.  Taken as unsigned
+// 16-bit integers, -inf (0xff80) and the NaNs with the sign bit set
+// (0xff81..0xffff) are the only patterns above the most negative finite value
+// (0xff7f, -3.39e38), so one packed unsigned minimum per dword turns -inf into
+// that value.  Its product with the identity weight (sqrt(D) >= 2.8 in its
+// high part) overflows to -inf in fp32: the key takes exactly zero weight
+// with no NaN, and a row whose every key is -inf ends with a zero row sum,
+// which sends it to the exact path (out = 0, lse = -inf).  The negative NaNs
+// the minimum would also turn into -inf are caught beforehand by
+// any_neg_nan_bf16, so NaN still reaches the exact path.
+__device__ inline uint4 clamp_neg_inf_bf16(uint4 x) {
+    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+    const us2 floor2 = {0xff7fu, 0xff7fu};
+    uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    for (int i = 0; i < 4; ++i)
+        w[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(us2, w[i]), floor2));
+    return uint4{w[0], w[1], w[2], w[3]};
+}
+
+// Whether one of the first n bfloat16 values of x is a NaN with the sign bit
+// set (0xff81..0xffff).
+__device__ inline bool any_neg_nan_bf16(uint4 x, int n) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    bool any = false;
+    for (int i = 0; i < 4; ++i)
+        any |= (2 * i < n && (w[i] & 0xffffu) > 0xff80u) || (2 * i + 1 < n && (w[i] >> 16) > 0xff80u);
+    return any;
 }
 
 // Whether one of the first n 16-bit values of x is other than -inf in
@@ -282,6 +314,8 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
 
     // binary16 with a mask: every key of the sequence masked by -inf so far
     bool all_neg_inf = E::kF16 && MASK;
+    // bfloat16 with a mask: a mask NaN with the sign bit set was seen
+    bool mask_neg_nan = false;
 
     copy_block(0, &sm.buf[0]);
     land_block(&sm.buf[0]);
@@ -306,7 +340,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
                 }
             if (MASKON) {
                 uint4 m = b->mt[2 * kt + (g & 1)];
-                if (E::kF16) m = clamp_neg_inf_f16(m);
+                m = E::kF16 ? clamp_neg_inf_f16(m) : clamp_neg_inf_bf16(m);
                 mop[kt] = as_v8<E>(m);
             }
         }
@@ -342,6 +376,8 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
             if (E::kF16)
                 all_neg_inf = all_neg_inf && mask_on &&
                               !wave_any(any_not_neg_inf_f16(mw, L - k0 - 8 * (lane & 7)));
+            else if (mask_on)
+                mask_neg_nan = mask_neg_nan || wave_any(any_neg_nan_bf16(mw, L - k0 - 8 * (lane & 7)));
         }
         if (mask_on) scores(cur, acc, std::true_type{});
         else scores(cur, acc, std::false_type{});
@@ -457,7 +493,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
     }
     // a sequence whose keys are all masked by -inf: the exact path returns
     // out = 0 and lse = -inf for it
-    bad |= all_neg_inf;
+    bad |= all_neg_inf || mask_neg_nan;
     if (__syncthreads_or(bad)) return false;
     for (int t = 0; t < kQTiles; ++t) {
         const int64_t i = s.q0 + 16 * t + c;
@@ -594,7 +630,8 @@ __device__ void run_exact(const Params& p, const Slice& s, ExactSmem& sm, int ti
             const f32x4 o = oacc[t][dh] * inv;
             *reinterpret_cast<uint2*>(dst) = uint2{pack2<E>(o[0], o[1]), pack2<E>(o[2], o[3])};
         }
-        if (s.lrow && g == 0) s.lrow[i] = l > 0.f ? (mrun[t] + __log2f(l)) * kLn2 : -INFINITY;
+        // a row sum of 0 (every key -inf) gives lse = -inf; a NaN one (a NaN bias) stays NaN
+        if (s.lrow && g == 0) s.lrow[i] = l > 0.f ? (mrun[t] + __log2f(l)) * kLn2 : (l == 0.f ? -INFINITY : l);
     }
 }
 

@@ -1,4 +1,4 @@
-// Backward pass on the matrix cores (bf16 / f16, head dimension 8, 16 or 32).
+// Backward pass on the matrix cores (bf16 / f16, head dimension 8, 16, 32 or 64).
 //
 // The gradients (page "DeepSpeed DS4Sci_EvoformerAttention 内核实战指南",
 // hmyw.cn, sections 4 and 5.4: the backward pass recomputes the weights from

@@ -199,6 +199,39 @@ def test_neg_inf_mask_rows(torch_dev):
     compare(o, l, ro, rl, "bf16", "neg-inf mask")
 
 
+@pytest.mark.parametrize("c", [2, 4])
+def test_bf16_neg_inf_tail_masks_on_workloads(torch_dev, c):
+    """The row and triangle workloads with their -1e9 mask entries replaced by -inf (bf16 keeps -inf on the
+    fast path by clamping it), element by element against the full oracle."""
+    w = S.workload(c)
+    mf = S.storage_to_f32(w.mask, "bf16").copy()
+    mf[mf <= -1e8] = -np.inf
+    w.mask = S.to_storage(mf, "bf16")
+    say(f"workload {c} with -inf masks")
+    parity_full(torch_dev, w)
+
+
+@pytest.mark.parametrize("L", [80, 77])
+def test_bf16_nan_mask_values(torch_dev, L):
+    """A NaN in a bf16 mask, with the sign bit set (which the -inf clamp must not turn into -inf) or clear,
+    makes every row of its sequence NaN, as in the definition; the other sequences keep full parity."""
+    B, N, H, D = 1, 4, 2, 32
+    w = S.random_problem(B, N, L, H, D, dtype="bf16", seed=L + 11, mask="zero", pair="normal")
+    m = w.mask.copy()
+    m[0, 0, 0, 0, 9] = 0xFFC1      # negative NaN
+    m[0, 1, 0, 0, L - 1] = 0x7FC0  # positive NaN
+    m[0, 2, 0, 0, 3:30] = 0xFF80   # -inf on part of the row
+    w.mask = m
+    o, l = run_gpu(torch_dev, w)
+    ro, rl = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype="bf16", nthreads=THREADS)
+    nan_seq = np.zeros(N, bool)
+    nan_seq[:2] = True
+    assert np.isnan(ro[:, nan_seq]).all() and np.isnan(rl[:, nan_seq]).all()
+    assert np.isnan(o[:, nan_seq]).all(), "a NaN mask value must make its sequence's outputs NaN"
+    assert np.isnan(l[:, nan_seq]).all(), "a NaN mask value must make its sequence's lse NaN"
+    compare(o[:, ~nan_seq], l[:, ~nan_seq], ro[:, ~nan_seq], rl[:, ~nan_seq], "bf16", f"other sequences, L={L}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("L", [77, 96])
 def test_neg_inf_pair_bias_exact_path(torch_dev, L, dtype):
@@ -455,7 +488,7 @@ def test_head_dim_64_workload_size(torch_dev):
 # cannot, so it takes -3e4 (finite) as well as -1e9 (which arrives as -inf).
 # L % 8 == 0 copies the bias tiles straight into LDS, L % 8 != 0 stages them.
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("dtype,value", [("bf16", -1e9), ("f16", -3e4), ("f16", -1e9)])
+@pytest.mark.parametrize("dtype,value", [("bf16", -1e9), ("bf16", -math.inf), ("f16", -3e4), ("f16", -1e9)])
 @pytest.mark.parametrize("D", [32, 64])
 @pytest.mark.parametrize("L", [256, 251])
 def test_masked_leading_and_middle_blocks(torch_dev, L, D, dtype, value):
