@@ -144,6 +144,8 @@ def main():
     ap.add_argument("--layout", choices=["dense", "transposed"], default="dense",
                     help="fwd: transposed stores Q/K/V/O as X[B, L, N, H, D] and reads them in place through "
                          "evo_attn_fwd_strided (triangle attention around the ending node without a copy)")
+    ap.add_argument("--no-pair-bias", action="store_true",
+                    help="drop the workload's pair bias (to price the pair-bias stream by difference)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-time budget of the oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-warm", action="store_true", help="skip the secondary warm-cache measurement")
@@ -187,6 +189,8 @@ def main():
 
     log(f"bench: generating workload {args.workload}")
     w = S.workload(args.workload, dtype=args.dtype)
+    if args.no_pair_bias:
+        w.pair = None
     B, N, L, H, D = w.shape
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
     dcode = E.torch_dtype_code(tdt)
