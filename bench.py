@@ -95,7 +95,7 @@ def environment(torch):
     return {"cpu_model": cpu, "host_threads": len(os.sched_getaffinity(0)), "gpu": props.name or None,
             "gcn_arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count,
             "rocm": rocm, "hip_runtime": torch.version.hip, "torch": torch.__version__,
-            "python": sys.version.split()[0]}
+            "numpy": __import__("numpy").__version__, "python": sys.version.split()[0]}
 
 
 def source_hash(dtype):
@@ -109,6 +109,21 @@ def algorithmic_bytes(shape, dtype, has_mask, has_pair):
     es = 4 if dtype == "f32" else 2
     return 4 * B * N * L * H * D * es + 4 * B * N * H * L + (B * N * L * es if has_mask else 0) + (
         B * H * L * L * es if has_pair else 0)
+
+
+def measured_counters(workload_name, dtype):
+    """MFMA-busy fraction, vector issue slots per score element and engine clock from the committed
+    rocprofv3 SQ counter summary, if it matches this kernel source."""
+    path = os.path.join(ROOT, "profiles", f"sq_counters_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256") != source_hash(dtype):
+        return None
+    keys = ("mfma_busy_frac", "valu_slots_per_score", "mfma_per_wave_block", "valu_per_wave_block",
+            "exp_per_wave_block", "engine_clock_ghz", "wait_frac_of_wave_time")
+    return {k: t[k] for k in keys} | {"source": f"profiles/sq_counters_{workload_name}.json"}
 
 
 def measured_traffic(workload_name, dtype):
@@ -155,10 +170,16 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run one plain copy kernel (torch.neg, out=) over this many MiB, "
                          "a known-size reference for the HBM byte counters")
+    ap.add_argument("--summarize-sq", nargs=2, metavar=("SQ_A_DIR", "SQ_B_DIR"),
+                    help="read the two rocprofv3 SQ counter passes of this script (see sq_commands) and write "
+                         "profiles/sq_counters_<workload>.json; runs on the host only")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="read two rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE) and write "
                          "profiles/traffic_<workload>.json; runs on the host only")
     args = ap.parse_args()
+    if args.summarize_sq:
+        summarize_sq(args.workload, *args.summarize_sq)
+        return
     if args.summarize_traffic:
         if args.copy_probe_mib <= 0:
             raise SystemExit("--summarize-traffic needs the --copy-probe-mib value the counter runs used")
@@ -316,6 +337,7 @@ def main():
                 "achieved_GBps": round(alg_bytes / (kern_us * 1e-6) / 1e9, 1),
                 "frac_of_8TBps": round(alg_bytes / (kern_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
         "warm": warm,
+        "counters": measured_counters(w.name, w.dtype),
         "env": environment(torch),
     }
 
@@ -705,6 +727,73 @@ def summarize_traffic(workload, probe_mib, fetch_dir, write_dir):
         "algorithmic_bytes": algorithmic_bytes(w.shape, w.dtype, w.mask is not None, w.pair is not None),
     }
     path = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
+SQ_A = ["SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_ANY",
+        "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
+SQ_B = ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_VALU_TRANS_F32", "SQ_WAVES",
+        "SQ_INSTS_SALU", "SQ_WAIT_INST_LDS"]
+
+
+def sq_commands(dir_a, dir_b):
+    """The three commands behind an SQ counter summary (one counter pass each, then the summary)."""
+    run = "-o tri -- python3 bench.py --steps 5 --warmup 1 --no-cpu-baseline --no-warm --spinup-seconds 0"
+    return [f"rocprofv3 --pmc {' '.join(SQ_A)} --output-format csv -d {dir_a} {run}",
+            f"rocprofv3 --pmc {' '.join(SQ_B)} --output-format csv -d {dir_b} {run}",
+            f"python3 bench.py --summarize-sq {dir_a} {dir_b}"]
+
+
+def summarize_sq(workload, dir_a, dir_b):
+    """MFMA-busy fraction, vector issue slots per score element and the engine clock of the attention
+    kernel, from two rocprofv3 SQ counter passes (means per dispatch; the clock from GRBM_GUI_ACTIVE per
+    XCD over the dispatches' own durations in the counter CSV)."""
+    import csv
+    import glob
+    import synthetic as S
+    w = S.workload(workload)
+    kname = {"bf16": "Bf16Fmt", "f16": "F16Fmt", "f32": "fwd_f32"}[w.dtype]
+    c = {n: _counter_means(dir_a, n, kname)[0] for n in SQ_A}
+    c.update({n: _counter_means(dir_b, n, kname)[0] for n in SQ_B})
+    durations = {}
+    for f in glob.glob(os.path.join(dir_a, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if kname in r["Kernel_Name"]:
+                    durations[(f, r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    dur_ns = sum(durations.values()) / len(durations)
+    xcds, simds = 8, 1024
+    grbm_per_xcd = c["GRBM_GUI_ACTIVE"] / xcds
+    B, N, L, H, D = w.shape
+    waves = c["SQ_WAVES"]
+    blocks_per_wave = -(-L // 64)  # 64-key blocks each wave visits
+    scores_per_wave_block = 32 * 64  # 32 queries x 64 keys
+    per_block = lambda x: x / waves / blocks_per_wave
+    valu_other = c["SQ_INSTS_VALU"] - c["SQ_INSTS_MFMA"]  # vector instructions, exponentials included
+    out = {
+        "workload": w.name,
+        "commands": sq_commands(dir_a, dir_b),
+        "kernel_name_contains": kname,
+        "kernel_source_sha256": source_hash(w.dtype),
+        "dispatches": len(durations),
+        "dispatch_ns_under_counters": round(dur_ns, 1),
+        "counters_per_dispatch": {k: round(v, 1) for k, v in c.items()},
+        "engine_clock_ghz": round(grbm_per_xcd / dur_ns, 3),
+        "mfma_busy_frac": round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (grbm_per_xcd * simds), 4),
+        "mfma_per_wave_block": round(per_block(c["SQ_INSTS_MFMA"]), 2),
+        "valu_per_wave_block": round(per_block(valu_other), 2),
+        "exp_per_wave_block": round(per_block(c["SQ_INSTS_VALU_TRANS_F32"]), 2),
+        # issue slots of the vector port per score element: each wave64 instruction covers 64 lanes, and a
+        # wave-block holds 32 x 64 score elements, i.e. 32 per lane
+        "valu_slots_per_score": round(per_block(valu_other) / (scores_per_wave_block / 64), 3),
+        "wait_frac_of_wave_time": round(c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"], 4),
+        "note": "per wave-block: one wave's 32 queries against one 64-key block; the vector counts include the "
+                "exponentials and exclude the MFMAs",
+    }
+    path = os.path.join(ROOT, "profiles", f"sq_counters_{w.name}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
