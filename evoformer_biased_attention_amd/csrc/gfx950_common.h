@@ -102,6 +102,24 @@ __device__ inline void dma16(Rsrc r, const void* lds, uint32_t voff, uint32_t so
                                              (int)soff, 0, 0);
 }
 
+// The same copy written as assembly: the compiler then neither tracks it nor
+// makes later LDS reads wait for it (with the builtin it orders every later
+// LDS read, of any buffer, behind the copy's completion).  The caller waits
+// for it itself (wait_all, or an s_waitcnt on the vector-memory count) before
+// a barrier publishes the data.  M0 carries the LDS address, taken from the
+// low 32 bits of the generic pointer (the LDS offset); one wait state
+// separates its write from the load that reads it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is named as clobbered on purpose
+__device__ inline void dma16_untracked(Rsrc r, const void* lds, uint32_t voff) {
+    const uint32_t a = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(a), "v"(voff), "s"(r)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Wait for every outstanding memory operation of this wave.
 __device__ inline void wait_all() { __builtin_amdgcn_s_waitcnt(0); }
 

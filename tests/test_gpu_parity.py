@@ -162,6 +162,43 @@ def test_ragged_f32(torch_dev, shape):
     parity_full(torch_dev, w)
 
 
+# fp32 inputs with 16-byte aligned bias rows (L % 4 == 0 in the dense layout)
+# and D in {16, 32, 64} take the matrix-core fp32 kernel; D = 8 and unaligned
+# rows take the vector-ALU one.  Both against the full oracle.
+F32_MFMA_SHAPES = [(1, 2, 4, 2, 16), (1, 3, 20, 2, 32), (2, 2, 68, 3, 32), (1, 2, 132, 2, 64), (1, 1, 256, 4, 16),
+                   (1, 2, 100, 2, 32), (2, 3, 64, 2, 64), (1, 1, 192, 1, 32)]
+
+
+@pytest.mark.parametrize("shape", F32_MFMA_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("bias", ["both", "mask", "pair", "none"])
+def test_f32_matrix_core_path(torch_dev, shape, bias):
+    B, N, L, H, D = shape
+    w = S.random_problem(B, N, L, H, D, dtype="f32", seed=sum(shape) + len(bias), mask="tail" if bias in ("both", "mask") else None,
+                         pair="normal" if bias in ("both", "pair") else None, mask_frac=0.3)
+    say(f"f32 matrix-core path {shape} bias={bias}")
+    parity_full(torch_dev, w)
+
+
+@pytest.mark.parametrize("L", [64, 96])
+def test_f32_infinite_and_nan_masks(torch_dev, L):
+    """fp32 masks with -inf on part of a row, on a whole row (out = 0, lse = -inf), a finite -1e9 on a
+    leading half, and a NaN (its sequence NaN)."""
+    B, N, H, D = 1, 5, 2, 32
+    w = S.random_problem(B, N, L, H, D, dtype="f32", seed=L + 5, mask="zero", pair="normal")
+    mf = np.zeros((B, N, 1, 1, L), np.float32)
+    mf[0, 0, ..., 10:50] = -np.inf
+    mf[0, 1] = -np.inf
+    mf[0, 2, ..., : L // 2] = -1e9
+    mf[0, 3, ..., 7] = np.nan
+    w.mask = mf
+    o, l = run_gpu(torch_dev, w)
+    ro, rl = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype="f32", nthreads=THREADS)
+    assert np.all(o[0, 1] == 0) and np.all(np.isneginf(l[0, 1]))
+    assert np.isnan(o[0, 3]).all() and np.isnan(l[0, 3]).all()
+    keep = np.array([True, True, True, False, True])
+    compare(o[:, keep], l[:, keep], ro[:, keep], rl[:, keep], "f32", f"fp32 infinite masks, L={L}")
+
+
 def test_large_bias_magnitudes(torch_dev):
     """Biases of scale 8 (peaked softmax) and random -1e9 masks."""
     w = S.random_problem(1, 4, 192, 2, 32, dtype="bf16", seed=77, mask="random", pair="normal", mask_frac=0.5,
