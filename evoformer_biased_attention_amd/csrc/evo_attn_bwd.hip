@@ -394,6 +394,12 @@ hipError_t launch_valu(const BwdArgs& a, int dtype, unsigned stages, hipStream_t
 // aligned, any L); the vector-ALU kernels take the rest (fp32).  The dq
 // stage goes first in either case: it writes delta.
 hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t stream) {
+    if (dtype == 0 && bwd_f32_mfma_eligible(a)) {
+        // fp32: dq and dk/dv on the matrix cores, the pair gradient on the vector ALUs
+        hipError_t e = launch_bwd_f32_mfma(a, kBwdF32MfmaStages, stream);
+        if (e != hipSuccess) return e;
+        return launch_valu(a, dtype, (kStageDq | kStageDkDv | kStageDpair) & ~kBwdF32MfmaStages, stream);
+    }
     const unsigned mfma = bwd_mfma_eligible(a, dtype) ? kBwdMfmaStages : 0u;
     hipError_t e = hipSuccess;
     if (mfma & kStageDq) e = launch_bwd_mfma(a, dtype, kStageDq, stream);

@@ -84,6 +84,13 @@ int64_t bwd_dpair_chunks(int64_t B, int64_t N, int64_t L, int64_t H);
 __host__ __device__ inline int64_t bwd_ws_row(int64_t L) { return (L + 3) / 4 * 4; }
 hipError_t launch_bwd_mfma(const BwdArgs& a, int dtype, unsigned stages, hipStream_t stream);
 
+// Matrix-core backward for fp32 inputs (evo_attn_bwd_f32.hip): the stages it
+// implements (dq + delta, dk/dv/dmask), whether it accepts the arguments, and
+// a launch of some of those stages in stage order.
+extern const unsigned kBwdF32MfmaStages;
+bool bwd_f32_mfma_eligible(const BwdArgs& a);
+hipError_t launch_bwd_f32_mfma(const BwdArgs& a, unsigned stages, hipStream_t stream);
+
 // Triangle multiplication, 16-bit formats, [planes][L][L] operands.
 hipError_t launch_trimul(const void* a, const void* w, void* x, int64_t planes, int64_t L, int incoming, int f16,
                          hipStream_t stream);

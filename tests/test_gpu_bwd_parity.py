@@ -189,6 +189,40 @@ def test_bwd_ragged(torch_dev, shape, d, dtype):
         parity(torch_dev, w, dout)
 
 
+# fp32 inputs with D in {16, 32}, 16-byte aligned bias rows (L % 4 == 0 in the
+# dense layout): dq and dk/dv/dmask run on the fp32 matrix-core kernels, the
+# pair gradient on the vector ALUs.  Every bias combination, bias gradients on
+# and off, against the full backward oracle.
+F32_MFMA_BWD = [(1, 2, 4, 2, 16), (1, 3, 20, 2, 32), (2, 2, 68, 3, 32), (1, 2, 132, 2, 16), (1, 1, 192, 4, 32)]
+
+
+@pytest.mark.parametrize("shape", F32_MFMA_BWD, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("bias", ["both", "mask", "pair", "none"])
+def test_bwd_f32_matrix_core_path(torch_dev, shape, bias):
+    B, N, L, H, D = shape
+    w = S.random_problem(B, N, L, H, D, dtype="f32", seed=sum(shape) * 7 + len(bias),
+                         mask="tail" if bias in ("both", "mask") else None,
+                         pair="normal" if bias in ("both", "pair") else None, mask_frac=0.3)
+    dout = S.random_dout(w.shape, "f32", seed=L + D + len(bias))
+    parity(torch_dev, w, dout)
+    if bias == "both":
+        parity(torch_dev, w, dout, want_dmask=False, want_dpair=False)
+
+
+def test_bwd_f32_matrix_core_masked_rows(torch_dev):
+    """fp32 backward with -inf masks on part of a row and on a whole row (no gradient passes through it),
+    and a peaked softmax (bias scale 8), on the matrix-core path."""
+    B, N, L, H, D = 1, 4, 96, 2, 32
+    w = S.random_problem(B, N, L, H, D, dtype="f32", seed=321, mask="zero", pair="normal", bias_scale=8.0)
+    mf = np.zeros((B, N, 1, 1, L), np.float32)
+    mf[0, 0, ..., 10:50] = -np.inf
+    mf[0, 1] = -np.inf
+    mf[0, 2, ..., 60:] = -1e9
+    w.mask = mf
+    dout = S.random_dout(w.shape, "f32", seed=322)
+    parity(torch_dev, w, dout)
+
+
 def single_key(torch, w, dout):
     """L = 1: dv = dO (P = 1) is compared as usual.  dq, dk, dmask and dpair vanish identically (the oracle
     returns exact zeros); the kernel's dS is the fp32 difference of two evaluations of the same D-term dot
