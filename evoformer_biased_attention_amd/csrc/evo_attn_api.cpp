@@ -348,7 +348,9 @@ namespace {
 // what the given workspace holds (0: none).  `a` carries the shape, the
 // biases present and the strides.
 int64_t usable_chunks(const evo::BwdArgs& a, evo_dtype_t dtype, size_t workspace_bytes) {
-    if (!evo::bwd_mfma_eligible(a, static_cast<int>(dtype))) return 0;
+    const bool mfma = dtype == EVO_DTYPE_F32 ? evo::bwd_f32_mfma_eligible(a)
+                                            : evo::bwd_mfma_eligible(a, static_cast<int>(dtype));
+    if (!mfma) return 0;
     const int64_t want = evo::bwd_dpair_chunks(a.B, a.N, a.L, a.H);
     int64_t per = 4;  // bytes of one chunk's partial sums
     for (int64_t s : {a.B, a.H, a.L, evo::bwd_ws_row(a.L)}) per = mul_checked(per, s);
@@ -369,8 +371,11 @@ extern "C" size_t evo_attn_bwd_workspace_size(const evo_shape_t* shape, evo_dtyp
     if (par < 0) return 0;
     evo_layout_t lay;
     evo_attn_dense_layout(shape, &lay);
+    // the workspace serves the pair gradient only: probe with a pair bias present
+    static const char kPresent = 0;
     evo::BwdArgs probe{};
     probe.B = shape->B, probe.N = shape->N, probe.L = shape->L, probe.H = shape->H, probe.D = shape->D;
+    probe.pair = &kPresent;
     probe.st = strides_of(lay);
     const int64_t c = usable_chunks(probe, dtype, ~static_cast<size_t>(0) >> 2);
     const int64_t bytes = mul_checked(par, c);

@@ -390,12 +390,11 @@ hipError_t launch_valu(const BwdArgs& a, int dtype, unsigned stages, hipStream_t
 }  // namespace
 
 // The matrix-core kernels take the stages they implement for the shapes
-// they accept (16-bit formats, D in {8, 16, 32, 64}, q/k/v/out rows 16-byte
-// aligned, any L); the vector-ALU kernels take the rest (fp32).  The dq
-// stage goes first in either case: it writes delta.
+// they accept (16-bit formats with D in {8, 16, 32, 64} and any L; fp32 with
+// D in {16, 32} and 16-byte aligned bias rows); the vector-ALU kernels take
+// the rest.  The dq stage goes first in either case: it writes delta.
 hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t stream) {
     if (dtype == 0 && bwd_f32_mfma_eligible(a)) {
-        // fp32: dq and dk/dv on the matrix cores, the pair gradient on the vector ALUs
         hipError_t e = launch_bwd_f32_mfma(a, kBwdF32MfmaStages, stream);
         if (e != hipSuccess) return e;
         return launch_valu(a, dtype, (kStageDq | kStageDkDv | kStageDpair) & ~kBwdF32MfmaStages, stream);

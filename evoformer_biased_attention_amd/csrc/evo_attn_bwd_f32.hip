@@ -1,7 +1,6 @@
-// Backward pass for fp32 inputs on the matrix cores: the dq (+ delta) and the
-// dk / dv / dmask stages with v_mfma_f32_16x16x4f32 (fp32 operands, fp32
-// accumulation).  The pair-gradient stage of fp32 inputs stays on the vector
-// ALUs (evo_attn_bwd.hip).
+// Backward pass for fp32 inputs on the matrix cores: the dq (+ delta), the
+// dk / dv / dmask and the pair-gradient stages with v_mfma_f32_16x16x4f32
+// (fp32 operands, fp32 accumulation).
 //
 // The gradients (page "DeepSpeed DS4Sci_EvoformerAttention 内核实战指南",
 // hmyw.cn, sections 4 and 5.4: the weights are recomputed from the saved
@@ -25,6 +24,9 @@
 //                      so dV^T = dO^T . P and dK^T = Q^T . dS contract over
 //                      them; the workgroup visits every head, so the mask
 //                      gradient of its keys is complete when it ends.
+//   bwd_dpair_f32_mfma scores transposed; the workgroup owns a 64 x 64 tile of
+//                      one (b, h) and sums dS over a range of n; with more
+//                      than one range, bwd_dpair_reduce_f32 adds the ranges.
 // LDS tiles of rows of D floats keep 16-byte chunks XOR-swizzled by row (as in
 // the fp32 forward), so that a 16-row operand read and a 4-row transposed read
 // spread over the banks.  Copies into LDS are untracked (see
@@ -73,7 +75,7 @@ __device__ inline void tile_run(const f32x4* t, int r, int g, float (&out)[D / 4
 
 struct BParams {
     const float *q, *k, *v, *mask, *pair, *out, *dout, *lse;
-    float *dq, *dk, *dv, *dmask, *delta;
+    float *dq, *dk, *dv, *dmask, *dpair, *delta;
     int64_t N, L, H;
     gfx::FastDiv rblocks, nd, hd;  // row blocks (128 queries for dq, 64 keys for dk/dv), N, H
     int64_t total;
@@ -421,6 +423,225 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_f32_mfma(BParams p) {
     if (p.dmask && g == 0 && key_live) p.dmask[b * st.mb + n * st.mn + key] = dmask;
 }
 
+// ---------------------------------------------------------------------------
+// dpair.  Workgroup = one (b, h) tile of 64 queries x 64 keys and one range
+// [n0, n1) of the N axis; wave w owns queries 16w .. 16w+15 against the 64
+// keys, scores transposed (lane c + 16g holds keys 16kt + 4g + i of query
+// 16w + c).  The pair rows of the tile are the same for every n and are read
+// once.  Per n the tile's K and V rows (and its 64 mask values) come through
+// LDS, shared by the four waves, one n ahead; each lane's own Q and dO
+// d-range, lse and delta go straight to registers, also one n ahead.  dS is
+// summed over the range in registers, n in order.  With one range the
+// workgroup writes dpair; with several it writes its range's sum to the
+// workspace and bwd_dpair_reduce_f32 adds the ranges in order.
+// ---------------------------------------------------------------------------
+template <int D>
+struct PrBuf {
+    f32x4 k[kKB * D / 4];
+    f32x4 v[kKB * D / 4];
+    f32x4 mt[kKB / 4];
+};
+
+struct PairParams {
+    BParams p;
+    float* ws;           // [chunks][B][H][L][bwd_ws_row(L)] fp32, or nullptr (one range: dpair itself)
+    int64_t chunks;      // N is split into this many contiguous ranges
+    gfx::FastDiv tiles;  // 64 x 64 tiles per (b, h): ceil(L/64)^2
+    gfx::FastDiv tdim;   // ceil(L/64)
+    gfx::FastDiv chd;    // chunks
+    int64_t bh;          // B * H
+};
+
+template <int D, bool MASK>
+__global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_f32_mfma(PairParams pp) {
+    constexpr int kS = D / 4;
+    const BParams& p = pp.p;
+    __shared__ __attribute__((aligned(16))) PrBuf<D> sm[2];
+
+    // order (b, h, range, query tile, key tile): the tiles of one (b, h,
+    // range) run on one XCD together and share each n's rows in its L2
+    const uint32_t id = (uint32_t)gfx::logical_block(blockIdx.x, p.total);
+    const uint32_t r1 = gfx::fdiv(id, pp.tiles), r2 = gfx::fdiv(r1, pp.chd), r3 = gfx::fdiv(r2, p.hd);
+    const uint32_t tile = id - r1 * pp.tiles.d;
+    const uint32_t ti = gfx::fdiv(tile, pp.tdim), tj = tile - ti * pp.tdim.d;
+    const int64_t chunk = r1 - r2 * pp.chd.d, h = r2 - r3 * p.hd.d, b = r3;
+    const Strides& st = p.st;
+    const int L = (int)p.L;
+    const int64_t N = p.N;
+    const int64_t n0 = chunk * N / pp.chunks, n1 = (chunk + 1) * N / pp.chunks;
+    const int i0 = (int)ti * kKB, j0 = (int)tj * kKB;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int c = lane & 15, g = lane >> 4;
+    const int qi = i0 + 16 * wave + c;  // this lane's query
+    const bool q_live = qi < L;
+
+    const uint32_t rowq = (uint32_t)st.q[2] * 4, rowk = (uint32_t)st.k[2] * 4, rowv = (uint32_t)st.v[2] * 4;
+    const uint32_t rowo = (uint32_t)st.o[2] * 4, rowp = (uint32_t)st.pi * 4;
+    const uint32_t last = (uint32_t)(L - 1);
+
+    // pair[b, h, qi, j0 + 16kt + 4g .. +3]: the accumulator input of every S^T product
+    f32x4 pbs[kKT];
+    {
+        const Rsrc rp = make_rsrc(p.pair + b * st.pb + h * st.ph, ((last * rowp + (uint32_t)L * 4u) + 15u) & ~15u);
+        for (int kt = 0; kt < kKT; ++kt)
+            pbs[kt] = __builtin_bit_cast(f32x4, bload16(rp, (uint32_t)qi * rowp + 4u * (uint32_t)(j0 + 16 * kt + 4 * g)));
+    }
+
+    RowCopy<D> ck, cv;
+    ck.init(wave, lane, rowk);
+    cv.init(wave, lane, rowv);
+    auto copy_step = [&](int64_t n, PrBuf<D>* __restrict__ dst) {
+        const Rsrc rk = make_rsrc(p.k + b * st.k[0] + n * st.k[1] + h * st.k[3], last * rowk + D * 4);
+        const Rsrc rv = make_rsrc(p.v + b * st.v[0] + n * st.v[1] + h * st.v[3], last * rowv + D * 4);
+        ck.issue(rk, dst->k, wave, (uint32_t)j0 * rowk);
+        cv.issue(rv, dst->v, wave, (uint32_t)j0 * rowv);
+        if (MASK && wave == 0 && lane < 16) {
+            const Rsrc rm = make_rsrc(p.mask + b * st.mb + n * st.mn, ((uint32_t)L * 4u + 15u) & ~15u);
+            dma16_untracked(rm, &dst->mt[0], 16u * lane + (uint32_t)j0 * 4u);
+        }
+    };
+    // this lane's Q and dO d-range, lse and delta at sequence n, as loaded
+    // (converted when used, so that the loads stay in flight meanwhile)
+    uint4 qraw[kS / 4], draw[kS / 4];
+    float lsraw = -INFINITY, dlraw = 0.f;
+    auto load_rows = [&](int64_t n) {
+        const Rsrc rq = make_rsrc(p.q + b * st.q[0] + n * st.q[1] + h * st.q[3], last * rowq + D * 4);
+        const Rsrc rd = make_rsrc(p.dout + b * st.o[0] + n * st.o[1] + h * st.o[3], last * rowo + D * 4);
+        for (int j = 0; j < kS / 4; ++j) {
+            const uint32_t d0 = 4u * (uint32_t)(kS * g + 4 * j);
+            qraw[j] = bload16(rq, (uint32_t)qi * rowq + d0);
+            draw[j] = bload16(rd, (uint32_t)qi * rowo + d0);
+        }
+        if (q_live) {
+            const int64_t row = ((b * N + n) * p.H + h) * st.lrow + qi;
+            lsraw = p.lse[row];
+            dlraw = p.delta[row];
+        }
+    };
+
+    f32x4 ds[kKT];
+    for (int kt = 0; kt < kKT; ++kt) ds[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    copy_step(n0, &sm[0]);
+    load_rows(n0);
+    gfx::wait_all();
+    __syncthreads();
+
+    for (int64_t n = n0; n < n1; ++n) {
+        const int it = (int)(n - n0);
+        const PrBuf<D>* __restrict__ cur = &sm[it & 1];
+        // Q/sqrt(D) and dO as B operands (lane group g's d-range of query c)
+        float qop[kS], dop[kS];
+        for (int j = 0; j < kS / 4; ++j) {
+            const uint4 wq = qraw[j], wd = draw[j];
+            qop[4 * j] = __builtin_bit_cast(float, wq.x) * p.scale;
+            qop[4 * j + 1] = __builtin_bit_cast(float, wq.y) * p.scale;
+            qop[4 * j + 2] = __builtin_bit_cast(float, wq.z) * p.scale;
+            qop[4 * j + 3] = __builtin_bit_cast(float, wq.w) * p.scale;
+            dop[4 * j] = __builtin_bit_cast(float, wd.x);
+            dop[4 * j + 1] = __builtin_bit_cast(float, wd.y);
+            dop[4 * j + 2] = __builtin_bit_cast(float, wd.z);
+            dop[4 * j + 3] = __builtin_bit_cast(float, wd.w);
+        }
+        const float lse2 = q_live ? lse2_of(lsraw) : INFINITY;
+        const float ndl = q_live ? -dlraw : 0.f;
+        if (n + 1 < n1) {
+            copy_step(n + 1, &sm[(it & 1) ^ 1]);
+            load_rows(n + 1);
+        }
+        for (int kt = 0; kt < kKT; ++kt) {
+            // S^T = K.Q^T/sqrt(D) + pair + mask and dP^T - delta = V.dO^T - delta
+            f32x4 acc = pbs[kt];
+            if (MASK) acc += cur->mt[4 * kt + g];
+            f32x4 dpm = f32x4{ndl, ndl, ndl, ndl};
+            float kf[kS], vf[kS];
+            tile_run<D>(cur->k, 16 * kt + c, g, kf);
+            tile_run<D>(cur->v, 16 * kt + c, g, vf);
+            for (int s = 0; s < kS; ++s) {
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[s], qop[s], acc, 0, 0, 0);
+                dpm = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[s], dop[s], dpm, 0, 0, 0);
+            }
+            for (int r = 0; r < 4; ++r)
+                ds[kt][r] = fmaf(__builtin_amdgcn_exp2f(fmaf(acc[r], kLog2e, -lse2)), dpm[r], ds[kt][r]);
+        }
+        gfx::wait_all();  // the next n's copies and rows have landed
+        __syncthreads();
+    }
+
+    // lane c + 16g: query qi, keys j0 + 16kt + 4g + 0..3 (those past L are not written)
+    if (!q_live) return;
+    for (int kt = 0; kt < kKT; ++kt) {
+        const int j = j0 + 16 * kt + 4 * g;
+        if (j >= L) continue;
+        if (pp.ws) {
+            *reinterpret_cast<f32x4*>(pp.ws + ((chunk * pp.bh + b * p.H + h) * p.L + qi) * bwd_ws_row(p.L) + j) = ds[kt];
+        } else {
+            float* dst = p.dpair + b * st.pb + h * st.ph + (int64_t)qi * st.pi + j;
+            if (j + 4 <= L) *reinterpret_cast<f32x4*>(dst) = ds[kt];
+            else
+                for (int e = 0; e < L - j; ++e) dst[e] = ds[kt][e];
+        }
+    }
+}
+
+// dpair[b,h,i,j] = sum over the workspace's ranges of their partial sums, in
+// range order; four consecutive keys per thread.  The workspace is dense
+// [chunks][B][H][L][bwd_ws_row(L)]; keys past L are skipped.
+struct ReduceF32 {
+    const float* ws;
+    float* dpair;
+    int64_t quads, chunks;  // B*H*L*bwd_ws_row(L) / 4; ranges
+    int64_t L, H;
+    int64_t pb, ph, pi;     // strides of dpair
+};
+
+__global__ __launch_bounds__(256) void bwd_dpair_reduce_f32(ReduceF32 r) {
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= r.quads) return;
+    f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int64_t ch = 0; ch < r.chunks; ++ch) t += reinterpret_cast<const f32x4*>(r.ws)[ch * r.quads + q];
+    const int64_t rq = bwd_ws_row(r.L) / 4, row = q / rq, j = 4 * (q - row * rq);  // row = (b * H + h) * L + i
+    if (j >= r.L) return;
+    const int64_t bh = row / r.L, i = row - bh * r.L, b = bh / r.H, h = bh - b * r.H;
+    float* dst = r.dpair + b * r.pb + h * r.ph + i * r.pi + j;
+    if (j + 4 <= r.L) *reinterpret_cast<f32x4*>(dst) = t;
+    else
+        for (int e = 0; e < r.L - j; ++e) dst[e] = t[e];
+}
+
+template <int D, bool MASK>
+hipError_t launch_dpair(const BParams& base, int64_t B, float* ws, int64_t chunks, hipStream_t stream) {
+    PairParams pp;
+    pp.p = base;
+    const int64_t tdim = (base.L + kKB - 1) / kKB;
+    pp.p.total = B * base.H * chunks * tdim * tdim;
+    if (pp.p.total >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
+    pp.ws = ws;
+    pp.chunks = chunks;
+    pp.tiles = gfx::make_fastdiv((uint32_t)(tdim * tdim));
+    pp.tdim = gfx::make_fastdiv((uint32_t)tdim);
+    pp.chd = gfx::make_fastdiv((uint32_t)chunks);
+    pp.bh = B * base.H;
+    void* args[] = {&pp};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dpair_f32_mfma<D, MASK>),
+                                   dim3((unsigned)pp.p.total), dim3(kWaves * 64), args, 0, stream);
+    if (e != hipSuccess || !ws) return e;
+    ReduceF32 r;
+    r.ws = ws;
+    r.dpair = base.dpair;
+    r.quads = B * base.H * base.L * bwd_ws_row(base.L) / 4;
+    r.chunks = chunks;
+    r.L = base.L;
+    r.H = base.H;
+    r.pb = base.st.pb, r.ph = base.st.ph, r.pi = base.st.pi;
+    const int64_t blocks = (r.quads + 255) / 256;
+    if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
+    void* rargs[] = {&r};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dpair_reduce_f32), dim3((unsigned)blocks), dim3(256),
+                           rargs, 0, stream);
+}
+
 template <int D, bool PAIR, bool MASK>
 hipError_t launch_stage(BParams p, int64_t B, unsigned stage, hipStream_t stream) {
     const int64_t L = p.L;
@@ -449,7 +670,7 @@ hipError_t launch_stage_dim(const BParams& p, int64_t B, bool pair, bool mask, u
 
 }  // namespace
 
-const unsigned kBwdF32MfmaStages = kStageDq | kStageDkDv;
+const unsigned kBwdF32MfmaStages = kStageDq | kStageDkDv | kStageDpair;
 
 // D in {16, 32} (D = 64 would spill in the dq kernel); q, k, v, out rows
 // 16-byte aligned (the C ABI checks that); pair and mask rows 16-byte
@@ -458,7 +679,8 @@ const unsigned kBwdF32MfmaStages = kStageDq | kStageDkDv;
 // buffer of a (b, n) slice and read as zero: the dk/dv kernel sums over its
 // query rows, and those past L must add exactly nothing.  Every byte offset
 // the kernels form stays below 2^31: rows up to 128 past L of every head,
-// pair rows up to 128 past L plus 64 keys.
+// pair rows up to 128 past L plus 64 keys.  The grids stay below 2^31
+// workgroups (the pair-gradient grid is at most its tile count + 2048).
 bool bwd_f32_mfma_eligible(const BwdArgs& a) {
     constexpr int64_t kLim = int64_t(1) << 31, kBig = int64_t(1) << 40;
     const int64_t L = a.L, H = a.H, D = a.D;
@@ -474,6 +696,8 @@ bool bwd_f32_mfma_eligible(const BwdArgs& a) {
     }
     if (a.pair && (a.st.pi >= kBig || ((L + 128) * a.st.pi + L + kKB) * 4 >= kLim)) return false;
     if (a.mask && (L + kKB) * 4 >= kLim) return false;
+    const int64_t tdim = (L + kKB - 1) / kKB;
+    if (a.B * H * tdim * tdim + 2048 >= kLim) return false;
     return a.B * a.N * H * ((L + 127) / 128) < kLim;
 }
 
@@ -491,6 +715,7 @@ hipError_t launch_bwd_f32_mfma(const BwdArgs& a, unsigned stages, hipStream_t st
     p.dk = static_cast<float*>(a.dk);
     p.dv = static_cast<float*>(a.dv);
     p.dmask = static_cast<float*>(a.dmask);
+    p.dpair = static_cast<float*>(a.dpair);
     p.delta = a.delta;
     p.N = a.N, p.L = a.L, p.H = a.H;
     p.nd = gfx::make_fastdiv((uint32_t)a.N);
@@ -506,6 +731,15 @@ hipError_t launch_bwd_f32_mfma(const BwdArgs& a, unsigned stages, hipStream_t st
         else if (a.D == 32) e = launch_stage_dim<32>(p, a.B, pair, mask, stage, stream);
         else e = launch_stage_dim<64>(p, a.B, pair, mask, stage, stream);
         if (e != hipSuccess) return e;
+    }
+    if ((stages & kStageDpair) && a.dpair) {
+        // with a workspace of at least two ranges, split N; else one range per tile
+        float* ws = a.ws && a.ws_chunks >= 2 ? a.ws : nullptr;
+        const int64_t chunks = ws ? a.ws_chunks : 1;
+        if (a.D == 16) e = mask ? launch_dpair<16, true>(p, a.B, ws, chunks, stream)
+                                : launch_dpair<16, false>(p, a.B, ws, chunks, stream);
+        else e = mask ? launch_dpair<32, true>(p, a.B, ws, chunks, stream)
+                      : launch_dpair<32, false>(p, a.B, ws, chunks, stream);
     }
     return e;
 }

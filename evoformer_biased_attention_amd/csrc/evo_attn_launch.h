@@ -85,8 +85,9 @@ __host__ __device__ inline int64_t bwd_ws_row(int64_t L) { return (L + 3) / 4 * 
 hipError_t launch_bwd_mfma(const BwdArgs& a, int dtype, unsigned stages, hipStream_t stream);
 
 // Matrix-core backward for fp32 inputs (evo_attn_bwd_f32.hip): the stages it
-// implements (dq + delta, dk/dv/dmask), whether it accepts the arguments, and
-// a launch of some of those stages in stage order.
+// implements (dq + delta, dk/dv/dmask, dpair), whether it accepts the
+// arguments, and a launch of some of those stages in stage order.  Its pair
+// gradient uses the workspace as the 16-bit kernels do (ws_chunks ranges).
 extern const unsigned kBwdF32MfmaStages;
 bool bwd_f32_mfma_eligible(const BwdArgs& a);
 hipError_t launch_bwd_f32_mfma(const BwdArgs& a, unsigned stages, hipStream_t stream);

@@ -20,9 +20,10 @@ hipError_t launch_bwd(const BwdArgs&, int, hipStream_t) { return ++evo_stub::lau
 hipError_t launch_trimul(const void*, const void*, void*, int64_t, int64_t, int, int, hipStream_t) {
     return ++evo_stub::launches, hipSuccess;
 }
-// the matrix-core backward takes every 16-bit call here, so that the
-// workspace arithmetic runs for all of them
+// the matrix-core backward kernels take every call here (16-bit and fp32),
+// so that the workspace arithmetic runs for all of them
 bool bwd_mfma_eligible(const BwdArgs&, int dtype) { return dtype != 0; }
+bool bwd_f32_mfma_eligible(const BwdArgs&) { return true; }
 int64_t bwd_dpair_chunks(int64_t, int64_t N, int64_t, int64_t) { return N < 8 ? N : 8; }
 
 }  // namespace evo

@@ -274,7 +274,10 @@ def test_bwd_workspace_size():
     ws = E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 32), E.EVO_DTYPE_BF16)
     assert ws > 0 and ws % plane(1, 4, 384) == 0 and ws // plane(1, 4, 384) >= 2
     assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 32), E.EVO_DTYPE_F16) == ws
-    assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 32), E.EVO_DTYPE_F32) == 0    # vector-ALU path
+    assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 32), E.EVO_DTYPE_F32) == ws   # fp32 matrix cores
+    assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 16), E.EVO_DTYPE_F32) == ws
+    assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 64), E.EVO_DTYPE_F32) == 0    # vector-ALU path
+    assert E.evo_attn_bwd_workspace_size((1, 384, 383, 4, 32), E.EVO_DTYPE_F32) == 0    # pair rows unaligned
     assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 64), E.EVO_DTYPE_BF16) == ws  # matrix cores for D = 64 too
     assert E.evo_attn_bwd_workspace_size((1, 8, 384, 4, 32), E.EVO_DTYPE_BF16) == 0     # N too small to split
     for L in (100, 383, 99):                                                          # any L on the matrix cores

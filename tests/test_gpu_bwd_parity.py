@@ -190,9 +190,10 @@ def test_bwd_ragged(torch_dev, shape, d, dtype):
 
 
 # fp32 inputs with D in {16, 32}, 16-byte aligned bias rows (L % 4 == 0 in the
-# dense layout): dq and dk/dv/dmask run on the fp32 matrix-core kernels, the
-# pair gradient on the vector ALUs.  Every bias combination, bias gradients on
-# and off, against the full backward oracle.
+# dense layout): every stage runs on the fp32 matrix-core kernels (N is too
+# small here for the pair gradient's workspace: one range of n per tile).
+# Every bias combination, bias gradients on and off, against the full backward
+# oracle.
 F32_MFMA_BWD = [(1, 2, 4, 2, 16), (1, 3, 20, 2, 32), (2, 2, 68, 3, 32), (1, 2, 132, 2, 16), (1, 1, 192, 4, 32)]
 
 
@@ -396,15 +397,16 @@ def test_bwd_rows_past_L_read_as_zero(torch_dev, dtype, L):
     compare_grads(got, want, dtype, f"NaN after every input, L={L}")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("L", [64, 72, 136, 200])
 def test_bwd_pair_gradient_split_over_n(torch_dev, dtype, L):
     """N large enough for the workspace path (the N axis of the pair gradient split over workgroups and the
-    partial sums added in order), L with partial 64-row tiles; the same gradients without a workspace."""
+    partial sums added in order), L with partial 64-row tiles; the same gradients without a workspace.
+    fp32 at these shapes (D = 32, L % 4 == 0) runs every stage on the fp32 matrix-core kernels."""
     import evoformer_biased_attention_amd as E
     w = S.random_problem(1, 24, L, 3, 32, dtype=dtype, seed=L + 7, mask="tail", pair="normal", mask_frac=0.2)
-    assert E.evo_attn_bwd_workspace_size(w.shape, E.torch_dtype_code(
-        torch_dev.bfloat16 if dtype == "bf16" else torch_dev.float16)) > 0
+    code = {"bf16": E.EVO_DTYPE_BF16, "f16": E.EVO_DTYPE_F16, "f32": E.EVO_DTYPE_F32}[dtype]
+    assert E.evo_attn_bwd_workspace_size(w.shape, code) > 0
     dout = S.random_dout(w.shape, dtype, seed=L + 8)
     split = parity(torch_dev, w, dout)
     single = parity(torch_dev, w, dout, use_ws=False)

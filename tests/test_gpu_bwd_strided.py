@@ -107,19 +107,19 @@ def test_column_attention_training_in_place(torch_dev, dtype):
     compare_delta(delta, w, dout, "column attention")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("use_ws", [True, False], ids=["workspace", "no_workspace"])
-def test_padded_lse_and_pair_rows(torch_dev, use_ws):
+def test_padded_lse_and_pair_rows(torch_dev, use_ws, dtype):
     """lse and delta in the guide's padded rows (ceil(L/32)*32, section 5.4) and a pair bias whose rows and
     matrices are padded (a slice of a wider tensor); dpair is written in the same padded layout and its
-    padding, like delta's, is left alone."""
+    padding, like delta's, is left alone.  fp32 here runs on the fp32 matrix-core kernels."""
     torch = torch_dev
     B, N, L, H, D = 1, 24, 80, 2, 32
-    dtype = "bf16"
     w = S.random_problem(B, N, L, H, D, dtype=dtype, seed=81, mask="tail", pair="normal")
     dout = S.random_dout(w.shape, dtype, seed=82)
     row = (L + 31) // 32 * 32
     pad_i, pad_l = L + 8, L + 16  # pair rows 88 apart; 96 rows per matrix
-    wide = np.zeros((B, 1, H, pad_l, pad_i), np.uint16)
+    wide = np.zeros((B, 1, H, pad_l, pad_i), w.pair.dtype)
     wide[..., :L, :L] = w.pair
     pair_full = to_dev(torch, wide, dtype)
     pair = pair_full[..., :L, :L]
