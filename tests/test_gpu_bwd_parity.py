@@ -414,6 +414,19 @@ def test_bwd_pair_gradient_split_over_n(torch_dev, dtype, L):
         np.testing.assert_array_equal(a, b)   # only the pair gradient takes another route
 
 
+def test_bwd_f32_split_over_n_head_dim_16(torch_dev):
+    """fp32, D = 16, with the workspace (pair gradient split over N) and without: only dpair takes another
+    route, and it stays within the fp32 bound either way."""
+    import evoformer_biased_attention_amd as E
+    w = S.random_problem(1, 32, 136, 3, 16, dtype="f32", seed=1616, mask="tail", pair="normal", mask_frac=0.2)
+    assert E.evo_attn_bwd_workspace_size(w.shape, E.EVO_DTYPE_F32) > 0
+    dout = S.random_dout(w.shape, "f32", seed=1617)
+    split = parity(torch_dev, w, dout)
+    single = parity(torch_dev, w, dout, use_ws=False)
+    for a, b in zip(split[:4], single[:4]):
+        np.testing.assert_array_equal(a, b)
+
+
 # ---------------------------------------------------------------------------
 # L % 8 != 0 on the matrix cores: the bias tiles are staged through registers,
 # the pair gradient's workspace rows are padded to a multiple of 4 keys, and

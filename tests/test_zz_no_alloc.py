@@ -24,6 +24,8 @@ def torch_dev():
 
 def dev(torch, x, dtype):
     t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype == "f32":
+        return t.to("cuda")
     return (t.view(torch.bfloat16) if dtype == "bf16" else t.view(torch.float16)).to("cuda")
 
 
@@ -61,6 +63,12 @@ def both(torch, shape, dtype, seed):
 def test_noalloc_matches_workspace_call_twice(torch_dev):
     both(torch_dev, (1, 64, 384, 4, 32), "bf16", 7001)   # 18.9 MB of partial sums
     both(torch_dev, (1, 24, 200, 2, 32), "f16", 7002)    # then a smaller problem: 0.96 MB
+
+
+def test_noalloc_matches_workspace_call_twice_f32(torch_dev):
+    """fp32 inputs on the fp32 matrix-core kernels, whose pair gradient uses the same split of N."""
+    both(torch_dev, (1, 48, 256, 4, 32), "f32", 7005)    # 6.3 MB of partial sums
+    both(torch_dev, (1, 24, 136, 2, 16), "f32", 7006)    # then a smaller problem with D = 16
 
 
 def test_noalloc_without_pair_gradient_uses_no_scratch(torch_dev):
