@@ -77,7 +77,7 @@ struct BParams {
     const float *q, *k, *v, *mask, *pair, *out, *dout, *lse;
     float *dq, *dk, *dv, *dmask, *dpair, *delta;
     int64_t N, L, H;
-    gfx::FastDiv rblocks, nd, hd;  // row blocks (128 queries for dq, 64 keys for dk/dv), N, H
+    gfx::FastDiv rblocks, nd, hd;  // row blocks (dq_rows<D>() queries for dq, 64 keys for dk/dv), N, H
     int64_t total;
     Strides st;
     float scale;  // 1 / sqrt(D)
@@ -110,8 +110,15 @@ struct RowCopy {
 
 // ---------------------------------------------------------------------------
 // dq and delta.  Workgroup = 128 queries of one (b, n, h); wave w owns
-// queries 32w .. 32w+31 as two 16-query tiles; key blocks of 64 in LDS.
+// queries 32w .. 32w+31 as two 16-query tiles; key blocks of 64 in LDS.  At
+// D = 64 a wave owns one 16-query tile (64 queries per workgroup), which
+// keeps its registers within two waves per SIMD.
 // ---------------------------------------------------------------------------
+template <int D>
+constexpr int dq_tiles() { return D == 64 ? 1 : 2; }
+template <int D>
+constexpr int dq_rows() { return kWaves * 16 * dq_tiles<D>(); }
+
 template <int D>
 struct DqBuf {
     f32x4 k[kKB * D / 4];
@@ -121,7 +128,7 @@ struct DqBuf {
 
 template <int D, bool PAIR, bool MASK>
 __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_f32_mfma(BParams p) {
-    constexpr int kS = D / 4, kDT = D / 16, kQT = 2;
+    constexpr int kS = D / 4, kDT = D / 16, kQT = dq_tiles<D>();
     __shared__ __attribute__((aligned(16))) DqBuf<D> sm[2];
 
     const uint32_t id = (uint32_t)gfx::logical_block(blockIdx.x, p.total);
@@ -134,7 +141,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_f32_mfma(BParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
     const int nblocks = (L + kKB - 1) / kKB;
-    const int q0 = (int)qb * 128 + wave * 32;
+    const int q0 = (int)qb * dq_rows<D>() + wave * 16 * kQT;
 
     const uint32_t rowq = (uint32_t)st.q[2] * 4, rowk = (uint32_t)st.k[2] * 4, rowv = (uint32_t)st.v[2] * 4;
     const uint32_t rowo = (uint32_t)st.o[2] * 4, rowp = (uint32_t)st.pi * 4;
@@ -647,7 +654,7 @@ hipError_t launch_stage(BParams p, int64_t B, unsigned stage, hipStream_t stream
     const int64_t L = p.L;
     void* args[] = {&p};
     if (stage == kStageDq) {
-        const int64_t qblocks = (L + 127) / 128;
+        const int64_t qblocks = (L + dq_rows<D>() - 1) / dq_rows<D>();
         p.total = B * p.N * p.H * qblocks;
         p.rblocks = gfx::make_fastdiv((uint32_t)qblocks);
         return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_f32_mfma<D, PAIR, MASK>),
@@ -672,9 +679,8 @@ hipError_t launch_stage_dim(const BParams& p, int64_t B, bool pair, bool mask, u
 
 const unsigned kBwdF32MfmaStages = kStageDq | kStageDkDv | kStageDpair;
 
-// D in {16, 32} (D = 64 would spill in the dq kernel); q, k, v, out rows
-// 16-byte aligned (the C ABI checks that); pair and mask rows 16-byte
-// aligned.  Each row of q, k, v and out spans every head (row stride at
+// D in {16, 32, 64}; q, k, v, out rows 16-byte aligned (the C ABI checks
+// that); pair and mask rows 16-byte aligned.  Each row of q, k, v and out spans every head (row stride at
 // least (H - 1) head strides + D), so that rows past L fall beyond the
 // buffer of a (b, n) slice and read as zero: the dk/dv kernel sums over its
 // query rows, and those past L must add exactly nothing.  Every byte offset
@@ -684,7 +690,7 @@ const unsigned kBwdF32MfmaStages = kStageDq | kStageDkDv | kStageDpair;
 bool bwd_f32_mfma_eligible(const BwdArgs& a) {
     constexpr int64_t kLim = int64_t(1) << 31, kBig = int64_t(1) << 40;
     const int64_t L = a.L, H = a.H, D = a.D;
-    if (D != 16 && D != 32) return false;
+    if (D != 16 && D != 32 && D != 64) return false;
     if (a.N >= kLim || H >= kLim || L >= kLim) return false;
     if (a.pair && (a.st.pb % 4 || a.st.ph % 4 || a.st.pi % 4)) return false;
     if (a.mask && (a.st.mb % 4 || a.st.mn % 4)) return false;
@@ -698,7 +704,7 @@ bool bwd_f32_mfma_eligible(const BwdArgs& a) {
     if (a.mask && (L + kKB) * 4 >= kLim) return false;
     const int64_t tdim = (L + kKB - 1) / kKB;
     if (a.B * H * tdim * tdim + 2048 >= kLim) return false;
-    return a.B * a.N * H * ((L + 127) / 128) < kLim;
+    return a.B * a.N * H * ((L + 63) / 64) < kLim;
 }
 
 hipError_t launch_bwd_f32_mfma(const BwdArgs& a, unsigned stages, hipStream_t stream) {
@@ -738,8 +744,10 @@ hipError_t launch_bwd_f32_mfma(const BwdArgs& a, unsigned stages, hipStream_t st
         const int64_t chunks = ws ? a.ws_chunks : 1;
         if (a.D == 16) e = mask ? launch_dpair<16, true>(p, a.B, ws, chunks, stream)
                                 : launch_dpair<16, false>(p, a.B, ws, chunks, stream);
-        else e = mask ? launch_dpair<32, true>(p, a.B, ws, chunks, stream)
-                      : launch_dpair<32, false>(p, a.B, ws, chunks, stream);
+        else if (a.D == 32) e = mask ? launch_dpair<32, true>(p, a.B, ws, chunks, stream)
+                                     : launch_dpair<32, false>(p, a.B, ws, chunks, stream);
+        else e = mask ? launch_dpair<64, true>(p, a.B, ws, chunks, stream)
+                      : launch_dpair<64, false>(p, a.B, ws, chunks, stream);
     }
     return e;
 }

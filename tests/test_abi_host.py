@@ -276,7 +276,8 @@ def test_bwd_workspace_size():
     assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 32), E.EVO_DTYPE_F16) == ws
     assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 32), E.EVO_DTYPE_F32) == ws   # fp32 matrix cores
     assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 16), E.EVO_DTYPE_F32) == ws
-    assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 64), E.EVO_DTYPE_F32) == 0    # vector-ALU path
+    assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 64), E.EVO_DTYPE_F32) == ws
+    assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 8), E.EVO_DTYPE_F32) == 0     # vector-ALU path
     assert E.evo_attn_bwd_workspace_size((1, 384, 383, 4, 32), E.EVO_DTYPE_F32) == 0    # pair rows unaligned
     assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 64), E.EVO_DTYPE_BF16) == ws  # matrix cores for D = 64 too
     assert E.evo_attn_bwd_workspace_size((1, 8, 384, 4, 32), E.EVO_DTYPE_BF16) == 0     # N too small to split

@@ -189,12 +189,13 @@ def test_bwd_ragged(torch_dev, shape, d, dtype):
         parity(torch_dev, w, dout)
 
 
-# fp32 inputs with D in {16, 32}, 16-byte aligned bias rows (L % 4 == 0 in the
-# dense layout): every stage runs on the fp32 matrix-core kernels (N is too
+# fp32 inputs with D in {16, 32, 64}, 16-byte aligned bias rows (L % 4 == 0 in
+# the dense layout): every stage runs on the fp32 matrix-core kernels (N is too
 # small here for the pair gradient's workspace: one range of n per tile).
 # Every bias combination, bias gradients on and off, against the full backward
 # oracle.
-F32_MFMA_BWD = [(1, 2, 4, 2, 16), (1, 3, 20, 2, 32), (2, 2, 68, 3, 32), (1, 2, 132, 2, 16), (1, 1, 192, 4, 32)]
+F32_MFMA_BWD = [(1, 2, 4, 2, 16), (1, 3, 20, 2, 32), (2, 2, 68, 3, 32), (1, 2, 132, 2, 16), (1, 1, 192, 4, 32),
+                (1, 2, 36, 2, 64), (2, 2, 100, 3, 64), (1, 1, 132, 2, 64)]
 
 
 @pytest.mark.parametrize("shape", F32_MFMA_BWD, ids=lambda s: "x".join(map(str, s)))
@@ -414,13 +415,14 @@ def test_bwd_pair_gradient_split_over_n(torch_dev, dtype, L):
         np.testing.assert_array_equal(a, b)   # only the pair gradient takes another route
 
 
-def test_bwd_f32_split_over_n_head_dim_16(torch_dev):
-    """fp32, D = 16, with the workspace (pair gradient split over N) and without: only dpair takes another
-    route, and it stays within the fp32 bound either way."""
+@pytest.mark.parametrize("d", [16, 64])
+def test_bwd_f32_split_over_n_head_dims(torch_dev, d):
+    """fp32, D = 16 and 64, with the workspace (pair gradient split over N) and without: only dpair takes
+    another route, and it stays within the fp32 bound either way."""
     import evoformer_biased_attention_amd as E
-    w = S.random_problem(1, 32, 136, 3, 16, dtype="f32", seed=1616, mask="tail", pair="normal", mask_frac=0.2)
+    w = S.random_problem(1, 32, 136, 3, d, dtype="f32", seed=1600 + d, mask="tail", pair="normal", mask_frac=0.2)
     assert E.evo_attn_bwd_workspace_size(w.shape, E.EVO_DTYPE_F32) > 0
-    dout = S.random_dout(w.shape, "f32", seed=1617)
+    dout = S.random_dout(w.shape, "f32", seed=1601 + d)
     split = parity(torch_dev, w, dout)
     single = parity(torch_dev, w, dout, use_ws=False)
     for a, b in zip(split[:4], single[:4]):
