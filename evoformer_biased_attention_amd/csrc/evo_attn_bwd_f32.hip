@@ -31,7 +31,10 @@
 // the fp32 forward), so that a 16-row operand read and a 4-row transposed read
 // spread over the banks.  Copies into LDS are untracked (see
 // dma16_untracked) and waited for explicitly before each barrier.  Buffer
-// resources return zeros past their range: rows past L read as zero.
+// resources return zeros past their range: rows past L read as zero.  Bias
+// rows that do not start 16-byte aligned (STAGED) are read with unaligned
+// 16-byte loads over their exact range, the mask row passing through
+// registers into LDS, and the pair gradient is written element by element.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -44,6 +47,7 @@ namespace evo {
 namespace {
 
 using gfx::bload16;
+using gfx::bload16_any;
 using gfx::dma16_untracked;
 using gfx::f32x4;
 using gfx::kLog2e;
@@ -126,7 +130,7 @@ struct DqBuf {
     f32x4 mt[kKB / 4];
 };
 
-template <int D, bool PAIR, bool MASK>
+template <int D, bool PAIR, bool MASK, bool STAGED>
 __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_f32_mfma(BParams p) {
     constexpr int kS = D / 4, kDT = D / 16, kQT = dq_tiles<D>();
     __shared__ __attribute__((aligned(16))) DqBuf<D> sm[2];
@@ -151,9 +155,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_f32_mfma(BParams p) {
     const Rsrc rv = make_rsrc(p.v + b * st.v[0] + n * st.v[1] + h * st.v[3], (uint32_t)(L - 1) * rowv + D * 4);
     const Rsrc ro = make_rsrc(p.out + os, (uint32_t)(L - 1) * rowo + D * 4);
     const Rsrc rdo = make_rsrc(p.dout + os, (uint32_t)(L - 1) * rowo + D * 4);
+    const uint32_t pbytes = (uint32_t)(L - 1) * rowp + (uint32_t)L * 4u, mbytes = (uint32_t)L * 4u;
     const Rsrc rp = make_rsrc(PAIR ? p.pair + b * st.pb + h * st.ph : p.q,
-                              PAIR ? (((uint32_t)(L - 1) * rowp + (uint32_t)L * 4u) + 15u) & ~15u : 0u);
-    const Rsrc rm = make_rsrc(MASK ? p.mask + b * st.mb + n * st.mn : p.q, MASK ? ((uint32_t)L * 4u + 15u) & ~15u : 0u);
+                              PAIR ? (STAGED ? pbytes : (pbytes + 15u) & ~15u) : 0u);
+    const Rsrc rm = make_rsrc(MASK ? p.mask + b * st.mb + n * st.mn : p.q,
+                              MASK ? (STAGED ? mbytes : (mbytes + 15u) & ~15u) : 0u);
     const int64_t lrow = ((b * p.N + n) * p.H + h) * st.lrow;
 
     // per query: Q/sqrt(D) and dO (B operands, lane group g's d-range), delta, lse
@@ -186,11 +192,18 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_f32_mfma(BParams p) {
     RowCopy<D> ck, cv;
     ck.init(wave, lane, rowk);
     cv.init(wave, lane, rowv);
+    uint4 mstage;  // STAGED: the mask chunk between its load and its landing in LDS
     auto copy_block = [&](int blk, DqBuf<D>* __restrict__ dst) {
         const uint32_t k0 = (uint32_t)blk * kKB;
         ck.issue(rk, dst->k, wave, k0 * rowk);
         cv.issue(rv, dst->v, wave, k0 * rowv);
-        if (MASK && wave == 0 && lane < 16) dma16_untracked(rm, &dst->mt[0], 16u * lane + k0 * 4u);
+        if (MASK && wave == 0 && lane < 16) {
+            if (STAGED) mstage = bload16_any(rm, 16u * lane + k0 * 4u, mbytes);
+            else dma16_untracked(rm, &dst->mt[0], 16u * lane + k0 * 4u);
+        }
+    };
+    auto land_mask = [&](DqBuf<D>* __restrict__ dst) {
+        if (STAGED && MASK && wave == 0 && lane < 16) dst->mt[lane] = __builtin_bit_cast(f32x4, mstage);
     };
     // the wave's pair rows in the score layout: tile t, key tile kt -> pair[q0 + 16t + c][k0 + 16kt + 4g .. +3]
     f32x4 pr[kQT][kKT];
@@ -198,8 +211,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_f32_mfma(BParams p) {
         const uint32_t k0 = (uint32_t)blk * kKB;
         for (int t = 0; t < kQT; ++t)
             for (int kt = 0; kt < kKT; ++kt)
-                pr[t][kt] = __builtin_bit_cast(
-                    f32x4, bload16(rp, (uint32_t)(q0 + 16 * t + c) * rowp + 4u * (k0 + 16 * kt + 4 * g)));
+            {
+                const uint32_t off = (uint32_t)(q0 + 16 * t + c) * rowp + 4u * (k0 + 16 * kt + 4 * g);
+                pr[t][kt] = __builtin_bit_cast(f32x4, STAGED ? bload16_any(rp, off, pbytes) : bload16(rp, off));
+            }
     };
 
     f32x4 dqacc[kQT][kDT];
@@ -207,6 +222,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_f32_mfma(BParams p) {
         for (int dt = 0; dt < kDT; ++dt) dqacc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     copy_block(0, &sm[0]);
+    land_mask(&sm[0]);
     if (PAIR) load_pair(0);
     gfx::wait_all();
     __syncthreads();
@@ -254,6 +270,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_f32_mfma(BParams p) {
                     for (int t = 0; t < kQT; ++t)
                         dqacc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, acc[t][kt][r], dqacc[t][dt], 0, 0, 0);
                 }
+        if (it + 1 < nblocks) land_mask(&sm[(it & 1) ^ 1]);
         gfx::wait_all();  // the next block's copies and pair rows have landed
         __syncthreads();
     }
@@ -459,7 +476,7 @@ struct PairParams {
     int64_t bh;          // B * H
 };
 
-template <int D, bool MASK>
+template <int D, bool MASK, bool STAGED>
 __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_f32_mfma(PairParams pp) {
     constexpr int kS = D / 4;
     const BParams& p = pp.p;
@@ -490,23 +507,32 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_f32_mfma(PairParams 
     // pair[b, h, qi, j0 + 16kt + 4g .. +3]: the accumulator input of every S^T product
     f32x4 pbs[kKT];
     {
-        const Rsrc rp = make_rsrc(p.pair + b * st.pb + h * st.ph, ((last * rowp + (uint32_t)L * 4u) + 15u) & ~15u);
-        for (int kt = 0; kt < kKT; ++kt)
-            pbs[kt] = __builtin_bit_cast(f32x4, bload16(rp, (uint32_t)qi * rowp + 4u * (uint32_t)(j0 + 16 * kt + 4 * g)));
+        const uint32_t pbytes = last * rowp + (uint32_t)L * 4u;
+        const Rsrc rp = make_rsrc(p.pair + b * st.pb + h * st.ph, STAGED ? pbytes : (pbytes + 15u) & ~15u);
+        for (int kt = 0; kt < kKT; ++kt) {
+            const uint32_t off = (uint32_t)qi * rowp + 4u * (uint32_t)(j0 + 16 * kt + 4 * g);
+            pbs[kt] = __builtin_bit_cast(f32x4, STAGED ? bload16_any(rp, off, pbytes) : bload16(rp, off));
+        }
     }
 
     RowCopy<D> ck, cv;
     ck.init(wave, lane, rowk);
     cv.init(wave, lane, rowv);
+    uint4 mstage;  // STAGED: the mask chunk between its load and its landing in LDS
     auto copy_step = [&](int64_t n, PrBuf<D>* __restrict__ dst) {
         const Rsrc rk = make_rsrc(p.k + b * st.k[0] + n * st.k[1] + h * st.k[3], last * rowk + D * 4);
         const Rsrc rv = make_rsrc(p.v + b * st.v[0] + n * st.v[1] + h * st.v[3], last * rowv + D * 4);
         ck.issue(rk, dst->k, wave, (uint32_t)j0 * rowk);
         cv.issue(rv, dst->v, wave, (uint32_t)j0 * rowv);
         if (MASK && wave == 0 && lane < 16) {
-            const Rsrc rm = make_rsrc(p.mask + b * st.mb + n * st.mn, ((uint32_t)L * 4u + 15u) & ~15u);
-            dma16_untracked(rm, &dst->mt[0], 16u * lane + (uint32_t)j0 * 4u);
+            const uint32_t mbytes = (uint32_t)L * 4u;
+            const Rsrc rm = make_rsrc(p.mask + b * st.mb + n * st.mn, STAGED ? mbytes : (mbytes + 15u) & ~15u);
+            if (STAGED) mstage = bload16_any(rm, 16u * lane + (uint32_t)j0 * 4u, mbytes);
+            else dma16_untracked(rm, &dst->mt[0], 16u * lane + (uint32_t)j0 * 4u);
         }
+    };
+    auto land_mask = [&](PrBuf<D>* __restrict__ dst) {
+        if (STAGED && MASK && wave == 0 && lane < 16) dst->mt[lane] = __builtin_bit_cast(f32x4, mstage);
     };
     // this lane's Q and dO d-range, lse and delta at sequence n, as loaded
     // (converted when used, so that the loads stay in flight meanwhile)
@@ -531,6 +557,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_f32_mfma(PairParams 
     for (int kt = 0; kt < kKT; ++kt) ds[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     copy_step(n0, &sm[0]);
+    land_mask(&sm[0]);
     load_rows(n0);
     gfx::wait_all();
     __syncthreads();
@@ -572,6 +599,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_f32_mfma(PairParams 
             for (int r = 0; r < 4; ++r)
                 ds[kt][r] = fmaf(__builtin_amdgcn_exp2f(fmaf(acc[r], kLog2e, -lse2)), dpm[r], ds[kt][r]);
         }
+        if (n + 1 < n1) land_mask(&sm[(it & 1) ^ 1]);
         gfx::wait_all();  // the next n's copies and rows have landed
         __syncthreads();
     }
@@ -585,9 +613,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_f32_mfma(PairParams 
             *reinterpret_cast<f32x4*>(pp.ws + ((chunk * pp.bh + b * p.H + h) * p.L + qi) * bwd_ws_row(p.L) + j) = ds[kt];
         } else {
             float* dst = p.dpair + b * st.pb + h * st.ph + (int64_t)qi * st.pi + j;
-            if (j + 4 <= L) *reinterpret_cast<f32x4*>(dst) = ds[kt];
+            if (!STAGED && j + 4 <= L) *reinterpret_cast<f32x4*>(dst) = ds[kt];
             else
-                for (int e = 0; e < L - j; ++e) dst[e] = ds[kt][e];
+                for (int e = 0; e < 4 && e < L - j; ++e) dst[e] = ds[kt][e];
         }
     }
 }
@@ -601,6 +629,7 @@ struct ReduceF32 {
     int64_t quads, chunks;  // B*H*L*bwd_ws_row(L) / 4; ranges
     int64_t L, H;
     int64_t pb, ph, pi;     // strides of dpair
+    int aligned;            // dpair rows start 16-byte aligned
 };
 
 __global__ __launch_bounds__(256) void bwd_dpair_reduce_f32(ReduceF32 r) {
@@ -612,13 +641,13 @@ __global__ __launch_bounds__(256) void bwd_dpair_reduce_f32(ReduceF32 r) {
     if (j >= r.L) return;
     const int64_t bh = row / r.L, i = row - bh * r.L, b = bh / r.H, h = bh - b * r.H;
     float* dst = r.dpair + b * r.pb + h * r.ph + i * r.pi + j;
-    if (j + 4 <= r.L) *reinterpret_cast<f32x4*>(dst) = t;
+    if (r.aligned && j + 4 <= r.L) *reinterpret_cast<f32x4*>(dst) = t;
     else
-        for (int e = 0; e < r.L - j; ++e) dst[e] = t[e];
+        for (int e = 0; e < 4 && e < r.L - j; ++e) dst[e] = t[e];
 }
 
 template <int D, bool MASK>
-hipError_t launch_dpair(const BParams& base, int64_t B, float* ws, int64_t chunks, hipStream_t stream) {
+hipError_t launch_dpair(const BParams& base, int64_t B, float* ws, int64_t chunks, bool staged, hipStream_t stream) {
     PairParams pp;
     pp.p = base;
     const int64_t tdim = (base.L + kKB - 1) / kKB;
@@ -631,8 +660,9 @@ hipError_t launch_dpair(const BParams& base, int64_t B, float* ws, int64_t chunk
     pp.chd = gfx::make_fastdiv((uint32_t)chunks);
     pp.bh = B * base.H;
     void* args[] = {&pp};
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dpair_f32_mfma<D, MASK>),
-                                   dim3((unsigned)pp.p.total), dim3(kWaves * 64), args, 0, stream);
+    const void* kern = staged ? reinterpret_cast<const void*>(&bwd_dpair_f32_mfma<D, MASK, true>)
+                              : reinterpret_cast<const void*>(&bwd_dpair_f32_mfma<D, MASK, false>);
+    hipError_t e = hipLaunchKernel(kern, dim3((unsigned)pp.p.total), dim3(kWaves * 64), args, 0, stream);
     if (e != hipSuccess || !ws) return e;
     ReduceF32 r;
     r.ws = ws;
@@ -642,6 +672,7 @@ hipError_t launch_dpair(const BParams& base, int64_t B, float* ws, int64_t chunk
     r.L = base.L;
     r.H = base.H;
     r.pb = base.st.pb, r.ph = base.st.ph, r.pi = base.st.pi;
+    r.aligned = !(r.pb % 4 || r.ph % 4 || r.pi % 4);
     const int64_t blocks = (r.quads + 255) / 256;
     if (blocks >= (int64_t(1) << 31)) return hipErrorInvalidConfiguration;
     void* rargs[] = {&r};
@@ -650,15 +681,16 @@ hipError_t launch_dpair(const BParams& base, int64_t B, float* ws, int64_t chunk
 }
 
 template <int D, bool PAIR, bool MASK>
-hipError_t launch_stage(BParams p, int64_t B, unsigned stage, hipStream_t stream) {
+hipError_t launch_stage(BParams p, int64_t B, unsigned stage, bool staged, hipStream_t stream) {
     const int64_t L = p.L;
     void* args[] = {&p};
     if (stage == kStageDq) {
         const int64_t qblocks = (L + dq_rows<D>() - 1) / dq_rows<D>();
         p.total = B * p.N * p.H * qblocks;
         p.rblocks = gfx::make_fastdiv((uint32_t)qblocks);
-        return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_f32_mfma<D, PAIR, MASK>),
-                               dim3((unsigned)p.total), dim3(kWaves * 64), args, 0, stream);
+        const void* kern = staged ? reinterpret_cast<const void*>(&bwd_dq_f32_mfma<D, PAIR, MASK, true>)
+                                  : reinterpret_cast<const void*>(&bwd_dq_f32_mfma<D, PAIR, MASK, false>);
+        return hipLaunchKernel(kern, dim3((unsigned)p.total), dim3(kWaves * 64), args, 0, stream);
     }
     const int64_t kblocks = (L + kKB - 1) / kKB;
     p.total = B * p.N * kblocks;
@@ -668,11 +700,12 @@ hipError_t launch_stage(BParams p, int64_t B, unsigned stage, hipStream_t stream
 }
 
 template <int D>
-hipError_t launch_stage_dim(const BParams& p, int64_t B, bool pair, bool mask, unsigned stage, hipStream_t stream) {
-    if (pair && mask) return launch_stage<D, true, true>(p, B, stage, stream);
-    if (pair) return launch_stage<D, true, false>(p, B, stage, stream);
-    if (mask) return launch_stage<D, false, true>(p, B, stage, stream);
-    return launch_stage<D, false, false>(p, B, stage, stream);
+hipError_t launch_stage_dim(const BParams& p, int64_t B, bool pair, bool mask, unsigned stage, bool staged,
+                            hipStream_t stream) {
+    if (pair && mask) return launch_stage<D, true, true>(p, B, stage, staged, stream);
+    if (pair) return launch_stage<D, true, false>(p, B, stage, staged, stream);
+    if (mask) return launch_stage<D, false, true>(p, B, stage, staged, stream);
+    return launch_stage<D, false, false>(p, B, stage, false, stream);
 }
 
 }  // namespace
@@ -680,8 +713,9 @@ hipError_t launch_stage_dim(const BParams& p, int64_t B, bool pair, bool mask, u
 const unsigned kBwdF32MfmaStages = kStageDq | kStageDkDv | kStageDpair;
 
 // D in {16, 32, 64}; q, k, v, out rows 16-byte aligned (the C ABI checks
-// that); pair and mask rows 16-byte aligned.  Each row of q, k, v and out spans every head (row stride at
-// least (H - 1) head strides + D), so that rows past L fall beyond the
+// that); bias rows at any stride (unaligned ones are staged).  Each row of
+// q, k, v and out spans every head (row stride at least (H - 1) head
+// strides + D), so that rows past L fall beyond the
 // buffer of a (b, n) slice and read as zero: the dk/dv kernel sums over its
 // query rows, and those past L must add exactly nothing.  Every byte offset
 // the kernels form stays below 2^31: rows up to 128 past L of every head,
@@ -692,8 +726,6 @@ bool bwd_f32_mfma_eligible(const BwdArgs& a) {
     const int64_t L = a.L, H = a.H, D = a.D;
     if (D != 16 && D != 32 && D != 64) return false;
     if (a.N >= kLim || H >= kLim || L >= kLim) return false;
-    if (a.pair && (a.st.pb % 4 || a.st.ph % 4 || a.st.pi % 4)) return false;
-    if (a.mask && (a.st.mb % 4 || a.st.mn % 4)) return false;
     for (const int64_t* t : {a.st.q, a.st.k, a.st.v, a.st.o}) {
         const int64_t row = t[2], head = t[3];
         if (row < 0 || head < 0 || row >= kBig || head >= kBig) return false;
@@ -730,24 +762,26 @@ hipError_t launch_bwd_f32_mfma(const BwdArgs& a, unsigned stages, hipStream_t st
     p.st = a.st;
     p.scale = (float)(1.0 / std::sqrt((double)a.D));
     const bool pair = a.pair != nullptr, mask = a.mask != nullptr;
+    // bias rows that do not all start 16-byte aligned are staged
+    const bool staged = (pair && (a.st.pb % 4 || a.st.ph % 4 || a.st.pi % 4)) || (mask && (a.st.mb % 4 || a.st.mn % 4));
     hipError_t e = hipSuccess;
     for (unsigned stage : {kStageDq, kStageDkDv}) {
         if (!(stages & stage)) continue;
-        if (a.D == 16) e = launch_stage_dim<16>(p, a.B, pair, mask, stage, stream);
-        else if (a.D == 32) e = launch_stage_dim<32>(p, a.B, pair, mask, stage, stream);
-        else e = launch_stage_dim<64>(p, a.B, pair, mask, stage, stream);
+        if (a.D == 16) e = launch_stage_dim<16>(p, a.B, pair, mask, stage, staged, stream);
+        else if (a.D == 32) e = launch_stage_dim<32>(p, a.B, pair, mask, stage, staged, stream);
+        else e = launch_stage_dim<64>(p, a.B, pair, mask, stage, staged, stream);
         if (e != hipSuccess) return e;
     }
     if ((stages & kStageDpair) && a.dpair) {
         // with a workspace of at least two ranges, split N; else one range per tile
         float* ws = a.ws && a.ws_chunks >= 2 ? a.ws : nullptr;
         const int64_t chunks = ws ? a.ws_chunks : 1;
-        if (a.D == 16) e = mask ? launch_dpair<16, true>(p, a.B, ws, chunks, stream)
-                                : launch_dpair<16, false>(p, a.B, ws, chunks, stream);
-        else if (a.D == 32) e = mask ? launch_dpair<32, true>(p, a.B, ws, chunks, stream)
-                                     : launch_dpair<32, false>(p, a.B, ws, chunks, stream);
-        else e = mask ? launch_dpair<64, true>(p, a.B, ws, chunks, stream)
-                      : launch_dpair<64, false>(p, a.B, ws, chunks, stream);
+        if (a.D == 16) e = mask ? launch_dpair<16, true>(p, a.B, ws, chunks, staged, stream)
+                                : launch_dpair<16, false>(p, a.B, ws, chunks, staged, stream);
+        else if (a.D == 32) e = mask ? launch_dpair<32, true>(p, a.B, ws, chunks, staged, stream)
+                                     : launch_dpair<32, false>(p, a.B, ws, chunks, staged, stream);
+        else e = mask ? launch_dpair<64, true>(p, a.B, ws, chunks, staged, stream)
+                      : launch_dpair<64, false>(p, a.B, ws, chunks, staged, stream);
     }
     return e;
 }

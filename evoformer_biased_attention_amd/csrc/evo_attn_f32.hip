@@ -5,7 +5,7 @@
 // hmyw.cn, sections 4, 5.2 and 5.4) with fp32 operands and fp32 arithmetic
 // throughout.
 //
-// fwd_f32_mfma (D = 16, 32, 64, bias rows 16-byte aligned): both products on
+// fwd_f32_mfma (D = 16, 32, 64, any bias strides): both products on
 // the matrix cores with v_mfma_f32_16x16x4f32, which multiplies fp32 values
 // and accumulates in fp32.  The layout follows the 16-bit kernel: scores are
 // formed transposed (S^T = K.Q^T, lane c + 16g holds query c and keys 4g ..
@@ -24,10 +24,11 @@
 // layout whose 16-byte chunks are XOR-swizzled by row so that the operand
 // reads spread over the banks.  Infinite and NaN values follow IEEE
 // arithmetic: a -inf bias gives its key zero weight, a row of all -inf gives
-// out = 0 and lse = -inf, and NaN propagates.
+// out = 0 and lse = -inf, and NaN propagates.  Bias rows that do not start
+// 16-byte aligned (STAGED) are read with unaligned 16-byte loads over the
+// exact range, and the mask row passes through registers into LDS.
 //
-// fwd_f32_kernel (every other case: D = 8, or bias rows that are not 16-byte
-// aligned): the vector ALUs.  One 64-lane wavefront per (b, n, h, block of 64
+// fwd_f32_kernel (D = 8): the vector ALUs.  One 64-lane wavefront per (b, n, h, block of 64
 // queries); each lane owns one query and keeps q, the output accumulator and
 // its running max / sum in registers.  Keys are visited in blocks of 64
 // staged in LDS, and each key updates the lane's state with a one-pass
@@ -47,6 +48,7 @@ using gfx::f32x4;
 using gfx::Rsrc;
 using gfx::make_rsrc;
 using gfx::bload16;
+using gfx::bload16_any;
 using gfx::dma16_untracked;
 using gfx::kOOB;
 using gfx::kLog2e;
@@ -170,7 +172,7 @@ struct MParams {
     float scale;  // 1 / sqrt(D)
 };
 
-template <int D, bool PAIR, bool MASK>
+template <int D, bool PAIR, bool MASK, bool STAGED>
 __global__ __launch_bounds__(kMWaves * 64, 2) void fwd_f32_mfma(MParams p) {
     constexpr int kCPR = D / 4;       // 16-byte chunks per row
     constexpr int kS = D / 4;         // contraction slices of the score product (4 d-values each)
@@ -197,12 +199,16 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void fwd_f32_mfma(MParams p) {
     const Rsrc rq = make_rsrc(p.q + b * st.q[0] + n * st.q[1] + h * st.q[3], (uint32_t)(L - 1) * rowq + D * 4);
     const Rsrc rk = make_rsrc(p.k + b * st.k[0] + n * st.k[1] + h * st.k[3], (uint32_t)(L - 1) * rowk + D * 4);
     const Rsrc rv = make_rsrc(p.v + b * st.v[0] + n * st.v[1] + h * st.v[3], (uint32_t)(L - 1) * rowv + D * 4);
-    // bias ranges end at the 16-byte boundary after the last element (rows are
-    // 16-byte aligned, so that granule lies in the page of the last element)
+    // bias ranges: rows 16-byte aligned, up to the 16-byte boundary after the
+    // last element (that granule lies in the page of the last element);
+    // STAGED, exactly the elements, whose last chunk bload16_any then reads
+    // element by element
     const uint32_t rowp = (uint32_t)st.pi * 4;
+    const uint32_t pbytes = (uint32_t)(L - 1) * rowp + (uint32_t)L * 4u, mbytes = (uint32_t)L * 4u;
     const Rsrc rp = make_rsrc(PAIR ? p.pair + b * st.pb + h * st.ph : p.q,
-                              PAIR ? (((uint32_t)(L - 1) * rowp + (uint32_t)L * 4u) + 15u) & ~15u : 0u);
-    const Rsrc rm = make_rsrc(MASK ? p.mask + b * st.mb + n * st.mn : p.q, MASK ? ((uint32_t)L * 4u + 15u) & ~15u : 0u);
+                              PAIR ? (STAGED ? pbytes : (pbytes + 15u) & ~15u) : 0u);
+    const Rsrc rm = make_rsrc(MASK ? p.mask + b * st.mb + n * st.mn : p.q,
+                              MASK ? (STAGED ? mbytes : (mbytes + 15u) & ~15u) : 0u);
 
     // Q operands, scaled: lane (c + 16g) holds q[q0 + 16t + c][gD/4 + s] / sqrt(D)
     // for slice s; rows past L read as zero
@@ -230,6 +236,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void fwd_f32_mfma(MParams p) {
         kvo[i][0] = (uint32_t)row * rowk + 16u * chunk;
         kvo[i][1] = (uint32_t)row * rowv + 16u * chunk;
     }
+    uint4 mstage;  // STAGED: the mask chunk between its load and its landing in LDS
     auto copy_block = [&](int blk, MBuf<D>* __restrict__ dst) {
         const uint32_t k0 = (uint32_t)blk * kMKB;
         for (int i = 0; i < kSegs / kMWaves; ++i) {
@@ -237,7 +244,13 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void fwd_f32_mfma(MParams p) {
             dma16_untracked(rk, &dst->k[64 * seg], kvo[i][0] + k0 * rowk);
             dma16_untracked(rv, &dst->v[64 * seg], kvo[i][1] + k0 * rowv);
         }
-        if (MASK && wave == 0 && lane < 16) dma16_untracked(rm, &dst->mt[0], 16u * lane + k0 * 4u);
+        if (MASK && wave == 0 && lane < 16) {
+            if (STAGED) mstage = bload16_any(rm, 16u * lane + k0 * 4u, mbytes);
+            else dma16_untracked(rm, &dst->mt[0], 16u * lane + k0 * 4u);
+        }
+    };
+    auto land_mask = [&](MBuf<D>* __restrict__ dst) {
+        if (STAGED && MASK && wave == 0 && lane < 16) dst->mt[lane] = __builtin_bit_cast(f32x4, mstage);
     };
     // ---- the wave's pair rows for one block, straight into registers in the
     // score layout: tile t, key tile kt -> pair[q0 + 16t + c][k0 + 16kt + 4g .. +3] ----
@@ -248,8 +261,10 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void fwd_f32_mfma(MParams p) {
             // query rows past L: their results are never stored; rows past the
             // matrix read as zero
             const uint32_t row = (uint32_t)(q0 + 16 * t + c);
-            for (int kt = 0; kt < kMKT; ++kt)
-                pr[t][kt] = __builtin_bit_cast(f32x4, bload16(rp, row * rowp + 4u * (k0 + 16 * kt + 4 * g)));
+            for (int kt = 0; kt < kMKT; ++kt) {
+                const uint32_t off = row * rowp + 4u * (k0 + 16 * kt + 4 * g);
+                pr[t][kt] = __builtin_bit_cast(f32x4, STAGED ? bload16_any(rp, off, pbytes) : bload16(rp, off));
+            }
         }
     };
 
@@ -262,6 +277,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void fwd_f32_mfma(MParams p) {
     }
 
     copy_block(0, &sm[0]);
+    land_mask(&sm[0]);
     if (PAIR) load_pair(0);
     gfx::wait_all();
     __syncthreads();
@@ -331,6 +347,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void fwd_f32_mfma(MParams p) {
                         oacc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf, acc[t][kt][r], oacc[t][dt], 0, 0, 0);
                 }
             }
+        if (it + 1 < nblocks) land_mask(&sm[(it & 1) ^ 1]);
         gfx::wait_all();  // the next block's copies and pair rows have landed
         __syncthreads();
     }
@@ -356,8 +373,12 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void fwd_f32_mfma(MParams p) {
 template <int D, bool PAIR, bool MASK>
 hipError_t launch_mfma_variant(MParams& p, hipStream_t stream) {
     void* args[] = {&p};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_f32_mfma<D, PAIR, MASK>), dim3((unsigned)p.total),
-                           dim3(kMWaves * 64), args, 0, stream);
+    // bias rows that do not all start 16-byte aligned are staged
+    const Strides& s = p.st;
+    const bool staged = (PAIR && (s.pb % 4 || s.ph % 4 || s.pi % 4)) || (MASK && (s.mb % 4 || s.mn % 4));
+    const void* k = staged ? reinterpret_cast<const void*>(&fwd_f32_mfma<D, PAIR, MASK, true>)
+                           : reinterpret_cast<const void*>(&fwd_f32_mfma<D, PAIR, MASK, false>);
+    return hipLaunchKernel(k, dim3((unsigned)p.total), dim3(kMWaves * 64), args, 0, stream);
 }
 
 template <int D>
@@ -369,13 +390,11 @@ hipError_t launch_mfma_dim(MParams& p, hipStream_t stream) {
     return launch_mfma_variant<D, false, false>(p, stream);
 }
 
-// Whether the matrix-core kernel takes these arguments: D in {16, 32, 64},
-// bias rows that start 16-byte aligned, and every byte offset it forms
-// (rows of one slice or pair matrix, up to 128 rows past L) below 2^31.
+// Whether the matrix-core kernel takes these arguments: D in {16, 32, 64}
+// and every byte offset it forms (rows of one slice or pair matrix, up to 128
+// rows past L) below 2^31.
 bool mfma_eligible(const FwdArgs& a) {
     if (a.D != 16 && a.D != 32 && a.D != 64) return false;
-    if (a.pair && (a.st.pb % 4 || a.st.ph % 4 || a.st.pi % 4)) return false;
-    if (a.mask && (a.st.mb % 4 || a.st.mn % 4)) return false;
     constexpr int64_t kLim = int64_t(1) << 31;
     for (int64_t rs : {a.st.q[2], a.st.k[2], a.st.v[2]})
         if ((a.L + kMBlockQ) * rs * 4 + a.D * 4 >= kLim) return false;

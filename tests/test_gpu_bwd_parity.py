@@ -211,6 +211,24 @@ def test_bwd_f32_matrix_core_path(torch_dev, shape, bias):
         parity(torch_dev, w, dout, want_dmask=False, want_dpair=False)
 
 
+F32_STAGED_BWD = [(1, 2, 5, 2, 16), (1, 3, 17, 2, 32), (2, 2, 65, 3, 32), (1, 2, 99, 2, 64), (1, 24, 130, 2, 32)]
+
+
+@pytest.mark.parametrize("shape", F32_STAGED_BWD, ids=lambda s: "x".join(map(str, s)))
+def test_bwd_f32_matrix_core_unaligned_bias_rows(torch_dev, shape):
+    """L % 4 != 0: the dense bias rows start at every 4-byte alignment, so the fp32 matrix-core kernels read
+    the pair rows with unaligned loads over their exact range, stage the mask row through registers and write
+    the pair gradient element by element (through the workspace reduction for N = 24).  Large biases sit on
+    the last element of every pair and mask row."""
+    B, N, L, H, D = shape
+    w = with_edge_biases(S.random_problem(B, N, L, H, D, dtype="f32", seed=sum(shape) * 11, mask="tail",
+                                          pair="normal", mask_frac=0.3))
+    dout = S.random_dout(w.shape, "f32", seed=L + 5 * D)
+    parity(torch_dev, w, dout)
+    if N >= 16:
+        parity(torch_dev, w, dout, use_ws=False)
+
+
 def test_bwd_f32_matrix_core_masked_rows(torch_dev):
     """fp32 backward with -inf masks on part of a row and on a whole row (no gradient passes through it),
     and a peaked softmax (bias scale 8), on the matrix-core path."""

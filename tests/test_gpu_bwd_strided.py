@@ -136,26 +136,26 @@ def test_padded_lse_and_pair_rows(torch_dev, use_ws, dtype):
     assert torch.isnan(d[..., L:]).all()
 
 
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
 @pytest.mark.parametrize("use_ws", [True, False], ids=["workspace", "no_workspace"])
 @pytest.mark.parametrize("L", [77, 96])
-def test_unaligned_bias_rows(torch_dev, L, use_ws):
+def test_unaligned_bias_rows(torch_dev, L, use_ws, dtype):
     """Pair rows L + 1 apart (matrices L + 3 rows apart) and mask rows L + 3 apart: every bias row starts
-    at another 2-byte alignment, also for L % 8 == 0, so the bias tiles are staged through registers.
+    at another alignment, also for L % 8 == 0, so the bias tiles are staged through registers.
     dpair and dmask are written in the same layouts and their padding is left alone."""
     torch = torch_dev
     B, N, H, D = 1, 24, 2, 32
-    dtype = "f16"
     w = S.random_problem(B, N, L, H, D, dtype=dtype, seed=L + 300, mask="tail", pair="normal")
     pf = S.storage_to_f32(w.pair, dtype).copy()
     pf[..., :, -1] = 3.0
     w.pair = S.to_storage(pf, dtype)
     dout = S.random_dout(w.shape, dtype, seed=L + 301)
     pad_i, pad_l = L + 1, L + 3
-    wide = np.zeros((B, 1, H, pad_l, pad_i), np.uint16)
+    wide = np.zeros((B, 1, H, pad_l, pad_i), w.pair.dtype)
     wide[..., :L, :L] = w.pair
     pair_full = to_dev(torch, wide, dtype)
     pair = pair_full[..., :L, :L]
-    wide_m = np.zeros((B, N, 1, 1, L + 3), np.uint16)
+    wide_m = np.zeros((B, N, 1, 1, L + 3), w.mask.dtype)
     wide_m[..., :L] = w.mask
     mask = to_dev(torch, wide_m, dtype)[..., :L]
     q, k, v, do = (to_dev(torch, x, dtype) for x in (w.q, w.k, w.v, dout))

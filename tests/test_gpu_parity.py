@@ -162,9 +162,10 @@ def test_ragged_f32(torch_dev, shape):
     parity_full(torch_dev, w)
 
 
-# fp32 inputs with 16-byte aligned bias rows (L % 4 == 0 in the dense layout)
-# and D in {16, 32, 64} take the matrix-core fp32 kernel; D = 8 and unaligned
-# rows take the vector-ALU one.  Both against the full oracle.
+# fp32 inputs with D in {16, 32, 64} take the matrix-core fp32 kernel (bias
+# rows that are not 16-byte aligned, L % 4 != 0 in the dense layout, through
+# its staged variant); D = 8 takes the vector-ALU one.  All against the full
+# oracle.
 F32_MFMA_SHAPES = [(1, 2, 4, 2, 16), (1, 3, 20, 2, 32), (2, 2, 68, 3, 32), (1, 2, 132, 2, 64), (1, 1, 256, 4, 16),
                    (1, 2, 100, 2, 32), (2, 3, 64, 2, 64), (1, 1, 192, 1, 32)]
 
@@ -179,7 +180,31 @@ def test_f32_matrix_core_path(torch_dev, shape, bias):
     parity_full(torch_dev, w)
 
 
-@pytest.mark.parametrize("L", [64, 96])
+F32_STAGED_SHAPES = [(1, 2, 5, 2, 16), (1, 3, 17, 2, 32), (2, 2, 65, 3, 32), (1, 2, 99, 2, 64), (1, 1, 130, 4, 16),
+                     (1, 2, 383, 2, 32)]
+
+
+@pytest.mark.parametrize("shape", F32_STAGED_SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("bias", ["both", "mask", "pair"])
+def test_f32_matrix_core_unaligned_bias_rows(torch_dev, shape, bias):
+    """L % 4 != 0: the dense bias rows start at every 4-byte alignment, so the fp32 matrix-core kernel
+    reads the pair rows with unaligned 16-byte loads over their exact range and stages the mask row through
+    registers.  Large biases sit on the last element of every pair and mask row."""
+    B, N, L, H, D = shape
+    w = S.random_problem(B, N, L, H, D, dtype="f32", seed=sum(shape) * 3 + len(bias),
+                         mask="tail" if bias in ("both", "mask") else None,
+                         pair="normal" if bias in ("both", "pair") else None, mask_frac=0.3)
+    if w.pair is not None:
+        w.pair = w.pair.copy()
+        w.pair[..., -1] = 3.0
+    if w.mask is not None:
+        w.mask = w.mask.copy()
+        w.mask[..., -1] = 2.0
+    say(f"f32 matrix-core path, unaligned bias rows {shape} bias={bias}")
+    parity_full(torch_dev, w)
+
+
+@pytest.mark.parametrize("L", [64, 96, 66, 97])
 def test_f32_infinite_and_nan_masks(torch_dev, L):
     """fp32 masks with -inf on part of a row, on a whole row (out = 0, lse = -inf), a finite -1e9 on a
     leading half, and a NaN (its sequence NaN)."""
