@@ -1099,11 +1099,24 @@ hipError_t launch_format(const BwdArgs& a, unsigned stages, hipStream_t stream) 
 const unsigned kBwdMfmaStages = kStageDq | kStageDkDv | kStageDpair;
 
 int64_t bwd_dpair_chunks(int64_t B, int64_t N, int64_t L, int64_t H) {
-    // about 2048 workgroups (eight per CU), at least 8 values of n per chunk
-    const int64_t tdim = (L + 63) / 64, tiles = B * H * tdim * tdim;
-    int64_t c = (2048 + tiles - 1) / tiles;
-    if (c > N / 8) c = N / 8;
-    return c < 2 ? 0 : c;
+    // The split kernels run about four workgroups per CU at once, so a launch
+    // proceeds in rounds of 1,024; a workgroup's time is its number of n.
+    // Take the split into at least two chunks of at least 8 values of n that
+    // minimises rounds x n per workgroup, the smallest such one (fewer partial
+    // sums to add): a mostly empty last round costs as much as a full one.
+    // (A single chunk would run the single-pass kernel, which is slower.)
+    constexpr int64_t kSlots = 1024, kMaxChunks = 4096;
+    const int64_t tdim = (L + 63) / 64;
+    if (B > (int64_t(1) << 40) / H || B * H > (int64_t(1) << 40) / (tdim * tdim)) return 0;  // no split
+    const int64_t tiles = B * H * tdim * tdim;  // below 2^40: tiles * c stays in range
+    const int64_t cmax = N / 8 < kMaxChunks ? N / 8 : kMaxChunks;
+    int64_t best = 0;
+    double best_cost = 0.0;
+    for (int64_t c = 2; c <= cmax; ++c) {
+        const double cost = (double)((tiles * c + kSlots - 1) / kSlots) * (double)((N + c - 1) / c);
+        if (best == 0 || cost < best_cost) best = c, best_cost = cost;
+    }
+    return best;
 }
 
 namespace {

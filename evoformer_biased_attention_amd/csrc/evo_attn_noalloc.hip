@@ -11,7 +11,9 @@
 // handed to the kernels.  Calls on one GPU share its array: calls that overlap
 // in time on one GPU (two streams, two threads) race on it.  The pair
 // gradient's partial sums are written in full before they are read, so the
-// array needs no clearing between calls.
+// array needs no clearing between calls.  A shape whose recommended workspace
+// is larger than the array gets as many whole chunks of partial sums as fit
+// (the pass then splits N that many ways).
 #include "../../include/evo_attn.h"
 
 #include <hip/hip_runtime.h>
@@ -60,8 +62,16 @@ extern "C" evo_status_t evo_attn_bwd_noalloc(const void* q, const void* k, const
     const evo_status_t st = evo_attn_bwd_check(q, k, v, mask_bias, pair_bias, out, lse, dout, dq, dk, dv,
                                                dmask_bias, dpair_bias, delta, nullptr, 0, shape, dtype);
     if (st != EVO_OK) return st;
-    const size_t need = dpair_bias ? evo_attn_bwd_workspace_size(shape, dtype) : 0;
-    if (need > kScratchBytes) return EVO_ERR_SCRATCH;
+    // as many of the recommended N-chunks as fit: a chunk is one fp32
+    // [B,H,L,ceil4(L)] plane (it is at most `want`, which fits in size_t)
+    const size_t want = dpair_bias ? evo_attn_bwd_workspace_size(shape, dtype) : 0;
+    size_t need = want;
+    if (want > kScratchBytes) {
+        const size_t plane = static_cast<size_t>(shape->B) * static_cast<size_t>(shape->H) *
+                             static_cast<size_t>(shape->L) * static_cast<size_t>((shape->L + 3) / 4 * 4) * 4u;
+        if (plane > kScratchBytes / 2) return EVO_ERR_SCRATCH;
+        need = kScratchBytes - kScratchBytes % plane;
+    }
     void* ws = nullptr;
     if (need) {
         int dev = 0;

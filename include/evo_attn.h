@@ -75,8 +75,8 @@ typedef enum {
     EVO_ERR_UNSUPPORTED = 6,  /* valid but not implemented (dtype / head dimension)         */
     EVO_ERR_HIP = 7,          /* the HIP runtime reported an error at launch                */
     EVO_ERR_NO_BIAS = 8,      /* evo_attn_bwd: a bias gradient requested for an absent bias  */
-    EVO_ERR_SCRATCH = 9       /* evo_attn_bwd_noalloc: the shape needs more scratch than the
-                                 library's static buffer holds                              */
+    EVO_ERR_SCRATCH = 9       /* evo_attn_bwd_noalloc: not even two chunks of the pair
+                                 gradient's partial sums fit the library's static buffer    */
 } evo_status_t;
 
 /*
@@ -305,18 +305,21 @@ evo_status_t evo_trimul_check(const void* a, const void* w, const void* x, const
 /*
  * evo_attn_bwd without a caller workspace and without any allocation, for
  * callers that cannot allocate device memory (code under HIP graph capture,
- * tight serving loops, harnesses that forbid allocation).  Arguments and
- * results are those of evo_attn_bwd with the workspace it recommends
- * (evo_attn_bwd_workspace_size): the pair gradient's partial sums go to a
- * static device array of the library instead, of
+ * tight serving loops, harnesses that forbid allocation).  Arguments are
+ * those of evo_attn_bwd; the pair gradient's partial sums go to a static
+ * device array of the library instead of a caller workspace, of
  * evo_attn_bwd_noalloc_scratch_bytes() bytes (40 MiB) on every GPU the library
- * runs on, held until the process ends.  A shape (with a pair gradient
- * requested) whose recommended workspace exceeds that returns EVO_ERR_SCRATCH
- * before anything is enqueued; use evo_attn_bwd with a workspace of your own
- * there.  The call makes no hipMalloc or hipFree; its first call on a device
- * looks up that device's array address (hipGetSymbolAddress).  Calls on one
- * GPU share its array: calls that overlap in time on one GPU race on it.
- * Results are bit-identical to evo_attn_bwd's with the recommended workspace.
+ * runs on, held until the process ends.  The pass splits N into as many of
+ * the recommended chunks (evo_attn_bwd_workspace_size) as fit in the array:
+ * results are bit-identical to evo_attn_bwd's with the recommended workspace
+ * when that fits in 40 MiB, and otherwise to evo_attn_bwd's with a workspace
+ * of the largest whole number of chunks that fits.  A shape (with a pair
+ * gradient requested) of which not even two chunks fit (B * H * L * L above
+ * about 5.2 million) returns EVO_ERR_SCRATCH before anything is enqueued;
+ * use evo_attn_bwd with a workspace of your own there.  The call makes no
+ * hipMalloc or hipFree; its first call on a device looks up that device's
+ * array address (hipGetSymbolAddress).  Calls on one GPU share its array:
+ * calls that overlap in time on one GPU race on it.
  */
 evo_status_t evo_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* mask_bias,
                                   const void* pair_bias, const void* out, const float* lse, const void* dout,

@@ -245,12 +245,14 @@ def test_bwd_noalloc_host_checks():
 
     cap = E.evo_attn_bwd_noalloc_scratch_bytes()
     assert cap == 40 << 20
-    # the N = L = 384 triangle-attention shape fits (35.4 MB of partial sums)
+    # the N = L = 384 triangle-attention shape fits (7 chunks, 16.5 MB of partial sums)
     assert 0 < E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 32), E.EVO_DTYPE_BF16) <= cap
     assert call(q=None) == E.EVO_ERR_NULL_POINTER
     assert call(dq=a["q"]) == E.EVO_ERR_ALIASING
     assert call(mask_bias=None) == E.EVO_ERR_NO_BIAS
-    big = (1, 32, 640, 10, 32)  # 1000 tiles of 64 x 64, three N-chunks: 49.2 MB
+    # N = L = 768: 16 recommended chunks of 9.4 MB; the call uses the 4 that fit (GPU test in test_zz_no_alloc)
+    assert E.evo_attn_bwd_workspace_size((1, 768, 768, 4, 32), E.EVO_DTYPE_BF16) > cap
+    big = (1, 32, 1280, 4, 32)  # one chunk is 26.2 MB: not even two fit
     assert E.evo_attn_bwd_workspace_size(big, E.EVO_DTYPE_BF16) > cap
     assert call(shape=big) == E.EVO_ERR_SCRATCH
     assert "static buffer" in E.evo_status_string(E.EVO_ERR_SCRATCH)

@@ -29,7 +29,9 @@ def dev(torch, x, dtype):
     return (t.view(torch.bfloat16) if dtype == "bf16" else t.view(torch.float16)).to("cuda")
 
 
-def both(torch, shape, dtype, seed):
+def both(torch, shape, dtype, seed, over_scratch=False):
+    """The static-scratch call against evo_attn_bwd with a caller workspace: of the recommended size, or, when
+    that exceeds the scratch (over_scratch), of the scratch's size, which gives the same split of N."""
     import evoformer_biased_attention_amd as E
     B, N, L, H, D = shape
     w = S.random_problem(B, N, L, H, D, dtype=dtype, seed=seed, mask="tail", pair="normal")
@@ -38,7 +40,11 @@ def both(torch, shape, dtype, seed):
     out, lse = E.fwd(q, k, v, m, p)
     code = E.torch_dtype_code(q.dtype)
     need = E.evo_attn_bwd_workspace_size(shape, code)
-    assert 0 < need <= E.evo_attn_bwd_noalloc_scratch_bytes()
+    scratch = E.evo_attn_bwd_noalloc_scratch_bytes()
+    if over_scratch:
+        assert need > scratch
+        need = scratch
+    assert 0 < need <= scratch
     stream = torch.cuda.current_stream().cuda_stream
     results = []
     for noalloc in (False, True):
@@ -61,8 +67,16 @@ def both(torch, shape, dtype, seed):
 
 
 def test_noalloc_matches_workspace_call_twice(torch_dev):
-    both(torch_dev, (1, 64, 384, 4, 32), "bf16", 7001)   # 18.9 MB of partial sums
+    both(torch_dev, (1, 64, 384, 4, 32), "bf16", 7001)   # 16.5 MB of partial sums (7 chunks)
     both(torch_dev, (1, 24, 200, 2, 32), "f16", 7002)    # then a smaller problem: 0.96 MB
+
+
+def test_noalloc_splits_what_fits_in_the_scratch(torch_dev):
+    """N = L = 768: the recommended workspace (16 chunks, 151 MB) exceeds the 40 MiB scratch; the call splits N
+    into the 4 chunks that fit, bit-identical to evo_attn_bwd given a workspace of the scratch's size.  Then a
+    smaller problem that fits whole."""
+    both(torch_dev, (1, 768, 768, 4, 32), "bf16", 7007, over_scratch=True)
+    both(torch_dev, (1, 24, 200, 2, 32), "f16", 7008)
 
 
 def test_noalloc_matches_workspace_call_twice_f32(torch_dev):
