@@ -55,14 +55,18 @@ def test_forward_graph_replays(torch_dev, L):
         assert torch.equal(got_o, ref_o) and torch.equal(got_l, ref_l), f"replay {rep}"
 
 
-def test_backward_graph_replays(torch_dev):
-    """The backward with its workspace (pair gradient split over N) captured and replayed."""
+@pytest.mark.parametrize("entry", ["workspace", "noalloc"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_graph_replays(torch_dev, dtype, entry):
+    """The backward captured and replayed: with its workspace (pair gradient split over N), or through the
+    no-allocation entry point (the split's partial sums in the library's static array), on the 16-bit and the
+    fp32 matrix-core kernels."""
     torch = torch_dev
     import evoformer_biased_attention_amd as E
     B, N, L, H, D = 1, 24, 80, 2, 32
-    w = S.random_problem(B, N, L, H, D, dtype="bf16", seed=910, mask="tail", pair="normal")
-    q, k, v, m, p = (to_dev(torch, x, "bf16") for x in (w.q, w.k, w.v, w.mask, w.pair))
-    dout = to_dev(torch, S.random_dout(w.shape, "bf16", seed=911), "bf16")
+    w = S.random_problem(B, N, L, H, D, dtype=dtype, seed=910, mask="tail", pair="normal")
+    q, k, v, m, p = (to_dev(torch, x, dtype) for x in (w.q, w.k, w.v, w.mask, w.pair))
+    dout = to_dev(torch, S.random_dout(w.shape, dtype, seed=911), dtype)
     out, lse = E.fwd(q, k, v, m, p)
     code = E.torch_dtype_code(q.dtype)
     grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(m), torch.empty_like(p)]
@@ -72,6 +76,8 @@ def test_backward_graph_replays(torch_dev):
     ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
 
     def launch(stream):
+        if entry == "noalloc":  # its first call on the device (the warm-up below) looks up the array's address
+            return E.evo_attn_bwd_noalloc(q, k, v, m, p, out, lse, dout, *grads, delta, w.shape, code, stream)
         return E.evo_attn_bwd(q, k, v, m, p, out, lse, dout, *grads, delta, w.shape, code, stream, workspace=ws,
                               workspace_bytes=ws_bytes)
 
