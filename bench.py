@@ -523,9 +523,9 @@ def bench_bwd(args, w, dev, torch, E, S):
                    "mask": w.mask is not None, "pair_bias": w.pair is not None, "mode": args.mode,
                    "input_sets": R, "flop_per_step": flops, "workspace_bytes": ws_bytes},
         # 16-bit inputs: every product on the matrix cores, priced against the dense bf16/f16 MFMA peak;
-        # f32 inputs: the fp32 matrix-core kernels where they apply (D 16 or 32, bias rows a multiple of
-        # 4 elements), else the vector-ALU kernels; fp32 matrix and vector peaks are both 157.3 TFLOP/s
-        "roofline": {"bound": "mfma" if (w.dtype != "f32" or (D in (16, 32) and L % 4 == 0)) else "alu",
+        # f32 inputs: the fp32 matrix-core kernels (every head dimension and bias stride of the dense and
+        # transposed layouts), priced against the 157.3 TFLOP/s fp32 matrix peak
+        "roofline": {"bound": "mfma",
                      "achieved": round(achieved, 3),
                      "peak": PEAK_BF16_TFLOPS if w.dtype != "f32" else PEAK_F32_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / (PEAK_BF16_TFLOPS if w.dtype != "f32" else PEAK_F32_TFLOPS), 4),

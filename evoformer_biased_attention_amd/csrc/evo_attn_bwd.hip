@@ -390,8 +390,8 @@ hipError_t launch_valu(const BwdArgs& a, int dtype, unsigned stages, hipStream_t
 }  // namespace
 
 // The matrix-core kernels take the stages they implement for the shapes
-// they accept (16-bit formats with D in {8, 16, 32, 64} and any L; fp32 with
-// D in {16, 32} and 16-byte aligned bias rows); the vector-ALU kernels take
+// they accept (every dtype with D in {8, 16, 32, 64} and any L, on layouts
+// whose rows span every head and fit 32-bit offsets); the vector-ALU kernels take
 // the rest.  The dq stage goes first in either case: it writes delta.
 hipError_t launch_bwd(const BwdArgs& a, int dtype, hipStream_t stream) {
     if (dtype == 0 && bwd_f32_mfma_eligible(a)) {

@@ -51,6 +51,7 @@ using gfx::bload16_any;
 using gfx::dma16_untracked;
 using gfx::f32x4;
 using gfx::kLog2e;
+using gfx::kOOB;
 using gfx::make_rsrc;
 using gfx::Rsrc;
 
@@ -91,20 +92,24 @@ struct BParams {
 // that every weight of the row is exactly zero
 __device__ inline float lse2_of(float lse) { return lse == -INFINITY ? INFINITY : lse * kLog2e; }
 
-// Copy requests of one block of 64 rows of a [L][row] fp32 tensor: lane l of
-// request I holds row I*(256/D) + l/(D/4), slot position l % (D/4), i.e. chunk
-// (l % (D/4)) ^ sw(row); wave w takes requests w, w + 4, ...
-template <int D>
+// Copy requests of one block of 64 rows of a [L][row] fp32 tensor into an LDS
+// tile of KD-float rows: lane l of request I holds row I*(256/KD) + l/(KD/4),
+// slot position l % (KD/4), i.e. chunk (l % (KD/4)) ^ sw(row); wave w takes
+// requests w, w + 4, ...  Chunks past the D floats of a row (D = 8 in a tile
+// laid out for 16) read from kOOB and land as zeros; a block's base offset
+// (below 2^31) keeps them past the range.
+template <int KD, int D = KD>
 struct RowCopy {
-    static constexpr int kRPS = 256 / D;       // rows per 1 KB request
+    static constexpr int kRPS = 256 / KD;      // rows per 1 KB request
     static constexpr int kSegs = kKB / kRPS;   // requests per block
     static constexpr int kPer = kSegs / kWaves;
     static_assert(kSegs % kWaves == 0, "requests per wave");
     uint32_t off[kPer];
     __device__ void init(int wave, int lane, uint32_t rowbytes) {
         for (int i = 0; i < kPer; ++i) {
-            const int seg = wave + kWaves * i, row = seg * kRPS + lane / (D / 4);
-            off[i] = (uint32_t)row * rowbytes + 16u * (uint32_t)((lane % (D / 4)) ^ sw<D>(row));
+            const int seg = wave + kWaves * i, row = seg * kRPS + lane / (KD / 4);
+            const uint32_t chunk = (uint32_t)((lane % (KD / 4)) ^ sw<KD>(row));
+            off[i] = (KD == D || chunk < D / 4) ? (uint32_t)row * rowbytes + 16u * chunk : kOOB;
         }
     }
     __device__ void issue(Rsrc r, f32x4* dst, int wave, uint32_t base) const {
@@ -113,11 +118,18 @@ struct RowCopy {
 };
 
 // ---------------------------------------------------------------------------
+// The three kernels run D = 8 as D = 16 (KD, the width the tiles are laid out
+// for): the 16-byte chunks of a row past D read as zero (an offset beyond the
+// buffer range), which pads Q, K, V and dO with zero columns, adds nothing to
+// the scores, dP and delta, and leaves the gradient rows past D unstored.
+//
 // dq and delta.  Workgroup = 128 queries of one (b, n, h); wave w owns
 // queries 32w .. 32w+31 as two 16-query tiles; key blocks of 64 in LDS.  At
 // D = 64 a wave owns one 16-query tile (64 queries per workgroup), which
 // keeps its registers within two waves per SIMD.
 // ---------------------------------------------------------------------------
+template <int D>
+constexpr int tile_width() { return D < 16 ? 16 : D; }
 template <int D>
 constexpr int dq_tiles() { return D == 64 ? 1 : 2; }
 template <int D>
@@ -132,8 +144,9 @@ struct DqBuf {
 
 template <int D, bool PAIR, bool MASK, bool STAGED>
 __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_f32_mfma(BParams p) {
-    constexpr int kS = D / 4, kDT = D / 16, kQT = dq_tiles<D>();
-    __shared__ __attribute__((aligned(16))) DqBuf<D> sm[2];
+    constexpr int KD = tile_width<D>();
+    constexpr int kS = KD / 4, kDT = KD / 16, kQT = dq_tiles<D>();
+    __shared__ __attribute__((aligned(16))) DqBuf<KD> sm[2];
 
     const uint32_t id = (uint32_t)gfx::logical_block(blockIdx.x, p.total);
     const uint32_t r1 = gfx::fdiv(id, p.rblocks), r2 = gfx::fdiv(r1, p.hd), r3 = gfx::fdiv(r2, p.nd);
@@ -169,8 +182,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_f32_mfma(BParams p) {
         const uint32_t rq_off = (uint32_t)i * rowq, ro_off = (uint32_t)i * rowo;
         float part = 0.f;
         for (int j = 0; j < kS / 4; ++j) {
-            const uint32_t d0 = 4u * (uint32_t)(kS * g + 4 * j);
-            const uint4 wq = bload16(rq, rq_off + d0), wd = bload16(rdo, ro_off + d0), wo = bload16(ro, ro_off + d0);
+            const uint32_t e0 = (uint32_t)(kS * g + 4 * j), d0 = 4u * e0;
+            const bool din = D >= 16 || e0 < (uint32_t)D;
+            const uint4 wq = bload16(rq, din ? rq_off + d0 : kOOB), wd = bload16(rdo, din ? ro_off + d0 : kOOB);
+            const uint4 wo = bload16(ro, din ? ro_off + d0 : kOOB);
             const float qv[4] = {__builtin_bit_cast(float, wq.x), __builtin_bit_cast(float, wq.y),
                                  __builtin_bit_cast(float, wq.z), __builtin_bit_cast(float, wq.w)};
             const float dv4[4] = {__builtin_bit_cast(float, wd.x), __builtin_bit_cast(float, wd.y),
@@ -189,11 +204,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_f32_mfma(BParams p) {
         if (g == 0 && i < L) p.delta[lrow + i] = delta;
     }
 
-    RowCopy<D> ck, cv;
+    RowCopy<KD, D> ck, cv;
     ck.init(wave, lane, rowk);
     cv.init(wave, lane, rowv);
     uint4 mstage;  // STAGED: the mask chunk between its load and its landing in LDS
-    auto copy_block = [&](int blk, DqBuf<D>* __restrict__ dst) {
+    auto copy_block = [&](int blk, DqBuf<KD>* __restrict__ dst) {
         const uint32_t k0 = (uint32_t)blk * kKB;
         ck.issue(rk, dst->k, wave, k0 * rowk);
         cv.issue(rv, dst->v, wave, k0 * rowv);
@@ -202,7 +217,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_f32_mfma(BParams p) {
             else dma16_untracked(rm, &dst->mt[0], 16u * lane + k0 * 4u);
         }
     };
-    auto land_mask = [&](DqBuf<D>* __restrict__ dst) {
+    auto land_mask = [&](DqBuf<KD>* __restrict__ dst) {
         if (STAGED && MASK && wave == 0 && lane < 16) dst->mt[lane] = __builtin_bit_cast(f32x4, mstage);
     };
     // the wave's pair rows in the score layout: tile t, key tile kt -> pair[q0 + 16t + c][k0 + 16kt + 4g .. +3]
@@ -228,7 +243,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_f32_mfma(BParams p) {
     __syncthreads();
 
     for (int it = 0; it < nblocks; ++it) {
-        const DqBuf<D>* __restrict__ cur = &sm[it & 1];
+        const DqBuf<KD>* __restrict__ cur = &sm[it & 1];
         const int k0 = it * kKB;
         if (it + 1 < nblocks) copy_block(it + 1, &sm[(it & 1) ^ 1]);
         // S^T (keys 16kt + 4g + i, query c) from pair + mask, then K.Q^T/sqrt(D)
@@ -244,8 +259,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_f32_mfma(BParams p) {
         if (PAIR && it + 1 < nblocks) load_pair(it + 1);
         for (int kt = 0; kt < kKT; ++kt) {
             float kf[kS], vf[kS];
-            tile_run<D>(cur->k, 16 * kt + c, g, kf);
-            tile_run<D>(cur->v, 16 * kt + c, g, vf);
+            tile_run<KD>(cur->k, 16 * kt + c, g, kf);
+            tile_run<KD>(cur->v, 16 * kt + c, g, vf);
             for (int s = 0; s < kS; ++s)
                 for (int t = 0; t < kQT; ++t) {
                     acc[t][kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[s], qop[t][s], acc[t][kt], 0, 0, 0);
@@ -266,7 +281,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_f32_mfma(BParams p) {
         for (int kt = 0; kt < kKT; ++kt)
             for (int r = 0; r < 4; ++r)
                 for (int dt = 0; dt < kDT; ++dt) {
-                    const float kv = tile_at<D>(cur->k, 16 * kt + 4 * g + r, 16 * dt + c);
+                    const float kv = tile_at<KD>(cur->k, 16 * kt + 4 * g + r, 16 * dt + c);
                     for (int t = 0; t < kQT; ++t)
                         dqacc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kv, acc[t][kt][r], dqacc[t][dt], 0, 0, 0);
                 }
@@ -281,7 +296,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_f32_mfma(BParams p) {
         const int i = q0 + 16 * t + c;
         if (i >= L) continue;
         for (int dt = 0; dt < kDT; ++dt)
-            *reinterpret_cast<f32x4*>(p.dq + qs + (int64_t)i * st.q[2] + 16 * dt + 4 * g) = dqacc[t][dt] * p.scale;
+            if (D >= 16 || 16 * dt + 4 * g < D)
+                *reinterpret_cast<f32x4*>(p.dq + qs + (int64_t)i * st.q[2] + 16 * dt + 4 * g) = dqacc[t][dt] * p.scale;
     }
 }
 
@@ -301,8 +317,9 @@ struct KvBuf {
 
 template <int D, bool PAIR, bool MASK>
 __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_f32_mfma(BParams p) {
-    constexpr int kS = D / 4, kDT = D / 16;
-    __shared__ __attribute__((aligned(16))) KvBuf<D> sm[2];
+    constexpr int KD = tile_width<D>();
+    constexpr int kS = KD / 4, kDT = KD / 16;
+    __shared__ __attribute__((aligned(16))) KvBuf<KD> sm[2];
 
     const uint32_t id = (uint32_t)gfx::logical_block(blockIdx.x, p.total);
     const uint32_t r1 = gfx::fdiv(id, p.rblocks), r2 = gfx::fdiv(r1, p.nd);
@@ -332,11 +349,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_f32_mfma(BParams p) {
     const Rsrc rdo = make_rsrc(p.dout + obn, last * rowo + lasth * ho + D * 4);
     const float mkey = MASK && key_live ? p.mask[b * st.mb + n * st.mn + key] : 0.f;
 
-    RowCopy<D> cq, cdo;
+    RowCopy<KD, D> cq, cdo;
     cq.init(wave, lane, rowq);
     cdo.init(wave, lane, rowo);
     float lsv = INFINITY, dlv = 0.f;  // wave 0: this lane's query of the step being copied
-    auto copy_step = [&](int it, KvBuf<D>* __restrict__ dst) {
+    auto copy_step = [&](int it, KvBuf<KD>* __restrict__ dst) {
         const int hh = it / nqb, q0 = (it - hh * nqb) * kKB;
         cq.issue(rq, dst->q, wave, (uint32_t)q0 * rowq + (uint32_t)hh * hq);
         cdo.issue(rdo, dst->dout, wave, (uint32_t)q0 * rowo + (uint32_t)hh * ho);
@@ -347,7 +364,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_f32_mfma(BParams p) {
             dlv = i < L ? -p.delta[row] : 0.f;
         }
     };
-    auto put_rows = [&](KvBuf<D>* __restrict__ dst) {
+    auto put_rows = [&](KvBuf<KD>* __restrict__ dst) {
         if (wave == 0) {
             reinterpret_cast<float*>(dst->ls)[lane] = lsv;
             reinterpret_cast<float*>(dst->dl)[lane] = dlv;
@@ -377,15 +394,16 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_f32_mfma(BParams p) {
     __syncthreads();
 
     for (int it = 0; it < nsteps; ++it) {
-        const KvBuf<D>* __restrict__ cur = &sm[it & 1];
+        const KvBuf<KD>* __restrict__ cur = &sm[it & 1];
         const int hh = it / nqb, qblk = it - hh * nqb;
         if (qblk == 0) {
             // a new head: this lane's K/sqrt(D) and V rows (B operands of S and dP)
             const int kr = key_live ? key : L - 1;
             for (int j = 0; j < kS / 4; ++j) {
-                const uint32_t d0 = 4u * (uint32_t)(kS * g + 4 * j);
-                const uint4 wk = bload16(rk, (uint32_t)kr * rowk + (uint32_t)hh * hk + d0);
-                const uint4 wv = bload16(rv, (uint32_t)kr * rowv + (uint32_t)hh * hv + d0);
+                const uint32_t e0 = (uint32_t)(kS * g + 4 * j), d0 = 4u * e0;
+                const bool din = D >= 16 || e0 < (uint32_t)D;
+                const uint4 wk = bload16(rk, din ? (uint32_t)kr * rowk + (uint32_t)hh * hk + d0 : kOOB);
+                const uint4 wv = bload16(rv, din ? (uint32_t)kr * rowv + (uint32_t)hh * hv + d0 : kOOB);
                 kop[4 * j] = __builtin_bit_cast(float, wk.x) * p.scale;
                 kop[4 * j + 1] = __builtin_bit_cast(float, wk.y) * p.scale;
                 kop[4 * j + 2] = __builtin_bit_cast(float, wk.z) * p.scale;
@@ -407,8 +425,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_f32_mfma(BParams p) {
             f32x4 s4 = PAIR ? pcur[qt] + mkey : f32x4{mkey, mkey, mkey, mkey};
             f32x4 dpm = cur->dl[4 * qt + g];
             float qf[kS], df[kS];
-            tile_run<D>(cur->q, 16 * qt + c, g, qf);
-            tile_run<D>(cur->dout, 16 * qt + c, g, df);
+            tile_run<KD>(cur->q, 16 * qt + c, g, qf);
+            tile_run<KD>(cur->dout, 16 * qt + c, g, df);
             for (int s = 0; s < kS; ++s) {
                 s4 = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[s], kop[s], s4, 0, 0, 0);
                 dpm = __builtin_amdgcn_mfma_f32_16x16x4f32(df[s], vop[s], dpm, 0, 0, 0);
@@ -424,8 +442,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_f32_mfma(BParams p) {
             // from lane group g; operands A[m = d][k]: lane (c + 16g) takes row 16qt + 4g + r, column 16dt + c
             for (int r = 0; r < 4; ++r)
                 for (int dt = 0; dt < kDT; ++dt) {
-                    const float dov = tile_at<D>(cur->dout, 16 * qt + 4 * g + r, 16 * dt + c);
-                    const float qv = tile_at<D>(cur->q, 16 * qt + 4 * g + r, 16 * dt + c);
+                    const float dov = tile_at<KD>(cur->dout, 16 * qt + 4 * g + r, 16 * dt + c);
+                    const float qv = tile_at<KD>(cur->q, 16 * qt + 4 * g + r, 16 * dt + c);
                     dvacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(dov, pw[r], dvacc[dt], 0, 0, 0);
                     dkacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv, ds[r], dkacc[dt], 0, 0, 0);
                 }
@@ -436,6 +454,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_f32_mfma(BParams p) {
             const int64_t ko = kbn + (int64_t)hh * st.k[3] + (int64_t)key * st.k[2];
             const int64_t vo = vbn + (int64_t)hh * st.v[3] + (int64_t)key * st.v[2];
             for (int dt = 0; dt < kDT; ++dt) {
+                if (D < 16 && 16 * dt + 4 * g >= D) continue;  // the padded rows
                 *reinterpret_cast<f32x4*>(p.dk + ko + 16 * dt + 4 * g) = dkacc[dt] * p.scale;
                 *reinterpret_cast<f32x4*>(p.dv + vo + 16 * dt + 4 * g) = dvacc[dt];
             }
@@ -478,9 +497,10 @@ struct PairParams {
 
 template <int D, bool MASK, bool STAGED>
 __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_f32_mfma(PairParams pp) {
-    constexpr int kS = D / 4;
+    constexpr int KD = tile_width<D>();
+    constexpr int kS = KD / 4;
     const BParams& p = pp.p;
-    __shared__ __attribute__((aligned(16))) PrBuf<D> sm[2];
+    __shared__ __attribute__((aligned(16))) PrBuf<KD> sm[2];
 
     // order (b, h, range, query tile, key tile): the tiles of one (b, h,
     // range) run on one XCD together and share each n's rows in its L2
@@ -515,11 +535,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_f32_mfma(PairParams 
         }
     }
 
-    RowCopy<D> ck, cv;
+    RowCopy<KD, D> ck, cv;
     ck.init(wave, lane, rowk);
     cv.init(wave, lane, rowv);
     uint4 mstage;  // STAGED: the mask chunk between its load and its landing in LDS
-    auto copy_step = [&](int64_t n, PrBuf<D>* __restrict__ dst) {
+    auto copy_step = [&](int64_t n, PrBuf<KD>* __restrict__ dst) {
         const Rsrc rk = make_rsrc(p.k + b * st.k[0] + n * st.k[1] + h * st.k[3], last * rowk + D * 4);
         const Rsrc rv = make_rsrc(p.v + b * st.v[0] + n * st.v[1] + h * st.v[3], last * rowv + D * 4);
         ck.issue(rk, dst->k, wave, (uint32_t)j0 * rowk);
@@ -531,7 +551,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_f32_mfma(PairParams 
             else dma16_untracked(rm, &dst->mt[0], 16u * lane + (uint32_t)j0 * 4u);
         }
     };
-    auto land_mask = [&](PrBuf<D>* __restrict__ dst) {
+    auto land_mask = [&](PrBuf<KD>* __restrict__ dst) {
         if (STAGED && MASK && wave == 0 && lane < 16) dst->mt[lane] = __builtin_bit_cast(f32x4, mstage);
     };
     // this lane's Q and dO d-range, lse and delta at sequence n, as loaded
@@ -542,9 +562,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_f32_mfma(PairParams 
         const Rsrc rq = make_rsrc(p.q + b * st.q[0] + n * st.q[1] + h * st.q[3], last * rowq + D * 4);
         const Rsrc rd = make_rsrc(p.dout + b * st.o[0] + n * st.o[1] + h * st.o[3], last * rowo + D * 4);
         for (int j = 0; j < kS / 4; ++j) {
-            const uint32_t d0 = 4u * (uint32_t)(kS * g + 4 * j);
-            qraw[j] = bload16(rq, (uint32_t)qi * rowq + d0);
-            draw[j] = bload16(rd, (uint32_t)qi * rowo + d0);
+            const uint32_t e0 = (uint32_t)(kS * g + 4 * j), d0 = 4u * e0;
+            const bool din = D >= 16 || e0 < (uint32_t)D;
+            qraw[j] = bload16(rq, din ? (uint32_t)qi * rowq + d0 : kOOB);
+            draw[j] = bload16(rd, din ? (uint32_t)qi * rowo + d0 : kOOB);
         }
         if (q_live) {
             const int64_t row = ((b * N + n) * p.H + h) * st.lrow + qi;
@@ -564,7 +585,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_f32_mfma(PairParams 
 
     for (int64_t n = n0; n < n1; ++n) {
         const int it = (int)(n - n0);
-        const PrBuf<D>* __restrict__ cur = &sm[it & 1];
+        const PrBuf<KD>* __restrict__ cur = &sm[it & 1];
         // Q/sqrt(D) and dO as B operands (lane group g's d-range of query c)
         float qop[kS], dop[kS];
         for (int j = 0; j < kS / 4; ++j) {
@@ -590,8 +611,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_f32_mfma(PairParams 
             if (MASK) acc += cur->mt[4 * kt + g];
             f32x4 dpm = f32x4{ndl, ndl, ndl, ndl};
             float kf[kS], vf[kS];
-            tile_run<D>(cur->k, 16 * kt + c, g, kf);
-            tile_run<D>(cur->v, 16 * kt + c, g, vf);
+            tile_run<KD>(cur->k, 16 * kt + c, g, kf);
+            tile_run<KD>(cur->v, 16 * kt + c, g, vf);
             for (int s = 0; s < kS; ++s) {
                 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[s], qop[s], acc, 0, 0, 0);
                 dpm = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[s], dop[s], dpm, 0, 0, 0);
@@ -712,7 +733,7 @@ hipError_t launch_stage_dim(const BParams& p, int64_t B, bool pair, bool mask, u
 
 const unsigned kBwdF32MfmaStages = kStageDq | kStageDkDv | kStageDpair;
 
-// D in {16, 32, 64}; q, k, v, out rows 16-byte aligned (the C ABI checks
+// D in {8, 16, 32, 64}; q, k, v, out rows 16-byte aligned (the C ABI checks
 // that); bias rows at any stride (unaligned ones are staged).  Each row of
 // q, k, v and out spans every head (row stride at least (H - 1) head
 // strides + D), so that rows past L fall beyond the
@@ -724,7 +745,7 @@ const unsigned kBwdF32MfmaStages = kStageDq | kStageDkDv | kStageDpair;
 bool bwd_f32_mfma_eligible(const BwdArgs& a) {
     constexpr int64_t kLim = int64_t(1) << 31, kBig = int64_t(1) << 40;
     const int64_t L = a.L, H = a.H, D = a.D;
-    if (D != 16 && D != 32 && D != 64) return false;
+    if (D != 8 && D != 16 && D != 32 && D != 64) return false;
     if (a.N >= kLim || H >= kLim || L >= kLim) return false;
     for (const int64_t* t : {a.st.q, a.st.k, a.st.v, a.st.o}) {
         const int64_t row = t[2], head = t[3];
@@ -767,7 +788,8 @@ hipError_t launch_bwd_f32_mfma(const BwdArgs& a, unsigned stages, hipStream_t st
     hipError_t e = hipSuccess;
     for (unsigned stage : {kStageDq, kStageDkDv}) {
         if (!(stages & stage)) continue;
-        if (a.D == 16) e = launch_stage_dim<16>(p, a.B, pair, mask, stage, staged, stream);
+        if (a.D == 8) e = launch_stage_dim<8>(p, a.B, pair, mask, stage, staged, stream);
+        else if (a.D == 16) e = launch_stage_dim<16>(p, a.B, pair, mask, stage, staged, stream);
         else if (a.D == 32) e = launch_stage_dim<32>(p, a.B, pair, mask, stage, staged, stream);
         else e = launch_stage_dim<64>(p, a.B, pair, mask, stage, staged, stream);
         if (e != hipSuccess) return e;
@@ -776,7 +798,9 @@ hipError_t launch_bwd_f32_mfma(const BwdArgs& a, unsigned stages, hipStream_t st
         // with a workspace of at least two ranges, split N; else one range per tile
         float* ws = a.ws && a.ws_chunks >= 2 ? a.ws : nullptr;
         const int64_t chunks = ws ? a.ws_chunks : 1;
-        if (a.D == 16) e = mask ? launch_dpair<16, true>(p, a.B, ws, chunks, staged, stream)
+        if (a.D == 8) e = mask ? launch_dpair<8, true>(p, a.B, ws, chunks, staged, stream)
+                               : launch_dpair<8, false>(p, a.B, ws, chunks, staged, stream);
+        else if (a.D == 16) e = mask ? launch_dpair<16, true>(p, a.B, ws, chunks, staged, stream)
                                 : launch_dpair<16, false>(p, a.B, ws, chunks, staged, stream);
         else if (a.D == 32) e = mask ? launch_dpair<32, true>(p, a.B, ws, chunks, staged, stream)
                                      : launch_dpair<32, false>(p, a.B, ws, chunks, staged, stream);

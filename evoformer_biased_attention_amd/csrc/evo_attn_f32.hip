@@ -5,7 +5,8 @@
 // hmyw.cn, sections 4, 5.2 and 5.4) with fp32 operands and fp32 arithmetic
 // throughout.
 //
-// fwd_f32_mfma (D = 16, 32, 64, any bias strides): both products on
+// fwd_f32_mfma (D = 8, 16, 32, 64, any bias strides; D = 8 zero-padded to
+// 16): both products on
 // the matrix cores with v_mfma_f32_16x16x4f32, which multiplies fp32 values
 // and accumulates in fp32.  The layout follows the 16-bit kernel: scores are
 // formed transposed (S^T = K.Q^T, lane c + 16g holds query c and keys 4g ..
@@ -28,7 +29,8 @@
 // 16-byte aligned (STAGED) are read with unaligned 16-byte loads over the
 // exact range, and the mask row passes through registers into LDS.
 //
-// fwd_f32_kernel (D = 8): the vector ALUs.  One 64-lane wavefront per (b, n, h, block of 64
+// fwd_f32_kernel (layouts whose offsets the matrix-core kernel cannot form in
+// 32 bits): the vector ALUs.  One 64-lane wavefront per (b, n, h, block of 64
 // queries); each lane owns one query and keeps q, the output accumulator and
 // its running max / sum in registers.  Keys are visited in blocks of 64
 // staged in LDS, and each key updates the lane's state with a one-pass
@@ -172,16 +174,20 @@ struct MParams {
     float scale;  // 1 / sqrt(D)
 };
 
+// D = 8 runs as D = 16 (KD): the 16-byte chunks of a row past D read as zero
+// (an offset beyond the buffer range), which pads Q and K with zero dimensions
+// and V with zero columns; the output rows past D are not stored.
 template <int D, bool PAIR, bool MASK, bool STAGED>
 __global__ __launch_bounds__(kMWaves * 64, 2) void fwd_f32_mfma(MParams p) {
-    constexpr int kCPR = D / 4;       // 16-byte chunks per row
-    constexpr int kS = D / 4;         // contraction slices of the score product (4 d-values each)
-    constexpr int kDT = D / 16;       // 16-wide d tiles of the output
-    constexpr int kRPS = 256 / D;     // K / V rows per 1 KB copy request
+    constexpr int KD = D < 16 ? 16 : D;  // the width the tiles are laid out for
+    constexpr int kCPR = KD / 4;      // 16-byte chunks per row
+    constexpr int kS = KD / 4;        // contraction slices of the score product (4 d-values each)
+    constexpr int kDT = KD / 16;      // 16-wide d tiles of the output
+    constexpr int kRPS = 256 / KD;    // K / V rows per 1 KB copy request
     constexpr int kSegs = kMKB / kRPS;  // copy requests per tensor and block
-    static_assert(D == 16 || D == 32 || D == 64, "head dimensions 16, 32, 64");
+    static_assert(D == 8 || D == 16 || D == 32 || D == 64, "head dimensions 8, 16, 32, 64");
     static_assert(kSegs % kMWaves == 0, "copy requests per wave");
-    __shared__ __attribute__((aligned(16))) MBuf<D> sm[2];
+    __shared__ __attribute__((aligned(16))) MBuf<KD> sm[2];
 
     const uint32_t id = (uint32_t)gfx::logical_block(blockIdx.x, p.total);
     const uint32_t r1 = gfx::fdiv(id, p.qblocks), r2 = gfx::fdiv(r1, p.hd), r3 = gfx::fdiv(r2, p.nd);
@@ -216,7 +222,8 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void fwd_f32_mfma(MParams p) {
     for (int t = 0; t < kMQTiles; ++t) {
         const uint32_t row = (uint32_t)(q0 + 16 * t + c);
         for (int j = 0; j < kS / 4; ++j) {
-            const uint4 w = bload16(rq, row * rowq + 4u * (uint32_t)(kS * g + 4 * j));
+            const uint32_t d0 = (uint32_t)(kS * g + 4 * j);
+            const uint4 w = bload16(rq, (D >= 16 || d0 < (uint32_t)D) ? row * rowq + 4u * d0 : kOOB);
             qop[t][4 * j + 0] = __builtin_bit_cast(float, w.x) * p.scale;
             qop[t][4 * j + 1] = __builtin_bit_cast(float, w.y) * p.scale;
             qop[t][4 * j + 2] = __builtin_bit_cast(float, w.z) * p.scale;
@@ -232,12 +239,14 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void fwd_f32_mfma(MParams p) {
     for (int i = 0; i < kSegs / kMWaves; ++i) {
         const int seg = wave + kMWaves * i;
         const int row = seg * kRPS + lane / kCPR;
-        const uint32_t chunk = (uint32_t)((lane % kCPR) ^ msw<D>(row));
-        kvo[i][0] = (uint32_t)row * rowk + 16u * chunk;
-        kvo[i][1] = (uint32_t)row * rowv + 16u * chunk;
+        const uint32_t chunk = (uint32_t)((lane % kCPR) ^ msw<KD>(row));
+        // chunks past D: kOOB, to which a block's k0 * row adds less than 2^31
+        const bool din = KD == D || chunk < D / 4;
+        kvo[i][0] = din ? (uint32_t)row * rowk + 16u * chunk : kOOB;
+        kvo[i][1] = din ? (uint32_t)row * rowv + 16u * chunk : kOOB;
     }
     uint4 mstage;  // STAGED: the mask chunk between its load and its landing in LDS
-    auto copy_block = [&](int blk, MBuf<D>* __restrict__ dst) {
+    auto copy_block = [&](int blk, MBuf<KD>* __restrict__ dst) {
         const uint32_t k0 = (uint32_t)blk * kMKB;
         for (int i = 0; i < kSegs / kMWaves; ++i) {
             const int seg = wave + kMWaves * i;
@@ -249,7 +258,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void fwd_f32_mfma(MParams p) {
             else dma16_untracked(rm, &dst->mt[0], 16u * lane + k0 * 4u);
         }
     };
-    auto land_mask = [&](MBuf<D>* __restrict__ dst) {
+    auto land_mask = [&](MBuf<KD>* __restrict__ dst) {
         if (STAGED && MASK && wave == 0 && lane < 16) dst->mt[lane] = __builtin_bit_cast(f32x4, mstage);
     };
     // ---- the wave's pair rows for one block, straight into registers in the
@@ -283,7 +292,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void fwd_f32_mfma(MParams p) {
     __syncthreads();
 
     for (int it = 0; it < nblocks; ++it) {
-        const MBuf<D>* __restrict__ cur = &sm[it & 1];
+        const MBuf<KD>* __restrict__ cur = &sm[it & 1];
         const int k0 = it * kMKB;
         // the next block's K, V and mask: their buffer was last read before the
         // barrier that ended the previous step; the copies are untracked, so
@@ -302,7 +311,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void fwd_f32_mfma(MParams p) {
             const int row = 16 * kt + c;
             float kf[kS];
             for (int j = 0; j < kS / 4; ++j) {
-                const f32x4 w = cur->k[row * kCPR + ((kS / 4 * g + j) ^ msw<D>(row))];
+                const f32x4 w = cur->k[row * kCPR + ((kS / 4 * g + j) ^ msw<KD>(row))];
                 kf[4 * j + 0] = w[0], kf[4 * j + 1] = w[1], kf[4 * j + 2] = w[2], kf[4 * j + 3] = w[3];
             }
             for (int s2 = 0; s2 < kS; ++s2)
@@ -342,7 +351,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void fwd_f32_mfma(MParams p) {
                 const float* vrow = reinterpret_cast<const float*>(&cur->v[row * kCPR]);
                 for (int dt = 0; dt < kDT; ++dt) {
                     const int d = 16 * dt + c;
-                    const float vf = vrow[4 * ((d >> 2) ^ msw<D>(row)) + (d & 3)];
+                    const float vf = vrow[4 * ((d >> 2) ^ msw<KD>(row)) + (d & 3)];
                     for (int t = 0; t < kMQTiles; ++t)
                         oacc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf, acc[t][kt][r], oacc[t][dt], 0, 0, 0);
                 }
@@ -360,6 +369,7 @@ __global__ __launch_bounds__(kMWaves * 64, 2) void fwd_f32_mfma(MParams p) {
         // a row sum of 0 (every key -inf) gives out = 0; a NaN one stays NaN
         const float inv = l > 0.f ? 1.f / l : (l == 0.f ? 0.f : l);
         for (int dt = 0; dt < kDT; ++dt) {
+            if (D < 16 && 16 * dt + 4 * g >= D) continue;  // the padded output rows
             const f32x4 o = oacc[t][dt] * inv;
             *reinterpret_cast<f32x4*>(p.out + b * st.o[0] + n * st.o[1] + h * st.o[3] + (int64_t)i * st.o[2] +
                                       16 * dt + 4 * g) = o;
@@ -390,11 +400,11 @@ hipError_t launch_mfma_dim(MParams& p, hipStream_t stream) {
     return launch_mfma_variant<D, false, false>(p, stream);
 }
 
-// Whether the matrix-core kernel takes these arguments: D in {16, 32, 64}
+// Whether the matrix-core kernel takes these arguments: D in {8, 16, 32, 64}
 // and every byte offset it forms (rows of one slice or pair matrix, up to 128
 // rows past L) below 2^31.
 bool mfma_eligible(const FwdArgs& a) {
-    if (a.D != 16 && a.D != 32 && a.D != 64) return false;
+    if (a.D != 8 && a.D != 16 && a.D != 32 && a.D != 64) return false;
     constexpr int64_t kLim = int64_t(1) << 31;
     for (int64_t rs : {a.st.q[2], a.st.k[2], a.st.v[2]})
         if ((a.L + kMBlockQ) * rs * 4 + a.D * 4 >= kLim) return false;
@@ -421,6 +431,7 @@ hipError_t launch_mfma(const FwdArgs& a, hipStream_t stream) {
     p.hd = gfx::make_fastdiv((uint32_t)a.H);
     p.st = a.st;
     p.scale = (float)(1.0 / std::sqrt((double)a.D));
+    if (a.D == 8) return launch_mfma_dim<8>(p, stream);
     if (a.D == 16) return launch_mfma_dim<16>(p, stream);
     if (a.D == 32) return launch_mfma_dim<32>(p, stream);
     return launch_mfma_dim<64>(p, stream);

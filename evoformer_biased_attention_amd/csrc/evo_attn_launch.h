@@ -38,7 +38,8 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 // f16 inputs, D in {8, 16, 32, 64}: the same MFMA kernel on binary16 operands.
 hipError_t launch_fwd_f16(const FwdArgs& a, hipStream_t stream);
 
-// f32 inputs, D in {8, 16, 32, 64}: vector-ALU kernel.
+// f32 inputs, D in {8, 16, 32, 64}: the fp32 matrix-core kernel, or the
+// vector-ALU one for layouts past its 32-bit offsets.
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 
 struct BwdArgs {

@@ -249,9 +249,9 @@ evo_status_t evo_attn_bwd_check(const void* q, const void* k, const void* v, con
  * strides giving distinct elements distinct addresses, and the extents (first
  * to last element) of outputs, workspace and inputs pairwise disjoint
  * (EVO_ERR_ALIASING).  Layouts the matrix-core kernels cannot address with
- * 32-bit offsets (or whose rows do not span every head, or whose bias strides
- * are not multiples of 16 bytes) run on the vector-ALU kernels: slower, same
- * results.
+ * 32-bit offsets, or whose rows do not span every head, run on the vector-ALU
+ * kernels: slower, same results.  Bias rows at any stride stay on the matrix
+ * cores.
  */
 evo_status_t evo_attn_bwd_strided(const void* q, const void* k, const void* v, const void* mask_bias,
                                   const void* pair_bias, const void* out, const float* lse, const void* dout,

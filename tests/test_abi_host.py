@@ -279,7 +279,7 @@ def test_bwd_workspace_size():
     assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 32), E.EVO_DTYPE_F32) == ws   # fp32 matrix cores
     assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 16), E.EVO_DTYPE_F32) == ws
     assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 64), E.EVO_DTYPE_F32) == ws
-    assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 8), E.EVO_DTYPE_F32) == 0     # vector-ALU path
+    assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 8), E.EVO_DTYPE_F32) == ws
     ws_f32_odd = E.evo_attn_bwd_workspace_size((1, 384, 383, 4, 32), E.EVO_DTYPE_F32)  # staged bias rows
     assert ws_f32_odd > 0 and ws_f32_odd % plane(1, 4, 383) == 0
     assert E.evo_attn_bwd_workspace_size((1, 384, 384, 4, 64), E.EVO_DTYPE_BF16) == ws  # matrix cores for D = 64 too

@@ -189,13 +189,14 @@ def test_bwd_ragged(torch_dev, shape, d, dtype):
         parity(torch_dev, w, dout)
 
 
-# fp32 inputs with D in {16, 32, 64}, 16-byte aligned bias rows (L % 4 == 0 in
-# the dense layout): every stage runs on the fp32 matrix-core kernels (N is too
-# small here for the pair gradient's workspace: one range of n per tile).
+# fp32 inputs with 16-byte aligned bias rows (L % 4 == 0 in the dense layout):
+# every stage runs on the fp32 matrix-core kernels, D = 8 as D = 16 with
+# zero-padded chunks (N is too small here for the pair gradient's workspace:
+# one range of n per tile).
 # Every bias combination, bias gradients on and off, against the full backward
 # oracle.
 F32_MFMA_BWD = [(1, 2, 4, 2, 16), (1, 3, 20, 2, 32), (2, 2, 68, 3, 32), (1, 2, 132, 2, 16), (1, 1, 192, 4, 32),
-                (1, 2, 36, 2, 64), (2, 2, 100, 3, 64), (1, 1, 132, 2, 64)]
+                (1, 2, 36, 2, 64), (2, 2, 100, 3, 64), (1, 1, 132, 2, 64), (1, 2, 4, 2, 8), (2, 2, 132, 3, 8)]
 
 
 @pytest.mark.parametrize("shape", F32_MFMA_BWD, ids=lambda s: "x".join(map(str, s)))
@@ -211,7 +212,8 @@ def test_bwd_f32_matrix_core_path(torch_dev, shape, bias):
         parity(torch_dev, w, dout, want_dmask=False, want_dpair=False)
 
 
-F32_STAGED_BWD = [(1, 2, 5, 2, 16), (1, 3, 17, 2, 32), (2, 2, 65, 3, 32), (1, 2, 99, 2, 64), (1, 24, 130, 2, 32)]
+F32_STAGED_BWD = [(1, 2, 5, 2, 16), (1, 3, 17, 2, 32), (2, 2, 65, 3, 32), (1, 2, 99, 2, 64), (1, 24, 130, 2, 32),
+                  (1, 20, 77, 2, 8)]
 
 
 @pytest.mark.parametrize("shape", F32_STAGED_BWD, ids=lambda s: "x".join(map(str, s)))
@@ -433,9 +435,9 @@ def test_bwd_pair_gradient_split_over_n(torch_dev, dtype, L):
         np.testing.assert_array_equal(a, b)   # only the pair gradient takes another route
 
 
-@pytest.mark.parametrize("d", [16, 64])
+@pytest.mark.parametrize("d", [8, 16, 64])
 def test_bwd_f32_split_over_n_head_dims(torch_dev, d):
-    """fp32, D = 16 and 64, with the workspace (pair gradient split over N) and without: only dpair takes
+    """fp32, D = 8, 16 and 64, with the workspace (pair gradient split over N) and without: only dpair takes
     another route, and it stays within the fp32 bound either way."""
     import evoformer_biased_attention_amd as E
     w = S.random_problem(1, 32, 136, 3, d, dtype="f32", seed=1600 + d, mask="tail", pair="normal", mask_frac=0.2)

@@ -213,6 +213,30 @@ def test_head_major_layout_runs_and_matches(torch_dev, dtype):
     compare_grads(got, want, dtype, "head-major layout")
 
 
+@pytest.mark.parametrize("D", [8, 32])
+def test_f32_row_offsets_past_31_bits(torch_dev, D):
+    """fp32 Q rows 4,000,000 floats apart (Q, and so dQ, in 256 MB buffers): the byte offsets of the rows up
+    to 128 past L exceed 2^31, which the matrix-core kernels do not form, so both passes run on the
+    vector-ALU kernels; out and every gradient still match the oracle."""
+    torch = torch_dev
+    from test_gpu_parity import compare as compare_fwd
+    B, N, L, H, rs = 1, 1, 16, 2, 4_000_000
+    w = S.random_problem(B, N, L, H, D, dtype="f32", seed=95 + D, mask="tail", pair="normal", mask_frac=0.2)
+    dout = S.random_dout(w.shape, "f32", seed=96 + D)
+    buf = torch.zeros((L, rs), dtype=torch.float32, device="cuda")
+    buf[:, : H * D].copy_(to_dev(torch, w.q, "f32").reshape(L, H * D))
+    q = buf[:, : H * D].view(L, H, D)[None, None]
+    assert q.stride(2) == rs
+    k, v, do = (to_dev(torch, x, "f32") for x in (w.k, w.v, dout))
+    got, delta, raw = strided_bwd(torch, q, k, v, to_dev(torch, w.mask, "f32"), to_dev(torch, w.pair, "f32"), do)
+    ro, rl = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype="f32", nthreads=THREADS)
+    compare_fwd(f64(raw[6]), None, ro, None, "f32", f"rows {rs} apart, D={D}")
+    want = oracle.bwd(w.q, w.k, w.v, w.mask, w.pair, dout, dtype="f32", nthreads=THREADS)
+    compare_grads(got, want, "f32", f"rows {rs} apart, D={D}")
+    compare_delta(delta, w, dout, f"rows {rs} apart, D={D}")
+    del buf
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
 def test_dense_layout_through_strided_entry_is_identical(torch_dev, dtype):
     torch = torch_dev

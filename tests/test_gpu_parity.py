@@ -162,12 +162,11 @@ def test_ragged_f32(torch_dev, shape):
     parity_full(torch_dev, w)
 
 
-# fp32 inputs with D in {16, 32, 64} take the matrix-core fp32 kernel (bias
-# rows that are not 16-byte aligned, L % 4 != 0 in the dense layout, through
-# its staged variant); D = 8 takes the vector-ALU one.  All against the full
-# oracle.
+# fp32 inputs take the matrix-core fp32 kernel (bias rows that are not 16-byte
+# aligned, L % 4 != 0 in the dense layout, through its staged variant); D = 8
+# runs as D = 16 with zero-padded chunks.  All against the full oracle.
 F32_MFMA_SHAPES = [(1, 2, 4, 2, 16), (1, 3, 20, 2, 32), (2, 2, 68, 3, 32), (1, 2, 132, 2, 64), (1, 1, 256, 4, 16),
-                   (1, 2, 100, 2, 32), (2, 3, 64, 2, 64), (1, 1, 192, 1, 32)]
+                   (1, 2, 100, 2, 32), (2, 3, 64, 2, 64), (1, 1, 192, 1, 32), (1, 2, 4, 2, 8), (2, 2, 132, 3, 8)]
 
 
 @pytest.mark.parametrize("shape", F32_MFMA_SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -181,7 +180,7 @@ def test_f32_matrix_core_path(torch_dev, shape, bias):
 
 
 F32_STAGED_SHAPES = [(1, 2, 5, 2, 16), (1, 3, 17, 2, 32), (2, 2, 65, 3, 32), (1, 2, 99, 2, 64), (1, 1, 130, 4, 16),
-                     (1, 2, 383, 2, 32)]
+                     (1, 2, 383, 2, 32), (1, 3, 77, 2, 8)]
 
 
 @pytest.mark.parametrize("shape", F32_STAGED_SHAPES, ids=lambda s: "x".join(map(str, s)))

@@ -3,8 +3,8 @@
 Each case draws a dtype, a head dimension, B, N, L, H, the bias subset and the kind of mask (tail padding,
 random keys, or N(0, s^2) values) and a bias scale, then checks the forward (out and lse) and the backward
 (every gradient and delta) element by element at the same tolerances as the fixed-shape tests.  The cases
-cross the kernel families' boundaries: 16-bit and fp32 matrix-core kernels, the fp32 vector-ALU kernels
-(D = 8), aligned and staged bias rows (L % 8 and L % 4), partial 64-key blocks, and the pair gradient's
+cross the kernel families' boundaries: 16-bit and fp32 matrix-core kernels (D = 8 padded with zero columns on
+both), aligned and staged bias rows (L % 8 and L % 4), partial 64-key blocks, and the pair gradient's
 workspace split over N when N is large enough.  A sequence whose every key would carry the finite -1e9 mask
 (no parity claim for such rows) gets its first key unmasked.
 
