@@ -231,10 +231,11 @@ def test_bwd_f32_matrix_core_unaligned_bias_rows(torch_dev, shape):
         parity(torch_dev, w, dout, use_ws=False)
 
 
-def test_bwd_f32_matrix_core_masked_rows(torch_dev):
+@pytest.mark.parametrize("D", [32, 8])
+def test_bwd_f32_matrix_core_masked_rows(torch_dev, D):
     """fp32 backward with -inf masks on part of a row and on a whole row (no gradient passes through it),
-    and a peaked softmax (bias scale 8), on the matrix-core path."""
-    B, N, L, H, D = 1, 4, 96, 2, 32
+    and a peaked softmax (bias scale 8), on the matrix-core path (D = 8 zero-padded to 16)."""
+    B, N, L, H = 1, 4, 96, 2
     w = S.random_problem(B, N, L, H, D, dtype="f32", seed=321, mask="zero", pair="normal", bias_scale=8.0)
     mf = np.zeros((B, N, 1, 1, L), np.float32)
     mf[0, 0, ..., 10:50] = -np.inf

@@ -203,11 +203,12 @@ def test_f32_matrix_core_unaligned_bias_rows(torch_dev, shape, bias):
     parity_full(torch_dev, w)
 
 
+@pytest.mark.parametrize("D", [32, 8])
 @pytest.mark.parametrize("L", [64, 96, 66, 97])
-def test_f32_infinite_and_nan_masks(torch_dev, L):
+def test_f32_infinite_and_nan_masks(torch_dev, L, D):
     """fp32 masks with -inf on part of a row, on a whole row (out = 0, lse = -inf), a finite -1e9 on a
-    leading half, and a NaN (its sequence NaN)."""
-    B, N, H, D = 1, 5, 2, 32
+    leading half, and a NaN (its sequence NaN).  D = 8 runs zero-padded to 16."""
+    B, N, H = 1, 5, 2
     w = S.random_problem(B, N, L, H, D, dtype="f32", seed=L + 5, mask="zero", pair="normal")
     mf = np.zeros((B, N, 1, 1, L), np.float32)
     mf[0, 0, ..., 10:50] = -np.inf
@@ -220,7 +221,7 @@ def test_f32_infinite_and_nan_masks(torch_dev, L):
     assert np.all(o[0, 1] == 0) and np.all(np.isneginf(l[0, 1]))
     assert np.isnan(o[0, 3]).all() and np.isnan(l[0, 3]).all()
     keep = np.array([True, True, True, False, True])
-    compare(o[:, keep], l[:, keep], ro[:, keep], rl[:, keep], "f32", f"fp32 infinite masks, L={L}")
+    compare(o[:, keep], l[:, keep], ro[:, keep], rl[:, keep], "f32", f"fp32 infinite masks, L={L}, D={D}")
 
 
 def test_large_bias_magnitudes(torch_dev):
