@@ -437,23 +437,43 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
     }
     float lsv = 0.f, dlv = 0.f;  // wave 0: this lane's query of the step being copied
     uint4 pstage[PCW];           // STAGED: pair chunks between their load and their landing in LDS
-    auto copy_block = [&](int it, KvBuf<QS, kDH, KT>* __restrict__ dst) {
-        const int h = it / nqb, q0 = (it - h * nqb) * QS;
-        dma16(rq, &dst->q[qhh][64 * qrg], qoff + (uint32_t)q0 * rowq + (uint32_t)h * hq, 0);
-        dma16(rdo, &dst->dout[qhh][64 * qrg], dooff + (uint32_t)q0 * rowo + (uint32_t)h * ho, 0);
+    // The step copied next: head ch, queries from cq0; its byte offsets within
+    // the q and dO buffers, its pair matrix and its lse / delta rows.  All are
+    // advanced step by step (no division or 64-bit product inside the loop).
+    int ch = 0, cq0 = 0;
+    uint32_t cqo = 0, cdo = 0;
+    const u16* cpair = PAIR ? p.pair + b * st.pb : p.q;
+    const float* clse = p.lse + bn * p.H * st.lrow;
+    const float* cdelta = p.delta + bn * p.H * st.lrow;
+    auto copy_block = [&](KvBuf<QS, kDH, KT>* __restrict__ dst) {
+        dma16(rq, &dst->q[qhh][64 * qrg], qoff + cqo, 0);
+        dma16(rdo, &dst->dout[qhh][64 * qrg], dooff + cdo, 0);
         if (PAIR) {
             const uint32_t prange = last * rowp + (uint32_t)L * 2u;
-            const Rsrc rp = make_rsrc(p.pair + b * st.pb + h * st.ph, bias_range(prange, STAGED));
+            const Rsrc rp = make_rsrc(cpair, bias_range(prange, STAGED));
             for (int j = 0; j < PCW; ++j) {
-                if (STAGED) pstage[j] = bload16_any(rp, pvo[j] + (uint32_t)q0 * rowp, prange);
-                else dma16(rp, &dst->pt[64 * (PCW * wave + j)], pvo[j] + (uint32_t)q0 * rowp, 0);
+                if (STAGED) pstage[j] = bload16_any(rp, pvo[j] + (uint32_t)cq0 * rowp, prange);
+                else dma16(rp, &dst->pt[64 * (PCW * wave + j)], pvo[j] + (uint32_t)cq0 * rowp, 0);
             }
         }
         if (wave == 0 && lane < QS) {
-            const int i = q0 + lane;
-            const int64_t row = (bn * p.H + h) * st.lrow + i;
-            lsv = i < L ? lse_base2(p.lse[row]) : INFINITY;
-            dlv = i < L ? -p.delta[row] : 0.f;  // negated: the accumulator input of dP
+            const int i = cq0 + lane;
+            lsv = i < L ? lse_base2(clse[i]) : INFINITY;
+            dlv = i < L ? -cdelta[i] : 0.f;  // negated: the accumulator input of dP
+        }
+    };
+    auto next_copy = [&]() {
+        cq0 += QS;
+        cqo += (uint32_t)QS * rowq;
+        cdo += (uint32_t)QS * rowo;
+        if (cq0 >= L) {  // the next head
+            cq0 = 0;
+            ++ch;
+            cqo = (uint32_t)ch * hq;
+            cdo = (uint32_t)ch * ho;
+            cpair += st.ph;
+            clse += st.lrow;
+            cdelta += st.lrow;
         }
     };
     auto put_rows = [&](KvBuf<QS, kDH, KT>* __restrict__ dst) {
@@ -470,15 +490,16 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
     float dm[KT];
     for (int t = 0; t < KT; ++t) dm[t] = 0.f;
 
-    copy_block(0, &sm[0]);
+    copy_block(&sm[0]);
+    next_copy();
     put_rows(&sm[0]);
     wait_all();
     __syncthreads();
 
+    int h = 0, qbk = 0;  // the step's head and query block
     for (int it = 0; it < nsteps; ++it) {
         const KvBuf<QS, kDH, KT>* __restrict__ cur = &sm[it & 1];
         KvBuf<QS, kDH, KT>* __restrict__ nxt = &sm[(it & 1) ^ 1];
-        const int h = it / nqb, qbk = it - h * nqb;
         if (qbk == 0) {
             for (int t = 0; t < KT; ++t) {
                 const uint32_t j = (uint32_t)(kw0 + 16 * t + c);
@@ -528,7 +549,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
             dlq[qt] = *reinterpret_cast<const float4*>(&cur->dl[16 * qt + 4 * g]);
         }
 
-        if (it + 1 < nsteps) copy_block(it + 1, nxt);
+        if (it + 1 < nsteps) {
+            copy_block(nxt);
+            next_copy();
+        }
 
         f32x4 sc[QT][KT], dp[QT][KT];
         for (int qt = 0; qt < QT; ++qt)
@@ -596,6 +620,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
                 }
             }
         }
+        if (++qbk == nqb) qbk = 0, ++h;
     }
     if (MASK && p.dmask)
         for (int t = 0; t < KT; ++t) {
@@ -861,11 +886,26 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
     }
     float lsv = 0.f, dlv = 0.f;
     uint4 mstage;  // STAGED: the mask chunk between its load and its landing in LDS
-    auto copy_step = [&](int64_t n, Buf* __restrict__ dst) {
-        const Rsrc rq = make_rsrc(p.q + b * st.q[0] + n * st.q[1] + h * st.q[3], last * rowq + D * 2);
-        const Rsrc rd = make_rsrc(p.dout + b * st.o[0] + n * st.o[1] + h * st.o[3], last * rowo + D * 2);
-        const Rsrc rk = make_rsrc(p.k + b * st.k[0] + n * st.k[1] + h * st.k[3], last * rowk + D * 2);
-        const Rsrc rv = make_rsrc(p.v + b * st.v[0] + n * st.v[1] + h * st.v[3], last * rowv + D * 2);
+    // slices of the sequence copied next (n0 first), advanced by one n per step
+    // (no 64-bit product inside the loop)
+    const u16* cq = p.q + b * st.q[0] + n0 * st.q[1] + h * st.q[3];
+    const u16* cd = p.dout + b * st.o[0] + n0 * st.o[1] + h * st.o[3];
+    const u16* ck = p.k + b * st.k[0] + n0 * st.k[1] + h * st.k[3];
+    const u16* cv = p.v + b * st.v[0] + n0 * st.v[1] + h * st.v[3];
+    const u16* cm = MASK ? p.mask + b * st.mb + n0 * st.mn : p.q;
+    const int64_t lstep = p.H * st.lrow;  // lse / delta elements between consecutive n
+    const float* clse = p.lse + ((b * N + n0) * p.H + h) * st.lrow;
+    const float* cdelta = p.delta + ((b * N + n0) * p.H + h) * st.lrow;
+    auto next_step = [&]() {
+        cq += st.q[1], cd += st.o[1], ck += st.k[1], cv += st.v[1];
+        if (MASK) cm += st.mn;
+        clse += lstep, cdelta += lstep;
+    };
+    auto copy_step = [&](Buf* __restrict__ dst) {
+        const Rsrc rq = make_rsrc(cq, last * rowq + D * 2);
+        const Rsrc rd = make_rsrc(cd, last * rowo + D * 2);
+        const Rsrc rk = make_rsrc(ck, last * rowk + D * 2);
+        const Rsrc rv = make_rsrc(cv, last * rowv + D * 2);
         for (int hh = 0; hh < kDH; ++hh) {
             dma16(rq, &dst->q[hh][64 * wave], qoff[hh], 0);
             dma16(rd, &dst->dout[hh][64 * wave], dooff[hh], 0);
@@ -873,15 +913,14 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
             dma16(rv, &dst->v[hh][64 * wave], voff[hh], 0);
         }
         if (MASK && wave == 0 && lane < 8) {
-            const Rsrc rm = make_rsrc(p.mask + b * st.mb + n * st.mn, bias_range((uint32_t)L * 2u, STAGED));
+            const Rsrc rm = make_rsrc(cm, bias_range((uint32_t)L * 2u, STAGED));
             if (STAGED) mstage = bload16_any(rm, (uint32_t)j0 * 2u + 16u * lane, (uint32_t)L * 2u);
             else dma16(rm, &dst->mt[0], (uint32_t)j0 * 2u + 16u * lane, 0);
         }
         if (wave == 1) {
             const int i = i0 + lane;
-            const int64_t row = ((b * N + n) * p.H + h) * st.lrow + i;
-            lsv = i < L ? lse_base2(p.lse[row]) : INFINITY;
-            dlv = i < L ? -p.delta[row] : 0.f;  // negated: the accumulator input of dP
+            lsv = i < L ? lse_base2(clse[i]) : INFINITY;
+            dlv = i < L ? -cdelta[i] : 0.f;  // negated: the accumulator input of dP
         }
     };
     auto put_rows = [&](Buf* __restrict__ dst) {
@@ -895,7 +934,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
     f32x4 acc[kKT];
     for (int kt = 0; kt < kKT; ++kt) acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    copy_step(n0, &sm[0]);
+    copy_step(&sm[0]);
+    next_step();
     put_rows(&sm[0]);
     wait_all();
     __syncthreads();
@@ -918,7 +958,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
             if (MASK) mb[kt] = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(&cur->mt[2 * kt + (g >> 1)]) + 8 * (g & 1));
         }
         const float lsq = cur->ls[16 * wave + c], dlq = cur->dl[16 * wave + c];
-        if (n + 1 < n1) copy_step(n + 1, nxt);
+        if (n + 1 < n1) {
+            copy_step(nxt);
+            next_step();
+        }
         for (int kt = 0; kt < kKT; ++kt) {
             f32x4 sc = pbs[kt], dp = f32x4{dlq, dlq, dlq, dlq};  // -delta: dP - delta comes out
             for (int hh = 0; hh < kDH; ++hh) {
