@@ -280,9 +280,12 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
     const uint32_t prange = PAIR ? pbytes : 0u;
     auto copy_block = [&](int blk, Buf* __restrict__ dst) {
         const uint32_t k0 = (uint32_t)blk * kKB;
+        // Untracked copies: the compiler would otherwise make every later LDS
+        // read (of the other buffer too) wait for them.  wait_all() at the
+        // end of the step waits for them before the barrier.
         for (int hh = 0; hh < kDH; ++hh) {
-            dma16(rk, &dst->k[hh][64 * wave], ko[hh] + k0 * rowk, 0);
-            dma16(rv, &dst->v[hh][64 * wave], vo[hh] + k0 * rowv, 0);
+            dma16_untracked(rk, &dst->k[hh][64 * wave], ko[hh] + k0 * rowk);
+            dma16_untracked(rv, &dst->v[hh][64 * wave], vo[hh] + k0 * rowv);
         }
         if (STAGED) {
             if (PAIR)
@@ -290,8 +293,8 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
             if (MASK && wave == 0 && lane < 8) mstage = bload16_any(rm, 16u * lane + k0 * 2u, mbytes);
         } else {
             if (PAIR)
-                for (int j = 0; j < 4; ++j) dma16(rp, &dst->pt[64 * (4 * wave + j)], pvo[j] + k0 * 2u, 0);
-            if (MASK && wave == 0 && lane < 8) dma16(rm, &dst->mt[0], 16u * lane + k0 * 2u, 0);
+                for (int j = 0; j < 4; ++j) dma16_untracked(rp, &dst->pt[64 * (4 * wave + j)], pvo[j] + k0 * 2u);
+            if (MASK && wave == 0 && lane < 8) dma16_untracked(rm, &dst->mt[0], 16u * lane + k0 * 2u);
         }
     };
     // STAGED: the staged chunks into the slots the direct copies would fill
@@ -357,15 +360,19 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
                 for (int t = 0; t < kQTiles; ++t) acc[t][kt] = E::mfma(kop[kt][hh], qop[t][hh], acc[t][kt]);
     };
 
-    // One block of keys; TAIL marks the last block when L % 64 != 0.  Every
-    // LDS read of the block (score operands, then the V operands of P.V) is
-    // issued before the next block's copy into the other buffer: the
-    // compiler orders LDS reads after an LDS-destination load behind that
-    // load's completion, which would expose the global latency here.
+    // One block of keys; TAIL marks the last block when L % 64 != 0.  The
+    // direct copies of the next block are issued first (see below); with
+    // STAGED every LDS read of the block is issued before the next block's
+    // staged loads, whose registers the block's operands free.
     auto step = [&](int it, const Buf* __restrict__ cur, Buf* __restrict__ nxt, auto tail_tag) {
         constexpr bool TAIL = decltype(tail_tag)::value;
         const int k0 = it * kKB;
 
+        // The next block's copies go first: the other buffer's readers all
+        // passed the barrier that ended the previous step, and the copies
+        // then have the whole step to land.  (STAGED: its loads into
+        // registers keep their place below, where their registers are free.)
+        if (!STAGED && it + 1 < nblocks) copy_block(it + 1, nxt);
         f32x4 acc[kQTiles][kKT];
         bool mask_on = false;
         if (MASK) {
@@ -399,7 +406,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
                 vop[cc][dh] = as_v8<E>(uint4{lo.x, lo.y, hi.x, hi.y});
             }
 
-        if (it + 1 < nblocks) copy_block(it + 1, nxt);  // lands while this block is processed
+        if (STAGED && it + 1 < nblocks) copy_block(it + 1, nxt);  // lands while this block is processed
 
         if (TAIL)  // keys past L take no weight
             for (int kt = 0; kt < kKT; ++kt)
