@@ -278,15 +278,20 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
     // its landing in LDS
     uint4 pstage[4], mstage;
     const uint32_t prange = PAIR ? pbytes : 0u;
-    auto copy_block = [&](int blk, Buf* __restrict__ dst) {
+    // K and V always go straight into LDS, as untracked copies (the compiler
+    // would otherwise make every later LDS read, of the other buffer too,
+    // wait for them); wait_all() at the end of the step waits for them
+    // before the barrier.  The bias tiles go straight into LDS the same way,
+    // or (STAGED) through registers.
+    auto copy_kv = [&](int blk, Buf* __restrict__ dst) {
         const uint32_t k0 = (uint32_t)blk * kKB;
-        // Untracked copies: the compiler would otherwise make every later LDS
-        // read (of the other buffer too) wait for them.  wait_all() at the
-        // end of the step waits for them before the barrier.
         for (int hh = 0; hh < kDH; ++hh) {
             dma16_untracked(rk, &dst->k[hh][64 * wave], ko[hh] + k0 * rowk);
             dma16_untracked(rv, &dst->v[hh][64 * wave], vo[hh] + k0 * rowv);
         }
+    };
+    auto copy_bias = [&](int blk, Buf* __restrict__ dst) {
+        const uint32_t k0 = (uint32_t)blk * kKB;
         if (STAGED) {
             if (PAIR)
                 for (int j = 0; j < 4; ++j) pstage[j] = bload16_any(rp, pvo[j] + k0 * 2u, prange);
@@ -320,7 +325,8 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
     // bfloat16 with a mask: a mask NaN with the sign bit set was seen
     bool mask_neg_nan = false;
 
-    copy_block(0, &sm.buf[0]);
+    copy_kv(0, &sm.buf[0]);
+    copy_bias(0, &sm.buf[0]);
     land_block(&sm.buf[0]);
     wait_all();
     __syncthreads();
@@ -361,18 +367,21 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
     };
 
     // One block of keys; TAIL marks the last block when L % 64 != 0.  The
-    // direct copies of the next block are issued first (see below); with
-    // STAGED every LDS read of the block is issued before the next block's
-    // staged loads, whose registers the block's operands free.
+    // next block's direct copies are issued first (see below); with STAGED
+    // the bias loads into registers come after the block's LDS reads, whose
+    // registers they reuse.
     auto step = [&](int it, const Buf* __restrict__ cur, Buf* __restrict__ nxt, auto tail_tag) {
         constexpr bool TAIL = decltype(tail_tag)::value;
         const int k0 = it * kKB;
 
         // The next block's copies go first: the other buffer's readers all
         // passed the barrier that ended the previous step, and the copies
-        // then have the whole step to land.  (STAGED: its loads into
+        // then have the whole step to land.  (STAGED: the bias loads into
         // registers keep their place below, where their registers are free.)
-        if (!STAGED && it + 1 < nblocks) copy_block(it + 1, nxt);
+        if (it + 1 < nblocks) {
+            copy_kv(it + 1, nxt);
+            if (!STAGED) copy_bias(it + 1, nxt);
+        }
         f32x4 acc[kQTiles][kKT];
         bool mask_on = false;
         if (MASK) {
@@ -406,7 +415,7 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
                 vop[cc][dh] = as_v8<E>(uint4{lo.x, lo.y, hi.x, hi.y});
             }
 
-        if (STAGED && it + 1 < nblocks) copy_block(it + 1, nxt);  // lands while this block is processed
+        if (STAGED && it + 1 < nblocks) copy_bias(it + 1, nxt);  // lands while this block is processed
 
         if (TAIL)  // keys past L take no weight
             for (int kt = 0; kt < kKT; ++kt)
