@@ -496,20 +496,27 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
     wait_all();
     __syncthreads();
 
+    // the wave's K and V rows of head hd (A operands over d, key 16t + c, chunk g of each half)
+    auto load_kv = [&](int hd) {
+        for (int t = 0; t < KT; ++t) {
+            const uint32_t j = (uint32_t)(kw0 + 16 * t + c);
+            for (int hh = 0; hh < kDH; ++hh) {
+                const bool in = 4 * hh + g < kDC;
+                kop[t][hh] = as_v8<E>(bload16(rk, in ? j * rowk + (uint32_t)hd * hk + 64u * hh + 16u * g : kOOB, 0));
+                vop[t][hh] = as_v8<E>(bload16(rv, in ? j * rowv + (uint32_t)hd * hv + 64u * hh + 16u * g : kOOB, 0));
+            }
+        }
+    };
     int h = 0, qbk = 0;  // the step's head and query block
     for (int it = 0; it < nsteps; ++it) {
         const KvBuf<QS, kDH, KT>* __restrict__ cur = &sm[it & 1];
         KvBuf<QS, kDH, KT>* __restrict__ nxt = &sm[(it & 1) ^ 1];
         if (qbk == 0) {
-            for (int t = 0; t < KT; ++t) {
-                const uint32_t j = (uint32_t)(kw0 + 16 * t + c);
-                for (int hh = 0; hh < kDH; ++hh) {
-                    const bool in = 4 * hh + g < kDC;
-                    kop[t][hh] = as_v8<E>(bload16(rk, in ? j * rowk + (uint32_t)h * hk + 64u * hh + 16u * g : kOOB, 0));
-                    vop[t][hh] = as_v8<E>(bload16(rv, in ? j * rowv + (uint32_t)h * hv + 64u * hh + 16u * g : kOOB, 0));
-                }
+            // aligned bias rows: later heads were loaded during the previous
+            // head's last step (STAGED has no registers to spare for that)
+            if (h == 0 || STAGED) load_kv(h);
+            for (int t = 0; t < KT; ++t)
                 for (int dh = 0; dh < kDHT; ++dh) dkacc[t][dh] = dvacc[t][dh] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
         }
         // A operands: Q and dO rows (query 16qt + c, chunk g of each half);
         // transposed Q and dO for the products over queries (column 16dh + c
@@ -564,6 +571,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
                     dp[qt][t] = E::mfma(ado[qt][hh], vop[t][hh], dp[qt][t]);
                 }
             }
+        // the head's last step: its K and V rows are no longer needed, so the
+        // next head's are loaded now and land during the rest of the step
+        if (!STAGED && qbk == nqb - 1 && h + 1 < H) load_kv(h + 1);
         // lane (c + 16g) holds S[query 16qt + 4g + r][key 16t + c]
         V8 pm[KT][CC], dsm[KT][CC];
         for (int t = 0; t < KT; ++t) {
