@@ -141,9 +141,9 @@ __global__ __launch_bounds__(64 * kNW, 4) void trimul_kernel(TmParams p) {
                 oa = offa[q] + (uint32_t)k0 * (uint32_t)L * 2u;  // k rows past L start beyond the range
                 ow = offw[q] + (uint32_t)k0 * (uint32_t)L * 2u;
             }
-            if (!STAGED) {
-                dma16(ra, &dst->a[64 * (SEG * wave + q)], oa);
-                dma16(rw, &dst->w[64 * (SEG * wave + q)], ow);
+            if (!STAGED) {  // untracked: waited for by wait_all() before the step's barrier
+                dma16_untracked(ra, &dst->a[64 * (SEG * wave + q)], oa);
+                dma16_untracked(rw, &dst->w[64 * (SEG * wave + q)], ow);
             } else {
                 sa[q] = bload16_any(ra, oa, range);
                 sw[q] = bload16_any(rw, ow, range);
@@ -175,8 +175,10 @@ __global__ __launch_bounds__(64 * kNW, 4) void trimul_kernel(TmParams p) {
     __syncthreads();
     for (int st = 0; st < nsteps; ++st) {
         const TmBuf<KS>* __restrict__ cur = &sm[st & 1];
-        // every LDS read of the step first: the compiler orders an LDS read
-        // that follows a copy into LDS behind that copy's completion
+        // direct copies of the next step go first (the other buffer's readers
+        // all passed the previous barrier); STAGED loads into registers come
+        // after the step's LDS reads, whose registers they reuse
+        if (!STAGED && st + 1 < nsteps) copy_step(st + 1, &sm[(st & 1) ^ 1]);
         V8 aop[KC][4], bop[KC][4];  // A operand: w side (rows j); B operand: a side (columns i)
         for (int kc = 0; kc < KC; ++kc)
             for (int q = 0; q < 4; ++q) {
@@ -202,7 +204,7 @@ __global__ __launch_bounds__(64 * kNW, 4) void trimul_kernel(TmParams p) {
                     }
                 }
             }
-        if (st + 1 < nsteps) copy_step(st + 1, &sm[(st & 1) ^ 1]);
+        if (STAGED && st + 1 < nsteps) copy_step(st + 1, &sm[(st & 1) ^ 1]);
         for (int kc = 0; kc < KC; ++kc)
             for (int mt = 0; mt < 4; ++mt)
                 for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = E::mfma(aop[kc][mt], bop[kc][nt], acc[mt][nt]);
