@@ -118,7 +118,7 @@ struct DqBuf {
 // elements); their tiles go global -> registers -> LDS through unaligned
 // 16-byte loads, into the slots the direct copies would fill.
 template <class E, int D, bool PAIR, bool MASK, bool STAGED>
-__global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
+__global__ __launch_bounds__(kWaves * 64, (D <= 32 && !STAGED) ? 3 : 2) void bwd_dq_mfma(Params p) {
     using V8 = typename E::v8;
     constexpr int kDC = D / 8;           // 16-byte chunks per row
     constexpr int kDH = (D + 31) / 32;   // 32-wide halves of a row
@@ -204,9 +204,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
     const uint32_t prange = PAIR ? last * rowp + (uint32_t)L * 2u : 0u;
     auto copy_block = [&](int blk, Buf* __restrict__ dst) {
         const uint32_t k0 = (uint32_t)blk * kKB;
+        // untracked copies (later LDS reads of the other buffer need not wait
+        // for them); wait_all() before the step's barrier waits for them
         for (int hh = 0; hh < kDH; ++hh) {
-            dma16(rk, &dst->k[hh][64 * wave], ko[hh] + k0 * rowk, 0);
-            dma16(rv, &dst->v[hh][64 * wave], vo[hh] + k0 * rowv, 0);
+            dma16_untracked(rk, &dst->k[hh][64 * wave], ko[hh] + k0 * rowk);
+            dma16_untracked(rv, &dst->v[hh][64 * wave], vo[hh] + k0 * rowv);
         }
         if (STAGED) {
             if (PAIR)
@@ -214,8 +216,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
             if (MASK && wave == 0 && lane < 8) mstage = bload16_any(rm, 16u * lane + k0 * 2u, (uint32_t)L * 2u);
         } else {
             if (PAIR)
-                for (int j = 0; j < 4; ++j) dma16(rp, &dst->pt[64 * (4 * wave + j)], pvo[j] + k0 * 2u, 0);
-            if (MASK && wave == 0 && lane < 8) dma16(rm, &dst->mt[0], 16u * lane + k0 * 2u, 0);
+                for (int j = 0; j < 4; ++j) dma16_untracked(rp, &dst->pt[64 * (4 * wave + j)], pvo[j] + k0 * 2u);
+            if (MASK && wave == 0 && lane < 8) dma16_untracked(rm, &dst->mt[0], 16u * lane + k0 * 2u);
         }
     };
     auto land_block = [&](Buf* __restrict__ dst) {
@@ -237,6 +239,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
     auto step = [&](int it, const Buf* __restrict__ cur, Buf* __restrict__ nxt, auto tail_tag) {
         constexpr bool TAIL = decltype(tail_tag)::value;
         const int k0 = it * kKB;
+        // aligned bias rows: the next block's copies first (the other buffer's
+        // readers all passed the previous barrier); STAGED keeps them after
+        // the block's LDS reads, whose registers its staged loads reuse
+        if (!STAGED && it + 1 < nblocks) copy_block(it + 1, nxt);
         // A operands: K and V rows (key 16kt + c, chunk g) and transposed K
         // for dQ^T = K^T.dS^T (column 16dh + c over keys 32cc + 4g + 0..3 and
         // 32cc + 16 + 4g + 0..3)
@@ -268,7 +274,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dq_mfma(Params p) {
                 }
         }
 
-        if (it + 1 < nblocks) copy_block(it + 1, nxt);
+        if (STAGED && it + 1 < nblocks) copy_block(it + 1, nxt);
 
         f32x4 s[2][kKT], dp[2][kKT];
         for (int kt = 0; kt < kKT; ++kt)
@@ -446,14 +452,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
     const float* clse = p.lse + bn * p.H * st.lrow;
     const float* cdelta = p.delta + bn * p.H * st.lrow;
     auto copy_block = [&](KvBuf<QS, kDH, KT>* __restrict__ dst) {
-        dma16(rq, &dst->q[qhh][64 * qrg], qoff + cqo, 0);
-        dma16(rdo, &dst->dout[qhh][64 * qrg], dooff + cdo, 0);
+        // untracked copies, waited for by wait_all() before the step's barrier
+        dma16_untracked(rq, &dst->q[qhh][64 * qrg], qoff + cqo);
+        dma16_untracked(rdo, &dst->dout[qhh][64 * qrg], dooff + cdo);
         if (PAIR) {
             const uint32_t prange = last * rowp + (uint32_t)L * 2u;
             const Rsrc rp = make_rsrc(cpair, bias_range(prange, STAGED));
             for (int j = 0; j < PCW; ++j) {
                 if (STAGED) pstage[j] = bload16_any(rp, pvo[j] + (uint32_t)cq0 * rowp, prange);
-                else dma16(rp, &dst->pt[64 * (PCW * wave + j)], pvo[j] + (uint32_t)cq0 * rowp, 0);
+                else dma16_untracked(rp, &dst->pt[64 * (PCW * wave + j)], pvo[j] + (uint32_t)cq0 * rowp);
             }
         }
         if (wave == 0 && lane < QS) {
@@ -511,6 +518,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
     for (int it = 0; it < nsteps; ++it) {
         const KvBuf<QS, kDH, KT>* __restrict__ cur = &sm[it & 1];
         KvBuf<QS, kDH, KT>* __restrict__ nxt = &sm[(it & 1) ^ 1];
+        // aligned bias rows: the next step's copies first (see the dq kernel)
+        if (!STAGED && it + 1 < nsteps) {
+            copy_block(nxt);
+            next_copy();
+        }
         if (qbk == 0) {
             // aligned bias rows: later heads were loaded during the previous
             // head's last step (STAGED has no registers to spare for that)
@@ -556,7 +568,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
             dlq[qt] = *reinterpret_cast<const float4*>(&cur->dl[16 * qt + 4 * g]);
         }
 
-        if (it + 1 < nsteps) {
+        if (STAGED && it + 1 < nsteps) {
             copy_block(nxt);
             next_copy();
         }
@@ -916,16 +928,17 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
         const Rsrc rd = make_rsrc(cd, last * rowo + D * 2);
         const Rsrc rk = make_rsrc(ck, last * rowk + D * 2);
         const Rsrc rv = make_rsrc(cv, last * rowv + D * 2);
+        // untracked copies, waited for by wait_all() before the step's barrier
         for (int hh = 0; hh < kDH; ++hh) {
-            dma16(rq, &dst->q[hh][64 * wave], qoff[hh], 0);
-            dma16(rd, &dst->dout[hh][64 * wave], dooff[hh], 0);
-            dma16(rk, &dst->k[hh][64 * wave], koff[hh], 0);
-            dma16(rv, &dst->v[hh][64 * wave], voff[hh], 0);
+            dma16_untracked(rq, &dst->q[hh][64 * wave], qoff[hh]);
+            dma16_untracked(rd, &dst->dout[hh][64 * wave], dooff[hh]);
+            dma16_untracked(rk, &dst->k[hh][64 * wave], koff[hh]);
+            dma16_untracked(rv, &dst->v[hh][64 * wave], voff[hh]);
         }
         if (MASK && wave == 0 && lane < 8) {
             const Rsrc rm = make_rsrc(cm, bias_range((uint32_t)L * 2u, STAGED));
             if (STAGED) mstage = bload16_any(rm, (uint32_t)j0 * 2u + 16u * lane, (uint32_t)L * 2u);
-            else dma16(rm, &dst->mt[0], (uint32_t)j0 * 2u + 16u * lane, 0);
+            else dma16_untracked(rm, &dst->mt[0], (uint32_t)j0 * 2u + 16u * lane);
         }
         if (wave == 1) {
             const int i = i0 + lane;
@@ -953,6 +966,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
         const int it = (int)(n - n0);
         const Buf* __restrict__ cur = &sm[it & 1];
         Buf* __restrict__ nxt = &sm[(it & 1) ^ 1];
+        // aligned mask rows: the next step's copies first (see the dq kernel)
+        if (!STAGED && n + 1 < n1) {
+            copy_step(nxt);
+            next_step();
+        }
         const int sw = g ^ ((c >> 2) & 3);
         V8 qop[kDH], dop[kDH], kop[kKT][kDH], vop[kKT][kDH];
         for (int hh = 0; hh < kDH; ++hh) {
@@ -968,7 +986,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
             if (MASK) mb[kt] = *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(&cur->mt[2 * kt + (g >> 1)]) + 8 * (g & 1));
         }
         const float lsq = cur->ls[16 * wave + c], dlq = cur->dl[16 * wave + c];
-        if (n + 1 < n1) {
+        if (STAGED && n + 1 < n1) {
             copy_step(nxt);
             next_step();
         }
