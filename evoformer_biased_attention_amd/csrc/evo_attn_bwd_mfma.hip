@@ -202,23 +202,28 @@ __global__ __launch_bounds__(kWaves * 64, (D <= 32 && !STAGED) ? 3 : 2) void bwd
     }
     uint4 pstage[4], mstage;  // STAGED: chunks between their load and their landing in LDS
     const uint32_t prange = PAIR ? last * rowp + (uint32_t)L * 2u : 0u;
-    auto copy_block = [&](int blk, Buf* __restrict__ dst) {
+    // The copies of a block: the direct ones (K, V and, with aligned rows, the
+    // bias tiles) go straight into LDS as untracked copies, waited for by
+    // wait_all() before the step's barrier; STAGED bias chunks go through
+    // registers (copy_staged), after the step's LDS reads, whose registers they reuse.
+    auto copy_direct = [&](int blk, Buf* __restrict__ dst) {
         const uint32_t k0 = (uint32_t)blk * kKB;
-        // untracked copies (later LDS reads of the other buffer need not wait
-        // for them); wait_all() before the step's barrier waits for them
         for (int hh = 0; hh < kDH; ++hh) {
             dma16_untracked(rk, &dst->k[hh][64 * wave], ko[hh] + k0 * rowk);
             dma16_untracked(rv, &dst->v[hh][64 * wave], vo[hh] + k0 * rowv);
         }
-        if (STAGED) {
-            if (PAIR)
-                for (int j = 0; j < 4; ++j) pstage[j] = bload16_any(rp, pvo[j] + k0 * 2u, prange);
-            if (MASK && wave == 0 && lane < 8) mstage = bload16_any(rm, 16u * lane + k0 * 2u, (uint32_t)L * 2u);
-        } else {
+        if (!STAGED) {
             if (PAIR)
                 for (int j = 0; j < 4; ++j) dma16_untracked(rp, &dst->pt[64 * (4 * wave + j)], pvo[j] + k0 * 2u);
             if (MASK && wave == 0 && lane < 8) dma16_untracked(rm, &dst->mt[0], 16u * lane + k0 * 2u);
         }
+    };
+    auto copy_staged = [&](int blk) {
+        if (!STAGED) return;
+        const uint32_t k0 = (uint32_t)blk * kKB;
+        if (PAIR)
+            for (int j = 0; j < 4; ++j) pstage[j] = bload16_any(rp, pvo[j] + k0 * 2u, prange);
+        if (MASK && wave == 0 && lane < 8) mstage = bload16_any(rm, 16u * lane + k0 * 2u, (uint32_t)L * 2u);
     };
     auto land_block = [&](Buf* __restrict__ dst) {
         if (!STAGED) return;
@@ -231,7 +236,8 @@ __global__ __launch_bounds__(kWaves * 64, (D <= 32 && !STAGED) ? 3 : 2) void bwd
     for (int t = 0; t < 2; ++t)
         for (int dh = 0; dh < kDHT; ++dh) dqacc[t][dh] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    copy_block(0, &sm[0]);
+    copy_direct(0, &sm[0]);
+    copy_staged(0);
     land_block(&sm[0]);
     wait_all();
     __syncthreads();
@@ -239,10 +245,9 @@ __global__ __launch_bounds__(kWaves * 64, (D <= 32 && !STAGED) ? 3 : 2) void bwd
     auto step = [&](int it, const Buf* __restrict__ cur, Buf* __restrict__ nxt, auto tail_tag) {
         constexpr bool TAIL = decltype(tail_tag)::value;
         const int k0 = it * kKB;
-        // aligned bias rows: the next block's copies first (the other buffer's
-        // readers all passed the previous barrier); STAGED keeps them after
-        // the block's LDS reads, whose registers its staged loads reuse
-        if (!STAGED && it + 1 < nblocks) copy_block(it + 1, nxt);
+        // the next block's direct copies first (the other buffer's readers all
+        // passed the previous barrier), its staged chunks after the reads
+        if (it + 1 < nblocks) copy_direct(it + 1, nxt);
         // A operands: K and V rows (key 16kt + c, chunk g) and transposed K
         // for dQ^T = K^T.dS^T (column 16dh + c over keys 32cc + 4g + 0..3 and
         // 32cc + 16 + 4g + 0..3)
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(kWaves * 64, (D <= 32 && !STAGED) ? 3 : 2) void bwd
                 }
         }
 
-        if (STAGED && it + 1 < nblocks) copy_block(it + 1, nxt);
+        if (STAGED && it + 1 < nblocks) copy_staged(it + 1);
 
         f32x4 s[2][kKT], dp[2][kKT];
         for (int kt = 0; kt < kKT; ++kt)
@@ -451,17 +456,24 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
     const u16* cpair = PAIR ? p.pair + b * st.pb : p.q;
     const float* clse = p.lse + bn * p.H * st.lrow;
     const float* cdelta = p.delta + bn * p.H * st.lrow;
-    auto copy_block = [&](KvBuf<QS, kDH, KT>* __restrict__ dst) {
-        // untracked copies, waited for by wait_all() before the step's barrier
+    // The copies of the step at the cursor: the direct ones (q, dO and, with
+    // aligned rows, the pair tile) go straight into LDS as untracked copies,
+    // waited for by wait_all() before the step's barrier; copy_rest loads the
+    // lse / delta rows and (STAGED) the pair chunks into registers.
+    auto copy_direct = [&](KvBuf<QS, kDH, KT>* __restrict__ dst) {
         dma16_untracked(rq, &dst->q[qhh][64 * qrg], qoff + cqo);
         dma16_untracked(rdo, &dst->dout[qhh][64 * qrg], dooff + cdo);
-        if (PAIR) {
+        if (PAIR && !STAGED) {
+            const Rsrc rp = make_rsrc(cpair, bias_range(last * rowp + (uint32_t)L * 2u, false));
+            for (int j = 0; j < PCW; ++j)
+                dma16_untracked(rp, &dst->pt[64 * (PCW * wave + j)], pvo[j] + (uint32_t)cq0 * rowp);
+        }
+    };
+    auto copy_rest = [&]() {
+        if (PAIR && STAGED) {
             const uint32_t prange = last * rowp + (uint32_t)L * 2u;
-            const Rsrc rp = make_rsrc(cpair, bias_range(prange, STAGED));
-            for (int j = 0; j < PCW; ++j) {
-                if (STAGED) pstage[j] = bload16_any(rp, pvo[j] + (uint32_t)cq0 * rowp, prange);
-                else dma16_untracked(rp, &dst->pt[64 * (PCW * wave + j)], pvo[j] + (uint32_t)cq0 * rowp);
-            }
+            const Rsrc rp = make_rsrc(cpair, bias_range(prange, true));
+            for (int j = 0; j < PCW; ++j) pstage[j] = bload16_any(rp, pvo[j] + (uint32_t)cq0 * rowp, prange);
         }
         if (wave == 0 && lane < QS) {
             const int i = cq0 + lane;
@@ -497,7 +509,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
     float dm[KT];
     for (int t = 0; t < KT; ++t) dm[t] = 0.f;
 
-    copy_block(&sm[0]);
+    copy_direct(&sm[0]);
+    copy_rest();
     next_copy();
     put_rows(&sm[0]);
     wait_all();
@@ -518,10 +531,14 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
     for (int it = 0; it < nsteps; ++it) {
         const KvBuf<QS, kDH, KT>* __restrict__ cur = &sm[it & 1];
         KvBuf<QS, kDH, KT>* __restrict__ nxt = &sm[(it & 1) ^ 1];
-        // aligned bias rows: the next step's copies first (see the dq kernel)
-        if (!STAGED && it + 1 < nsteps) {
-            copy_block(nxt);
-            next_copy();
+        // the next step's direct copies first (see the dq kernel); STAGED
+        // loads its registers after the step's reads
+        if (it + 1 < nsteps) {
+            copy_direct(nxt);
+            if (!STAGED) {
+                copy_rest();
+                next_copy();
+            }
         }
         if (qbk == 0) {
             // aligned bias rows: later heads were loaded during the previous
@@ -569,7 +586,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dkdv_mfma(Params p) {
         }
 
         if (STAGED && it + 1 < nsteps) {
-            copy_block(nxt);
+            copy_rest();
             next_copy();
         }
 
@@ -923,22 +940,30 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
         if (MASK) cm += st.mn;
         clse += lstep, cdelta += lstep;
     };
-    auto copy_step = [&](Buf* __restrict__ dst) {
+    // The copies of the step at the cursor: the direct ones (q, dO, k, v and,
+    // with aligned rows, the mask chunk) go straight into LDS as untracked
+    // copies, waited for by wait_all() before the step's barrier; copy_rest
+    // loads the lse / delta rows and (STAGED) the mask chunk into registers.
+    auto copy_direct = [&](Buf* __restrict__ dst) {
         const Rsrc rq = make_rsrc(cq, last * rowq + D * 2);
         const Rsrc rd = make_rsrc(cd, last * rowo + D * 2);
         const Rsrc rk = make_rsrc(ck, last * rowk + D * 2);
         const Rsrc rv = make_rsrc(cv, last * rowv + D * 2);
-        // untracked copies, waited for by wait_all() before the step's barrier
         for (int hh = 0; hh < kDH; ++hh) {
             dma16_untracked(rq, &dst->q[hh][64 * wave], qoff[hh]);
             dma16_untracked(rd, &dst->dout[hh][64 * wave], dooff[hh]);
             dma16_untracked(rk, &dst->k[hh][64 * wave], koff[hh]);
             dma16_untracked(rv, &dst->v[hh][64 * wave], voff[hh]);
         }
-        if (MASK && wave == 0 && lane < 8) {
-            const Rsrc rm = make_rsrc(cm, bias_range((uint32_t)L * 2u, STAGED));
-            if (STAGED) mstage = bload16_any(rm, (uint32_t)j0 * 2u + 16u * lane, (uint32_t)L * 2u);
-            else dma16_untracked(rm, &dst->mt[0], (uint32_t)j0 * 2u + 16u * lane);
+        if (MASK && !STAGED && wave == 0 && lane < 8) {
+            const Rsrc rm = make_rsrc(cm, bias_range((uint32_t)L * 2u, false));
+            dma16_untracked(rm, &dst->mt[0], (uint32_t)j0 * 2u + 16u * lane);
+        }
+    };
+    auto copy_rest = [&]() {
+        if (MASK && STAGED && wave == 0 && lane < 8) {
+            const Rsrc rm = make_rsrc(cm, bias_range((uint32_t)L * 2u, true));
+            mstage = bload16_any(rm, (uint32_t)j0 * 2u + 16u * lane, (uint32_t)L * 2u);
         }
         if (wave == 1) {
             const int i = i0 + lane;
@@ -957,7 +982,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
     f32x4 acc[kKT];
     for (int kt = 0; kt < kKT; ++kt) acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    copy_step(&sm[0]);
+    copy_direct(&sm[0]);
+    copy_rest();
     next_step();
     put_rows(&sm[0]);
     wait_all();
@@ -966,10 +992,14 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
         const int it = (int)(n - n0);
         const Buf* __restrict__ cur = &sm[it & 1];
         Buf* __restrict__ nxt = &sm[(it & 1) ^ 1];
-        // aligned mask rows: the next step's copies first (see the dq kernel)
-        if (!STAGED && n + 1 < n1) {
-            copy_step(nxt);
-            next_step();
+        // the next step's direct copies first (see the dq kernel); STAGED
+        // loads its registers after the step's reads
+        if (n + 1 < n1) {
+            copy_direct(nxt);
+            if (!STAGED) {
+                copy_rest();
+                next_step();
+            }
         }
         const int sw = g ^ ((c >> 2) & 3);
         V8 qop[kDH], dop[kDH], kop[kKT][kDH], vop[kKT][kDH];
@@ -987,7 +1017,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void bwd_dpair_part(PartParams pp) 
         }
         const float lsq = cur->ls[16 * wave + c], dlq = cur->dl[16 * wave + c];
         if (STAGED && n + 1 < n1) {
-            copy_step(nxt);
+            copy_rest();
             next_step();
         }
         for (int kt = 0; kt < kKT; ++kt) {
