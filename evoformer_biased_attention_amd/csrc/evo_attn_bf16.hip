@@ -165,6 +165,16 @@ __device__ inline bool any_neg_nan_bf16(uint4 x, int n) {
     return any;
 }
 
+// The same for all 8 values (the whole chunk lies below L): one packed
+// unsigned maximum over the chunk, then its two halves against 0xff80.
+__device__ inline bool any_neg_nan_bf16_all(uint4 x) {
+    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+    const us2 m = __builtin_elementwise_max(
+        __builtin_elementwise_max(__builtin_bit_cast(us2, x.x), __builtin_bit_cast(us2, x.y)),
+        __builtin_elementwise_max(__builtin_bit_cast(us2, x.z), __builtin_bit_cast(us2, x.w)));
+    return m[0] > 0xff80u || m[1] > 0xff80u;
+}
+
 // Whether one of the first n 16-bit values of x is other than -inf in
 // binary16 (0xfc00).
 __device__ inline bool any_not_neg_inf_f16(uint4 x, int n) {
@@ -392,8 +402,14 @@ __device__ bool run_fast(const Params& p, const Slice& s, FastSmem<(D + 31) / 32
             if (E::kF16)
                 all_neg_inf = all_neg_inf && mask_on &&
                               !wave_any(any_not_neg_inf_f16(mw, L - k0 - 8 * (lane & 7)));
-            else if (mask_on)
-                mask_neg_nan = mask_neg_nan || wave_any(any_neg_nan_bf16(mw, L - k0 - 8 * (lane & 7)));
+            else if (mask_on) {
+                // a chunk that ends past L (only in the last block) needs the element-wise test
+                const int nk = L - k0 - 8 * (lane & 7);
+                bool nn;
+                if (wave_any(nk < 8)) nn = any_neg_nan_bf16(mw, nk);
+                else nn = any_neg_nan_bf16_all(mw);
+                mask_neg_nan = mask_neg_nan || wave_any(nn);
+            }
         }
         if (mask_on) scores(cur, acc, std::true_type{});
         else scores(cur, acc, std::false_type{});
