@@ -195,6 +195,20 @@ def test_bwd_ragged(torch_dev, shape, d, dtype):
 # one range of n per tile).
 # Every bias combination, bias gradients on and off, against the full backward
 # oracle.
+# The dk/dv stage loads the next head's K and V rows during the current
+# head's last query step (aligned bias rows), and every stage issues the next
+# step's copies at the top of the step.  Heads with one query step (L <= 64:
+# that step is both the head's first and its last) and with two, four heads,
+# against the oracle.
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("L,D", [(8, 32), (64, 32), (64, 64), (128, 16), (128, 32)])
+def test_bwd_next_head_rows_loaded_early(torch_dev, dtype, L, D):
+    w = S.random_problem(1, 3, L, 4, D, dtype=dtype, seed=L * 10 + D, mask="tail", pair="normal", mask_frac=0.2)
+    dout = S.random_dout(w.shape, dtype, seed=L + D)
+    say(f"next-head rows {dtype} L={L} D={D}")
+    parity(torch_dev, w, dout)
+
+
 F32_MFMA_BWD = [(1, 2, 4, 2, 16), (1, 3, 20, 2, 32), (2, 2, 68, 3, 32), (1, 2, 132, 2, 16), (1, 1, 192, 4, 32),
                 (1, 2, 36, 2, 64), (2, 2, 100, 3, 64), (1, 1, 132, 2, 64), (1, 2, 4, 2, 8), (2, 2, 132, 3, 8)]
 

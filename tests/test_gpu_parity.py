@@ -294,6 +294,28 @@ def test_bf16_nan_mask_values(torch_dev, L):
     compare(o[:, ~nan_seq], l[:, ~nan_seq], ro[:, ~nan_seq], rl[:, ~nan_seq], "bf16", f"other sequences, L={L}")
 
 
+@pytest.mark.parametrize("L", [200, 203])
+def test_bf16_negative_nan_mask_later_blocks(torch_dev, L):
+    """A negative NaN in a bf16 mask in a middle 64-key block (its chunk lies wholly below L, tested with one
+    packed maximum) and in the last key (the last block, where chunks end past L and the test goes element by
+    element): both sequences come out NaN; a sequence with a -inf run and a clean one keep full parity."""
+    B, N, H, D = 1, 4, 2, 32
+    w = S.random_problem(B, N, L, H, D, dtype="bf16", seed=L + 29, mask="zero", pair="normal")
+    m = w.mask.copy()
+    m[0, 0, 0, 0, 130] = 0xFFC1      # negative NaN, third block
+    m[0, 1, 0, 0, L - 1] = 0xFFFF    # negative NaN, last key
+    m[0, 2, 0, 0, 64:128] = 0xFF80   # -inf over a whole block
+    w.mask = m
+    o, l = run_gpu(torch_dev, w)
+    ro, rl = oracle.fwd(w.q, w.k, w.v, w.mask, w.pair, dtype="bf16", nthreads=THREADS)
+    nan_seq = np.zeros(N, bool)
+    nan_seq[:2] = True
+    assert np.isnan(ro[:, nan_seq]).all() and np.isnan(rl[:, nan_seq]).all()
+    assert np.isnan(o[:, nan_seq]).all(), "a NaN mask value must make its sequence's outputs NaN"
+    assert np.isnan(l[:, nan_seq]).all(), "a NaN mask value must make its sequence's lse NaN"
+    compare(o[:, ~nan_seq], l[:, ~nan_seq], ro[:, ~nan_seq], rl[:, ~nan_seq], "bf16", f"other sequences, L={L}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("L", [77, 96])
 def test_neg_inf_pair_bias_exact_path(torch_dev, L, dtype):
